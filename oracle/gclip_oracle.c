@@ -1,0 +1,219 @@
+/*
+ * gclip_oracle.c -- plain, slow, obviously correct CPU oracle for global
+ * L2-norm gradient clipping.  TEST INFRASTRUCTURE ONLY: it exists so that the
+ * GPU library can be checked against it.  Only the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg load it; the product path never does.
+ *
+ * What it computes (all in IEEE binary64, one element at a time, in list order):
+ *
+ *   "Gradient clipping" glossary page (paweldubiel.com), section "Mechanism and
+ *   details": for a threshold c > 0, the clipped gradient is g itself when
+ *   ||g||_2 <= c and c * g / ||g||_2 otherwise.
+ *
+ *   "Grad clip" lesson page (unhomeschool.com, ru), section "Math": the norm is
+ *   the square root of the sum of g^2 over every element of every parameter
+ *   tensor (the whole list is one vector, section "Two variants: Per-Tensor or
+ *   Global"), and the factor applied when clipping is max_norm / norm.
+ *
+ *   "Backprop" lesson page (unhomeschool.com, vi), section "Accumulation across
+ *   microbatches": after summing microbatch gradients the buffer is averaged by
+ *   1/n_microbatches before the optimizer step; the glossary page, section
+ *   "Order changes the result", puts clipping after the whole effective batch
+ *   has been collected.  So the norm is that of the averaged gradient a*g and
+ *   the factor written back is a * coef.
+ *
+ *   Glossary page, section "Mechanism and details", last paragraph: a NaN or
+ *   infinite value calls for diagnosis, and an error-if-nonfinite switch lets
+ *   the caller stop that update.
+ *
+ * Readings where the pages are silent (each one is listed in the design notes):
+ *   - the tie norm == c leaves the gradient unchanged (both pages write "<=");
+ *   - no epsilon is added to the norm before dividing;
+ *   - "non-finite" is tested on the elements (any NaN or +-Inf);
+ *   - with the stop switch on and a non-finite element, nothing is written;
+ *   - with the switch off, plain IEEE arithmetic decides (NaN > c is false);
+ *   - outputs are rounded once, to nearest-even, into the storage format,
+ *     keeping subnormals and overflowing to +-Inf.
+ *
+ * Storage formats are decoded and encoded from their bit layouts (IEEE 754
+ * binary32 and binary16; bfloat16 is the top half of binary32), not through
+ * any GPU code.  Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_F16 1
+#define OR_BF16 2
+
+/* exponent bits / stored mantissa bits / bytes per element of each format */
+static int fmt_ebits(int dt) { return dt == OR_F16 ? 5 : 8; }
+static int fmt_mbits(int dt) { return dt == OR_F32 ? 23 : (dt == OR_F16 ? 10 : 7); }
+static int fmt_bytes(int dt) { return dt == OR_F32 ? 4 : 2; }
+
+static uint32_t load_bits(const void* base, int64_t i, int dt) {
+  if (fmt_bytes(dt) == 4) {
+    uint32_t b;
+    memcpy(&b, (const unsigned char*)base + 4 * i, 4);
+    return b;
+  }
+  uint16_t h;
+  memcpy(&h, (const unsigned char*)base + 2 * i, 2);
+  return h;
+}
+
+static void store_bits(void* base, int64_t i, int dt, uint32_t b) {
+  if (fmt_bytes(dt) == 4) {
+    memcpy((unsigned char*)base + 4 * i, &b, 4);
+  } else {
+    uint16_t h = (uint16_t)b;
+    memcpy((unsigned char*)base + 2 * i, &h, 2);
+  }
+}
+
+/* Value of a bit pattern: (-1)^s * 1.m * 2^(e-bias) for normal numbers,
+ * (-1)^s * 0.m * 2^(1-bias) for subnormals, Inf/NaN when e is all ones. */
+double oracle_decode_bits(uint32_t bits, int32_t dt) {
+  const int eb = fmt_ebits(dt), mb = fmt_mbits(dt);
+  const int bias = (1 << (eb - 1)) - 1;
+  const uint32_t sign = (bits >> (eb + mb)) & 1u;
+  const uint32_t e = (bits >> mb) & ((1u << eb) - 1u);
+  const uint32_t m = bits & ((1u << mb) - 1u);
+  double v;
+  if (e == (1u << eb) - 1u) {
+    v = (m == 0) ? INFINITY : NAN;
+  } else if (e == 0) {
+    v = ldexp((double)m, 1 - bias - mb);
+  } else {
+    v = ldexp((double)((1u << mb) + m), (int)e - bias - mb);
+  }
+  return sign ? -v : v;
+}
+
+/* Round a binary64 value once, to nearest with ties to even, into the format
+ * and return its bit pattern.  Subnormal results are kept; a result whose
+ * rounded magnitude exceeds the largest finite value becomes +-Inf. */
+uint32_t oracle_encode(double x, int32_t dt) {
+  const int eb = fmt_ebits(dt), mb = fmt_mbits(dt);
+  const int bias = (1 << (eb - 1)) - 1;
+  const int emin = 1 - bias, emax = bias;
+  const uint32_t sign = signbit(x) ? (1u << (eb + mb)) : 0u;
+  const uint32_t exp_all = ((1u << eb) - 1u) << mb;
+  if (isnan(x)) return sign | exp_all | (1u << (mb - 1));
+  if (isinf(x)) return sign | exp_all;
+  if (x == 0.0) return sign;
+  double a = fabs(x);
+  int e2;
+  (void)frexp(a, &e2);
+  int E = e2 - 1;                       /* 2^E <= a < 2^(E+1) */
+  if (E > emax) return sign | exp_all;  /* already beyond the top binade */
+  if (E < emin) E = emin;               /* subnormal range: fixed quantum */
+  const double q = ldexp(a, mb - E);    /* a / quantum, exact (power of two) */
+  double r = nearbyint(q);              /* default rounding: nearest, ties even */
+  const double one = ldexp(1.0, mb);    /* 2^mb: the implicit leading bit */
+  if (r >= 2.0 * one) {                 /* rounded up into the next binade */
+    r = one;
+    E += 1;
+    if (E > emax) return sign | exp_all;
+  }
+  if (r >= one) {
+    return sign | ((uint32_t)(E + bias) << mb) | (uint32_t)(r - one);
+  }
+  return sign | (uint32_t)r; /* subnormal or zero: biased exponent 0 */
+}
+
+double oracle_decode(const void* base, int64_t i, int32_t dt) {
+  return oracle_decode_bits(load_bits(base, i, dt), dt);
+}
+
+static int dtype_ok(int32_t dt) { return dt == OR_F32 || dt == OR_F16 || dt == OR_BF16; }
+
+/* Sum over every element of every tensor, in list order, of (a*g)^2; also
+ * whether any element is NaN or +-Inf.  Returns 0, or -1 on a bad argument. */
+int oracle_sumsq(const void* const* ptrs, const int64_t* numels, int32_t n, int32_t dt, double avg,
+                 double* sumsq, int32_t* nonfinite) {
+  if (n < 0 || !dtype_ok(dt) || !sumsq || !nonfinite) return -1;
+  double total = 0.0;
+  int32_t nf = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    if (numels[t] < 0) return -1;
+    for (int64_t i = 0; i < numels[t]; ++i) {
+      const double g = oracle_decode(ptrs[t], i, dt);
+      if (!isfinite(g)) nf = 1;
+      const double u = avg * g;
+      total += u * u;
+    }
+  }
+  *sumsq = total;
+  *nonfinite = nf;
+  return 0;
+}
+
+/* Sum of (a*g)^2 of each tensor on its own (per-tensor diagnostics). */
+int oracle_tensor_sumsq(const void* const* ptrs, const int64_t* numels, int32_t n, int32_t dt, double avg,
+                        double* out) {
+  if (n < 0 || !dtype_ok(dt) || !out) return -1;
+  for (int32_t t = 0; t < n; ++t) {
+    if (numels[t] < 0) return -1;
+    double s = 0.0;
+    for (int64_t i = 0; i < numels[t]; ++i) {
+      const double u = avg * oracle_decode(ptrs[t], i, dt);
+      s += u * u;
+    }
+    out[t] = s;
+  }
+  return 0;
+}
+
+/* The decision.  coef = c / norm when norm > c (strictly), else 1; the factor
+ * written back is a * coef.  skip = 1 when a non-finite element was seen and
+ * the caller asked to stop such an update: then nothing is written. */
+int oracle_decide(double norm, int32_t nonfinite, double max_norm, double avg, int32_t error_if_nonfinite,
+                  double* scale, int32_t* clipped, int32_t* skip) {
+  if (!scale || !clipped || !skip) return -1;
+  const int32_t clip = (norm > max_norm) ? 1 : 0;
+  const double coef = clip ? max_norm / norm : 1.0;
+  *clipped = clip;
+  *skip = (nonfinite && error_if_nonfinite) ? 1 : 0;
+  *scale = avg * coef;
+  return 0;
+}
+
+/* In place: g <- round(g * s) for every element, unless s == 1 (nothing to
+ * do: the gradient passes unchanged, so no byte is rewritten). */
+int oracle_scale(void* const* ptrs, const int64_t* numels, int32_t n, int32_t dt, double s) {
+  if (n < 0 || !dtype_ok(dt)) return -1;
+  if (s == 1.0) return 0;
+  for (int32_t t = 0; t < n; ++t) {
+    if (numels[t] < 0) return -1;
+    for (int64_t i = 0; i < numels[t]; ++i) {
+      const double g = oracle_decode(ptrs[t], i, dt);
+      store_bits(ptrs[t], i, dt, oracle_encode(g * s, dt));
+    }
+  }
+  return 0;
+}
+
+/* The whole path: norm of the averaged gradient, decision, scale in place.
+ * out[0] = sumsq, out[1] = norm, out[2] = applied factor; flags[0] =
+ * nonfinite, flags[1] = clipped, flags[2] = skipped (nothing written). */
+int oracle_clip(void* const* ptrs, const int64_t* numels, int32_t n, int32_t dt, double max_norm, double avg,
+                int32_t error_if_nonfinite, double* out, int32_t* flags) {
+  if (!out || !flags) return -1;
+  double sumsq;
+  int32_t nonfinite;
+  if (oracle_sumsq((const void* const*)ptrs, numels, n, dt, avg, &sumsq, &nonfinite) != 0) return -1;
+  const double norm = sqrt(sumsq);
+  double s;
+  int32_t clipped, skip;
+  oracle_decide(norm, nonfinite, max_norm, avg, error_if_nonfinite, &s, &clipped, &skip);
+  out[0] = sumsq;
+  out[1] = norm;
+  out[2] = skip ? 1.0 : s;
+  flags[0] = nonfinite;
+  flags[1] = clipped;
+  flags[2] = skip;
+  if (skip) return 0;
+  return oracle_scale(ptrs, numels, n, dt, s);
+}

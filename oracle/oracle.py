@@ -1,0 +1,173 @@
+"""ctypes front end of the C oracle in gclip_oracle.c (test infrastructure only).
+
+Each function works on host numpy arrays holding the raw storage of one
+gradient tensor: float32 arrays for "f32", uint16 bit patterns for "f16" and
+"bf16".  The arithmetic all happens in the C file, in binary64:
+
+- ``sumsq``/``clip_`` follow the "Math" section of the grad-clip lesson page
+  (unhomeschool.com, ru): the norm is the square root of the sum of squares of
+  every element of every tensor, and a clip multiplies every element by
+  max_norm / norm;
+- ``decide`` follows the case split of the glossary page (paweldubiel.com,
+  "Mechanism and details"): unchanged when the norm is at most c, otherwise
+  scaled by c / norm; the averaging factor 1/n_microbatches of the backprop
+  page (unhomeschool.com, vi, "Accumulation across microbatches") multiplies
+  the gradient before its norm is taken and is folded into the written factor.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, F16, BF16 = "f32", "f16", "bf16"
+DTYPES = (F32, F16, BF16)
+_CODE = {F32: 0, F16: 1, BF16: 2}
+_NP = {F32: np.float32, F16: np.uint16, BF16: np.uint16}
+
+class Oracle:
+    """Handle on one build of the C oracle (the default build, or another
+    build of the same source that a test asks for)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_decode_bits.argtypes = [ctypes.c_uint32, ctypes.c_int32]
+        lib.oracle_decode_bits.restype = ctypes.c_double
+        lib.oracle_encode.argtypes = [ctypes.c_double, ctypes.c_int32]
+        lib.oracle_encode.restype = ctypes.c_uint32
+        lib.oracle_sumsq.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                     dp, i32p]
+        lib.oracle_sumsq.restype = ctypes.c_int
+        lib.oracle_tensor_sumsq.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_double, dp]
+        lib.oracle_tensor_sumsq.restype = ctypes.c_int
+        lib.oracle_decide.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                                      ctypes.c_int32, dp, i32p, i32p]
+        lib.oracle_decide.restype = ctypes.c_int
+        lib.oracle_scale.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]
+        lib.oracle_scale.restype = ctypes.c_int
+        lib.oracle_clip.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                    ctypes.c_double, ctypes.c_int32, dp, i32p]
+        lib.oracle_clip.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def decode_bits(self, bits: int, dtype: str) -> float:
+        """Value of one stored bit pattern, as a Python float (binary64)."""
+        return self.lib.oracle_decode_bits(int(bits), _CODE[dtype])
+
+    def encode(self, x: float, dtype: str) -> int:
+        """Bit pattern of x rounded once to nearest-even in the storage format."""
+        return int(self.lib.oracle_encode(float(x), _CODE[dtype]))
+
+    def sumsq(self, arrays, dtype: str, avg_factor: float = 1.0):
+        """(sum over all elements of (a*g)^2, any element NaN/Inf) in binary64."""
+        ptrs, numels, n = _marshal(arrays, dtype)
+        s = ctypes.c_double()
+        nf = ctypes.c_int32()
+        rc = self.lib.oracle_sumsq(ptrs, numels, n, _CODE[dtype], float(avg_factor), ctypes.byref(s),
+                                   ctypes.byref(nf))
+        if rc != 0:
+            raise ValueError("oracle_sumsq rejected its arguments")
+        return s.value, bool(nf.value)
+
+    def tensor_sumsq(self, arrays, dtype: str, avg_factor: float = 1.0) -> np.ndarray:
+        """Per-tensor sums of (a*g)^2 in binary64."""
+        ptrs, numels, n = _marshal(arrays, dtype)
+        out = np.zeros(max(n, 1), dtype=np.float64)
+        rc = self.lib.oracle_tensor_sumsq(ptrs, numels, n, _CODE[dtype], float(avg_factor),
+                                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+        if rc != 0:
+            raise ValueError("oracle_tensor_sumsq rejected its arguments")
+        return out[:n]
+
+    def decide(self, norm: float, nonfinite: bool, max_norm: float, avg_factor: float = 1.0,
+               error_if_nonfinite: bool = False):
+        """(factor a*coef, clipped, skipped) for a given norm."""
+        s = ctypes.c_double()
+        c = ctypes.c_int32()
+        k = ctypes.c_int32()
+        self.lib.oracle_decide(float(norm), int(bool(nonfinite)), float(max_norm), float(avg_factor),
+                               int(bool(error_if_nonfinite)), ctypes.byref(s), ctypes.byref(c), ctypes.byref(k))
+        return s.value, bool(c.value), bool(k.value)
+
+    def scale_(self, arrays, dtype: str, s: float) -> None:
+        """In place: every element becomes round(g*s); nothing is written when s == 1."""
+        ptrs, numels, n = _marshal(arrays, dtype)
+        if self.lib.oracle_scale(ptrs, numels, n, _CODE[dtype], float(s)) != 0:
+            raise ValueError("oracle_scale rejected its arguments")
+
+    def clip_(self, arrays, dtype: str, max_norm: float, avg_factor: float = 1.0,
+              error_if_nonfinite: bool = False) -> dict:
+        """The whole path, in place.  Returns sumsq, norm (pre-clip), scale, flags."""
+        ptrs, numels, n = _marshal(arrays, dtype)
+        out = (ctypes.c_double * 3)()
+        flags = (ctypes.c_int32 * 3)()
+        rc = self.lib.oracle_clip(ptrs, numels, n, _CODE[dtype], float(max_norm), float(avg_factor),
+                                  int(bool(error_if_nonfinite)), out, flags)
+        if rc != 0:
+            raise ValueError("oracle_clip rejected its arguments")
+        return {"sumsq": out[0], "norm": out[1], "scale": out[2], "nonfinite": bool(flags[0]),
+                "clipped": bool(flags[1]), "skipped": bool(flags[2])}
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from gclip_oracle.c (built on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def _marshal(arrays, dtype):
+    if dtype not in _CODE:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    for a in arrays:
+        if a.dtype != _NP[dtype] or not a.flags.c_contiguous:
+            raise TypeError(f"oracle expects contiguous {np.dtype(_NP[dtype]).name} storage for {dtype}")
+    n = len(arrays)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[a.ctypes.data for a in arrays])
+    numels = (ctypes.c_int64 * max(n, 1))(*[a.size for a in arrays])
+    return ptrs, numels, n
+
+
+def decode_bits(bits, dtype):
+    return default().decode_bits(bits, dtype)
+
+
+def encode(x, dtype):
+    return default().encode(x, dtype)
+
+
+def sumsq(arrays, dtype, avg_factor=1.0):
+    return default().sumsq(arrays, dtype, avg_factor)
+
+
+def tensor_sumsq(arrays, dtype, avg_factor=1.0):
+    return default().tensor_sumsq(arrays, dtype, avg_factor)
+
+
+def decide(norm, nonfinite, max_norm, avg_factor=1.0, error_if_nonfinite=False):
+    return default().decide(norm, nonfinite, max_norm, avg_factor, error_if_nonfinite)
+
+
+def scale_(arrays, dtype, s):
+    return default().scale_(arrays, dtype, s)
+
+
+def clip_(arrays, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False):
+    return default().clip_(arrays, dtype, max_norm, avg_factor, error_if_nonfinite)

@@ -1,0 +1,411 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, none of which retypes the oracle's own formula.
+
+Every pin takes an ``oracle.Oracle`` handle so the same pins can be run
+against deliberately broken builds of the oracle (tests/test_oracle_mutants.py).
+Values are decoded here with numpy / torch / struct, never with the oracle's
+own decoder.
+"""
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+
+from synth import gradsets as gs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DTYPES = ("f32", "f16", "bf16")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- decoding helpers (library routines)
+def values(a: np.ndarray, dtype: str) -> np.ndarray:
+    """binary64 values of raw storage, through numpy's own conversions."""
+    if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "f16":
+        return a.view(np.float16).astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def struct_value(bits: int, dtype: str) -> float:
+    """One value through Python's struct module (IEEE binary16/binary32)."""
+    if dtype == "f32":
+        return struct.unpack("<f", struct.pack("<I", int(bits)))[0]
+    if dtype == "f16":
+        return struct.unpack("<e", struct.pack("<H", int(bits)))[0]
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+def raw_bits(a: np.ndarray, dtype: str) -> np.ndarray:
+    return a.view(np.uint32) if dtype == "f32" else a.view(np.uint16)
+
+
+def ulp(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the storage format at |v| (upper neighbour)."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    if dtype == "f32":
+        return np.spacing(v.astype(np.float32)).astype(np.float64)
+    if dtype == "f16":
+        return np.spacing(v.astype(np.float16)).astype(np.float64)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    e = np.maximum(e, -126.0)
+    return np.exp2(e - 7.0)
+
+
+def lib_round(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """Raw storage of x64 rounded to nearest-even by numpy (f32, f16)."""
+    if dtype == "f32":
+        return np.asarray(x64, dtype=np.float64).astype(np.float32)
+    if dtype == "f16":
+        return np.asarray(x64, dtype=np.float64).astype(np.float16).view(np.uint16)
+    raise ValueError("numpy has no bfloat16")
+
+
+def store(vals, dtype):
+    return gs.to_storage(np.asarray(vals, dtype=np.float64), dtype)
+
+
+# ---------------------------------------------------------------- the pins
+def pin_worked_6_8(o):
+    """[6, 8] with threshold 5 has norm 10 and becomes [3, 4] (glossary page,
+    'Shorten the arrow, keep the direction'); exact in every storage format."""
+    gd = golden("worked_6_8.json")
+    for dt in DTYPES:
+        arrs = [store(gd["g"], dt)]
+        r = o.clip_(arrs, dt, gd["max_norm"])
+        assert r["norm"] == gd["norm"], (dt, r)
+        assert r["clipped"] and not r["nonfinite"] and not r["skipped"], (dt, r)
+        assert r["scale"] == gd["max_norm"] / gd["norm"], (dt, r)
+        assert list(values(arrs[0], dt)) == gd["clipped"], (dt, values(arrs[0], dt))
+
+
+def pin_not_per_coordinate(o):
+    """Norm clipping keeps the direction; clipping each coordinate to [-5, 5]
+    would give [5, 5] with norm about 7.07 (glossary page)."""
+    gd = golden("worked_6_8.json")
+    a = [store(gd["g"], "f32")]
+    o.clip_(a, "f32", gd["max_norm"])
+    out = values(a[0], "f32")
+    per_coord = np.clip(np.array(gd["g"]), -gd["max_norm"], gd["max_norm"])
+    assert list(per_coord) == gd["per_coordinate_clipped"]
+    assert abs(np.linalg.norm(per_coord) - gd["per_coordinate_norm_approx"]) < 5e-3
+    assert not np.array_equal(out, per_coord)
+    assert np.linalg.norm(out) == gd["max_norm"]
+    # same direction: out is a positive multiple of g
+    g = np.array(gd["g"])
+    assert abs(out[0] * g[1] - out[1] * g[0]) == 0.0 and out[0] / g[0] > 0
+
+
+def pin_sgd_step_length(o):
+    """Plain SGD with lr 0.1: the clipped step has length 0.5 instead of 1."""
+    gd = golden("worked_6_8.json")
+    a = [store(gd["g"], "f32")]
+    o.clip_(a, "f32", gd["max_norm"])
+    lr = gd["sgd_lr"]
+    assert abs(np.linalg.norm(-lr * values(a[0], "f32")) - gd["sgd_step_length_clipped"]) < 1e-12
+    assert abs(np.linalg.norm(-lr * np.array(gd["g"])) - gd["sgd_step_length_unclipped"]) < 1e-12
+
+
+def pin_accumulate_then_clip(o):
+    """10 and -9 add up to 1, which a clip at 5 keeps; clipping each first gives
+    5 and -5, summing to 0 (glossary page, 'Order changes the result').  On a
+    one-element list norm clipping and value clipping coincide."""
+    gd = golden("accumulate_then_clip.json")
+    c = gd["max_norm"]
+    clipped_each = []
+    for v in gd["contributions"]:
+        a = [store([v], "f32")]
+        o.clip_(a, "f32", c)
+        clipped_each.append(float(values(a[0], "f32")[0]))
+    assert clipped_each == gd["clipped_contributions"]
+    assert sum(clipped_each) == gd["sum_of_clipped"]
+    acc = np.float32(gd["contributions"][0]) + np.float32(gd["contributions"][1])
+    a = [np.array([acc], dtype=np.float32)]
+    r = o.clip_(a, "f32", c)
+    assert float(a[0][0]) == gd["clip_of_sum"] and not r["clipped"] and r["norm"] == gd["sum"]
+
+
+def pin_tie_passes_unchanged(o):
+    """norm == max_norm passes unchanged (grad-clip lesson 'Math': '<=' passes;
+    glossary page uses '<=' too); just below the norm it clips."""
+    for dt in DTYPES:
+        a = [store([3.0, 4.0], dt)]
+        before = a[0].copy()
+        r = o.clip_(a, dt, 5.0)
+        assert not r["clipped"] and r["scale"] == 1.0, (dt, r)
+        assert np.array_equal(raw_bits(a[0], dt), raw_bits(before, dt))
+    a = [store([3.0, 4.0], "f32")]
+    r = o.clip_(a, "f32", 5.0 * (1 - 2.0 ** -30))
+    assert r["clipped"] and r["scale"] < 1.0
+
+
+def pin_below_threshold_bitwise(o):
+    """norm <= max_norm: every byte of every tensor is left as it was."""
+    rng = np.random.default_rng(11)
+    for dt in DTYPES:
+        for _ in range(5):
+            g = gs.random_list(rng, dt, max_tensors=5, max_numel=40)
+            norm = math.sqrt(sum(float(np.sum(values(x, dt) ** 2)) for x in g.arrays))
+            before = [x.copy() for x in g.arrays]
+            r = o.clip_(g.arrays, dt, max(2.0 * norm, 1e-30))
+            assert not r["clipped"]
+            for x, y in zip(g.arrays, before):
+                assert np.array_equal(raw_bits(x, dt), raw_bits(y, dt))
+
+
+def pin_post_clip_norm(o):
+    """After a clip the global norm is max_norm (grad-clip lesson 'Math'), up
+    to the rounding of each stored output: |‖out‖ - c| <= sqrt(sum ulp(out)^2)."""
+    rng = np.random.default_rng(12)
+    for dt in DTYPES:
+        for c in (1.0, 0.37, 5.0):
+            g = gs.random_list(rng, dt, max_tensors=6, max_numel=50, sigma=3.0)
+            if not g.arrays or sum(x.size for x in g.arrays) == 0:
+                continue
+            r = o.clip_(g.arrays, dt, c)
+            if not r["clipped"]:
+                continue
+            outv = np.concatenate([values(x, dt) for x in g.arrays])
+            bound = math.sqrt(float(np.sum(ulp(outv, dt) ** 2))) + 1e-14 * c
+            assert abs(np.linalg.norm(outv) - c) <= bound, (dt, c, np.linalg.norm(outv), bound)
+
+
+def pin_single_global_factor(o):
+    """One factor for every element of every tensor (grad-clip lesson, 'Two
+    variants'): each output is g*s rounded once to nearest-even (numpy's
+    rounding for f32/f16; a half-ulp bound for bf16)."""
+    rng = np.random.default_rng(13)
+    for dt in DTYPES:
+        g = gs.random_list(rng, dt, max_tensors=6, max_numel=50, sigma=2.0)
+        g.arrays.append(store(rng.standard_normal(64) * 4.0, dt))
+        inp = [values(x, dt) for x in g.arrays]
+        r = o.clip_(g.arrays, dt, 0.5)
+        assert r["clipped"]
+        s = r["scale"]
+        for x, v in zip(g.arrays, inp):
+            if dt in ("f32", "f16"):
+                assert np.array_equal(raw_bits(x, dt), raw_bits(lib_round(v * s, dt), dt)), dt
+            else:
+                out = values(x, dt)
+                assert np.all(np.abs(out - v * s) <= 0.5 * ulp(v * s, dt) * 1.0000001), dt
+
+
+def pin_joint_norm_library(o):
+    """The norm covers all tensors jointly (glossary page on clip_grad_norm_):
+    sumsq == sum over tensors of numpy.linalg.norm(t)^2, and per-tensor sums
+    match numpy tensor by tensor."""
+    rng = np.random.default_rng(14)
+    for dt in DTYPES:
+        arrs = [store(rng.standard_normal(n) * sd, dt) for n, sd in ((1000, 1.0), (37, 0.01), (1, 5.0), (513, 2.0))]
+        s, nf = o.sumsq(arrs, dt)
+        ref = sum(np.linalg.norm(values(x, dt)) ** 2 for x in arrs)
+        assert not nf and abs(s - ref) <= 1e-12 * ref, (dt, s, ref)
+        per = o.tensor_sumsq(arrs, dt)
+        for p, x in zip(per, arrs):
+            q = np.linalg.norm(values(x, dt)) ** 2
+            assert abs(p - q) <= 1e-12 * q
+        # a single tensor reduces to the library 2-norm
+        r = o.clip_([arrs[0].copy()], dt, 1e9)
+        assert abs(r["norm"] - np.linalg.norm(values(arrs[0], dt))) <= 1e-13 * r["norm"]
+
+
+def pin_bruteforce_exact(o):
+    """Tiny random lists: math.fsum of the exact squares (values decoded by
+    struct) is the correctly rounded sum; Fraction decides S > c^2 exactly."""
+    rng = np.random.default_rng(15)
+    for dt in DTYPES:
+        for trial in range(30):
+            sigma = [1.0, 1e-3, 1e-6, 300.0][trial % 4] if dt != "f16" else [1.0, 1e-3, 1e-6, 30.0][trial % 4]
+            g = gs.random_list(rng, dt, max_tensors=5, max_numel=50, sigma=sigma)
+            a = [0.25, 1.0, 1.0 / 3.0][trial % 3]
+            vals = [struct_value(b, dt) for x in g.arrays for b in raw_bits(x, dt)]
+            exact = sum((Fraction(a) * Fraction(v)) ** 2 for v in vals) if vals else Fraction(0)
+            s, nf = o.sumsq(g.arrays, dt, a)
+            assert not nf
+            n = max(len(vals), 1)
+            assert abs(Fraction(s) - exact) <= Fraction(n + 2) * Fraction(2.0 ** -52) * exact, (dt, s, float(exact))
+            fs = math.fsum((a * v) ** 2 for v in vals) if a != 1.0 / 3.0 else None
+            if fs is not None:
+                assert abs(s - fs) <= n * 2.0 ** -53 * fs
+            # exact decision; skip near-ties the rounding of S could flip
+            for c in (0.5, 1.0, 3.0, 40.0):
+                c2 = Fraction(c) ** 2
+                if exact != 0 and abs(exact - c2) <= Fraction(1, 10 ** 9) * c2:
+                    continue
+                arrs = [x.copy() for x in g.arrays]
+                r = o.clip_(arrs, dt, c, a)
+                assert r["clipped"] == (exact > c2), (dt, c, float(exact))
+
+
+def pin_decode_library(o):
+    """Every fp16 and bf16 bit pattern, and many fp32 ones, decode to the same
+    value as numpy's / torch's conversion (NaN to NaN)."""
+    import torch
+    allbits = np.arange(65536, dtype=np.uint32)
+    ref16 = allbits.astype(np.uint16).view(np.float16).astype(np.float64)
+    refbf = torch.from_numpy(allbits.astype(np.uint16).view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    rng = np.random.default_rng(16)
+    f32bits = np.concatenate([rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32),
+                              np.array([0, 1, 0x7F800000, 0xFF800000, 0x7FC00000, 0x80000001, 0x00800000, 0x7F7FFFFF],
+                                       dtype=np.uint32)])
+    with np.errstate(invalid="ignore"):
+        ref32 = f32bits.view(np.float32).astype(np.float64)
+    for dt, bits, ref in (("f16", allbits, ref16), ("bf16", allbits, refbf), ("f32", f32bits, ref32)):
+        got = np.array([o.decode_bits(int(b), dt) for b in bits])
+        same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+        assert np.all(same), (dt, bits[~same][:5])
+        sign_ok = np.signbit(got[ref == 0]) == np.signbit(ref[ref == 0])
+        assert np.all(sign_ok), dt
+
+
+def _encode_cases(rng, dt):
+    emin, mb, emax = {"f32": (-126, 23, 127), "f16": (-14, 10, 15), "bf16": (-126, 7, 127)}[dt]
+    xs = list(rng.standard_normal(3000) * np.exp2(rng.integers(emin - mb - 2, emax + 2, 3000)))
+    # exact midpoints between neighbours (ties) and values just off them
+    for _ in range(1500):
+        e = int(rng.integers(emin - 1, emax))
+        m = int(rng.integers(0, 2 ** mb))
+        q = max(e, emin) - mb
+        mid = (2 ** mb + m + 0.5) * 2.0 ** q if e >= emin else (m + 0.5) * 2.0 ** q
+        xs += [mid, -mid, math.nextafter(mid, 0), math.nextafter(mid, math.inf)]
+    top = (2.0 - 2.0 ** -mb) * 2.0 ** emax
+    xs += [top, top * (1 + 2.0 ** -(mb + 2)), top * (1 + 2.0 ** -(mb + 1)), 2.0 ** (emin - mb - 1),
+           2.0 ** (emin - mb - 1) * 1.5, 2.0 ** (emin - mb), 0.0, -0.0, math.inf, -math.inf, 1e300, -1e-300]
+    return np.array(xs, dtype=np.float64)
+
+
+def pin_encode_library(o):
+    """Round-to-nearest-even into each format agrees with numpy (binary64 to
+    float32 / float16) and with torch (float32 to bfloat16), including ties,
+    subnormals, overflow, signed zero, infinities and NaN."""
+    import torch
+    rng = np.random.default_rng(17)
+    for dt in ("f32", "f16"):
+        xs = _encode_cases(rng, dt)
+        with np.errstate(over="ignore"):
+            ref = raw_bits(lib_round(xs, dt), dt).astype(np.int64)
+        got = np.array([o.encode(float(x), dt) for x in xs], dtype=np.int64)
+        assert np.array_equal(got, ref), (dt, xs[got != ref][:5], got[got != ref][:5], ref[got != ref][:5])
+    with np.errstate(over="ignore"):
+        xs = _encode_cases(rng, "bf16").astype(np.float32)  # float32 inputs: torch rounds float32 -> bf16 once
+    xs = xs[np.isfinite(xs) | np.isinf(xs)]
+    ref = torch.from_numpy(xs).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).astype(np.int64)
+    got = np.array([o.encode(float(x), "bf16") for x in xs], dtype=np.int64)
+    assert np.array_equal(got, ref), (xs[got != ref][:5], got[got != ref][:5], ref[got != ref][:5])
+    for dt in DTYPES:
+        nan_bits = o.encode(float("nan"), dt)
+        assert math.isnan(struct_value(nan_bits, dt))
+
+
+def pin_nonfinite(o):
+    """A NaN or +-Inf anywhere sets the flag; with error_if_nonfinite the
+    update is stopped (glossary page: nothing is written); without it plain
+    IEEE arithmetic decides: NaN > c is false (nothing clipped), an infinite
+    norm gives the factor c/Inf = 0."""
+    rng = np.random.default_rng(18)
+    for dt in DTYPES:
+        for where in ("first", "middle", "last"):
+            for bad in (math.nan, math.inf, -math.inf):
+                arrs = [store(rng.standard_normal(5), dt), store(rng.standard_normal(7), dt)]
+                t, i = {"first": (0, 0), "middle": (1, 3), "last": (1, 6)}[where]
+                arrs[t][i] = store([bad], dt)[0]
+                before = [x.copy() for x in arrs]
+                r = o.clip_(arrs, dt, 1.0, 1.0, True)
+                assert r["nonfinite"] and r["skipped"], (dt, where, bad, r)
+                for x, y in zip(arrs, before):
+                    assert np.array_equal(raw_bits(x, dt), raw_bits(y, dt))
+                arrs = [y.copy() for y in before]
+                r = o.clip_(arrs, dt, 1.0, 1.0, False)
+                assert r["nonfinite"] and not r["skipped"]
+                if math.isnan(bad):
+                    assert math.isnan(r["norm"]) and not r["clipped"] and r["scale"] == 1.0
+                    for x, y in zip(arrs, before):
+                        assert np.array_equal(raw_bits(x, dt), raw_bits(y, dt))
+                else:
+                    assert r["norm"] == math.inf and r["clipped"] and r["scale"] == 0.0
+                    for x, y in zip(arrs, before):
+                        vx, vy = values(x, dt), values(y, dt)
+                        fin = np.isfinite(vy)
+                        assert np.all(vx[fin] == 0.0) and np.array_equal(np.signbit(vx[fin]), np.signbit(vy[fin]))
+                        assert np.all(np.isnan(vx[~fin]))
+    # all finite: flag clear
+    r = o.clip_([store([1e30, -1e30], "f32")], "f32", 1.0)
+    assert not r["nonfinite"]
+
+
+def pin_avg_factor(o):
+    """Averaging by 1/n_microbatches precedes the norm (backprop lesson,
+    'Accumulation across microbatches'; glossary page, 'Order changes the
+    result'): the norm of a*g is a times the norm of g, and with a = 1/4 the
+    fused factor equals averaging first, then clipping, bit for bit."""
+    rng = np.random.default_rng(19)
+    for dt in DTYPES:
+        arrs = [store(rng.standard_normal(n) * 0.3, dt) for n in (100, 7, 33)]
+        s1, _ = o.sumsq(arrs, dt, 1.0)
+        s4, _ = o.sumsq(arrs, dt, 0.25)
+        assert s4 == s1 / 16.0
+        s3, _ = o.sumsq(arrs, dt, 1.0 / 3.0)
+        assert abs(s3 - s1 / 9.0) <= 1e-14 * s1
+        fused = [x.copy() for x in arrs]
+        r = o.clip_(fused, dt, 0.5, 0.25)
+        assert r["clipped"] and abs(r["norm"] - math.sqrt(s1) / 4.0) <= 1e-15 * r["norm"]
+        twostep = [x.copy() for x in arrs]
+        o.scale_(twostep, dt, 0.25)
+        r2 = o.clip_(twostep, dt, 0.5, 1.0)
+        for x, y in zip(fused, twostep):
+            assert np.array_equal(raw_bits(x, dt), raw_bits(y, dt)), dt
+        # averaging without a clip still writes a*g
+        arrs2 = [x.copy() for x in arrs]
+        r3 = o.clip_(arrs2, dt, 1e6, 0.25)
+        assert not r3["clipped"] and r3["scale"] == 0.25
+        for x, y in zip(arrs2, arrs):
+            assert np.array_equal(values(x, dt), values(y, dt) * 0.25)
+
+
+def pin_scale_invariance(o):
+    """norm(2^k g) == 2^k norm(g) exactly (power-of-two scaling is exact away
+    from overflow and underflow)."""
+    rng = np.random.default_rng(20)
+    for dt in DTYPES:
+        v = rng.standard_normal(300)
+        base = [store(v, dt)]
+        s0, _ = o.sumsq(base, dt)
+        for k in (-3, 2, 5):
+            sk, _ = o.sumsq([store(values(base[0], dt) * 2.0 ** k, dt)], dt)
+            assert sk == s0 * 4.0 ** k, (dt, k)
+
+
+def pin_empty_and_zero_size(o):
+    """An empty list has norm 0 and writes nothing; zero-size tensors add nothing."""
+    r = o.clip_([], "f32", 1.0)
+    assert r["norm"] == 0.0 and not r["clipped"] and not r["nonfinite"]
+    rng = np.random.default_rng(21)
+    for dt in DTYPES:
+        a = store(rng.standard_normal(40) * 2, dt)
+        z = store([], dt)
+        r1 = o.clip_([a.copy()], dt, 1.0)
+        arrs = [z.copy(), a.copy(), z.copy()]
+        r2 = o.clip_(arrs, dt, 1.0)
+        assert r1["sumsq"] == r2["sumsq"] and r1["scale"] == r2["scale"]
+
+
+def pin_infinite_threshold(o):
+    """max_norm = +inf never clips."""
+    a = [store([1e30, 3.0], "f32")]
+    r = o.clip_(a, "f32", math.inf)
+    assert not r["clipped"] and r["scale"] == 1.0
+
+
+ALL_PINS = [pin_worked_6_8, pin_not_per_coordinate, pin_sgd_step_length, pin_accumulate_then_clip,
+            pin_tie_passes_unchanged, pin_below_threshold_bitwise, pin_post_clip_norm, pin_single_global_factor,
+            pin_joint_norm_library, pin_bruteforce_exact, pin_decode_library, pin_encode_library, pin_nonfinite,
+            pin_avg_factor, pin_scale_invariance, pin_empty_and_zero_size, pin_infinite_threshold]
