@@ -1,0 +1,228 @@
+"""global_l2_norm_amd -- global L2-norm gradient clipping on MI355X.
+
+A thin Python face of libgclip (include/gclip.h).  The functions named like
+the C ABI take raw device addresses; ``GradList`` wraps a list of torch
+tensors (torch is used here only for device memory and streams).
+
+The path (grad clip lesson, unhomeschool.com ru, section "Math"): the norm is
+the square root of the sum of g^2 over every element of every tensor; only
+if it exceeds max_norm is every element multiplied by max_norm / norm.  The
+averaging factor a (backprop lesson, unhomeschool.com vi, "Accumulation
+across microbatches") multiplies g before its norm is taken, and the
+error-if-nonfinite switch (glossary page, paweldubiel.com, "Mechanism and
+details") stops the update when a NaN or Inf is present.
+"""
+import ctypes
+
+from . import _lib
+from ._lib import (GCLIP_BF16, GCLIP_F16, GCLIP_F32, GCLIP_PATH_AUTO, GCLIP_PATH_FUSED, GCLIP_PATH_SPLIT,
+                   GclipListInfo, GclipPlanEntry, GclipResult)
+
+__all__ = ["GclipError", "GclipResult", "GradList", "clip_grad_norm_", "gclip_list_create", "gclip_list_destroy",
+           "gclip_list_info", "gclip_list_set_path", "gclip_norm", "gclip_scale", "gclip_clip_",
+           "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string", "gclip_version",
+           "GCLIP_F32", "GCLIP_F16", "GCLIP_BF16", "GCLIP_PATH_AUTO", "GCLIP_PATH_FUSED", "GCLIP_PATH_SPLIT"]
+
+DTYPE_CODES = {"f32": GCLIP_F32, "f16": GCLIP_F16, "bf16": GCLIP_BF16}
+
+
+class GclipError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = f"{where}: {_lib.STATUS_NAMES.get(status, status)} ({_lib.lib.gclip_status_string(status).decode()})"
+        if status == _lib.GCLIP_EHIP:
+            msg += f", hipError {_lib.lib.gclip_last_hip_error()}"
+        super().__init__(msg)
+
+
+def _check(status, where):
+    if status != _lib.GCLIP_OK:
+        raise GclipError(status, where)
+
+
+# ---------------------------------------------------------------- C ABI names
+def gclip_list_create(d_ptrs, numels, dtype):
+    """Handle (int) of a new list; d_ptrs are device addresses, numels sizes."""
+    n = len(d_ptrs)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*d_ptrs)
+    sizes = (ctypes.c_int64 * max(n, 1))(*numels)
+    out = ctypes.c_void_p()
+    _check(_lib.lib.gclip_list_create(ptrs, sizes, n, int(dtype), ctypes.byref(out)), "gclip_list_create")
+    return out.value
+
+
+def gclip_list_destroy(handle):
+    _check(_lib.lib.gclip_list_destroy(handle), "gclip_list_destroy")
+
+
+def gclip_list_info(handle):
+    info = GclipListInfo()
+    _check(_lib.lib.gclip_list_info(handle, ctypes.byref(info)), "gclip_list_info")
+    return info.as_dict()
+
+
+def gclip_list_set_path(handle, path):
+    _check(_lib.lib.gclip_list_set_path(handle, int(path)), "gclip_list_set_path")
+
+
+def gclip_norm(handle, avg_factor, d_result, stream):
+    _check(_lib.lib.gclip_norm(handle, float(avg_factor), d_result, stream), "gclip_norm")
+
+
+def gclip_scale(handle, max_norm, avg_factor, error_if_nonfinite, d_result, stream):
+    _check(_lib.lib.gclip_scale(handle, float(max_norm), float(avg_factor), int(bool(error_if_nonfinite)),
+                                d_result, stream), "gclip_scale")
+
+
+def gclip_clip_(handle, max_norm, avg_factor, error_if_nonfinite, d_result, stream):
+    _check(_lib.lib.gclip_clip_(handle, float(max_norm), float(avg_factor), int(bool(error_if_nonfinite)),
+                                d_result, stream), "gclip_clip_")
+
+
+def gclip_result_read(d_result, stream, error_if_nonfinite=False):
+    """(status, dict) after the stream's queued work has finished."""
+    r = GclipResult()
+    st = _lib.lib.gclip_result_read(d_result, stream, ctypes.byref(r), int(bool(error_if_nonfinite)))
+    if st not in (_lib.GCLIP_OK, _lib.GCLIP_ENONFINITE, _lib.GCLIP_EDEVICE):
+        raise GclipError(st, "gclip_result_read")
+    return st, r.as_dict()
+
+
+def gclip_plan_query(addrs, numels, dtype, n_workers, worker_threads):
+    """List of (worker, tensor, elem_begin, elem_count, kind) runs; no GPU involved."""
+    n = len(addrs)
+    a = (ctypes.c_uint64 * max(n, 1))(*addrs)
+    s = (ctypes.c_int64 * max(n, 1))(*numels)
+    need = ctypes.c_int64()
+    st = _lib.lib.gclip_plan_query(a, s, n, int(dtype), int(n_workers), int(worker_threads), None, 0,
+                                   ctypes.byref(need))
+    if st not in (_lib.GCLIP_OK, _lib.GCLIP_ERANGE):
+        raise GclipError(st, "gclip_plan_query")
+    cap = need.value
+    buf = (GclipPlanEntry * max(cap, 1))()
+    _check(_lib.lib.gclip_plan_query(a, s, n, int(dtype), int(n_workers), int(worker_threads), buf, cap,
+                                     ctypes.byref(need)), "gclip_plan_query")
+    return [(e.worker, e.tensor, e.elem_begin, e.elem_count, e.kind) for e in buf[:need.value]]
+
+
+def gclip_plan_trace(addrs, numels, dtype, n_workers, mode):
+    """(addresses, workers) numpy arrays of every lane access a kernel would
+    make (mode 0 norm, 1 scale, 2/3 fused first/second pass); no GPU involved."""
+    import numpy as np
+    n = len(addrs)
+    a = (ctypes.c_uint64 * max(n, 1))(*addrs)
+    s = (ctypes.c_int64 * max(n, 1))(*numels)
+    need = ctypes.c_int64()
+    st = _lib.lib.gclip_plan_trace(a, s, n, int(dtype), int(n_workers), int(mode), None, None, 0, ctypes.byref(need))
+    if st not in (_lib.GCLIP_OK, _lib.GCLIP_ERANGE):
+        raise GclipError(st, "gclip_plan_trace")
+    cap = need.value
+    out_a = np.zeros(max(cap, 1), dtype=np.uint64)
+    out_w = np.zeros(max(cap, 1), dtype=np.int32)
+    _check(_lib.lib.gclip_plan_trace(a, s, n, int(dtype), int(n_workers), int(mode),
+                                     out_a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                     out_w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), cap, ctypes.byref(need)),
+           "gclip_plan_trace")
+    return out_a[:cap], out_w[:cap]
+
+
+def gclip_status_string(status):
+    return _lib.lib.gclip_status_string(int(status)).decode()
+
+
+def gclip_version():
+    return _lib.lib.gclip_version()
+
+
+# ---------------------------------------------------------------- torch-facing wrapper
+def _torch_dtype_code(t):
+    import torch
+    m = {torch.float32: GCLIP_F32, torch.float16: GCLIP_F16, torch.bfloat16: GCLIP_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported gradient dtype {t.dtype}")
+    return m[t.dtype]
+
+
+class GradList:
+    """A fixed list of same-dtype, contiguous gradient tensors on one GPU.
+
+    The descriptor table and a 64-byte device result block are allocated once
+    here; norm / scale / clip_ only enqueue kernels on the given (default:
+    current) stream and allocate nothing.  The tensors are referenced so that
+    their storage cannot be freed while the list exists.
+    """
+
+    def __init__(self, tensors):
+        import torch
+        tensors = list(tensors)
+        if not torch.cuda.is_available():
+            raise RuntimeError("GradList needs a GPU")
+        codes = {_torch_dtype_code(t) for t in tensors}
+        if len(codes) > 1:
+            raise TypeError("all tensors of a list must share one dtype")
+        for t in tensors:
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("tensors must be contiguous device tensors")
+        self.tensors = tensors
+        self.dtype = codes.pop() if codes else GCLIP_F32
+        self.device = tensors[0].device if tensors else torch.device("cuda", torch.cuda.current_device())
+        with torch.cuda.device(self.device):
+            self.result = torch.zeros(64, dtype=torch.uint8, device=self.device)
+            self.handle = gclip_list_create([t.data_ptr() for t in tensors], [t.numel() for t in tensors],
+                                            self.dtype)
+
+    @staticmethod
+    def _stream(stream):
+        import torch
+        s = torch.cuda.current_stream() if stream is None else stream
+        return s.cuda_stream
+
+    @property
+    def d_result(self):
+        return self.result.data_ptr()
+
+    def info(self):
+        return gclip_list_info(self.handle)
+
+    def set_path(self, path):
+        gclip_list_set_path(self.handle, path)
+
+    def norm(self, avg_factor=1.0, stream=None):
+        gclip_norm(self.handle, avg_factor, self.d_result, self._stream(stream))
+
+    def scale(self, max_norm, avg_factor=1.0, error_if_nonfinite=False, stream=None):
+        gclip_scale(self.handle, max_norm, avg_factor, error_if_nonfinite, self.d_result, self._stream(stream))
+
+    def clip_(self, max_norm, avg_factor=1.0, error_if_nonfinite=False, stream=None):
+        gclip_clip_(self.handle, max_norm, avg_factor, error_if_nonfinite, self.d_result, self._stream(stream))
+
+    def read(self, error_if_nonfinite=False, stream=None):
+        """Wait for the stream and return (status, result dict)."""
+        return gclip_result_read(self.d_result, self._stream(stream), error_if_nonfinite)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            gclip_list_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def clip_grad_norm_(tensors, max_norm, avg_factor=1.0, error_if_nonfinite=False, grad_list=None):
+    """Clip a list of gradient tensors in place by their global L2 norm and
+    return the pre-clip norm (of avg_factor * g).  Raises GclipError when
+    error_if_nonfinite is set and a NaN/Inf element was found (nothing is
+    written then).  Pass a persistent ``grad_list`` to avoid rebuilding the
+    descriptor table on every call."""
+    gl = grad_list if grad_list is not None else GradList(tensors)
+    gl.clip_(max_norm, avg_factor, error_if_nonfinite)
+    st, r = gl.read(error_if_nonfinite)
+    if grad_list is None:
+        gl.close()
+    if st != _lib.GCLIP_OK:
+        raise GclipError(st, "clip_grad_norm_")
+    return r["norm"]

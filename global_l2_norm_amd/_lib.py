@@ -1,0 +1,90 @@
+"""ctypes declarations of libgclip's C ABI (include/gclip.h).
+
+Marshalling only: every step of the clipping path runs in the HIP kernels of
+libgclip.so.  Importing this module fails loudly when the library has not
+been built -- there is no fallback.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgclip.so")
+
+GCLIP_F32, GCLIP_F16, GCLIP_BF16 = 0, 1, 2
+GCLIP_OK, GCLIP_EINVAL, GCLIP_EDTYPE, GCLIP_ENOMEM, GCLIP_EHIP, GCLIP_ENONFINITE, GCLIP_EDEVICE, GCLIP_ERANGE = range(8)
+GCLIP_PATH_AUTO, GCLIP_PATH_FUSED, GCLIP_PATH_SPLIT = 0, 1, 2
+
+STATUS_NAMES = {GCLIP_OK: "GCLIP_OK", GCLIP_EINVAL: "GCLIP_EINVAL", GCLIP_EDTYPE: "GCLIP_EDTYPE",
+                GCLIP_ENOMEM: "GCLIP_ENOMEM", GCLIP_EHIP: "GCLIP_EHIP", GCLIP_ENONFINITE: "GCLIP_ENONFINITE",
+                GCLIP_EDEVICE: "GCLIP_EDEVICE", GCLIP_ERANGE: "GCLIP_ERANGE"}
+
+
+class GclipResult(ctypes.Structure):
+    _fields_ = [("sumsq", ctypes.c_double), ("norm", ctypes.c_double), ("scale", ctypes.c_double),
+                ("max_norm", ctypes.c_double), ("nonfinite", ctypes.c_int32), ("clipped", ctypes.c_int32),
+                ("skipped", ctypes.c_int32), ("decided", ctypes.c_int32), ("status", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
+
+    def as_dict(self):
+        return {"sumsq": self.sumsq, "norm": self.norm, "scale": self.scale, "max_norm": self.max_norm,
+                "nonfinite": bool(self.nonfinite), "clipped": bool(self.clipped), "skipped": bool(self.skipped),
+                "decided": bool(self.decided), "status": int(self.status)}
+
+
+class GclipListInfo(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int64), ("n_elements", ctypes.c_int64), ("n_bytes", ctypes.c_int64),
+                ("n_segments", ctypes.c_int64), ("n_vectors", ctypes.c_int64), ("n_scalars", ctypes.c_int64),
+                ("n_workers", ctypes.c_int32), ("worker_threads", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("path", ctypes.c_int32), ("resident_vectors", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class GclipPlanEntry(ctypes.Structure):
+    _fields_ = [("worker", ctypes.c_int32), ("tensor", ctypes.c_int32), ("elem_begin", ctypes.c_int64),
+                ("elem_count", ctypes.c_int64), ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+assert ctypes.sizeof(GclipResult) == 64
+
+
+def _declare(lib):
+    vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    sig = {
+        "gclip_list_create": ([ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32, ctypes.POINTER(vp)], i32),
+        "gclip_list_destroy": ([vp], i32),
+        "gclip_list_info": ([vp, ctypes.POINTER(GclipListInfo)], i32),
+        "gclip_list_set_path": ([vp, i32], i32),
+        "gclip_norm": ([vp, dbl, vp, vp], i32),
+        "gclip_scale": ([vp, dbl, dbl, i32, vp, vp], i32),
+        "gclip_clip_": ([vp, dbl, dbl, i32, vp, vp], i32),
+        "gclip_result_read": ([vp, vp, ctypes.POINTER(GclipResult), i32], i32),
+        "gclip_plan_query": ([ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(i64), i32, i32, i32, i32,
+                              ctypes.POINTER(GclipPlanEntry), i64, ctypes.POINTER(i64)], i32),
+        "gclip_plan_trace": ([ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(i64), i32, i32, i32, i32,
+                              ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(i32), i64, ctypes.POINTER(i64)], i32),
+        "gclip_status_string": ([i32], ctypes.c_char_p),
+        "gclip_last_hip_error": ([], i32),
+        "gclip_version": ([], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+def load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m global_l2_norm_amd.build` "
+                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    return _declare(ctypes.CDLL(LIB_PATH))
+
+
+lib = load()
+
+# The C ABI's declared entry points (include/gclip.h), for the export check.
+EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_list_set_path", "gclip_norm",
+           "gclip_scale", "gclip_clip_", "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string",
+           "gclip_last_hip_error", "gclip_version")

@@ -1,0 +1,319 @@
+// gclip_api.cpp -- the C ABI of libgclip (declared in include/gclip.h):
+// argument checking, the one-time allocation of a list's descriptor table
+// and workspace, and dispatch of the kernels in gclip_kernels.hip.
+//
+// As on the backprop lesson page (unhomeschool.com vi, section "Cost of
+// general frameworks"), dispatch happens at the C level and every buffer is
+// allocated once at start-up: only gclip_list_create / gclip_list_destroy
+// allocate or synchronise; the hot calls only enqueue kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/gclip.h"
+#include "gclip_plan.hpp"
+
+namespace gclip {
+int worker_threads();
+int64_t fused_resident_vectors_per_worker();
+hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result* res, hipStream_t st);
+hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
+                        hipStream_t st);
+hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
+                        uint32_t epoch, hipStream_t st);
+hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu);
+}  // namespace gclip
+
+struct gclip_list {
+  gclip::HostPlan plan;
+  gclip::DevPlan dev{};
+  void* blob = nullptr;
+  int device = 0;
+  bool fused_ok = false;
+  int32_t path = GCLIP_PATH_SPLIT;
+  uint32_t epoch = 0;
+};
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+gclip_status hip_fail(hipError_t e) {
+  g_last_hip = (int32_t)e;
+  return GCLIP_EHIP;
+}
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool factor_ok(double a) { return std::isfinite(a) && a > 0.0; }
+bool threshold_ok(double c) { return !std::isnan(c) && c > 0.0; }
+bool result_ptr_ok(const gclip_result* r) { return r && reinterpret_cast<uintptr_t>(r) % 8 == 0; }
+
+// Device check of a hot call (argument values are checked before this).
+gclip_status check_device(const gclip_list* list) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev != list->device) return GCLIP_EINVAL;
+  return GCLIP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gclip_version(void) { return GCLIP_VERSION; }
+
+int32_t gclip_last_hip_error(void) { return g_last_hip; }
+
+const char* gclip_status_string(int32_t status) {
+  switch (status) {
+    case GCLIP_OK: return "ok";
+    case GCLIP_EINVAL: return "invalid argument";
+    case GCLIP_EDTYPE: return "unknown dtype";
+    case GCLIP_ENOMEM: return "device allocation failed";
+    case GCLIP_EHIP: return "HIP runtime error";
+    case GCLIP_ENONFINITE: return "non-finite gradient element";
+    case GCLIP_EDEVICE: return "device-side failure";
+    case GCLIP_ERANGE: return "output buffer too small";
+    default: return "unknown status";
+  }
+}
+
+gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int32_t n_tensors, int32_t dtype,
+                              int32_t n_workers, int32_t worker_threads, gclip_plan_entry* out, int64_t cap,
+                              int64_t* n_out) {
+  if (!n_out || cap < 0 || (cap > 0 && !out)) return GCLIP_EINVAL;
+  try {
+    gclip::HostPlan p;
+    const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, n_workers, worker_threads, p, nullptr);
+    if (rc != 0) return (gclip_status)rc;
+    int64_t k = 0;
+    auto emit = [&](int32_t w, int32_t t, int64_t b, int64_t c, int32_t kind) {
+      if (k < cap) out[k] = gclip_plan_entry{w, t, b, c, kind, 0};
+      ++k;
+    };
+    for (int32_t w = 0; w < n_workers; ++w) {
+      const uint64_t vb = p.wk_vbegin[(size_t)w], ve = p.wk_vbegin[(size_t)w + 1];
+      for (int64_t s = p.wk_seg[(size_t)w]; vb < ve && s < p.nseg(); ++s) {
+        const uint64_t sb = p.seg_vbegin[(size_t)s], se = p.seg_vbegin[(size_t)s + 1];
+        if (sb >= ve) break;
+        const uint64_t lo = vb > sb ? vb : sb, hi = ve < se ? ve : se;
+        if (lo >= hi) continue;
+        emit(w, p.seg_tensor[(size_t)s], p.seg_elem0[(size_t)s] + (int64_t)(lo - sb) * p.vec_elems,
+             (int64_t)(hi - lo) * p.vec_elems, 0);
+      }
+      const uint64_t cb = p.wk_scbegin[(size_t)w], ce = p.wk_scbegin[(size_t)w + 1];
+      for (uint64_t i = cb; i < ce;) {
+        uint64_t j = i + 1;
+        while (j < ce && p.sc_tensor[j] == p.sc_tensor[i] && p.sc_elem[j] == p.sc_elem[j - 1] + 1) ++j;
+        emit(w, p.sc_tensor[i], p.sc_elem[i], (int64_t)(j - i), 1);
+        i = j;
+      }
+    }
+    *n_out = k;
+    return k > cap ? GCLIP_ERANGE : GCLIP_OK;
+  } catch (const std::bad_alloc&) {
+    return GCLIP_ENOMEM;
+  }
+}
+
+gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32_t n_tensors, int32_t dtype,
+                               gclip_list** out) {
+  if (!out) return GCLIP_EINVAL;
+  *out = nullptr;
+  if (!gclip::dtype_valid(dtype)) return GCLIP_EDTYPE;
+  if (n_tensors < 0 || (n_tensors > 0 && (!d_ptrs || !numels))) return GCLIP_EINVAL;
+  static_assert(sizeof(uint64_t) == sizeof(void*), "64-bit addresses");
+  gclip_list* L = nullptr;
+  try {
+    {
+      // every argument error is reported before any HIP call
+      const int rc = gclip::plan_validate(reinterpret_cast<const uint64_t*>(d_ptrs), numels, n_tensors, dtype,
+                                          nullptr, nullptr, nullptr);
+      if (rc != 0) return (gclip_status)rc;
+    }
+    L = new gclip_list();
+    hipError_t e = hipGetDevice(&L->device);
+    if (e != hipSuccess) {
+      delete L;
+      return hip_fail(e);
+    }
+    int ncu = 0, coop = 0;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, L->device)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, L->device)) != hipSuccess) {
+      delete L;
+      return hip_fail(e);
+    }
+    int bpc = 0;
+    if ((e = gclip::fused_capacity(dtype, &bpc)) != hipSuccess) {
+      delete L;
+      return hip_fail(e);
+    }
+    L->fused_ok = coop != 0 && bpc >= 1;
+    L->path = L->fused_ok ? GCLIP_PATH_FUSED : GCLIP_PATH_SPLIT;
+
+    const uint64_t* addrs = reinterpret_cast<const uint64_t*>(d_ptrs);
+    std::string why;
+    const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, ncu, gclip::worker_threads(), L->plan, &why);
+    if (rc != 0) {
+      delete L;
+      return (gclip_status)rc;
+    }
+    const gclip::HostPlan& P = L->plan;
+    const size_t nseg = (size_t)P.nseg(), nw = (size_t)P.nworkers, nsc = (size_t)P.nsc();
+    const size_t A = 256;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+      const size_t at = off;
+      off = round_up(off + (bytes ? bytes : 8), A);
+      return at;
+    };
+    const size_t o_segv = take((nseg + 1) * 8), o_sega = take(nseg * 8), o_wkv = take((nw + 1) * 8),
+                 o_wks = take(nw * 4), o_wksc = take((nw + 1) * 8), o_sca = take(nsc * 8), o_part = take(nw * 8),
+                 o_bc = take(8), o_sync = take(8 * 4);
+    if ((e = hipMalloc(&L->blob, off)) != hipSuccess) {
+      delete L;
+      g_last_hip = (int32_t)e;
+      return GCLIP_ENOMEM;
+    }
+    char* b = static_cast<char*>(L->blob);
+    auto up = [&](size_t o, const void* src, size_t bytes) -> hipError_t {
+      if (bytes == 0) return hipSuccess;
+      return hipMemcpy(b + o, src, bytes, hipMemcpyHostToDevice);
+    };
+    if ((e = hipMemset(L->blob, 0, off)) != hipSuccess || (e = up(o_segv, P.seg_vbegin.data(), (nseg + 1) * 8)) ||
+        (e = up(o_sega, P.seg_addr.data(), nseg * 8)) || (e = up(o_wkv, P.wk_vbegin.data(), (nw + 1) * 8)) ||
+        (e = up(o_wks, P.wk_seg.data(), nw * 4)) || (e = up(o_wksc, P.wk_scbegin.data(), (nw + 1) * 8)) ||
+        (e = up(o_sca, P.sc_addr.data(), nsc * 8)) || (e = hipDeviceSynchronize()) != hipSuccess) {
+      (void)hipFree(L->blob);
+      delete L;
+      return hip_fail(e);
+    }
+    gclip::DevPlan& D = L->dev;
+    D.seg_vbegin = reinterpret_cast<const uint64_t*>(b + o_segv);
+    D.seg_addr = reinterpret_cast<const uint64_t*>(b + o_sega);
+    D.wk_vbegin = reinterpret_cast<const uint64_t*>(b + o_wkv);
+    D.wk_seg = reinterpret_cast<const uint32_t*>(b + o_wks);
+    D.wk_scbegin = reinterpret_cast<const uint64_t*>(b + o_wksc);
+    D.sc_addr = reinterpret_cast<const uint64_t*>(b + o_sca);
+    D.partials = reinterpret_cast<double*>(b + o_part);
+    D.bcast = reinterpret_cast<double*>(b + o_bc);
+    D.sync = reinterpret_cast<uint32_t*>(b + o_sync);
+    D.nworkers = P.nworkers;
+    D.nseg = (int32_t)nseg;
+    *out = L;
+    return GCLIP_OK;
+  } catch (const std::bad_alloc&) {
+    if (L) {
+      if (L->blob) (void)hipFree(L->blob);
+      delete L;
+    }
+    return GCLIP_ENOMEM;
+  }
+}
+
+gclip_status gclip_list_destroy(gclip_list* list) {
+  if (!list) return GCLIP_OK;
+  hipError_t e = hipSuccess;
+  if (list->blob) e = hipFree(list->blob);
+  delete list;
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_list_info(const gclip_list* list, gclip_list_info_t* out) {
+  if (!list || !out) return GCLIP_EINVAL;
+  const gclip::HostPlan& P = list->plan;
+  std::memset(out, 0, sizeof(*out));
+  out->n_tensors = P.n_tensors;
+  out->n_elements = P.n_elements;
+  out->n_bytes = P.n_bytes;
+  out->n_segments = P.nseg();
+  out->n_vectors = (int64_t)P.nvec();
+  out->n_scalars = (int64_t)P.nsc();
+  out->n_workers = P.nworkers;
+  out->worker_threads = P.threads;
+  out->dtype = P.dtype;
+  out->path = list->path;
+  int64_t res = 0;
+  if (list->path == GCLIP_PATH_FUSED) {
+    const int64_t cap = gclip::fused_resident_vectors_per_worker();
+    for (int32_t w = 0; w < P.nworkers; ++w) {
+      const int64_t n = (int64_t)(P.wk_vbegin[(size_t)w + 1] - P.wk_vbegin[(size_t)w]);
+      const int64_t steps = (n + P.threads - 1) / P.threads;
+      const int64_t rsteps = steps < cap / P.threads ? steps : cap / P.threads;
+      // resident steps are the last ones; the share's final step may be partial
+      res += rsteps == 0 ? 0 : n - (steps - rsteps) * P.threads;
+    }
+  }
+  out->resident_vectors = res;
+  return GCLIP_OK;
+}
+
+gclip_status gclip_list_set_path(gclip_list* list, int32_t path) {
+  if (!list) return GCLIP_EINVAL;
+  switch (path) {
+    case GCLIP_PATH_AUTO: list->path = list->fused_ok ? GCLIP_PATH_FUSED : GCLIP_PATH_SPLIT; return GCLIP_OK;
+    case GCLIP_PATH_FUSED:
+      if (!list->fused_ok) return GCLIP_EINVAL;
+      list->path = GCLIP_PATH_FUSED;
+      return GCLIP_OK;
+    case GCLIP_PATH_SPLIT: list->path = GCLIP_PATH_SPLIT; return GCLIP_OK;
+    default: return GCLIP_EINVAL;
+  }
+}
+
+gclip_status gclip_norm(gclip_list* list, double avg_factor, gclip_result* d_result, void* stream) {
+  if (!list || !result_ptr_ok(d_result) || !factor_ok(avg_factor)) return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
+  const hipError_t e =
+      gclip::launch_norm(list->dev, list->plan.dtype, avg_factor, d_result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_scale(gclip_list* list, double max_norm, double avg_factor, int32_t error_if_nonfinite,
+                         gclip_result* d_result, void* stream) {
+  if (!list || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(avg_factor)) return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
+  const hipError_t e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg_factor,
+                                           error_if_nonfinite ? 1 : 0, d_result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_clip_(gclip_list* list, double max_norm, double avg_factor, int32_t error_if_nonfinite,
+                         gclip_result* d_result, void* stream) {
+  if (!list || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(avg_factor)) return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int err = error_if_nonfinite ? 1 : 0;
+  hipError_t e;
+  if (list->path == GCLIP_PATH_FUSED) {
+    if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
+    e = gclip::launch_fused(list->dev, list->plan.dtype, max_norm, avg_factor, err, d_result, list->epoch, s);
+  } else {
+    e = gclip::launch_norm(list->dev, list->plan.dtype, avg_factor, d_result, s);
+    if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg_factor, err, d_result, s);
+  }
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_result_read(const gclip_result* d_result, void* stream, gclip_result* h_out,
+                               int32_t error_if_nonfinite) {
+  if (!d_result || !h_out) return GCLIP_EINVAL;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(h_out, d_result, sizeof(gclip_result), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (h_out->status != 0) return GCLIP_EDEVICE;
+  if (h_out->nonfinite && error_if_nonfinite) return GCLIP_ENONFINITE;
+  return GCLIP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// gclip_plan.cpp -- host construction of a gradient list's descriptor table.
+// Pure C++: no HIP call, so it can be exercised without a GPU.
+#include "gclip_plan.hpp"
+
+#include <algorithm>
+#include <utility>
+
+namespace gclip {
+
+namespace {
+
+// Balanced split of [0, total) into n parts: part w starts at w*q + min(w, r).
+uint64_t share_begin(uint64_t total, int32_t n, int32_t w) {
+  const uint64_t q = total / (uint64_t)n, r = total % (uint64_t)n;
+  return (uint64_t)w * q + std::min<uint64_t>((uint64_t)w, r);
+}
+
+}  // namespace
+
+int plan_validate(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, std::string* why,
+                  int64_t* n_elements, int64_t* n_bytes) {
+  auto fail = [&](int code, const char* msg) {
+    if (why) *why = msg;
+    return code;
+  };
+  if (!dtype_valid(dtype)) return fail(2, "unknown dtype");
+  if (n < 0) return fail(1, "negative tensor count");
+  if (n > 0 && (!addrs || !numels)) return fail(1, "NULL address or size array");
+  const int esize = dtype_bytes(dtype);
+  std::vector<std::pair<uint64_t, uint64_t>> ranges;
+  ranges.reserve((size_t)n);
+  const uint64_t kMaxElems = (uint64_t)1 << 56;
+  int64_t ne_total = 0, nb_total = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    if (numels[t] < 0) return fail(1, "negative element count");
+    if (numels[t] == 0) continue;
+    if ((uint64_t)numels[t] > kMaxElems) return fail(1, "tensor too large");
+    if (addrs[t] == 0) return fail(1, "NULL tensor address");
+    if (addrs[t] % (uint64_t)esize != 0) return fail(1, "tensor address not aligned to its element size");
+    const uint64_t bytes = (uint64_t)numels[t] * (uint64_t)esize;
+    if (addrs[t] + bytes < addrs[t]) return fail(1, "tensor range wraps the address space");
+    ranges.emplace_back(addrs[t], addrs[t] + bytes);
+    ne_total += numels[t];
+    nb_total += (int64_t)bytes;
+  }
+  std::sort(ranges.begin(), ranges.end());
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].first < ranges[i - 1].second) return fail(1, "tensors overlap or repeat");
+  if (n_elements) *n_elements = ne_total;
+  if (n_bytes) *n_bytes = nb_total;
+  return 0;
+}
+
+int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
+               int32_t threads, HostPlan& out, std::string* why) {
+  const int rc = plan_validate(addrs, numels, n, dtype, why, nullptr, nullptr);
+  if (rc != 0) return rc;
+  if (nworkers <= 0 || threads <= 0) {
+    if (why) *why = "non-positive launch shape";
+    return 1;
+  }
+  HostPlan p;
+  p.dtype = dtype;
+  p.esize = dtype_bytes(dtype);
+  p.vec_elems = kVecBytes / p.esize;
+  p.nworkers = nworkers;
+  p.threads = threads;
+  p.n_tensors = n;
+  plan_validate(addrs, numels, n, dtype, nullptr, &p.n_elements, &p.n_bytes);
+
+  // segments and scalars, in list order
+  p.seg_vbegin.push_back(0);
+  for (int32_t t = 0; t < n; ++t) {
+    const int64_t ne = numels[t];
+    if (ne == 0) continue;
+    const uint64_t a = addrs[t];
+    int64_t head = (int64_t)(((uint64_t)kVecBytes - a % kVecBytes) % kVecBytes) / p.esize;
+    if (head > ne) head = ne;
+    const int64_t body = (ne - head) / p.vec_elems;
+    auto add_scalars = [&](int64_t b, int64_t e) {
+      for (int64_t i = b; i < e; ++i) {
+        p.sc_addr.push_back(a + (uint64_t)i * (uint64_t)p.esize);
+        p.sc_tensor.push_back(t);
+        p.sc_elem.push_back(i);
+      }
+    };
+    if (body < kMinSegVectors) {
+      add_scalars(0, ne);
+      continue;
+    }
+    add_scalars(0, head);
+    p.seg_addr.push_back(a + (uint64_t)head * (uint64_t)p.esize);
+    p.seg_tensor.push_back(t);
+    p.seg_elem0.push_back(head);
+    p.seg_vbegin.push_back(p.seg_vbegin.back() + (uint64_t)body);
+    add_scalars(head + body * p.vec_elems, ne);
+  }
+
+  // worker shares
+  const uint64_t nv = p.nvec(), ns = p.nsc();
+  p.wk_vbegin.resize((size_t)nworkers + 1);
+  p.wk_scbegin.resize((size_t)nworkers + 1);
+  p.wk_seg.resize((size_t)nworkers);
+  for (int32_t w = 0; w <= nworkers; ++w) {
+    p.wk_vbegin[(size_t)w] = share_begin(nv, nworkers, w);
+    p.wk_scbegin[(size_t)w] = share_begin(ns, nworkers, w);
+  }
+  for (int32_t w = 0; w < nworkers; ++w) {
+    const uint64_t vb = p.wk_vbegin[(size_t)w];
+    size_t s = 0;
+    if (p.nseg() > 0) {
+      // last segment whose start is <= vb
+      s = (size_t)(std::upper_bound(p.seg_vbegin.begin(), p.seg_vbegin.end() - 1, vb) - p.seg_vbegin.begin()) - 1;
+      if (s >= (size_t)p.nseg()) s = (size_t)p.nseg() - 1;
+    }
+    p.wk_seg[(size_t)w] = (uint32_t)s;
+  }
+  out = std::move(p);
+  return 0;
+}
+
+}  // namespace gclip

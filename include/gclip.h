@@ -1,0 +1,229 @@
+/*
+ * gclip.h -- C ABI of libgclip: global L2-norm gradient clipping on one
+ * MI355X (gfx950) GPU.
+ *
+ * What the library computes (the three pages this work follows):
+ *
+ *   Grad clip lesson (unhomeschool.com, ru), section "Math": the global norm is
+ *   the square root of the sum of g^2 over every element of every gradient
+ *   tensor; when it exceeds max_norm every element is multiplied by
+ *   max_norm / norm, otherwise the gradients pass unchanged.  Section "Two
+ *   variants: Per-Tensor or Global": all gradients are treated as one vector
+ *   and every tensor gets the same factor.
+ *
+ *   Gradient clipping glossary (paweldubiel.com), section "Mechanism and
+ *   details": g is kept when ||g||_2 <= c and becomes c g / ||g||_2 when
+ *   ||g||_2 > c, for a threshold c > 0; a NaN or infinite value calls for
+ *   diagnosis and an error-if-nonfinite switch stops that update.  Section
+ *   "Order changes the result": clip after the whole effective batch has been
+ *   accumulated.
+ *
+ *   Backprop lesson (unhomeschool.com, vi), section "Accumulation across
+ *   microbatches": gradients are summed with += over microbatches and then
+ *   averaged by 1/n_microbatches before the optimizer step.  Here that
+ *   average is the avg_factor a: the norm is that of a*g and the factor
+ *   written back is a*coef.  Section "Cost of general frameworks": dispatch
+ *   from C and every buffer allocated once at start-up -- the hot calls below
+ *   allocate nothing and never synchronise.
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are HIP device addresses on the current device; host
+ *     pointers are ordinary process memory.  `stream` is a hipStream_t
+ *     (NULL = the default stream).
+ *   - Every function returns a gclip_status.  Argument errors are detected on
+ *     the host before anything is enqueued; nothing is thrown or aborted.
+ *   - The hot calls (gclip_norm, gclip_scale, gclip_clip_) only enqueue work:
+ *     they allocate nothing, copy nothing to the host and never block.
+ *   - Data-dependent status (a NaN or Inf in the gradients) is asynchronous:
+ *     it lands in the device result block and gclip_result_read turns it into
+ *     GCLIP_ENONFINITE.
+ */
+#ifndef GCLIP_H
+#define GCLIP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GCLIP_VERSION 1
+
+/* Storage format of every element of a list (one format per list). */
+typedef enum gclip_dtype {
+  GCLIP_F32 = 0,  /* IEEE binary32 */
+  GCLIP_F16 = 1,  /* IEEE binary16 */
+  GCLIP_BF16 = 2  /* bfloat16: the top 16 bits of a binary32 */
+} gclip_dtype;
+
+typedef enum gclip_status {
+  GCLIP_OK = 0,
+  GCLIP_EINVAL = 1,     /* bad argument (NULL, negative size, overlap, misalignment, bad threshold) */
+  GCLIP_EDTYPE = 2,     /* unknown dtype */
+  GCLIP_ENOMEM = 3,     /* device allocation failed (gclip_list_create only) */
+  GCLIP_EHIP = 4,       /* a HIP runtime call failed; gclip_last_hip_error() holds its code */
+  GCLIP_ENONFINITE = 5, /* gclip_result_read: a NaN/Inf element was seen and the caller asked to stop */
+  GCLIP_EDEVICE = 6,    /* gclip_result_read: the kernels reported a failure (result.status != 0) */
+  GCLIP_ERANGE = 7      /* a buffer given to a query function is too small */
+} gclip_status;
+
+/* Which kernels gclip_clip_ uses (gclip_list_set_path). */
+typedef enum gclip_path {
+  GCLIP_PATH_AUTO = 0,  /* fused when the device supports cooperative launch, else split */
+  GCLIP_PATH_FUSED = 1, /* one cooperative kernel: norm, grid-wide decision, scale; part of each
+                           workgroup's slice stays in registers and LDS between the two passes */
+  GCLIP_PATH_SPLIT = 2  /* two kernels: partial sums with the final reduce folded into the last
+                           workgroup, then the scale pass */
+} gclip_path;
+
+/* Opaque list handle: the device descriptor table of one gradient list plus
+ * its small workspace (per-workgroup partial sums and two counters). */
+typedef struct gclip_list gclip_list;
+
+/* Result block, 64 bytes, written by the kernels into DEVICE memory that the
+ * caller owns (allocate it once; any 8-byte-aligned device address). */
+typedef struct gclip_result {
+  double sumsq;       /* sum over every element of (a*g)^2, in binary64 */
+  double norm;        /* sqrt(sumsq): the global norm before clipping */
+  double scale;       /* factor multiplied into every element: a*coef; 1.0 when nothing was written */
+  double max_norm;    /* threshold of the last decision */
+  int32_t nonfinite;  /* 1 when some element is NaN or +-Inf */
+  int32_t clipped;    /* 1 when norm > max_norm (NaN > c is false) */
+  int32_t skipped;    /* 1 when nothing was written because nonfinite && error_if_nonfinite */
+  int32_t decided;    /* 1 once a scale pass has made its decision; 0 after gclip_norm alone */
+  int32_t status;     /* 0, or a device-side failure code (a grid barrier that timed out) */
+  int32_t reserved[3];
+} gclip_result;
+
+/* Summary of a list's descriptor table (gclip_list_info). */
+typedef struct gclip_list_info_t {
+  int64_t n_tensors;
+  int64_t n_elements;      /* total elements over all tensors */
+  int64_t n_bytes;         /* total bytes of gradient storage */
+  int64_t n_segments;      /* 16-byte-aligned vector runs */
+  int64_t n_vectors;       /* 16-byte vectors over all runs */
+  int64_t n_scalars;       /* elements handled one by one (unaligned ends, tiny tensors) */
+  int32_t n_workers;       /* workgroups of the launch (one per compute unit) */
+  int32_t worker_threads;  /* threads per workgroup */
+  int32_t dtype;
+  int32_t path;            /* gclip_path that gclip_clip_ will use */
+  int64_t resident_vectors; /* vectors the fused kernel keeps on chip between its passes */
+} gclip_list_info_t;
+
+/* One entry of a plan description (gclip_plan_query): a run of elements of
+ * one tensor that one worker handles, either as 16-byte vectors (kind 0) or
+ * element by element (kind 1). */
+typedef struct gclip_plan_entry {
+  int32_t worker;
+  int32_t tensor;
+  int64_t elem_begin;
+  int64_t elem_count;
+  int32_t kind;
+  int32_t reserved;
+} gclip_plan_entry;
+
+/* Build the descriptor table of a gradient list on the current device.
+ * (Grad clip lesson, section "The naive algorithm cannot work on a GPU": the
+ * tensors have very different shapes, so one launch must cover all of them;
+ * section "ANDREA's three-kernel pipeline": one block per chunk, hundreds of
+ * blocks across all tensors, partial sums in a small scratch buffer.)
+ *   d_ptrs[i]  device address of tensor i's first element (contiguous storage,
+ *              aligned to the element size); may be NULL when numels[i] == 0
+ *   numels[i]  element count of tensor i (>= 0)
+ *   n_tensors  >= 0 (0 is an empty list: norm 0, nothing written)
+ *   dtype      a gclip_dtype, the same for every tensor
+ *   out        receives the handle
+ * The caller keeps ownership of the gradient buffers: they must stay
+ * allocated and must not move while the list exists.  Overlapping or
+ * duplicated ranges are rejected with GCLIP_EINVAL (they would be counted and
+ * scaled twice).  This call allocates device memory and synchronises. */
+gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32_t n_tensors, int32_t dtype,
+                               gclip_list** out);
+
+/* Free a list's device table and workspace.  Synchronises.  NULL is a no-op. */
+gclip_status gclip_list_destroy(gclip_list* list);
+
+/* Fill *out with the shape of a list's descriptor table. */
+gclip_status gclip_list_info(const gclip_list* list, gclip_list_info_t* out);
+
+/* Choose the kernels gclip_clip_ uses for this list (a gclip_path).  FUSED
+ * on a device without cooperative launch returns GCLIP_EINVAL. */
+gclip_status gclip_list_set_path(gclip_list* list, int32_t path);
+
+/* Norm pass: sum of squares of a*g over the whole list, reduced to one
+ * binary64 scalar on the device (grad clip lesson, section "ANDREA's
+ * three-kernel pipeline", kernels 1 and 2; section "Math", the norm).
+ *   avg_factor  a > 0 and finite (1/n_microbatches; 1.0 for none)
+ *   d_result    device result block; receives sumsq, norm, nonfinite and
+ *               decided = 0
+ * One kernel launch on `stream`; a fixed summation order makes the result
+ * bit-identical from run to run.  A list must not be used by two calls that
+ * are in flight at once (they share the workspace). */
+gclip_status gclip_norm(gclip_list* list, double avg_factor, gclip_result* d_result, void* stream);
+
+/* Scale pass (grad clip lesson, section "ANDREA's three-kernel pipeline",
+ * kernel 3; glossary page, "Mechanism and details").  Reads d_result->sumsq
+ * and d_result->nonfinite (as left by gclip_norm, or replaced by the caller,
+ * e.g. after summing sumsq across ranks), then on the device:
+ *   norm = sqrt(sumsq); coef = (norm > max_norm) ? max_norm / norm : 1;
+ *   s = avg_factor * coef;
+ *   if (nonfinite && error_if_nonfinite) or s == 1: write nothing;
+ *   else every element g becomes g * s rounded to nearest-even in its format.
+ *   max_norm     c > 0, not NaN; +inf means never clip
+ *   avg_factor   the same a given to gclip_norm
+ *   error_if_nonfinite  nonzero: a NaN/Inf element stops the update
+ * Writes scale, clipped, skipped, max_norm and decided = 1 into d_result. */
+gclip_status gclip_scale(gclip_list* list, double max_norm, double avg_factor, int32_t error_if_nonfinite,
+                         gclip_result* d_result, void* stream);
+
+/* The whole path in place: gclip_norm followed by gclip_scale, as one
+ * cooperative kernel (GCLIP_PATH_FUSED) or two launches (GCLIP_PATH_SPLIT).
+ * Same arguments, same result block, same bits as the two calls. */
+gclip_status gclip_clip_(gclip_list* list, double max_norm, double avg_factor, int32_t error_if_nonfinite,
+                         gclip_result* d_result, void* stream);
+
+/* Copy the device result block to *h_out after the work queued on `stream`
+ * has finished.  The only call that waits.  Returns GCLIP_EDEVICE when
+ * h_out->status != 0, else GCLIP_ENONFINITE when h_out->nonfinite and
+ * error_if_nonfinite, else GCLIP_OK. */
+gclip_status gclip_result_read(const gclip_result* d_result, void* stream, gclip_result* h_out,
+                               int32_t error_if_nonfinite);
+
+/* Describe, without touching any GPU, how a list would be split: the runs
+ * of each worker, in the order the kernels visit them.  Addresses only need
+ * their alignment (they are never dereferenced).
+ *   n_workers, worker_threads  launch shape to plan for (> 0)
+ *   out, cap                   array of cap entries (may be NULL when cap == 0)
+ *   n_out                      receives the number of entries needed
+ * Returns GCLIP_ERANGE when cap is too small (n_out is still set). */
+gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int32_t n_tensors, int32_t dtype,
+                              int32_t n_workers, int32_t worker_threads, gclip_plan_entry* out, int64_t cap,
+                              int64_t* n_out);
+
+/* Replay on the host, without any GPU, the address walk one kernel would
+ * make over a list planned for n_workers workers (the kernels' own cursor
+ * code, compiled for the host), for checking it on the CPU:
+ *   mode 0  norm kernel, 1  scale kernel,
+ *        2  fused kernel, first pass, 3  fused kernel, second pass
+ * Fills out_addr[i] (address of a 16-byte vector, or, with bit 63 set, of a
+ * single element) and out_worker[i] for every lane access in visiting order;
+ * n_out receives the count.  GCLIP_ERANGE when cap is too
+ * small; GCLIP_EINVAL when the lanes of a step disagree on the cursor. */
+gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* numels, int32_t n_tensors, int32_t dtype,
+                              int32_t n_workers, int32_t mode, uint64_t* out_addr, int32_t* out_worker, int64_t cap,
+                              int64_t* n_out);
+
+/* A static string naming a status code. */
+const char* gclip_status_string(int32_t status);
+
+/* The hipError_t behind the last GCLIP_EHIP returned on this thread. */
+int32_t gclip_last_hip_error(void);
+
+/* GCLIP_VERSION of the built library. */
+int32_t gclip_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GCLIP_H */

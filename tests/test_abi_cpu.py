@@ -1,0 +1,144 @@
+"""The C ABI on the CPU: the library loads and exports every function that
+include/gclip.h declares; argument errors come back before any GPU work; the
+descriptor table covers every element exactly once, in balanced shares; and
+the kernels' own address walk, replayed on the host, stays inside the
+tensors and visits every byte once per pass."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import global_l2_norm_amd as g
+from global_l2_norm_amd import _lib
+from synth import gradsets as gs
+from tests.abi_util import ESIZE, check_walk, fake_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gclip.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gclip_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("gclip_norm", "gclip_scale", "gclip_clip_", "gclip_list_create", "gclip_list_destroy",
+                     "gclip_result_read"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    assert set(_lib.EXPORTS) == set(declared_functions())
+    for n in declared_functions():
+        assert hasattr(_lib.lib, n)
+
+
+def test_version_and_status_strings():
+    assert g.gclip_version() == 1
+    for code in range(8):
+        assert g.gclip_status_string(code) not in ("", "unknown status")
+    assert g.gclip_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("args,code", [
+    (([0x1000], [-1], 0), _lib.GCLIP_EINVAL),               # negative size
+    (([0x1002], [10], 0), _lib.GCLIP_EINVAL),               # fp32 tensor not 4-byte aligned
+    (([0x1001], [10], 1), _lib.GCLIP_EINVAL),               # fp16 tensor at an odd address
+    (([0x1000, 0x1010], [10, 10], 0), _lib.GCLIP_EINVAL),   # overlap
+    (([0x1000, 0x1000], [4, 4], 2), _lib.GCLIP_EINVAL),     # the same tensor twice
+    (([0], [10], 0), _lib.GCLIP_EINVAL),                    # NULL with elements
+    (([0x1000], [10], 3), _lib.GCLIP_EDTYPE),               # unknown dtype
+])
+def test_list_create_rejects_bad_lists(args, code):
+    with pytest.raises(g.GclipError) as e:
+        g.gclip_list_create(*args)
+    assert e.value.status == code
+
+
+def test_hot_calls_reject_bad_arguments_before_any_gpu_work():
+    L = _lib.lib
+    assert L.gclip_norm(None, 1.0, None, None) == _lib.GCLIP_EINVAL
+    assert L.gclip_scale(None, 1.0, 1.0, 0, None, None) == _lib.GCLIP_EINVAL
+    assert L.gclip_clip_(None, float("nan"), 1.0, 0, None, None) == _lib.GCLIP_EINVAL
+    assert L.gclip_list_destroy(None) == _lib.GCLIP_OK
+    assert L.gclip_result_read(None, None, None, 0) == _lib.GCLIP_EINVAL
+
+
+def _random_numels(rng):
+    sizes = [0, 1, 2, 3, 5, 7, 63, 64 * 4 - 1, 64 * 4, 64 * 4 + 1, 1000, 4099, 40000, 123457]
+    return [int(rng.choice(sizes)) for _ in range(int(rng.integers(1, 30)))]
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_covers_every_element_once(dtype, seed):
+    rng = np.random.default_rng(100 + seed)
+    numels = _random_numels(rng)
+    es = ESIZE[dtype]
+    addrs = fake_layout(rng, numels, es, misalign=bool(seed % 2))
+    nw = int(rng.choice([1, 3, 7, 256]))
+    entries = g.gclip_plan_query(addrs, numels, dtype, nw, 512)
+    cover = [np.zeros(n, dtype=np.int32) for n in numels]
+    vec_per_worker = np.zeros(nw, dtype=np.int64)
+    sc_per_worker = np.zeros(nw, dtype=np.int64)
+    for w, t, b, c, kind in entries:
+        assert 0 <= w < nw and c > 0
+        cover[t][b:b + c] += 1
+        if kind == 0:
+            assert (addrs[t] + b * es) % 16 == 0 and (c * es) % 16 == 0
+            vec_per_worker[w] += c * es // 16
+        else:
+            sc_per_worker[w] += c
+    for cv in cover:
+        assert np.all(cv == 1)
+    assert vec_per_worker.max() - vec_per_worker.min() <= 1
+    assert sc_per_worker.max() - sc_per_worker.min() <= 1
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+@pytest.mark.parametrize("seed", range(4))
+def test_kernel_walk_stays_inside_and_covers_once(mode, dtype, seed):
+    rng = np.random.default_rng(200 + seed)
+    es = ESIZE[dtype]
+    numels = _random_numels(rng)
+    if seed >= 2:  # big enough that the fused kernel also streams part of each share
+        numels += [3_000_001, 777_777]
+    addrs = fake_layout(rng, numels, es, misalign=bool(seed % 2))
+    nw = [1, 3, 4, 8][seed]
+    ta, tw = g.gclip_plan_trace(addrs, numels, dtype, nw, mode)
+    check_walk(ta, addrs, numels, es)
+    assert tw.min() >= 0 and tw.max() < nw
+
+
+@pytest.mark.parametrize("mode", [0, 2, 3])
+def test_kernel_walk_on_andrea120m_shapes(mode):
+    shapes = gs.shapes_andrea120m()
+    numels = [int(np.prod(s)) for _, s in shapes]
+    rng = np.random.default_rng(7)
+    addrs = fake_layout(rng, numels, 4, misalign=False)
+    ta, _ = g.gclip_plan_trace(addrs, numels, 0, 256, mode)
+    check_walk(ta, addrs, numels, 4)
+
+
+def test_kernel_walk_on_shrunk_gpt_shapes_with_4096_scalars():
+    shapes = [("embed", (503, 2048))]
+    for l in range(2):
+        shapes += [(f"h{l}.QKV", (2048, 6144)), (f"h{l}.LN1.gamma", (2048,)), (f"h{l}.O", (2048, 2048))]
+    shapes += [(f"s{i}", (1,)) for i in range(4096)]
+    numels = [int(np.prod(s)) for _, s in shapes]
+    rng = np.random.default_rng(8)
+    addrs = fake_layout(rng, numels, 2, misalign=True)
+    for mode in (0, 1, 2, 3):
+        ta, _ = g.gclip_plan_trace(addrs, numels, 2, 256, mode)
+        check_walk(ta, addrs, numels, 2)

@@ -1,0 +1,423 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Tolerances: the global norm within relative 1e-5 of the oracle's for every
+format; clipped fp32 elements within relative 1e-5 (exact zero where the
+oracle's is zero); clipped fp16/bf16 elements within 1 ulp of the storage
+format; the non-finite flag exactly; untouched gradients bitwise.  Every
+case runs on both kernel paths (one fused cooperative kernel, and the split
+pair) unless it says otherwise.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gradsets as gs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+PATHS = ("fused", "split")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("the gpu tests need an MI355X")
+    import global_l2_norm_amd  # noqa: F401  (fails loudly when libgclip.so is missing)
+
+
+def _G():
+    import global_l2_norm_amd as G
+    return G
+
+
+def make_list(tensors, path):
+    G = _G()
+    gl = G.GradList(tensors)
+    gl.set_path(G.GCLIP_PATH_FUSED if path == "fused" else G.GCLIP_PATH_SPLIT)
+    return gl
+
+
+def gpu_clip(arrays, dtype, max_norm, avg=1.0, err=False, path="fused", call="clip", views=None):
+    """Upload, clip on the GPU, download.  call='clip' uses gclip_clip_,
+    call='two' uses gclip_norm followed by gclip_scale."""
+    ts = views if views is not None else gu.upload(arrays, dtype)
+    gl = make_list(ts, path)
+    if call == "clip":
+        gl.clip_(max_norm, avg, err)
+    else:
+        gl.norm(avg)
+        gl.scale(max_norm, avg, err)
+    st, r = gl.read(err)
+    out = gu.download(ts, dtype)
+    gl.close()
+    return st, r, out
+
+
+def oracle_clip(arrays, dtype, max_norm, avg=1.0, err=False):
+    ref = [a.copy() for a in arrays]
+    r = oracle.clip_(ref, dtype, max_norm, avg, err)
+    return r, ref
+
+
+def check_against_oracle(arrays, dtype, max_norm, avg=1.0, err=False, path="fused", call="clip", what=""):
+    st, r, out = gpu_clip(arrays, dtype, max_norm, avg, err, path, call)
+    ro, ref = oracle_clip(arrays, dtype, max_norm, avg, err)
+    assert r["status"] == 0
+    assert r["nonfinite"] == ro["nonfinite"], what
+    gu.assert_norm_close(r["norm"], ro["norm"], what)
+    if not math.isnan(ro["norm"]):
+        assert r["clipped"] == ro["clipped"], what
+    assert r["skipped"] == ro["skipped"], what
+    if ro["skipped"] or ro["scale"] == 1.0:
+        gu.assert_bitwise_equal(out, arrays, what + " (must be untouched)")
+    else:
+        gu.assert_elems_close(out, ref, dtype, what)
+    return st, r, ro, out
+
+
+# ------------------------------------------------------------------ the pages' worked examples
+@pytest.mark.parametrize("call", ["clip", "two"])
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_worked_example_6_8(dtype, path, call):
+    """[6, 8] at threshold 5 becomes exactly [3, 4] (glossary page)."""
+    a = [gs.to_storage(np.array([6.0, 8.0]), dtype)]
+    st, r, out = gpu_clip(a, dtype, 5.0, path=path, call=call)
+    assert st == 0 and r["norm"] == 10.0 and r["scale"] == 0.5 and r["clipped"] and r["decided"]
+    assert list(gu.values(out[0], dtype)) == [3.0, 4.0]
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_accumulate_then_clip(path):
+    """10 and -9 sum to 1, which survives a clip at 5; each clipped alone
+    gives 5 and -5 (glossary page, 'Order changes the result')."""
+    outs = []
+    for v in (10.0, -9.0, 1.0):
+        _, r, out = gpu_clip([np.array([v], dtype=np.float32)], "f32", 5.0, path=path)
+        outs.append(float(out[0][0]))
+    assert outs == [5.0, -5.0, 1.0]
+    assert outs[0] + outs[1] == 0.0
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_tie_writes_nothing(dtype, path):
+    """norm == max_norm passes unchanged (grad clip lesson, 'Math')."""
+    a = [gs.to_storage(np.array([3.0, 4.0]), dtype)]
+    st, r, out = gpu_clip(a, dtype, 5.0, path=path)
+    assert not r["clipped"] and r["scale"] == 1.0 and r["norm"] == 5.0
+    gu.assert_bitwise_equal(out, a)
+
+
+# ------------------------------------------------------------------ small and ragged lists
+@pytest.mark.parametrize("call", ["clip", "two"])
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_config(path, call):
+    g = gs.tiny_f32()
+    check_against_oracle(g.arrays, "f32", 1.0, path=path, call=call, what="tiny")
+
+
+def ragged_arrays(rng, dtype, big=False):
+    sizes = [1, 2, 3, 5, 7, 63, 255, 256, 257, 1000, 1023, 4096 + 7, 65_537, 300_001]
+    if big:
+        sizes += [3_000_017, 1_048_576]
+    numels = [int(rng.choice(sizes)) for _ in range(int(rng.integers(3, 25)))]
+    return [gs.to_storage(rng.standard_normal(n) * float(rng.choice([1e-3, 1.0, 30.0])), dtype) for n in numels]
+
+
+def upload_as_views(arrays, dtype, rng):
+    """Each tensor a view at an odd element offset inside one device buffer."""
+    import torch
+    offs, total = [], 0
+    for a in arrays:
+        total += int(rng.integers(1, 8))
+        offs.append(total)
+        total += a.size
+    buf = torch.zeros(total + 8, dtype=gu.torch_dtype(dtype), device="cuda")
+    views = []
+    for a, o in zip(arrays, offs):
+        v = buf[o:o + a.size]
+        v.copy_(gu.upload([a], dtype)[0])
+        views.append(v)
+    return buf, views
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_ragged_lists_misaligned_views(dtype, path, seed):
+    rng = np.random.default_rng(1000 + seed)
+    arrays = ragged_arrays(rng, dtype, big=seed >= 2)
+    c = float(rng.choice([0.5, 2.0, 1e9]))
+    buf, views = upload_as_views(arrays, dtype, rng)
+    st, r, out = gpu_clip(arrays, dtype, c, path=path, views=views)
+    ro, ref = oracle_clip(arrays, dtype, c)
+    gu.assert_norm_close(r["norm"], ro["norm"], "ragged")
+    assert r["clipped"] == ro["clipped"]
+    if ro["clipped"]:
+        gu.assert_elems_close(out, ref, dtype, "ragged")
+    else:
+        gu.assert_bitwise_equal(out, arrays, "ragged, not clipped")
+    # the padding between views is never written
+    import torch
+    mask = torch.ones(buf.numel(), dtype=torch.bool, device="cuda")
+    for v in views:
+        o = v.storage_offset()
+        mask[o:o + v.numel()] = False
+    assert int(torch.count_nonzero(buf[mask].float())) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_medium_list_streams_past_the_resident_part(dtype):
+    """Shares large enough that the fused kernel also re-reads part of them."""
+    rng = np.random.default_rng(77)
+    n_total = 40_000_000 if dtype == "f32" else 80_000_000
+    sizes = [n_total // 2 + 13, n_total // 3 + 1, n_total - n_total // 2 - n_total // 3 - 14]
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-3, dtype) for n in sizes]
+    for path in PATHS:
+        check_against_oracle(arrays, dtype, 1.0, path=path, what=f"medium {dtype} {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_many_tiny_tensors(path):
+    rng = np.random.default_rng(5)
+    arrays = [gs.to_storage(rng.standard_normal(1), "bf16") for _ in range(4096)]
+    arrays += [gs.to_storage(rng.standard_normal(7) * 0.1, "bf16") for _ in range(500)]
+    arrays += [gs.to_storage(rng.standard_normal(2048) * 0.01, "bf16") for _ in range(50)]
+    check_against_oracle(arrays, "bf16", 1.0, path=path, what="many tiny")
+
+
+# ------------------------------------------------------------------ the full configurations
+@pytest.fixture(scope="module")
+def c2():
+    return gs.andrea120m_f32()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_andrea120m_f32(c2, path):
+    st, r, ro, out = check_against_oracle(c2.arrays, "f32", c2.max_norm, path=path, what="andrea120m f32")
+    assert r["clipped"] and abs(r["norm"] - 9.605) < 0.01
+    # binary64 accumulation: far inside the stated tolerance
+    assert abs(r["sumsq"] - ro["sumsq"]) <= 1e-12 * ro["sumsq"]
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_andrea120m_f16_spike(path):
+    g = gs.andrea120m_f16_spike()
+    st, r, ro, out = check_against_oracle(g.arrays, "f16", g.max_norm, path=path, what="andrea120m f16 spike")
+    assert r["clipped"] and 290 < r["norm"] < 305
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_andrea120m_f16_small_writes_nothing(path):
+    g = gs.andrea120m_f16_small()
+    st, r, ro, out = check_against_oracle(g.arrays, "f16", g.max_norm, path=path, what="andrea120m f16 small")
+    assert not r["clipped"] and r["scale"] == 1.0 and 0.09 < r["norm"] < 0.1
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_andrea120m_f32_accum4(path):
+    g = gs.andrea120m_f32_accum4()
+    st, r, ro, out = check_against_oracle(g.arrays, "f32", g.max_norm, avg=g.avg_factor, path=path,
+                                          what="andrea120m accum4")
+    assert r["clipped"] and abs(r["norm"] - 4.802) < 0.01
+
+
+@pytest.fixture(scope="module")
+def c5():
+    return gs.gpt1p3b_bf16()
+
+
+def sample_indices(n, rng, k=256, frac=1e-3):
+    idx = np.concatenate([np.arange(min(k, n)), np.arange(max(0, n - k), n),
+                          rng.integers(0, n, size=int(n * frac)) if n > 0 else np.zeros(0, dtype=np.int64)])
+    return np.unique(idx)
+
+
+def compare_sampled(arrays, out, dtype, s, rng, what):
+    """Elements at sampled positions against the oracle's rounding of g*s."""
+    for t, (a, o) in enumerate(zip(arrays, out)):
+        idx = sample_indices(a.size, rng)
+        ref = [a[idx].copy()]
+        oracle.scale_(ref, dtype, s)
+        bad = gu.elem_mismatches(o[idx], ref[0], dtype)
+        assert not bad.any(), f"{what}: tensor {t}, {int(bad.sum())} sampled elements outside tolerance"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("path", PATHS)
+def test_gpt1p3b_bf16(c5, path):
+    st, r, out = gpu_clip(c5.arrays, "bf16", c5.max_norm, path=path)
+    s_ref, nf = oracle.sumsq(c5.arrays, "bf16")
+    n_ref = math.sqrt(s_ref)
+    assert not nf and not r["nonfinite"] and r["status"] == 0
+    gu.assert_norm_close(r["norm"], n_ref, "gpt1p3b")
+    assert abs(r["sumsq"] - s_ref) <= 1e-12 * s_ref
+    s, clipped, skip = oracle.decide(n_ref, nf, c5.max_norm)
+    assert clipped and r["clipped"] and abs(r["scale"] - s) <= 1e-12 * s
+    compare_sampled(c5.arrays, out, "bf16", s, np.random.default_rng(3), "gpt1p3b")
+
+
+def with_value(g, tensor, index, bits):
+    arrays = list(g.arrays)
+    t = g.names.index(tensor)
+    arrays[t] = arrays[t].copy()
+    arrays[t][index] = bits
+    return arrays
+
+
+@pytest.mark.timeout(900)
+def test_gpt1p3b_bf16_nan(c5):
+    """One NaN in block 23's W_2: the flag is set exactly; with the stop
+    switch nothing is written, without it NaN > c is false and (a = 1)
+    nothing is written either."""
+    G = _G()
+    arrays = with_value(c5, gs.NAN_TENSOR, gs.NAN_INDEX, 0x7FC0)
+    s_ref, nf = oracle.sumsq(arrays, "bf16")
+    assert nf and math.isnan(s_ref)
+    for path in PATHS:
+        for err in (True, False):
+            st, r, out = gpu_clip(arrays, "bf16", 1.0, err=err, path=path)
+            assert r["nonfinite"] and math.isnan(r["norm"]) and not r["clipped"]
+            assert r["skipped"] == err
+            assert st == (G._lib.GCLIP_ENONFINITE if err else G._lib.GCLIP_OK)
+            gu.assert_bitwise_equal(out, arrays, f"nan err={err} {path}")
+
+
+@pytest.mark.timeout(900)
+def test_gpt1p3b_bf16_nan_in_last_scalar_and_inf_in_embed(c5):
+    arrays = with_value(c5, "scalar4095", 0, 0x7FC0)
+    st, r, out = gpu_clip(arrays, "bf16", 1.0, err=True)
+    assert r["nonfinite"] and r["skipped"]
+    gu.assert_bitwise_equal(out, arrays, "nan in the last one-element tensor")
+    n_embed = c5.arrays[0].size
+    for bits in (0x7F80, 0xFF80):  # +Inf, -Inf in the tail element of embed
+        arrays = with_value(c5, "embed", n_embed - 1, bits)
+        st, r, out = gpu_clip(arrays, "bf16", 1.0, err=False)
+        assert r["nonfinite"] and r["norm"] == math.inf and r["clipped"] and r["scale"] == 0.0
+        compare_sampled(arrays, out, "bf16", 0.0, np.random.default_rng(4), "inf in embed")
+        assert np.isnan(gu.values(out[0][-1:], "bf16")[0])
+
+
+# ------------------------------------------------------------------ non-finite elements, small
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_nonfinite_positions(dtype, path):
+    rng = np.random.default_rng(9)
+    base = [gs.to_storage(rng.standard_normal(n) * 0.5, dtype) for n in (3, 5000, 257, 1)]
+    bad_bits = {"f32": [np.float32("nan"), np.float32("inf"), np.float32("-inf")],
+                "f16": [0x7E00, 0x7C00, 0xFC00], "bf16": [0x7FC0, 0x7F80, 0xFF80]}[dtype]
+    for t, i in ((0, 0), (1, 2500), (1, 4999), (2, 256), (3, 0)):
+        for bits in bad_bits:
+            arrays = [a.copy() for a in base]
+            arrays[t][i] = bits
+            for err in (True, False):
+                check_against_oracle(arrays, dtype, 1.0, err=err, path=path, what=f"nonfinite t{t} i{i} err{err}")
+
+
+# ------------------------------------------------------------------ determinism and metamorphic checks
+def test_bitwise_repeatable_and_paths_agree(c2):
+    G = _G()
+    runs = []
+    for path in ("fused", "fused", "split", "split"):
+        st, r, out = gpu_clip(c2.arrays, "f32", 1.0, path=path)
+        runs.append((r, out))
+    for r, out in runs[1:]:
+        gu.assert_bitwise_equal(out, runs[0][1], "run to run / path to path")
+        for k in ("sumsq", "norm", "scale", "clipped", "nonfinite"):
+            assert r[k] == runs[0][0][k], k
+    # gclip_norm alone gives the same bits as the fused path's norm
+    ts = gu.upload(c2.arrays, "f32")
+    gl = G.GradList(ts)
+    gl.norm(1.0)
+    _, rn = gl.read()
+    gl.close()
+    assert rn["sumsq"] == runs[0][0]["sumsq"] and not rn["decided"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_power_of_two_scaling_is_exact(dtype):
+    rng = np.random.default_rng(11)
+    arrays = [gs.to_storage(rng.standard_normal(n) * 0.25, dtype) for n in (100_000, 777, 3)]
+    _, r0, _ = gpu_clip(arrays, dtype, 1e30)
+    scaled = [gs.to_storage(gu.values(a, dtype) * 4.0, dtype) for a in arrays]
+    _, r1, _ = gpu_clip(scaled, dtype, 1e30)
+    assert r1["sumsq"] == 16.0 * r0["sumsq"] and r1["norm"] == 4.0 * r0["norm"]
+
+
+def test_scale_with_caller_supplied_sumsq():
+    """gclip_scale decides from the sumsq in the result block, e.g. one
+    summed over several ranks: a block claiming 4x the local sumsq doubles
+    the norm the decision sees."""
+    import torch
+    G = _G()
+    rng = np.random.default_rng(12)
+    arrays = [gs.to_storage(rng.standard_normal(1000), "f32")]
+    local_sumsq, _ = oracle.sumsq(arrays, "f32")
+    ts = gu.upload(arrays, "f32")
+    gl = G.GradList(ts)
+    blk = G.GclipResult()
+    blk.sumsq = 4.0 * local_sumsq
+    host = torch.frombuffer(bytearray(bytes(blk)), dtype=torch.uint8)
+    gl.result.copy_(host)
+    gl.scale(1.0, 1.0, False)
+    st, r = gl.read()
+    out = gu.download(ts, "f32")
+    gl.close()
+    s, clipped, _ = oracle.decide(2.0 * math.sqrt(local_sumsq), False, 1.0)
+    assert r["clipped"] and abs(r["scale"] - s) <= 1e-15 * s
+    ref = [arrays[0].copy()]
+    oracle.scale_(ref, "f32", s)
+    gu.assert_elems_close(out, ref, "f32", "external sumsq")
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("path", PATHS)
+def test_empty_list(path):
+    G = _G()
+    gl = make_list([], path)
+    gl.clip_(1.0)
+    st, r = gl.read()
+    gl.close()
+    assert st == 0 and r["norm"] == 0.0 and not r["clipped"] and r["scale"] == 1.0
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_size_tensors_and_infinite_threshold(path):
+    import torch
+    rng = np.random.default_rng(13)
+    arrays = [np.zeros(0, dtype=np.float32), gs.to_storage(rng.standard_normal(999) * 3, "f32"),
+              np.zeros(0, dtype=np.float32)]
+    check_against_oracle(arrays, "f32", 1.0, path=path, what="zero-size")
+    st, r, out = gpu_clip(arrays, "f32", math.inf, path=path)
+    assert not r["clipped"]
+    gu.assert_bitwise_equal(out, arrays)
+
+
+def test_averaging_without_clip_still_writes():
+    rng = np.random.default_rng(14)
+    arrays = [gs.to_storage(rng.standard_normal(5000) * 1e-3, "f32")]
+    for path in PATHS:
+        st, r, ro, out = check_against_oracle(arrays, "f32", 1e6, avg=0.25, path=path, what="average only")
+        assert not r["clipped"] and r["scale"] == 0.25
+
+
+def test_invalid_arguments_enqueue_nothing():
+    G = _G()
+    arrays = [np.array([6.0, 8.0], dtype=np.float32)]
+    ts = gu.upload(arrays, "f32")
+    gl = G.GradList(ts)
+    for bad in (float("nan"), 0.0, -1.0):
+        with pytest.raises(G.GclipError):
+            gl.clip_(bad)
+    for bad in (0.0, -0.5, float("inf"), float("nan")):
+        with pytest.raises(G.GclipError):
+            gl.clip_(5.0, avg_factor=bad)
+    import torch
+    torch.cuda.synchronize()
+    assert list(gu.values(gu.download(ts, "f32")[0], "f32")) == [6.0, 8.0]
+    gl.close()
