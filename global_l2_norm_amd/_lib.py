@@ -79,6 +79,15 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built: run `python -m global_l2_norm_amd.build` "
                            "(hipcc --offload-arch=gfx950); there is no fallback path")
+    # PyTorch-ROCm wheels carry their own HIP runtime.  Loading torch first
+    # lets libgclip bind to that same runtime, so the process holds one HIP
+    # runtime and the device memory and streams torch hands over are valid
+    # for our kernels; loaded the other way round, two runtimes end up in the
+    # process and the second one finds no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     return _declare(ctypes.CDLL(LIB_PATH))
 
 

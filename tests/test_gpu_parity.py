@@ -201,8 +201,9 @@ def c2():
 def test_andrea120m_f32(c2, path):
     st, r, ro, out = check_against_oracle(c2.arrays, "f32", c2.max_norm, path=path, what="andrea120m f32")
     assert r["clipped"] and abs(r["norm"] - 9.605) < 0.01
-    # binary64 accumulation: far inside the stated tolerance
-    assert abs(r["sumsq"] - ro["sumsq"]) <= 1e-12 * ro["sumsq"]
+    # binary64 accumulation on both sides: the gap is bounded by the oracle's
+    # own sequential summation error, (N - 1) * 2^-53 of the sum for positive terms
+    assert abs(r["sumsq"] - ro["sumsq"]) <= c2.numel * 2.0 ** -53 * ro["sumsq"]
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -256,9 +257,9 @@ def test_gpt1p3b_bf16(c5, path):
     n_ref = math.sqrt(s_ref)
     assert not nf and not r["nonfinite"] and r["status"] == 0
     gu.assert_norm_close(r["norm"], n_ref, "gpt1p3b")
-    assert abs(r["sumsq"] - s_ref) <= 1e-12 * s_ref
+    assert abs(r["sumsq"] - s_ref) <= c5.numel * 2.0 ** -53 * s_ref
     s, clipped, skip = oracle.decide(n_ref, nf, c5.max_norm)
-    assert clipped and r["clipped"] and abs(r["scale"] - s) <= 1e-12 * s
+    assert clipped and r["clipped"] and abs(r["scale"] - s) <= c5.numel * 2.0 ** -53 * s
     compare_sampled(c5.arrays, out, "bf16", s, np.random.default_rng(3), "gpt1p3b")
 
 
