@@ -1,0 +1,305 @@
+"""Benchmark of the global L2-norm clipping path on one MI355X.
+
+One step is one gclip_clip_ call (norm of the whole list, the decision, and
+the in-place scale) over the ANDREA-120M-shaped fp32 gradient list (124
+tensors, 92,248,320 elements, N(0, 1e-3^2): norm ~9.6 > max_norm 1.0, so every
+step clips).  Between steps, outside the timed region, the gradients are
+restored from a pristine device copy and a 2 GiB buffer is read so that no
+cache holds the list (a read, so no dirty lines are left to drain into the
+timed call).  Each step is bracketed by HIP events on the stream the kernels
+run on; value = algorithmic bytes / mean event time, where the algorithmic
+bytes are N*s read by the norm pass plus 2*N*s read and written by the scale
+pass.
+
+Prints one JSON line.  Other modes:
+  --config NAME        another synthetic set (synth.gradsets.CONFIGS)
+  --path fused|split   force the kernel path
+  --profile-pass       a short run for rocprofv3 (no CPU baseline, plus a
+                       calibration copy of known size for the PMC counters)
+  --summarize-rocprof  turn rocprofv3 output into the summaries kept in
+                       profiles/ (see the --help of that mode)
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "clip_grad_norm GB/s and % of HBM peak, ANDREA-120M-shaped grads"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["global_l2_norm_amd/csrc/gclip_kernels.hip", "global_l2_norm_amd/csrc/gclip_cursor.hpp"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_grad_clip_fused__andrea120m_f32__pmc.txt")
+WORKLOADS = {
+    "andrea120m_f32": "ANDREA-120M-shaped fp32 gradient list: 124 tensors (tok_embed [8449,768], pos_embed "
+                      "[1024,768], 12 blocks of W_Q/W_K/W_V/W_O [768,768], W_1 [768,3072], W_2 [3072,768], four "
+                      "[768] norms, final norm 2x[768]), 92,248,320 elements, N(0,1e-3^2), max_norm 1.0",
+}
+
+
+CALIBRATION_BYTES = 369_000_000
+
+
+def upload(arrays, dtype):
+    """Host raw storage (float32 or uint16 bit patterns) to device tensors."""
+    import numpy as np
+    import torch
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    if dtype == "f32":
+        return [torch.from_numpy(np.ascontiguousarray(a)).to("cuda") for a in arrays]
+    return [torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(tdt) for a in arrays]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(numel, esize, wrote):
+    return numel * esize * (3 if wrote else 1)
+
+
+def read_traffic(numel_bytes_alg):
+    """HBM bytes per launch from the committed PMC summary, or None when it
+    is missing or was taken on other kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(g, min_seconds=10.0):
+    """The oracle as it stands, on this host, on the same workload."""
+    import oracle
+    reps, total = 0, 0.0
+    work = [a.copy() for a in g.arrays]
+    while total < min_seconds or reps == 0:
+        for w, a in zip(work, g.arrays):
+            w[...] = a
+        t0 = time.perf_counter()
+        r = oracle.clip_(work, g.dtype, g.max_norm, g.avg_factor, g.error_if_nonfinite)
+        total += time.perf_counter() - t0
+        reps += 1
+    wrote = not (r["skipped"] or r["scale"] == 1.0)
+    esize = 4 if g.dtype == "f32" else 2
+    sec = total / reps
+    return {"value": round(algorithmic_bytes(g.numel, esize, wrote) / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole {g.name} list ({g.numel} elements), norm+decision+scale, {reps} rep(s), "
+                      f"{sec:.2f} s each, single-threaded binary64 C"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="andrea120m_f32")
+    ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--summarize-rocprof", nargs="+", metavar="ARG",
+                    help="KIND OUT DIR...: KIND is 'trace' (a --kernel-trace --stats output dir) or 'pmc' "
+                         "(FETCH_SIZE dir, then WRITE_SIZE dir); OUT is the summary file to write")
+    a = ap.parse_args()
+
+    if a.summarize_rocprof:
+        return summarize(a.summarize_rocprof, " ".join(sys.argv))
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus})",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import global_l2_norm_amd as G
+    from synth import gradsets as gs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    g = gs.make(a.config)
+    esize = 4 if g.dtype == "f32" else 2
+    tensors = upload(g.arrays, g.dtype)
+    pristine = [t.clone() for t in tensors]
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    flush.fill_(1)
+    gl = G.GradList(tensors)
+    if a.path != "auto":
+        gl.set_path(G.GCLIP_PATH_FUSED if a.path == "fused" else G.GCLIP_PATH_SPLIT)
+    info = gl.info()
+    path_name = {1: "fused", 2: "split"}[info["path"]]
+    stream = torch.cuda.current_stream()
+
+    def restore():
+        for t, p in zip(tensors, pristine):
+            t.copy_(p)
+        if not a.no_flush:
+            flush.sum(dtype=torch.int64)
+
+    if a.profile_pass:
+        # calibration for the PMC counters: an elementwise kernel that reads
+        # and writes exactly CALIBRATION_BYTES each (torch.neg), then a few clips
+        src = torch.full((CALIBRATION_BYTES // 4,), 3.0, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            flush.sum(dtype=torch.int64)
+            torch.neg(src, out=dst)
+        for _ in range(max(a.steps, 1)):
+            restore()
+            gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
+        torch.cuda.synchronize()
+        st, r = gl.read()
+        print(json.dumps({"profile_pass": True, "config": a.config, "path": path_name, "steps": a.steps,
+                          "norm": r["norm"], "status": st}), flush=True)
+        return 0
+
+    for _ in range(a.warmup):
+        restore()
+        gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(a.steps):
+        restore()
+        ev[i][0].record(stream)
+        gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    st, r = gl.read(g.error_if_nonfinite)
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    mean_ms = statistics.fmean(ms)
+    wrote = not (r["skipped"] or r["scale"] == 1.0)
+    alg = algorithmic_bytes(g.numel, esize, wrote)
+    gbps = alg / (mean_ms * 1e-3) / 1e9
+    traffic = read_traffic(alg) if (a.config == "andrea120m_f32" and path_name == "fused") else None
+    out = {
+        "metric": METRIC if a.config == "andrea120m_f32" else f"clip_grad_norm GB/s and % of HBM peak, {a.config}",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(mean_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": g.dtype,
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS.get(a.config, a.config), "name": a.config, "path": path_name,
+                   "launches_per_step": 1 if path_name == "fused" else 2,
+                   "n_tensors": len(g.arrays), "n_elements": g.numel, "algorithmic_bytes_per_step": alg,
+                   "clipped": bool(r["clipped"]), "cache_state": "cold" if not a.no_flush else "after restore"},
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "elements_per_s": round(g.numel / (mean_ms * 1e-3), 1),
+        "ms_per_step_median": round(statistics.median(ms), 5),
+        "ms_per_step_min": round(min(ms), 5),
+        "wall_s_timed_loop_incl_restore_and_flush": round(t_wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "k_grad_clip_fused" if path_name == "fused" else "k_grad_norm_partial+k_grad_scale",
+                     "resident_bytes": info["resident_vectors"] * 16},
+        "norm": r["norm"],
+    }
+    if st not in (0,) or r["status"] != 0:
+        out["error"] = f"status {st}, device status {r['status']}"
+    gl.close()
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(g)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _stats_rows(d):
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_rows(d):
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(args, cmdline):
+    """Write a short text summary of rocprofv3 output into profiles/."""
+    kind, out = args[0], args[1]
+    dirs = args[2:]
+    lines = [f"# written by: python {cmdline}", f"kernel_source_sha256_16: {kernel_source_hash()}"]
+    if kind == "trace":
+        rows = _stats_rows(dirs[0])
+        lines.append("# rocprofv3 --kernel-trace --stats: per-kernel time (ns)")
+        lines.append(f"{'kernel':60s} {'calls':>6s} {'avg_ns':>12s} {'min_ns':>12s} {'max_ns':>12s} {'pct':>6s}")
+        for r in rows:
+            name = r.get("Name", "")
+            short = name.split("(")[0][-60:]
+            lines.append(f"{short:60s} {r.get('Calls', ''):>6s} {float(r.get('AverageNs', 0)):12.1f} "
+                         f"{float(r.get('MinNs', 0)):12.1f} {float(r.get('MaxNs', 0)):12.1f} "
+                         f"{float(r.get('Percentage', 0)):6.2f}")
+    elif kind == "pmc":
+        per = {}
+        for d, counter in zip(dirs, ("FETCH_SIZE", "WRITE_SIZE")):
+            rows = _counter_rows(d)
+            acc = {}
+            for r in rows:
+                if r.get("Counter_Name", "") != counter:
+                    continue
+                name = r.get("Kernel_Name", "")
+                key = ("clip" if "k_grad_clip_fused" in name else "copy" if "neg" in name.lower() else None)
+                if key is None:
+                    continue
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
+            per[counter] = {k: statistics.median(v) for k, v in acc.items()}
+        copy_bytes = CALIBRATION_BYTES
+        f_cal = per["FETCH_SIZE"]["copy"] * 1024 / copy_bytes
+        w_cal = per["WRITE_SIZE"]["copy"] * 1024 / copy_bytes
+        fetch = per["FETCH_SIZE"]["clip"] * 1024 / f_cal
+        write = per["WRITE_SIZE"]["clip"] * 1024 / w_cal
+        lines += ["# rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, median over dispatches)",
+                  f"fetch_kib_per_dispatch_clip: {per['FETCH_SIZE']['clip']:.1f}",
+                  f"write_kib_per_dispatch_clip: {per['WRITE_SIZE']['clip']:.1f}",
+                  f"fetch_kib_per_dispatch_copy_369MB: {per['FETCH_SIZE']['copy']:.1f}",
+                  f"write_kib_per_dispatch_copy_369MB: {per['WRITE_SIZE']['copy']:.1f}",
+                  f"fetch_calibration (counter bytes / copy bytes): {f_cal:.4f}",
+                  f"write_calibration (counter bytes / copy bytes): {w_cal:.4f}",
+                  f"hbm_fetch_bytes_per_dispatch: {fetch:.0f}",
+                  f"hbm_write_bytes_per_dispatch: {write:.0f}",
+                  f"hbm_bytes_per_dispatch: {fetch + write:.0f}"]
+    else:
+        raise SystemExit("kind must be 'trace' or 'pmc'")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

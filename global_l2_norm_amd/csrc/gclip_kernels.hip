@@ -18,7 +18,8 @@
 //   - lane sums are reduced by an xor butterfly inside each wave and in wave
 //     order through LDS; per-worker partials are summed in worker order by
 //     whichever workgroup arrives last (an agent-scope ticket), so the bits
-//     of the norm do not depend on scheduling;
+//     of the norm do not depend on scheduling; cross-workgroup data moves
+//     only through agent-scope atomics (see complete_stores);
 //   - the fused kernel (cooperative launch, all workgroups resident) keeps
 //     the last kRegSteps + kLdsSteps steps of each worker's share in VGPRs and
 //     LDS across the grid-wide decision, so the scale pass writes those bytes
@@ -37,29 +38,83 @@ constexpr uint32_t kSpinLimit = 1u << 26;  // bounded wait at the grid barrier
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ u32x4 load_vec(uint64_t a) { return *reinterpret_cast<const u32x4*>(a); }
-__device__ __forceinline__ void store_vec(uint64_t a, u32x4 q) { *reinterpret_cast<u32x4*>(a) = q; }
+// Gradient memory is accessed through global-address-space pointers so that
+// the loads are global_load (vector memory counter only), not flat loads,
+// which would also be waited for by every scalar-load and LDS wait.
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+typedef __attribute__((address_space(1))) uint16_t g_u16;
+
+__device__ __forceinline__ u32x4 load_vec(uint64_t a) { return *reinterpret_cast<const g_u32x4*>(a); }
+__device__ __forceinline__ void store_vec(uint64_t a, u32x4 q) { *reinterpret_cast<g_u32x4*>(a) = q; }
 
 // ---------------------------------------------------------------- element arithmetic
-template <int DT>
-__device__ __forceinline__ void acc_vec(const u32x4 q, double (&acc)[4]) {
+// Sum of the squares of one vector's elements, exact in binary64 for the
+// fallback and within 7 * 2^-24 relative otherwise.  The common case sums the
+// squares in fp32 (binary64 arithmetic on every element would cost more
+// issue slots than the memory pass leaves), which is safe while the fp32 sum
+// lies in [2^-100, 2^126): no square overflowed and an underflowed square
+// (< 2^-126, at most 8 of them) is below 2^-24 of the sum.  Any other vector
+// -- huge or tiny elements, NaN, Inf -- is summed again in binary64, where
+// squares of every finite fp32/fp16/bf16 value are exact and cannot
+// overflow; an all-zero vector is 0 exactly.  fp16 values can never leave
+// the safe range (|x| <= 65504, squares of subnormals are normal fp32).
+__device__ __forceinline__ double sumsq64_f32(const u32x4 q) {
+  double d = 0.0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint32_t w = q[c];
-    if constexpr (DT == GCLIP_F32) {
-      const double x = (double)__uint_as_float(w);
-      acc[c] = __builtin_fma(x, x, acc[c]);
-    } else if constexpr (DT == GCLIP_F16) {
-      const double lo = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-      const double hi = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-      acc[c] = __builtin_fma(lo, lo, acc[c]);
-      acc[c] = __builtin_fma(hi, hi, acc[c]);
-    } else {
-      const double lo = (double)__uint_as_float(w << 16);
-      const double hi = (double)__uint_as_float(w & 0xffff0000u);
-      acc[c] = __builtin_fma(lo, lo, acc[c]);
-      acc[c] = __builtin_fma(hi, hi, acc[c]);
+    const double x = (double)__uint_as_float(q[c]);
+    d = __builtin_fma(x, x, d);
+  }
+  return d;
+}
+
+__device__ __forceinline__ double sumsq64_bf16(const u32x4 q) {
+  double d = 0.0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const double lo = (double)__uint_as_float(q[c] << 16), hi = (double)__uint_as_float(q[c] & 0xffff0000u);
+    d = __builtin_fma(lo, lo, d);
+    d = __builtin_fma(hi, hi, d);
+  }
+  return d;
+}
+
+__device__ __forceinline__ bool fp32_sum_safe(float s) { return s >= 0x1p-100f && s < 0x1p+126f; }
+
+template <int DT>
+__device__ __forceinline__ double vec_sumsq(const u32x4 q) {
+  if constexpr (DT == GCLIP_F32) {
+    const float x0 = __uint_as_float(q[0]), x1 = __uint_as_float(q[1]);
+    const float x2 = __uint_as_float(q[2]), x3 = __uint_as_float(q[3]);
+    float s = x0 * x0;
+    s = __builtin_fmaf(x1, x1, s);
+    s = __builtin_fmaf(x2, x2, s);
+    s = __builtin_fmaf(x3, x3, s);
+    if (__builtin_expect(fp32_sum_safe(s), 1)) return (double)s;
+    if (((q[0] | q[1] | q[2] | q[3]) & 0x7fffffffu) == 0u) return 0.0;
+    return sumsq64_f32(q);
+  } else if constexpr (DT == GCLIP_F16) {
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[c] & 0xffffu));
+      const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[c] >> 16));
+      s = __builtin_fmaf(lo, lo, s);
+      s = __builtin_fmaf(hi, hi, s);
     }
+    return (double)s;
+  } else {
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float lo = __uint_as_float(q[c] << 16), hi = __uint_as_float(q[c] & 0xffff0000u);
+      s = __builtin_fmaf(lo, lo, s);
+      s = __builtin_fmaf(hi, hi, s);
+    }
+    if (__builtin_expect(fp32_sum_safe(s), 1)) return (double)s;
+    if (((q[0] | q[1] | q[2] | q[3]) & 0x7fff7fffu) == 0u) return 0.0;
+    return sumsq64_bf16(q);
   }
 }
 
@@ -109,14 +164,14 @@ __device__ __forceinline__ u32x4 scale_vec(u32x4 q, double s64, float s32) {
 
 template <int DT>
 __device__ __forceinline__ uint32_t load_elem(uint64_t a) {
-  if constexpr (DT == GCLIP_F32) return *reinterpret_cast<const uint32_t*>(a);
-  else return (uint32_t)*reinterpret_cast<const uint16_t*>(a);
+  if constexpr (DT == GCLIP_F32) return *reinterpret_cast<const g_u32*>(a);
+  else return (uint32_t)*reinterpret_cast<const g_u16*>(a);
 }
 
 template <int DT>
 __device__ __forceinline__ void store_elem(uint64_t a, uint32_t bits) {
-  if constexpr (DT == GCLIP_F32) *reinterpret_cast<uint32_t*>(a) = bits;
-  else *reinterpret_cast<uint16_t*>(a) = (uint16_t)bits;
+  if constexpr (DT == GCLIP_F32) *reinterpret_cast<g_u32*>(a) = bits;
+  else *reinterpret_cast<g_u16*>(a) = (uint16_t)bits;
 }
 
 // ---------------------------------------------------------------- reductions
@@ -136,8 +191,12 @@ __device__ __forceinline__ double wg_sum(double v, double* red) {
   return t;
 }
 
-__device__ __forceinline__ double lane_total(const double (&acc)[4], double accs) {
-  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + accs;
+// A lane's total: its per-slot accumulators in slot order, then its single elements.
+__device__ __forceinline__ double lane_total(const double (&acc)[kUnroll], double accs) {
+  double t = acc[0];
+#pragma unroll
+  for (int u = 1; u < kUnroll; ++u) t += acc[u];
+  return t + accs;
 }
 
 // Sum of the workers' partials in worker order (lane i takes i, i + kThreads, ...).
@@ -165,25 +224,71 @@ __device__ __forceinline__ Decision decide(double sumsq, int nonfinite, double m
   return d;
 }
 
-// ---------------------------------------------------------------- norm pass pieces
+// ---------------------------------------------------------------- group loads and stores
+// Load the vectors of one group into q (zeros where a lane has no vector).
+__device__ __forceinline__ void load_group(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j,
+                                           uint64_t j1, u32x4 (&q)[kUnroll]) {
+  const uint32_t t = threadIdx.x;
+  uint64_t base = 0;
+  const int kind = group_kind(cur, vb, ve, j, j1, base);
+  if (kind == kGroupFull) {
+    const g_u32x4* g = reinterpret_cast<const g_u32x4*>(uniform64(base));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = g[u * kThreads + t];
+  } else if (kind == kGroupTail) {
+    const g_u32x4* g = reinterpret_cast<const g_u32x4*>(uniform64(base));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      q[u] = tail_ok(vb, ve, j, j1, u, t) ? g[u * kThreads + t] : u32x4{0u, 0u, 0u, 0u};
+  } else {
+    uint64_t a[kUnroll];
+    bool ok[kUnroll];
+    cross_addrs(p, cur, vb, ve, j, j1, t, a, ok);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = ok[u] ? load_vec(a[u]) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Store f(vector u) for every vector of one group (the addresses of the
+// group are recomputed exactly as load_group computed them).
+template <typename F>
+__device__ __forceinline__ void store_group(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j,
+                                            uint64_t j1, F&& f) {
+  const uint32_t t = threadIdx.x;
+  uint64_t base = 0;
+  const int kind = group_kind(cur, vb, ve, j, j1, base);
+  if (kind == kGroupFull) {
+    g_u32x4* g = reinterpret_cast<g_u32x4*>(uniform64(base));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) g[u * kThreads + t] = f(u);
+  } else if (kind == kGroupTail) {
+    g_u32x4* g = reinterpret_cast<g_u32x4*>(uniform64(base));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (tail_ok(vb, ve, j, j1, u, t)) g[u * kThreads + t] = f(u);
+  } else {
+    uint64_t a[kUnroll];
+    bool ok[kUnroll];
+    cross_addrs(p, cur, vb, ve, j, j1, t, a, ok);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (ok[u]) store_vec(a[u], f(u));
+  }
+}
+
+// ---------------------------------------------------------------- norm and scale passes
 // Streamed steps [j0, j1) of a worker's share, accumulating into acc.
+// Step j of a share always adds into acc[j % kUnroll]: groups start at
+// multiples of kUnroll in every kernel, so the norm kernel and the fused
+// kernel add the same values in the same order.
 template <int DT>
 __device__ __forceinline__ void norm_steps(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j0,
-                                           uint64_t j1, double (&acc)[4]) {
-  const uint32_t t = threadIdx.x;
+                                           uint64_t j1, double (&acc)[kUnroll]) {
   for (uint64_t j = j0; j < j1; j += kUnroll) {
     u32x4 q[kUnroll];
+    load_group(p, cur, vb, ve, j, j1, q);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      q[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j + u < j1) {
-        const uint64_t b = vb + (j + u) * kThreads, v = b + t;
-        const uint64_t a = step_addr(p, cur, b, ve, v);
-        if (v < ve) q[u] = load_vec(a);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc_vec<DT>(q[u], acc);
+    for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
   }
 }
 
@@ -195,28 +300,16 @@ __device__ __forceinline__ double norm_scalars(const DevPlan& p, int w) {
   return s;
 }
 
+// Streamed steps [j0, j1): read, multiply, write back.  The group's loads are
+// all issued before its first store.
 template <int DT>
 __device__ __forceinline__ void scale_steps(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j0,
                                             uint64_t j1, double s64, float s32) {
-  const uint32_t t = threadIdx.x;
   for (uint64_t j = j0; j < j1; j += kUnroll) {
     u32x4 q[kUnroll];
-    uint64_t a[kUnroll];
-    bool ok[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      ok[u] = false;
-      a[u] = 0;
-      if (j + u < j1) {
-        const uint64_t b = vb + (j + u) * kThreads, v = b + t;
-        a[u] = step_addr(p, cur, b, ve, v);
-        ok[u] = v < ve;
-        if (ok[u]) q[u] = load_vec(a[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (ok[u]) store_vec(a[u], scale_vec<DT>(q[u], s64, s32));
+    Cursor c2 = cur;
+    load_group(p, cur, vb, ve, j, j1, q);
+    store_group(p, c2, vb, ve, j, j1, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
   }
 }
 
@@ -245,18 +338,37 @@ __device__ __forceinline__ void write_decision(gclip_result* res, const Decision
   res->decided = 1;
 }
 
+// Cross-workgroup data (per-workgroup partials, the decision, the counters)
+// is written and read only with agent-scope atomics, which go to the
+// device-coherent level of the memory system.  Waiting for those stores to
+// complete before the next atomic is issued orders them for every reader, so
+// no agent-scope fence is needed: on gfx950 such a fence writes back and
+// invalidates the whole L2 of the XCD, which costs ~18 us when 256
+// workgroups do it at the end of a pass.
+__device__ __forceinline__ void complete_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Ticket: returns true in the last workgroup to arrive (all threads).
 __device__ __forceinline__ bool arrive(const DevPlan& p, int w, double part, int* flag) {
   if (threadIdx.x == 0) {
     __hip_atomic_store(&p.partials[w], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const uint32_t prev = __hip_atomic_fetch_add(&p.sync[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    complete_stores();
+    const uint32_t prev = __hip_atomic_fetch_add(&p.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = (prev == (uint32_t)p.nworkers - 1u) ? 1 : 0;
   }
   __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *flag != 0;
+}
+
+// After the last workgroup has summed the partials it overwrites them with
+// NaN, so a partial that was somehow read before it was written could only
+// ever show up as a NaN norm, never as a plausible wrong one.
+__device__ __forceinline__ void poison_partials(const DevPlan& p) {
+  for (int i = threadIdx.x; i < p.nworkers; i += kThreads)
+    __hip_atomic_store(&p.partials[i], __builtin_nan(""), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- kernels
@@ -268,7 +380,9 @@ __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, doubl
   __shared__ int flag;
   const int w = blockIdx.x;
   const uint64_t vb = p.wk_vbegin[w], ve = p.wk_vbegin[w + 1];
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
   if (vb < ve) {
     Cursor cur;
     cursor_load(p, cur, p.wk_seg[w]);
@@ -277,6 +391,7 @@ __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, doubl
   const double part = wg_sum(lane_total(acc, norm_scalars<DT>(p, w)), red);
   if (arrive(p, w, part, &flag)) {
     const double S = partials_sum(p, red);
+    poison_partials(p);
     if (threadIdx.x == 0) {
       write_norm(res, S, avg);
       res->scale = 1.0;
@@ -330,7 +445,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   const uint32_t nreg = fs.nreg;  // register steps [js, js + nreg)
   const uint32_t nlds = fs.nlds;  // LDS steps [js + nreg, nsteps)
 
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
   u32x4 keep[kRegSteps];
   Cursor cur0, cur_reg, cur_lds;
   if (vb < ve) {
@@ -340,36 +457,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
     cur_reg = cur;
     cursor_seek(p, cur_reg, vb + js * kThreads);
     cur = cur_reg;
+    // register steps: issue every load first, then accumulate in step order
 #pragma unroll
-    for (int k = 0; k < kRegSteps; ++k) {
-      keep[k] = u32x4{0u, 0u, 0u, 0u};
-      if ((uint32_t)k < nreg) {
-        const uint64_t b = vb + (js + k) * kThreads, v = b + t;
-        const uint64_t a = step_addr(p, cur, b, ve, v);
-        if (v < ve) keep[k] = load_vec(a);
-      }
+    for (int g = 0; g < kRegSteps / kUnroll; ++g) {
+      u32x4 q[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q[u] = u32x4{0u, 0u, 0u, 0u};
+      if ((uint32_t)(g * kUnroll) < nreg) load_group(p, cur, vb, ve, js + g * kUnroll, js + nreg, q);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) keep[g * kUnroll + u] = q[u];
     }
 #pragma unroll
     for (int k = 0; k < kRegSteps; ++k)
-      if ((uint32_t)k < nreg) acc_vec<DT>(keep[k], acc);
+      if ((uint32_t)k < nreg) acc[k % kUnroll] += vec_sumsq<DT>(keep[k]);
     cur_lds = cur;
     cursor_seek(p, cur_lds, vb + (js + nreg) * kThreads);
     cur = cur_lds;
     for (uint32_t k0 = 0; k0 < nlds; k0 += kUnroll) {
       u32x4 q[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        q[u] = u32x4{0u, 0u, 0u, 0u};
-        if (k0 + u < nlds) {
-          const uint64_t b = vb + (js + nreg + k0 + u) * kThreads, v = b + t;
-          const uint64_t a = step_addr(p, cur, b, ve, v);
-          if (v < ve) q[u] = load_vec(a);
-        }
-      }
+      load_group(p, cur, vb, ve, js + nreg + k0, js + nreg + nlds, q);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         if (k0 + u < nlds) {
-          acc_vec<DT>(q[u], acc);
+          acc[u] += vec_sumsq<DT>(q[u]);
           keep_lds[(k0 + u) * kThreads + t] = q[u];
         }
       }
@@ -381,6 +491,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   if (t == 0) timed_out = 0;
   if (arrive(p, w, part, &flag)) {
     const double S = partials_sum(p, red);
+    poison_partials(p);
     if (t == 0) {
       const double sumsq = (avg * avg) * S;
       const int nonfinite = __builtin_isfinite(S) ? 0 : 1;
@@ -392,11 +503,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
       __hip_atomic_store(&p.bcast[0], d.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&p.sync[2], (uint32_t)d.skip, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&p.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.sync[1], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      complete_stores();
+      __hip_atomic_store(&p.sync[1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else if (t == 0) {
     uint32_t spins = 0;
-    while (__hip_atomic_load(&p.sync[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+    while (__hip_atomic_load(&p.sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
       __builtin_amdgcn_s_sleep(2);
       if (++spins > kSpinLimit) {
         timed_out = 1;
@@ -413,19 +525,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
     if (vb < ve) {
       Cursor cur = cur_reg;
 #pragma unroll
-      for (int k = 0; k < kRegSteps; ++k) {
-        if ((uint32_t)k < nreg) {
-          const uint64_t b = vb + (js + k) * kThreads, v = b + t;
-          const uint64_t a = step_addr(p, cur, b, ve, v);
-          if (v < ve) store_vec(a, scale_vec<DT>(keep[k], s64, s32));
-        }
+      for (int g = 0; g < kRegSteps / kUnroll; ++g) {
+        if ((uint32_t)(g * kUnroll) < nreg)
+          store_group(p, cur, vb, ve, js + g * kUnroll, js + nreg,
+                      [&](int u) { return scale_vec<DT>(keep[g * kUnroll + u], s64, s32); });
       }
       cur = cur_lds;
-      for (uint32_t k = 0; k < nlds; ++k) {
-        const uint64_t b = vb + (js + nreg + k) * kThreads, v = b + t;
-        const uint64_t a = step_addr(p, cur, b, ve, v);
-        if (v < ve) store_vec(a, scale_vec<DT>(keep_lds[k * kThreads + t], s64, s32));
-      }
+      for (uint32_t k0 = 0; k0 < nlds; k0 += kUnroll)
+        store_group(p, cur, vb, ve, js + nreg + k0, js + nreg + nlds,
+                    [&](int u) { return scale_vec<DT>(keep_lds[(k0 + u) * kThreads + t], s64, s32); });
       cur = cur0;
       scale_steps<DT>(p, cur, vb, ve, 0, js, s64, s32);
     }
@@ -436,9 +544,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   // workgroup gave up waiting at the barrier (then its share was not scaled).
   __syncthreads();
   if (t == 0) {
-    __threadfence();
     if (timed_out) __hip_atomic_fetch_or(&p.sync[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev = __hip_atomic_fetch_add(&p.sync[4], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    complete_stores();
+    const uint32_t prev = __hip_atomic_fetch_add(&p.sync[4], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == (uint32_t)p.nworkers - 1u) {
       const uint32_t lost = __hip_atomic_exchange(&p.sync[3], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       res->status = lost ? 1 : 0;

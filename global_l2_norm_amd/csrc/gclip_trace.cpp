@@ -34,28 +34,43 @@ struct Recorder {
   }
 };
 
-// One step of kThreads lanes: every lane starts from the same cursor and, the
-// loop being uniform, every lane must end on the same cursor.
-void replay_step(const DevPlan& p, Cursor& cur, uint64_t b, uint64_t ve, int32_t w, Recorder* rec) {
+// One group of up to kUnroll steps for all kThreads lanes: every lane starts
+// from the same cursor and, the cursor work being uniform, every lane must
+// end on the same cursor.
+void replay_group(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j, uint64_t j1, int32_t w,
+                  Recorder* rec) {
+  uint64_t base = 0;
+  const int kind = group_kind(cur, vb, ve, j, j1, base);
+  if (kind != kGroupCross) {
+    for (uint32_t t = 0; t < (uint32_t)kThreads; ++t)
+      for (int u = 0; u < kUnroll; ++u) {
+        const bool ok = kind == kGroupFull || tail_ok(vb, ve, j, j1, u, t);
+        if (kind == kGroupFull && !tail_ok(vb, ve, j, j1, u, t) && rec) rec->uniform_ok = false;
+        if (ok && rec) rec->put(w, base + ((uint64_t)u * kThreads + t) * kVecBytes);
+      }
+    return;
+  }
   Cursor end{};
-  for (int t = 0; t < kThreads; ++t) {
+  for (uint32_t t = 0; t < (uint32_t)kThreads; ++t) {
     Cursor c = cur;
-    const uint64_t v = b + (uint64_t)t;
-    const uint64_t a = step_addr(p, c, b, ve, v);
-    if (v < ve && rec) rec->put(w, a);
-    if (t == 0) end = c;
-    else if (c.s != end.s || c.beg != end.beg || c.end != end.end || c.addr != end.addr) {
+    uint64_t a[kUnroll];
+    bool ok[kUnroll];
+    cross_addrs(p, c, vb, ve, j, j1, t, a, ok);
+    if (rec)
+      for (int u = 0; u < kUnroll; ++u)
+        if (ok[u]) rec->put(w, a[u]);
+    if (t == 0) {
+      end = c;
+    } else if (c.s != end.s || c.beg != end.beg || c.end != end.end || c.addr != end.addr) {
       if (rec) rec->uniform_ok = false;
     }
   }
   cur = end;
 }
 
-void replay_steps(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j0, uint64_t j1, int32_t w,
-                  Recorder* rec) {
-  for (uint64_t j = j0; j < j1; j += kUnroll)
-    for (int u = 0; u < kUnroll; ++u)
-      if (j + u < j1) replay_step(p, cur, vb + (j + u) * kThreads, ve, w, rec);
+void replay_groups(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j0, uint64_t j1, int32_t w,
+                   Recorder* rec) {
+  for (uint64_t j = j0; j < j1; j += kUnroll) replay_group(p, cur, vb, ve, j, j1, w, rec);
 }
 
 }  // namespace
@@ -86,31 +101,31 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
         cursor_load(p, cur0, p.wk_seg[w]);
         if (mode <= 1) {  // k_grad_norm_partial / k_grad_scale
           Cursor cur = cur0;
-          replay_steps(p, cur, vb, ve, 0, (ve - vb + kThreads - 1) / kThreads, w, &rec);
+          replay_groups(p, cur, vb, ve, 0, (ve - vb + kThreads - 1) / kThreads, w, &rec);
         } else {  // k_grad_clip_fused, phase 1 (mode 2) or phase 2 (mode 3)
           const FusedSplit fs = fused_split(vb, ve);
           Recorder* r1 = mode == 2 ? &rec : nullptr;
+          Recorder* r2 = mode == 3 ? &rec : nullptr;
+          const uint64_t jr = fs.js + fs.nreg, jl = jr + fs.nlds;
           Cursor cur = cur0;
-          replay_steps(p, cur, vb, ve, 0, fs.js, w, r1);
+          replay_groups(p, cur, vb, ve, 0, fs.js, w, r1);
           Cursor cur_reg = cur;
           cursor_seek(p, cur_reg, vb + fs.js * kThreads);
           cur = cur_reg;
-          for (uint32_t k = 0; k < fs.nreg; ++k) replay_step(p, cur, vb + (fs.js + k) * kThreads, ve, w, r1);
+          for (int g = 0; g < kRegSteps / kUnroll; ++g)
+            if ((uint32_t)(g * kUnroll) < fs.nreg) replay_group(p, cur, vb, ve, fs.js + g * kUnroll, jr, w, r1);
           Cursor cur_lds = cur;
-          cursor_seek(p, cur_lds, vb + (fs.js + fs.nreg) * kThreads);
-          if (mode == 2) {
-            cur = cur_lds;
-            for (uint32_t k0 = 0; k0 < fs.nlds; k0 += kUnroll)
-              for (int u = 0; u < kUnroll; ++u)
-                if (k0 + u < fs.nlds) replay_step(p, cur, vb + (fs.js + fs.nreg + k0 + u) * kThreads, ve, w, &rec);
-          } else {
+          cursor_seek(p, cur_lds, vb + jr * kThreads);
+          cur = cur_lds;
+          replay_groups(p, cur, vb, ve, jr, jl, w, r1);
+          if (mode == 3) {
             cur = cur_reg;
-            for (uint32_t k = 0; k < fs.nreg; ++k) replay_step(p, cur, vb + (fs.js + k) * kThreads, ve, w, &rec);
+            for (int g = 0; g < kRegSteps / kUnroll; ++g)
+              if ((uint32_t)(g * kUnroll) < fs.nreg) replay_group(p, cur, vb, ve, fs.js + g * kUnroll, jr, w, r2);
             cur = cur_lds;
-            for (uint32_t k = 0; k < fs.nlds; ++k)
-              replay_step(p, cur, vb + (fs.js + fs.nreg + k) * kThreads, ve, w, &rec);
+            replay_groups(p, cur, vb, ve, jr, jl, w, r2);
             cur = cur0;
-            replay_steps(p, cur, vb, ve, 0, fs.js, w, &rec);
+            replay_groups(p, cur, vb, ve, 0, fs.js, w, r2);
           }
         }
       }

@@ -186,6 +186,17 @@ def andrea120m_f32_accum4(seed: int = 4, threads=None):
     return g
 
 
+def flat_f32(seed: int = 6, threads=None):
+    """The ANDREA-120M element count as one fp32 tensor (the same bytes with
+    no tensor boundaries), N(0, 1e-3^2), max_norm 1.0."""
+    n = sum(int(np.prod(s)) for _, s in shapes_andrea120m())
+    chunks = 16
+    sizes = [n // chunks + (1 if i < n % chunks else 0) for i in range(chunks)]
+    parts = _pool_map(lambda i: to_storage(_draw([seed, i], sizes[i], 1e-3), F32), list(range(chunks)),
+                      threads or _default_threads())
+    return GradSet("flat_f32", F32, ["flat"], [(n,)], [np.concatenate(parts)])
+
+
 NAN_TENSOR = "h23.W_2"
 NAN_INDEX = 1_234_567
 
@@ -224,6 +235,7 @@ CONFIGS = {
     "andrea120m_f16_small": andrea120m_f16_small,
     "andrea120m_f32_accum4": andrea120m_f32_accum4,
     "gpt1p3b_bf16": gpt1p3b_bf16,
+    "flat_f32": flat_f32,
 }
 
 
