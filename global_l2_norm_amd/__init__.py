@@ -19,7 +19,7 @@ from ._lib import (GCLIP_BF16, GCLIP_F16, GCLIP_F32, GCLIP_PATH_AUTO, GCLIP_PATH
                    GclipListInfo, GclipPlanEntry, GclipResult)
 
 __all__ = ["GclipError", "GclipResult", "GradList", "clip_grad_norm_", "gclip_list_create", "gclip_list_destroy",
-           "gclip_list_info", "gclip_list_set_path", "gclip_norm", "gclip_scale", "gclip_clip_",
+           "gclip_list_info", "gclip_list_set_path", "gclip_list_set_wait", "gclip_norm", "gclip_scale", "gclip_clip_",
            "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string", "gclip_version",
            "GCLIP_F32", "GCLIP_F16", "GCLIP_BF16", "GCLIP_PATH_AUTO", "GCLIP_PATH_FUSED", "GCLIP_PATH_SPLIT"]
 
@@ -63,6 +63,10 @@ def gclip_list_info(handle):
 
 def gclip_list_set_path(handle, path):
     _check(_lib.lib.gclip_list_set_path(handle, int(path)), "gclip_list_set_path")
+
+
+def gclip_list_set_wait(handle, microseconds):
+    _check(_lib.lib.gclip_list_set_wait(handle, int(microseconds)), "gclip_list_set_wait")
 
 
 def gclip_norm(handle, avg_factor, d_result, stream):
@@ -186,6 +190,9 @@ class GradList:
 
     def set_path(self, path):
         gclip_list_set_path(self.handle, path)
+
+    def set_wait(self, microseconds):
+        gclip_list_set_wait(self.handle, microseconds)
 
     def norm(self, avg_factor=1.0, stream=None):
         gclip_norm(self.handle, avg_factor, self.d_result, self._stream(stream))

@@ -23,12 +23,13 @@ class GclipResult(ctypes.Structure):
     _fields_ = [("sumsq", ctypes.c_double), ("norm", ctypes.c_double), ("scale", ctypes.c_double),
                 ("max_norm", ctypes.c_double), ("nonfinite", ctypes.c_int32), ("clipped", ctypes.c_int32),
                 ("skipped", ctypes.c_int32), ("decided", ctypes.c_int32), ("status", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3)]
+                ("handed_back", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
     def as_dict(self):
         return {"sumsq": self.sumsq, "norm": self.norm, "scale": self.scale, "max_norm": self.max_norm,
                 "nonfinite": bool(self.nonfinite), "clipped": bool(self.clipped), "skipped": bool(self.skipped),
-                "decided": bool(self.decided), "status": int(self.status)}
+                "decided": bool(self.decided), "status": int(self.status),
+                "handed_back": int(self.handed_back)}
 
 
 class GclipListInfo(ctypes.Structure):
@@ -56,6 +57,7 @@ def _declare(lib):
         "gclip_list_destroy": ([vp], i32),
         "gclip_list_info": ([vp, ctypes.POINTER(GclipListInfo)], i32),
         "gclip_list_set_path": ([vp, i32], i32),
+        "gclip_list_set_wait": ([vp, ctypes.c_int64], i32),
         "gclip_norm": ([vp, dbl, vp, vp], i32),
         "gclip_scale": ([vp, dbl, dbl, i32, vp, vp], i32),
         "gclip_clip_": ([vp, dbl, dbl, i32, vp, vp], i32),
@@ -94,6 +96,7 @@ def load():
 lib = load()
 
 # The C ABI's declared entry points (include/gclip.h), for the export check.
-EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_list_set_path", "gclip_norm",
+EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_list_set_path",
+           "gclip_list_set_wait", "gclip_norm",
            "gclip_scale", "gclip_clip_", "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string",
            "gclip_last_hip_error", "gclip_version")

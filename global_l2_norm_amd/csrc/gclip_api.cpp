@@ -8,6 +8,7 @@
 // allocate or synchronise; the hot calls only enqueue kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -19,14 +20,21 @@
 
 namespace gclip {
 int worker_threads();
-int64_t fused_resident_vectors_per_worker();
+uint64_t resident_cap_vectors();
+uint64_t chunk_vectors();
 hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result* res, hipStream_t st);
 hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
                         hipStream_t st);
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
-                        uint32_t epoch, hipStream_t st);
+                        uint32_t epoch, uint64_t wait_ticks, hipStream_t st);
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu);
 }  // namespace gclip
+
+// How long a workgroup of the fused kernel waits at the grid-wide decision
+// before it hands its block back.  On an idle device the last workgroup
+// arrives some tens of microseconds after the first.
+constexpr int64_t kDefaultWaitUs = 1000;
+constexpr int64_t kMaxWaitUs = 60 * 1000 * 1000;
 
 struct gclip_list {
   gclip::HostPlan plan;
@@ -36,6 +44,9 @@ struct gclip_list {
   bool fused_ok = false;
   int32_t path = GCLIP_PATH_SPLIT;
   uint32_t epoch = 0;
+  int64_t wait_us = kDefaultWaitUs;
+  uint64_t clock_khz = 0;  // device wall clock
+  uint64_t wait_ticks = 0;
 };
 
 namespace {
@@ -90,23 +101,32 @@ gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int3
   if (!n_out || cap < 0 || (cap > 0 && !out)) return GCLIP_EINVAL;
   try {
     gclip::HostPlan p;
-    const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, n_workers, worker_threads, p, nullptr);
+    const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, n_workers, worker_threads,
+                                     gclip::resident_cap_vectors(), gclip::chunk_vectors(), p, nullptr);
     if (rc != 0) return (gclip_status)rc;
     int64_t k = 0;
     auto emit = [&](int32_t w, int32_t t, int64_t b, int64_t c, int32_t kind) {
       if (k < cap) out[k] = gclip_plan_entry{w, t, b, c, kind, 0};
       ++k;
     };
-    for (int32_t w = 0; w < n_workers; ++w) {
-      const uint64_t vb = p.wk_vbegin[(size_t)w], ve = p.wk_vbegin[(size_t)w + 1];
-      for (int64_t s = p.wk_seg[(size_t)w]; vb < ve && s < p.nseg(); ++s) {
+    // the runs of the vector space [lo, hi) as (tensor, elements) pieces
+    auto emit_vectors = [&](int32_t w, uint64_t lo, uint64_t hi, int32_t kind) {
+      if (lo >= hi) return;
+      int64_t s = (int64_t)(std::upper_bound(p.seg_vbegin.begin(), p.seg_vbegin.end() - 1, lo) -
+                            p.seg_vbegin.begin()) - 1;
+      for (; s < p.nseg(); ++s) {
         const uint64_t sb = p.seg_vbegin[(size_t)s], se = p.seg_vbegin[(size_t)s + 1];
-        if (sb >= ve) break;
-        const uint64_t lo = vb > sb ? vb : sb, hi = ve < se ? ve : se;
-        if (lo >= hi) continue;
-        emit(w, p.seg_tensor[(size_t)s], p.seg_elem0[(size_t)s] + (int64_t)(lo - sb) * p.vec_elems,
-             (int64_t)(hi - lo) * p.vec_elems, 0);
+        if (sb >= hi) break;
+        const uint64_t a = lo > sb ? lo : sb, b = hi < se ? hi : se;
+        if (a >= b) continue;
+        emit(w, p.seg_tensor[(size_t)s], p.seg_elem0[(size_t)s] + (int64_t)(a - sb) * p.vec_elems,
+             (int64_t)(b - a) * p.vec_elems, kind);
       }
+    };
+    for (int32_t w = 0; w < n_workers; ++w) {
+      emit_vectors(w, p.shr_begin[(size_t)w], p.shr_begin[(size_t)w + 1], 3);
+      const uint64_t b = p.sb + (uint64_t)w * p.rb;
+      emit_vectors(w, b < p.nvec() ? b : p.nvec(), b + p.rb < p.nvec() ? b + p.rb : p.nvec(), 0);
       const uint64_t cb = p.wk_scbegin[(size_t)w], ce = p.wk_scbegin[(size_t)w + 1];
       for (uint64_t i = cb; i < ce;) {
         uint64_t j = i + 1;
@@ -114,6 +134,10 @@ gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int3
         emit(w, p.sc_tensor[i], p.sc_elem[i], (int64_t)(j - i), 1);
         i = j;
       }
+    }
+    for (uint64_t c = 0; c < p.nchunk(); ++c) {
+      const uint64_t b = c * p.cv;
+      emit_vectors(-1, b, b + p.cv < p.nvec() ? b + p.cv : p.nvec(), 2);
     }
     *n_out = k;
     return k > cap ? GCLIP_ERANGE : GCLIP_OK;
@@ -143,9 +167,9 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       delete L;
       return hip_fail(e);
     }
-    int ncu = 0, coop = 0;
+    int ncu = 0, clk = 0;
     if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, L->device)) != hipSuccess ||
-        (e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, L->device)) != hipSuccess) {
+        (e = hipDeviceGetAttribute(&clk, hipDeviceAttributeWallClockRate, L->device)) != hipSuccess) {
       delete L;
       return hip_fail(e);
     }
@@ -154,18 +178,21 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       delete L;
       return hip_fail(e);
     }
-    L->fused_ok = coop != 0 && bpc >= 1;
+    L->fused_ok = bpc >= 1 && clk > 0;
     L->path = L->fused_ok ? GCLIP_PATH_FUSED : GCLIP_PATH_SPLIT;
+    L->clock_khz = clk > 0 ? (uint64_t)clk : 0;
+    L->wait_ticks = (uint64_t)L->wait_us * L->clock_khz / 1000;
 
     const uint64_t* addrs = reinterpret_cast<const uint64_t*>(d_ptrs);
     std::string why;
-    const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, ncu, gclip::worker_threads(), L->plan, &why);
+    const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, ncu, gclip::worker_threads(),
+                                     gclip::resident_cap_vectors(), gclip::chunk_vectors(), L->plan, &why);
     if (rc != 0) {
       delete L;
       return (gclip_status)rc;
     }
     const gclip::HostPlan& P = L->plan;
-    const size_t nseg = (size_t)P.nseg(), nw = (size_t)P.nworkers, nsc = (size_t)P.nsc();
+    const size_t nseg = (size_t)P.nseg(), nw = (size_t)P.nworkers, nsc = (size_t)P.nsc(), nch = (size_t)P.nchunk();
     const size_t A = 256;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -173,9 +200,10 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       off = round_up(off + (bytes ? bytes : 8), A);
       return at;
     };
-    const size_t o_segv = take((nseg + 1) * 8), o_sega = take(nseg * 8), o_wkv = take((nw + 1) * 8),
-                 o_wks = take(nw * 4), o_wksc = take((nw + 1) * 8), o_sca = take(nsc * 8), o_part = take(nw * 8),
-                 o_bc = take(8), o_sync = take(8 * 4);
+    const size_t o_segv = take((nseg + 1) * 8), o_sega = take(nseg * 8), o_blk = take(nw * 4),
+                 o_shb = take((nw + 1) * 8), o_shs = take(nw * 4), o_chk = take(nch * 4), o_wksc = take((nw + 1) * 8),
+                 o_sca = take(nsc * 8), o_part = take(nw * 8), o_bc = take(8),
+                 o_sync = take((size_t)gclip::kSyncWords * 4), o_bst = take(nw * 4);
     if ((e = hipMalloc(&L->blob, off)) != hipSuccess) {
       delete L;
       g_last_hip = (int32_t)e;
@@ -187,8 +215,9 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       return hipMemcpy(b + o, src, bytes, hipMemcpyHostToDevice);
     };
     if ((e = hipMemset(L->blob, 0, off)) != hipSuccess || (e = up(o_segv, P.seg_vbegin.data(), (nseg + 1) * 8)) ||
-        (e = up(o_sega, P.seg_addr.data(), nseg * 8)) || (e = up(o_wkv, P.wk_vbegin.data(), (nw + 1) * 8)) ||
-        (e = up(o_wks, P.wk_seg.data(), nw * 4)) || (e = up(o_wksc, P.wk_scbegin.data(), (nw + 1) * 8)) ||
+        (e = up(o_sega, P.seg_addr.data(), nseg * 8)) || (e = up(o_blk, P.blk_seg.data(), nw * 4)) ||
+        (e = up(o_shb, P.shr_begin.data(), (nw + 1) * 8)) || (e = up(o_shs, P.shr_seg.data(), nw * 4)) ||
+        (e = up(o_chk, P.chk_seg.data(), nch * 4)) || (e = up(o_wksc, P.wk_scbegin.data(), (nw + 1) * 8)) ||
         (e = up(o_sca, P.sc_addr.data(), nsc * 8)) || (e = hipDeviceSynchronize()) != hipSuccess) {
       (void)hipFree(L->blob);
       delete L;
@@ -197,13 +226,21 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     gclip::DevPlan& D = L->dev;
     D.seg_vbegin = reinterpret_cast<const uint64_t*>(b + o_segv);
     D.seg_addr = reinterpret_cast<const uint64_t*>(b + o_sega);
-    D.wk_vbegin = reinterpret_cast<const uint64_t*>(b + o_wkv);
-    D.wk_seg = reinterpret_cast<const uint32_t*>(b + o_wks);
+    D.blk_seg = reinterpret_cast<const uint32_t*>(b + o_blk);
+    D.shr_begin = reinterpret_cast<const uint64_t*>(b + o_shb);
+    D.shr_seg = reinterpret_cast<const uint32_t*>(b + o_shs);
+    D.chk_seg = reinterpret_cast<const uint32_t*>(b + o_chk);
     D.wk_scbegin = reinterpret_cast<const uint64_t*>(b + o_wksc);
     D.sc_addr = reinterpret_cast<const uint64_t*>(b + o_sca);
     D.partials = reinterpret_cast<double*>(b + o_part);
     D.bcast = reinterpret_cast<double*>(b + o_bc);
     D.sync = reinterpret_cast<uint32_t*>(b + o_sync);
+    D.bstate = reinterpret_cast<uint32_t*>(b + o_bst);
+    D.nvec = P.nvec();
+    D.rb = P.rb;
+    D.sb = P.sb;
+    D.cv = P.cv;
+    D.nchunk = (uint32_t)nch;
     D.nworkers = P.nworkers;
     D.nseg = (int32_t)nseg;
     *out = L;
@@ -239,17 +276,8 @@ gclip_status gclip_list_info(const gclip_list* list, gclip_list_info_t* out) {
   out->worker_threads = P.threads;
   out->dtype = P.dtype;
   out->path = list->path;
-  int64_t res = 0;
-  if (list->path == GCLIP_PATH_FUSED) {
-    const int64_t cap = gclip::fused_resident_vectors_per_worker();
-    for (int32_t w = 0; w < P.nworkers; ++w) {
-      const int64_t n = (int64_t)(P.wk_vbegin[(size_t)w + 1] - P.wk_vbegin[(size_t)w]);
-      const int64_t steps = (n + P.threads - 1) / P.threads;
-      const int64_t rsteps = steps < cap / P.threads ? steps : cap / P.threads;
-      // resident steps are the last ones; the share's final step may be partial
-      res += rsteps == 0 ? 0 : n - (steps - rsteps) * P.threads;
-    }
-  }
+  // the fused kernel keeps every block on chip: the vectors from sb on
+  const int64_t res = list->path == GCLIP_PATH_FUSED ? (int64_t)(P.nvec() - P.sb) : 0;
   out->resident_vectors = res;
   return GCLIP_OK;
 }
@@ -265,6 +293,13 @@ gclip_status gclip_list_set_path(gclip_list* list, int32_t path) {
     case GCLIP_PATH_SPLIT: list->path = GCLIP_PATH_SPLIT; return GCLIP_OK;
     default: return GCLIP_EINVAL;
   }
+}
+
+gclip_status gclip_list_set_wait(gclip_list* list, int64_t microseconds) {
+  if (!list || microseconds < 0 || microseconds > kMaxWaitUs) return GCLIP_EINVAL;
+  list->wait_us = microseconds;
+  list->wait_ticks = (uint64_t)microseconds * list->clock_khz / 1000;
+  return GCLIP_OK;
 }
 
 gclip_status gclip_norm(gclip_list* list, double avg_factor, gclip_result* d_result, void* stream) {
@@ -296,7 +331,8 @@ gclip_status gclip_clip_(gclip_list* list, double max_norm, double avg_factor, i
   hipError_t e;
   if (list->path == GCLIP_PATH_FUSED) {
     if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
-    e = gclip::launch_fused(list->dev, list->plan.dtype, max_norm, avg_factor, err, d_result, list->epoch, s);
+    e = gclip::launch_fused(list->dev, list->plan.dtype, max_norm, avg_factor, err, d_result, list->epoch,
+                            list->wait_ticks, s);
   } else {
     e = gclip::launch_norm(list->dev, list->plan.dtype, avg_factor, d_result, s);
     if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg_factor, err, d_result, s);

@@ -26,14 +26,24 @@ namespace gclip {
 #ifndef GCLIP_LDS_STEPS
 #define GCLIP_LDS_STEPS 19
 #endif
+#ifndef GCLIP_CHUNK_STEPS
+#define GCLIP_CHUNK_STEPS 16
+#endif
+
 constexpr int kThreads = GCLIP_THREADS;     // threads per workgroup (8 waves, two per SIMD)
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = GCLIP_UNROLL;       // vectors in flight per lane in the streamed loops
 constexpr int kRegSteps = GCLIP_REG_STEPS;  // fused kernel: steps of kThreads vectors kept in VGPRs
 constexpr int kLdsSteps = GCLIP_LDS_STEPS;  // fused kernel: steps kept in LDS (kThreads * 16 B each)
+constexpr int kChunkSteps = GCLIP_CHUNK_STEPS;  // steps per claimed chunk
+// What the fused kernel keeps on chip per worker, and a chunk, in vectors.
+constexpr uint64_t kResidentCap = (uint64_t)(kRegSteps + kLdsSteps) * kThreads;
+constexpr uint64_t kChunkVectors = (uint64_t)kChunkSteps * kThreads;
 static_assert(kThreads % 64 == 0 && kThreads <= 1024, "whole waves, at most 1024 threads");
-static_assert((size_t)kLdsSteps * kThreads * 16 + 1024 <= 160 * 1024, "LDS of one workgroup on gfx950");
+static_assert((size_t)kLdsSteps * kThreads * 16 + (size_t)kThreads * 4 + 1024 <= 160 * 1024,
+              "LDS of one workgroup on gfx950");
 static_assert(kRegSteps % kUnroll == 0, "register steps come in whole groups");
+static_assert(kChunkSteps % kUnroll == 0, "chunks come in whole groups");
 
 struct Cursor {
   uint32_t s;
@@ -123,25 +133,54 @@ __host__ __device__ __forceinline__ void cross_addrs(const DevPlan& p, Cursor& c
   }
 }
 
-// How a worker's share splits in the fused kernel: streamed steps [0, js),
-// register steps [js, js + nreg), LDS steps [js + nreg, nsteps).  js is a
-// multiple of kUnroll (so every group starts at a multiple of kUnroll, as in
-// the other kernels) and the resident part is at most kRegSteps + kLdsSteps.
-struct FusedSplit {
-  uint64_t nsteps, js;
-  uint32_t nreg, nlds;
+// A run of the vector space [b, e) and the segment holding b.
+struct Range {
+  uint64_t b, e;
+  uint32_t seg;
 };
 
-__host__ __device__ __forceinline__ FusedSplit fused_split(uint64_t vb, uint64_t ve) {
-  FusedSplit f;
-  f.nsteps = (ve - vb + kThreads - 1) / kThreads;
-  const uint64_t cap = (uint64_t)(kRegSteps + kLdsSteps);
-  const uint64_t over = f.nsteps > cap ? f.nsteps - cap : 0;
-  f.js = (over + kUnroll - 1) / kUnroll * kUnroll;
-  if (f.js > f.nsteps) f.js = f.nsteps;
-  const uint64_t nres = f.nsteps - f.js;
-  f.nreg = nres < (uint64_t)kRegSteps ? (uint32_t)nres : (uint32_t)kRegSteps;
-  f.nlds = (uint32_t)(nres - f.nreg);
+__host__ __device__ __forceinline__ Range block_range(const DevPlan& p, int32_t w) {
+  Range r;
+  r.b = p.sb + (uint64_t)w * p.rb;
+  r.e = r.b + p.rb < p.nvec ? r.b + p.rb : p.nvec;
+  if (r.b > r.e) r.b = r.e;
+  r.seg = p.blk_seg[w];
+  return r;
+}
+
+__host__ __device__ __forceinline__ Range share_range(const DevPlan& p, int32_t w) {
+  Range r;
+  r.b = p.shr_begin[w];
+  r.e = p.shr_begin[w + 1];
+  r.seg = p.shr_seg[w];
+  return r;
+}
+
+// Chunk c cut at `end` (nvec for the scale kernel, sb for the fused kernel).
+__host__ __device__ __forceinline__ Range chunk_range(const DevPlan& p, uint32_t c, uint64_t end) {
+  Range r;
+  r.b = (uint64_t)c * p.cv;
+  r.e = r.b + p.cv < end ? r.b + p.cv : end;
+  r.seg = p.chk_seg[c];
+  return r;
+}
+
+__host__ __device__ __forceinline__ uint64_t range_steps(const Range& r) {
+  return (r.e - r.b + kThreads - 1) / kThreads;
+}
+
+// How a block splits in the fused kernel: register steps [0, nreg), LDS
+// steps [nreg, nsteps).  nreg is kRegSteps (a multiple of kUnroll) unless the
+// block is shorter, so every group starts at a multiple of kUnroll.
+struct BlockSplit {
+  uint32_t nsteps, nreg, nlds;
+};
+
+__host__ __device__ __forceinline__ BlockSplit block_split(const Range& r) {
+  BlockSplit f;
+  f.nsteps = (uint32_t)range_steps(r);
+  f.nreg = f.nsteps < (uint32_t)kRegSteps ? f.nsteps : (uint32_t)kRegSteps;
+  f.nlds = f.nsteps - f.nreg;
   return f;
 }
 

@@ -9,21 +9,30 @@
 // "Accumulation across microbatches") is folded in as the factor a.
 //
 // MI355X design:
-//   - one workgroup of kThreads per compute unit; worker w owns an equal
-//     share of the list's 16-byte vector space (gclip_plan.hpp), read with
-//     dwordx4 loads, kUnroll vectors in flight per lane;
-//   - squares are accumulated per lane in binary64: the square of an fp32,
-//     fp16 or bf16 value is exact there and the sum cannot overflow, so the
-//     sum is non-finite exactly when some element is NaN or +-Inf;
+//   - one workgroup of kThreads per compute unit.  For the sum of squares,
+//     worker w reads a fixed part of the list's 16-byte vector space
+//     (gclip_plan.hpp): an equal share of the streamed region and its block
+//     at the end of the space.  For scaling, which needs no partial sums, the
+//     workers claim chunks at run time from eight pools, one per XCD, so that
+//     the XCDs that stream faster take more of them.  Loads are dwordx4 with
+//     kUnroll vectors in flight per lane, the next group's loads issued
+//     before the current group is used;
+//   - each vector's squares are summed in fp32 and added into per-lane
+//     binary64 accumulators (vec_sumsq states when a vector is summed again
+//     in binary64), so the sum cannot overflow and is non-finite exactly when
+//     some element is NaN or +-Inf;
 //   - lane sums are reduced by an xor butterfly inside each wave and in wave
-//     order through LDS; per-worker partials are summed in worker order by
-//     whichever workgroup arrives last (an agent-scope ticket), so the bits
-//     of the norm do not depend on scheduling; cross-workgroup data moves
-//     only through agent-scope atomics (see complete_stores);
-//   - the fused kernel (cooperative launch, all workgroups resident) keeps
-//     the last kRegSteps + kLdsSteps steps of each worker's share in VGPRs and
-//     LDS across the grid-wide decision, so the scale pass writes those bytes
-//     without reading them again from HBM.
+//     order through LDS into one partial per worker; the partials are summed
+//     in index order by whichever workgroup arrives last (an agent-scope
+//     ticket), so the bits of the norm do not depend on scheduling and both
+//     paths give the same bits; cross-workgroup data moves only through
+//     agent-scope atomics (see complete_stores);
+//   - the fused kernel keeps each worker's block (up to kRegSteps +
+//     kLdsSteps steps) in VGPRs and LDS across the grid-wide decision, so the
+//     scale pass writes those bytes without reading them again from HBM; it
+//     is an ordinary launch whose waits are bounded (a workgroup that waits
+//     too long hands its block back to the others), so it cannot deadlock
+//     when other work holds some compute units.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -174,54 +183,12 @@ __device__ __forceinline__ void store_elem(uint64_t a, uint32_t bits) {
   else *reinterpret_cast<g_u16*>(a) = (uint16_t)bits;
 }
 
-// ---------------------------------------------------------------- reductions
-// Sum of v over the workgroup, the same bits in every thread.  Butterfly
-// inside each wave (a + b == b + a, so every lane holds the same sum), then
-// the wave sums in wave order.
-__device__ __forceinline__ double wg_sum(double v, double* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();  // red may still be read by a previous call
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  double t = red[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) t += red[i];
-  return t;
-}
-
 // A lane's total: its per-slot accumulators in slot order, then its single elements.
 __device__ __forceinline__ double lane_total(const double (&acc)[kUnroll], double accs) {
   double t = acc[0];
 #pragma unroll
   for (int u = 1; u < kUnroll; ++u) t += acc[u];
   return t + accs;
-}
-
-// Sum of the workers' partials in worker order (lane i takes i, i + kThreads, ...).
-__device__ __forceinline__ double partials_sum(const DevPlan& p, double* red) {
-  double v = 0.0;
-  for (int i = threadIdx.x; i < p.nworkers; i += kThreads)
-    v += __hip_atomic_load(&p.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return wg_sum(v, red);
-}
-
-struct Decision {
-  double s;
-  int clipped, skip;
-};
-
-// Grad clip lesson "Math" / glossary "Mechanism and details": unchanged when
-// norm <= c, factor c / norm when norm > c; times the averaging factor a.
-__device__ __forceinline__ Decision decide(double sumsq, int nonfinite, double max_norm, double avg, int err) {
-  Decision d;
-  const double norm = sqrt(sumsq);
-  d.clipped = norm > max_norm ? 1 : 0;
-  const double coef = d.clipped ? max_norm / norm : 1.0;
-  d.skip = (nonfinite && err) ? 1 : 0;
-  d.s = avg * coef;
-  return d;
 }
 
 // ---------------------------------------------------------------- group loads and stores
@@ -241,11 +208,18 @@ __device__ __forceinline__ void load_group(const DevPlan& p, Cursor& cur, uint64
     for (int u = 0; u < kUnroll; ++u)
       q[u] = tail_ok(vb, ve, j, j1, u, t) ? g[u * kThreads + t] : u32x4{0u, 0u, 0u, 0u};
   } else {
-    uint64_t a[kUnroll];
-    bool ok[kUnroll];
-    cross_addrs(p, cur, vb, ve, j, j1, t, a, ok);
+    // crossing group: walk the cursor step by step (the same walk as
+    // cross_addrs), each load issued as soon as its address is known
+    const uint64_t b0 = vb + j * kThreads;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) q[u] = ok[u] ? load_vec(a[u]) : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < kUnroll; ++u) {
+      q[u] = u32x4{0u, 0u, 0u, 0u};
+      if (j + u < j1) {
+        const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
+        const uint64_t a = step_addr(p, cur, b, ve, v);
+        if (v < ve) q[u] = load_vec(a);
+      }
+    }
   }
 }
 
@@ -267,28 +241,42 @@ __device__ __forceinline__ void store_group(const DevPlan& p, Cursor& cur, uint6
     for (int u = 0; u < kUnroll; ++u)
       if (tail_ok(vb, ve, j, j1, u, t)) g[u * kThreads + t] = f(u);
   } else {
-    uint64_t a[kUnroll];
-    bool ok[kUnroll];
-    cross_addrs(p, cur, vb, ve, j, j1, t, a, ok);
+    const uint64_t b0 = vb + j * kThreads;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (ok[u]) store_vec(a[u], f(u));
+    for (int u = 0; u < kUnroll; ++u) {
+      if (j + u < j1) {
+        const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
+        const uint64_t a = step_addr(p, cur, b, ve, v);
+        if (v < ve) store_vec(a, f(u));
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------- norm and scale passes
-// Streamed steps [j0, j1) of a worker's share, accumulating into acc.
-// Step j of a share always adds into acc[j % kUnroll]: groups start at
-// multiples of kUnroll in every kernel, so the norm kernel and the fused
-// kernel add the same values in the same order.
+// Steps [j0, j1) of the run [vb, ve), accumulating into acc.  Step j always
+// adds into acc[j % kUnroll] (groups start at multiples of kUnroll in every
+// kernel), so every kernel adds the same values in the same order.  The next
+// group's loads are issued before the current group is summed, so a lane
+// always has a full group of loads in flight.
 template <int DT>
 __device__ __forceinline__ void norm_steps(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j0,
                                            uint64_t j1, double (&acc)[kUnroll]) {
+  if (j0 >= j1) return;
+  u32x4 q[kUnroll];
+  load_group(p, cur, vb, ve, j0, j1, q);
   for (uint64_t j = j0; j < j1; j += kUnroll) {
-    u32x4 q[kUnroll];
-    load_group(p, cur, vb, ve, j, j1, q);
+    u32x4 q2[kUnroll];
+    if (j + kUnroll < j1) {
+      load_group(p, cur, vb, ve, j + kUnroll, j1, q2);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q2[u] = u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
   }
 }
 
@@ -300,8 +288,8 @@ __device__ __forceinline__ double norm_scalars(const DevPlan& p, int w) {
   return s;
 }
 
-// Streamed steps [j0, j1): read, multiply, write back.  The group's loads are
-// all issued before its first store.
+// Steps [j0, j1) of the run [vb, ve): read, multiply, write back.  A group's
+// loads are all issued before its first store.
 template <int DT>
 __device__ __forceinline__ void scale_steps(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j0,
                                             uint64_t j1, double s64, float s32) {
@@ -322,6 +310,154 @@ __device__ __forceinline__ void scale_scalars(const DevPlan& p, int w, double s6
   }
 }
 
+// ---------------------------------------------------------------- chunk claiming
+constexpr uint32_t kNone = 0xffffffffu;
+
+// Chunk c lives in pool c % kPools; pool q holds chunks q, q + kPools, ...
+// below nch.
+__device__ __forceinline__ uint32_t pool_size(uint32_t nch, uint32_t q) {
+  return q < nch ? (nch - q + kPools - 1) / kPools : 0u;
+}
+
+// Claim state of one workgroup, kept by its thread 0: the pool it draws from
+// (its own XCD's first) and how many pools it has found empty.
+struct Claimer {
+  uint32_t pool, dry;
+};
+
+// The next chunk for this workgroup, or kNone once every pool is empty.
+// Thread 0 only.  Each pool's counter only grows during a launch, so a pool
+// found empty stays empty.
+__device__ __forceinline__ uint32_t claim(uint32_t* pools, uint32_t nch, Claimer& cl) {
+  while (cl.dry < (uint32_t)kPools) {
+    const uint32_t q = cl.pool;
+    const uint32_t k = __hip_atomic_fetch_add(&pools[q * kSyncLineWords], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (k < pool_size(nch, q)) return q + k * (uint32_t)kPools;
+    cl.pool = (q + 1) % (uint32_t)kPools;
+    ++cl.dry;
+  }
+  return kNone;
+}
+
+__device__ __forceinline__ uint32_t* scale_pools(const DevPlan& p) { return p.sync + kSyncLineWords; }
+
+__device__ __forceinline__ void reset_pools(uint32_t* pools) {
+  for (int q = 0; q < kPools; ++q)
+    __hip_atomic_store(&pools[q * kSyncLineWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Claims run two chunks ahead: the chunk after next is claimed while the
+// current one streams and is handed over at the per-chunk barrier through
+// LDS slot i % 2 (a slot is rewritten only two barriers after it was read).
+struct ClaimSlots {
+  uint32_t claim[2];
+};
+
+// Scale in place every chunk below nch that this workgroup claims, each cut
+// at `end`.  The next chunk's first group is loaded before the current
+// chunk's last stores.
+template <int DT>
+__device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, uint32_t nch, uint64_t end,
+                                             double s64, float s32) {
+  const uint32_t t = threadIdx.x;
+  uint32_t* pools = scale_pools(p);
+  Claimer cl{blockIdx.x % (uint32_t)kPools, 0u};
+  if (t == 0) {
+    sl.claim[0] = claim(pools, nch, cl);
+    sl.claim[1] = claim(pools, nch, cl);
+  }
+  __syncthreads();
+  uint32_t c = sl.claim[0], cn = sl.claim[1];
+  __syncthreads();
+  Cursor cur;
+  u32x4 q[kUnroll];
+  if (c != kNone) {
+    const Range r = chunk_range(p, c, end);
+    cursor_load(p, cur, r.seg);
+    load_group(p, cur, r.b, r.e, 0, range_steps(r), q);
+  }
+  for (uint32_t i = 0; c != kNone; ++i) {
+    uint32_t cnn = kNone;
+    if (t == 0) cnn = claim(pools, nch, cl);
+    const Range r = chunk_range(p, c, end);
+    const uint64_t ns = range_steps(r);
+    Cursor cst;
+    cursor_load(p, cst, r.seg);
+    Cursor curn = cur;
+    for (uint64_t j = 0; j < ns; j += kUnroll) {
+      u32x4 q2[kUnroll];
+      if (j + kUnroll < ns) {
+        load_group(p, cur, r.b, r.e, j + kUnroll, ns, q2);
+      } else if (cn != kNone) {
+        const Range rn = chunk_range(p, cn, end);
+        cursor_load(p, curn, rn.seg);
+        load_group(p, curn, rn.b, rn.e, 0, range_steps(rn), q2);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) q2[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+      store_group(p, cst, r.b, r.e, j, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
+    }
+    const uint32_t par = i & 1u;
+    if (t == 0) sl.claim[par] = cnn;
+    __syncthreads();
+    c = cn;
+    cn = sl.claim[par];
+    cur = curn;
+  }
+}
+
+// Chunks that cover [0, end).
+__device__ __forceinline__ uint32_t chunks_below(const DevPlan& p, uint64_t end) {
+  return (uint32_t)((end + p.cv - 1) / p.cv);
+}
+
+// ---------------------------------------------------------------- reductions and the decision
+// Sum of v over the workgroup, the same bits in every thread.  Butterfly
+// inside each wave (a + b == b + a, so every lane holds the same sum), then
+// the wave sums in wave order.
+__device__ __forceinline__ double wg_sum(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();  // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  double t = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) t += red[i];
+  return t;
+}
+
+// Sum of the workers' partials in index order (lane i takes i, i + kThreads, ...).
+__device__ __forceinline__ double partials_sum(const DevPlan& p, double* red) {
+  double v = 0.0;
+  const uint32_t n = (uint32_t)p.nworkers;
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads)
+    v += __hip_atomic_load(&p.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return wg_sum(v, red);
+}
+
+struct Decision {
+  double s;
+  int clipped, skip;
+};
+
+// Grad clip lesson "Math" / glossary "Mechanism and details": unchanged when
+// norm <= c, factor c / norm when norm > c; times the averaging factor a.
+__device__ __forceinline__ Decision decide(double sumsq, int nonfinite, double max_norm, double avg, int err) {
+  Decision d;
+  const double norm = sqrt(sumsq);
+  d.clipped = norm > max_norm ? 1 : 0;
+  const double coef = d.clipped ? max_norm / norm : 1.0;
+  d.skip = (nonfinite && err) ? 1 : 0;
+  d.s = avg * coef;
+  return d;
+}
+
 __device__ __forceinline__ void write_norm(gclip_result* res, double S, double avg) {
   const double sumsq = (avg * avg) * S;
   res->sumsq = sumsq;
@@ -338,23 +474,23 @@ __device__ __forceinline__ void write_decision(gclip_result* res, const Decision
   res->decided = 1;
 }
 
-// Cross-workgroup data (per-workgroup partials, the decision, the counters)
-// is written and read only with agent-scope atomics, which go to the
-// device-coherent level of the memory system.  Waiting for those stores to
-// complete before the next atomic is issued orders them for every reader, so
-// no agent-scope fence is needed: on gfx950 such a fence writes back and
-// invalidates the whole L2 of the XCD, which costs ~18 us when 256
-// workgroups do it at the end of a pass.
+// Cross-workgroup data (partials, the decision, the counters) is written and
+// read only with agent-scope atomics, which go to the device-coherent level
+// of the memory system.  Waiting for those stores to complete before the
+// next atomic is issued orders them for every reader, so no agent-scope
+// fence is needed: on gfx950 such a fence writes back and invalidates the
+// whole L2 of the XCD, which costs ~18 us when 256 workgroups do it at the
+// end of a pass.
 __device__ __forceinline__ void complete_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Ticket: returns true in the last workgroup to arrive (all threads).
-__device__ __forceinline__ bool arrive(const DevPlan& p, int w, double part, int* flag) {
+// Ticket: returns true in the last workgroup to arrive (all threads).  The
+// caller's partials must already be stored (agent-scope atomics).
+__device__ __forceinline__ bool arrive(const DevPlan& p, int* flag) {
   if (threadIdx.x == 0) {
-    __hip_atomic_store(&p.partials[w], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     complete_stores();
     const uint32_t prev = __hip_atomic_fetch_add(&p.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = (prev == (uint32_t)p.nworkers - 1u) ? 1 : 0;
@@ -363,33 +499,128 @@ __device__ __forceinline__ bool arrive(const DevPlan& p, int w, double part, int
   return *flag != 0;
 }
 
+// Blocks handed back by the fused kernel.  Worker w's state word is kHeld
+// while w holds its block (or has written it), kHanded once w has stopped
+// waiting at the decision and left its block unscaled in memory, kTaken once
+// another workgroup has taken it over.  sync[3] counts the hand-backs.
+constexpr uint32_t kHeld = 0u, kHanded = 2u, kTaken = 3u;
+
+struct HandSlots {
+  uint32_t n;
+  uint32_t list[kThreads];
+};
+
+// Take over every block handed back so far and scale it from memory, with
+// the worker's single elements (whole workgroup).
+template <int DT>
+__device__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, float s32) {
+  for (uint32_t base = 0; base < (uint32_t)p.nworkers; base += kThreads) {
+    if (threadIdx.x == 0) hs.n = 0;
+    __syncthreads();
+    const uint32_t i = base + threadIdx.x;
+    if (i < (uint32_t)p.nworkers &&
+        __hip_atomic_load(&p.bstate[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kHanded) {
+      uint32_t expected = kHanded;
+      if (__hip_atomic_compare_exchange_strong(&p.bstate[i], &expected, kTaken, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        hs.list[atomicAdd(&hs.n, 1u)] = i;
+    }
+    __syncthreads();
+    const uint32_t n = hs.n;
+    for (uint32_t k = 0; k < n; ++k) {
+      const int v = (int)hs.list[k];
+      const Range r = block_range(p, v);
+      if (r.b < r.e) {
+        Cursor cur;
+        cursor_load(p, cur, r.seg);
+        scale_steps<DT>(p, cur, r.b, r.e, 0, range_steps(r), s64, s32);
+      }
+      scale_scalars<DT>(p, v, s64, s32);
+    }
+    __syncthreads();
+  }
+}
+
+// Second ticket, at the very end.  The last workgroup to finish -- every
+// other one has then left the pools and the block states alone -- resets the
+// scale pools and, after a fused launch, scales whatever blocks are still
+// handed back (the decision is published before the deciding workgroup
+// finishes, so it is known here), clears their states and records how many
+// workers handed their block back.
+template <int DT>
+__device__ void finish(const DevPlan& p, gclip_result* res, bool fused, HandSlots& hs, int* flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    complete_stores();
+    const uint32_t prev = __hip_atomic_fetch_add(&p.sync[4], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = (prev == (uint32_t)p.nworkers - 1u) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*flag == 0) return;
+  if (fused) {
+    const uint32_t handed = __hip_atomic_load(&p.sync[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (handed != 0u) {
+      const double s = __hip_atomic_load(&p.bcast[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t skip = __hip_atomic_load(&p.sync[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (skip == 0u && s != 1.0) take_handed_blocks<DT>(p, hs, s, (float)s);
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < (uint32_t)p.nworkers; i += kThreads)
+        __hip_atomic_store(&p.bstate[i], kHeld, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (threadIdx.x == 0) {
+      res->handed_back = (int32_t)handed;
+      __hip_atomic_store(&p.sync[3], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (threadIdx.x == 0) {
+    reset_pools(scale_pools(p));
+    __hip_atomic_store(&p.sync[4], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // After the last workgroup has summed the partials it overwrites them with
 // NaN, so a partial that was somehow read before it was written could only
 // ever show up as a NaN norm, never as a plausible wrong one.
 __device__ __forceinline__ void poison_partials(const DevPlan& p) {
-  for (int i = threadIdx.x; i < p.nworkers; i += kThreads)
+  const uint32_t n = (uint32_t)p.nworkers;
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads)
     __hip_atomic_store(&p.partials[i], __builtin_nan(""), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- kernels
-// Kernels 1 and 2 of the pages' pipeline: partial sums of squares, with the
-// final reduction folded into the last workgroup to arrive.
+// Worker w's partial sum of squares: its streamed share, then its block, then
+// its single elements, reduced over the workgroup.  The fused kernel adds the
+// same values in the same order, so both paths give the same bits.
+template <int DT>
+__device__ __forceinline__ void norm_share(const DevPlan& p, int w, double (&acc)[kUnroll]) {
+  const Range sh = share_range(p, w);
+  if (sh.b < sh.e) {
+    Cursor cur;
+    cursor_load(p, cur, sh.seg);
+    norm_steps<DT>(p, cur, sh.b, sh.e, 0, range_steps(sh), acc);
+  }
+}
+
+// Kernels 1 and 2 of the pages' pipeline: one partial sum of squares per
+// worker, with the final reduction folded into the last workgroup to arrive.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, double avg, gclip_result* res) {
   __shared__ double red[kWaves];
   __shared__ int flag;
   const int w = blockIdx.x;
-  const uint64_t vb = p.wk_vbegin[w], ve = p.wk_vbegin[w + 1];
   double acc[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
-  if (vb < ve) {
+  norm_share<DT>(p, w, acc);
+  const Range r = block_range(p, w);
+  if (r.b < r.e) {
     Cursor cur;
-    cursor_load(p, cur, p.wk_seg[w]);
-    norm_steps<DT>(p, cur, vb, ve, 0, (ve - vb + kThreads - 1) / kThreads, acc);
+    cursor_load(p, cur, r.seg);
+    norm_steps<DT>(p, cur, r.b, r.e, 0, range_steps(r), acc);
   }
   const double part = wg_sum(lane_total(acc, norm_scalars<DT>(p, w)), red);
-  if (arrive(p, w, part, &flag)) {
+  if (threadIdx.x == 0) __hip_atomic_store(&p.partials[w], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (arrive(p, &flag)) {
     const double S = partials_sum(p, red);
     poison_partials(p);
     if (threadIdx.x == 0) {
@@ -399,86 +630,87 @@ __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, doubl
       res->skipped = 0;
       res->decided = 0;
       res->status = 0;
+      res->handed_back = 0;
       __hip_atomic_store(&p.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// Kernel 3: the decision from the device result block, then g <- g * s, or
-// an immediate exit without a single write.
+// Kernel 3: the decision from the device result block, then g <- g * s over
+// the chunks each workgroup claims, or no write at all.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_norm, double avg, int err,
                                                          gclip_result* res) {
+  __shared__ ClaimSlots sl;
+  __shared__ HandSlots hs;
+  __shared__ int flag;
   const int w = blockIdx.x;
   const Decision d = decide(res->sumsq, res->nonfinite, max_norm, avg, err);
   if (w == 0 && threadIdx.x == 0) write_decision(res, d, max_norm);
-  if (d.skip || d.s == 1.0) return;
-  const double s64 = d.s;
-  const float s32 = (float)d.s;
-  const uint64_t vb = p.wk_vbegin[w], ve = p.wk_vbegin[w + 1];
-  if (vb < ve) {
-    Cursor cur;
-    cursor_load(p, cur, p.wk_seg[w]);
-    scale_steps<DT>(p, cur, vb, ve, 0, (ve - vb + kThreads - 1) / kThreads, s64, s32);
+  if (!(d.skip || d.s == 1.0)) {
+    const double s64 = d.s;
+    const float s32 = (float)d.s;
+    scale_chunks<DT>(p, sl, p.nchunk, p.nvec, s64, s32);
+    scale_scalars<DT>(p, w, s64, s32);
   }
-  scale_scalars<DT>(p, w, s64, s32);
+  finish<DT>(p, res, false, hs, &flag);
 }
 
-// The whole path in one cooperative launch.  Phase 1 reads the worker's
-// share once (the last resident steps into VGPRs and LDS), the last workgroup
-// to arrive reduces the partials and decides, and phase 2 scales: resident
-// steps are written straight from VGPRs/LDS, the rest is read again.
+// The whole path in one launch.  Phase 1 streams the worker's share and
+// reads its block into VGPRs and LDS; the last workgroup to arrive reduces
+// the partials and decides; phase 2 writes the block straight from
+// VGPRs/LDS, then reads, scales and writes the chunks of the streamed region
+// it claims.  The launch does not need every workgroup resident at once: a
+// workgroup that has waited wait_ticks (wall-clock ticks) for the decision
+// hands its block back and exits, freeing its compute unit for the
+// workgroups still to run, and the workgroups that do see the decision --
+// in the end the last one to finish -- scale the handed-back blocks from
+// memory.
 template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, double max_norm, double avg, int err,
-                                                                 gclip_result* res, uint32_t epoch) {
+                                                                 gclip_result* res, uint32_t epoch,
+                                                                 uint64_t wait_ticks) {
   __shared__ u32x4 keep_lds[kLdsSteps * kThreads];
   __shared__ double red[kWaves];
+  __shared__ ClaimSlots sl;
+  __shared__ HandSlots hs;
   __shared__ int flag;
-  __shared__ int timed_out;
+  __shared__ int gave_up;
+  __shared__ int handed;
   __shared__ double bc_s;
   __shared__ int bc_skip;
   const int w = blockIdx.x;
   const uint32_t t = threadIdx.x;
-  const uint64_t vb = p.wk_vbegin[w], ve = p.wk_vbegin[w + 1];
-  const FusedSplit fs = fused_split(vb, ve);
-  const uint64_t js = fs.js;      // streamed steps [0, js)
-  const uint32_t nreg = fs.nreg;  // register steps [js, js + nreg)
-  const uint32_t nlds = fs.nlds;  // LDS steps [js + nreg, nsteps)
 
   double acc[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+  norm_share<DT>(p, w, acc);
+  const Range r = block_range(p, w);
+  const BlockSplit bs = block_split(r);
   u32x4 keep[kRegSteps];
-  Cursor cur0, cur_reg, cur_lds;
-  if (vb < ve) {
-    cursor_load(p, cur0, p.wk_seg[w]);
-    Cursor cur = cur0;
-    norm_steps<DT>(p, cur, vb, ve, 0, js, acc);
-    cur_reg = cur;
-    cursor_seek(p, cur_reg, vb + js * kThreads);
-    cur = cur_reg;
+  if (r.b < r.e) {
+    Cursor cur;
+    cursor_load(p, cur, r.seg);
     // register steps: issue every load first, then accumulate in step order
 #pragma unroll
     for (int g = 0; g < kRegSteps / kUnroll; ++g) {
       u32x4 q[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) q[u] = u32x4{0u, 0u, 0u, 0u};
-      if ((uint32_t)(g * kUnroll) < nreg) load_group(p, cur, vb, ve, js + g * kUnroll, js + nreg, q);
+      if ((uint32_t)(g * kUnroll) < bs.nreg) load_group(p, cur, r.b, r.e, g * kUnroll, bs.nreg, q);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) keep[g * kUnroll + u] = q[u];
     }
 #pragma unroll
     for (int k = 0; k < kRegSteps; ++k)
-      if ((uint32_t)k < nreg) acc[k % kUnroll] += vec_sumsq<DT>(keep[k]);
-    cur_lds = cur;
-    cursor_seek(p, cur_lds, vb + (js + nreg) * kThreads);
-    cur = cur_lds;
-    for (uint32_t k0 = 0; k0 < nlds; k0 += kUnroll) {
+      if ((uint32_t)k < bs.nreg) acc[k % kUnroll] += vec_sumsq<DT>(keep[k]);
+    for (uint32_t k0 = 0; k0 < bs.nlds; k0 += kUnroll) {
       u32x4 q[kUnroll];
-      load_group(p, cur, vb, ve, js + nreg + k0, js + nreg + nlds, q);
+      load_group(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps, q);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        if (k0 + u < nlds) {
+        if (k0 + u < bs.nlds) {
           acc[u] += vec_sumsq<DT>(q[u]);
           keep_lds[(k0 + u) * kThreads + t] = q[u];
         }
@@ -486,10 +718,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
     }
   }
   const double part = wg_sum(lane_total(acc, norm_scalars<DT>(p, w)), red);
+  if (t == 0) __hip_atomic_store(&p.partials[w], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // grid-wide decision: the last workgroup to arrive reduces and releases
-  if (t == 0) timed_out = 0;
-  if (arrive(p, w, part, &flag)) {
+  if (t == 0) gave_up = 0;
+  if (arrive(p, &flag)) {
     const double S = partials_sum(p, red);
     poison_partials(p);
     if (t == 0) {
@@ -498,6 +731,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
       const Decision d = decide(sumsq, nonfinite, max_norm, avg, err);
       write_norm(res, S, avg);
       write_decision(res, d, max_norm);
+      res->status = 0;
       bc_s = d.s;
       bc_skip = d.skip;
       __hip_atomic_store(&p.bcast[0], d.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -507,57 +741,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
       __hip_atomic_store(&p.sync[1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else if (t == 0) {
-    uint32_t spins = 0;
+    const uint64_t t0 = wall_clock64();
     while (__hip_atomic_load(&p.sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
       __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) {
-        timed_out = 1;
+      if (wall_clock64() - t0 > wait_ticks) {
+        // hand the block back: its state is visible before the count
+        __hip_atomic_store(&p.bstate[w], kHanded, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        complete_stores();
+        __hip_atomic_fetch_add(&p.sync[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gave_up = 1;
         break;
       }
     }
-    bc_s = __hip_atomic_load(&p.bcast[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bc_skip = (int)__hip_atomic_load(&p.sync[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!gave_up) {
+      bc_s = __hip_atomic_load(&p.bcast[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bc_skip = (int)__hip_atomic_load(&p.sync[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __syncthreads();
   const double s64 = bc_s;
-  if (!timed_out && !bc_skip && s64 != 1.0) {
+  if (!gave_up && !bc_skip && s64 != 1.0) {
     const float s32 = (float)s64;
-    if (vb < ve) {
-      Cursor cur = cur_reg;
+    if (r.b < r.e) {
+      Cursor cur;
+      cursor_load(p, cur, r.seg);
 #pragma unroll
       for (int g = 0; g < kRegSteps / kUnroll; ++g) {
-        if ((uint32_t)(g * kUnroll) < nreg)
-          store_group(p, cur, vb, ve, js + g * kUnroll, js + nreg,
+        if ((uint32_t)(g * kUnroll) < bs.nreg)
+          store_group(p, cur, r.b, r.e, g * kUnroll, bs.nreg,
                       [&](int u) { return scale_vec<DT>(keep[g * kUnroll + u], s64, s32); });
       }
-      cur = cur_lds;
-      for (uint32_t k0 = 0; k0 < nlds; k0 += kUnroll)
-        store_group(p, cur, vb, ve, js + nreg + k0, js + nreg + nlds,
+      for (uint32_t k0 = 0; k0 < bs.nlds; k0 += kUnroll)
+        store_group(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps,
                     [&](int u) { return scale_vec<DT>(keep_lds[(k0 + u) * kThreads + t], s64, s32); });
-      cur = cur0;
-      scale_steps<DT>(p, cur, vb, ve, 0, js, s64, s32);
     }
+    scale_chunks<DT>(p, sl, chunks_below(p, p.sb), p.sb, s64, s32);
     scale_scalars<DT>(p, w, s64, s32);
+    if (t == 0) handed = (int)__hip_atomic_load(&p.sync[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (handed) take_handed_blocks<DT>(p, hs, s64, s32);
   }
-
-  // Second ticket: the last workgroup to finish records whether any
-  // workgroup gave up waiting at the barrier (then its share was not scaled).
-  __syncthreads();
-  if (t == 0) {
-    if (timed_out) __hip_atomic_fetch_or(&p.sync[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    complete_stores();
-    const uint32_t prev = __hip_atomic_fetch_add(&p.sync[4], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == (uint32_t)p.nworkers - 1u) {
-      const uint32_t lost = __hip_atomic_exchange(&p.sync[3], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      res->status = lost ? 1 : 0;
-      __hip_atomic_store(&p.sync[4], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  finish<DT>(p, res, true, hs, &flag);
 }
 
 // ---------------------------------------------------------------- host launchers
 int worker_threads() { return kThreads; }
-int64_t fused_resident_vectors_per_worker() { return (int64_t)(kRegSteps + kLdsSteps) * kThreads; }
+uint64_t resident_cap_vectors() { return kResidentCap; }
+uint64_t chunk_vectors() { return kChunkVectors; }
 
 hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result* res, hipStream_t st) {
   const dim3 grid((unsigned)p.nworkers), block(kThreads);
@@ -581,16 +811,26 @@ hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double
 }
 
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
-                        uint32_t epoch, hipStream_t st) {
-  DevPlan pc = p;
-  void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch};
-  const void* fn = dtype == GCLIP_F32   ? (const void*)k_grad_clip_fused<GCLIP_F32>
-                   : dtype == GCLIP_F16 ? (const void*)k_grad_clip_fused<GCLIP_F16>
-                                        : (const void*)k_grad_clip_fused<GCLIP_BF16>;
-  return hipLaunchCooperativeKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
+                        uint32_t epoch, uint64_t wait_ticks, hipStream_t st) {
+  const dim3 grid((unsigned)p.nworkers), block(kThreads);
+  switch (dtype) {
+    case GCLIP_F32:
+      hipLaunchKernelGGL(k_grad_clip_fused<GCLIP_F32>, grid, block, 0, st, p, max_norm, avg, err, res, epoch,
+                         wait_ticks);
+      break;
+    case GCLIP_F16:
+      hipLaunchKernelGGL(k_grad_clip_fused<GCLIP_F16>, grid, block, 0, st, p, max_norm, avg, err, res, epoch,
+                         wait_ticks);
+      break;
+    default:
+      hipLaunchKernelGGL(k_grad_clip_fused<GCLIP_BF16>, grid, block, 0, st, p, max_norm, avg, err, res, epoch,
+                         wait_ticks);
+      break;
+  }
+  return hipGetLastError();
 }
 
-// Workgroups of the fused kernel that fit on the device at once.
+// Workgroups of the fused kernel that fit on one compute unit at once.
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu) {
   const void* fn = dtype == GCLIP_F32   ? (const void*)k_grad_clip_fused<GCLIP_F32>
                    : dtype == GCLIP_F16 ? (const void*)k_grad_clip_fused<GCLIP_F16>

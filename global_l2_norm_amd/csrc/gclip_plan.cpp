@@ -52,10 +52,10 @@ int plan_validate(const uint64_t* addrs, const int64_t* numels, int32_t n, int32
 }
 
 int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
-               int32_t threads, HostPlan& out, std::string* why) {
+               int32_t threads, uint64_t resident_cap, uint64_t chunk_vectors, HostPlan& out, std::string* why) {
   const int rc = plan_validate(addrs, numels, n, dtype, why, nullptr, nullptr);
   if (rc != 0) return rc;
-  if (nworkers <= 0 || threads <= 0) {
+  if (nworkers <= 0 || threads <= 0 || chunk_vectors == 0) {
     if (why) *why = "non-positive launch shape";
     return 1;
   }
@@ -96,25 +96,34 @@ int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t 
     add_scalars(head + body * p.vec_elems, ne);
   }
 
-  // worker shares
+  // blocks at the end, equal static shares of the streamed region, chunks
   const uint64_t nv = p.nvec(), ns = p.nsc();
-  p.wk_vbegin.resize((size_t)nworkers + 1);
-  p.wk_scbegin.resize((size_t)nworkers + 1);
-  p.wk_seg.resize((size_t)nworkers);
-  for (int32_t w = 0; w <= nworkers; ++w) {
-    p.wk_vbegin[(size_t)w] = share_begin(nv, nworkers, w);
-    p.wk_scbegin[(size_t)w] = share_begin(ns, nworkers, w);
+  const uint64_t even = (nv + (uint64_t)nworkers - 1) / (uint64_t)nworkers;
+  p.rb = even < resident_cap ? even : resident_cap;
+  p.sb = nv > (uint64_t)nworkers * p.rb ? nv - (uint64_t)nworkers * p.rb : 0;
+  p.cv = chunk_vectors;
+  const uint64_t nchunk = (nv + p.cv - 1) / p.cv;
+  if (nchunk > 0xffffffffull) {
+    if (why) *why = "too many chunks";
+    return 1;
   }
+  // segment holding vector v (v < nv): last segment whose start is <= v
+  auto seg_of = [&](uint64_t v) -> uint32_t {
+    return (uint32_t)((std::upper_bound(p.seg_vbegin.begin(), p.seg_vbegin.end() - 1, v) - p.seg_vbegin.begin()) - 1);
+  };
+  p.blk_seg.assign((size_t)nworkers, 0);
+  p.shr_seg.assign((size_t)nworkers, 0);
+  p.shr_begin.resize((size_t)nworkers + 1);
+  for (int32_t w = 0; w <= nworkers; ++w) p.shr_begin[(size_t)w] = share_begin(p.sb, nworkers, w);
   for (int32_t w = 0; w < nworkers; ++w) {
-    const uint64_t vb = p.wk_vbegin[(size_t)w];
-    size_t s = 0;
-    if (p.nseg() > 0) {
-      // last segment whose start is <= vb
-      s = (size_t)(std::upper_bound(p.seg_vbegin.begin(), p.seg_vbegin.end() - 1, vb) - p.seg_vbegin.begin()) - 1;
-      if (s >= (size_t)p.nseg()) s = (size_t)p.nseg() - 1;
-    }
-    p.wk_seg[(size_t)w] = (uint32_t)s;
+    const uint64_t b = p.sb + (uint64_t)w * p.rb;
+    if (b < nv) p.blk_seg[(size_t)w] = seg_of(b);
+    if (p.shr_begin[(size_t)w] < p.shr_begin[(size_t)w + 1]) p.shr_seg[(size_t)w] = seg_of(p.shr_begin[(size_t)w]);
   }
+  p.chk_seg.resize((size_t)nchunk);
+  for (uint64_t c = 0; c < nchunk; ++c) p.chk_seg[(size_t)c] = seg_of(c * p.cv);
+  p.wk_scbegin.resize((size_t)nworkers + 1);
+  for (int32_t w = 0; w <= nworkers; ++w) p.wk_scbegin[(size_t)w] = share_begin(ns, nworkers, w);
   out = std::move(p);
   return 0;
 }

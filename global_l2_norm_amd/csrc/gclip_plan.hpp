@@ -10,10 +10,15 @@
 //     vectors; the segments are laid end to end into one vector space;
 //   - the unaligned head and tail elements of each tensor, and every element
 //     of a tensor whose aligned body is shorter than kMinSegVectors, go to a
-//     list of single elements ("scalars");
-//   - worker w (one workgroup) owns an equal share of the vector space and an
-//     equal share of the scalar list, so every worker moves the same bytes
-//     whatever the tensor sizes.
+//     list of single elements ("scalars"), shared out equally by worker;
+//   - the vector space ends with one "block" of rb vectors per worker
+//     (workgroup): what the fused kernel keeps on chip between its passes;
+//   - the rest, the streamed region [0, sb), is shared out equally for the
+//     summing pass, one static share per worker, so that every worker's
+//     partial sum has a fixed content and order;
+//   - for scaling, the region is cut into "chunks" of cv vectors that the
+//     workers claim at run time, so that the faster XCDs take more of them
+//     (scaling needs no partial sums, so who takes a chunk does not matter).
 #pragma once
 
 #include <cstdint>
@@ -41,8 +46,13 @@ struct HostPlan {
   std::vector<uint64_t> seg_addr;    // nseg: address of the segment's first vector
   std::vector<int32_t> seg_tensor;   // nseg
   std::vector<int64_t> seg_elem0;    // nseg: element index of the segment start in its tensor
-  std::vector<uint64_t> wk_vbegin;   // nworkers + 1
-  std::vector<uint32_t> wk_seg;      // nworkers: segment holding wk_vbegin[w]
+  uint64_t rb = 0;                   // vectors per block: worker w's is [sb + w rb, sb + (w + 1) rb) cut at nvec
+  uint64_t sb = 0;                   // end of the streamed region, start of the blocks
+  uint64_t cv = 0;                   // vectors per chunk: chunk c is [c cv, (c + 1) cv) cut at nvec
+  std::vector<uint32_t> blk_seg;     // nworkers: segment holding each block's first vector
+  std::vector<uint64_t> shr_begin;   // nworkers + 1: worker w's streamed share is [shr_begin[w], shr_begin[w + 1])
+  std::vector<uint32_t> shr_seg;     // nworkers: segment holding each share's first vector
+  std::vector<uint32_t> chk_seg;     // nchunk: segment holding each chunk's first vector
   std::vector<uint64_t> sc_addr;     // nsc: address of each single element
   std::vector<int32_t> sc_tensor;    // nsc
   std::vector<int64_t> sc_elem;      // nsc
@@ -51,6 +61,7 @@ struct HostPlan {
   int64_t nseg() const { return (int64_t)seg_addr.size(); }
   uint64_t nvec() const { return seg_vbegin.empty() ? 0 : seg_vbegin.back(); }
   uint64_t nsc() const { return (uint64_t)sc_addr.size(); }
+  uint64_t nchunk() const { return (uint64_t)chk_seg.size(); }  // chunks over the whole vector space
 };
 
 // Check a list: sizes >= 0, addresses non-NULL and aligned to the element
@@ -58,23 +69,35 @@ struct HostPlan {
 int plan_validate(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, std::string* why,
                   int64_t* n_elements, int64_t* n_bytes);
 
-// Validate a list and build its plan.  Returns a gclip_status code (0 = OK)
-// and, on failure, a short reason in *why.
+// Validate a list and build its plan for nworkers workgroups of `threads`
+// lanes: blocks of at most resident_cap vectors and chunks of chunk_vectors.
+// Returns a gclip_status code (0 = OK) and, on failure, a reason in *why.
 int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
-               int32_t threads, HostPlan& out, std::string* why);
+               int32_t threads, uint64_t resident_cap, uint64_t chunk_vectors, HostPlan& out, std::string* why);
 
 // Device view of a plan plus the list's workspace (all device addresses).
+// sync holds 128-byte lines of counters: line 0 the arrival ticket, epoch,
+// skip flag, count of handed-back blocks and finish ticket; lines 1..kPools
+// the chunk pools claimed while scaling (one pool per XCD).
+constexpr int kPools = 8;
+constexpr int kSyncLineWords = 32;  // 128 bytes
+constexpr int kSyncWords = kSyncLineWords * (1 + kPools);
+
 struct DevPlan {
   const uint64_t* seg_vbegin;
   const uint64_t* seg_addr;
-  const uint64_t* wk_vbegin;
-  const uint32_t* wk_seg;
+  const uint32_t* blk_seg;
+  const uint64_t* shr_begin;
+  const uint32_t* shr_seg;
+  const uint32_t* chk_seg;
   const uint64_t* wk_scbegin;
   const uint64_t* sc_addr;
-  double* partials;   // nworkers partial sums of g^2 (binary64)
+  double* partials;   // nworkers partial sums (share + block + single elements)
   double* bcast;      // [0]: factor decided inside the fused kernel
-  uint32_t* sync;     // [0] arrival ticket, [1] epoch released by the last arrival, [2] skip flag,
-                      // [3] barrier-timeout flag, [4] finish ticket (fused kernel)
+  uint32_t* sync;     // kSyncWords counters (see above)
+  uint32_t* bstate;   // nworkers: whether each block was handed back by the fused kernel
+  uint64_t nvec, rb, sb, cv;
+  uint32_t nchunk;    // chunks over [0, nvec); those below sb cover the streamed region
   int32_t nworkers;
   int32_t nseg;
 };

@@ -82,55 +82,61 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
     return GCLIP_EINVAL;
   try {
     HostPlan hp;
-    const int rc = plan_build(addrs, numels, n_tensors, dtype, n_workers, kThreads, hp, nullptr);
+    const int rc =
+        plan_build(addrs, numels, n_tensors, dtype, n_workers, kThreads, kResidentCap, kChunkVectors, hp, nullptr);
     if (rc != 0) return (gclip_status)rc;
     DevPlan p{};
     p.seg_vbegin = hp.seg_vbegin.data();
     p.seg_addr = hp.seg_addr.data();
-    p.wk_vbegin = hp.wk_vbegin.data();
-    p.wk_seg = hp.wk_seg.data();
+    p.blk_seg = hp.blk_seg.data();
+    p.shr_begin = hp.shr_begin.data();
+    p.shr_seg = hp.shr_seg.data();
+    p.chk_seg = hp.chk_seg.data();
     p.wk_scbegin = hp.wk_scbegin.data();
     p.sc_addr = hp.sc_addr.data();
+    p.nvec = hp.nvec();
+    p.rb = hp.rb;
+    p.sb = hp.sb;
+    p.cv = hp.cv;
+    p.nchunk = (uint32_t)hp.nchunk();
     p.nworkers = hp.nworkers;
     p.nseg = (int32_t)hp.nseg();
     Recorder rec{out_addr, out_worker, cap};
+    // claimed chunks below nch, cut at `end`: any worker, so reported as worker -1
+    auto replay_chunks = [&](uint32_t nch, uint64_t end) {
+      for (uint32_t c = 0; c < nch; ++c) {
+        const Range r = chunk_range(p, c, end);
+        Cursor cur;
+        cursor_load(p, cur, r.seg);
+        replay_groups(p, cur, r.b, r.e, 0, range_steps(r), -1, &rec);
+      }
+    };
     for (int32_t w = 0; w < p.nworkers; ++w) {
-      const uint64_t vb = p.wk_vbegin[w], ve = p.wk_vbegin[w + 1];
-      if (vb < ve) {
-        Cursor cur0;
-        cursor_load(p, cur0, p.wk_seg[w]);
-        if (mode <= 1) {  // k_grad_norm_partial / k_grad_scale
-          Cursor cur = cur0;
-          replay_groups(p, cur, vb, ve, 0, (ve - vb + kThreads - 1) / kThreads, w, &rec);
-        } else {  // k_grad_clip_fused, phase 1 (mode 2) or phase 2 (mode 3)
-          const FusedSplit fs = fused_split(vb, ve);
-          Recorder* r1 = mode == 2 ? &rec : nullptr;
-          Recorder* r2 = mode == 3 ? &rec : nullptr;
-          const uint64_t jr = fs.js + fs.nreg, jl = jr + fs.nlds;
-          Cursor cur = cur0;
-          replay_groups(p, cur, vb, ve, 0, fs.js, w, r1);
-          Cursor cur_reg = cur;
-          cursor_seek(p, cur_reg, vb + fs.js * kThreads);
-          cur = cur_reg;
+      if (mode == 0 || mode == 2) {  // the summing passes stream the worker's share first
+        const Range sh = share_range(p, w);
+        if (sh.b < sh.e) {
+          Cursor cur;
+          cursor_load(p, cur, sh.seg);
+          replay_groups(p, cur, sh.b, sh.e, 0, range_steps(sh), w, &rec);
+        }
+      }
+      const Range r = block_range(p, w);
+      if (r.b < r.e && mode != 1) {
+        Cursor cur;
+        cursor_load(p, cur, r.seg);
+        if (mode == 0) {  // k_grad_norm_partial: the block as streamed groups
+          replay_groups(p, cur, r.b, r.e, 0, range_steps(r), w, &rec);
+        } else {  // k_grad_clip_fused, either pass: register groups, then LDS groups
+          const BlockSplit bs = block_split(r);
           for (int g = 0; g < kRegSteps / kUnroll; ++g)
-            if ((uint32_t)(g * kUnroll) < fs.nreg) replay_group(p, cur, vb, ve, fs.js + g * kUnroll, jr, w, r1);
-          Cursor cur_lds = cur;
-          cursor_seek(p, cur_lds, vb + jr * kThreads);
-          cur = cur_lds;
-          replay_groups(p, cur, vb, ve, jr, jl, w, r1);
-          if (mode == 3) {
-            cur = cur_reg;
-            for (int g = 0; g < kRegSteps / kUnroll; ++g)
-              if ((uint32_t)(g * kUnroll) < fs.nreg) replay_group(p, cur, vb, ve, fs.js + g * kUnroll, jr, w, r2);
-            cur = cur_lds;
-            replay_groups(p, cur, vb, ve, jr, jl, w, r2);
-            cur = cur0;
-            replay_groups(p, cur, vb, ve, 0, fs.js, w, r2);
-          }
+            if ((uint32_t)(g * kUnroll) < bs.nreg) replay_group(p, cur, r.b, r.e, g * kUnroll, bs.nreg, w, &rec);
+          replay_groups(p, cur, r.b, r.e, bs.nreg, bs.nsteps, w, &rec);
         }
       }
       for (uint64_t i = p.wk_scbegin[w]; i < p.wk_scbegin[w + 1]; ++i) rec.put(w, p.sc_addr[i] | kElementTag);
     }
+    if (mode == 1) replay_chunks(p.nchunk, p.nvec);                                  // k_grad_scale
+    if (mode == 3) replay_chunks((uint32_t)((p.sb + p.cv - 1) / p.cv), p.sb);  // fused, second pass
     *n_out = rec.n;
     if (!rec.uniform_ok) return GCLIP_EINVAL;
     return rec.n > cap ? GCLIP_ERANGE : GCLIP_OK;

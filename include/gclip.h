@@ -69,9 +69,9 @@ typedef enum gclip_status {
 
 /* Which kernels gclip_clip_ uses (gclip_list_set_path). */
 typedef enum gclip_path {
-  GCLIP_PATH_AUTO = 0,  /* fused when the device supports cooperative launch, else split */
-  GCLIP_PATH_FUSED = 1, /* one cooperative kernel: norm, grid-wide decision, scale; part of each
-                           workgroup's slice stays in registers and LDS between the two passes */
+  GCLIP_PATH_AUTO = 0,  /* fused when its kernel fits on a compute unit, else split */
+  GCLIP_PATH_FUSED = 1, /* one kernel: norm, grid-wide decision, scale; each workgroup's block
+                           stays in registers and LDS between the two passes */
   GCLIP_PATH_SPLIT = 2  /* two kernels: partial sums with the final reduce folded into the last
                            workgroup, then the scale pass */
 } gclip_path;
@@ -91,8 +91,10 @@ typedef struct gclip_result {
   int32_t clipped;    /* 1 when norm > max_norm (NaN > c is false) */
   int32_t skipped;    /* 1 when nothing was written because nonfinite && error_if_nonfinite */
   int32_t decided;    /* 1 once a scale pass has made its decision; 0 after gclip_norm alone */
-  int32_t status;     /* 0, or a device-side failure code (a grid barrier that timed out) */
-  int32_t reserved[3];
+  int32_t status;     /* 0, or a device-side failure code */
+  int32_t handed_back; /* fused path: workgroups that stopped waiting at the grid-wide decision
+                          (gclip_list_set_wait); their blocks were scaled from memory by others */
+  int32_t reserved[2];
 } gclip_result;
 
 /* Summary of a list's descriptor table (gclip_list_info). */
@@ -111,8 +113,15 @@ typedef struct gclip_list_info_t {
 } gclip_list_info_t;
 
 /* One entry of a plan description (gclip_plan_query): a run of elements of
- * one tensor that one worker handles, either as 16-byte vectors (kind 0) or
- * element by element (kind 1). */
+ * one tensor, which is
+ *   kind 0  part of a worker's block of 16-byte vectors (read by the worker
+ *           in both summing passes; kept on chip by the fused kernel and
+ *           written back by the same worker),
+ *   kind 1  single elements of a worker (every pass),
+ *   kind 2  part of a chunk of 16-byte vectors that any worker may claim at
+ *           run time when scaling (worker -1; chunks cover the whole list,
+ *           the fused kernel uses those below the first block, cut there),
+ *   kind 3  part of a worker's streamed share (summing passes only). */
 typedef struct gclip_plan_entry {
   int32_t worker;
   int32_t tensor;
@@ -147,8 +156,18 @@ gclip_status gclip_list_destroy(gclip_list* list);
 gclip_status gclip_list_info(const gclip_list* list, gclip_list_info_t* out);
 
 /* Choose the kernels gclip_clip_ uses for this list (a gclip_path).  FUSED
- * on a device without cooperative launch returns GCLIP_EINVAL. */
+ * where its kernel cannot run returns GCLIP_EINVAL. */
 gclip_status gclip_list_set_path(gclip_list* list, int32_t path);
+
+/* The fused kernel is an ordinary launch, so its workgroups need not all be
+ * resident at once (other work may hold some compute units).  A workgroup
+ * that has waited `microseconds` at the grid-wide decision hands its block
+ * back and exits; the workgroups that see the decision then read that block
+ * again from memory and scale it.  The result is the same either way, only
+ * slower; result.handed_back counts such workgroups.  0 <= microseconds <=
+ * 60e6 (default 1000; 0 makes every workgroup but the deciding one hand its
+ * block back, which tests that path).  Host-only setting, no GPU work. */
+gclip_status gclip_list_set_wait(gclip_list* list, int64_t microseconds);
 
 /* Norm pass: sum of squares of a*g over the whole list, reduced to one
  * binary64 scalar on the device (grad clip lesson, section "ANDREA's
@@ -177,7 +196,7 @@ gclip_status gclip_scale(gclip_list* list, double max_norm, double avg_factor, i
                          gclip_result* d_result, void* stream);
 
 /* The whole path in place: gclip_norm followed by gclip_scale, as one
- * cooperative kernel (GCLIP_PATH_FUSED) or two launches (GCLIP_PATH_SPLIT).
+ * kernel (GCLIP_PATH_FUSED) or two launches (GCLIP_PATH_SPLIT).
  * Same arguments, same result block, same bits as the two calls. */
 gclip_status gclip_clip_(gclip_list* list, double max_norm, double avg_factor, int32_t error_if_nonfinite,
                          gclip_result* d_result, void* stream);
@@ -206,8 +225,9 @@ gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int3
  *   mode 0  norm kernel, 1  scale kernel,
  *        2  fused kernel, first pass, 3  fused kernel, second pass
  * Fills out_addr[i] (address of a 16-byte vector, or, with bit 63 set, of a
- * single element) and out_worker[i] for every lane access in visiting order;
- * n_out receives the count.  GCLIP_ERANGE when cap is too
+ * single element) and out_worker[i] for every lane access; accesses to
+ * chunks, which any worker may claim at run time, carry worker -1.  n_out
+ * receives the count.  GCLIP_ERANGE when cap is too
  * small; GCLIP_EINVAL when the lanes of a step disagree on the cursor. */
 gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* numels, int32_t n_tensors, int32_t dtype,
                               int32_t n_workers, int32_t mode, uint64_t* out_addr, int32_t* out_worker, int64_t cap,

@@ -88,20 +88,38 @@ def test_plan_covers_every_element_once(dtype, seed):
     addrs = fake_layout(rng, numels, es, misalign=bool(seed % 2))
     nw = int(rng.choice([1, 3, 7, 256]))
     entries = g.gclip_plan_query(addrs, numels, dtype, nw, 512)
-    cover = [np.zeros(n, dtype=np.int32) for n in numels]
-    vec_per_worker = np.zeros(nw, dtype=np.int64)
+    # the summing passes read blocks, shares and single elements; the scaling
+    # pass reads chunks and the same single elements
+    sum_cover = [np.zeros(n, dtype=np.int32) for n in numels]
+    scale_cover = [np.zeros(n, dtype=np.int32) for n in numels]
+    blk_vectors = np.zeros(nw, dtype=np.int64)
+    shr_vectors = np.zeros(nw, dtype=np.int64)
     sc_per_worker = np.zeros(nw, dtype=np.int64)
     for w, t, b, c, kind in entries:
-        assert 0 <= w < nw and c > 0
-        cover[t][b:b + c] += 1
-        if kind == 0:
+        assert c > 0 and kind in (0, 1, 2, 3)
+        assert (w == -1) == (kind == 2) and -1 <= w < nw
+        if kind != 2:
+            sum_cover[t][b:b + c] += 1
+        if kind in (1, 2):
+            scale_cover[t][b:b + c] += 1
+        if kind != 1:
             assert (addrs[t] + b * es) % 16 == 0 and (c * es) % 16 == 0
-            vec_per_worker[w] += c * es // 16
-        else:
+        if kind == 0:
+            blk_vectors[w] += c * es // 16
+        elif kind == 3:
+            shr_vectors[w] += c * es // 16
+        elif kind == 1:
             sc_per_worker[w] += c
-    for cv in cover:
+    for cv in sum_cover + scale_cover:
         assert np.all(cv == 1)
-    assert vec_per_worker.max() - vec_per_worker.min() <= 1
+    # blocks: equal, except that the last non-empty one may be cut short;
+    # streamed shares differ by at most one vector
+    full = blk_vectors[blk_vectors > 0]
+    if len(full) > 1:
+        assert np.all(full[:-1] == full[0]) and full[-1] <= full[0]
+    assert shr_vectors.max() - shr_vectors.min() <= 1
+    if shr_vectors.sum() > 0:  # a streamed region only once every block is full
+        assert np.all(blk_vectors == blk_vectors[0])
     assert sc_per_worker.max() - sc_per_worker.min() <= 1
 
 
@@ -118,7 +136,7 @@ def test_kernel_walk_stays_inside_and_covers_once(mode, dtype, seed):
     nw = [1, 3, 4, 8][seed]
     ta, tw = g.gclip_plan_trace(addrs, numels, dtype, nw, mode)
     check_walk(ta, addrs, numels, es)
-    assert tw.min() >= 0 and tw.max() < nw
+    assert tw.min() >= -1 and tw.max() < nw
 
 
 @pytest.mark.parametrize("mode", [0, 2, 3])

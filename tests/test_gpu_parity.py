@@ -454,3 +454,90 @@ def test_one_list_reused_on_new_data(path):
         else:
             gu.assert_bitwise_equal(out, new, f"call {k}")
     gl.close()
+
+
+# ------------------------------------------------------------------ the fused kernel's bounded wait
+def _clip_with_wait(arrays, dtype, max_norm, wait_us, err=False, calls=1):
+    G = _G()
+    ts = gu.upload(arrays, dtype)
+    gl = make_list(ts, "fused")
+    gl.set_wait(wait_us)
+    res = []
+    for _ in range(calls):
+        gl.clip_(max_norm, 1.0, err)
+        res.append(gl.read(err))
+    out = gu.download(ts, dtype)
+    gl.close()
+    return res, out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_handed_back_blocks_give_the_same_bits(dtype):
+    """With no wait at all, every workgroup but the deciding one hands its
+    block back; the blocks are then scaled from memory by others, with the
+    same result as the split path and the oracle."""
+    rng = np.random.default_rng(31)
+    arrays = ragged_arrays(rng, dtype, big=True)
+    arrays.append(gs.to_storage(rng.standard_normal(6_000_001) * 1e-3, dtype))
+    [(st, r)], out = _clip_with_wait(arrays, dtype, 0.5, 0)
+    assert st == 0 and r["status"] == 0
+    assert r["handed_back"] >= 1, r
+    _, r_split, out_split = gpu_clip(arrays, dtype, 0.5, path="split")
+    gu.assert_bitwise_equal(out, out_split, f"hand-back {dtype} vs split")
+    assert r["sumsq"] == r_split["sumsq"] and r["scale"] == r_split["scale"]
+    ro, ref = oracle_clip(arrays, dtype, 0.5)
+    gu.assert_norm_close(r["norm"], ro["norm"], "hand-back")
+    assert r["clipped"] == ro["clipped"] == 1
+    gu.assert_elems_close(out, ref, dtype, f"hand-back {dtype}")
+
+
+def test_hand_back_then_normal_wait_on_one_list():
+    """The block states are cleared after a launch with hand-backs: the next
+    calls on the same list (no wait, then the default wait) each scale
+    exactly once."""
+    import torch
+    G = _G()
+    rng = np.random.default_rng(32)
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-2, "f32") for n in (5_000_003, 777_777, 4099, 3)]
+    ts = gu.upload(arrays, "f32")
+    gl = make_list(ts, "fused")
+    cur = [a.copy() for a in arrays]
+    for k, wait in enumerate((0, 0, 1000, 0, 1000)):
+        gl.set_wait(wait)
+        gl.clip_(1.0)
+        st, r = gl.read()
+        ro, ref = oracle_clip(cur, "f32", 1.0)
+        out = gu.download(ts, "f32")
+        gu.assert_norm_close(r["norm"], ro["norm"], f"call {k}")
+        if ro["clipped"]:
+            gu.assert_elems_close(out, ref, "f32", f"call {k}")
+        # next call starts from a fresh random draw so that it clips again
+        cur = [gs.to_storage(rng.standard_normal(a.size) * 1e-2, "f32") for a in arrays]
+        for t, a in zip(ts, cur):
+            t.copy_(torch.from_numpy(a).to("cuda"))
+    gl.close()
+
+
+@pytest.mark.parametrize("err", [True, False])
+def test_hand_back_with_nothing_to_write(err):
+    """A NaN with error_if_nonfinite (skip) and a norm under the threshold
+    (factor 1) write nothing, also when blocks were handed back."""
+    rng = np.random.default_rng(33)
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-3, "bf16") for n in (4_000_000, 12345, 5)]
+    if err:
+        arrays[0][1_999_999] = 0x7fc0  # bf16 NaN
+    [(st, r)], out = _clip_with_wait(arrays, "bf16", 1e30, 0, err=err)
+    gu.assert_bitwise_equal(out, arrays, "nothing written")
+    assert r["skipped"] == (1 if err else 0) and r["scale"] == 1.0
+
+
+def test_set_wait_rejects_out_of_range():
+    G = _G()
+    ts = gu.upload([np.ones(100, dtype=np.float32)], "f32")
+    gl = G.GradList(ts)
+    for bad in (-1, 60_000_001):
+        with pytest.raises(G.GclipError):
+            gl.set_wait(bad)
+    gl.set_wait(0)
+    gl.set_wait(60_000_000)
+    gl.close()
