@@ -119,10 +119,12 @@ def main():
     ap.add_argument("--summarize-rocprof", nargs="+", metavar="ARG",
                     help="KIND OUT DIR...: KIND is 'trace' (a --kernel-trace --stats output dir) or 'pmc' "
                          "(FETCH_SIZE dir, then WRITE_SIZE dir); OUT is the summary file to write")
+    ap.add_argument("--rocprof-command", action="append", default=[],
+                    help="with --summarize-rocprof: the command that produced each output dir (repeatable)")
     a = ap.parse_args()
 
     if a.summarize_rocprof:
-        return summarize(a.summarize_rocprof, " ".join(sys.argv))
+        return summarize(a.summarize_rocprof, a.rocprof_command)
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus})",
               file=sys.stderr)
@@ -141,8 +143,9 @@ def main():
     esize = 4 if g.dtype == "f32" else 2
     tensors = upload(g.arrays, g.dtype)
     pristine = [t.clone() for t in tensors]
-    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-    flush.fill_(1)
+    # read-only flush: a sum over an int64 view (no cast, so no temporaries
+    # are written and no dirty lines are left to drain into the timed call)
+    flush = torch.ones((2 << 30) // 8, dtype=torch.int64, device="cuda")
     gl = G.GradList(tensors)
     if a.path != "auto":
         gl.set_path(G.GCLIP_PATH_FUSED if a.path == "fused" else G.GCLIP_PATH_SPLIT)
@@ -154,7 +157,7 @@ def main():
         for t, p in zip(tensors, pristine):
             t.copy_(p)
         if not a.no_flush:
-            flush.sum(dtype=torch.int64)
+            flush.sum()
 
     if a.profile_pass:
         # calibration for the PMC counters: an elementwise kernel that reads
@@ -162,7 +165,7 @@ def main():
         src = torch.full((CALIBRATION_BYTES // 4,), 3.0, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            flush.sum(dtype=torch.int64)
+            flush.sum()
             torch.neg(src, out=dst)
         for _ in range(max(a.steps, 1)):
             restore()
@@ -249,19 +252,35 @@ def _counter_rows(d):
         return list(csv.DictReader(f))
 
 
-def summarize(args, cmdline):
+def _short_kernel(name):
+    base = name.split("(")[0]
+    for k in ("k_grad_clip_fused", "k_grad_norm_partial", "k_grad_scale", "k_calib_copy", "k_flush_read"):
+        if k in base:
+            return base.replace("void ", "").strip()
+    if "neg_kernel" in name:
+        return "torch neg (elementwise, calibration copy)"
+    if "reduce_kernel" in base:
+        return "torch sum (reduce, cache flush)"
+    if "direct_copy_kernel" in name:
+        return "torch copy_ (elementwise, restore)"
+    return base.replace("void ", "").strip()[-60:]
+
+
+def summarize(args, commands):
     """Write a short text summary of rocprofv3 output into profiles/."""
     kind, out = args[0], args[1]
     dirs = args[2:]
-    lines = [f"# written by: python {cmdline}", f"kernel_source_sha256_16: {kernel_source_hash()}"]
+    lines = ["# summary of rocprofv3 output, written by: python bench.py --summarize-rocprof " + " ".join(args)]
+    for c in commands:
+        lines.append(f"# profiled command: {c}")
+    lines.append(f"kernel_source_sha256_16: {kernel_source_hash()}")
     if kind == "trace":
         rows = _stats_rows(dirs[0])
         lines.append("# rocprofv3 --kernel-trace --stats: per-kernel time (ns)")
-        lines.append(f"{'kernel':60s} {'calls':>6s} {'avg_ns':>12s} {'min_ns':>12s} {'max_ns':>12s} {'pct':>6s}")
+        lines.append(f"{'kernel':62s} {'calls':>6s} {'avg_ns':>12s} {'min_ns':>12s} {'max_ns':>12s} {'pct':>6s}")
         for r in rows:
-            name = r.get("Name", "")
-            short = name.split("(")[0][-60:]
-            lines.append(f"{short:60s} {r.get('Calls', ''):>6s} {float(r.get('AverageNs', 0)):12.1f} "
+            short = _short_kernel(r.get("Name", ""))[:62]
+            lines.append(f"{short:62s} {r.get('Calls', ''):>6s} {float(r.get('AverageNs', 0)):12.1f} "
                          f"{float(r.get('MinNs', 0)):12.1f} {float(r.get('MaxNs', 0)):12.1f} "
                          f"{float(r.get('Percentage', 0)):6.2f}")
     elif kind == "pmc":
@@ -273,7 +292,8 @@ def summarize(args, cmdline):
                 if r.get("Counter_Name", "") != counter:
                     continue
                 name = r.get("Kernel_Name", "")
-                key = ("clip" if "k_grad_clip_fused" in name else "copy" if "neg" in name.lower() else None)
+                key = ("clip" if "k_grad_clip_fused" in name else
+                       "copy" if ("neg_kernel" in name or "k_calib_copy" in name) else None)
                 if key is None:
                     continue
                 acc.setdefault(key, []).append(float(r["Counter_Value"]))
@@ -283,11 +303,13 @@ def summarize(args, cmdline):
         w_cal = per["WRITE_SIZE"]["copy"] * 1024 / copy_bytes
         fetch = per["FETCH_SIZE"]["clip"] * 1024 / f_cal
         write = per["WRITE_SIZE"]["clip"] * 1024 / w_cal
-        lines += ["# rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, median over dispatches)",
+        lines += ["# rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, median over dispatches);",
+                  "# each scaled by what the counter reads for a copy kernel that reads and writes",
+                  f"# exactly {CALIBRATION_BYTES} bytes",
                   f"fetch_kib_per_dispatch_clip: {per['FETCH_SIZE']['clip']:.1f}",
                   f"write_kib_per_dispatch_clip: {per['WRITE_SIZE']['clip']:.1f}",
-                  f"fetch_kib_per_dispatch_copy_369MB: {per['FETCH_SIZE']['copy']:.1f}",
-                  f"write_kib_per_dispatch_copy_369MB: {per['WRITE_SIZE']['copy']:.1f}",
+                  f"fetch_kib_per_dispatch_copy: {per['FETCH_SIZE']['copy']:.1f}",
+                  f"write_kib_per_dispatch_copy: {per['WRITE_SIZE']['copy']:.1f}",
                   f"fetch_calibration (counter bytes / copy bytes): {f_cal:.4f}",
                   f"write_calibration (counter bytes / copy bytes): {w_cal:.4f}",
                   f"hbm_fetch_bytes_per_dispatch: {fetch:.0f}",

@@ -20,8 +20,14 @@ namespace gclip {
 #ifndef GCLIP_UNROLL
 #define GCLIP_UNROLL 8
 #endif
+#ifndef GCLIP_NT_SUM
+#define GCLIP_NT_SUM 1
+#endif
+#ifndef GCLIP_NT_SCALE
+#define GCLIP_NT_SCALE 1
+#endif
 #ifndef GCLIP_REG_STEPS
-#define GCLIP_REG_STEPS 32
+#define GCLIP_REG_STEPS 40
 #endif
 #ifndef GCLIP_LDS_STEPS
 #define GCLIP_LDS_STEPS 19
