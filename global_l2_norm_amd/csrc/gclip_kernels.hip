@@ -58,8 +58,8 @@ typedef __attribute__((address_space(1))) uint16_t g_u16;
 // catch (the Infinity Cache does not keep read data between the passes), so
 // they are read with nontemporal loads, which stream through the caches
 // without displacing other lines: a cold 369 MB read ran about 10% faster
-// that way on MI355X.  Stores stay ordinary: nontemporal stores made the
-// read-modify-write passes markedly slower.  (Both kinds of load can be
+// that way on MI355X.  Stores stay ordinary: next to nontemporal loads,
+// nontemporal stores made the read-modify-write passes markedly slower.  (Both kinds of load can be
 // chosen per pass at build time.)
 constexpr bool kNtSum = GCLIP_NT_SUM != 0;
 constexpr bool kNtScale = GCLIP_NT_SCALE != 0;
