@@ -32,6 +32,9 @@ namespace gclip {
 #ifndef GCLIP_LDS_STEPS
 #define GCLIP_LDS_STEPS 19
 #endif
+#ifndef GCLIP_SUM_CHUNKS_PER_WORKER
+#define GCLIP_SUM_CHUNKS_PER_WORKER 1
+#endif
 #ifndef GCLIP_CHUNK_STEPS
 #define GCLIP_CHUNK_STEPS 16
 #endif
@@ -41,15 +44,41 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = GCLIP_UNROLL;       // vectors in flight per lane in the streamed loops
 constexpr int kRegSteps = GCLIP_REG_STEPS;  // fused kernel: steps of kThreads vectors kept in VGPRs
 constexpr int kLdsSteps = GCLIP_LDS_STEPS;  // fused kernel: steps kept in LDS (kThreads * 16 B each)
-constexpr int kChunkSteps = GCLIP_CHUNK_STEPS;  // steps per claimed chunk
+constexpr int kChunkSteps = GCLIP_CHUNK_STEPS;         // steps per claimed scale chunk
+constexpr int kSumChunksPerWorker = GCLIP_SUM_CHUNKS_PER_WORKER;  // sum chunks per worker (about)
 // What the fused kernel keeps on chip per worker, and a chunk, in vectors.
 constexpr uint64_t kResidentCap = (uint64_t)(kRegSteps + kLdsSteps) * kThreads;
 constexpr uint64_t kChunkVectors = (uint64_t)kChunkSteps * kThreads;
+constexpr uint64_t kGroupVectors = (uint64_t)kUnroll * kThreads;  // one group of kUnroll steps
 static_assert(kThreads % 64 == 0 && kThreads <= 1024, "whole waves, at most 1024 threads");
 static_assert((size_t)kLdsSteps * kThreads * 16 + (size_t)kThreads * 4 + 1024 <= 160 * 1024,
               "LDS of one workgroup on gfx950");
 static_assert(kRegSteps % kUnroll == 0, "register steps come in whole groups");
 static_assert(kChunkSteps % kUnroll == 0, "chunks come in whole groups");
+
+// Read of a descriptor table.  The tables never change while a kernel runs,
+// so on the device they are read through the constant address space: with a
+// workgroup-uniform index that is a scalar load, which the wave can wait for
+// without draining its vector loads (those complete in order, so waiting on
+// a vector load of the table would also wait for every gradient load issued
+// before it).
+template <typename T>
+__host__ __device__ __forceinline__ T ld_table(const T* p, uint64_t i) {
+#ifdef __HIP_DEVICE_COMPILE__
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+#else
+  return p[i];
+#endif
+}
+
+// A workgroup-uniform 32-bit value moved to a scalar register.
+__host__ __device__ __forceinline__ uint32_t uniform32(uint32_t x) {
+#ifdef __HIP_DEVICE_COMPILE__
+  return __builtin_amdgcn_readfirstlane(x);
+#else
+  return x;
+#endif
+}
 
 struct Cursor {
   uint32_t s;
@@ -58,9 +87,9 @@ struct Cursor {
 
 __host__ __device__ __forceinline__ void cursor_load(const DevPlan& p, Cursor& c, uint32_t s) {
   c.s = s;
-  c.beg = p.seg_vbegin[s];
-  c.end = p.seg_vbegin[s + 1];
-  c.addr = p.seg_addr[s];
+  c.beg = ld_table(p.seg_vbegin, s);
+  c.end = ld_table(p.seg_vbegin, (uint64_t)s + 1);
+  c.addr = ld_table(p.seg_addr, s);
 }
 
 // Move the (workgroup-uniform) cursor forward to the segment holding vector v.
@@ -96,10 +125,10 @@ __host__ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
 }
 
 // A group is the steps j .. j + kUnroll - 1 (capped at j1) of a worker's
-// share [vb, ve).  Three kinds:
+// run [vb, ve).  Three kinds:
 //   kGroupFull  inside the cursor's segment, every step whole: lane t's
 //               vector u is at base + (u * kThreads + t) * 16, no predicates;
-//   kGroupTail  inside the segment, but the share (or j1) ends in the group:
+//   kGroupTail  inside the segment, but the run (or j1) ends in the group:
 //               same addresses, vector u valid when tail_ok() says so;
 //   kGroupCross crosses a segment end: addresses from cross_addrs().
 // The first two leave the cursor where it is.
@@ -150,24 +179,25 @@ __host__ __device__ __forceinline__ Range block_range(const DevPlan& p, int32_t 
   r.b = p.sb + (uint64_t)w * p.rb;
   r.e = r.b + p.rb < p.nvec ? r.b + p.rb : p.nvec;
   if (r.b > r.e) r.b = r.e;
-  r.seg = p.blk_seg[w];
+  r.seg = ld_table(p.blk_seg, (uint64_t)w);
   return r;
 }
 
-__host__ __device__ __forceinline__ Range share_range(const DevPlan& p, int32_t w) {
-  Range r;
-  r.b = p.shr_begin[w];
-  r.e = p.shr_begin[w + 1];
-  r.seg = p.shr_seg[w];
-  return r;
-}
-
-// Chunk c cut at `end` (nvec for the scale kernel, sb for the fused kernel).
+// Scale chunk c cut at `end` (sb for the streamed region, nvec for the split scale kernel).
 __host__ __device__ __forceinline__ Range chunk_range(const DevPlan& p, uint32_t c, uint64_t end) {
   Range r;
   r.b = (uint64_t)c * p.cv;
   r.e = r.b + p.cv < end ? r.b + p.cv : end;
-  r.seg = p.chk_seg[c];
+  r.seg = ld_table(p.chk_seg, c);
+  return r;
+}
+
+// Sum chunk c (cut at sb).
+__host__ __device__ __forceinline__ Range sum_chunk_range(const DevPlan& p, uint32_t c) {
+  Range r;
+  r.b = (uint64_t)c * p.cvs;
+  r.e = r.b + p.cvs < p.sb ? r.b + p.cvs : p.sb;
+  r.seg = ld_table(p.sum_seg, c);
   return r;
 }
 

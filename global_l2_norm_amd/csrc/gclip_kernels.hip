@@ -9,24 +9,25 @@
 // "Accumulation across microbatches") is folded in as the factor a.
 //
 // MI355X design:
-//   - one workgroup of kThreads per compute unit.  For the sum of squares,
-//     worker w reads a fixed part of the list's 16-byte vector space
-//     (gclip_plan.hpp): an equal share of the streamed region and its block
-//     at the end of the space.  For scaling, which needs no partial sums, the
-//     workers claim chunks at run time from eight pools, one per XCD, so that
-//     the XCDs that stream faster take more of them.  Loads are dwordx4 with
-//     kUnroll vectors in flight per lane, the next group's loads issued
+//   - one workgroup of kThreads per compute unit.  The list's 16-byte
+//     vector space (gclip_plan.hpp) ends with one block per worker; the rest
+//     is cut into chunks that the workers claim at run time from eight
+//     pools, one per XCD, so that the XCDs that stream faster take more of
+//     them -- in the summing pass as in the scaling pass.  Loads are dwordx4
+//     with kUnroll vectors in flight per lane, the next group's loads issued
 //     before the current group is used;
 //   - each vector's squares are summed in fp32 and added into per-lane
 //     binary64 accumulators (vec_sumsq states when a vector is summed again
 //     in binary64), so the sum cannot overflow and is non-finite exactly when
 //     some element is NaN or +-Inf;
-//   - lane sums are reduced by an xor butterfly inside each wave and in wave
-//     order through LDS into one partial per worker; the partials are summed
-//     in index order by whichever workgroup arrives last (an agent-scope
-//     ticket), so the bits of the norm do not depend on scheduling and both
-//     paths give the same bits; cross-workgroup data moves only through
-//     agent-scope atomics (see complete_stores);
+//   - lane sums are reduced by an xor butterfly inside each wave into one
+//     partial per chunk and wave (a slot of the chunk's own), and over the
+//     workgroup into one partial per worker for its block; the last
+//     workgroup to arrive (a two-level agent-scope ticket) sums all partials
+//     in index order, so the bits of the norm do not depend on scheduling or
+//     on which workgroup took which chunk, and both paths give the same
+//     bits; cross-workgroup data moves only through agent-scope atomics (see
+//     complete_stores);
 //   - the fused kernel keeps each worker's block (up to kRegSteps +
 //     kLdsSteps steps) in VGPRs and LDS across the grid-wide decision, so the
 //     scale pass writes those bytes without reading them again from HBM; it
@@ -43,7 +44,6 @@
 
 namespace gclip {
 
-constexpr uint32_t kSpinLimit = 1u << 26;  // bounded wait at the grid barrier
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -58,9 +58,11 @@ typedef __attribute__((address_space(1))) uint16_t g_u16;
 // catch (the Infinity Cache does not keep read data between the passes), so
 // they are read with nontemporal loads, which stream through the caches
 // without displacing other lines: a cold 369 MB read ran about 10% faster
-// that way on MI355X.  Stores stay ordinary: next to nontemporal loads,
-// nontemporal stores made the read-modify-write passes markedly slower.  (Both kinds of load can be
-// chosen per pass at build time.)
+// that way on MI355X.  Stores are ordinary for lists below kNtStoreMinBytes
+// -- the 256 MB Infinity Cache then absorbs much of the write-back, and
+// nontemporal stores made a 369 MB scale pass 18% slower -- and nontemporal
+// for larger lists, whose writes only thrash it (3% faster at 2.6 GB).
+// (The load kind of each pass can be chosen at build time.)
 constexpr bool kNtSum = GCLIP_NT_SUM != 0;
 constexpr bool kNtScale = GCLIP_NT_SCALE != 0;
 
@@ -69,10 +71,15 @@ __device__ __forceinline__ u32x4 ld_vec(const g_u32x4* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
-__device__ __forceinline__ void st_vec(g_u32x4* p, u32x4 q) { *p = q; }
+template <bool NT>
+__device__ __forceinline__ void st_vec(g_u32x4* p, u32x4 q) {
+  if constexpr (NT) __builtin_nontemporal_store(q, p);
+  else *p = q;
+}
 template <bool NT>
 __device__ __forceinline__ u32x4 load_vec(uint64_t a) { return ld_vec<NT>(reinterpret_cast<const g_u32x4*>(a)); }
-__device__ __forceinline__ void store_vec(uint64_t a, u32x4 q) { st_vec(reinterpret_cast<g_u32x4*>(a), q); }
+template <bool NT>
+__device__ __forceinline__ void store_vec(uint64_t a, u32x4 q) { st_vec<NT>(reinterpret_cast<g_u32x4*>(a), q); }
 
 // ---------------------------------------------------------------- element arithmetic
 // Sum of the squares of one vector's elements, exact in binary64 for the
@@ -243,7 +250,7 @@ __device__ __forceinline__ void load_group(const DevPlan& p, Cursor& cur, uint64
 
 // Store f(vector u) for every vector of one group (the addresses of the
 // group are recomputed exactly as load_group computed them).
-template <typename F>
+template <bool NT, typename F>
 __device__ __forceinline__ void store_group(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j,
                                             uint64_t j1, F&& f) {
   const uint32_t t = threadIdx.x;
@@ -252,12 +259,12 @@ __device__ __forceinline__ void store_group(const DevPlan& p, Cursor& cur, uint6
   if (kind == kGroupFull) {
     g_u32x4* g = reinterpret_cast<g_u32x4*>(uniform64(base));
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) st_vec(&g[u * kThreads + t], f(u));
+    for (int u = 0; u < kUnroll; ++u) st_vec<NT>(&g[u * kThreads + t], f(u));
   } else if (kind == kGroupTail) {
     g_u32x4* g = reinterpret_cast<g_u32x4*>(uniform64(base));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (tail_ok(vb, ve, j, j1, u, t)) st_vec(&g[u * kThreads + t], f(u));
+      if (tail_ok(vb, ve, j, j1, u, t)) st_vec<NT>(&g[u * kThreads + t], f(u));
   } else {
     const uint64_t b0 = vb + j * kThreads;
 #pragma unroll
@@ -265,7 +272,7 @@ __device__ __forceinline__ void store_group(const DevPlan& p, Cursor& cur, uint6
       if (j + u < j1) {
         const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
         const uint64_t a = step_addr(p, cur, b, ve, v);
-        if (v < ve) store_vec(a, f(u));
+        if (v < ve) store_vec<NT>(a, f(u));
       }
     }
   }
@@ -301,7 +308,7 @@ __device__ __forceinline__ void norm_steps(const DevPlan& p, Cursor& cur, uint64
 template <int DT>
 __device__ __forceinline__ double norm_scalars(const DevPlan& p, int w) {
   double s = 0.0;
-  const uint64_t b = p.wk_scbegin[w], e = p.wk_scbegin[w + 1];
+  const uint64_t b = ld_table(p.wk_scbegin, (uint64_t)w), e = ld_table(p.wk_scbegin, (uint64_t)w + 1);
   for (uint64_t i = b + threadIdx.x; i < e; i += kThreads) s += elem_square<DT>(load_elem<DT>(p.sc_addr[i]));
   return s;
 }
@@ -315,17 +322,79 @@ __device__ __forceinline__ void scale_steps(const DevPlan& p, Cursor& cur, uint6
     u32x4 q[kUnroll];
     Cursor c2 = cur;
     load_group<kNtScale>(p, cur, vb, ve, j, j1, q);
-    store_group(p, c2, vb, ve, j, j1, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
+    store_group<false>(p, c2, vb, ve, j, j1, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
   }
 }
 
 template <int DT>
 __device__ __forceinline__ void scale_scalars(const DevPlan& p, int w, double s64, float s32) {
-  const uint64_t b = p.wk_scbegin[w], e = p.wk_scbegin[w + 1];
+  const uint64_t b = ld_table(p.wk_scbegin, (uint64_t)w), e = ld_table(p.wk_scbegin, (uint64_t)w + 1);
   for (uint64_t i = b + threadIdx.x; i < e; i += kThreads) {
     const uint64_t a = p.sc_addr[i];
     store_elem<DT>(a, scale_elem<DT>(load_elem<DT>(a), s64, s32));
   }
+}
+
+// ---------------------------------------------------------------- counters in the workspace
+// Cross-workgroup data (partials, the decision, the counters) is written and
+// read only with agent-scope atomics, which go to the device-coherent level
+// of the memory system.
+__device__ __forceinline__ uint32_t atomic_ld(const uint32_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_st(uint32_t* a, uint32_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_add(uint32_t* a, uint32_t v) {
+  return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double atomic_ld(const double* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_st(double* a, double v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Words of line 0 of sync.
+constexpr int kEpochWord = 0, kSkipWord = 1, kHandedWord = 2;
+
+__device__ __forceinline__ uint32_t* sum_pools(const DevPlan& p) { return p.sync + kSyncLineWords; }
+__device__ __forceinline__ uint32_t* scale_pools(const DevPlan& p) { return p.sync + (1 + kPools) * kSyncLineWords; }
+__device__ __forceinline__ uint32_t* arrival_tickets(const DevPlan& p) {
+  return p.sync + (1 + 2 * kPools) * kSyncLineWords;
+}
+__device__ __forceinline__ uint32_t* finish_tickets(const DevPlan& p) {
+  return p.sync + (2 + 3 * kPools) * kSyncLineWords;
+}
+
+// Waiting for this workgroup's stores to complete before its next atomic is
+// issued orders them for every reader, so no agent-scope fence is needed: on
+// gfx950 such a fence writes back and invalidates the whole L2 of the XCD,
+// which costs ~18 us when 256 workgroups do it at the end of a pass.
+__device__ __forceinline__ void complete_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Ticket over every workgroup of a launch, in two levels: workgroup w counts
+// in the line of its group w % kPools (its XCD: workgroups are dealt to the
+// XCDs in turn), the last of each group counts in the top line.  No counter
+// takes more than ~nworkers / kPools atomics at once.  True in exactly one
+// workgroup, the last to take the ticket.  The counter a workgroup completes
+// is reset by it for the next launch.  Thread 0 only; its stores must be
+// complete (complete_stores) before the call.
+__device__ __forceinline__ bool take_ticket(uint32_t* lines, int32_t nworkers) {
+  const uint32_t g = blockIdx.x % (uint32_t)kPools;
+  const uint32_t members = ((uint32_t)nworkers - g + kPools - 1) / kPools;
+  const uint32_t groups = nworkers < kPools ? (uint32_t)nworkers : (uint32_t)kPools;
+  uint32_t* mine = lines + g * kSyncLineWords;
+  uint32_t* top = lines + kPools * kSyncLineWords;
+  if (atomic_add(mine, 1u) != members - 1u) return false;
+  atomic_st(mine, 0u);
+  if (atomic_add(top, 1u) != groups - 1u) return false;
+  atomic_st(top, 0u);
+  return true;
 }
 
 // ---------------------------------------------------------------- chunk claiming
@@ -338,31 +407,51 @@ __device__ __forceinline__ uint32_t pool_size(uint32_t nch, uint32_t q) {
 }
 
 // Claim state of one workgroup, kept by its thread 0: the pool it draws from
-// (its own XCD's first) and how many pools it has found empty.
+// (its own XCD's first) and whether every pool has been found empty.
 struct Claimer {
-  uint32_t pool, dry;
+  uint32_t pool;
+  bool dry;
 };
 
-// The next chunk for this workgroup, or kNone once every pool is empty.
-// Thread 0 only.  Each pool's counter only grows during a launch, so a pool
-// found empty stays empty.
-__device__ __forceinline__ uint32_t claim(uint32_t* pools, uint32_t nch, Claimer& cl) {
-  while (cl.dry < (uint32_t)kPools) {
-    const uint32_t q = cl.pool;
-    const uint32_t k = __hip_atomic_fetch_add(&pools[q * kSyncLineWords], 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    if (k < pool_size(nch, q)) return q + k * (uint32_t)kPools;
-    cl.pool = (q + 1) % (uint32_t)kPools;
-    ++cl.dry;
+// A claim is taken in two steps: the ticket is drawn before a chunk streams
+// and turned into a chunk after it, so waiting for the counter's reply
+// overlaps the chunk's loads instead of draining them.  Thread 0 only.
+__device__ __forceinline__ uint32_t claim_issue(uint32_t* pools, const Claimer& cl) {
+  return cl.dry ? 0u : atomic_add(&pools[cl.pool * kSyncLineWords], 1u);
+}
+
+// The chunk of ticket tk (drawn on pool cl.pool), or, when that pool is
+// empty, a chunk of another pool: every pool's counter is read at once and a
+// pool that still has chunks is claimed from, until a claim succeeds or all
+// are empty (kNone).  Counters only grow during a launch, so a pool found
+// empty stays empty, and a failed claim leaves its pool empty: the loop ends
+// within kPools failures.
+__device__ __forceinline__ uint32_t claim_resolve(uint32_t* pools, uint32_t nch, Claimer& cl, uint32_t tk) {
+  if (cl.dry) return kNone;
+  if (tk < pool_size(nch, cl.pool)) return cl.pool + tk * (uint32_t)kPools;
+  for (int round = 0; round <= kPools; ++round) {
+    // the first pool after cl.pool, in circular order, that still has chunks
+    uint32_t pick = kNone, best = kPools;
+#pragma unroll
+    for (int q = 0; q < kPools; ++q) {
+      const uint32_t cnt = atomic_ld(&pools[q * kSyncLineWords]);
+      const uint32_t dist = ((uint32_t)q + 2u * kPools - cl.pool - 1u) % (uint32_t)kPools;
+      if (cnt < pool_size(nch, (uint32_t)q) && dist < best) {
+        best = dist;
+        pick = (uint32_t)q;
+      }
+    }
+    if (pick == kNone) break;
+    cl.pool = pick;
+    const uint32_t k2 = atomic_add(&pools[pick * kSyncLineWords], 1u);
+    if (k2 < pool_size(nch, pick)) return pick + k2 * (uint32_t)kPools;
   }
+  cl.dry = true;
   return kNone;
 }
 
-__device__ __forceinline__ uint32_t* scale_pools(const DevPlan& p) { return p.sync + kSyncLineWords; }
-
 __device__ __forceinline__ void reset_pools(uint32_t* pools) {
-  for (int q = 0; q < kPools; ++q)
-    __hip_atomic_store(&pools[q * kSyncLineWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int q = 0; q < kPools; ++q) atomic_st(&pools[q * kSyncLineWords], 0u);
 }
 
 // Claims run two chunks ahead: the chunk after next is claimed while the
@@ -372,22 +461,111 @@ struct ClaimSlots {
   uint32_t claim[2];
 };
 
-// Scale in place every chunk below nch that this workgroup claims, each cut
-// at `end`.  The next chunk's first group is loaded before the current
-// chunk's last stores.
-template <int DT>
-__device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, uint32_t nch, uint64_t end,
-                                             double s64, float s32) {
-  const uint32_t t = threadIdx.x;
-  uint32_t* pools = scale_pools(p);
-  Claimer cl{blockIdx.x % (uint32_t)kPools, 0u};
-  if (t == 0) {
-    sl.claim[0] = claim(pools, nch, cl);
-    sl.claim[1] = claim(pools, nch, cl);
+__device__ __forceinline__ void first_claims(uint32_t* pools, uint32_t nch, Claimer& cl, ClaimSlots& sl,
+                                             uint32_t& c, uint32_t& cn) {
+  if (threadIdx.x == 0) {
+    const uint32_t a = claim_resolve(pools, nch, cl, claim_issue(pools, cl));
+    sl.claim[0] = a;
+    sl.claim[1] = a == kNone ? kNone : claim_resolve(pools, nch, cl, claim_issue(pools, cl));
   }
   __syncthreads();
-  uint32_t c = sl.claim[0], cn = sl.claim[1];
+  c = uniform32(sl.claim[0]);
+  cn = uniform32(sl.claim[1]);
   __syncthreads();
+}
+
+// The chunk loops below draw the ticket for the chunk after next when a
+// chunk starts, before its later groups are loaded, and resolve it after the
+// chunk's last group has been waited for: loads and atomics complete in
+// order, so by then the ticket's reply is in and resolving it costs no wait.
+// Only then is the next chunk's first group loaded, so it stays in flight
+// across the chunk's barrier.  (Resolving after that load made the wave wait
+// for it too: every chunk ended with nothing in flight.)
+
+// Load the first group of scale chunk cn (cut at end), or zeros when there is none.
+template <bool NT>
+__device__ __forceinline__ void load_next_first(const DevPlan& p, Cursor& curn, uint32_t cn, uint64_t end,
+                                                u32x4 (&q)[kUnroll]) {
+  if (cn != kNone) {
+    const Range rn = chunk_range(p, cn, end);
+    cursor_load(p, curn, rn.seg);
+    load_group<NT>(p, curn, rn.b, rn.e, 0, range_steps(rn), q);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Sum every sum chunk of the streamed region [0, sb) that this workgroup claims.
+// Each wave reduces its lanes' sums over a chunk to one value and stores it
+// in the chunk's own slot, partials[c * kWaves + wave], so the final sum does
+// not depend on which workgroup took the chunk; the only barrier per chunk
+// hands the next claim to every wave.
+template <int DT>
+__device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
+  const uint32_t nch = p.nsum;
+  if (nch == 0) return;
+  const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+  uint32_t* pools = sum_pools(p);
+  Claimer cl{blockIdx.x % (uint32_t)kPools, false};
+  uint32_t c, cn;
+  first_claims(pools, nch, cl, sl, c, cn);
+  Cursor cur;
+  u32x4 q[kUnroll];
+  if (c != kNone) {
+    const Range r = sum_chunk_range(p, c);
+    cursor_load(p, cur, r.seg);
+    load_group<kNtSum>(p, cur, r.b, r.e, 0, range_steps(r), q);
+  }
+  for (uint32_t i = 0; c != kNone; ++i) {
+    const Range r = sum_chunk_range(p, c);
+    const uint64_t ns = range_steps(r);
+    uint32_t tk = 0;
+    if (t == 0 && cn != kNone) tk = claim_issue(pools, cl);
+    double acc[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+    for (uint64_t j = 0; j + kUnroll < ns; j += kUnroll) {
+      u32x4 q2[kUnroll];
+      load_group<kNtSum>(p, cur, r.b, r.e, j + kUnroll, ns, q2);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
+    const uint32_t par = i & 1u;
+    if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(pools, nch, cl, tk) : kNone;
+    Cursor curn;
+    if (cn != kNone) {
+      const Range rn = sum_chunk_range(p, cn);
+      cursor_load(p, curn, rn.seg);
+      load_group<kNtSum>(p, curn, rn.b, rn.e, 0, range_steps(rn), q);
+    }
+    double v = lane_total(acc, 0.0);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) atomic_st(&p.partials[(size_t)c * kWaves + wave], v);
+    __syncthreads();
+    c = cn;
+    cn = uniform32(sl.claim[par]);
+    cur = curn;
+  }
+}
+
+// Scale in place every chunk below nch that this workgroup claims, each cut
+// at `end`.  A chunk's last group is scaled into registers before the ticket
+// is resolved, and stored after it.
+template <int DT, bool NTS>
+__device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, uint32_t nch, uint64_t end,
+                                             double s64, float s32) {
+  if (nch == 0) return;
+  const uint32_t t = threadIdx.x;
+  uint32_t* pools = scale_pools(p);
+  Claimer cl{blockIdx.x % (uint32_t)kPools, false};
+  uint32_t c, cn;
+  first_claims(pools, nch, cl, sl, c, cn);
   Cursor cur;
   u32x4 q[kUnroll];
   if (c != kNone) {
@@ -396,41 +574,35 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, u
     load_group<kNtScale>(p, cur, r.b, r.e, 0, range_steps(r), q);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
-    uint32_t cnn = kNone;
-    if (t == 0) cnn = claim(pools, nch, cl);
     const Range r = chunk_range(p, c, end);
     const uint64_t ns = range_steps(r);
+    uint32_t tk = 0;
+    if (t == 0 && cn != kNone) tk = claim_issue(pools, cl);
     Cursor cst;
     cursor_load(p, cst, r.seg);
-    Cursor curn = cur;
-    for (uint64_t j = 0; j < ns; j += kUnroll) {
+    uint64_t j = 0;
+    for (; j + kUnroll < ns; j += kUnroll) {
       u32x4 q2[kUnroll];
-      if (j + kUnroll < ns) {
-        load_group<kNtScale>(p, cur, r.b, r.e, j + kUnroll, ns, q2);
-      } else if (cn != kNone) {
-        const Range rn = chunk_range(p, cn, end);
-        cursor_load(p, curn, rn.seg);
-        load_group<kNtScale>(p, curn, rn.b, rn.e, 0, range_steps(rn), q2);
-      } else {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) q2[u] = u32x4{0u, 0u, 0u, 0u};
-      }
-      store_group(p, cst, r.b, r.e, j, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
+      load_group<kNtScale>(p, cur, r.b, r.e, j + kUnroll, ns, q2);
+      store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = scale_vec<DT>(q[u], s64, s32);
     const uint32_t par = i & 1u;
-    if (t == 0) sl.claim[par] = cnn;
+    if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(pools, nch, cl, tk) : kNone;
+    store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return q[u]; });
+    Cursor curn;
+    u32x4 q2[kUnroll];
+    load_next_first<kNtScale>(p, curn, cn, end, q2);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
     __syncthreads();
     c = cn;
-    cn = sl.claim[par];
+    cn = uniform32(sl.claim[par]);
     cur = curn;
   }
-}
-
-// Chunks that cover [0, end).
-__device__ __forceinline__ uint32_t chunks_below(const DevPlan& p, uint64_t end) {
-  return (uint32_t)((end + p.cv - 1) / p.cv);
 }
 
 // ---------------------------------------------------------------- reductions and the decision
@@ -450,13 +622,28 @@ __device__ __forceinline__ double wg_sum(double v, double* red) {
   return t;
 }
 
-// Sum of the workers' partials in index order (lane i takes i, i + kThreads, ...).
+// Partials: one per wave per sum chunk, then one per worker.
+__device__ __forceinline__ uint32_t npartials(const DevPlan& p) {
+  return p.nsum * (uint32_t)kWaves + (uint32_t)p.nworkers;
+}
+__device__ __forceinline__ double* worker_partial(const DevPlan& p, int w) {
+  return p.partials + (size_t)p.nsum * kWaves + w;
+}
+
+// Sum of all partials in index order (lane i takes i, i + kThreads, ...).
 __device__ __forceinline__ double partials_sum(const DevPlan& p, double* red) {
   double v = 0.0;
-  const uint32_t n = (uint32_t)p.nworkers;
-  for (uint32_t i = threadIdx.x; i < n; i += kThreads)
-    v += __hip_atomic_load(&p.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t n = npartials(p);
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads) v += atomic_ld(&p.partials[i]);
   return wg_sum(v, red);
+}
+
+// After the last workgroup has summed the partials it overwrites them with
+// NaN, so a partial that was somehow read before it was written could only
+// ever show up as a NaN norm, never as a plausible wrong one.
+__device__ __forceinline__ void poison_partials(const DevPlan& p) {
+  const uint32_t n = npartials(p);
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads) atomic_st(&p.partials[i], __builtin_nan(""));
 }
 
 struct Decision {
@@ -492,26 +679,12 @@ __device__ __forceinline__ void write_decision(gclip_result* res, const Decision
   res->decided = 1;
 }
 
-// Cross-workgroup data (partials, the decision, the counters) is written and
-// read only with agent-scope atomics, which go to the device-coherent level
-// of the memory system.  Waiting for those stores to complete before the
-// next atomic is issued orders them for every reader, so no agent-scope
-// fence is needed: on gfx950 such a fence writes back and invalidates the
-// whole L2 of the XCD, which costs ~18 us when 256 workgroups do it at the
-// end of a pass.
-__device__ __forceinline__ void complete_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Ticket: returns true in the last workgroup to arrive (all threads).  The
-// caller's partials must already be stored (agent-scope atomics).
+// Arrival after the summing pass: true in the last workgroup (all threads).
+// The caller's partials must already be stored.
 __device__ __forceinline__ bool arrive(const DevPlan& p, int* flag) {
   if (threadIdx.x == 0) {
     complete_stores();
-    const uint32_t prev = __hip_atomic_fetch_add(&p.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (prev == (uint32_t)p.nworkers - 1u) ? 1 : 0;
+    *flag = take_ticket(arrival_tickets(p), p.nworkers) ? 1 : 0;
   }
   __syncthreads();
   return *flag != 0;
@@ -520,7 +693,8 @@ __device__ __forceinline__ bool arrive(const DevPlan& p, int* flag) {
 // Blocks handed back by the fused kernel.  Worker w's state word is kHeld
 // while w holds its block (or has written it), kHanded once w has stopped
 // waiting at the decision and left its block unscaled in memory, kTaken once
-// another workgroup has taken it over.  sync[3] counts the hand-backs.
+// another workgroup has taken it over.  Line 0's kHandedWord counts the
+// hand-backs.
 constexpr uint32_t kHeld = 0u, kHanded = 2u, kTaken = 3u;
 
 struct HandSlots {
@@ -531,13 +705,12 @@ struct HandSlots {
 // Take over every block handed back so far and scale it from memory, with
 // the worker's single elements (whole workgroup).
 template <int DT>
-__device__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, float s32) {
+__device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, float s32) {
   for (uint32_t base = 0; base < (uint32_t)p.nworkers; base += kThreads) {
     if (threadIdx.x == 0) hs.n = 0;
     __syncthreads();
     const uint32_t i = base + threadIdx.x;
-    if (i < (uint32_t)p.nworkers &&
-        __hip_atomic_load(&p.bstate[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kHanded) {
+    if (i < (uint32_t)p.nworkers && atomic_ld(&p.bstate[i]) == kHanded) {
       uint32_t expected = kHanded;
       if (__hip_atomic_compare_exchange_strong(&p.bstate[i], &expected, kTaken, __ATOMIC_RELAXED,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
@@ -566,70 +739,48 @@ __device__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, 
 // finishes, so it is known here), clears their states and records how many
 // workers handed their block back.
 template <int DT>
-__device__ void finish(const DevPlan& p, gclip_result* res, bool fused, HandSlots& hs, int* flag) {
+__device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool fused, HandSlots& hs, int* flag) {
   __syncthreads();
   if (threadIdx.x == 0) {
     complete_stores();
-    const uint32_t prev = __hip_atomic_fetch_add(&p.sync[4], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (prev == (uint32_t)p.nworkers - 1u) ? 1 : 0;
+    *flag = take_ticket(finish_tickets(p), p.nworkers) ? 1 : 0;
   }
   __syncthreads();
   if (*flag == 0) return;
   if (fused) {
-    const uint32_t handed = __hip_atomic_load(&p.sync[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t handed = atomic_ld(&p.sync[kHandedWord]);
     if (handed != 0u) {
-      const double s = __hip_atomic_load(&p.bcast[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t skip = __hip_atomic_load(&p.sync[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const double s = atomic_ld(&p.bcast[0]);
+      const uint32_t skip = atomic_ld(&p.sync[kSkipWord]);
       if (skip == 0u && s != 1.0) take_handed_blocks<DT>(p, hs, s, (float)s);
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < (uint32_t)p.nworkers; i += kThreads)
-        __hip_atomic_store(&p.bstate[i], kHeld, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t i = threadIdx.x; i < (uint32_t)p.nworkers; i += kThreads) atomic_st(&p.bstate[i], kHeld);
     }
     if (threadIdx.x == 0) {
       res->handed_back = (int32_t)handed;
-      __hip_atomic_store(&p.sync[3], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      atomic_st(&p.sync[kHandedWord], 0u);
     }
   }
-  if (threadIdx.x == 0) {
-    reset_pools(scale_pools(p));
-    __hip_atomic_store(&p.sync[4], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// After the last workgroup has summed the partials it overwrites them with
-// NaN, so a partial that was somehow read before it was written could only
-// ever show up as a NaN norm, never as a plausible wrong one.
-__device__ __forceinline__ void poison_partials(const DevPlan& p) {
-  const uint32_t n = (uint32_t)p.nworkers;
-  for (uint32_t i = threadIdx.x; i < n; i += kThreads)
-    __hip_atomic_store(&p.partials[i], __builtin_nan(""), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) reset_pools(scale_pools(p));
 }
 
 // ---------------------------------------------------------------- kernels
-// Worker w's partial sum of squares: its streamed share, then its block, then
-// its single elements, reduced over the workgroup.  The fused kernel adds the
-// same values in the same order, so both paths give the same bits.
-template <int DT>
-__device__ __forceinline__ void norm_share(const DevPlan& p, int w, double (&acc)[kUnroll]) {
-  const Range sh = share_range(p, w);
-  if (sh.b < sh.e) {
-    Cursor cur;
-    cursor_load(p, cur, sh.seg);
-    norm_steps<DT>(p, cur, sh.b, sh.e, 0, range_steps(sh), acc);
-  }
-}
-
-// Kernels 1 and 2 of the pages' pipeline: one partial sum of squares per
-// worker, with the final reduction folded into the last workgroup to arrive.
+// Kernels 1 and 2 of the pages' pipeline.  Partial sums of squares: the
+// chunks of the streamed region this workgroup claims (one partial per chunk
+// and wave), then worker w's block and single elements (one partial per
+// worker); the last workgroup to arrive sums every partial in index order.
+// The fused kernel adds the same values in the same order, so both paths
+// give the same bits.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, double avg, gclip_result* res) {
   __shared__ double red[kWaves];
+  __shared__ ClaimSlots sl;
   __shared__ int flag;
   const int w = blockIdx.x;
+  norm_chunks<DT>(p, sl);
   double acc[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
-  norm_share<DT>(p, w, acc);
   const Range r = block_range(p, w);
   if (r.b < r.e) {
     Cursor cur;
@@ -637,11 +788,12 @@ __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, doubl
     norm_steps<DT>(p, cur, r.b, r.e, 0, range_steps(r), acc);
   }
   const double part = wg_sum(lane_total(acc, norm_scalars<DT>(p, w)), red);
-  if (threadIdx.x == 0) __hip_atomic_store(&p.partials[w], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) atomic_st(worker_partial(p, w), part);
   if (arrive(p, &flag)) {
     const double S = partials_sum(p, red);
     poison_partials(p);
     if (threadIdx.x == 0) {
+      reset_pools(sum_pools(p));
       write_norm(res, S, avg);
       res->scale = 1.0;
       res->clipped = 0;
@@ -649,14 +801,13 @@ __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, doubl
       res->decided = 0;
       res->status = 0;
       res->handed_back = 0;
-      __hip_atomic_store(&p.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
 // Kernel 3: the decision from the device result block, then g <- g * s over
 // the chunks each workgroup claims, or no write at all.
-template <int DT>
+template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_norm, double avg, int err,
                                                          gclip_result* res) {
   __shared__ ClaimSlots sl;
@@ -668,23 +819,46 @@ __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_n
   if (!(d.skip || d.s == 1.0)) {
     const double s64 = d.s;
     const float s32 = (float)d.s;
-    scale_chunks<DT>(p, sl, p.nchunk, p.nvec, s64, s32);
+    scale_chunks<DT, NTS>(p, sl, p.nchunk, p.nvec, s64, s32);
     scale_scalars<DT>(p, w, s64, s32);
   }
   finish<DT>(p, res, false, hs, &flag);
 }
 
-// The whole path in one launch.  Phase 1 streams the worker's share and
-// reads its block into VGPRs and LDS; the last workgroup to arrive reduces
-// the partials and decides; phase 2 writes the block straight from
-// VGPRs/LDS, then reads, scales and writes the chunks of the streamed region
-// it claims.  The launch does not need every workgroup resident at once: a
-// workgroup that has waited wait_ticks (wall-clock ticks) for the decision
-// hands its block back and exits, freeing its compute unit for the
-// workgroups still to run, and the workgroups that do see the decision --
-// in the end the last one to finish -- scale the handed-back blocks from
-// memory.
-template <int DT>
+// Phase 2 of the fused kernel: the block straight from VGPRs and LDS, then
+// the scale chunks of the streamed region this workgroup claims.
+template <int DT, bool NTS>
+__device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSlots& sl, const Range& r,
+                                                       const BlockSplit& bs, const u32x4 (&keep)[kRegSteps],
+                                                       const u32x4* keep_lds, double s64, float s32) {
+  const uint32_t t = threadIdx.x;
+  if (r.b < r.e) {
+    Cursor cur;
+    cursor_load(p, cur, r.seg);
+#pragma unroll
+    for (int g = 0; g < kRegSteps / kUnroll; ++g) {
+      if ((uint32_t)(g * kUnroll) < bs.nreg)
+        store_group<NTS>(p, cur, r.b, r.e, g * kUnroll, bs.nreg,
+                         [&](int u) { return scale_vec<DT>(keep[g * kUnroll + u], s64, s32); });
+    }
+    for (uint32_t k0 = 0; k0 < bs.nlds; k0 += kUnroll)
+      store_group<NTS>(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps,
+                       [&](int u) { return scale_vec<DT>(keep_lds[(k0 + u) * kThreads + t], s64, s32); });
+  }
+  scale_chunks<DT, NTS>(p, sl, p.nchs, p.sb, s64, s32);
+}
+
+// The whole path in one launch.  Phase 1 sums the chunks of the streamed
+// region the workgroup claims, then reads its block into VGPRs and LDS; the
+// last workgroup to arrive reduces the partials and decides; phase 2 writes
+// the block straight from VGPRs/LDS, then reads, scales and writes the
+// chunks of the streamed region it claims.  The launch does not need every
+// workgroup resident at once: a workgroup that has waited wait_ticks
+// (wall-clock ticks) for the decision hands its block back and exits,
+// freeing its compute unit for the workgroups still to run, and the
+// workgroups that do see the decision -- in the end the last one to finish
+// -- scale the handed-back blocks from memory.
+template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, double max_norm, double avg, int err,
                                                                  gclip_result* res, uint32_t epoch,
                                                                  uint64_t wait_ticks) {
@@ -700,10 +874,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   const int w = blockIdx.x;
   const uint32_t t = threadIdx.x;
 
+  norm_chunks<DT>(p, sl);
   double acc[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
-  norm_share<DT>(p, w, acc);
   const Range r = block_range(p, w);
   const BlockSplit bs = block_split(r);
   u32x4 keep[kRegSteps];
@@ -736,7 +910,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
     }
   }
   const double part = wg_sum(lane_total(acc, norm_scalars<DT>(p, w)), red);
-  if (t == 0) __hip_atomic_store(&p.partials[w], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == 0) atomic_st(worker_partial(p, w), part);
 
   // grid-wide decision: the last workgroup to arrive reduces and releases
   if (t == 0) gave_up = 0;
@@ -752,50 +926,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
       res->status = 0;
       bc_s = d.s;
       bc_skip = d.skip;
-      __hip_atomic_store(&p.bcast[0], d.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.sync[2], (uint32_t)d.skip, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      reset_pools(sum_pools(p));
+      atomic_st(&p.bcast[0], d.s);
+      atomic_st(&p.sync[kSkipWord], (uint32_t)d.skip);
       complete_stores();
-      __hip_atomic_store(&p.sync[1], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      atomic_st(&p.sync[kEpochWord], epoch);
     }
   } else if (t == 0) {
     const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(&p.sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+    while (atomic_ld(&p.sync[kEpochWord]) != epoch) {
       __builtin_amdgcn_s_sleep(2);
       if (wall_clock64() - t0 > wait_ticks) {
         // hand the block back: its state is visible before the count
-        __hip_atomic_store(&p.bstate[w], kHanded, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        atomic_st(&p.bstate[w], kHanded);
         complete_stores();
-        __hip_atomic_fetch_add(&p.sync[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        atomic_add(&p.sync[kHandedWord], 1u);
         gave_up = 1;
         break;
       }
     }
     if (!gave_up) {
-      bc_s = __hip_atomic_load(&p.bcast[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bc_skip = (int)__hip_atomic_load(&p.sync[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bc_s = atomic_ld(&p.bcast[0]);
+      bc_skip = (int)atomic_ld(&p.sync[kSkipWord]);
     }
   }
   __syncthreads();
   const double s64 = bc_s;
   if (!gave_up && !bc_skip && s64 != 1.0) {
     const float s32 = (float)s64;
-    if (r.b < r.e) {
-      Cursor cur;
-      cursor_load(p, cur, r.seg);
-#pragma unroll
-      for (int g = 0; g < kRegSteps / kUnroll; ++g) {
-        if ((uint32_t)(g * kUnroll) < bs.nreg)
-          store_group(p, cur, r.b, r.e, g * kUnroll, bs.nreg,
-                      [&](int u) { return scale_vec<DT>(keep[g * kUnroll + u], s64, s32); });
-      }
-      for (uint32_t k0 = 0; k0 < bs.nlds; k0 += kUnroll)
-        store_group(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps,
-                    [&](int u) { return scale_vec<DT>(keep_lds[(k0 + u) * kThreads + t], s64, s32); });
-    }
-    scale_chunks<DT>(p, sl, chunks_below(p, p.sb), p.sb, s64, s32);
+    write_block_and_chunks<DT, NTS>(p, sl, r, bs, keep, keep_lds, s64, s32);
     scale_scalars<DT>(p, w, s64, s32);
-    if (t == 0) handed = (int)__hip_atomic_load(&p.sync[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == 0) handed = (int)atomic_ld(&p.sync[kHandedWord]);
     __syncthreads();
     if (handed) take_handed_blocks<DT>(p, hs, s64, s32);
   }
@@ -806,6 +967,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
 int worker_threads() { return kThreads; }
 uint64_t resident_cap_vectors() { return kResidentCap; }
 uint64_t chunk_vectors() { return kChunkVectors; }
+uint32_t sum_chunks_per_worker() { return (uint32_t)kSumChunksPerWorker; }
+uint64_t group_vectors() { return kGroupVectors; }
 
 hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result* res, hipStream_t st) {
   const dim3 grid((unsigned)p.nworkers), block(kThreads);
@@ -817,43 +980,44 @@ hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result
   return hipGetLastError();
 }
 
+// Kernel of dtype DT with ordinary (NTS false) or nontemporal stores.
+template <bool NTS>
+const void* scale_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_grad_scale<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_grad_scale<GCLIP_F16, NTS>
+                              : (const void*)k_grad_scale<GCLIP_BF16, NTS>;
+}
+template <bool NTS>
+const void* fused_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_grad_clip_fused<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_grad_clip_fused<GCLIP_F16, NTS>
+                              : (const void*)k_grad_clip_fused<GCLIP_BF16, NTS>;
+}
+
 hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
                         hipStream_t st) {
-  const dim3 grid((unsigned)p.nworkers), block(kThreads);
-  switch (dtype) {
-    case GCLIP_F32: hipLaunchKernelGGL(k_grad_scale<GCLIP_F32>, grid, block, 0, st, p, max_norm, avg, err, res); break;
-    case GCLIP_F16: hipLaunchKernelGGL(k_grad_scale<GCLIP_F16>, grid, block, 0, st, p, max_norm, avg, err, res); break;
-    default: hipLaunchKernelGGL(k_grad_scale<GCLIP_BF16>, grid, block, 0, st, p, max_norm, avg, err, res); break;
-  }
-  return hipGetLastError();
+  DevPlan pc = p;
+  void* args[] = {&pc, &max_norm, &avg, &err, &res};
+  const void* fn = p.nt_store ? scale_kernel<true>(dtype) : scale_kernel<false>(dtype);
+  return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }
 
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
                         uint32_t epoch, uint64_t wait_ticks, hipStream_t st) {
-  const dim3 grid((unsigned)p.nworkers), block(kThreads);
-  switch (dtype) {
-    case GCLIP_F32:
-      hipLaunchKernelGGL(k_grad_clip_fused<GCLIP_F32>, grid, block, 0, st, p, max_norm, avg, err, res, epoch,
-                         wait_ticks);
-      break;
-    case GCLIP_F16:
-      hipLaunchKernelGGL(k_grad_clip_fused<GCLIP_F16>, grid, block, 0, st, p, max_norm, avg, err, res, epoch,
-                         wait_ticks);
-      break;
-    default:
-      hipLaunchKernelGGL(k_grad_clip_fused<GCLIP_BF16>, grid, block, 0, st, p, max_norm, avg, err, res, epoch,
-                         wait_ticks);
-      break;
-  }
-  return hipGetLastError();
+  DevPlan pc = p;
+  void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch, &wait_ticks};
+  const void* fn = p.nt_store ? fused_kernel<true>(dtype) : fused_kernel<false>(dtype);
+  return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }
 
-// Workgroups of the fused kernel that fit on one compute unit at once.
+// Workgroups of the fused kernel that fit on one compute unit at once (the
+// smaller of its two store variants).
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu) {
-  const void* fn = dtype == GCLIP_F32   ? (const void*)k_grad_clip_fused<GCLIP_F32>
-                   : dtype == GCLIP_F16 ? (const void*)k_grad_clip_fused<GCLIP_F16>
-                                        : (const void*)k_grad_clip_fused<GCLIP_BF16>;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kThreads, 0);
+  int a = 0, b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, fused_kernel<false>(dtype), kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fused_kernel<true>(dtype), kThreads, 0);
+  *blocks_per_cu = a < b ? a : b;
+  return e;
 }
 
 }  // namespace gclip

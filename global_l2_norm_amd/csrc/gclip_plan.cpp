@@ -52,10 +52,11 @@ int plan_validate(const uint64_t* addrs, const int64_t* numels, int32_t n, int32
 }
 
 int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
-               int32_t threads, uint64_t resident_cap, uint64_t chunk_vectors, HostPlan& out, std::string* why) {
+               int32_t threads, uint64_t resident_cap, uint64_t chunk_vectors, uint32_t sum_chunks_per_worker,
+               uint64_t group_vectors, HostPlan& out, std::string* why) {
   const int rc = plan_validate(addrs, numels, n, dtype, why, nullptr, nullptr);
   if (rc != 0) return rc;
-  if (nworkers <= 0 || threads <= 0 || chunk_vectors == 0) {
+  if (nworkers <= 0 || threads <= 0 || chunk_vectors == 0 || sum_chunks_per_worker == 0 || group_vectors == 0) {
     if (why) *why = "non-positive launch shape";
     return 1;
   }
@@ -96,14 +97,23 @@ int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t 
     add_scalars(head + body * p.vec_elems, ne);
   }
 
-  // blocks at the end, equal static shares of the streamed region, chunks
+  // blocks at the end, chunks over the whole space
   const uint64_t nv = p.nvec(), ns = p.nsc();
   const uint64_t even = (nv + (uint64_t)nworkers - 1) / (uint64_t)nworkers;
   p.rb = even < resident_cap ? even : resident_cap;
   p.sb = nv > (uint64_t)nworkers * p.rb ? nv - (uint64_t)nworkers * p.rb : 0;
   p.cv = chunk_vectors;
+  // sum chunks: about sum_chunks_per_worker per worker, in whole groups of
+  // steps (each chunk boundary costs the streaming loop a partial drain, so
+  // fewer, larger chunks are faster as long as the workers stay balanced)
+  {
+    const uint64_t want = (uint64_t)nworkers * sum_chunks_per_worker;
+    const uint64_t per = (p.sb + want - 1) / want;
+    p.cvs = (per + group_vectors - 1) / group_vectors * group_vectors;
+    if (p.cvs == 0) p.cvs = group_vectors;
+  }
   const uint64_t nchunk = (nv + p.cv - 1) / p.cv;
-  if (nchunk > 0xffffffffull) {
+  if (nchunk > 0xffffffffull / 64) {
     if (why) *why = "too many chunks";
     return 1;
   }
@@ -112,16 +122,19 @@ int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t 
     return (uint32_t)((std::upper_bound(p.seg_vbegin.begin(), p.seg_vbegin.end() - 1, v) - p.seg_vbegin.begin()) - 1);
   };
   p.blk_seg.assign((size_t)nworkers, 0);
-  p.shr_seg.assign((size_t)nworkers, 0);
-  p.shr_begin.resize((size_t)nworkers + 1);
-  for (int32_t w = 0; w <= nworkers; ++w) p.shr_begin[(size_t)w] = share_begin(p.sb, nworkers, w);
   for (int32_t w = 0; w < nworkers; ++w) {
     const uint64_t b = p.sb + (uint64_t)w * p.rb;
     if (b < nv) p.blk_seg[(size_t)w] = seg_of(b);
-    if (p.shr_begin[(size_t)w] < p.shr_begin[(size_t)w + 1]) p.shr_seg[(size_t)w] = seg_of(p.shr_begin[(size_t)w]);
   }
   p.chk_seg.resize((size_t)nchunk);
   for (uint64_t c = 0; c < nchunk; ++c) p.chk_seg[(size_t)c] = seg_of(c * p.cv);
+  const uint64_t nsum = (p.sb + p.cvs - 1) / p.cvs;
+  if (nsum > 0xffffffffull / 64) {
+    if (why) *why = "too many chunks";
+    return 1;
+  }
+  p.sum_seg.resize((size_t)nsum);
+  for (uint64_t c = 0; c < nsum; ++c) p.sum_seg[(size_t)c] = seg_of(c * p.cvs);
   p.wk_scbegin.resize((size_t)nworkers + 1);
   for (int32_t w = 0; w <= nworkers; ++w) p.wk_scbegin[(size_t)w] = share_begin(ns, nworkers, w);
   out = std::move(p);

@@ -13,12 +13,13 @@
 //     list of single elements ("scalars"), shared out equally by worker;
 //   - the vector space ends with one "block" of rb vectors per worker
 //     (workgroup): what the fused kernel keeps on chip between its passes;
-//   - the rest, the streamed region [0, sb), is shared out equally for the
-//     summing pass, one static share per worker, so that every worker's
-//     partial sum has a fixed content and order;
-//   - for scaling, the region is cut into "chunks" of cv vectors that the
-//     workers claim at run time, so that the faster XCDs take more of them
-//     (scaling needs no partial sums, so who takes a chunk does not matter).
+//   - the rest, the streamed region [0, sb), is cut into chunks that the
+//     workers claim at run time, so that the XCDs that stream faster take
+//     more of them: "sum chunks" of cvs vectors for the summing passes (a
+//     sum chunk's partial goes to a slot of its own, so the content and
+//     order of the final sum do not depend on which worker took which
+//     chunk), and "scale chunks" of cv vectors for scaling.  The split scale
+//     kernel cuts the whole space [0, nvec) into scale chunks the same way.
 #pragma once
 
 #include <cstdint>
@@ -48,11 +49,11 @@ struct HostPlan {
   std::vector<int64_t> seg_elem0;    // nseg: element index of the segment start in its tensor
   uint64_t rb = 0;                   // vectors per block: worker w's is [sb + w rb, sb + (w + 1) rb) cut at nvec
   uint64_t sb = 0;                   // end of the streamed region, start of the blocks
-  uint64_t cv = 0;                   // vectors per chunk: chunk c is [c cv, (c + 1) cv) cut at nvec
+  uint64_t cv = 0;                   // vectors per scale chunk: chunk c is [c cv, (c + 1) cv) cut at nvec (or sb)
+  uint64_t cvs = 0;                  // vectors per sum chunk: chunk c is [c cvs, (c + 1) cvs) cut at sb
   std::vector<uint32_t> blk_seg;     // nworkers: segment holding each block's first vector
-  std::vector<uint64_t> shr_begin;   // nworkers + 1: worker w's streamed share is [shr_begin[w], shr_begin[w + 1])
-  std::vector<uint32_t> shr_seg;     // nworkers: segment holding each share's first vector
-  std::vector<uint32_t> chk_seg;     // nchunk: segment holding each chunk's first vector
+  std::vector<uint32_t> chk_seg;     // nchunk: segment holding each scale chunk's first vector
+  std::vector<uint32_t> sum_seg;     // nsum: segment holding each sum chunk's first vector
   std::vector<uint64_t> sc_addr;     // nsc: address of each single element
   std::vector<int32_t> sc_tensor;    // nsc
   std::vector<int64_t> sc_elem;      // nsc
@@ -61,7 +62,9 @@ struct HostPlan {
   int64_t nseg() const { return (int64_t)seg_addr.size(); }
   uint64_t nvec() const { return seg_vbegin.empty() ? 0 : seg_vbegin.back(); }
   uint64_t nsc() const { return (uint64_t)sc_addr.size(); }
-  uint64_t nchunk() const { return (uint64_t)chk_seg.size(); }  // chunks over the whole vector space
+  uint64_t nchunk() const { return (uint64_t)chk_seg.size(); }  // scale chunks over the whole vector space
+  uint64_t nchunk_streamed() const { return cv ? (sb + cv - 1) / cv : 0; }  // scale chunks below sb
+  uint64_t nsum() const { return (uint64_t)sum_seg.size(); }  // sum chunks (below sb)
 };
 
 // Check a list: sizes >= 0, addresses non-NULL and aligned to the element
@@ -70,34 +73,44 @@ int plan_validate(const uint64_t* addrs, const int64_t* numels, int32_t n, int32
                   int64_t* n_elements, int64_t* n_bytes);
 
 // Validate a list and build its plan for nworkers workgroups of `threads`
-// lanes: blocks of at most resident_cap vectors and chunks of chunk_vectors.
+// lanes: blocks of at most resident_cap vectors, scale chunks of
+// chunk_vectors and about sum_chunks_per_worker sum chunks per worker, each a
+// whole number of group_vectors.
 // Returns a gclip_status code (0 = OK) and, on failure, a reason in *why.
 int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
-               int32_t threads, uint64_t resident_cap, uint64_t chunk_vectors, HostPlan& out, std::string* why);
+               int32_t threads, uint64_t resident_cap, uint64_t chunk_vectors, uint32_t sum_chunks_per_worker,
+               uint64_t group_vectors, HostPlan& out, std::string* why);
 
 // Device view of a plan plus the list's workspace (all device addresses).
-// sync holds 128-byte lines of counters: line 0 the arrival ticket, epoch,
-// skip flag, count of handed-back blocks and finish ticket; lines 1..kPools
-// the chunk pools claimed while scaling (one pool per XCD).
+// sync holds 128-byte lines of counters (one line per counter group, so that
+// the XCDs do not share lines):
+//   line 0                       epoch, skip flag, count of handed-back blocks
+//   lines 1 .. kPools            chunk pools of the summing passes (one per XCD)
+//   lines 1 + kPools ..          chunk pools of the scaling passes
+//   lines 1 + 2 kPools ..        arrival tickets: one per XCD group, then the top one
+//   lines 2 + 3 kPools ..        finish tickets: one per XCD group, then the top one
 constexpr int kPools = 8;
+constexpr int64_t kNtStoreMinBytes = (int64_t)1 << 30;
 constexpr int kSyncLineWords = 32;  // 128 bytes
-constexpr int kSyncWords = kSyncLineWords * (1 + kPools);
+constexpr int kSyncWords = kSyncLineWords * (3 + 4 * kPools);
 
 struct DevPlan {
   const uint64_t* seg_vbegin;
   const uint64_t* seg_addr;
   const uint32_t* blk_seg;
-  const uint64_t* shr_begin;
-  const uint32_t* shr_seg;
   const uint32_t* chk_seg;
+  const uint32_t* sum_seg;
   const uint64_t* wk_scbegin;
   const uint64_t* sc_addr;
-  double* partials;   // nworkers partial sums (share + block + single elements)
+  double* partials;   // nsum * kWaves sum-chunk partials, then nworkers worker partials (block + single elements)
   double* bcast;      // [0]: factor decided inside the fused kernel
   uint32_t* sync;     // kSyncWords counters (see above)
   uint32_t* bstate;   // nworkers: whether each block was handed back by the fused kernel
-  uint64_t nvec, rb, sb, cv;
-  uint32_t nchunk;    // chunks over [0, nvec); those below sb cover the streamed region
+  uint64_t nvec, rb, sb, cv, cvs;
+  uint32_t nchunk;    // scale chunks over [0, nvec)
+  uint32_t nchs;      // scale chunks over the streamed region [0, sb)
+  uint32_t nsum;      // sum chunks over the streamed region [0, sb)
+  uint32_t nt_store;  // 1: the scale passes write with nontemporal stores (lists of kNtStoreMinBytes or more)
   int32_t nworkers;
   int32_t nseg;
 };

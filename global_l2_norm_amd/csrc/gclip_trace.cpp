@@ -83,15 +83,15 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
   try {
     HostPlan hp;
     const int rc =
-        plan_build(addrs, numels, n_tensors, dtype, n_workers, kThreads, kResidentCap, kChunkVectors, hp, nullptr);
+        plan_build(addrs, numels, n_tensors, dtype, n_workers, kThreads, kResidentCap, kChunkVectors,
+                   (uint32_t)kSumChunksPerWorker, kGroupVectors, hp, nullptr);
     if (rc != 0) return (gclip_status)rc;
     DevPlan p{};
     p.seg_vbegin = hp.seg_vbegin.data();
     p.seg_addr = hp.seg_addr.data();
     p.blk_seg = hp.blk_seg.data();
-    p.shr_begin = hp.shr_begin.data();
-    p.shr_seg = hp.shr_seg.data();
     p.chk_seg = hp.chk_seg.data();
+    p.sum_seg = hp.sum_seg.data();
     p.wk_scbegin = hp.wk_scbegin.data();
     p.sc_addr = hp.sc_addr.data();
     p.nvec = hp.nvec();
@@ -99,6 +99,9 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
     p.sb = hp.sb;
     p.cv = hp.cv;
     p.nchunk = (uint32_t)hp.nchunk();
+    p.nchs = (uint32_t)hp.nchunk_streamed();
+    p.nsum = (uint32_t)hp.nsum();
+    p.cvs = hp.cvs;
     p.nworkers = hp.nworkers;
     p.nseg = (int32_t)hp.nseg();
     Recorder rec{out_addr, out_worker, cap};
@@ -111,15 +114,16 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
         replay_groups(p, cur, r.b, r.e, 0, range_steps(r), -1, &rec);
       }
     };
-    for (int32_t w = 0; w < p.nworkers; ++w) {
-      if (mode == 0 || mode == 2) {  // the summing passes stream the worker's share first
-        const Range sh = share_range(p, w);
-        if (sh.b < sh.e) {
-          Cursor cur;
-          cursor_load(p, cur, sh.seg);
-          replay_groups(p, cur, sh.b, sh.e, 0, range_steps(sh), w, &rec);
-        }
+    // the summing passes claim the sum chunks of the streamed region first
+    if (mode == 0 || mode == 2) {
+      for (uint32_t c = 0; c < p.nsum; ++c) {
+        const Range r = sum_chunk_range(p, c);
+        Cursor cur;
+        cursor_load(p, cur, r.seg);
+        replay_groups(p, cur, r.b, r.e, 0, range_steps(r), -1, &rec);
       }
+    }
+    for (int32_t w = 0; w < p.nworkers; ++w) {
       const Range r = block_range(p, w);
       if (r.b < r.e && mode != 1) {
         Cursor cur;
@@ -135,8 +139,8 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
       }
       for (uint64_t i = p.wk_scbegin[w]; i < p.wk_scbegin[w + 1]; ++i) rec.put(w, p.sc_addr[i] | kElementTag);
     }
-    if (mode == 1) replay_chunks(p.nchunk, p.nvec);                                  // k_grad_scale
-    if (mode == 3) replay_chunks((uint32_t)((p.sb + p.cv - 1) / p.cv), p.sb);  // fused, second pass
+    if (mode == 1) replay_chunks(p.nchunk, p.nvec);  // k_grad_scale
+    if (mode == 3) replay_chunks(p.nchs, p.sb);      // fused, second pass
     *n_out = rec.n;
     if (!rec.uniform_ok) return GCLIP_EINVAL;
     return rec.n > cap ? GCLIP_ERANGE : GCLIP_OK;

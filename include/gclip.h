@@ -114,14 +114,19 @@ typedef struct gclip_list_info_t {
 
 /* One entry of a plan description (gclip_plan_query): a run of elements of
  * one tensor, which is
- *   kind 0  part of a worker's block of 16-byte vectors (read by the worker
- *           in both summing passes; kept on chip by the fused kernel and
- *           written back by the same worker),
+ *   kind 0  part of a worker's block of 16-byte vectors (the blocks end the
+ *           list; each is read by its worker in both summing passes, kept on
+ *           chip by the fused kernel and written back by the same worker),
  *   kind 1  single elements of a worker (every pass),
- *   kind 2  part of a chunk of 16-byte vectors that any worker may claim at
- *           run time when scaling (worker -1; chunks cover the whole list,
- *           the fused kernel uses those below the first block, cut there),
- *   kind 3  part of a worker's streamed share (summing passes only). */
+ *   kind 2  part of a chunk of 16-byte vectors over the whole list, claimed
+ *           at run time by any worker in the split scale pass (worker -1),
+ *   kind 3  part of a sum chunk of the streamed region before the blocks
+ *           (cut where the blocks begin), claimed at run time by any worker
+ *           in the summing passes (worker -1),
+ *   kind 4  part of a scale chunk of that streamed region, claimed at run
+ *           time by any worker in the fused kernel's scale pass (worker -1).
+ * The summing passes cover kinds 0, 1 and 3, the split scale pass kinds 1 and
+ * 2, the fused scale pass kinds 0, 1 and 4. */
 typedef struct gclip_plan_entry {
   int32_t worker;
   int32_t tensor;

@@ -88,37 +88,41 @@ def test_plan_covers_every_element_once(dtype, seed):
     addrs = fake_layout(rng, numels, es, misalign=bool(seed % 2))
     nw = int(rng.choice([1, 3, 7, 256]))
     entries = g.gclip_plan_query(addrs, numels, dtype, nw, 512)
-    # the summing passes read blocks, shares and single elements; the scaling
-    # pass reads chunks and the same single elements
+    # the summing passes read blocks, single elements and the sum chunks of
+    # the streamed region; the split scale pass the scale chunks over the
+    # whole list and the same single elements; the fused scale pass blocks,
+    # single elements and the scale chunks of the streamed region
     sum_cover = [np.zeros(n, dtype=np.int32) for n in numels]
     scale_cover = [np.zeros(n, dtype=np.int32) for n in numels]
+    fused_cover = [np.zeros(n, dtype=np.int32) for n in numels]
     blk_vectors = np.zeros(nw, dtype=np.int64)
-    shr_vectors = np.zeros(nw, dtype=np.int64)
     sc_per_worker = np.zeros(nw, dtype=np.int64)
+    streamed = 0
     for w, t, b, c, kind in entries:
-        assert c > 0 and kind in (0, 1, 2, 3)
-        assert (w == -1) == (kind == 2) and -1 <= w < nw
-        if kind != 2:
+        assert c > 0 and kind in (0, 1, 2, 3, 4)
+        assert (w == -1) == (kind in (2, 3, 4)) and -1 <= w < nw
+        if kind in (0, 1, 3):
             sum_cover[t][b:b + c] += 1
         if kind in (1, 2):
             scale_cover[t][b:b + c] += 1
+        if kind in (0, 1, 4):
+            fused_cover[t][b:b + c] += 1
         if kind != 1:
             assert (addrs[t] + b * es) % 16 == 0 and (c * es) % 16 == 0
         if kind == 0:
             blk_vectors[w] += c * es // 16
         elif kind == 3:
-            shr_vectors[w] += c * es // 16
+            streamed += c * es // 16
         elif kind == 1:
             sc_per_worker[w] += c
-    for cv in sum_cover + scale_cover:
+    for cv in sum_cover + scale_cover + fused_cover:
         assert np.all(cv == 1)
     # blocks: equal, except that the last non-empty one may be cut short;
-    # streamed shares differ by at most one vector
+    # a streamed region only once every block is full
     full = blk_vectors[blk_vectors > 0]
     if len(full) > 1:
         assert np.all(full[:-1] == full[0]) and full[-1] <= full[0]
-    assert shr_vectors.max() - shr_vectors.min() <= 1
-    if shr_vectors.sum() > 0:  # a streamed region only once every block is full
+    if streamed > 0:
         assert np.all(blk_vectors == blk_vectors[0])
     assert sc_per_worker.max() - sc_per_worker.min() <= 1
 
