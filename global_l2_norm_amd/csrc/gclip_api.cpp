@@ -21,9 +21,7 @@
 namespace gclip {
 int worker_threads();
 uint64_t resident_cap_vectors();
-uint64_t chunk_vectors();
-uint32_t sum_chunks_per_worker();
-uint64_t group_vectors();
+ChunkShape chunk_shape();
 hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result* res, hipStream_t st);
 hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
                         hipStream_t st);
@@ -104,8 +102,7 @@ gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int3
   try {
     gclip::HostPlan p;
     const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, n_workers, worker_threads,
-                                     gclip::resident_cap_vectors(), gclip::chunk_vectors(),
-                                     gclip::sum_chunks_per_worker(), gclip::group_vectors(), p, nullptr);
+                                     gclip::resident_cap_vectors(), gclip::chunk_shape(), p, nullptr);
     if (rc != 0) return (gclip_status)rc;
     int64_t k = 0;
     auto emit = [&](int32_t w, int32_t t, int64_t b, int64_t c, int32_t kind) {
@@ -137,18 +134,12 @@ gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int3
         i = j;
       }
     }
-    for (uint64_t c = 0; c < p.nchunk(); ++c) {
-      const uint64_t b = c * p.cv;
-      emit_vectors(-1, b, b + p.cv < p.nvec() ? b + p.cv : p.nvec(), 2);
-    }
+    for (uint64_t c = 0; c < p.nchunk(); ++c) emit_vectors(-1, p.spl_vb[c], p.spl_vb[c + 1], 2);
     for (uint64_t c = 0; c < p.nsum(); ++c) {
       const uint64_t b = c * p.cvs;
       emit_vectors(-1, b, b + p.cvs < p.sb ? b + p.cvs : p.sb, 3);
     }
-    for (uint64_t c = 0; c < p.nchunk_streamed(); ++c) {
-      const uint64_t b = c * p.cv;
-      emit_vectors(-1, b, b + p.cv < p.sb ? b + p.cv : p.sb, 4);
-    }
+    for (uint64_t c = 0; c < p.nchunk_streamed(); ++c) emit_vectors(-1, p.fus_vb[c], p.fus_vb[c + 1], 4);
     *n_out = k;
     return k > cap ? GCLIP_ERANGE : GCLIP_OK;
   } catch (const std::bad_alloc&) {
@@ -196,8 +187,7 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     const uint64_t* addrs = reinterpret_cast<const uint64_t*>(d_ptrs);
     std::string why;
     const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, ncu, gclip::worker_threads(),
-                                     gclip::resident_cap_vectors(), gclip::chunk_vectors(),
-                                     gclip::sum_chunks_per_worker(), gclip::group_vectors(), L->plan, &why);
+                                     gclip::resident_cap_vectors(), gclip::chunk_shape(), L->plan, &why);
     if (rc != 0) {
       delete L;
       return (gclip_status)rc;
@@ -214,7 +204,8 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       return at;
     };
     const size_t o_segv = take((nseg + 1) * 8), o_sega = take(nseg * 8), o_blk = take(nw * 4),
-                 o_chk = take(nch * 4), o_sum = take(nsum * 4), o_wksc = take((nw + 1) * 8),
+                 o_splv = take((nch + 1) * 8), o_spls = take(nch * 4), o_fusv = take((nchs + 1) * 8),
+                 o_fuss = take(nchs * 4), o_sum = take(nsum * 4), o_wksc = take((nw + 1) * 8),
                  o_sca = take(nsc * 8), o_part = take((nsum * waves + nw) * 8), o_bc = take(8),
                  o_sync = take((size_t)gclip::kSyncWords * 4), o_bst = take(nw * 4);
     if ((e = hipMalloc(&L->blob, off)) != hipSuccess) {
@@ -229,7 +220,8 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     };
     if ((e = hipMemset(L->blob, 0, off)) != hipSuccess || (e = up(o_segv, P.seg_vbegin.data(), (nseg + 1) * 8)) ||
         (e = up(o_sega, P.seg_addr.data(), nseg * 8)) || (e = up(o_blk, P.blk_seg.data(), nw * 4)) ||
-        (e = up(o_chk, P.chk_seg.data(), nch * 4)) || (e = up(o_sum, P.sum_seg.data(), nsum * 4)) || (e = up(o_wksc, P.wk_scbegin.data(), (nw + 1) * 8)) ||
+        (e = up(o_splv, P.spl_vb.data(), (nch + 1) * 8)) || (e = up(o_spls, P.spl_seg.data(), nch * 4)) ||
+        (e = up(o_fusv, P.fus_vb.data(), (nchs + 1) * 8)) || (e = up(o_fuss, P.fus_seg.data(), nchs * 4)) || (e = up(o_sum, P.sum_seg.data(), nsum * 4)) || (e = up(o_wksc, P.wk_scbegin.data(), (nw + 1) * 8)) ||
         (e = up(o_sca, P.sc_addr.data(), nsc * 8)) || (e = hipDeviceSynchronize()) != hipSuccess) {
       (void)hipFree(L->blob);
       delete L;
@@ -239,7 +231,10 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     D.seg_vbegin = reinterpret_cast<const uint64_t*>(b + o_segv);
     D.seg_addr = reinterpret_cast<const uint64_t*>(b + o_sega);
     D.blk_seg = reinterpret_cast<const uint32_t*>(b + o_blk);
-    D.chk_seg = reinterpret_cast<const uint32_t*>(b + o_chk);
+    D.spl_vb = reinterpret_cast<const uint64_t*>(b + o_splv);
+    D.spl_seg = reinterpret_cast<const uint32_t*>(b + o_spls);
+    D.fus_vb = reinterpret_cast<const uint64_t*>(b + o_fusv);
+    D.fus_seg = reinterpret_cast<const uint32_t*>(b + o_fuss);
     D.sum_seg = reinterpret_cast<const uint32_t*>(b + o_sum);
     D.wk_scbegin = reinterpret_cast<const uint64_t*>(b + o_wksc);
     D.sc_addr = reinterpret_cast<const uint64_t*>(b + o_sca);
@@ -250,7 +245,6 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     D.nvec = P.nvec();
     D.rb = P.rb;
     D.sb = P.sb;
-    D.cv = P.cv;
     D.nchunk = (uint32_t)nch;
     D.nchs = (uint32_t)nchs;
     D.nsum = (uint32_t)nsum;

@@ -35,8 +35,14 @@ namespace gclip {
 #ifndef GCLIP_SUM_CHUNKS_PER_WORKER
 #define GCLIP_SUM_CHUNKS_PER_WORKER 1
 #endif
-#ifndef GCLIP_CHUNK_STEPS
-#define GCLIP_CHUNK_STEPS 16
+#ifndef GCLIP_SCALE_MIN_STEPS
+#define GCLIP_SCALE_MIN_STEPS 16
+#endif
+#ifndef GCLIP_SCALE_MAX_STEPS
+#define GCLIP_SCALE_MAX_STEPS 16
+#endif
+#ifndef GCLIP_SCALE_GUIDE
+#define GCLIP_SCALE_GUIDE 2
 #endif
 
 constexpr int kThreads = GCLIP_THREADS;     // threads per workgroup (8 waves, two per SIMD)
@@ -44,17 +50,20 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = GCLIP_UNROLL;       // vectors in flight per lane in the streamed loops
 constexpr int kRegSteps = GCLIP_REG_STEPS;  // fused kernel: steps of kThreads vectors kept in VGPRs
 constexpr int kLdsSteps = GCLIP_LDS_STEPS;  // fused kernel: steps kept in LDS (kThreads * 16 B each)
-constexpr int kChunkSteps = GCLIP_CHUNK_STEPS;         // steps per claimed scale chunk
+constexpr int kScaleMinSteps = GCLIP_SCALE_MIN_STEPS;  // scale chunks: at least this many steps,
+constexpr int kScaleMaxSteps = GCLIP_SCALE_MAX_STEPS;  // at most this many,
+constexpr int kScaleGuide = GCLIP_SCALE_GUIDE;         // about (work left) / (kScaleGuide * workers)
 constexpr int kSumChunksPerWorker = GCLIP_SUM_CHUNKS_PER_WORKER;  // sum chunks per worker (about)
 // What the fused kernel keeps on chip per worker, and a chunk, in vectors.
 constexpr uint64_t kResidentCap = (uint64_t)(kRegSteps + kLdsSteps) * kThreads;
-constexpr uint64_t kChunkVectors = (uint64_t)kChunkSteps * kThreads;
 constexpr uint64_t kGroupVectors = (uint64_t)kUnroll * kThreads;  // one group of kUnroll steps
 static_assert(kThreads % 64 == 0 && kThreads <= 1024, "whole waves, at most 1024 threads");
 static_assert((size_t)kLdsSteps * kThreads * 16 + (size_t)kThreads * 4 + 1024 <= 160 * 1024,
               "LDS of one workgroup on gfx950");
 static_assert(kRegSteps % kUnroll == 0, "register steps come in whole groups");
-static_assert(kChunkSteps % kUnroll == 0, "chunks come in whole groups");
+static_assert(kScaleMinSteps % kUnroll == 0 && kScaleMaxSteps % kUnroll == 0 && kScaleMinSteps > 0 &&
+                  kScaleMaxSteps >= kScaleMinSteps && kScaleGuide > 0,
+              "scale chunks come in whole groups");
 
 // Read of a descriptor table.  The tables never change while a kernel runs,
 // so on the device they are read through the constant address space: with a
@@ -183,12 +192,12 @@ __host__ __device__ __forceinline__ Range block_range(const DevPlan& p, int32_t 
   return r;
 }
 
-// Scale chunk c cut at `end` (sb for the streamed region, nvec for the split scale kernel).
-__host__ __device__ __forceinline__ Range chunk_range(const DevPlan& p, uint32_t c, uint64_t end) {
+// Chunk c of a chunk table: [vb[c], vb[c + 1]) (scale chunks).
+__host__ __device__ __forceinline__ Range tab_chunk_range(const uint64_t* vb, const uint32_t* seg, uint32_t c) {
   Range r;
-  r.b = (uint64_t)c * p.cv;
-  r.e = r.b + p.cv < end ? r.b + p.cv : end;
-  r.seg = ld_table(p.chk_seg, c);
+  r.b = ld_table(vb, c);
+  r.e = ld_table(vb, (uint64_t)c + 1);
+  r.seg = ld_table(seg, c);
   return r;
 }
 

@@ -398,26 +398,35 @@ __device__ __forceinline__ bool take_ticket(uint32_t* lines, int32_t nworkers) {
 }
 
 // ---------------------------------------------------------------- chunk claiming
+// Workgroup w takes chunk w first, without any claim; chunks nworkers ..
+// nch - 1 are claimed at run time from kPools pools, the one of the
+// workgroup's own XCD first.  Pool q holds chunks nworkers + q, nworkers + q
+// + kPools, ...; a claim is a ticket drawn on a pool's counter.
 constexpr uint32_t kNone = 0xffffffffu;
 
-// Chunk c lives in pool c % kPools; pool q holds chunks q, q + kPools, ...
-// below nch.
-__device__ __forceinline__ uint32_t pool_size(uint32_t nch, uint32_t q) {
-  return q < nch ? (nch - q + kPools - 1) / kPools : 0u;
+struct Claimer {
+  uint32_t* pools;
+  uint32_t base;   // first claimed chunk (nworkers)
+  uint32_t ndyn;   // claimed chunks
+  uint32_t pool;   // pool drawn from
+  bool dry;        // every pool found empty
+};
+
+__device__ __forceinline__ Claimer make_claimer(uint32_t* pools, const DevPlan& p, uint32_t nch) {
+  const uint32_t base = (uint32_t)p.nworkers;
+  const uint32_t ndyn = nch > base ? nch - base : 0u;
+  return Claimer{pools, base, ndyn, blockIdx.x % (uint32_t)kPools, ndyn == 0u};
 }
 
-// Claim state of one workgroup, kept by its thread 0: the pool it draws from
-// (its own XCD's first) and whether every pool has been found empty.
-struct Claimer {
-  uint32_t pool;
-  bool dry;
-};
+__device__ __forceinline__ uint32_t pool_size(const Claimer& cl, uint32_t q) {
+  return q < cl.ndyn ? (cl.ndyn - q + kPools - 1) / kPools : 0u;
+}
 
 // A claim is taken in two steps: the ticket is drawn before a chunk streams
 // and turned into a chunk after it, so waiting for the counter's reply
 // overlaps the chunk's loads instead of draining them.  Thread 0 only.
-__device__ __forceinline__ uint32_t claim_issue(uint32_t* pools, const Claimer& cl) {
-  return cl.dry ? 0u : atomic_add(&pools[cl.pool * kSyncLineWords], 1u);
+__device__ __forceinline__ uint32_t claim_issue(const Claimer& cl) {
+  return cl.dry ? 0u : atomic_add(&cl.pools[cl.pool * kSyncLineWords], 1u);
 }
 
 // The chunk of ticket tk (drawn on pool cl.pool), or, when that pool is
@@ -426,25 +435,25 @@ __device__ __forceinline__ uint32_t claim_issue(uint32_t* pools, const Claimer& 
 // are empty (kNone).  Counters only grow during a launch, so a pool found
 // empty stays empty, and a failed claim leaves its pool empty: the loop ends
 // within kPools failures.
-__device__ __forceinline__ uint32_t claim_resolve(uint32_t* pools, uint32_t nch, Claimer& cl, uint32_t tk) {
+__device__ __forceinline__ uint32_t claim_resolve(Claimer& cl, uint32_t tk) {
   if (cl.dry) return kNone;
-  if (tk < pool_size(nch, cl.pool)) return cl.pool + tk * (uint32_t)kPools;
+  if (tk < pool_size(cl, cl.pool)) return cl.base + cl.pool + tk * (uint32_t)kPools;
   for (int round = 0; round <= kPools; ++round) {
     // the first pool after cl.pool, in circular order, that still has chunks
     uint32_t pick = kNone, best = kPools;
 #pragma unroll
     for (int q = 0; q < kPools; ++q) {
-      const uint32_t cnt = atomic_ld(&pools[q * kSyncLineWords]);
+      const uint32_t cnt = atomic_ld(&cl.pools[q * kSyncLineWords]);
       const uint32_t dist = ((uint32_t)q + 2u * kPools - cl.pool - 1u) % (uint32_t)kPools;
-      if (cnt < pool_size(nch, (uint32_t)q) && dist < best) {
+      if (cnt < pool_size(cl, (uint32_t)q) && dist < best) {
         best = dist;
         pick = (uint32_t)q;
       }
     }
     if (pick == kNone) break;
     cl.pool = pick;
-    const uint32_t k2 = atomic_add(&pools[pick * kSyncLineWords], 1u);
-    if (k2 < pool_size(nch, pick)) return pick + k2 * (uint32_t)kPools;
+    const uint32_t k2 = atomic_add(&cl.pools[pick * kSyncLineWords], 1u);
+    if (k2 < pool_size(cl, pick)) return cl.base + pick + k2 * (uint32_t)kPools;
   }
   cl.dry = true;
   return kNone;
@@ -461,67 +470,45 @@ struct ClaimSlots {
   uint32_t claim[2];
 };
 
-__device__ __forceinline__ void first_claims(uint32_t* pools, uint32_t nch, Claimer& cl, ClaimSlots& sl,
-                                             uint32_t& c, uint32_t& cn) {
-  if (threadIdx.x == 0) {
-    const uint32_t a = claim_resolve(pools, nch, cl, claim_issue(pools, cl));
-    sl.claim[0] = a;
-    sl.claim[1] = a == kNone ? kNone : claim_resolve(pools, nch, cl, claim_issue(pools, cl));
-  }
-  __syncthreads();
-  c = uniform32(sl.claim[0]);
-  cn = uniform32(sl.claim[1]);
-  __syncthreads();
-}
-
 // The chunk loops below draw the ticket for the chunk after next when a
 // chunk starts, before its later groups are loaded, and resolve it after the
 // chunk's last group has been waited for: loads and atomics complete in
 // order, so by then the ticket's reply is in and resolving it costs no wait.
 // Only then is the next chunk's first group loaded, so it stays in flight
 // across the chunk's barrier.  (Resolving after that load made the wave wait
-// for it too: every chunk ended with nothing in flight.)
+// for it too: every chunk ended with nothing in flight.)  At the start, the
+// ticket for the second chunk is drawn before the first chunk's first group
+// is loaded and resolved after it.
 
-// Load the first group of scale chunk cn (cut at end), or zeros when there is none.
-template <bool NT>
-__device__ __forceinline__ void load_next_first(const DevPlan& p, Cursor& curn, uint32_t cn, uint64_t end,
-                                                u32x4 (&q)[kUnroll]) {
-  if (cn != kNone) {
-    const Range rn = chunk_range(p, cn, end);
-    cursor_load(p, curn, rn.seg);
-    load_group<NT>(p, curn, rn.b, rn.e, 0, range_steps(rn), q);
-  } else {
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) q[u] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-// Sum every sum chunk of the streamed region [0, sb) that this workgroup claims.
-// Each wave reduces its lanes' sums over a chunk to one value and stores it
-// in the chunk's own slot, partials[c * kWaves + wave], so the final sum does
-// not depend on which workgroup took the chunk; the only barrier per chunk
-// hands the next claim to every wave.
+// Sum every sum chunk of the streamed region [0, sb) that this workgroup
+// takes.  Each wave reduces its lanes' sums over a chunk to one value and
+// stores it in the chunk's own slot, partials[c * kWaves + wave], so the
+// final sum does not depend on which workgroup took the chunk; the only
+// barrier per chunk hands the next claim to every wave.
 template <int DT>
 __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
   const uint32_t nch = p.nsum;
-  if (nch == 0) return;
+  if (blockIdx.x >= nch) return;  // then no chunk is left to claim either
   const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
-  uint32_t* pools = sum_pools(p);
-  Claimer cl{blockIdx.x % (uint32_t)kPools, false};
-  uint32_t c, cn;
-  first_claims(pools, nch, cl, sl, c, cn);
+  Claimer cl = make_claimer(sum_pools(p), p, nch);
+  uint32_t c = blockIdx.x, cn;
   Cursor cur;
   u32x4 q[kUnroll];
-  if (c != kNone) {
+  {
+    uint32_t tk = 0;
+    if (t == 0) tk = claim_issue(cl);
     const Range r = sum_chunk_range(p, c);
     cursor_load(p, cur, r.seg);
     load_group<kNtSum>(p, cur, r.b, r.e, 0, range_steps(r), q);
+    if (t == 0) sl.claim[1] = claim_resolve(cl, tk);
+    __syncthreads();
+    cn = uniform32(sl.claim[1]);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
     const Range r = sum_chunk_range(p, c);
     const uint64_t ns = range_steps(r);
     uint32_t tk = 0;
-    if (t == 0 && cn != kNone) tk = claim_issue(pools, cl);
+    if (t == 0 && cn != kNone) tk = claim_issue(cl);
     double acc[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
@@ -536,7 +523,7 @@ __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
     const uint32_t par = i & 1u;
-    if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(pools, nch, cl, tk) : kNone;
+    if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(cl, tk) : kNone;
     Cursor curn;
     if (cn != kNone) {
       const Range rn = sum_chunk_range(p, cn);
@@ -554,30 +541,33 @@ __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
   }
 }
 
-// Scale in place every chunk below nch that this workgroup claims, each cut
-// at `end`.  A chunk's last group is scaled into registers before the ticket
-// is resolved, and stored after it.
+// Scale in place every chunk of the table (vb, seg, nch) that this workgroup
+// takes.  A chunk's last group is scaled into registers before the ticket is
+// resolved, and stored after it.
 template <int DT, bool NTS>
-__device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, uint32_t nch, uint64_t end,
-                                             double s64, float s32) {
-  if (nch == 0) return;
+__device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, const uint64_t* vb,
+                                             const uint32_t* seg, uint32_t nch, double s64, float s32) {
+  if (blockIdx.x >= nch) return;  // then no chunk is left to claim either
   const uint32_t t = threadIdx.x;
-  uint32_t* pools = scale_pools(p);
-  Claimer cl{blockIdx.x % (uint32_t)kPools, false};
-  uint32_t c, cn;
-  first_claims(pools, nch, cl, sl, c, cn);
+  Claimer cl = make_claimer(scale_pools(p), p, nch);
+  uint32_t c = blockIdx.x, cn;
   Cursor cur;
   u32x4 q[kUnroll];
-  if (c != kNone) {
-    const Range r = chunk_range(p, c, end);
+  {
+    uint32_t tk = 0;
+    if (t == 0) tk = claim_issue(cl);
+    const Range r = tab_chunk_range(vb, seg, c);
     cursor_load(p, cur, r.seg);
     load_group<kNtScale>(p, cur, r.b, r.e, 0, range_steps(r), q);
+    if (t == 0) sl.claim[1] = claim_resolve(cl, tk);
+    __syncthreads();
+    cn = uniform32(sl.claim[1]);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
-    const Range r = chunk_range(p, c, end);
+    const Range r = tab_chunk_range(vb, seg, c);
     const uint64_t ns = range_steps(r);
     uint32_t tk = 0;
-    if (t == 0 && cn != kNone) tk = claim_issue(pools, cl);
+    if (t == 0 && cn != kNone) tk = claim_issue(cl);
     Cursor cst;
     cursor_load(p, cst, r.seg);
     uint64_t j = 0;
@@ -591,13 +581,17 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, u
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) q[u] = scale_vec<DT>(q[u], s64, s32);
     const uint32_t par = i & 1u;
-    if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(pools, nch, cl, tk) : kNone;
+    if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(cl, tk) : kNone;
     store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return q[u]; });
     Cursor curn;
-    u32x4 q2[kUnroll];
-    load_next_first<kNtScale>(p, curn, cn, end, q2);
+    if (cn != kNone) {
+      u32x4 q2[kUnroll];
+      const Range rn = tab_chunk_range(vb, seg, cn);
+      cursor_load(p, curn, rn.seg);
+      load_group<kNtScale>(p, curn, rn.b, rn.e, 0, range_steps(rn), q2);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
+      for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
+    }
     __syncthreads();
     c = cn;
     cn = uniform32(sl.claim[par]);
@@ -819,7 +813,7 @@ __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_n
   if (!(d.skip || d.s == 1.0)) {
     const double s64 = d.s;
     const float s32 = (float)d.s;
-    scale_chunks<DT, NTS>(p, sl, p.nchunk, p.nvec, s64, s32);
+    scale_chunks<DT, NTS>(p, sl, p.spl_vb, p.spl_seg, p.nchunk, s64, s32);
     scale_scalars<DT>(p, w, s64, s32);
   }
   finish<DT>(p, res, false, hs, &flag);
@@ -845,7 +839,7 @@ __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSl
       store_group<NTS>(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps,
                        [&](int u) { return scale_vec<DT>(keep_lds[(k0 + u) * kThreads + t], s64, s32); });
   }
-  scale_chunks<DT, NTS>(p, sl, p.nchs, p.sb, s64, s32);
+  scale_chunks<DT, NTS>(p, sl, p.fus_vb, p.fus_seg, p.nchs, s64, s32);
 }
 
 // The whole path in one launch.  Phase 1 sums the chunks of the streamed
@@ -966,9 +960,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
 // ---------------------------------------------------------------- host launchers
 int worker_threads() { return kThreads; }
 uint64_t resident_cap_vectors() { return kResidentCap; }
-uint64_t chunk_vectors() { return kChunkVectors; }
-uint32_t sum_chunks_per_worker() { return (uint32_t)kSumChunksPerWorker; }
-uint64_t group_vectors() { return kGroupVectors; }
+ChunkShape chunk_shape() {
+  ChunkShape c;
+  c.group_vectors = kGroupVectors;
+  c.sum_chunks_per_worker = (uint32_t)kSumChunksPerWorker;
+  c.scale_min_vectors = (uint64_t)kScaleMinSteps * kThreads;
+  c.scale_max_vectors = (uint64_t)kScaleMaxSteps * kThreads;
+  c.scale_guide = (uint32_t)kScaleGuide;
+  return c;
+}
 
 hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result* res, hipStream_t st) {
   const dim3 grid((unsigned)p.nworkers), block(kThreads);

@@ -15,6 +15,25 @@ uint64_t share_begin(uint64_t total, int32_t n, int32_t w) {
   return (uint64_t)w * q + std::min<uint64_t>((uint64_t)w, r);
 }
 
+// Guided schedule over [0, total): each chunk about (work left) /
+// (guide * nworkers), in whole groups, between min_v and max_v vectors.
+// Returns the chunk starts plus total.
+std::vector<uint64_t> guided_chunks(uint64_t total, int32_t nworkers, uint64_t group, uint64_t min_v, uint64_t max_v,
+                                    uint32_t guide) {
+  std::vector<uint64_t> vb{0};
+  uint64_t b = 0;
+  while (b < total) {
+    const uint64_t left = total - b, div = (uint64_t)guide * (uint64_t)nworkers;
+    uint64_t n = (left + div - 1) / div;
+    n = (n + group - 1) / group * group;
+    if (n < min_v) n = min_v;
+    if (n > max_v) n = max_v;
+    b = left > n ? b + n : total;
+    vb.push_back(b);
+  }
+  return vb;
+}
+
 }  // namespace
 
 int plan_validate(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, std::string* why,
@@ -52,11 +71,13 @@ int plan_validate(const uint64_t* addrs, const int64_t* numels, int32_t n, int32
 }
 
 int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
-               int32_t threads, uint64_t resident_cap, uint64_t chunk_vectors, uint32_t sum_chunks_per_worker,
-               uint64_t group_vectors, HostPlan& out, std::string* why) {
+               int32_t threads, uint64_t resident_cap, const ChunkShape& shape, HostPlan& out, std::string* why) {
   const int rc = plan_validate(addrs, numels, n, dtype, why, nullptr, nullptr);
   if (rc != 0) return rc;
-  if (nworkers <= 0 || threads <= 0 || chunk_vectors == 0 || sum_chunks_per_worker == 0 || group_vectors == 0) {
+  const uint64_t group_vectors = shape.group_vectors;
+  if (nworkers <= 0 || threads <= 0 || group_vectors == 0 || shape.sum_chunks_per_worker == 0 ||
+      shape.scale_guide == 0 || shape.scale_min_vectors == 0 || shape.scale_min_vectors % group_vectors != 0 ||
+      shape.scale_max_vectors < shape.scale_min_vectors || shape.scale_max_vectors % group_vectors != 0) {
     if (why) *why = "non-positive launch shape";
     return 1;
   }
@@ -102,18 +123,20 @@ int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t 
   const uint64_t even = (nv + (uint64_t)nworkers - 1) / (uint64_t)nworkers;
   p.rb = even < resident_cap ? even : resident_cap;
   p.sb = nv > (uint64_t)nworkers * p.rb ? nv - (uint64_t)nworkers * p.rb : 0;
-  p.cv = chunk_vectors;
   // sum chunks: about sum_chunks_per_worker per worker, in whole groups of
   // steps (each chunk boundary costs the streaming loop a partial drain, so
   // fewer, larger chunks are faster as long as the workers stay balanced)
   {
-    const uint64_t want = (uint64_t)nworkers * sum_chunks_per_worker;
+    const uint64_t want = (uint64_t)nworkers * shape.sum_chunks_per_worker;
     const uint64_t per = (p.sb + want - 1) / want;
     p.cvs = (per + group_vectors - 1) / group_vectors * group_vectors;
     if (p.cvs == 0) p.cvs = group_vectors;
   }
-  const uint64_t nchunk = (nv + p.cv - 1) / p.cv;
-  if (nchunk > 0xffffffffull / 64) {
+  p.spl_vb = guided_chunks(nv, nworkers, group_vectors, shape.scale_min_vectors, shape.scale_max_vectors,
+                           shape.scale_guide);
+  p.fus_vb = guided_chunks(p.sb, nworkers, group_vectors, shape.scale_min_vectors, shape.scale_max_vectors,
+                           shape.scale_guide);
+  if (p.spl_vb.size() > 0xffffffffull / 64 || p.fus_vb.size() > 0xffffffffull / 64) {
     if (why) *why = "too many chunks";
     return 1;
   }
@@ -126,8 +149,10 @@ int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t 
     const uint64_t b = p.sb + (uint64_t)w * p.rb;
     if (b < nv) p.blk_seg[(size_t)w] = seg_of(b);
   }
-  p.chk_seg.resize((size_t)nchunk);
-  for (uint64_t c = 0; c < nchunk; ++c) p.chk_seg[(size_t)c] = seg_of(c * p.cv);
+  p.spl_seg.resize(p.spl_vb.size() - 1);
+  for (size_t c = 0; c < p.spl_seg.size(); ++c) p.spl_seg[c] = seg_of(p.spl_vb[c]);
+  p.fus_seg.resize(p.fus_vb.size() - 1);
+  for (size_t c = 0; c < p.fus_seg.size(); ++c) p.fus_seg[c] = seg_of(p.fus_vb[c]);
   const uint64_t nsum = (p.sb + p.cvs - 1) / p.cvs;
   if (nsum > 0xffffffffull / 64) {
     if (why) *why = "too many chunks";

@@ -18,8 +18,10 @@
 //     more of them: "sum chunks" of cvs vectors for the summing passes (a
 //     sum chunk's partial goes to a slot of its own, so the content and
 //     order of the final sum do not depend on which worker took which
-//     chunk), and "scale chunks" of cv vectors for scaling.  The split scale
-//     kernel cuts the whole space [0, nvec) into scale chunks the same way.
+//     chunk), and "scale chunks" for the fused kernel's scale pass.  The
+//     split scale kernel cuts the whole space [0, nvec) into scale chunks.
+//     Scale chunks can shrink as the work left shrinks (guided scheduling);
+//     the default keeps them at one size, which measured as fast.
 #pragma once
 
 #include <cstdint>
@@ -49,10 +51,12 @@ struct HostPlan {
   std::vector<int64_t> seg_elem0;    // nseg: element index of the segment start in its tensor
   uint64_t rb = 0;                   // vectors per block: worker w's is [sb + w rb, sb + (w + 1) rb) cut at nvec
   uint64_t sb = 0;                   // end of the streamed region, start of the blocks
-  uint64_t cv = 0;                   // vectors per scale chunk: chunk c is [c cv, (c + 1) cv) cut at nvec (or sb)
   uint64_t cvs = 0;                  // vectors per sum chunk: chunk c is [c cvs, (c + 1) cvs) cut at sb
   std::vector<uint32_t> blk_seg;     // nworkers: segment holding each block's first vector
-  std::vector<uint32_t> chk_seg;     // nchunk: segment holding each scale chunk's first vector
+  std::vector<uint64_t> spl_vb;      // nchunk + 1: scale chunk c of the split kernel is [spl_vb[c], spl_vb[c + 1])
+  std::vector<uint32_t> spl_seg;     // nchunk: segment holding each of those chunks' first vector
+  std::vector<uint64_t> fus_vb;      // nchs + 1: scale chunks of the fused kernel, over [0, sb)
+  std::vector<uint32_t> fus_seg;     // nchs
   std::vector<uint32_t> sum_seg;     // nsum: segment holding each sum chunk's first vector
   std::vector<uint64_t> sc_addr;     // nsc: address of each single element
   std::vector<int32_t> sc_tensor;    // nsc
@@ -62,8 +66,8 @@ struct HostPlan {
   int64_t nseg() const { return (int64_t)seg_addr.size(); }
   uint64_t nvec() const { return seg_vbegin.empty() ? 0 : seg_vbegin.back(); }
   uint64_t nsc() const { return (uint64_t)sc_addr.size(); }
-  uint64_t nchunk() const { return (uint64_t)chk_seg.size(); }  // scale chunks over the whole vector space
-  uint64_t nchunk_streamed() const { return cv ? (sb + cv - 1) / cv : 0; }  // scale chunks below sb
+  uint64_t nchunk() const { return (uint64_t)spl_seg.size(); }           // split scale chunks (whole space)
+  uint64_t nchunk_streamed() const { return (uint64_t)fus_seg.size(); }  // fused scale chunks (below sb)
   uint64_t nsum() const { return (uint64_t)sum_seg.size(); }  // sum chunks (below sb)
 };
 
@@ -73,13 +77,19 @@ int plan_validate(const uint64_t* addrs, const int64_t* numels, int32_t n, int32
                   int64_t* n_elements, int64_t* n_bytes);
 
 // Validate a list and build its plan for nworkers workgroups of `threads`
-// lanes: blocks of at most resident_cap vectors, scale chunks of
-// chunk_vectors and about sum_chunks_per_worker sum chunks per worker, each a
-// whole number of group_vectors.
+// lanes: blocks of at most resident_cap vectors, and sum and scale chunks
+// as `shape` says.
 // Returns a gclip_status code (0 = OK) and, on failure, a reason in *why.
+struct ChunkShape {
+  uint64_t group_vectors;          // chunks are whole groups of steps
+  uint32_t sum_chunks_per_worker;  // sum chunks: about this many per worker
+  uint64_t scale_min_vectors;      // scale chunks: between these sizes, ...
+  uint64_t scale_max_vectors;
+  uint32_t scale_guide;            // ... about (work left) / (scale_guide * nworkers) each
+};
+
 int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
-               int32_t threads, uint64_t resident_cap, uint64_t chunk_vectors, uint32_t sum_chunks_per_worker,
-               uint64_t group_vectors, HostPlan& out, std::string* why);
+               int32_t threads, uint64_t resident_cap, const ChunkShape& shape, HostPlan& out, std::string* why);
 
 // Device view of a plan plus the list's workspace (all device addresses).
 // sync holds 128-byte lines of counters (one line per counter group, so that
@@ -98,7 +108,10 @@ struct DevPlan {
   const uint64_t* seg_vbegin;
   const uint64_t* seg_addr;
   const uint32_t* blk_seg;
-  const uint32_t* chk_seg;
+  const uint64_t* spl_vb;
+  const uint32_t* spl_seg;
+  const uint64_t* fus_vb;
+  const uint32_t* fus_seg;
   const uint32_t* sum_seg;
   const uint64_t* wk_scbegin;
   const uint64_t* sc_addr;
@@ -106,9 +119,9 @@ struct DevPlan {
   double* bcast;      // [0]: factor decided inside the fused kernel
   uint32_t* sync;     // kSyncWords counters (see above)
   uint32_t* bstate;   // nworkers: whether each block was handed back by the fused kernel
-  uint64_t nvec, rb, sb, cv, cvs;
-  uint32_t nchunk;    // scale chunks over [0, nvec)
-  uint32_t nchs;      // scale chunks over the streamed region [0, sb)
+  uint64_t nvec, rb, sb, cvs;
+  uint32_t nchunk;    // split scale chunks over [0, nvec)
+  uint32_t nchs;      // fused scale chunks over the streamed region [0, sb)
   uint32_t nsum;      // sum chunks over the streamed region [0, sb)
   uint32_t nt_store;  // 1: the scale passes write with nontemporal stores (lists of kNtStoreMinBytes or more)
   int32_t nworkers;

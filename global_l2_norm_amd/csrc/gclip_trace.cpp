@@ -14,6 +14,10 @@
 #include "gclip_cursor.hpp"
 #include "gclip_plan.hpp"
 
+namespace gclip {
+ChunkShape chunk_shape();
+}
+
 namespace {
 
 using namespace gclip;
@@ -83,21 +87,22 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
   try {
     HostPlan hp;
     const int rc =
-        plan_build(addrs, numels, n_tensors, dtype, n_workers, kThreads, kResidentCap, kChunkVectors,
-                   (uint32_t)kSumChunksPerWorker, kGroupVectors, hp, nullptr);
+        plan_build(addrs, numels, n_tensors, dtype, n_workers, kThreads, kResidentCap, chunk_shape(), hp, nullptr);
     if (rc != 0) return (gclip_status)rc;
     DevPlan p{};
     p.seg_vbegin = hp.seg_vbegin.data();
     p.seg_addr = hp.seg_addr.data();
     p.blk_seg = hp.blk_seg.data();
-    p.chk_seg = hp.chk_seg.data();
+    p.spl_vb = hp.spl_vb.data();
+    p.spl_seg = hp.spl_seg.data();
+    p.fus_vb = hp.fus_vb.data();
+    p.fus_seg = hp.fus_seg.data();
     p.sum_seg = hp.sum_seg.data();
     p.wk_scbegin = hp.wk_scbegin.data();
     p.sc_addr = hp.sc_addr.data();
     p.nvec = hp.nvec();
     p.rb = hp.rb;
     p.sb = hp.sb;
-    p.cv = hp.cv;
     p.nchunk = (uint32_t)hp.nchunk();
     p.nchs = (uint32_t)hp.nchunk_streamed();
     p.nsum = (uint32_t)hp.nsum();
@@ -105,10 +110,10 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
     p.nworkers = hp.nworkers;
     p.nseg = (int32_t)hp.nseg();
     Recorder rec{out_addr, out_worker, cap};
-    // claimed chunks below nch, cut at `end`: any worker, so reported as worker -1
-    auto replay_chunks = [&](uint32_t nch, uint64_t end) {
+    // claimed chunks of a table: any worker, so reported as worker -1
+    auto replay_chunks = [&](const uint64_t* vb, const uint32_t* seg, uint32_t nch) {
       for (uint32_t c = 0; c < nch; ++c) {
-        const Range r = chunk_range(p, c, end);
+        const Range r = tab_chunk_range(vb, seg, c);
         Cursor cur;
         cursor_load(p, cur, r.seg);
         replay_groups(p, cur, r.b, r.e, 0, range_steps(r), -1, &rec);
@@ -139,8 +144,8 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
       }
       for (uint64_t i = p.wk_scbegin[w]; i < p.wk_scbegin[w + 1]; ++i) rec.put(w, p.sc_addr[i] | kElementTag);
     }
-    if (mode == 1) replay_chunks(p.nchunk, p.nvec);  // k_grad_scale
-    if (mode == 3) replay_chunks(p.nchs, p.sb);      // fused, second pass
+    if (mode == 1) replay_chunks(p.spl_vb, p.spl_seg, p.nchunk);  // k_grad_scale
+    if (mode == 3) replay_chunks(p.fus_vb, p.fus_seg, p.nchs);    // fused, second pass
     *n_out = rec.n;
     if (!rec.uniform_ok) return GCLIP_EINVAL;
     return rec.n > cap ? GCLIP_ERANGE : GCLIP_OK;
