@@ -217,3 +217,40 @@ int oracle_clip(void* const* ptrs, const int64_t* numels, int32_t n, int32_t dt,
   if (skip) return 0;
   return oracle_scale(ptrs, numels, n, dt, s);
 }
+
+/* One AdamW step on one tensor, after the clip.  Grad clip lesson, section
+ * "Order matters: Pre-Adam": the clip runs before AdamW's moments m, v and
+ * the weights are updated, so the moments only ever see the clipped
+ * gradient; backprop lesson, section "Optimizer state": AdamW keeps the two
+ * moments per weight, in binary32 beside binary32 weights (section "Signals
+ * & checkpoints").  The update itself is not printed on the pages; it is
+ * AdamW as published (Loshchilov and Hutter, "Decoupled weight decay
+ * regularization", with the bias-corrected moments of Kingma and Ba's Adam),
+ * in binary64, element by element:
+ *   g    = s * grad                        (s: the factor the clip decided)
+ *   m'   = b1 * m + (1 - b1) * g
+ *   v'   = b2 * v + (1 - b2) * g * g
+ *   mhat = m' / (1 - b1^step),  vhat = v' / (1 - b2^step)
+ *   p'   = p - lr * (mhat / (sqrt(vhat) + eps) + wd * p)
+ * step >= 1 counts the optimizer steps taken, this one included.  Inputs are
+ * the binary32 weights and moments and the gradient in format dt; results
+ * are binary64. */
+int oracle_adamw(const float* p, const void* grad, const float* m, const float* v, int64_t n, int32_t dt,
+                 double s, double lr, double b1, double b2, double eps, double wd, int64_t step,
+                 double* p_out, double* m_out, double* v_out) {
+  if (n < 0 || !dtype_ok(dt) || step < 1 || !p_out || !m_out || !v_out) return -1;
+  const double bc1 = 1.0 - pow(b1, (double)step);
+  const double bc2 = 1.0 - pow(b2, (double)step);
+  for (int64_t i = 0; i < n; ++i) {
+    const double g = s * oracle_decode(grad, i, dt);
+    const double mi = b1 * (double)m[i] + (1.0 - b1) * g;
+    const double vi = b2 * (double)v[i] + (1.0 - b2) * g * g;
+    const double mhat = mi / bc1;
+    const double vhat = vi / bc2;
+    const double pi = (double)p[i];
+    p_out[i] = pi - lr * (mhat / (sqrt(vhat) + eps) + wd * pi);
+    m_out[i] = mi;
+    v_out[i] = vi;
+  }
+  return 0;
+}

@@ -54,6 +54,11 @@ class Oracle:
         lib.oracle_clip.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_int32, dp, i32p]
         lib.oracle_clip.restype = ctypes.c_int
+        f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_adamw.argtypes = [f32p, vp, f32p, f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double,
+                                     ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_double, ctypes.c_int64, dp, dp, dp]
+        lib.oracle_adamw.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -116,6 +121,54 @@ class Oracle:
                 "clipped": bool(flags[1]), "skipped": bool(flags[2])}
 
 
+    def adamw(self, p, grad, m, v, dtype: str, s: float, lr: float, beta1: float, beta2: float, eps: float,
+              weight_decay: float, step: int):
+        """One AdamW step on one tensor with the clipped gradient s * grad.
+        p, m, v: float32 arrays (left as they are); grad: raw storage of dtype.
+        Returns binary64 arrays (p', m', v')."""
+        p = np.ascontiguousarray(p, dtype=np.float32)
+        m = np.ascontiguousarray(m, dtype=np.float32)
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        grad = np.ascontiguousarray(grad, dtype=_NP[dtype])
+        n = p.size
+        if not (grad.size == m.size == v.size == n):
+            raise ValueError("p, grad, m and v must have the same size")
+        outs = [np.empty(n, dtype=np.float64) for _ in range(3)]
+        f32p = ctypes.POINTER(ctypes.c_float)
+        dp = ctypes.POINTER(ctypes.c_double)
+        rc = self.lib.oracle_adamw(p.ctypes.data_as(f32p), ctypes.c_void_p(grad.ctypes.data),
+                                   m.ctypes.data_as(f32p), v.ctypes.data_as(f32p), n, _CODE[dtype], float(s),
+                                   float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step),
+                                   *[o.ctypes.data_as(dp) for o in outs])
+        if rc != 0:
+            raise ValueError("oracle_adamw rejected its arguments")
+        return tuple(outs)
+
+    def clip_adamw(self, params, grads, m, v, dtype: str, max_norm: float, avg_factor: float = 1.0,
+                   error_if_nonfinite: bool = False, *, lr: float, beta1: float, beta2: float, eps: float,
+                   weight_decay: float, step: int):
+        """The clip of the gradient list followed by one AdamW step on every
+        tensor with the clipped gradient (nothing changes when the stop switch
+        fires).  The gradients themselves are not written.  Returns the
+        decision (as clip_ does) and lists of binary64 p', m', v'."""
+        ptrs, numels, n = _marshal(grads, dtype)
+        sumsq = ctypes.c_double()
+        nonfinite = ctypes.c_int32()
+        if self.lib.oracle_sumsq(ptrs, numels, n, _CODE[dtype], float(avg_factor), ctypes.byref(sumsq),
+                                 ctypes.byref(nonfinite)) != 0:
+            raise ValueError("oracle_sumsq rejected its arguments")
+        norm = float(np.sqrt(sumsq.value))
+        scale, clipped, skip = self.decide(norm, bool(nonfinite.value), max_norm, avg_factor, error_if_nonfinite)
+        res = {"sumsq": sumsq.value, "norm": norm, "scale": 1.0 if skip else scale,
+               "nonfinite": bool(nonfinite.value), "clipped": clipped, "skipped": skip}
+        if skip:
+            return res, ([np.asarray(x, np.float64) for x in params], [np.asarray(x, np.float64) for x in m],
+                         [np.asarray(x, np.float64) for x in v])
+        outs = [self.adamw(pp, g, mm, vv, dtype, scale, lr, beta1, beta2, eps, weight_decay, step)
+                for pp, g, mm, vv in zip(params, grads, m, v)]
+        return res, ([o[0] for o in outs], [o[1] for o in outs], [o[2] for o in outs])
+
+
 _default = None
 
 
@@ -171,3 +224,11 @@ def scale_(arrays, dtype, s):
 
 def clip_(arrays, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False):
     return default().clip_(arrays, dtype, max_norm, avg_factor, error_if_nonfinite)
+
+
+def adamw(p, grad, m, v, dtype, s, lr, beta1, beta2, eps, weight_decay, step):
+    return default().adamw(p, grad, m, v, dtype, s, lr, beta1, beta2, eps, weight_decay, step)
+
+
+def clip_adamw(params, grads, m, v, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False, **hp):
+    return default().clip_adamw(params, grads, m, v, dtype, max_norm, avg_factor, error_if_nonfinite, **hp)

@@ -405,7 +405,111 @@ def pin_infinite_threshold(o):
     assert not r["clipped"] and r["scale"] == 1.0
 
 
+# ------------------------------------------------------------------ AdamW after the clip
+# Grad clip lesson, "Order matters: Pre-Adam": AdamW's moments see the
+# clipped gradient.  The update is AdamW as published (decoupled weight decay,
+# bias-corrected moments); these pins fix it against closed forms of the
+# algorithm and against torch.optim.AdamW run in float64 on the CPU.
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def pin_adamw_first_step(o):
+    """From zero moments, step 1: m' = (1 - b1) g, v' = (1 - b2) g^2, the
+    bias-corrected moments are g and g^2, so the step is g / (|g| + eps)."""
+    rng = np.random.default_rng(30)
+    for dt in DTYPES:
+        g = store(rng.standard_normal(50) * 0.1, dt)
+        gv = values(g, dt)
+        p = _f32(rng.standard_normal(50))
+        z = np.zeros(50, np.float32)
+        s = 0.75
+        pn, mn, vn = o.adamw(p, g, z, z, dt, s, step=1, **HP)
+        gs = s * gv
+        assert np.allclose(mn, (1 - HP["beta1"]) * gs, rtol=1e-15, atol=0)
+        assert np.allclose(vn, (1 - HP["beta2"]) * gs * gs, rtol=1e-15, atol=0)
+        p64 = p.astype(np.float64)
+        want = p64 - HP["lr"] * (gs / (np.abs(gs) + HP["eps"]) + HP["weight_decay"] * p64)
+        assert np.allclose(pn, want, rtol=1e-14, atol=1e-18)
+
+
+def pin_adamw_decay_only(o):
+    """A zero gradient on zero moments leaves only the decoupled decay:
+    p' = p (1 - lr wd)."""
+    p = _f32(np.linspace(-2, 2, 9))
+    z = np.zeros(9, np.float32)
+    pn, mn, vn = o.adamw(p, z, z, z, "f32", 1.0, step=3, **HP)
+    assert np.all(mn == 0) and np.all(vn == 0)
+    assert np.allclose(pn, p.astype(np.float64) * (1 - HP["lr"] * HP["weight_decay"]), rtol=1e-15, atol=0)
+
+
+def pin_adamw_constant_gradient(o):
+    """With the same gradient every step from zero moments, m_t = (1 - b1^t) g
+    and v_t = (1 - b2^t) g^2 (a geometric sum), so the bias-corrected moments
+    are exactly g and g^2 at every step."""
+    g = _f32([0.5, -0.25, 2.0, -3.0])
+    p = _f32([1.0, 1.0, -1.0, 0.5])
+    m = np.zeros(4, np.float32)
+    v = np.zeros(4, np.float32)
+    b1, b2 = HP["beta1"], HP["beta2"]
+    for t in range(1, 7):
+        pn, mn, vn = o.adamw(p, g, m, v, "f32", 1.0, step=t, **HP)
+        assert np.allclose(mn, (1 - b1 ** t) * g.astype(np.float64), rtol=1e-6)
+        assert np.allclose(vn, (1 - b2 ** t) * g.astype(np.float64) ** 2, rtol=1e-6)
+        g64 = g.astype(np.float64)
+        step = g64 / (np.abs(g64) + HP["eps"])
+        assert np.allclose(pn, p.astype(np.float64) * (1 - HP["lr"] * HP["weight_decay"]) - HP["lr"] * step,
+                           rtol=1e-9)
+        p, m, v = _f32(pn), _f32(mn), _f32(vn)
+
+
+def pin_adamw_matches_torch(o):
+    """Several steps with changing gradients against torch.optim.AdamW in
+    float64 (same binary32 state fed to both at every step)."""
+    import torch
+    rng = np.random.default_rng(31)
+    n = 64
+    p = _f32(rng.standard_normal(n))
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    hp = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    for t in range(1, 6):
+        g = store(rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 0), "f32")
+        s = float(rng.uniform(0.2, 1.0))
+        pn, mn, vn = o.adamw(p, g, m, v, "f32", s, step=t, **hp)
+        tp = torch.nn.Parameter(torch.from_numpy(p.astype(np.float64)))
+        opt = torch.optim.AdamW([tp], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                                weight_decay=hp["weight_decay"], foreach=False)
+        tp.grad = torch.from_numpy(g.astype(np.float64) * s)
+        opt.state[tp] = {"step": torch.tensor(float(t - 1)), "exp_avg": torch.from_numpy(m.astype(np.float64)),
+                         "exp_avg_sq": torch.from_numpy(v.astype(np.float64))}
+        opt.step()
+        st = opt.state[tp]
+        assert np.allclose(pn, tp.detach().numpy(), rtol=1e-12, atol=1e-15), t
+        assert np.allclose(mn, st["exp_avg"].numpy(), rtol=1e-12, atol=1e-18), t
+        assert np.allclose(vn, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-20), t
+        p, m, v = _f32(pn), _f32(mn), _f32(vn)
+
+
+def pin_adamw_after_clip(o):
+    """The moments see the clipped gradient: [6, 8] clipped at 5 gives
+    [3, 4] (glossary page worked example), so m' = (1 - b1) [3, 4]; with a
+    NaN and the stop switch on nothing changes at all."""
+    p = _f32([1.0, -1.0])
+    z = np.zeros(2, np.float32)
+    res, (pn, mn, vn) = o.clip_adamw([p], [_f32([6.0, 8.0])], [z], [z], "f32", 5.0, step=1, **HP)
+    assert res["clipped"] and res["scale"] == 0.5
+    assert np.array_equal(mn[0], (1 - HP["beta1"]) * np.array([3.0, 4.0]))
+    res, (pn, mn, vn) = o.clip_adamw([p], [_f32([np.nan, 8.0])], [z], [z], "f32", 5.0, 1.0, True, step=1, **HP)
+    assert res["skipped"] and np.array_equal(pn[0], p) and np.all(mn[0] == 0) and np.all(vn[0] == 0)
+
+
 ALL_PINS = [pin_worked_6_8, pin_not_per_coordinate, pin_sgd_step_length, pin_accumulate_then_clip,
             pin_tie_passes_unchanged, pin_below_threshold_bitwise, pin_post_clip_norm, pin_single_global_factor,
             pin_joint_norm_library, pin_bruteforce_exact, pin_decode_library, pin_encode_library, pin_nonfinite,
-            pin_avg_factor, pin_scale_invariance, pin_empty_and_zero_size, pin_infinite_threshold]
+            pin_avg_factor, pin_scale_invariance, pin_empty_and_zero_size, pin_infinite_threshold,
+            pin_adamw_first_step, pin_adamw_decay_only, pin_adamw_constant_gradient, pin_adamw_matches_torch,
+            pin_adamw_after_clip]

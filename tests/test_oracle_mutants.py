@@ -31,6 +31,17 @@ MUTANTS = {
     "avg_squared_twice": ("const double u = avg * g;", "const double u = avg * avg * g;"),
     "scale_skips_last_element": ("for (int64_t i = 0; i < numels[t]; ++i) {\n      const double g = oracle_decode(ptrs[t], i, dt);\n      store_bits",
                                  "for (int64_t i = 0; i + 1 < numels[t]; ++i) {\n      const double g = oracle_decode(ptrs[t], i, dt);\n      store_bits"),
+    "adamw_no_bias_correction": ("const double mhat = mi / bc1;", "const double mhat = mi;"),
+    "adamw_eps_inside_sqrt": ("p_out[i] = pi - lr * (mhat / (sqrt(vhat) + eps) + wd * pi);",
+                              "p_out[i] = pi - lr * (mhat / sqrt(vhat + eps) + wd * pi);"),
+    "adamw_decay_coupled": ("const double g = s * oracle_decode(grad, i, dt);",
+                            "const double g = s * oracle_decode(grad, i, dt) + wd * (double)p[i];"),
+    "adamw_betas_swapped": ("const double mi = b1 * (double)m[i] + (1.0 - b1) * g;",
+                            "const double mi = b2 * (double)m[i] + (1.0 - b2) * g;"),
+    "adamw_clip_factor_dropped": ("const double g = s * oracle_decode(grad, i, dt);",
+                                  "const double g = oracle_decode(grad, i, dt);"),
+    "adamw_step_off_by_one": ("const double bc1 = 1.0 - pow(b1, (double)step);",
+                              "const double bc1 = 1.0 - pow(b1, (double)(step + 1));"),
     "overflow_not_to_inf": ("if (E > emax) return sign | exp_all;  /* already", "if (E > emax + 1) return sign | exp_all;  /* already"),
 }
 
