@@ -16,11 +16,12 @@ import ctypes
 
 from . import _lib
 from ._lib import (GCLIP_BF16, GCLIP_F16, GCLIP_F32, GCLIP_PATH_AUTO, GCLIP_PATH_FUSED, GCLIP_PATH_SPLIT,
-                   GclipListInfo, GclipPlanEntry, GclipResult)
+                   GclipAdamwHparams, GclipListInfo, GclipPlanEntry, GclipResult)
 
 __all__ = ["GclipError", "GclipResult", "GradList", "clip_grad_norm_", "gclip_list_create", "gclip_list_destroy",
            "gclip_list_info", "gclip_list_set_path", "gclip_list_set_wait", "gclip_norm", "gclip_scale", "gclip_clip_",
            "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string", "gclip_version",
+           "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step", "AdamWList",
            "GCLIP_F32", "GCLIP_F16", "GCLIP_BF16", "GCLIP_PATH_AUTO", "GCLIP_PATH_FUSED", "GCLIP_PATH_SPLIT"]
 
 DTYPE_CODES = {"f32": GCLIP_F32, "f16": GCLIP_F16, "bf16": GCLIP_BF16}
@@ -138,6 +139,28 @@ def gclip_version():
     return _lib.lib.gclip_version()
 
 
+def gclip_adamw_create(d_params, d_grads, d_exp_avg, d_exp_avg_sq, numels, grad_dtype):
+    n = len(numels)
+    arrs = [(ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(a)) for a in x])
+            for x in (d_params, d_grads, d_exp_avg, d_exp_avg_sq)]
+    ne = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in numels])
+    out = ctypes.c_void_p()
+    _check(_lib.lib.gclip_adamw_create(*arrs, ne, n, int(grad_dtype), ctypes.byref(out)), "gclip_adamw_create")
+    return out
+
+
+def gclip_adamw_destroy(handle):
+    _check(_lib.lib.gclip_adamw_destroy(handle), "gclip_adamw_destroy")
+
+
+def gclip_adamw_step(handle, lr, beta1, beta2, eps, weight_decay, step, max_norm, avg_factor, error_if_nonfinite,
+                     d_result, stream):
+    hp = GclipAdamwHparams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+    _check(_lib.lib.gclip_adamw_step(handle, ctypes.byref(hp), float(max_norm), float(avg_factor),
+                                     int(bool(error_if_nonfinite)), ctypes.c_void_p(int(d_result)),
+                                     ctypes.c_void_p(int(stream))), "gclip_adamw_step")
+
+
 # ---------------------------------------------------------------- torch-facing wrapper
 def _torch_dtype_code(t):
     import torch
@@ -210,6 +233,58 @@ class GradList:
     def close(self):
         if getattr(self, "handle", None):
             gclip_list_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class AdamWList:
+    """AdamW over a fixed list of binary32 weights, their gradients (any list
+    dtype) and binary32 moments, driven by the clip decision of a GradList
+    over the same gradients: ``grads.norm(a)`` then ``opt.step(grads, ...)``
+    is the clip followed by the optimizer step with the clipped gradient,
+    without writing the clipped gradient back."""
+
+    def __init__(self, params, grads, exp_avg, exp_avg_sq):
+        import torch
+        params, grads, exp_avg, exp_avg_sq = (list(x) for x in (params, grads, exp_avg, exp_avg_sq))
+        if not (len(params) == len(grads) == len(exp_avg) == len(exp_avg_sq)):
+            raise ValueError("the four lists must have the same length")
+        for x in params + exp_avg + exp_avg_sq:
+            if x.dtype != torch.float32:
+                raise TypeError("weights and moments must be float32")
+        codes = {_torch_dtype_code(g) for g in grads}
+        if len(codes) > 1:
+            raise TypeError("all gradients must share one dtype")
+        for group in (params, grads, exp_avg, exp_avg_sq):
+            for x in group:
+                if not x.is_cuda or not x.is_contiguous():
+                    raise ValueError("tensors must be contiguous device tensors")
+        for a, b, c, d in zip(params, grads, exp_avg, exp_avg_sq):
+            if not (a.numel() == b.numel() == c.numel() == d.numel()):
+                raise ValueError("weight, gradient and moments of one tensor must have the same size")
+        self.tensors = (params, grads, exp_avg, exp_avg_sq)
+        self.dtype = codes.pop() if codes else GCLIP_F32
+        self.device = params[0].device if params else torch.device("cuda", torch.cuda.current_device())
+        with torch.cuda.device(self.device):
+            self.handle = gclip_adamw_create([p.data_ptr() for p in params], [g.data_ptr() for g in grads],
+                                             [m.data_ptr() for m in exp_avg], [v.data_ptr() for v in exp_avg_sq],
+                                             [p.numel() for p in params], self.dtype)
+
+    def step(self, grad_list, *, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step, max_norm,
+             avg_factor=1.0, error_if_nonfinite=False, stream=None):
+        """One optimizer step; grad_list.norm(avg_factor) must have run first
+        on the same stream.  The decision lands in grad_list's result block."""
+        gclip_adamw_step(self.handle, lr, beta1, beta2, eps, weight_decay, step, max_norm, avg_factor,
+                         error_if_nonfinite, grad_list.d_result, GradList._stream(stream))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            gclip_adamw_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -47,6 +47,11 @@ class GclipPlanEntry(ctypes.Structure):
                 ("elem_count", ctypes.c_int64), ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class GclipAdamwHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
+
+
 assert ctypes.sizeof(GclipResult) == 64
 
 
@@ -66,6 +71,9 @@ def _declare(lib):
                               ctypes.POINTER(GclipPlanEntry), i64, ctypes.POINTER(i64)], i32),
         "gclip_plan_trace": ([ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(i64), i32, i32, i32, i32,
                               ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(i32), i64, ctypes.POINTER(i64)], i32),
+        "gclip_adamw_create": ([ctypes.POINTER(vp)] * 4 + [ctypes.POINTER(i64), i32, i32, ctypes.POINTER(vp)], i32),
+        "gclip_adamw_destroy": ([vp], i32),
+        "gclip_adamw_step": ([vp, ctypes.POINTER(GclipAdamwHparams), dbl, dbl, i32, vp, vp], i32),
         "gclip_status_string": ([i32], ctypes.c_char_p),
         "gclip_last_hip_error": ([], i32),
         "gclip_version": ([], i32),
@@ -99,4 +107,4 @@ lib = load()
 EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_list_set_path",
            "gclip_list_set_wait", "gclip_norm",
            "gclip_scale", "gclip_clip_", "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string",
-           "gclip_last_hip_error", "gclip_version")
+           "gclip_last_hip_error", "gclip_version", "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step")

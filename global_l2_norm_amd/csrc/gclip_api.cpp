@@ -14,6 +14,8 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/gclip.h"
 #include "gclip_plan.hpp"
@@ -28,6 +30,8 @@ hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
                         uint32_t epoch, uint64_t wait_ticks, hipStream_t st);
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu);
+hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, double avg, int err,
+                        gclip_result* res, hipStream_t st);
 }  // namespace gclip
 
 // How long a workgroup of the fused kernel waits at the grid-wide decision
@@ -47,6 +51,13 @@ struct gclip_list {
   int64_t wait_us = kDefaultWaitUs;
   uint64_t clock_khz = 0;  // device wall clock
   uint64_t wait_ticks = 0;
+};
+
+struct gclip_adamw {
+  gclip::AdamPiece* pieces = nullptr;
+  uint32_t npieces = 0;
+  int32_t dtype = 0;
+  int device = 0;
 };
 
 namespace {
@@ -72,6 +83,35 @@ gclip_status check_device(const gclip_list* list) {
   if (dev != list->device) return GCLIP_EINVAL;
   return GCLIP_OK;
 }
+
+// The pieces of an AdamW list (see AdamPiece): for each tensor, vector pieces
+// of up to kAdamPieceElems elements when all four addresses allow 4-element
+// accesses, then the last (< 4) elements as a scalar piece; otherwise scalar
+// pieces throughout.
+void adamw_pieces(const uint64_t* p, const uint64_t* g, const uint64_t* m, const uint64_t* v, const int64_t* numels,
+                  int32_t n, uint64_t es, std::vector<gclip::AdamPiece>& out) {
+  for (int32_t t = 0; t < n; ++t) {
+    const uint64_t ne = (uint64_t)numels[t];
+    const bool vec = p[t] % 16 == 0 && m[t] % 16 == 0 && v[t] % 16 == 0 && g[t] % (4 * es) == 0;
+    uint64_t e = 0;
+    auto push = [&](uint64_t cnt, uint32_t isvec) {
+      out.push_back(gclip::AdamPiece{p[t] + e * 4, g[t] + e * es, m[t] + e * 4, v[t] + e * 4, (uint32_t)cnt, isvec});
+      e += cnt;
+    };
+    if (vec) {
+      while (ne - e >= 4) {
+        const uint64_t left = (ne - e) / 4 * 4;
+        push(left < gclip::kAdamPieceElems ? left : gclip::kAdamPieceElems, 1u);
+      }
+    }
+    while (e < ne) {
+      const uint64_t left = ne - e;
+      push(left < gclip::kAdamPieceElems ? left : gclip::kAdamPieceElems, 0u);
+    }
+  }
+}
+
+bool unit_interval(double b) { return std::isfinite(b) && b >= 0.0 && b < 1.0; }
 
 }  // namespace
 
@@ -346,6 +386,110 @@ gclip_status gclip_clip_(gclip_list* list, double max_norm, double avg_factor, i
     e = gclip::launch_norm(list->dev, list->plan.dtype, avg_factor, d_result, s);
     if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg_factor, err, d_result, s);
   }
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_adamw_create(void* const* d_params, void* const* d_grads, void* const* d_exp_avg,
+                                void* const* d_exp_avg_sq, const int64_t* numels, int32_t n_tensors,
+                                int32_t grad_dtype, gclip_adamw** out) {
+  if (!out) return GCLIP_EINVAL;
+  *out = nullptr;
+  if (!gclip::dtype_valid(grad_dtype)) return GCLIP_EDTYPE;
+  if (n_tensors < 0 || (n_tensors > 0 && (!d_params || !d_grads || !d_exp_avg || !d_exp_avg_sq || !numels)))
+    return GCLIP_EINVAL;
+  const uint64_t es = (uint64_t)gclip::dtype_bytes(grad_dtype);
+  const uint64_t* P = reinterpret_cast<const uint64_t*>(d_params);
+  const uint64_t* G = reinterpret_cast<const uint64_t*>(d_grads);
+  const uint64_t* M = reinterpret_cast<const uint64_t*>(d_exp_avg);
+  const uint64_t* V = reinterpret_cast<const uint64_t*>(d_exp_avg_sq);
+  gclip_adamw* A = nullptr;
+  try {
+    // every argument error is reported before any HIP call
+    std::vector<std::pair<uint64_t, uint64_t>> ranges;
+    for (int32_t t = 0; t < n_tensors; ++t) {
+      if (numels[t] < 0) return GCLIP_EINVAL;
+      if (numels[t] == 0) continue;
+      if ((uint64_t)numels[t] > ((uint64_t)1 << 56)) return GCLIP_EINVAL;
+      const uint64_t a[4] = {P[t], G[t], M[t], V[t]};
+      const uint64_t size[4] = {4, es, 4, 4};
+      for (int k = 0; k < 4; ++k) {
+        if (a[k] == 0 || a[k] % size[k] != 0) return GCLIP_EINVAL;
+        const uint64_t bytes = (uint64_t)numels[t] * size[k];
+        if (a[k] + bytes < a[k]) return GCLIP_EINVAL;
+        ranges.emplace_back(a[k], a[k] + bytes);
+      }
+    }
+    std::sort(ranges.begin(), ranges.end());
+    for (size_t i = 1; i < ranges.size(); ++i)
+      if (ranges[i].first < ranges[i - 1].second) return GCLIP_EINVAL;
+    std::vector<gclip::AdamPiece> pieces;
+    adamw_pieces(P, G, M, V, numels, n_tensors, es, pieces);
+    if (pieces.size() > 0x7fffffffull) return GCLIP_EINVAL;
+    A = new gclip_adamw();
+    A->dtype = grad_dtype;
+    A->npieces = (uint32_t)pieces.size();
+    hipError_t e = hipGetDevice(&A->device);
+    if (e != hipSuccess) {
+      delete A;
+      return hip_fail(e);
+    }
+    const size_t bytes = pieces.size() * sizeof(gclip::AdamPiece);
+    if (bytes > 0) {
+      if ((e = hipMalloc(&A->pieces, bytes)) != hipSuccess) {
+        delete A;
+        g_last_hip = (int32_t)e;
+        return GCLIP_ENOMEM;
+      }
+      if ((e = hipMemcpy(A->pieces, pieces.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+        (void)hipFree(A->pieces);
+        delete A;
+        return hip_fail(e);
+      }
+    }
+    *out = A;
+    return GCLIP_OK;
+  } catch (const std::bad_alloc&) {
+    if (A) {
+      if (A->pieces) (void)hipFree(A->pieces);
+      delete A;
+    }
+    return GCLIP_ENOMEM;
+  }
+}
+
+gclip_status gclip_adamw_destroy(gclip_adamw* opt) {
+  if (!opt) return GCLIP_OK;
+  hipError_t e = hipSuccess;
+  if (opt->pieces) e = hipFree(opt->pieces);
+  delete opt;
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm, double avg_factor,
+                              int32_t error_if_nonfinite, gclip_result* d_result, void* stream) {
+  if (!opt || !hp || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(avg_factor)) return GCLIP_EINVAL;
+  if (!std::isfinite(hp->lr) || hp->lr < 0.0 || !unit_interval(hp->beta1) || !unit_interval(hp->beta2) ||
+      !std::isfinite(hp->eps) || hp->eps <= 0.0 || !std::isfinite(hp->weight_decay) || hp->weight_decay < 0.0 ||
+      hp->step < 1)
+    return GCLIP_EINVAL;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev != opt->device) return GCLIP_EINVAL;
+  const double bc1 = 1.0 - std::pow(hp->beta1, (double)hp->step);
+  const double bc2 = 1.0 - std::pow(hp->beta2, (double)hp->step);
+  gclip::AdamHp h;
+  h.step_size = (float)(hp->lr / bc1);
+  h.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  h.eps = (float)hp->eps;
+  h.decay = (float)(1.0 - hp->lr * hp->weight_decay);
+  h.b1 = (float)hp->beta1;
+  h.omb1 = (float)(1.0 - hp->beta1);
+  h.b2 = (float)hp->beta2;
+  h.omb2 = (float)(1.0 - hp->beta2);
+  gclip::AdamPlan plan{opt->pieces, opt->npieces};
+  e = gclip::launch_adamw(plan, opt->dtype, h, max_norm, avg_factor, error_if_nonfinite ? 1 : 0, d_result,
+                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 

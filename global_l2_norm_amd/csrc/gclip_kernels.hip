@@ -957,6 +957,93 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   finish<DT>(p, res, true, hs, &flag);
 }
 
+// ---------------------------------------------------------------- AdamW on the clipped gradient
+// Grad clip lesson, "Order matters: Pre-Adam": the optimizer's moments see
+// the clipped gradient.  Each workgroup updates one piece of one tensor: the
+// weights p and moments m, v (binary32) from the gradient times the factor s
+// of the clip decision, which is read from the result block -- the clipped
+// gradient itself is never written.
+typedef __attribute__((address_space(1))) float g_f32;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x2 g_u32x2;
+
+template <int DT>
+__device__ __forceinline__ float grad_value(uint32_t bits) {
+  if constexpr (DT == GCLIP_F32) return __uint_as_float(bits);
+  else if constexpr (DT == GCLIP_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+  else return __uint_as_float(bits << 16);
+}
+
+// Four consecutive gradient values from a 4-element-aligned address.
+template <int DT>
+__device__ __forceinline__ void load_grad4(uint64_t a, float (&g)[4]) {
+  if constexpr (DT == GCLIP_F32) {
+    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const g_u32x4*>(a));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) g[k] = __uint_as_float(q[k]);
+  } else {
+    const u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const g_u32x2*>(a));
+    g[0] = grad_value<DT>(q[0] & 0xffffu);
+    g[1] = grad_value<DT>(q[0] >> 16);
+    g[2] = grad_value<DT>(q[1] & 0xffffu);
+    g[3] = grad_value<DT>(q[1] >> 16);
+  }
+}
+
+__device__ __forceinline__ void adamw_elem(float& p, float& m, float& v, float g, const AdamHp& h) {
+  m = h.b1 * m + h.omb1 * g;
+  v = h.b2 * v + h.omb2 * (g * g);
+  const float denom = sqrtf(v) * h.inv_sqrt_bc2 + h.eps;
+  p = p * h.decay - h.step_size * (m / denom);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kAdamThreads) void k_adamw_clip(AdamPlan P, AdamHp h, double max_norm, double avg,
+                                                             int err, gclip_result* res) {
+  const Decision d = decide(res->sumsq, res->nonfinite, max_norm, avg, err);
+  if (blockIdx.x == 0 && threadIdx.x == 0) write_decision(res, d, max_norm);
+  if (d.skip || blockIdx.x >= P.npieces) return;
+  const float s = (float)d.s;
+  const AdamPiece pc = ld_table(P.pieces, blockIdx.x);
+  constexpr uint32_t es = DT == GCLIP_F32 ? 4u : 2u;
+  if (pc.vec) {
+    for (uint32_t i = threadIdx.x * 4u; i < pc.count; i += kAdamThreads * 4u) {
+      g_u32x4* pp = reinterpret_cast<g_u32x4*>(pc.p + (uint64_t)i * 4u);
+      g_u32x4* mp = reinterpret_cast<g_u32x4*>(pc.m + (uint64_t)i * 4u);
+      g_u32x4* vp = reinterpret_cast<g_u32x4*>(pc.v + (uint64_t)i * 4u);
+      const u32x4 p4 = __builtin_nontemporal_load(pp);
+      const u32x4 m4 = __builtin_nontemporal_load(mp);
+      const u32x4 v4 = __builtin_nontemporal_load(vp);
+      float g[4];
+      load_grad4<DT>(pc.g + (uint64_t)i * es, g);
+      u32x4 po, mo, vo;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float pk = __uint_as_float(p4[k]), mk = __uint_as_float(m4[k]), vk = __uint_as_float(v4[k]);
+        adamw_elem(pk, mk, vk, g[k] * s, h);
+        po[k] = __float_as_uint(pk);
+        mo[k] = __float_as_uint(mk);
+        vo[k] = __float_as_uint(vk);
+      }
+      *pp = po;
+      *mp = mo;
+      *vp = vo;
+    }
+  } else {
+    for (uint32_t i = threadIdx.x; i < pc.count; i += kAdamThreads) {
+      g_f32* pp = reinterpret_cast<g_f32*>(pc.p + (uint64_t)i * 4u);
+      g_f32* mp = reinterpret_cast<g_f32*>(pc.m + (uint64_t)i * 4u);
+      g_f32* vp = reinterpret_cast<g_f32*>(pc.v + (uint64_t)i * 4u);
+      float pk = *pp, mk = *mp, vk = *vp;
+      const float g = grad_value<DT>(load_elem<DT>(pc.g + (uint64_t)i * es));
+      adamw_elem(pk, mk, vk, g * s, h);
+      *pp = pk;
+      *mp = mk;
+      *vp = vk;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host launchers
 int worker_threads() { return kThreads; }
 uint64_t resident_cap_vectors() { return kResidentCap; }
@@ -1008,6 +1095,17 @@ hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double
   void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch, &wait_ticks};
   const void* fn = p.nt_store ? fused_kernel<true>(dtype) : fused_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
+}
+
+hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, double avg, int err,
+                        gclip_result* res, hipStream_t st) {
+  const dim3 grid(plan.npieces > 0 ? plan.npieces : 1u), block(kAdamThreads);
+  switch (dtype) {
+    case GCLIP_F32: hipLaunchKernelGGL(k_adamw_clip<GCLIP_F32>, grid, block, 0, st, plan, h, max_norm, avg, err, res); break;
+    case GCLIP_F16: hipLaunchKernelGGL(k_adamw_clip<GCLIP_F16>, grid, block, 0, st, plan, h, max_norm, avg, err, res); break;
+    default: hipLaunchKernelGGL(k_adamw_clip<GCLIP_BF16>, grid, block, 0, st, plan, h, max_norm, avg, err, res); break;
+  }
+  return hipGetLastError();
 }
 
 // Workgroups of the fused kernel that fit on one compute unit at once (the

@@ -128,4 +128,33 @@ struct DevPlan {
   int32_t nseg;
 };
 
+// ---------------------------------------------------------------- AdamW on the clipped gradient
+// One piece of the optimizer's work: elements [0, count) of one tensor in the
+// four parallel lists, from the given addresses.  vec != 0 when the weights
+// and both moments are 16-byte aligned there, the gradient is aligned to 4
+// elements and count is a multiple of 4: a lane then moves 4 elements per
+// access.
+struct AdamPiece {
+  uint64_t p, g, m, v;
+  uint32_t count, vec;
+};
+
+constexpr int kAdamThreads = 256;
+constexpr uint32_t kAdamPieceElems = 8192;
+
+struct AdamPlan {
+  const AdamPiece* pieces;
+  uint32_t npieces;
+};
+
+// Per-step constants, rounded to binary32 from binary64 on the host.
+struct AdamHp {
+  float step_size;     // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+  float eps;
+  float decay;         // 1 - lr * wd
+  float b1, omb1;      // beta1, 1 - beta1
+  float b2, omb2;      // beta2, 1 - beta2
+};
+
 }  // namespace gclip

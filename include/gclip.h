@@ -213,6 +213,65 @@ gclip_status gclip_clip_(gclip_list* list, double max_norm, double avg_factor, i
 gclip_status gclip_result_read(const gclip_result* d_result, void* stream, gclip_result* h_out,
                                int32_t error_if_nonfinite);
 
+/* ---------------------------------------------------------------------------
+ * Optimizer step on the clipped gradient (AdamW).
+ *
+ * Grad clip lesson, section "Order matters: Pre-Adam": the clip runs before
+ * AdamW updates its moments m, v and the weights, so the moments only see the
+ * clipped gradient.  Backprop lesson, section "Optimizer state": AdamW keeps
+ * m and v per weight; section "Signals & checkpoints": weights, m and v are
+ * binary32.  Instead of writing the clipped gradient back and reading it
+ * again, the optimizer reads the factor the clip decided from the result
+ * block and multiplies each gradient element by it on load: the clip then
+ * costs one read pass (gclip_norm) before the optimizer.
+ *
+ * The update is AdamW as published (decoupled weight decay; the moments of
+ * Adam with bias correction), in binary32 arithmetic:
+ *   g  = s * grad                     s: the factor of the clip decision
+ *   m  = beta1 * m + (1 - beta1) * g
+ *   v  = beta2 * v + (1 - beta2) * g * g
+ *   p  = p * (1 - lr * wd) - (lr / (1 - beta1^t)) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * where t = step (>= 1, this step included).
+ * ------------------------------------------------------------------------- */
+
+/* Opaque handle: the device table of four parallel tensor lists. */
+typedef struct gclip_adamw gclip_adamw;
+
+typedef struct gclip_adamw_hparams {
+  double lr;            /* >= 0, finite */
+  double beta1, beta2;  /* in [0, 1) */
+  double eps;           /* > 0, finite */
+  double weight_decay;  /* >= 0, finite (decoupled) */
+  int64_t step;         /* >= 1: steps taken, this one included */
+} gclip_adamw_hparams;
+
+/* Build the table of one parameter list on the current device.
+ *   d_params, d_exp_avg, d_exp_avg_sq  binary32 tensors (weights, m, v),
+ *                                      aligned to 4 bytes
+ *   d_grads     gradient tensors in grad_dtype (a gclip_dtype), aligned to
+ *               the element size; the same list gclip_list_create was given
+ *   numels[i]   element count of tensor i in all four lists (>= 0)
+ * The caller keeps ownership of every buffer; they must stay allocated and
+ * must not move while the handle exists.  Any overlap between two of the
+ * 4 * n_tensors ranges is rejected with GCLIP_EINVAL.  Allocates device
+ * memory and synchronises. */
+gclip_status gclip_adamw_create(void* const* d_params, void* const* d_grads, void* const* d_exp_avg,
+                                void* const* d_exp_avg_sq, const int64_t* numels, int32_t n_tensors,
+                                int32_t grad_dtype, gclip_adamw** out);
+
+/* Free a handle's device table.  Synchronises.  NULL is a no-op. */
+gclip_status gclip_adamw_destroy(gclip_adamw* opt);
+
+/* One optimizer step on `stream`.  Reads d_result->sumsq and nonfinite (as
+ * gclip_norm left them over the same gradients, or as the caller replaced
+ * them), decides as gclip_scale does and writes scale, clipped, skipped,
+ * max_norm and decided = 1 into d_result; then, unless skipped (a NaN/Inf
+ * gradient with error_if_nonfinite: weights and moments stay bitwise
+ * unchanged), updates every weight and both moments with g = s * grad.  The
+ * gradients are only read.  One kernel launch, no allocation, no sync. */
+gclip_status gclip_adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm, double avg_factor,
+                              int32_t error_if_nonfinite, gclip_result* d_result, void* stream);
+
 /* Describe, without touching any GPU, how a list would be split: the runs
  * of each worker, in the order the kernels visit them.  Addresses only need
  * their alignment (they are never dereferenced).
