@@ -23,6 +23,7 @@ import argparse
 import glob
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -112,7 +113,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="andrea120m_f32")
-    ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto")
+    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw"], default="auto",
+                    help="adamw: time the clip fused into an AdamW step (gclip_norm + gclip_adamw_step) "
+                         "against gclip_clip_ followed by the same AdamW step")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -147,6 +150,8 @@ def main():
     # are written and no dirty lines are left to drain into the timed call)
     flush = torch.ones((2 << 30) // 8, dtype=torch.int64, device="cuda")
     gl = G.GradList(tensors)
+    if a.path == "adamw":
+        return bench_adamw(a, G, g, tensors, pristine, flush, gl)
     if a.path != "auto":
         gl.set_path(G.GCLIP_PATH_FUSED if a.path == "fused" else G.GCLIP_PATH_SPLIT)
     info = gl.info()
@@ -230,6 +235,86 @@ def main():
     gl.close()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(g)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+ADAMW_HP = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def bench_adamw(a, G, g, grads, pristine, flush, gl):
+    """The clip fused into AdamW: a step is gclip_norm over the gradients and
+    one gclip_adamw_step (weights and both moments binary32, the gradient
+    multiplied by the clip factor on load), against the separate form:
+    gclip_clip_ writing the clipped gradient back, then the same AdamW step
+    with factor 1.  Weights and moments are restored before every step, the
+    caches flushed, and each step is timed with HIP events."""
+    import torch
+    n = g.numel
+    esize = 4 if g.dtype == "f32" else 2
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    params = [torch.randn(t.numel(), device="cuda", generator=gen) * 0.02 for t in grads]
+    m = [torch.zeros(t.numel(), device="cuda") for t in grads]
+    v = [torch.zeros(t.numel(), device="cuda") for t in grads]
+    p0 = [x.clone() for x in params]
+    opt = G.AdamWList(params, grads, m, v)
+    stream = torch.cuda.current_stream()
+
+    def restore():
+        for x, y in zip(grads, pristine):
+            x.copy_(y)
+        for x, y in zip(params, p0):
+            x.copy_(y)
+        for x in m + v:
+            x.zero_()
+        flush.sum()
+
+    def run(fused, ev):
+        restore()
+        ev[0].record(stream)
+        if fused:
+            gl.norm(g.avg_factor)
+        else:
+            gl.clip_(g.max_norm, g.avg_factor)
+        ev[1].record(stream)
+        if fused:
+            opt.step(gl, step=1, max_norm=g.max_norm, avg_factor=g.avg_factor, **ADAMW_HP)
+        else:
+            opt.step(gl, step=1, max_norm=math.inf, avg_factor=1.0, **ADAMW_HP)
+        ev[2].record(stream)
+
+    times = {}
+    for fused in (True, False):
+        for _ in range(a.warmup):
+            run(fused, [torch.cuda.Event(enable_timing=True) for _ in range(3)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+        for ev in evs:
+            run(fused, ev)
+        torch.cuda.synchronize()
+        times[fused] = ([e[0].elapsed_time(e[2]) for e in evs], [e[1].elapsed_time(e[2]) for e in evs])
+    opt.close()
+    step_ms = statistics.fmean(times[True][0])
+    adam_ms = statistics.fmean(times[True][1])
+    sep_ms = statistics.fmean(times[False][0])
+    adam_bytes = n * (esize + 3 * 4 + 3 * 4)  # read g, p, m, v; write p, m, v
+    alg = n * esize + adam_bytes
+    out = {
+        "metric": "clip + AdamW step GB/s, ANDREA-120M-shaped fp32 weights, moments and grads",
+        "value": round(alg / (step_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": g.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOADS.get(a.config, a.config) + "; AdamW lr 3e-4, betas (0.9, 0.95), "
+                               "eps 1e-8, wd 0.1, step 1", "name": a.config, "path": "norm + adamw",
+                   "launches_per_step": 2, "algorithmic_bytes_per_step": alg},
+        "pct_hbm_peak": round(100.0 * alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "separate_ms_per_step": round(sep_ms, 5),
+        "separate_algorithmic_bytes": 3 * n * esize + adam_bytes,
+        "saved_vs_separate": round(1.0 - step_ms / sep_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(adam_bytes / (adam_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(adam_bytes / (adam_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "k_adamw_clip", "ms_per_launch": round(adam_ms, 5)},
+    }
     print(json.dumps(out), flush=True)
     return 0
 

@@ -997,6 +997,19 @@ __device__ __forceinline__ void adamw_elem(float& p, float& m, float& v, float g
   p = p * h.decay - h.step_size * (m / denom);
 }
 
+#ifndef GCLIP_ADAM_UNROLL
+#define GCLIP_ADAM_UNROLL 4
+#endif
+#ifndef GCLIP_ADAM_NT_STORE
+#define GCLIP_ADAM_NT_STORE 0
+#endif
+constexpr int kAdamUnroll = GCLIP_ADAM_UNROLL;
+constexpr bool kAdamNtStore = GCLIP_ADAM_NT_STORE != 0;
+#ifndef GCLIP_ADAM_NT_LOAD
+#define GCLIP_ADAM_NT_LOAD 1
+#endif
+constexpr bool kAdamNtLoad = GCLIP_ADAM_NT_LOAD != 0;
+
 template <int DT>
 __global__ __launch_bounds__(kAdamThreads) void k_adamw_clip(AdamPlan P, AdamHp h, double max_norm, double avg,
                                                              int err, gclip_result* res) {
@@ -1007,27 +1020,39 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw_clip(AdamPlan P, AdamHp 
   const AdamPiece pc = ld_table(P.pieces, blockIdx.x);
   constexpr uint32_t es = DT == GCLIP_F32 ? 4u : 2u;
   if (pc.vec) {
-    for (uint32_t i = threadIdx.x * 4u; i < pc.count; i += kAdamThreads * 4u) {
-      g_u32x4* pp = reinterpret_cast<g_u32x4*>(pc.p + (uint64_t)i * 4u);
-      g_u32x4* mp = reinterpret_cast<g_u32x4*>(pc.m + (uint64_t)i * 4u);
-      g_u32x4* vp = reinterpret_cast<g_u32x4*>(pc.v + (uint64_t)i * 4u);
-      const u32x4 p4 = __builtin_nontemporal_load(pp);
-      const u32x4 m4 = __builtin_nontemporal_load(mp);
-      const u32x4 v4 = __builtin_nontemporal_load(vp);
-      float g[4];
-      load_grad4<DT>(pc.g + (uint64_t)i * es, g);
-      u32x4 po, mo, vo;
+    // kAdamUnroll iterations at a time: every load first, then the math, then the stores
+    constexpr uint32_t stride = kAdamThreads * 4u;
+    for (uint32_t i0 = threadIdx.x * 4u; i0 < pc.count; i0 += stride * kAdamUnroll) {
+      u32x4 p4[kAdamUnroll], m4[kAdamUnroll], v4[kAdamUnroll];
+      float g[kAdamUnroll][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float pk = __uint_as_float(p4[k]), mk = __uint_as_float(m4[k]), vk = __uint_as_float(v4[k]);
-        adamw_elem(pk, mk, vk, g[k] * s, h);
-        po[k] = __float_as_uint(pk);
-        mo[k] = __float_as_uint(mk);
-        vo[k] = __float_as_uint(vk);
+      for (int u = 0; u < kAdamUnroll; ++u) {
+        const uint32_t i = i0 + (uint32_t)u * stride;
+        if (i < pc.count) {
+          p4[u] = ld_vec<kAdamNtLoad>(reinterpret_cast<const g_u32x4*>(pc.p + (uint64_t)i * 4u));
+          m4[u] = ld_vec<kAdamNtLoad>(reinterpret_cast<const g_u32x4*>(pc.m + (uint64_t)i * 4u));
+          v4[u] = ld_vec<kAdamNtLoad>(reinterpret_cast<const g_u32x4*>(pc.v + (uint64_t)i * 4u));
+          load_grad4<DT>(pc.g + (uint64_t)i * es, g[u]);
+        }
       }
-      *pp = po;
-      *mp = mo;
-      *vp = vo;
+#pragma unroll
+      for (int u = 0; u < kAdamUnroll; ++u) {
+        const uint32_t i = i0 + (uint32_t)u * stride;
+        if (i < pc.count) {
+          u32x4 po, mo, vo;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float pk = __uint_as_float(p4[u][k]), mk = __uint_as_float(m4[u][k]), vk = __uint_as_float(v4[u][k]);
+            adamw_elem(pk, mk, vk, g[u][k] * s, h);
+            po[k] = __float_as_uint(pk);
+            mo[k] = __float_as_uint(mk);
+            vo[k] = __float_as_uint(vk);
+          }
+          st_vec<kAdamNtStore>(reinterpret_cast<g_u32x4*>(pc.p + (uint64_t)i * 4u), po);
+          st_vec<kAdamNtStore>(reinterpret_cast<g_u32x4*>(pc.m + (uint64_t)i * 4u), mo);
+          st_vec<kAdamNtStore>(reinterpret_cast<g_u32x4*>(pc.v + (uint64_t)i * 4u), vo);
+        }
+      }
     }
   } else {
     for (uint32_t i = threadIdx.x; i < pc.count; i += kAdamThreads) {

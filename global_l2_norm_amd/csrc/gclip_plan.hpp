@@ -139,8 +139,11 @@ struct AdamPiece {
   uint32_t count, vec;
 };
 
+#ifndef GCLIP_ADAM_PIECE
+#define GCLIP_ADAM_PIECE 4096
+#endif
 constexpr int kAdamThreads = 256;
-constexpr uint32_t kAdamPieceElems = 8192;
+constexpr uint32_t kAdamPieceElems = GCLIP_ADAM_PIECE;
 
 struct AdamPlan {
   const AdamPiece* pieces;
