@@ -254,3 +254,39 @@ int oracle_adamw(const float* p, const void* grad, const float* m, const float* 
   }
   return 0;
 }
+
+/* Loss scaling (glossary page, introduction and section "Order changes the
+ * result"): with loss scaling the gradients are unscaled first, so that the
+ * threshold applies to their true size.  The averaging factor of a step is
+ * then a = 1 / (n_microbatches * S) for the binary32 loss scale S, and the
+ * norm, the decision and the written factor follow from it as above. */
+double oracle_amp_avg(double n_microbatches, float scale) {
+  return 1.0 / (n_microbatches * (double)scale);
+}
+
+/* The loss scale after a step.  The pages do not give the rule; it is
+ * dynamic loss scaling as published (Micikevicius et al., "Mixed precision
+ * training"): after a step whose gradients held a NaN or Inf the scale is
+ * multiplied by backoff and the count of clean steps restarts from 0;
+ * otherwise the count grows by one, and when it reaches interval the scale
+ * is multiplied by growth -- unless that product is not finite in binary32
+ * -- and the count restarts.  Products are formed in binary64 and rounded
+ * once to the binary32 scale. */
+int oracle_amp_update(float* scale, int32_t* tracker, int32_t found_inf, double growth, double backoff,
+                      int32_t interval) {
+  if (!scale || !tracker || interval < 1) return -1;
+  if (found_inf) {
+    *scale = (float)((double)*scale * backoff);
+    *tracker = 0;
+    return 0;
+  }
+  const int32_t clean = *tracker + 1;
+  if (clean == interval) {
+    const float grown = (float)((double)*scale * growth);
+    if (isfinite(grown)) *scale = grown;
+    *tracker = 0;
+  } else {
+    *tracker = clean;
+  }
+  return 0;
+}

@@ -59,6 +59,11 @@ class Oracle:
                                      ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_double, ctypes.c_int64, dp, dp, dp]
         lib.oracle_adamw.restype = ctypes.c_int
+        lib.oracle_amp_avg.argtypes = [ctypes.c_double, ctypes.c_float]
+        lib.oracle_amp_avg.restype = ctypes.c_double
+        lib.oracle_amp_update.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_int32]
+        lib.oracle_amp_update.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -168,6 +173,30 @@ class Oracle:
                 for pp, g, mm, vv in zip(params, grads, m, v)]
         return res, ([o[0] for o in outs], [o[1] for o in outs], [o[2] for o in outs])
 
+    def amp_avg(self, n_microbatches: float, scale: float) -> float:
+        """The averaging factor 1 / (n * S) of a loss-scaled step (S binary32)."""
+        return self.lib.oracle_amp_avg(float(n_microbatches), float(np.float32(scale)))
+
+    def amp_update(self, scale: float, tracker: int, found_inf: bool, growth: float = 2.0, backoff: float = 0.5,
+                   interval: int = 2000):
+        """(scale', tracker') after one step (dynamic loss scaling)."""
+        sc = ctypes.c_float(float(np.float32(scale)))
+        tr = ctypes.c_int32(int(tracker))
+        if self.lib.oracle_amp_update(ctypes.byref(sc), ctypes.byref(tr), int(bool(found_inf)), float(growth),
+                                      float(backoff), int(interval)) != 0:
+            raise ValueError("oracle_amp_update rejected its arguments")
+        return float(np.float32(sc.value)), int(tr.value)
+
+    def clip_amp_(self, arrays, dtype: str, max_norm: float, n_microbatches: float, scale: float,
+                  tracker: int = 0, growth: float = 2.0, backoff: float = 0.5, interval: int = 2000):
+        """Unscale by 1 / (n * S), clip in place -- nothing written when an
+        element is NaN or Inf (found-inf) -- and update the loss scale.
+        Returns the clip result dict plus found_inf, scale' and tracker'."""
+        r = self.clip_(arrays, dtype, max_norm, self.amp_avg(n_microbatches, scale), True)
+        sc, tr = self.amp_update(scale, tracker, r["nonfinite"], growth, backoff, interval)
+        r.update({"found_inf": r["nonfinite"], "loss_scale": sc, "growth_tracker": tr})
+        return r
+
 
 _default = None
 
@@ -228,6 +257,18 @@ def clip_(arrays, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False):
 
 def adamw(p, grad, m, v, dtype, s, lr, beta1, beta2, eps, weight_decay, step):
     return default().adamw(p, grad, m, v, dtype, s, lr, beta1, beta2, eps, weight_decay, step)
+
+
+def amp_avg(n_microbatches, scale):
+    return default().amp_avg(n_microbatches, scale)
+
+
+def amp_update(scale, tracker, found_inf, growth=2.0, backoff=0.5, interval=2000):
+    return default().amp_update(scale, tracker, found_inf, growth, backoff, interval)
+
+
+def clip_amp_(arrays, dtype, max_norm, n_microbatches, scale, tracker=0, growth=2.0, backoff=0.5, interval=2000):
+    return default().clip_amp_(arrays, dtype, max_norm, n_microbatches, scale, tracker, growth, backoff, interval)
 
 
 def clip_adamw(params, grads, m, v, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False, **hp):

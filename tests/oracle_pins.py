@@ -507,9 +507,68 @@ def pin_adamw_after_clip(o):
     assert res["skipped"] and np.array_equal(pn[0], p) and np.all(mn[0] == 0) and np.all(vn[0] == 0)
 
 
+# ------------------------------------------------------------------ loss scaling (AMP)
+def pin_amp_unscale_before_clip(o):
+    """Glossary page, "Order changes the result": with loss scaling, unscale
+    first so that the threshold applies to the true gradient.  [6, 8] scaled
+    by S = 1024 and clipped at 5 must come out as [3, 4] (unscaled); clipping
+    the scaled gradient first and unscaling after would give [3, 4] / 1024."""
+    for dt in DTYPES:
+        a = [store([6.0 * 1024, 8.0 * 1024], dt)]
+        r = o.clip_amp_(a, dt, 5.0, 1.0, 1024.0)
+        assert r["norm"] == 10.0 and r["clipped"] and not r["found_inf"]
+        assert np.array_equal(values(a[0], dt), [3.0, 4.0]), (dt, values(a[0], dt))
+    # with n microbatches the factor is 1 / (n S)
+    assert o.amp_avg(4.0, 65536.0) == 1.0 / (4.0 * 65536.0)
+    assert o.amp_avg(3.0, 1000.0) == 1.0 / 3000.0
+
+
+def pin_amp_found_inf_writes_nothing(o):
+    """A NaN or Inf in the scaled gradients is found-inf: nothing is written
+    and the scale backs off."""
+    for bad in (math.nan, math.inf):
+        a = [store([1.0, bad, 3.0], "f16")]
+        before = raw_bits(a[0], "f16").copy()
+        r = o.clip_amp_(a, "f16", 1.0, 2.0, 256.0, tracker=5, growth=2.0, backoff=0.5, interval=10)
+        assert r["found_inf"] and r["skipped"] and r["loss_scale"] == 128.0 and r["growth_tracker"] == 0
+        assert np.array_equal(raw_bits(a[0], "f16"), before)
+
+
+def pin_amp_update_closed_form(o):
+    """Clean steps grow the scale by growth every interval steps; a found-inf
+    step backs it off and restarts the count; a growth that would overflow
+    binary32 is not taken."""
+    sc, tr = 1024.0, 0
+    for k in range(1, 11):
+        sc, tr = o.amp_update(sc, tr, False, 2.0, 0.5, 4)
+        assert sc == 1024.0 * 2.0 ** (k // 4) and tr == k % 4, (k, sc, tr)
+    sc, tr = o.amp_update(sc, tr, True, 2.0, 0.5, 4)
+    assert sc == 2048.0 and tr == 0
+    big = float(np.float32(1.5 * 2.0 ** 127))
+    sc, tr = o.amp_update(big, 0, False, 2.0, 0.5, 1)
+    assert sc == big and tr == 0
+
+
+def pin_amp_update_matches_torch(o):
+    """Against torch's own loss-scale update, bit for bit, over a random
+    sequence of clean and found-inf steps and non-power-of-two factors."""
+    import torch
+    rng = np.random.default_rng(40)
+    for growth, backoff, interval in ((2.0, 0.5, 3), (1.5, 0.7, 2), (3.0, 0.25, 5)):
+        ts = torch.tensor([777.0], dtype=torch.float32)
+        tt = torch.tensor([0], dtype=torch.int32)
+        sc, tr = 777.0, 0
+        for _ in range(40):
+            inf = bool(rng.random() < 0.2)
+            torch._amp_update_scale_(ts, tt, torch.tensor([1.0 if inf else 0.0]), growth, backoff, interval)
+            sc, tr = o.amp_update(sc, tr, inf, growth, backoff, interval)
+            assert sc == float(ts.item()) and tr == int(tt.item()), (growth, backoff, interval, sc, ts.item())
+
+
 ALL_PINS = [pin_worked_6_8, pin_not_per_coordinate, pin_sgd_step_length, pin_accumulate_then_clip,
             pin_tie_passes_unchanged, pin_below_threshold_bitwise, pin_post_clip_norm, pin_single_global_factor,
             pin_joint_norm_library, pin_bruteforce_exact, pin_decode_library, pin_encode_library, pin_nonfinite,
             pin_avg_factor, pin_scale_invariance, pin_empty_and_zero_size, pin_infinite_threshold,
             pin_adamw_first_step, pin_adamw_decay_only, pin_adamw_constant_gradient, pin_adamw_matches_torch,
-            pin_adamw_after_clip]
+            pin_adamw_after_clip, pin_amp_unscale_before_clip, pin_amp_found_inf_writes_nothing,
+            pin_amp_update_closed_form, pin_amp_update_matches_torch]

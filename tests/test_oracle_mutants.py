@@ -42,6 +42,14 @@ MUTANTS = {
                                   "const double g = oracle_decode(grad, i, dt);"),
     "adamw_step_off_by_one": ("const double bc1 = 1.0 - pow(b1, (double)step);",
                               "const double bc1 = 1.0 - pow(b1, (double)(step + 1));"),
+    "amp_scale_not_inverted": ("return 1.0 / (n_microbatches * (double)scale);",
+                               "return n_microbatches * (double)scale;"),
+    "amp_microbatches_ignored": ("return 1.0 / (n_microbatches * (double)scale);", "return 1.0 / (double)scale;"),
+    "amp_backoff_keeps_count": ("    *scale = (float)((double)*scale * backoff);\n    *tracker = 0;",
+                                "    *scale = (float)((double)*scale * backoff);"),
+    "amp_grows_on_inf": ("    *scale = (float)((double)*scale * backoff);", "    *scale = (float)((double)*scale * growth);"),
+    "amp_no_overflow_guard": ("if (isfinite(grown)) *scale = grown;", "*scale = grown;"),
+    "amp_interval_off_by_one": ("if (clean == interval) {", "if (clean > interval) {"),
     "overflow_not_to_inf": ("if (E > emax) return sign | exp_all;  /* already", "if (E > emax + 1) return sign | exp_all;  /* already"),
 }
 
