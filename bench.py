@@ -14,6 +14,7 @@ pass.
 Prints one JSON line.  Other modes:
   --config NAME        another synthetic set (synth.gradsets.CONFIGS)
   --path fused|split   force the kernel path
+  --path adamw|amp     the clip fused into AdamW; the loss-scaled clip
   --profile-pass       a short run for rocprofv3 (no CPU baseline, plus a
                        calibration copy of known size for the PMC counters)
   --summarize-rocprof  turn rocprofv3 output into the summaries kept in
@@ -113,9 +114,10 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="andrea120m_f32")
-    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw"], default="auto",
+    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw", "amp"], default="auto",
                     help="adamw: time the clip fused into an AdamW step (gclip_norm + gclip_adamw_step) "
-                         "against gclip_clip_ followed by the same AdamW step")
+                         "against gclip_clip_ followed by the same AdamW step; amp: time the loss-scaled "
+                         "clip (gclip_clip_amp_) against gclip_clip_ with the same factor given by the host")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -152,6 +154,8 @@ def main():
     gl = G.GradList(tensors)
     if a.path == "adamw":
         return bench_adamw(a, G, g, tensors, pristine, flush, gl)
+    if a.path == "amp":
+        return bench_amp(a, G, g, tensors, pristine, flush, gl)
     if a.path != "auto":
         gl.set_path(G.GCLIP_PATH_FUSED if a.path == "fused" else G.GCLIP_PATH_SPLIT)
     info = gl.info()
@@ -314,6 +318,72 @@ def bench_adamw(a, G, g, grads, pristine, flush, gl):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(adam_bytes / (adam_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "k_adamw_clip", "ms_per_launch": round(adam_ms, 5)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+AMP_SCALE = 1024.0
+
+
+def bench_amp(a, G, g, grads, pristine, flush, gl):
+    """The loss-scaled clip: the list is read as gradients of a loss scaled by
+    S = 1024, so a = 1 / (n S) is read on the device from the loss-scale
+    state, and max_norm is divided by S so that the decision is that of the
+    plain run; the loss-scale update follows on the same stream.  Against
+    gclip_clip_ with the same factor given by the host.  Gradients and state
+    are restored and the caches flushed before every step."""
+    import torch
+    n_mb = 1.0 / g.avg_factor
+    max_norm = g.max_norm / AMP_SCALE
+    amp = G.AmpState(grads[0].device, AMP_SCALE)
+    stream = torch.cuda.current_stream()
+
+    def restore():
+        for x, y in zip(grads, pristine):
+            x.copy_(y)
+        amp.set(AMP_SCALE)
+        flush.sum()
+
+    def run(loss_scaled, ev):
+        restore()
+        ev[0].record(stream)
+        if loss_scaled:
+            gl.clip_amp_(max_norm, n_mb, amp)
+        else:
+            gl.clip_(max_norm, g.avg_factor / AMP_SCALE, True)
+        ev[1].record(stream)
+
+    times = {}
+    for loss_scaled in (True, False):
+        for _ in range(a.warmup):
+            run(loss_scaled, [torch.cuda.Event(enable_timing=True) for _ in range(2)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+        for ev in evs:
+            run(loss_scaled, ev)
+        torch.cuda.synchronize()
+        times[loss_scaled] = [e[0].elapsed_time(e[1]) for e in evs]
+        st, r = gl.read()
+        if loss_scaled:
+            state = amp.read()
+    esize = 4 if g.dtype == "f32" else 2
+    wrote = not (r["skipped"] or r["scale"] == 1.0)
+    alg = algorithmic_bytes(g.numel, esize, wrote)
+    ms = statistics.fmean(times[True])
+    plain_ms = statistics.fmean(times[False])
+    gbps = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": f"loss-scaled clip_grad_norm GB/s, {a.config}", "value": round(gbps, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": g.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOADS.get(a.config, a.config) + f"; read as scaled by S = {AMP_SCALE:g}, "
+                               f"{n_mb:g} microbatch(es), max_norm {max_norm:g}", "name": a.config,
+                   "path": gl.info()["path"], "launches_per_step": "clip + 1 (loss-scale update)",
+                   "algorithmic_bytes_per_step": alg, "clipped": bool(r["clipped"])},
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "host_factor_ms_per_step": round(plain_ms, 5),
+        "loss_scale_overhead_ms": round(ms - plain_ms, 5),
+        "state_after": {"scale": state[0], "growth_tracker": state[1], "found_inf": state[2]},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -16,12 +16,13 @@ import ctypes
 
 from . import _lib
 from ._lib import (GCLIP_BF16, GCLIP_F16, GCLIP_F32, GCLIP_PATH_AUTO, GCLIP_PATH_FUSED, GCLIP_PATH_SPLIT,
-                   GclipAdamwHparams, GclipListInfo, GclipPlanEntry, GclipResult)
+                   GclipAdamwHparams, GclipAmpParams, GclipListInfo, GclipPlanEntry, GclipResult)
 
 __all__ = ["GclipError", "GclipResult", "GradList", "clip_grad_norm_", "gclip_list_create", "gclip_list_destroy",
            "gclip_list_info", "gclip_list_set_path", "gclip_list_set_wait", "gclip_norm", "gclip_scale", "gclip_clip_",
            "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string", "gclip_version",
            "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step", "AdamWList",
+           "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp", "AmpState",
            "GCLIP_F32", "GCLIP_F16", "GCLIP_BF16", "GCLIP_PATH_AUTO", "GCLIP_PATH_FUSED", "GCLIP_PATH_SPLIT"]
 
 DTYPE_CODES = {"f32": GCLIP_F32, "f16": GCLIP_F16, "bf16": GCLIP_BF16}
@@ -161,6 +162,33 @@ def gclip_adamw_step(handle, lr, beta1, beta2, eps, weight_decay, step, max_norm
                                      ctypes.c_void_p(int(stream))), "gclip_adamw_step")
 
 
+def _amp_params(growth_factor, backoff_factor, growth_interval):
+    return GclipAmpParams(float(growth_factor), float(backoff_factor), int(growth_interval), 0)
+
+
+def gclip_norm_amp(handle, n_microbatches, d_amp, d_result, stream):
+    _check(_lib.lib.gclip_norm_amp(handle, float(n_microbatches), ctypes.c_void_p(int(d_amp)),
+                                   ctypes.c_void_p(int(d_result)), ctypes.c_void_p(int(stream))), "gclip_norm_amp")
+
+
+def gclip_clip_amp_(handle, max_norm, n_microbatches, d_amp, growth_factor, backoff_factor, growth_interval,
+                    d_result, stream):
+    prm = _amp_params(growth_factor, backoff_factor, growth_interval)
+    _check(_lib.lib.gclip_clip_amp_(handle, float(max_norm), float(n_microbatches), ctypes.c_void_p(int(d_amp)),
+                                    ctypes.byref(prm), ctypes.c_void_p(int(d_result)), ctypes.c_void_p(int(stream))),
+           "gclip_clip_amp_")
+
+
+def gclip_adamw_step_amp(handle, lr, beta1, beta2, eps, weight_decay, step, max_norm, n_microbatches, d_amp,
+                         growth_factor, backoff_factor, growth_interval, d_result, stream):
+    hp = GclipAdamwHparams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+    prm = _amp_params(growth_factor, backoff_factor, growth_interval)
+    _check(_lib.lib.gclip_adamw_step_amp(handle, ctypes.byref(hp), float(max_norm), float(n_microbatches),
+                                         ctypes.c_void_p(int(d_amp)), ctypes.byref(prm),
+                                         ctypes.c_void_p(int(d_result)), ctypes.c_void_p(int(stream))),
+           "gclip_adamw_step_amp")
+
+
 # ---------------------------------------------------------------- torch-facing wrapper
 def _torch_dtype_code(t):
     import torch
@@ -226,6 +254,16 @@ class GradList:
     def clip_(self, max_norm, avg_factor=1.0, error_if_nonfinite=False, stream=None):
         gclip_clip_(self.handle, max_norm, avg_factor, error_if_nonfinite, self.d_result, self._stream(stream))
 
+    def norm_amp(self, n_microbatches, amp, stream=None):
+        """Norm of the unscaled, averaged gradient: a = 1 / (n * S), S read
+        from ``amp`` on the device."""
+        gclip_norm_amp(self.handle, n_microbatches, amp.d_state, self.d_result, self._stream(stream))
+
+    def clip_amp_(self, max_norm, n_microbatches, amp, stream=None):
+        """Unscale, clip (nothing written on found-inf) and update ``amp``."""
+        gclip_clip_amp_(self.handle, max_norm, n_microbatches, amp.d_state, amp.growth_factor, amp.backoff_factor,
+                        amp.growth_interval, self.d_result, self._stream(stream))
+
     def read(self, error_if_nonfinite=False, stream=None):
         """Wait for the stream and return (status, result dict)."""
         return gclip_result_read(self.d_result, self._stream(stream), error_if_nonfinite)
@@ -240,6 +278,36 @@ class GradList:
             self.close()
         except Exception:
             pass
+
+
+class AmpState:
+    """The loss-scale state of loss-scaled steps: 16 bytes in device memory
+    (binary32 scale, int32 count of clean steps, int32 found-inf flag of the
+    last step) and the update's parameters (dynamic loss scaling)."""
+
+    def __init__(self, device, init_scale=65536.0, growth_factor=2.0, backoff_factor=0.5, growth_interval=2000):
+        import torch
+        self.buf = torch.zeros(4, dtype=torch.int32, device=device)
+        self.growth_factor = float(growth_factor)
+        self.backoff_factor = float(backoff_factor)
+        self.growth_interval = int(growth_interval)
+        self.set(init_scale, 0)
+
+    @property
+    def d_state(self):
+        return self.buf.data_ptr()
+
+    def set(self, scale, growth_tracker=0, found_inf=0):
+        import torch
+        self.buf[0:1].view(torch.float32).fill_(float(scale))
+        self.buf[1] = int(growth_tracker)
+        self.buf[2] = int(found_inf)
+
+    def read(self):
+        """(scale, growth_tracker, found_inf) after the work queued so far."""
+        import torch
+        h = self.buf.cpu()
+        return float(h[0:1].view(torch.float32).item()), int(h[1]), bool(h[2])
 
 
 class AdamWList:
@@ -281,6 +349,14 @@ class AdamWList:
         on the same stream.  The decision lands in grad_list's result block."""
         gclip_adamw_step(self.handle, lr, beta1, beta2, eps, weight_decay, step, max_norm, avg_factor,
                          error_if_nonfinite, grad_list.d_result, GradList._stream(stream))
+
+    def step_amp(self, grad_list, amp, *, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step, max_norm,
+                 n_microbatches=1.0, stream=None):
+        """A loss-scaled step: grad_list.norm_amp(n, amp) must have run first
+        on the same stream; skipped on found-inf; then ``amp`` is updated."""
+        gclip_adamw_step_amp(self.handle, lr, beta1, beta2, eps, weight_decay, step, max_norm, n_microbatches,
+                             amp.d_state, amp.growth_factor, amp.backoff_factor, amp.growth_interval,
+                             grad_list.d_result, GradList._stream(stream))
 
     def close(self):
         if getattr(self, "handle", None):

@@ -52,7 +52,18 @@ class GclipAdamwHparams(ctypes.Structure):
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
 
 
+class GclipAmpState(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("growth_tracker", ctypes.c_int32), ("found_inf", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class GclipAmpParams(ctypes.Structure):
+    _fields_ = [("growth_factor", ctypes.c_double), ("backoff_factor", ctypes.c_double),
+                ("growth_interval", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 assert ctypes.sizeof(GclipResult) == 64
+assert ctypes.sizeof(GclipAmpState) == 16
 
 
 def _declare(lib):
@@ -74,6 +85,10 @@ def _declare(lib):
         "gclip_adamw_create": ([ctypes.POINTER(vp)] * 4 + [ctypes.POINTER(i64), i32, i32, ctypes.POINTER(vp)], i32),
         "gclip_adamw_destroy": ([vp], i32),
         "gclip_adamw_step": ([vp, ctypes.POINTER(GclipAdamwHparams), dbl, dbl, i32, vp, vp], i32),
+        "gclip_norm_amp": ([vp, dbl, vp, vp, vp], i32),
+        "gclip_clip_amp_": ([vp, dbl, dbl, vp, ctypes.POINTER(GclipAmpParams), vp, vp], i32),
+        "gclip_adamw_step_amp": ([vp, ctypes.POINTER(GclipAdamwHparams), dbl, dbl, vp,
+                                  ctypes.POINTER(GclipAmpParams), vp, vp], i32),
         "gclip_status_string": ([i32], ctypes.c_char_p),
         "gclip_last_hip_error": ([], i32),
         "gclip_version": ([], i32),
@@ -107,4 +122,5 @@ lib = load()
 EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_list_set_path",
            "gclip_list_set_wait", "gclip_norm",
            "gclip_scale", "gclip_clip_", "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string",
-           "gclip_last_hip_error", "gclip_version", "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step")
+           "gclip_last_hip_error", "gclip_version", "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step",
+           "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp")

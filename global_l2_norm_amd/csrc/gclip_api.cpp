@@ -24,14 +24,16 @@ namespace gclip {
 int worker_threads();
 uint64_t resident_cap_vectors();
 ChunkShape chunk_shape();
-hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result* res, hipStream_t st);
-hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
+hipError_t launch_norm(const DevPlan& p, int32_t dtype, AvgSrc avg, gclip_result* res, hipStream_t st);
+hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         hipStream_t st);
-hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
+hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         uint32_t epoch, uint64_t wait_ticks, hipStream_t st);
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu);
-hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, double avg, int err,
+hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,
                         gclip_result* res, hipStream_t st);
+hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
+                             int32_t interval, hipStream_t s);
 }  // namespace gclip
 
 // How long a workgroup of the fused kernel waits at the grid-wide decision
@@ -356,7 +358,8 @@ gclip_status gclip_norm(gclip_list* list, double avg_factor, gclip_result* d_res
   gclip_status st = check_device(list);
   if (st != GCLIP_OK) return st;
   const hipError_t e =
-      gclip::launch_norm(list->dev, list->plan.dtype, avg_factor, d_result, static_cast<hipStream_t>(stream));
+      gclip::launch_norm(list->dev, list->plan.dtype, gclip::AvgSrc{avg_factor, nullptr}, d_result,
+                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 
@@ -365,27 +368,65 @@ gclip_status gclip_scale(gclip_list* list, double max_norm, double avg_factor, i
   if (!list || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(avg_factor)) return GCLIP_EINVAL;
   gclip_status st = check_device(list);
   if (st != GCLIP_OK) return st;
-  const hipError_t e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg_factor,
-                                           error_if_nonfinite ? 1 : 0, d_result, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      gclip::launch_scale(list->dev, list->plan.dtype, max_norm, gclip::AvgSrc{avg_factor, nullptr},
+                          error_if_nonfinite ? 1 : 0, d_result, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
+
+namespace {
+// The path's kernels on an already validated list: fused, or norm then scale.
+hipError_t launch_clip(gclip_list* list, double max_norm, gclip::AvgSrc avg, int err, gclip_result* d_result,
+                       hipStream_t s) {
+  if (list->path == GCLIP_PATH_FUSED) {
+    if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
+    return gclip::launch_fused(list->dev, list->plan.dtype, max_norm, avg, err, d_result, list->epoch,
+                               list->wait_ticks, s);
+  }
+  hipError_t e = gclip::launch_norm(list->dev, list->plan.dtype, avg, d_result, s);
+  if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg, err, d_result, s);
+  return e;
+}
+
+bool amp_state_ptr_ok(const gclip_amp_state* a) { return a && reinterpret_cast<uintptr_t>(a) % 4 == 0; }
+bool amp_params_ok(const gclip_amp_params* a) {
+  return a && std::isfinite(a->growth_factor) && a->growth_factor >= 1.0 && std::isfinite(a->backoff_factor) &&
+         a->backoff_factor > 0.0 && a->backoff_factor <= 1.0 && a->growth_interval >= 1;
+}
+}  // namespace
 
 gclip_status gclip_clip_(gclip_list* list, double max_norm, double avg_factor, int32_t error_if_nonfinite,
                          gclip_result* d_result, void* stream) {
   if (!list || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(avg_factor)) return GCLIP_EINVAL;
   gclip_status st = check_device(list);
   if (st != GCLIP_OK) return st;
+  const hipError_t e = launch_clip(list, max_norm, gclip::AvgSrc{avg_factor, nullptr}, error_if_nonfinite ? 1 : 0,
+                                   d_result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_norm_amp(gclip_list* list, double n_microbatches, const gclip_amp_state* d_amp,
+                            gclip_result* d_result, void* stream) {
+  if (!list || !result_ptr_ok(d_result) || !factor_ok(n_microbatches) || !amp_state_ptr_ok(d_amp))
+    return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
+  const hipError_t e = gclip::launch_norm(list->dev, list->plan.dtype, gclip::AvgSrc{n_microbatches, &d_amp->scale},
+                                          d_result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_clip_amp_(gclip_list* list, double max_norm, double n_microbatches, gclip_amp_state* d_amp,
+                             const gclip_amp_params* amp, gclip_result* d_result, void* stream) {
+  if (!list || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(n_microbatches) ||
+      !amp_state_ptr_ok(d_amp) || !amp_params_ok(amp))
+    return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int err = error_if_nonfinite ? 1 : 0;
-  hipError_t e;
-  if (list->path == GCLIP_PATH_FUSED) {
-    if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
-    e = gclip::launch_fused(list->dev, list->plan.dtype, max_norm, avg_factor, err, d_result, list->epoch,
-                            list->wait_ticks, s);
-  } else {
-    e = gclip::launch_norm(list->dev, list->plan.dtype, avg_factor, d_result, s);
-    if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg_factor, err, d_result, s);
-  }
+  hipError_t e = launch_clip(list, max_norm, gclip::AvgSrc{n_microbatches, &d_amp->scale}, 1, d_result, s);
+  if (e == hipSuccess)
+    e = gclip::launch_amp_update(d_result, d_amp, amp->growth_factor, amp->backoff_factor, amp->growth_interval, s);
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 
@@ -465,9 +506,11 @@ gclip_status gclip_adamw_destroy(gclip_adamw* opt) {
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 
-gclip_status gclip_adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm, double avg_factor,
-                              int32_t error_if_nonfinite, gclip_result* d_result, void* stream) {
-  if (!opt || !hp || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(avg_factor)) return GCLIP_EINVAL;
+namespace {
+gclip_status adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm, gclip::AvgSrc avg,
+                        int32_t error_if_nonfinite, gclip_result* d_result, const gclip_amp_state* amp_state,
+                        const gclip_amp_params* amp, void* stream) {
+  if (!opt || !hp || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(avg.a)) return GCLIP_EINVAL;
   if (!std::isfinite(hp->lr) || hp->lr < 0.0 || !unit_interval(hp->beta1) || !unit_interval(hp->beta2) ||
       !std::isfinite(hp->eps) || hp->eps <= 0.0 || !std::isfinite(hp->weight_decay) || hp->weight_decay < 0.0 ||
       hp->step < 1)
@@ -488,9 +531,27 @@ gclip_status gclip_adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, d
   h.b2 = (float)hp->beta2;
   h.omb2 = (float)(1.0 - hp->beta2);
   gclip::AdamPlan plan{opt->pieces, opt->npieces};
-  e = gclip::launch_adamw(plan, opt->dtype, h, max_norm, avg_factor, error_if_nonfinite ? 1 : 0, d_result,
-                          static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  e = gclip::launch_adamw(plan, opt->dtype, h, max_norm, avg, error_if_nonfinite ? 1 : 0, d_result, s);
+  if (e == hipSuccess && amp)
+    e = gclip::launch_amp_update(d_result, const_cast<gclip_amp_state*>(amp_state), amp->growth_factor,
+                                 amp->backoff_factor, amp->growth_interval, s);
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+}  // namespace
+
+gclip_status gclip_adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm, double avg_factor,
+                              int32_t error_if_nonfinite, gclip_result* d_result, void* stream) {
+  return adamw_step(opt, hp, max_norm, gclip::AvgSrc{avg_factor, nullptr}, error_if_nonfinite, d_result, nullptr,
+                    nullptr, stream);
+}
+
+gclip_status gclip_adamw_step_amp(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm,
+                                  double n_microbatches, gclip_amp_state* d_amp, const gclip_amp_params* amp,
+                                  gclip_result* d_result, void* stream) {
+  if (!amp_state_ptr_ok(d_amp) || !amp_params_ok(amp)) return GCLIP_EINVAL;
+  return adamw_step(opt, hp, max_norm, gclip::AvgSrc{n_microbatches, &d_amp->scale}, 1, d_result, d_amp, amp,
+                    stream);
 }
 
 gclip_status gclip_result_read(const gclip_result* d_result, void* stream, gclip_result* h_out,

@@ -657,11 +657,25 @@ __device__ __forceinline__ Decision decide(double sumsq, int nonfinite, double m
   return d;
 }
 
+// The averaging factor: given by the host, or 1 / (n * S) with the loss
+// scale S read from device memory (loss-scaled steps).
+__device__ __forceinline__ double avg_value(const AvgSrc& s) {
+  return s.scale ? 1.0 / (s.a * (double)*s.scale) : s.a;
+}
+
+// The flag of a NaN/Inf element: the raw sum of squares is not finite.  An
+// averaging factor that is not finite and positive (only possible when it
+// comes from a loss scale that is not) counts as one too, so that nothing
+// is written.
+__device__ __forceinline__ int nonfinite_of(double S, double avg) {
+  return (__builtin_isfinite(S) && __builtin_isfinite(avg) && avg > 0.0) ? 0 : 1;
+}
+
 __device__ __forceinline__ void write_norm(gclip_result* res, double S, double avg) {
   const double sumsq = (avg * avg) * S;
   res->sumsq = sumsq;
   res->norm = sqrt(sumsq);
-  res->nonfinite = __builtin_isfinite(S) ? 0 : 1;
+  res->nonfinite = nonfinite_of(S, avg);
 }
 
 __device__ __forceinline__ void write_decision(gclip_result* res, const Decision& d, double max_norm) {
@@ -766,7 +780,8 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
 // The fused kernel adds the same values in the same order, so both paths
 // give the same bits.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, double avg, gclip_result* res) {
+__global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, AvgSrc avs, gclip_result* res) {
+  const double avg = avg_value(avs);
   __shared__ double red[kWaves];
   __shared__ ClaimSlots sl;
   __shared__ int flag;
@@ -802,8 +817,9 @@ __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, doubl
 // Kernel 3: the decision from the device result block, then g <- g * s over
 // the chunks each workgroup claims, or no write at all.
 template <int DT, bool NTS>
-__global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_norm, double avg, int err,
+__global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_norm, AvgSrc avs, int err,
                                                          gclip_result* res) {
+  const double avg = avg_value(avs);
   __shared__ ClaimSlots sl;
   __shared__ HandSlots hs;
   __shared__ int flag;
@@ -853,9 +869,10 @@ __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSl
 // workgroups that do see the decision -- in the end the last one to finish
 // -- scale the handed-back blocks from memory.
 template <int DT, bool NTS>
-__global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, double max_norm, double avg, int err,
+__global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, double max_norm, AvgSrc avs, int err,
                                                                  gclip_result* res, uint32_t epoch,
                                                                  uint64_t wait_ticks) {
+  const double avg = avg_value(avs);
   __shared__ u32x4 keep_lds[kLdsSteps * kThreads];
   __shared__ double red[kWaves];
   __shared__ ClaimSlots sl;
@@ -913,8 +930,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
     poison_partials(p);
     if (t == 0) {
       const double sumsq = (avg * avg) * S;
-      const int nonfinite = __builtin_isfinite(S) ? 0 : 1;
-      const Decision d = decide(sumsq, nonfinite, max_norm, avg, err);
+      const Decision d = decide(sumsq, nonfinite_of(S, avg), max_norm, avg, err);
       write_norm(res, S, avg);
       write_decision(res, d, max_norm);
       res->status = 0;
@@ -1011,8 +1027,9 @@ constexpr bool kAdamNtStore = GCLIP_ADAM_NT_STORE != 0;
 constexpr bool kAdamNtLoad = GCLIP_ADAM_NT_LOAD != 0;
 
 template <int DT>
-__global__ __launch_bounds__(kAdamThreads) void k_adamw_clip(AdamPlan P, AdamHp h, double max_norm, double avg,
+__global__ __launch_bounds__(kAdamThreads) void k_adamw_clip(AdamPlan P, AdamHp h, double max_norm, AvgSrc avs,
                                                              int err, gclip_result* res) {
+  const double avg = avg_value(avs);
   const Decision d = decide(res->sumsq, res->nonfinite, max_norm, avg, err);
   if (blockIdx.x == 0 && threadIdx.x == 0) write_decision(res, d, max_norm);
   if (d.skip || blockIdx.x >= P.npieces) return;
@@ -1082,7 +1099,7 @@ ChunkShape chunk_shape() {
   return c;
 }
 
-hipError_t launch_norm(const DevPlan& p, int32_t dtype, double avg, gclip_result* res, hipStream_t st) {
+hipError_t launch_norm(const DevPlan& p, int32_t dtype, AvgSrc avg, gclip_result* res, hipStream_t st) {
   const dim3 grid((unsigned)p.nworkers), block(kThreads);
   switch (dtype) {
     case GCLIP_F32: hipLaunchKernelGGL(k_grad_norm_partial<GCLIP_F32>, grid, block, 0, st, p, avg, res); break;
@@ -1106,7 +1123,7 @@ const void* fused_kernel(int32_t dtype) {
                               : (const void*)k_grad_clip_fused<GCLIP_BF16, NTS>;
 }
 
-hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
+hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         hipStream_t st) {
   DevPlan pc = p;
   void* args[] = {&pc, &max_norm, &avg, &err, &res};
@@ -1114,7 +1131,7 @@ hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, double
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }
 
-hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double avg, int err, gclip_result* res,
+hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         uint32_t epoch, uint64_t wait_ticks, hipStream_t st) {
   DevPlan pc = p;
   void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch, &wait_ticks};
@@ -1122,7 +1139,7 @@ hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, double
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }
 
-hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, double avg, int err,
+hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,
                         gclip_result* res, hipStream_t st) {
   const dim3 grid(plan.npieces > 0 ? plan.npieces : 1u), block(kAdamThreads);
   switch (dtype) {
@@ -1130,6 +1147,37 @@ hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, do
     case GCLIP_F16: hipLaunchKernelGGL(k_adamw_clip<GCLIP_F16>, grid, block, 0, st, plan, h, max_norm, avg, err, res); break;
     default: hipLaunchKernelGGL(k_adamw_clip<GCLIP_BF16>, grid, block, 0, st, plan, h, max_norm, avg, err, res); break;
   }
+  return hipGetLastError();
+}
+
+// The loss scale after a step (dynamic loss scaling as published by
+// Micikevicius et al.): found-inf multiplies it by backoff and restarts the
+// count of clean steps; a clean step counts, and the interval-th one
+// multiplies the scale by growth unless that is not finite in binary32.
+// One thread; the step's kernels ran before it on the same stream.
+__global__ void k_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
+                             int32_t interval) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  const int32_t inf = res->nonfinite ? 1 : 0;
+  st->found_inf = inf;
+  if (inf) {
+    st->scale = (float)((double)st->scale * backoff);
+    st->growth_tracker = 0;
+    return;
+  }
+  const int32_t clean = st->growth_tracker + 1;
+  if (clean == interval) {
+    const float grown = (float)((double)st->scale * growth);
+    if (__builtin_isfinite(grown)) st->scale = grown;
+    st->growth_tracker = 0;
+  } else {
+    st->growth_tracker = clean;
+  }
+}
+
+hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
+                             int32_t interval, hipStream_t s) {
+  hipLaunchKernelGGL(k_amp_update, dim3(1), dim3(64), 0, s, res, st, growth, backoff, interval);
   return hipGetLastError();
 }
 

@@ -128,6 +128,14 @@ struct DevPlan {
   int32_t nseg;
 };
 
+// The averaging factor of a call: a itself, or, for a loss-scaled step,
+// 1 / (a * S) with a = n_microbatches and the binary32 loss scale S read from
+// device memory when the kernel starts.
+struct AvgSrc {
+  double a;
+  const float* scale;
+};
+
 // ---------------------------------------------------------------- AdamW on the clipped gradient
 // One piece of the optimizer's work: elements [0, count) of one tensor in the
 // four parallel lists, from the given addresses.  vec != 0 when the weights

@@ -272,6 +272,58 @@ gclip_status gclip_adamw_destroy(gclip_adamw* opt);
 gclip_status gclip_adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm, double avg_factor,
                               int32_t error_if_nonfinite, gclip_result* d_result, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Loss-scaled steps (mixed precision).
+ *
+ * Glossary page, introduction and section "Order changes the result": with
+ * loss scaling the order of unscaling and clipping matters -- unscale first,
+ * so that the threshold applies to the gradients' true size.  Here the
+ * unscaling is folded into the averaging factor: a = 1 / (n_microbatches * S)
+ * with the loss scale S read from device memory when the kernels start, so
+ * the norm is that of the unscaled, averaged gradient and the written factor
+ * is a * coef.  A NaN/Inf element is found-inf: nothing is written (the stop
+ * switch is always on) and the optimizer step is to be skipped.  After the
+ * step the loss scale is updated on the device, by dynamic loss scaling as
+ * published (the pages do not give the rule): found-inf multiplies S by
+ * backoff_factor and restarts the count of clean steps; otherwise the count
+ * grows, and every growth_interval clean steps S is multiplied by
+ * growth_factor (unless that is not finite in binary32).
+ * ------------------------------------------------------------------------- */
+
+/* Loss-scale state, 16 bytes in DEVICE memory that the caller owns. */
+typedef struct gclip_amp_state {
+  float scale;             /* loss scale S > 0 (binary32) */
+  int32_t growth_tracker;  /* clean steps since the scale last changed */
+  int32_t found_inf;       /* 1 when the last step's gradients held a NaN/Inf */
+  int32_t reserved;
+} gclip_amp_state;
+
+typedef struct gclip_amp_params {
+  double growth_factor;     /* >= 1, finite */
+  double backoff_factor;    /* in (0, 1] */
+  int32_t growth_interval;  /* >= 1 */
+  int32_t reserved;
+} gclip_amp_params;
+
+/* gclip_norm of the unscaled, averaged gradient: a = 1 / (n_microbatches * S)
+ * with S = d_amp->scale.  n_microbatches > 0 and finite.  Does not update
+ * d_amp (gclip_clip_amp_ or gclip_adamw_step_amp do, after the step). */
+gclip_status gclip_norm_amp(gclip_list* list, double n_microbatches, const gclip_amp_state* d_amp,
+                            gclip_result* d_result, void* stream);
+
+/* gclip_clip_ with a = 1 / (n_microbatches * S) and error_if_nonfinite on,
+ * then the loss-scale update of d_amp (found_inf, scale, growth_tracker).
+ * The path's kernels plus one single-thread kernel; no allocation, no sync. */
+gclip_status gclip_clip_amp_(gclip_list* list, double max_norm, double n_microbatches, gclip_amp_state* d_amp,
+                             const gclip_amp_params* amp, gclip_result* d_result, void* stream);
+
+/* gclip_adamw_step with a = 1 / (n_microbatches * S) and error_if_nonfinite
+ * on (found-inf: weights and moments stay unchanged), then the loss-scale
+ * update.  To follow gclip_norm_amp over the same gradients and d_amp. */
+gclip_status gclip_adamw_step_amp(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm,
+                                  double n_microbatches, gclip_amp_state* d_amp, const gclip_amp_params* amp,
+                                  gclip_result* d_result, void* stream);
+
 /* Describe, without touching any GPU, how a list would be split: the runs
  * of each worker, in the order the kernels visit them.  Addresses only need
  * their alignment (they are never dereferenced).
