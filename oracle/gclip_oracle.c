@@ -218,6 +218,46 @@ int oracle_clip(void* const* ptrs, const int64_t* numels, int32_t n, int32_t dt,
   return oracle_scale(ptrs, numels, n, dt, s);
 }
 
+/* Per-tensor clipping (grad clip lesson, section "Two variants: Per-Tensor
+ * or Global"): every tensor is clipped on its own, by its own norm -- the
+ * case split of the global clip with one tensor in place of the whole list.
+ * Readings where the pages are silent: the averaging factor a multiplies
+ * every tensor before its norm is taken, as in the global clip; the stop
+ * switch stops the whole update, so one NaN/Inf anywhere in the list and no
+ * tensor is written.
+ * Per tensor t: tout[3t] = sumsq, tout[3t+1] = norm, tout[3t+2] = the factor
+ * written (1 when nothing is written); tflags[2t] = nonfinite, tflags[2t+1] =
+ * clipped.  For the list: out[0] = sumsq, out[1] = norm; flags[0] = any
+ * nonfinite, flags[1] = any tensor clipped, flags[2] = skipped. */
+int oracle_clip_per_tensor(void* const* ptrs, const int64_t* numels, int32_t n, int32_t dt, double max_norm,
+                           double avg, int32_t error_if_nonfinite, double* tout, int32_t* tflags, double* out,
+                           int32_t* flags) {
+  if (n < 0 || !out || !flags || (n > 0 && (!tout || !tflags))) return -1;
+  double list_sumsq;
+  int32_t list_nf;
+  if (oracle_sumsq((const void* const*)ptrs, numels, n, dt, avg, &list_sumsq, &list_nf) != 0) return -1;
+  const int32_t skip = (list_nf && error_if_nonfinite) ? 1 : 0;
+  int32_t any_clipped = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    double s_t;
+    int32_t nf_t, clipped_t, unused;
+    oracle_sumsq((const void* const*)&ptrs[t], &numels[t], 1, dt, avg, &tout[3 * t], &nf_t);
+    tout[3 * t + 1] = sqrt(tout[3 * t]);
+    oracle_decide(tout[3 * t + 1], nf_t, max_norm, avg, error_if_nonfinite, &s_t, &clipped_t, &unused);
+    tout[3 * t + 2] = skip ? 1.0 : s_t;
+    tflags[2 * t] = nf_t;
+    tflags[2 * t + 1] = clipped_t;
+    any_clipped |= clipped_t;
+    if (!skip) oracle_scale(&ptrs[t], &numels[t], 1, dt, s_t);
+  }
+  out[0] = list_sumsq;
+  out[1] = sqrt(list_sumsq);
+  flags[0] = list_nf;
+  flags[1] = any_clipped;
+  flags[2] = skip;
+  return 0;
+}
+
 /* One AdamW step on one tensor, after the clip.  Grad clip lesson, section
  * "Order matters: Pre-Adam": the clip runs before AdamW's moments m, v and
  * the weights are updated, so the moments only ever see the clipped

@@ -54,6 +54,9 @@ class Oracle:
         lib.oracle_clip.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_int32, dp, i32p]
         lib.oracle_clip.restype = ctypes.c_int
+        lib.oracle_clip_per_tensor.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_double, ctypes.c_double, ctypes.c_int32, dp, i32p, dp, i32p]
+        lib.oracle_clip_per_tensor.restype = ctypes.c_int
         f32p = ctypes.POINTER(ctypes.c_float)
         lib.oracle_adamw.argtypes = [f32p, vp, f32p, f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double,
                                      ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
@@ -173,6 +176,28 @@ class Oracle:
                 for pp, g, mm, vv in zip(params, grads, m, v)]
         return res, ([o[0] for o in outs], [o[1] for o in outs], [o[2] for o in outs])
 
+    def clip_per_tensor_(self, arrays, dtype: str, max_norm: float, avg_factor: float = 1.0,
+                         error_if_nonfinite: bool = False) -> dict:
+        """Per-tensor clipping in place: every tensor by its own norm (grad
+        clip lesson, "Two variants: Per-Tensor or Global").  Returns the
+        list's sumsq, norm and flags, and under "tensors" one dict per tensor
+        (sumsq, norm, scale written, nonfinite, clipped)."""
+        ptrs, numels, n = _marshal(arrays, dtype)
+        tout = np.zeros(3 * max(n, 1), dtype=np.float64)
+        tfl = np.zeros(2 * max(n, 1), dtype=np.int32)
+        out = (ctypes.c_double * 2)()
+        flags = (ctypes.c_int32 * 3)()
+        rc = self.lib.oracle_clip_per_tensor(ptrs, numels, n, _CODE[dtype], float(max_norm), float(avg_factor),
+                                             int(bool(error_if_nonfinite)),
+                                             tout.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                             tfl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out, flags)
+        if rc != 0:
+            raise ValueError("oracle_clip_per_tensor rejected its arguments")
+        tensors = [{"sumsq": tout[3 * t], "norm": tout[3 * t + 1], "scale": tout[3 * t + 2],
+                    "nonfinite": bool(tfl[2 * t]), "clipped": bool(tfl[2 * t + 1])} for t in range(n)]
+        return {"sumsq": out[0], "norm": out[1], "nonfinite": bool(flags[0]), "clipped": bool(flags[1]),
+                "skipped": bool(flags[2]), "tensors": tensors}
+
     def amp_avg(self, n_microbatches: float, scale: float) -> float:
         """The averaging factor 1 / (n * S) of a loss-scaled step (S binary32)."""
         return self.lib.oracle_amp_avg(float(n_microbatches), float(np.float32(scale)))
@@ -257,6 +282,10 @@ def clip_(arrays, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False):
 
 def adamw(p, grad, m, v, dtype, s, lr, beta1, beta2, eps, weight_decay, step):
     return default().adamw(p, grad, m, v, dtype, s, lr, beta1, beta2, eps, weight_decay, step)
+
+
+def clip_per_tensor_(arrays, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False):
+    return default().clip_per_tensor_(arrays, dtype, max_norm, avg_factor, error_if_nonfinite)
 
 
 def amp_avg(n_microbatches, scale):

@@ -565,10 +565,108 @@ def pin_amp_update_matches_torch(o):
             assert sc == float(ts.item()) and tr == int(tt.item()), (growth, backoff, interval, sc, ts.item())
 
 
+# ---------------------------------------------------------------- per-tensor clipping
+def pin_per_tensor_contrast(o):
+    """Grad clip lesson, "Two variants: Per-Tensor or Global": each tensor is
+    clipped by its own norm.  [6, 8] and [0.3, 0.4] at c = 1: the first
+    (norm 10) becomes [0.6, 0.8], the second (norm 0.5) passes unchanged, so
+    the ratio of the two norms goes from 20 to 2 (the distortion the page
+    names); the global clip keeps the ratio and shrinks both."""
+    for dt in DTYPES:
+        a = [store([6.0, 8.0], dt), store([0.3, 0.4], dt)]
+        second = raw_bits(a[1], dt).copy()
+        r = o.clip_per_tensor_(a, dt, 1.0)
+        t0, t1 = r["tensors"]
+        assert t0["norm"] == 10.0 and t0["clipped"] and t0["scale"] == 0.1
+        assert not t1["clipped"] and t1["scale"] == 1.0
+        assert abs(t1["norm"] - math.hypot(values(store([0.3], dt), dt)[0], values(store([0.4], dt), dt)[0])) \
+            <= 1e-15
+        assert np.array_equal(raw_bits(a[1], dt), second)
+        assert np.array_equal(raw_bits(a[0], dt), raw_bits(store([0.6, 0.8], dt), dt)), (dt, values(a[0], dt))
+        assert r["clipped"] and not r["skipped"] and not r["nonfinite"]
+        assert abs(r["norm"] - math.sqrt(100.0 + t1["sumsq"])) <= 1e-14 * r["norm"]
+        g = [store([6.0, 8.0], dt), store([0.3, 0.4], dt)]
+        o.clip_(g, dt, 1.0)
+        ratio_global = np.linalg.norm(values(g[0], dt)) / np.linalg.norm(values(g[1], dt))
+        ratio_tensor = np.linalg.norm(values(a[0], dt)) / np.linalg.norm(values(a[1], dt))
+        assert abs(ratio_global - 20.0) < 0.2 and abs(ratio_tensor - 2.0) < 0.02, (ratio_global, ratio_tensor)
+
+
+def pin_per_tensor_library(o):
+    """Per-tensor norms against numpy.linalg.norm tensor by tensor (so the
+    tensor boundaries are right), the list norm against the joint norm, and
+    the clipped values against torch.nn.utils.clip_grad_norm_ applied to
+    each tensor alone in float64: torch divides by norm + 1e-6, so a clipped
+    tensor may differ by that relative amount, an unclipped one not at all."""
+    import torch
+    rng = np.random.default_rng(60)
+    for dt in DTYPES:
+        sizes_sd = ((1000, 1.0), (37, 0.01), (1, 5.0), (513, 0.03), (0, 1.0), (200, 0.5))
+        arrs = [store(rng.standard_normal(n) * sd, dt) for n, sd in sizes_sd]
+        before = [values(x, dt) for x in arrs]
+        c = 1.0
+        r = o.clip_per_tensor_(arrs, dt, c)
+        joint = math.sqrt(sum(np.linalg.norm(v) ** 2 for v in before))
+        assert abs(r["norm"] - joint) <= 1e-13 * joint
+        for k, (t, v, x) in enumerate(zip(r["tensors"], before, arrs)):
+            nrm = float(np.linalg.norm(v))
+            assert abs(t["norm"] - nrm) <= 1e-13 * max(nrm, 1e-300), (dt, k)
+            assert t["clipped"] == (nrm > c), (dt, k)
+            prm = torch.nn.Parameter(torch.zeros(v.size, dtype=torch.float64))
+            prm.grad = torch.from_numpy(v.copy())
+            torch.nn.utils.clip_grad_norm_([prm], c)
+            ref = prm.grad.numpy()
+            got = values(x, dt)
+            if not t["clipped"]:
+                assert np.array_equal(raw_bits(x, dt), raw_bits(store(v, dt), dt)), (dt, k)
+            else:
+                tol = (2e-6 / nrm) * np.abs(ref) + ulp(ref, dt)
+                assert np.all(np.abs(got - ref) <= tol), (dt, k)
+                # after the clip the tensor's norm is c, up to the storage rounding
+                post = float(np.linalg.norm(got))
+                assert abs(post - c) <= 4 * float(ulp(np.array([1.0]), dt)[0]) * c, (dt, k, post)
+
+
+def pin_per_tensor_single_is_global(o):
+    """A one-tensor list: per-tensor and global clipping are the same
+    operation, bit for bit, also with averaging."""
+    rng = np.random.default_rng(61)
+    for dt in DTYPES:
+        for n, sd, c, a in ((700, 1.0, 5.0, 1.0), (700, 1.0, 50.0, 0.25), (33, 0.1, 0.2, 1.0 / 3.0)):
+            x = store(rng.standard_normal(n) * sd, dt)
+            g, t = [x.copy()], [x.copy()]
+            rg = o.clip_(g, dt, c, a)
+            rt = o.clip_per_tensor_(t, dt, c, a)
+            assert np.array_equal(raw_bits(g[0], dt), raw_bits(t[0], dt)), (dt, n, c, a)
+            assert rt["tensors"][0]["scale"] == rg["scale"] and rt["tensors"][0]["norm"] == rg["norm"]
+
+
+def pin_per_tensor_nonfinite(o):
+    """With the stop switch a NaN/Inf anywhere stops the whole update (no
+    tensor written); without it, the other tensors are clipped as usual and
+    the tensor with the NaN keeps its values (NaN > c is false)."""
+    for dt in DTYPES:
+        lst = [[3.0, 4.0], [math.nan, 1.0], [30.0, 40.0], []]
+        a = [store(v, dt) for v in lst]
+        before = [raw_bits(x, dt).copy() for x in a]
+        r = o.clip_per_tensor_(a, dt, 1.0, 1.0, True)
+        assert r["skipped"] and r["nonfinite"] and all(t["scale"] == 1.0 for t in r["tensors"])
+        assert all(np.array_equal(raw_bits(x, dt), b) for x, b in zip(a, before))
+        r = o.clip_per_tensor_(a, dt, 1.0, 1.0, False)
+        assert not r["skipped"] and r["nonfinite"]
+        assert [t["nonfinite"] for t in r["tensors"]] == [False, True, False, False]
+        assert [t["clipped"] for t in r["tensors"]] == [True, False, True, False]
+        assert np.array_equal(raw_bits(a[0], dt), raw_bits(store([0.6, 0.8], dt), dt))
+        assert np.array_equal(raw_bits(a[2], dt), raw_bits(store([0.6, 0.8], dt), dt))
+        assert np.array_equal(raw_bits(a[1], dt), before[1])
+        assert r["tensors"][3]["norm"] == 0.0 and r["tensors"][3]["scale"] == 1.0
+
+
 ALL_PINS = [pin_worked_6_8, pin_not_per_coordinate, pin_sgd_step_length, pin_accumulate_then_clip,
             pin_tie_passes_unchanged, pin_below_threshold_bitwise, pin_post_clip_norm, pin_single_global_factor,
             pin_joint_norm_library, pin_bruteforce_exact, pin_decode_library, pin_encode_library, pin_nonfinite,
             pin_avg_factor, pin_scale_invariance, pin_empty_and_zero_size, pin_infinite_threshold,
             pin_adamw_first_step, pin_adamw_decay_only, pin_adamw_constant_gradient, pin_adamw_matches_torch,
             pin_adamw_after_clip, pin_amp_unscale_before_clip, pin_amp_found_inf_writes_nothing,
-            pin_amp_update_closed_form, pin_amp_update_matches_torch]
+            pin_amp_update_closed_form, pin_amp_update_matches_torch, pin_per_tensor_contrast,
+            pin_per_tensor_library, pin_per_tensor_single_is_global, pin_per_tensor_nonfinite]

@@ -50,6 +50,14 @@ MUTANTS = {
     "amp_grows_on_inf": ("    *scale = (float)((double)*scale * backoff);", "    *scale = (float)((double)*scale * growth);"),
     "amp_no_overflow_guard": ("if (isfinite(grown)) *scale = grown;", "*scale = grown;"),
     "amp_interval_off_by_one": ("if (clean == interval) {", "if (clean > interval) {"),
+    "per_tensor_uses_list_norm": ("oracle_decide(tout[3 * t + 1], nf_t,", "oracle_decide(sqrt(list_sumsq), nf_t,"),
+    "per_tensor_takes_next_tensor": ("oracle_sumsq((const void* const*)&ptrs[t], &numels[t], 1, dt, avg, &tout[3 * t], &nf_t);",
+                                     "oracle_sumsq((const void* const*)&ptrs[t], &numels[t], t + 1 < n ? 2 : 1, dt, avg, &tout[3 * t], &nf_t);"),
+    "per_tensor_stop_only_bad_tensor": ("    tout[3 * t + 2] = skip ? 1.0 : s_t;", "    tout[3 * t + 2] = unused ? 1.0 : s_t;"),
+    "per_tensor_stop_ignored": ("    if (!skip) oracle_scale(&ptrs[t], &numels[t], 1, dt, s_t);",
+                                "    oracle_scale(&ptrs[t], &numels[t], 1, dt, s_t);"),
+    "per_tensor_scales_first_only": ("    if (!skip) oracle_scale(&ptrs[t], &numels[t], 1, dt, s_t);",
+                                     "    if (!skip && t == 0) oracle_scale(&ptrs[t], &numels[t], 1, dt, s_t);"),
     "overflow_not_to_inf": ("if (E > emax) return sign | exp_all;  /* already", "if (E > emax + 1) return sign | exp_all;  /* already"),
 }
 
