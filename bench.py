@@ -15,6 +15,7 @@ Prints one JSON line.  Other modes:
   --config NAME        another synthetic set (synth.gradsets.CONFIGS)
   --path fused|split   force the kernel path
   --path adamw|amp     the clip fused into AdamW; the loss-scaled clip
+  --path per_tensor    per-tensor clipping and per-tensor norms
   --profile-pass       a short run for rocprofv3 (no CPU baseline, plus a
                        calibration copy of known size for the PMC counters)
   --summarize-rocprof  turn rocprofv3 output into the summaries kept in
@@ -114,10 +115,12 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="andrea120m_f32")
-    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw", "amp"], default="auto",
+    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw", "amp", "per_tensor"], default="auto",
                     help="adamw: time the clip fused into an AdamW step (gclip_norm + gclip_adamw_step) "
                          "against gclip_clip_ followed by the same AdamW step; amp: time the loss-scaled "
-                         "clip (gclip_clip_amp_) against gclip_clip_ with the same factor given by the host")
+                         "clip (gclip_clip_amp_) against gclip_clip_ with the same factor given by the host; "
+                         "per_tensor: time the per-tensor clip (gclip_clip_per_tensor_) and the per-tensor "
+                         "norms alone (gclip_tensor_norms)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -156,6 +159,8 @@ def main():
         return bench_adamw(a, G, g, tensors, pristine, flush, gl)
     if a.path == "amp":
         return bench_amp(a, G, g, tensors, pristine, flush, gl)
+    if a.path == "per_tensor":
+        return bench_per_tensor(a, G, g, tensors, pristine, flush, gl)
     if a.path != "auto":
         gl.set_path(G.GCLIP_PATH_FUSED if a.path == "fused" else G.GCLIP_PATH_SPLIT)
     info = gl.info()
@@ -384,6 +389,69 @@ def bench_amp(a, G, g, grads, pristine, flush, gl):
         "host_factor_ms_per_step": round(plain_ms, 5),
         "loss_scale_overhead_ms": round(ms - plain_ms, 5),
         "state_after": {"scale": state[0], "growth_tracker": state[1], "found_inf": state[2]},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+PER_TENSOR_MAX_NORM = 0.5
+
+
+def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
+    """Per-tensor clipping (every tensor by its own norm) at max_norm 0.5,
+    which clips the large matrices and leaves the norm vectors alone; and the
+    per-tensor norms alone.  Gradients are restored and the caches flushed
+    before every step; each step is timed with HIP events."""
+    import torch
+    stream = torch.cuda.current_stream()
+    esize = 4 if g.dtype == "f32" else 2
+
+    def restore():
+        for x, y in zip(grads, pristine):
+            x.copy_(y)
+        flush.sum()
+
+    def run(which, ev):
+        restore()
+        ev[0].record(stream)
+        if which == "clip":
+            gl.clip_per_tensor_(PER_TENSOR_MAX_NORM, g.avg_factor)
+        else:
+            gl.tensor_norms(g.avg_factor)
+        ev[1].record(stream)
+
+    times = {}
+    for which in ("clip", "norms"):
+        for _ in range(a.warmup):
+            run(which, [torch.cuda.Event(enable_timing=True) for _ in range(2)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+        for ev in evs:
+            run(which, ev)
+        torch.cuda.synchronize()
+        times[which] = [e[0].elapsed_time(e[1]) for e in evs]
+        if which == "clip":
+            st, r = gl.read()
+            tr = gl.read_tensors()
+    numel = [t.numel() for t in grads]
+    clipped_elems = sum(n for n, t in zip(numel, tr) if float(t["scale"]) != 1.0)
+    alg = g.numel * esize + 2 * clipped_elems * esize
+    ms = statistics.fmean(times["clip"])
+    norm_ms = statistics.fmean(times["norms"])
+    gbps = alg / (ms * 1e-3) / 1e9
+    norm_gbps = g.numel * esize / (norm_ms * 1e-3) / 1e9
+    out = {
+        "metric": f"per-tensor clip GB/s, {a.config}", "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": g.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOADS.get(a.config, a.config) + f"; per-tensor max_norm {PER_TENSOR_MAX_NORM}",
+                   "name": a.config, "launches_per_step": 2, "algorithmic_bytes_per_step": alg,
+                   "tensors_clipped": int(sum(int(t["clipped"]) for t in tr)), "n_tensors": len(grads),
+                   "elements_written": clipped_elems},
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "tensor_norms_ms": round(norm_ms, 5),
+        "tensor_norms_gbps": round(norm_gbps, 1),
+        "tensor_norms_pct_hbm_peak": round(100.0 * norm_gbps / HBM_PEAK_GBPS, 2),
+        "status": st,
     }
     print(json.dumps(out), flush=True)
     return 0

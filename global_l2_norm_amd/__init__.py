@@ -23,9 +23,14 @@ __all__ = ["GclipError", "GclipResult", "GradList", "clip_grad_norm_", "gclip_li
            "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string", "gclip_version",
            "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step", "AdamWList",
            "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp", "AmpState",
+           "gclip_tensor_norms", "gclip_clip_per_tensor_", "TENSOR_RESULT_DTYPE",
            "GCLIP_F32", "GCLIP_F16", "GCLIP_BF16", "GCLIP_PATH_AUTO", "GCLIP_PATH_FUSED", "GCLIP_PATH_SPLIT"]
 
 DTYPE_CODES = {"f32": GCLIP_F32, "f16": GCLIP_F16, "bf16": GCLIP_BF16}
+
+# gclip_tensor_result, 32 bytes per tensor
+TENSOR_RESULT_DTYPE = [("sumsq", "<f8"), ("norm", "<f8"), ("scale", "<f8"), ("nonfinite", "<i4"),
+                       ("clipped", "<i4")]
 
 
 class GclipError(RuntimeError):
@@ -162,6 +167,18 @@ def gclip_adamw_step(handle, lr, beta1, beta2, eps, weight_decay, step, max_norm
                                      ctypes.c_void_p(int(stream))), "gclip_adamw_step")
 
 
+def gclip_tensor_norms(handle, avg_factor, d_tensors, d_result, stream):
+    _check(_lib.lib.gclip_tensor_norms(handle, float(avg_factor), ctypes.c_void_p(int(d_tensors)),
+                                       ctypes.c_void_p(int(d_result)), ctypes.c_void_p(int(stream))),
+           "gclip_tensor_norms")
+
+
+def gclip_clip_per_tensor_(handle, max_norm, avg_factor, error_if_nonfinite, d_tensors, d_result, stream):
+    _check(_lib.lib.gclip_clip_per_tensor_(handle, float(max_norm), float(avg_factor), int(bool(error_if_nonfinite)),
+                                           ctypes.c_void_p(int(d_tensors)), ctypes.c_void_p(int(d_result)),
+                                           ctypes.c_void_p(int(stream))), "gclip_clip_per_tensor_")
+
+
 def _amp_params(growth_factor, backoff_factor, growth_interval):
     return GclipAmpParams(float(growth_factor), float(backoff_factor), int(growth_interval), 0)
 
@@ -223,6 +240,7 @@ class GradList:
         self.device = tensors[0].device if tensors else torch.device("cuda", torch.cuda.current_device())
         with torch.cuda.device(self.device):
             self.result = torch.zeros(64, dtype=torch.uint8, device=self.device)
+            self.tensor_results = torch.zeros(32 * max(len(tensors), 1), dtype=torch.uint8, device=self.device)
             self.handle = gclip_list_create([t.data_ptr() for t in tensors], [t.numel() for t in tensors],
                                             self.dtype)
 
@@ -253,6 +271,27 @@ class GradList:
 
     def clip_(self, max_norm, avg_factor=1.0, error_if_nonfinite=False, stream=None):
         gclip_clip_(self.handle, max_norm, avg_factor, error_if_nonfinite, self.d_result, self._stream(stream))
+
+    def tensor_norms(self, avg_factor=1.0, stream=None):
+        """Every tensor's norm (and the list's, into the result block)."""
+        gclip_tensor_norms(self.handle, avg_factor, self.tensor_results.data_ptr(), self.d_result,
+                           self._stream(stream))
+
+    def clip_per_tensor_(self, max_norm, avg_factor=1.0, error_if_nonfinite=False, stream=None):
+        """Every tensor clipped by its own norm, in place."""
+        gclip_clip_per_tensor_(self.handle, max_norm, avg_factor, error_if_nonfinite, self.tensor_results.data_ptr(),
+                               self.d_result, self._stream(stream))
+
+    def read_tensors(self, stream=None):
+        """Wait for the stream; the per-tensor figures as a numpy record array."""
+        import numpy as np
+        self._wait(stream)
+        raw = self.tensor_results.cpu().numpy()[:32 * len(self.tensors)]
+        return raw.view(np.dtype(TENSOR_RESULT_DTYPE))
+
+    def _wait(self, stream=None):
+        import torch
+        (torch.cuda.current_stream() if stream is None else stream).synchronize()
 
     def norm_amp(self, n_microbatches, amp, stream=None):
         """Norm of the unscaled, averaged gradient: a = 1 / (n * S), S read

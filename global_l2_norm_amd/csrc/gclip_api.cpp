@@ -34,6 +34,9 @@ hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, do
                         gclip_result* res, hipStream_t st);
 hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
                              int32_t interval, hipStream_t s);
+hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
+                              gclip_tensor_result* out, gclip_result* res, hipStream_t st);
+hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st);
 }  // namespace gclip
 
 // How long a workgroup of the fused kernel waits at the grid-wide decision
@@ -45,6 +48,8 @@ constexpr int64_t kMaxWaitUs = 60 * 1000 * 1000;
 struct gclip_list {
   gclip::HostPlan plan;
   gclip::DevPlan dev{};
+  gclip::TensorHostPlan tplan;
+  gclip::TensorPlan tdev{};
   void* blob = nullptr;
   int device = 0;
   bool fused_ok = false;
@@ -234,7 +239,12 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       delete L;
       return (gclip_status)rc;
     }
+    if (gclip::tensor_plan_build(L->plan, gclip::kTensorPieceVectors, L->tplan) != 0) {
+      delete L;
+      return GCLIP_EINVAL;
+    }
     const gclip::HostPlan& P = L->plan;
+    const size_t ntp = L->tplan.pieces.size(), ntf = L->tplan.first.size();
     const size_t nseg = (size_t)P.nseg(), nw = (size_t)P.nworkers, nsc = (size_t)P.nsc(), nch = (size_t)P.nchunk();
     const size_t nchs = (size_t)P.nchunk_streamed(), nsum = (size_t)P.nsum();
     const size_t waves = (size_t)gclip::worker_threads() / 64;
@@ -249,7 +259,8 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
                  o_splv = take((nch + 1) * 8), o_spls = take(nch * 4), o_fusv = take((nchs + 1) * 8),
                  o_fuss = take(nchs * 4), o_sum = take(nsum * 4), o_wksc = take((nw + 1) * 8),
                  o_sca = take(nsc * 8), o_part = take((nsum * waves + nw) * 8), o_bc = take(8),
-                 o_sync = take((size_t)gclip::kSyncWords * 4), o_bst = take(nw * 4);
+                 o_sync = take((size_t)gclip::kSyncWords * 4), o_bst = take(nw * 4),
+                 o_tpc = take(ntp * sizeof(gclip::TPiece)), o_tfi = take(ntf * 4), o_tpa = take(ntp * 8);
     if ((e = hipMalloc(&L->blob, off)) != hipSuccess) {
       delete L;
       g_last_hip = (int32_t)e;
@@ -264,7 +275,9 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
         (e = up(o_sega, P.seg_addr.data(), nseg * 8)) || (e = up(o_blk, P.blk_seg.data(), nw * 4)) ||
         (e = up(o_splv, P.spl_vb.data(), (nch + 1) * 8)) || (e = up(o_spls, P.spl_seg.data(), nch * 4)) ||
         (e = up(o_fusv, P.fus_vb.data(), (nchs + 1) * 8)) || (e = up(o_fuss, P.fus_seg.data(), nchs * 4)) || (e = up(o_sum, P.sum_seg.data(), nsum * 4)) || (e = up(o_wksc, P.wk_scbegin.data(), (nw + 1) * 8)) ||
-        (e = up(o_sca, P.sc_addr.data(), nsc * 8)) || (e = hipDeviceSynchronize()) != hipSuccess) {
+        (e = up(o_sca, P.sc_addr.data(), nsc * 8)) ||
+        (e = up(o_tpc, L->tplan.pieces.data(), ntp * sizeof(gclip::TPiece))) ||
+        (e = up(o_tfi, L->tplan.first.data(), ntf * 4)) || (e = hipDeviceSynchronize()) != hipSuccess) {
       (void)hipFree(L->blob);
       delete L;
       return hip_fail(e);
@@ -294,6 +307,14 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     D.cvs = P.cvs;
     D.nworkers = P.nworkers;
     D.nseg = (int32_t)nseg;
+    gclip::TensorPlan& T = L->tdev;
+    T.pieces = reinterpret_cast<const gclip::TPiece*>(b + o_tpc);
+    T.first = reinterpret_cast<const uint32_t*>(b + o_tfi);
+    T.sc_addr = D.sc_addr;
+    T.partials = reinterpret_cast<double*>(b + o_tpa);
+    T.npieces = (uint32_t)ntp;
+    T.ntensors = (int32_t)P.n_tensors;
+    T.nt_store = D.nt_store;
     *out = L;
     return GCLIP_OK;
   } catch (const std::bad_alloc&) {
@@ -388,6 +409,10 @@ hipError_t launch_clip(gclip_list* list, double max_norm, gclip::AvgSrc avg, int
   return e;
 }
 
+bool tensor_out_ok(const gclip_list* list, const gclip_tensor_result* t) {
+  if (list->plan.n_tensors == 0) return true;
+  return t && reinterpret_cast<uintptr_t>(t) % 8 == 0;
+}
 bool amp_state_ptr_ok(const gclip_amp_state* a) { return a && reinterpret_cast<uintptr_t>(a) % 4 == 0; }
 bool amp_params_ok(const gclip_amp_params* a) {
   return a && std::isfinite(a->growth_factor) && a->growth_factor >= 1.0 && std::isfinite(a->backoff_factor) &&
@@ -402,6 +427,32 @@ gclip_status gclip_clip_(gclip_list* list, double max_norm, double avg_factor, i
   if (st != GCLIP_OK) return st;
   const hipError_t e = launch_clip(list, max_norm, gclip::AvgSrc{avg_factor, nullptr}, error_if_nonfinite ? 1 : 0,
                                    d_result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_tensor_norms(gclip_list* list, double avg_factor, gclip_tensor_result* d_tensors,
+                                gclip_result* d_result, void* stream) {
+  if (!list || !result_ptr_ok(d_result) || !factor_ok(avg_factor) || !tensor_out_ok(list, d_tensors))
+    return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
+  const hipError_t e = gclip::launch_tensor_norm(list->tdev, list->plan.dtype, gclip::AvgSrc{avg_factor, nullptr},
+                                                 0.0, 0, 0, d_tensors, d_result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double avg_factor,
+                                    int32_t error_if_nonfinite, gclip_tensor_result* d_tensors,
+                                    gclip_result* d_result, void* stream) {
+  if (!list || !result_ptr_ok(d_result) || !threshold_ok(max_norm) || !factor_ok(avg_factor) ||
+      !tensor_out_ok(list, d_tensors))
+    return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gclip::launch_tensor_norm(list->tdev, list->plan.dtype, gclip::AvgSrc{avg_factor, nullptr},
+                                           max_norm, 1, error_if_nonfinite ? 1 : 0, d_tensors, d_result, s);
+  if (e == hipSuccess) e = gclip::launch_tensor_scale(list->tdev, list->plan.dtype, d_tensors, s);
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 

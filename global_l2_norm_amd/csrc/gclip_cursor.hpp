@@ -229,4 +229,11 @@ __host__ __device__ __forceinline__ BlockSplit block_split(const Range& r) {
   return f;
 }
 
+// Per-tensor pieces (TPiece): the group at vector j of a piece gives lane t
+// its vectors j + u * kThreads + t, u < kUnroll, those below the piece's nvec.
+constexpr uint32_t kPieceGroup = (uint32_t)kThreads * kUnroll;
+__host__ __device__ __forceinline__ uint32_t piece_index(uint32_t j, int u, uint32_t t) {
+  return j + (uint32_t)u * kThreads + t;
+}
+
 }  // namespace gclip

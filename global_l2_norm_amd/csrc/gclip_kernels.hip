@@ -973,6 +973,169 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   finish<DT>(p, res, true, hs, &flag);
 }
 
+// ---------------------------------------------------------------- per-tensor norms and clipping
+// Grad clip lesson, "Two variants: Per-Tensor or Global": every tensor by its
+// own norm, in the three kernels of the lesson's pipeline.  k_tensor_partial:
+// one workgroup per piece (a run of one tensor, TPiece), kUnroll vectors in
+// flight per lane, one partial per piece, plain stores and no atomics (a
+// returning atomic per workgroup held each workgroup's slot for a round trip
+// to the device-coherent level, and the pieces of one large tensor queued on
+// its counter).  k_tensor_decide: one workgroup stages the partials in LDS,
+// every lane loading many at once, sums each tensor's pieces in piece order
+// and takes the decisions.  k_tensor_scale: one workgroup per piece.  Every
+// sum is taken in a fixed order, so the bits do not depend on scheduling.
+
+template <int DT>
+__device__ __forceinline__ double piece_sumsq(const TensorPlan& T, const TPiece& pc) {
+  const uint32_t t = threadIdx.x;
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+  const g_u32x4* base = reinterpret_cast<const g_u32x4*>(uniform64(pc.addr));
+  const uint32_t nvec = uniform32(pc.nvec);
+  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
+    u32x4 q[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      q[u] = i < nvec ? ld_vec<kNtSum>(base + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
+  }
+  double s = 0.0;
+  for (uint32_t i = t; i < pc.sc_count; i += kThreads) s += elem_square<DT>(load_elem<DT>(T.sc_addr[pc.sc_begin + i]));
+  return lane_total(acc, s);
+}
+
+template <int DT, bool NTS>
+__device__ __forceinline__ void piece_scale(const TensorPlan& T, const TPiece& pc, double s64, float s32) {
+  const uint32_t t = threadIdx.x;
+  g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
+  const uint32_t nvec = uniform32(pc.nvec);
+  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
+    u32x4 q[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      if (i < nvec) q[u] = ld_vec<kNtScale>(base + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      if (i < nvec) st_vec<NTS>(base + i, scale_vec<DT>(q[u], s64, s32));
+    }
+  }
+  for (uint32_t i = t; i < pc.sc_count; i += kThreads) {
+    const uint64_t a = T.sc_addr[pc.sc_begin + i];
+    store_elem<DT>(a, scale_elem<DT>(load_elem<DT>(a), s64, s32));
+  }
+}
+
+constexpr int kStage = 16384;  // partials staged in LDS at once by k_tensor_decide (128 KB)
+constexpr int kStageBatch = 16;  // loads in flight per lane while staging
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_tensor_partial(TensorPlan T) {
+  __shared__ double red[kWaves];
+  const TPiece pc = ld_table(T.pieces, blockIdx.x);
+  const double part = wg_sum(piece_sumsq<DT>(T, pc), red);
+  if (threadIdx.x == 0) T.partials[blockIdx.x] = part;
+}
+
+// One workgroup.  Every tensor's figures and, for the per-tensor clip (clip
+// != 0), its decision; then the list's result block.  With the stop switch,
+// a NaN/Inf in any tensor stops the whole update.  Tensor k is summed by
+// lane k % kThreads, in piece order, across the staged windows; its running
+// sum is kept in out[k].sumsq until the last window.
+__global__ __launch_bounds__(kThreads) void k_tensor_decide(TensorPlan T, AvgSrc avs, double max_norm, int clip,
+                                                            int err, gclip_tensor_result* out, gclip_result* res) {
+  __shared__ double stage[kStage];
+  __shared__ double red[kWaves];
+  const double avg = avg_value(avs);
+  const uint32_t t = threadIdx.x;
+  for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) out[k].sumsq = 0.0;
+  for (uint32_t w0 = 0; w0 < T.npieces; w0 += kStage) {
+    const uint32_t wn = T.npieces - w0 < (uint32_t)kStage ? T.npieces - w0 : (uint32_t)kStage;
+    __syncthreads();  // the previous window is no longer read
+    for (uint32_t i0 = 0; i0 < wn; i0 += (uint32_t)(kThreads * kStageBatch)) {
+      double v[kStageBatch];
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const uint32_t i = i0 + (uint32_t)u * kThreads + t;
+        v[u] = i < wn ? T.partials[w0 + i] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const uint32_t i = i0 + (uint32_t)u * kThreads + t;
+        if (i < wn) stage[i] = v[u];
+      }
+    }
+    __syncthreads();
+    for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) {
+      const uint32_t b = T.first[k], e = T.first[k + 1];
+      const uint32_t lo = b > w0 ? b : w0, hi = e < w0 + wn ? e : w0 + wn;
+      if (lo >= hi) continue;
+      double S = out[k].sumsq;
+#pragma unroll 8
+      for (uint32_t i = lo; i < hi; ++i) S += stage[i - w0];
+      out[k].sumsq = S;
+    }
+  }
+  double mine = 0.0;
+  int nf_mine = 0;
+  for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) {
+    const double S = out[k].sumsq;
+    const double sumsq = (avg * avg) * S;
+    const int nf = nonfinite_of(S, avg);
+    out[k].sumsq = sumsq;
+    out[k].norm = sqrt(sumsq);
+    out[k].nonfinite = nf;
+    mine += S;
+    nf_mine |= nf;
+  }
+  const double S = wg_sum(mine, red);
+  const int nf_any = __syncthreads_or(nf_mine);
+  const int skip = (clip && err && nf_any) ? 1 : 0;
+  int clipped_mine = 0;
+  for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) {
+    if (clip) {
+      const Decision d = decide(out[k].sumsq, out[k].nonfinite, max_norm, avg, err);
+      out[k].scale = (skip || d.s == 1.0) ? 1.0 : d.s;
+      out[k].clipped = d.clipped;
+      clipped_mine |= d.clipped;
+    } else {
+      out[k].scale = 1.0;
+      out[k].clipped = 0;
+    }
+  }
+  const int clipped_any = __syncthreads_or(clipped_mine);
+  // the partials have all been read: overwrite them with NaN, so that a
+  // partial read before it is written could only show up as a NaN norm
+  for (uint32_t i = t; i < T.npieces; i += kThreads) T.partials[i] = __builtin_nan("");
+  if (t == 0) {
+    write_norm(res, S, avg);
+    res->nonfinite = nf_any | res->nonfinite;
+    res->scale = 1.0;
+    res->clipped = clipped_any;
+    res->skipped = skip;
+    if (clip) res->max_norm = max_norm;
+    res->decided = clip ? 1 : 0;
+    res->status = 0;
+    res->handed_back = 0;
+  }
+}
+
+// Every piece multiplied by its tensor's factor (nothing written where that
+// factor is 1).  Grid: npieces.
+template <int DT, bool NTS>
+__global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const gclip_tensor_result* out) {
+  const TPiece pc = ld_table(T.pieces, blockIdx.x);
+  const double s64 = out[uniform32(pc.tensor)].scale;
+  if (s64 == 1.0) return;
+  piece_scale<DT, NTS>(T, pc, s64, (float)s64);
+}
+
 // ---------------------------------------------------------------- AdamW on the clipped gradient
 // Grad clip lesson, "Order matters: Pre-Adam": the optimizer's moments see
 // the clipped gradient.  Each workgroup updates one piece of one tensor: the
@@ -1137,6 +1300,37 @@ hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc
   void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch, &wait_ticks};
   const void* fn = p.nt_store ? fused_kernel<true>(dtype) : fused_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
+}
+
+hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
+                              gclip_tensor_result* out, gclip_result* res, hipStream_t st) {
+  if (T.npieces > 0) {
+    const dim3 grid(T.npieces), block(kThreads);
+    switch (dtype) {
+      case GCLIP_F32: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F32>, grid, block, 0, st, T); break;
+      case GCLIP_F16: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F16>, grid, block, 0, st, T); break;
+      default: hipLaunchKernelGGL(k_tensor_partial<GCLIP_BF16>, grid, block, 0, st, T); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, max_norm, clip, err, out, res);
+  return hipGetLastError();
+}
+
+template <bool NTS>
+const void* tensor_scale_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_tensor_scale<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_tensor_scale<GCLIP_F16, NTS>
+                              : (const void*)k_tensor_scale<GCLIP_BF16, NTS>;
+}
+
+hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st) {
+  if (T.npieces == 0) return hipSuccess;
+  TensorPlan tc = T;
+  void* args[] = {&tc, &out};
+  const void* fn = T.nt_store ? tensor_scale_kernel<true>(dtype) : tensor_scale_kernel<false>(dtype);
+  return hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
 }
 
 hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,

@@ -166,4 +166,35 @@ int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t 
   return 0;
 }
 
+int tensor_plan_build(const HostPlan& p, uint32_t piece_vectors, TensorHostPlan& out) {
+  if (piece_vectors == 0) return 1;
+  out.pieces.clear();
+  out.first.assign((size_t)p.n_tensors + 1, 0);
+  if (p.nsc() > 0xffffffffull) return 1;
+  size_t s = 0, c = 0;  // next segment, next single element (both in tensor order)
+  for (int64_t t = 0; t < p.n_tensors; ++t) {
+    out.first[(size_t)t] = (uint32_t)out.pieces.size();
+    const size_t c0 = c;
+    while (c < p.sc_tensor.size() && p.sc_tensor[c] == (int32_t)t) ++c;
+    const uint32_t nsc = (uint32_t)(c - c0);
+    bool first = true;
+    auto push = [&](uint64_t addr, uint32_t nvec) {
+      out.pieces.push_back(TPiece{addr, nvec, (uint32_t)t, first ? (uint32_t)c0 : 0u, first ? nsc : 0u, {0u, 0u}});
+      first = false;
+    };
+    if (s < p.seg_tensor.size() && p.seg_tensor[s] == (int32_t)t) {
+      const uint64_t nv = p.seg_vbegin[s + 1] - p.seg_vbegin[s];
+      for (uint64_t v = 0; v < nv; v += piece_vectors) {
+        const uint64_t k = nv - v < piece_vectors ? nv - v : piece_vectors;
+        push(p.seg_addr[s] + v * kVecBytes, (uint32_t)k);
+      }
+      ++s;
+    }
+    if (first && nsc > 0) push(0, 0);
+    if (out.pieces.size() > 0x7fffffffull) return 1;
+  }
+  out.first[(size_t)p.n_tensors] = (uint32_t)out.pieces.size();
+  return 0;
+}
+
 }  // namespace gclip

@@ -158,6 +158,45 @@ struct AdamPlan {
   uint32_t npieces;
 };
 
+// Per-tensor work (per-tensor norms and per-tensor clipping): the list cut
+// into pieces that each lie inside one tensor, so that one workgroup's sum
+// belongs to one tensor.  A piece is nvec 16-byte vectors from addr (a run
+// of its tensor's vector segment) and, on the tensor's first piece only, the
+// tensor's single elements sc_addr[sc_begin .. sc_begin + sc_count) of the
+// list's plan.  Pieces are in tensor order; tensor t owns pieces
+// first[t] .. first[t + 1] - 1 (none when it is empty).
+struct TPiece {
+  uint64_t addr;
+  uint32_t nvec, tensor;
+  uint32_t sc_begin, sc_count;
+  uint32_t pad[2];
+};
+static_assert(sizeof(TPiece) == 32, "one piece is one 32-byte scalar load");
+
+#ifndef GCLIP_TENSOR_PIECE_VECTORS
+#define GCLIP_TENSOR_PIECE_VECTORS 4096
+#endif
+constexpr uint32_t kTensorPieceVectors = GCLIP_TENSOR_PIECE_VECTORS;
+
+struct TensorHostPlan {
+  std::vector<TPiece> pieces;
+  std::vector<uint32_t> first;  // n_tensors + 1
+};
+
+// Cut a list's plan into per-tensor pieces of at most piece_vectors vectors.
+// Returns a gclip_status code (0 = OK).
+int tensor_plan_build(const HostPlan& p, uint32_t piece_vectors, TensorHostPlan& out);
+
+struct TensorPlan {
+  const TPiece* pieces;
+  const uint32_t* first;
+  const uint64_t* sc_addr;
+  double* partials;  // one per piece
+  uint32_t npieces;
+  int32_t ntensors;
+  uint32_t nt_store;
+};
+
 // Per-step constants, rounded to binary32 from binary64 on the host.
 struct AdamHp {
   float step_size;     // lr / (1 - beta1^t)

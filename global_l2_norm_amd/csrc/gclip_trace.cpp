@@ -82,7 +82,7 @@ void replay_groups(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint
 extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* numels, int32_t n_tensors,
                                          int32_t dtype, int32_t n_workers, int32_t mode, uint64_t* out_addr,
                                          int32_t* out_worker, int64_t cap, int64_t* n_out) {
-  if (!n_out || cap < 0 || (cap > 0 && (!out_addr || !out_worker)) || mode < 0 || mode > 3)
+  if (!n_out || cap < 0 || (cap > 0 && (!out_addr || !out_worker)) || mode < 0 || mode > 4)
     return GCLIP_EINVAL;
   try {
     HostPlan hp;
@@ -110,6 +110,28 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
     p.nworkers = hp.nworkers;
     p.nseg = (int32_t)hp.nseg();
     Recorder rec{out_addr, out_worker, cap};
+    if (mode == 4) {  // k_tensor_partial and k_tensor_scale: one workgroup per piece
+      TensorHostPlan tp;
+      if (tensor_plan_build(hp, kTensorPieceVectors, tp) != 0) return GCLIP_EINVAL;
+      for (const TPiece& pc : tp.pieces) {
+        for (uint32_t j = 0; j < pc.nvec; j += kPieceGroup)
+          for (uint32_t t = 0; t < (uint32_t)kThreads; ++t)
+            for (int u = 0; u < kUnroll; ++u) {
+              const uint32_t i = piece_index(j, u, t);
+              if (i < pc.nvec) rec.put((int32_t)pc.tensor, pc.addr + (uint64_t)i * kVecBytes);
+            }
+        for (uint32_t i = 0; i < pc.sc_count; ++i)
+          rec.put((int32_t)pc.tensor, hp.sc_addr[pc.sc_begin + i] | kElementTag);
+      }
+      for (int32_t t = 0; t < n_tensors; ++t)  // pieces in tensor order, as the final sums assume
+        if (tp.first[(size_t)t] > tp.first[(size_t)t + 1]) return GCLIP_EINVAL;
+      for (uint32_t k = 0; k < (uint32_t)tp.pieces.size(); ++k) {
+        const uint32_t t = tp.pieces[k].tensor;
+        if (k < tp.first[t] || k >= tp.first[t + 1]) return GCLIP_EINVAL;
+      }
+      *n_out = rec.n;
+      return rec.n > cap ? GCLIP_ERANGE : GCLIP_OK;
+    }
     // claimed chunks of a table: any worker, so reported as worker -1
     auto replay_chunks = [&](const uint64_t* vb, const uint32_t* seg, uint32_t nch) {
       for (uint32_t c = 0; c < nch; ++c) {

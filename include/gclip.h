@@ -273,6 +273,50 @@ gclip_status gclip_adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, d
                               int32_t error_if_nonfinite, gclip_result* d_result, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Per-tensor norms and per-tensor clipping.
+ *
+ * Grad clip lesson, section "Two variants: Per-Tensor or Global": besides the
+ * global clip (the whole list as one vector) the page describes clipping
+ * every tensor on its own, by its own norm -- simple, but it changes the
+ * tensors' relative sizes.  The per-tensor norms are also the diagnostic a
+ * run wants when one tensor spikes.  Both calls cut the list into pieces
+ * that each lie inside one tensor, sum each piece in one workgroup, and let
+ * the last workgroup to finish sum each tensor's pieces in order (so the bits
+ * do not depend on scheduling).
+ * ------------------------------------------------------------------------- */
+
+/* One tensor's figures, 32 bytes, in an array of n_tensors in DEVICE memory
+ * that the caller owns (8-byte aligned). */
+typedef struct gclip_tensor_result {
+  double sumsq;       /* sum over the tensor of (a*g)^2 */
+  double norm;        /* its square root */
+  double scale;       /* factor written into the tensor; 1.0 when nothing was written */
+  int32_t nonfinite;  /* 1 when the tensor holds a NaN/Inf element */
+  int32_t clipped;    /* 1 when the tensor's norm exceeded max_norm (per-tensor clip) */
+} gclip_tensor_result;
+
+/* Norms of every tensor of the list, of a*g, into d_tensors[0 .. n_tensors),
+ * and the list's norm into d_result (sumsq, norm, nonfinite; decided = 0),
+ * so that gclip_scale can follow to finish a global clip with per-tensor
+ * figures.  Writes no gradient.  Enqueues one kernel; no allocation, no
+ * synchronisation.  Errors as gclip_norm, plus GCLIP_EINVAL for a NULL or
+ * misaligned d_tensors when the list has tensors. */
+gclip_status gclip_tensor_norms(gclip_list* list, double avg_factor, gclip_tensor_result* d_tensors,
+                                gclip_result* d_result, void* stream);
+
+/* Per-tensor clipping in place: tensor t is multiplied by a * (max_norm /
+ * norm_t) when norm_t > max_norm, by a otherwise (nothing is written when
+ * that factor is 1).  With error_if_nonfinite, one NaN/Inf anywhere in the
+ * list stops the whole update: no tensor is written and d_result->skipped is
+ * set.  d_tensors receives every tensor's figures; d_result the list's sumsq,
+ * norm and nonfinite, clipped = 1 when any tensor was clipped, scale = 1.0
+ * (the factors are per tensor).  Two kernels on `stream`; no allocation, no
+ * synchronisation.  Errors as gclip_clip_. */
+gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double avg_factor,
+                                    int32_t error_if_nonfinite, gclip_tensor_result* d_tensors,
+                                    gclip_result* d_result, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Loss-scaled steps (mixed precision).
  *
  * Glossary page, introduction and section "Order changes the result": with
@@ -339,7 +383,9 @@ gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int3
  * make over a list planned for n_workers workers (the kernels' own cursor
  * code, compiled for the host), for checking it on the CPU:
  *   mode 0  norm kernel, 1  scale kernel,
- *        2  fused kernel, first pass, 3  fused kernel, second pass
+ *        2  fused kernel, first pass, 3  fused kernel, second pass,
+ *        4  per-tensor kernels (out_worker is then the tensor a piece
+ *           belongs to, not a worker)
  * Fills out_addr[i] (address of a 16-byte vector, or, with bit 63 set, of a
  * single element) and out_worker[i] for every lane access; accesses to
  * chunks, which any worker may claim at run time, carry worker -1.  n_out

@@ -13,7 +13,7 @@ import pytest
 import global_l2_norm_amd as g
 from global_l2_norm_amd import _lib
 from synth import gradsets as gs
-from tests.abi_util import ESIZE, check_walk, fake_layout
+from tests.abi_util import ESIZE, TAG, check_walk, fake_layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gclip.h")
@@ -164,3 +164,39 @@ def test_kernel_walk_on_shrunk_gpt_shapes_with_4096_scalars():
     for mode in (0, 1, 2, 3):
         ta, _ = g.gclip_plan_trace(addrs, numels, 2, 256, mode)
         check_walk(ta, addrs, numels, 2)
+
+
+# ---------------------------------------------------------------- per-tensor pieces
+def _check_tensor_attribution(ta, tw, addrs, numels, es):
+    """Every access of the per-tensor kernels is credited to the tensor that
+    holds it (out_worker is the piece's tensor in mode 4)."""
+    start = (ta & ~TAG).astype(np.uint64)
+    for t, (a, n) in enumerate(zip(addrs, numels)):
+        mine = start[tw == t]
+        assert np.all(mine >= a) and np.all(mine < a + n * es), f"tensor {t}: access outside it"
+        tagged = (ta[tw == t] & TAG) != 0
+        covered = int(np.where(tagged, es, 16).sum())
+        assert covered == n * es, f"tensor {t}: {covered} bytes credited, {n * es} held"
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+@pytest.mark.parametrize("seed", range(4))
+def test_tensor_pieces_cover_once_and_credit_their_tensor(dtype, seed):
+    rng = np.random.default_rng(400 + seed)
+    es = ESIZE[dtype]
+    numels = _random_numels(rng)
+    if seed >= 2:  # several pieces per tensor, and a ragged last piece
+        numels += [3_000_001, 0, 777_777, 5]
+    addrs = fake_layout(rng, numels, es, misalign=bool(seed % 2))
+    ta, tw = g.gclip_plan_trace(addrs, numels, dtype, 4, 4)
+    check_walk(ta, addrs, numels, es)
+    _check_tensor_attribution(ta, tw, addrs, numels, es)
+
+
+def test_tensor_pieces_on_andrea120m_shapes():
+    shapes = gs.shapes_andrea120m()
+    numels = [int(np.prod(s)) for _, s in shapes]
+    addrs = fake_layout(np.random.default_rng(9), numels, 4, misalign=False)
+    ta, tw = g.gclip_plan_trace(addrs, numels, 0, 256, 4)
+    check_walk(ta, addrs, numels, 4)
+    _check_tensor_attribution(ta, tw, addrs, numels, 4)

@@ -1,0 +1,220 @@
+"""GPU parity of the per-tensor calls (gclip_tensor_norms, gclip_clip_per_tensor_),
+through the C ABI, against the oracle's per-tensor clip.
+
+Tolerances are those of the global path: every tensor's norm and the list's
+within relative 1e-5 of the oracle's; clipped fp32 elements within relative
+1e-5, fp16/bf16 elements within 1 ulp; the per-tensor clipped and nonfinite
+flags exactly; tensors the oracle leaves alone bitwise unchanged.  Random
+thresholds are kept away from every tensor's norm by more than the norm
+tolerance, so that no decision is a near-tie."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gradsets as gs
+from tests import gpu_util as gu
+from tests.test_gpu_parity import ragged_arrays, upload_as_views
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("the gpu tests need an MI355X")
+    import global_l2_norm_amd  # noqa: F401  (fails loudly when libgclip.so is missing)
+
+
+def _G():
+    import global_l2_norm_amd as G
+    return G
+
+
+def gpu_per_tensor(arrays, dtype, max_norm, avg=1.0, err=False, views=None):
+    ts = views if views is not None else gu.upload(arrays, dtype)
+    gl = _G().GradList(ts)
+    gl.clip_per_tensor_(max_norm, avg, err)
+    st, r = gl.read(err)
+    tr = gl.read_tensors()
+    out = gu.download(ts, dtype)
+    gl.close()
+    return st, r, tr, out
+
+
+def check_tensor_figures(tr, ro, what):
+    assert len(tr) == len(ro["tensors"]), what
+    for k, (g, o) in enumerate(zip(tr, ro["tensors"])):
+        assert bool(g["nonfinite"]) == o["nonfinite"], (what, k)
+        gu.assert_norm_close(float(g["norm"]), o["norm"], f"{what} tensor {k}")
+        gu.assert_norm_close(float(g["sumsq"]), o["sumsq"], f"{what} tensor {k} sumsq")
+        if not math.isnan(o["norm"]):
+            assert bool(g["clipped"]) == o["clipped"], (what, k)
+            if o["scale"] == 1.0:
+                assert float(g["scale"]) == 1.0, (what, k)
+            else:
+                assert abs(float(g["scale"]) - o["scale"]) <= 1e-5 * abs(o["scale"]), (what, k)
+
+
+def check_per_tensor(arrays, dtype, max_norm, avg=1.0, err=False, views=None, what=""):
+    st, r, tr, out = gpu_per_tensor(arrays, dtype, max_norm, avg, err, views)
+    ref = [a.copy() for a in arrays]
+    ro = oracle.clip_per_tensor_(ref, dtype, max_norm, avg, err)
+    assert r["status"] == 0, what
+    assert r["nonfinite"] == ro["nonfinite"] and r["skipped"] == ro["skipped"], what
+    gu.assert_norm_close(r["norm"], ro["norm"], what)
+    assert r["clipped"] == ro["clipped"] and r["scale"] == 1.0, what
+    check_tensor_figures(tr, ro, what)
+    for k, (g, o, a) in enumerate(zip(out, ref, arrays)):
+        if ro["skipped"] or ro["tensors"][k]["scale"] == 1.0:
+            gu.assert_bitwise_equal([g], [a], f"{what} tensor {k} (must be untouched)")
+        else:
+            gu.assert_elems_close([g], [o], dtype, f"{what} tensor {k}")
+    return r, ro, tr, out
+
+
+def _threshold_off_ties(rng, arrays, dtype, avg=1.0):
+    norms = [math.sqrt(s) for s in oracle.tensor_sumsq(arrays, dtype, avg)]
+    for _ in range(100):
+        c = float(np.exp(rng.uniform(np.log(1e-3), np.log(1e3))))
+        if all(abs(n - c) > 1e-4 * c for n in norms):
+            return c
+    raise AssertionError("no threshold away from every norm")
+
+
+# ------------------------------------------------------------------ the page's contrast
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_contrast_6_8_and_small(dtype):
+    """[6, 8] and [0.3, 0.4] at c = 1: [0.6, 0.8] and the second unchanged."""
+    a = [gs.to_storage(np.array([6.0, 8.0]), dtype), gs.to_storage(np.array([0.3, 0.4]), dtype)]
+    r, ro, tr, out = check_per_tensor(a, dtype, 1.0, what=f"contrast {dtype}")
+    assert float(tr[0]["norm"]) == 10.0 and tr[0]["clipped"] and not tr[1]["clipped"]
+    assert np.array_equal(out[0], gs.to_storage(np.array([0.6, 0.8]), dtype))
+
+
+# ------------------------------------------------------------------ ragged lists
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_ragged_lists_misaligned_views(dtype, seed):
+    """Tensors of 1 .. 3M elements at odd element offsets (single elements at
+    both ends of each vector run), several pieces per big tensor."""
+    rng = np.random.default_rng(2000 + seed)
+    arrays = ragged_arrays(rng, dtype, big=seed >= 2)
+    avg = [1.0, 0.25, 1.0, 1.0 / 3.0][seed]
+    c = _threshold_off_ties(rng, arrays, dtype, avg)
+    buf, views = upload_as_views(arrays, dtype, rng)
+    check_per_tensor(arrays, dtype, c, avg, views=views, what=f"ragged {dtype} seed {seed}")
+    import torch
+    mask = torch.ones(buf.numel(), dtype=torch.bool, device="cuda")
+    for v in views:
+        o = v.storage_offset()
+        mask[o:o + v.numel()] = False
+    assert int(torch.count_nonzero(buf[mask].float())) == 0, "padding between views written"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_tensor_norms_then_global_scale(dtype):
+    """gclip_tensor_norms + gclip_scale is the global clip with per-tensor
+    figures: the list's norm and the written values as gclip_clip_'s."""
+    rng = np.random.default_rng(2100)
+    arrays = ragged_arrays(rng, dtype, big=True)
+    ts = gu.upload(arrays, dtype)
+    gl = _G().GradList(ts)
+    gl.tensor_norms(0.5)
+    st, r0 = gl.read()
+    tr = gl.read_tensors()
+    assert not r0["decided"]
+    gu.assert_bitwise_equal(gu.download(ts, dtype), arrays, "norms only: nothing written")
+    per = oracle.tensor_sumsq(arrays, dtype, 0.5)
+    for k, s in enumerate(per):
+        gu.assert_norm_close(float(tr[k]["sumsq"]), s, f"tensor {k}")
+        assert float(tr[k]["scale"]) == 1.0 and not tr[k]["clipped"]
+    ro_ = oracle.clip_([a.copy() for a in arrays], dtype, 1e30, 0.5)
+    gu.assert_norm_close(r0["norm"], ro_["norm"], "list norm")
+    c = 0.5 * ro_["norm"]
+    gl.scale(c, 0.5)
+    st, r = gl.read()
+    out = gu.download(ts, dtype)
+    ref = [a.copy() for a in arrays]
+    ro = oracle.clip_(ref, dtype, c, 0.5)
+    assert r["clipped"] and ro["clipped"]
+    gu.assert_elems_close(out, ref, dtype, "global scale after per-tensor norms")
+    gl.close()
+
+
+# ------------------------------------------------------------------ non-finite, empty, repeatability
+@pytest.mark.parametrize("err", (False, True))
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_nonfinite(dtype, err):
+    rng = np.random.default_rng(2200)
+    arrays = [gs.to_storage(rng.standard_normal(n) * 3.0, dtype) for n in (5000, 70_001, 33, 4096 * 8)]
+    arrays[1][12_345] = gs.to_storage(np.array([math.nan]), dtype)[0]
+    arrays[3][7] = gs.to_storage(np.array([-math.inf]), dtype)[0]
+    r, ro, tr, out = check_per_tensor(arrays, dtype, 1.0, err=err, what=f"nonfinite {dtype} err={err}")
+    assert r["nonfinite"] and list(tr["nonfinite"]) == [0, 1, 0, 1]
+    assert r["skipped"] == err
+
+
+def test_empty_lists_and_tensors():
+    G = _G()
+    import torch
+    for arrays in ([], [np.zeros(0, np.float32)], [np.zeros(0, np.float32), np.ones(3, np.float32) * 2.0,
+                                                    np.zeros(0, np.float32)]):
+        ts = gu.upload(arrays, "f32") if arrays else []
+        gl = G.GradList(ts)
+        gl.clip_per_tensor_(1.0)
+        st, r = gl.read()
+        tr = gl.read_tensors()
+        ro = oracle.clip_per_tensor_([a.copy() for a in arrays], "f32", 1.0)
+        gu.assert_norm_close(r["norm"], ro["norm"], "empty")
+        assert len(tr) == len(arrays)
+        check_tensor_figures(tr, ro, "empty")
+        gl.close()
+    torch.cuda.synchronize()
+
+
+def test_repeatable_bits():
+    rng = np.random.default_rng(2300)
+    arrays = ragged_arrays(rng, "f32", big=True)
+    ts = gu.upload(arrays, "f32")
+    gl = _G().GradList(ts)
+    runs = []
+    for _ in range(3):
+        gl.tensor_norms()
+        st, r = gl.read()
+        runs.append((r["sumsq"], gl.read_tensors()["sumsq"].tobytes()))
+    assert runs[0] == runs[1] == runs[2]
+    gl.close()
+
+
+def test_invalid_arguments():
+    import torch
+    G = _G()
+    ts = gu.upload([np.ones(10, np.float32)], "f32")
+    gl = G.GradList(ts)
+    s = torch.cuda.current_stream().cuda_stream
+    for bad in (0, gl.tensor_results.data_ptr() + 4):
+        with pytest.raises(G.GclipError):
+            G.gclip_tensor_norms(gl.handle, 1.0, bad, gl.d_result, s)
+        with pytest.raises(G.GclipError):
+            G.gclip_clip_per_tensor_(gl.handle, 1.0, 1.0, False, bad, gl.d_result, s)
+    for c, a in ((0.0, 1.0), (math.nan, 1.0), (1.0, 0.0), (1.0, math.inf)):
+        with pytest.raises(G.GclipError):
+            gl.clip_per_tensor_(c, a)
+    gu.assert_bitwise_equal(gu.download(ts, "f32"), [np.ones(10, np.float32)], "rejected calls write nothing")
+    gl.close()
+
+
+# ------------------------------------------------------------------ full size
+@pytest.mark.parametrize("dtype_cfg", ("andrea120m_f32", "andrea120m_f16_spike"))
+def test_andrea120m(dtype_cfg):
+    """The 124-tensor list at c = 0.5: the big matrices are clipped, the norm
+    vectors are not (their norms are ~0.03)."""
+    g = gs.make(dtype_cfg)
+    r, ro, tr, out = check_per_tensor(g.arrays, g.dtype, 0.5, what=dtype_cfg)
+    flags = [t["clipped"] for t in ro["tensors"]]
+    assert any(flags) and not all(flags)
