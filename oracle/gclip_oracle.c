@@ -218,6 +218,28 @@ int oracle_clip(void* const* ptrs, const int64_t* numels, int32_t n, int32_t dt,
   return oracle_scale(ptrs, numels, n, dt, s);
 }
 
+/* Accumulation across microbatches (backprop lesson, section "Accumulation
+ * across microbatches"): the backward pass of every microbatch adds its
+ * gradient into the gradient buffer (+=, not =), and the clip runs once the
+ * last one is in (glossary page, section "Order changes the result").  One
+ * such +=: acc[i] <- acc[i] + g[i] for every element, rounded once to the
+ * storage format.  The sum is formed in binary64 and then rounded to the
+ * format; binary64 carries at least 2p + 2 bits for every format here (p =
+ * 24, 11 and 8), so that pair of roundings gives the correctly rounded sum in
+ * the format, the IEEE addition of the format itself.  acc and g hold n
+ * tensors of numels[t] elements of format dt; g is only read. */
+int oracle_accumulate(void* const* acc, const void* const* g, const int64_t* numels, int32_t n, int32_t dt) {
+  if (n < 0 || !dtype_ok(dt) || (n > 0 && (!acc || !g || !numels))) return -1;
+  for (int32_t t = 0; t < n; ++t) {
+    if (numels[t] < 0) return -1;
+    for (int64_t i = 0; i < numels[t]; ++i) {
+      const double s = oracle_decode(acc[t], i, dt) + oracle_decode(g[t], i, dt);
+      store_bits(acc[t], i, dt, oracle_encode(s, dt));
+    }
+  }
+  return 0;
+}
+
 /* Per-tensor clipping (grad clip lesson, section "Two variants: Per-Tensor
  * or Global"): every tensor is clipped on its own, by its own norm -- the
  * case split of the global clip with one tensor in place of the whole list.

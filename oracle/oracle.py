@@ -54,6 +54,9 @@ class Oracle:
         lib.oracle_clip.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_int32, dp, i32p]
         lib.oracle_clip.restype = ctypes.c_int
+        lib.oracle_accumulate.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i64p, ctypes.c_int32,
+                                          ctypes.c_int32]
+        lib.oracle_accumulate.restype = ctypes.c_int
         lib.oracle_clip_per_tensor.argtypes = [ctypes.POINTER(vp), i64p, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_double, ctypes.c_double, ctypes.c_int32, dp, i32p, dp, i32p]
         lib.oracle_clip_per_tensor.restype = ctypes.c_int
@@ -176,6 +179,24 @@ class Oracle:
                 for pp, g, mm, vv in zip(params, grads, m, v)]
         return res, ([o[0] for o in outs], [o[1] for o in outs], [o[2] for o in outs])
 
+    def accumulate_(self, acc, contrib, dtype: str) -> None:
+        """acc[t] += contrib[t] in place, every element rounded once to the
+        storage format (backprop lesson, "Accumulation across microbatches")."""
+        if len(acc) != len(contrib) or any(a.shape != g.shape for a, g in zip(acc, contrib)):
+            raise ValueError("accumulate: the two lists must have the same shapes")
+        pa, numels, n = _marshal(acc, dtype)
+        pg, _, _ = _marshal(contrib, dtype)
+        if self.lib.oracle_accumulate(pa, pg, numels, n, _CODE[dtype]) != 0:
+            raise ValueError("oracle_accumulate rejected its arguments")
+
+    def accumulate_clip_(self, acc, contrib, dtype: str, max_norm: float, avg_factor: float = 1.0,
+                         error_if_nonfinite: bool = False) -> dict:
+        """The last microbatch's += followed by the clip of the sum: the norm
+        is that of a times the accumulated buffer (glossary page, "Order
+        changes the result": clip after the whole effective batch is in)."""
+        self.accumulate_(acc, contrib, dtype)
+        return self.clip_(acc, dtype, max_norm, avg_factor, error_if_nonfinite)
+
     def clip_per_tensor_(self, arrays, dtype: str, max_norm: float, avg_factor: float = 1.0,
                          error_if_nonfinite: bool = False) -> dict:
         """Per-tensor clipping in place: every tensor by its own norm (grad
@@ -282,6 +303,14 @@ def clip_(arrays, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False):
 
 def adamw(p, grad, m, v, dtype, s, lr, beta1, beta2, eps, weight_decay, step):
     return default().adamw(p, grad, m, v, dtype, s, lr, beta1, beta2, eps, weight_decay, step)
+
+
+def accumulate_(acc, contrib, dtype):
+    return default().accumulate_(acc, contrib, dtype)
+
+
+def accumulate_clip_(acc, contrib, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False):
+    return default().accumulate_clip_(acc, contrib, dtype, max_norm, avg_factor, error_if_nonfinite)
 
 
 def clip_per_tensor_(arrays, dtype, max_norm, avg_factor=1.0, error_if_nonfinite=False):

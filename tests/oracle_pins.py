@@ -565,6 +565,72 @@ def pin_amp_update_matches_torch(o):
             assert sc == float(ts.item()) and tr == int(tt.item()), (growth, backoff, interval, sc, ts.item())
 
 
+# ---------------------------------------------------------------- the last microbatch's +=
+def pin_accumulate_library(o):
+    """One += is the IEEE addition of the storage format: bit for bit the same
+    as numpy's float32 and float16 additions and torch's bfloat16 addition,
+    over random values of many magnitudes and the special cases (overflow to
+    Inf, Inf - Inf, subnormals, x + (-x) = +0, -0 + -0 = -0)."""
+    import torch
+    rng = np.random.default_rng(70)
+    special = {"f32": [3.0e38, 3.0e38, -0.0, -0.0, 1e-45, -1e-45, math.inf, -math.inf, 7.0, -7.0, 1e-40, 2e-40],
+               "f16": [60000.0, 60000.0, -0.0, -0.0, 6e-8, -6e-8, math.inf, -math.inf, 7.0, -7.0, 3e-6, 1e-6],
+               "bf16": [3.0e38, 3.0e38, -0.0, -0.0, 1e-39, -1e-39, math.inf, -math.inf, 7.0, -7.0, 5e-39, 1e-40]}
+    for dt in DTYPES:
+        lo, hi = (-17.0, 10.5) if dt == "f16" else (-30.0, 30.0)  # inside the format's range
+        mags = np.exp(rng.uniform(lo, hi, 4000)) * rng.choice([-1.0, 1.0], 4000)
+        x = store(np.concatenate([mags, special[dt][0::2]]), dt)
+        y = store(np.concatenate([rng.permutation(mags) * rng.uniform(0.0, 2.0, 4000), special[dt][1::2]]), dt)
+        acc = [x.copy()]
+        o.accumulate_(acc, [y], dt)
+        with np.errstate(over="ignore", invalid="ignore"):
+            if dt == "f32":
+                ref = (x + y).view(np.uint32)
+            elif dt == "f16":
+                ref = (x.view(np.float16) + y.view(np.float16)).view(np.uint16)
+            else:
+                tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+                ty = torch.from_numpy(y.view(np.int16)).view(torch.bfloat16)
+                ref = (tx + ty).view(torch.int16).numpy().view(np.uint16)
+        got = raw_bits(acc[0], dt)
+        nan = np.isnan(values(acc[0], dt))
+        assert np.array_equal(nan, np.isnan(values(ref if dt != "f32" else ref.view(np.float32), dt))), dt
+        assert np.array_equal(got[~nan], np.asarray(ref)[~nan]), (dt, np.flatnonzero(got[~nan] != ref[~nan])[:5])
+
+
+def pin_accumulate_four_microbatches(o):
+    """Four contributions added in order, ((c0 + c1) + c2) + c3, give numpy's
+    float32 sums bit for bit; the norm of the average (a = 1/4) of the buffer
+    is the library norm of 0.25 times it."""
+    rng = np.random.default_rng(71)
+    sizes = (1000, 3, 517)
+    cs = [[store(rng.standard_normal(n) * 1e-3, "f32") for n in sizes] for _ in range(4)]
+    acc = [c.copy() for c in cs[0]]
+    for k in range(1, 4):
+        o.accumulate_(acc, cs[k], "f32")
+    for t in range(len(sizes)):
+        ref = ((cs[0][t] + cs[1][t]) + cs[2][t]) + cs[3][t]
+        assert np.array_equal(acc[t].view(np.uint32), ref.view(np.uint32)), t
+    before = [a.copy() for a in cs[0]]
+    for k in range(1, 3):
+        o.accumulate_(before, cs[k], "f32")
+    r = o.accumulate_clip_(before, cs[3], "f32", 1e30, 0.25)
+    ref_norm = math.sqrt(sum(np.linalg.norm(0.25 * a.astype(np.float64)) ** 2 for a in acc))
+    assert abs(r["norm"] - ref_norm) <= 1e-13 * ref_norm
+    # the clip at 1e30 does not clip, but the averaging by 1/4 is written back (exact in binary32 here)
+    assert all(np.array_equal(x, y * np.float32(0.25)) for x, y in zip(before, acc))
+
+
+def pin_accumulate_then_clip_golden(o):
+    """Glossary page, "Order changes the result": 10 and -9 are accumulated to
+    1 first, and the clip of the sum at 5 keeps it."""
+    gd = golden("accumulate_then_clip.json")
+    for dt in DTYPES:
+        acc = [store([gd["contributions"][0]], dt)]
+        r = o.accumulate_clip_(acc, [store([gd["contributions"][1]], dt)], dt, gd["max_norm"])
+        assert values(acc[0], dt)[0] == gd["clip_of_sum"] and r["norm"] == gd["sum"] and not r["clipped"]
+
+
 # ---------------------------------------------------------------- per-tensor clipping
 def pin_per_tensor_contrast(o):
     """Grad clip lesson, "Two variants: Per-Tensor or Global": each tensor is
@@ -669,4 +735,5 @@ ALL_PINS = [pin_worked_6_8, pin_not_per_coordinate, pin_sgd_step_length, pin_acc
             pin_adamw_first_step, pin_adamw_decay_only, pin_adamw_constant_gradient, pin_adamw_matches_torch,
             pin_adamw_after_clip, pin_amp_unscale_before_clip, pin_amp_found_inf_writes_nothing,
             pin_amp_update_closed_form, pin_amp_update_matches_torch, pin_per_tensor_contrast,
-            pin_per_tensor_library, pin_per_tensor_single_is_global, pin_per_tensor_nonfinite]
+            pin_per_tensor_library, pin_per_tensor_single_is_global, pin_per_tensor_nonfinite,
+            pin_accumulate_library, pin_accumulate_four_microbatches, pin_accumulate_then_clip_golden]

@@ -58,6 +58,12 @@ MUTANTS = {
                                 "    oracle_scale(&ptrs[t], &numels[t], 1, dt, s_t);"),
     "per_tensor_scales_first_only": ("    if (!skip) oracle_scale(&ptrs[t], &numels[t], 1, dt, s_t);",
                                      "    if (!skip && t == 0) oracle_scale(&ptrs[t], &numels[t], 1, dt, s_t);"),
+    "accumulate_drops_contribution": ("const double s = oracle_decode(acc[t], i, dt) + oracle_decode(g[t], i, dt);",
+                                      "const double s = oracle_decode(acc[t], i, dt);"),
+    "accumulate_subtracts": ("const double s = oracle_decode(acc[t], i, dt) + oracle_decode(g[t], i, dt);",
+                             "const double s = oracle_decode(acc[t], i, dt) - oracle_decode(g[t], i, dt);"),
+    "accumulate_next_element": ("const double s = oracle_decode(acc[t], i, dt) + oracle_decode(g[t], i, dt);",
+                                "const double s = oracle_decode(acc[t], i, dt) + oracle_decode(g[t], i + 1 < numels[t] ? i + 1 : i, dt);"),
     "overflow_not_to_inf": ("if (E > emax) return sign | exp_all;  /* already", "if (E > emax + 1) return sign | exp_all;  /* already"),
 }
 
