@@ -16,6 +16,7 @@ Prints one JSON line.  Other modes:
   --path fused|split   force the kernel path
   --path adamw|amp     the clip fused into AdamW; the loss-scaled clip
   --path per_tensor    per-tensor clipping and per-tensor norms
+  --path accum         the last microbatch's += fused with the norm pass
   --profile-pass       a short run for rocprofv3 (no CPU baseline, plus a
                        calibration copy of known size for the PMC counters)
   --summarize-rocprof  turn rocprofv3 output into the summaries kept in
@@ -115,12 +116,15 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="andrea120m_f32")
-    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw", "amp", "per_tensor"], default="auto",
+    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw", "amp", "per_tensor", "accum"],
+                    default="auto",
                     help="adamw: time the clip fused into an AdamW step (gclip_norm + gclip_adamw_step) "
                          "against gclip_clip_ followed by the same AdamW step; amp: time the loss-scaled "
                          "clip (gclip_clip_amp_) against gclip_clip_ with the same factor given by the host; "
                          "per_tensor: time the per-tensor clip (gclip_clip_per_tensor_) and the per-tensor "
-                         "norms alone (gclip_tensor_norms)")
+                         "norms alone (gclip_tensor_norms); accum: time the last microbatch's += fused with the "
+                         "clip (gclip_accumulate_clip_) on the four-microbatch list against torch's += followed "
+                         "by gclip_clip_")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -147,6 +151,8 @@ def main():
         print("bench.py needs the GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if a.path == "accum":
+        return bench_accum(a, G, gs)
     g = gs.make(a.config)
     esize = 4 if g.dtype == "f32" else 2
     tensors = upload(g.arrays, g.dtype)
@@ -389,6 +395,84 @@ def bench_amp(a, G, g, grads, pristine, flush, gl):
         "host_factor_ms_per_step": round(plain_ms, 5),
         "loss_scale_overhead_ms": round(ms - plain_ms, 5),
         "state_after": {"scale": state[0], "growth_tracker": state[1], "found_inf": state[2]},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_accum(a, G, gs):
+    """The last microbatch's += fused with the norm pass, then the scale pass
+    (gclip_accumulate_clip_: three kernels), on the four-microbatch ANDREA-
+    120M fp32 list: the buffer holds ((c0 + c1) + c2), the contribution is c3,
+    a = 1/4, max_norm 1.0 (the average has norm ~4.8, so every step clips).
+    Against the separate form: torch's += (torch._foreach_add_) and then
+    gclip_clip_.  The buffer is restored and the caches flushed before every
+    step; each step and the accumulate kernel alone are timed with HIP
+    events."""
+    import torch
+    buf, last = gs.andrea120m_f32_accum4_parts()
+    acc = upload(buf.arrays, "f32")
+    contrib = upload(last.arrays, "f32")
+    pristine = [t.clone() for t in acc]
+    flush = torch.ones((2 << 30) // 8, dtype=torch.int64, device="cuda")
+    gl = G.GradList(acc)
+    c = G.Contribution(gl, contrib)
+    stream = torch.cuda.current_stream()
+    n = buf.numel
+    max_norm, avg = 1.0, buf.avg_factor
+
+    def restore():
+        for x, y in zip(acc, pristine):
+            x.copy_(y)
+        flush.sum()
+
+    def run(which, ev):
+        restore()
+        ev[0].record(stream)
+        if which == "fused":
+            gl.accumulate_clip_(c, max_norm, avg)
+        elif which == "norm_only":
+            gl.accumulate_norm(c, avg)
+        else:
+            torch._foreach_add_(acc, contrib)
+            gl.clip_(max_norm, avg)
+        ev[1].record(stream)
+
+    times = {}
+    for which in ("fused", "norm_only", "separate"):
+        for _ in range(a.warmup):
+            run(which, [torch.cuda.Event(enable_timing=True) for _ in range(2)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+        for ev in evs:
+            run(which, ev)
+        torch.cuda.synchronize()
+        times[which] = [e[0].elapsed_time(e[1]) for e in evs]
+        if which == "fused":
+            st, r = gl.read()
+    c.close()
+    gl.close()
+    ms = statistics.fmean(times["fused"])
+    acc_ms = statistics.fmean(times["norm_only"])
+    sep_ms = statistics.fmean(times["separate"])
+    alg = 5 * n * 4  # += reads the buffer and c3, writes the buffer; the scale pass reads and writes it
+    acc_alg = 3 * n * 4
+    gbps = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "last += fused with clip_grad_norm, GB/s, four-microbatch ANDREA-120M fp32",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOADS["andrea120m_f32"].replace(", N(0,1e-3^2), max_norm 1.0", "") +
+                   "; buffer ((c0+c1)+c2) and contribution c3, each N(0,1e-3^2), a = 1/4, max_norm 1.0",
+                   "name": "andrea120m_f32_accum4", "launches_per_step": 3, "algorithmic_bytes_per_step": alg,
+                   "clipped": bool(r["clipped"]), "norm": r["norm"]},
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "accumulate_norm_ms": round(acc_ms, 5),
+        "accumulate_norm_gbps": round(acc_alg / (acc_ms * 1e-3) / 1e9, 1),
+        "separate_ms_per_step": round(sep_ms, 5),
+        "separate_note": "torch._foreach_add_ then gclip_clip_ (fused kernel)",
+        "saved_vs_separate": round(1.0 - ms / sep_ms, 4),
+        "status": st,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -23,7 +23,8 @@ __all__ = ["GclipError", "GclipResult", "GradList", "clip_grad_norm_", "gclip_li
            "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string", "gclip_version",
            "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step", "AdamWList",
            "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp", "AmpState",
-           "gclip_tensor_norms", "gclip_clip_per_tensor_", "TENSOR_RESULT_DTYPE",
+           "gclip_tensor_norms", "gclip_clip_per_tensor_", "TENSOR_RESULT_DTYPE", "gclip_contrib_create",
+           "gclip_contrib_destroy", "gclip_accumulate_norm", "gclip_accumulate_clip_", "Contribution",
            "GCLIP_F32", "GCLIP_F16", "GCLIP_BF16", "GCLIP_PATH_AUTO", "GCLIP_PATH_FUSED", "GCLIP_PATH_SPLIT"]
 
 DTYPE_CODES = {"f32": GCLIP_F32, "f16": GCLIP_F16, "bf16": GCLIP_BF16}
@@ -179,6 +180,30 @@ def gclip_clip_per_tensor_(handle, max_norm, avg_factor, error_if_nonfinite, d_t
                                            ctypes.c_void_p(int(stream))), "gclip_clip_per_tensor_")
 
 
+def gclip_contrib_create(handle, d_contrib):
+    n = len(d_contrib)
+    arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(a)) for a in d_contrib])
+    out = ctypes.c_void_p()
+    _check(_lib.lib.gclip_contrib_create(handle, arr, ctypes.byref(out)), "gclip_contrib_create")
+    return out
+
+
+def gclip_contrib_destroy(handle):
+    _check(_lib.lib.gclip_contrib_destroy(handle), "gclip_contrib_destroy")
+
+
+def gclip_accumulate_norm(handle, contrib, avg_factor, d_tensors, d_result, stream):
+    _check(_lib.lib.gclip_accumulate_norm(handle, contrib, float(avg_factor), ctypes.c_void_p(int(d_tensors or 0)),
+                                          ctypes.c_void_p(int(d_result)), ctypes.c_void_p(int(stream))),
+           "gclip_accumulate_norm")
+
+
+def gclip_accumulate_clip_(handle, contrib, max_norm, avg_factor, error_if_nonfinite, d_result, stream):
+    _check(_lib.lib.gclip_accumulate_clip_(handle, contrib, float(max_norm), float(avg_factor),
+                                           int(bool(error_if_nonfinite)), ctypes.c_void_p(int(d_result)),
+                                           ctypes.c_void_p(int(stream))), "gclip_accumulate_clip_")
+
+
 def _amp_params(growth_factor, backoff_factor, growth_interval):
     return GclipAmpParams(float(growth_factor), float(backoff_factor), int(growth_interval), 0)
 
@@ -293,6 +318,18 @@ class GradList:
         import torch
         (torch.cuda.current_stream() if stream is None else stream).synchronize()
 
+    def accumulate_norm(self, contrib, avg_factor=1.0, per_tensor=False, stream=None):
+        """The last += (grads += contrib) fused with the norm pass; the
+        per-tensor figures too when per_tensor is set (read_tensors)."""
+        gclip_accumulate_norm(self.handle, contrib.handle, avg_factor,
+                              self.tensor_results.data_ptr() if per_tensor else 0, self.d_result,
+                              self._stream(stream))
+
+    def accumulate_clip_(self, contrib, max_norm, avg_factor=1.0, error_if_nonfinite=False, stream=None):
+        """The last += and the global clip of the sum."""
+        gclip_accumulate_clip_(self.handle, contrib.handle, max_norm, avg_factor, error_if_nonfinite, self.d_result,
+                               self._stream(stream))
+
     def norm_amp(self, n_microbatches, amp, stream=None):
         """Norm of the unscaled, averaged gradient: a = 1 / (n * S), S read
         from ``amp`` on the device."""
@@ -310,6 +347,35 @@ class GradList:
     def close(self):
         if getattr(self, "handle", None):
             gclip_list_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Contribution:
+    """One microbatch's gradient buffers registered for a GradList (same
+    shapes and dtype, each at the same address modulo 16 bytes as the list's
+    tensor): ``grads.accumulate_norm(contrib)`` is the last += fused with the
+    norm pass."""
+
+    def __init__(self, grad_list, tensors):
+        tensors = list(tensors)
+        if len(tensors) != len(grad_list.tensors):
+            raise ValueError("one contribution tensor per gradient tensor")
+        for c, t in zip(tensors, grad_list.tensors):
+            if c.dtype != t.dtype or c.numel() != t.numel() or not c.is_contiguous() or c.device != t.device:
+                raise ValueError("contribution tensors must match the gradients in dtype, size and device")
+        self.tensors = tensors
+        self.grad_list = grad_list
+        self.handle = gclip_contrib_create(grad_list.handle, [c.data_ptr() for c in tensors])
+
+    def close(self):
+        if getattr(self, "handle", None):
+            gclip_contrib_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -86,6 +86,10 @@ def _declare(lib):
         "gclip_adamw_destroy": ([vp], i32),
         "gclip_adamw_step": ([vp, ctypes.POINTER(GclipAdamwHparams), dbl, dbl, i32, vp, vp], i32),
         "gclip_tensor_norms": ([vp, dbl, vp, vp, vp], i32),
+        "gclip_contrib_create": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp)], i32),
+        "gclip_contrib_destroy": ([vp], i32),
+        "gclip_accumulate_norm": ([vp, vp, dbl, vp, vp, vp], i32),
+        "gclip_accumulate_clip_": ([vp, vp, dbl, dbl, i32, vp, vp], i32),
         "gclip_clip_per_tensor_": ([vp, dbl, dbl, i32, vp, vp, vp], i32),
         "gclip_norm_amp": ([vp, dbl, vp, vp, vp], i32),
         "gclip_clip_amp_": ([vp, dbl, dbl, vp, ctypes.POINTER(GclipAmpParams), vp, vp], i32),
@@ -126,4 +130,5 @@ EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_
            "gclip_scale", "gclip_clip_", "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string",
            "gclip_last_hip_error", "gclip_version", "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step",
            "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp", "gclip_tensor_norms",
-           "gclip_clip_per_tensor_")
+           "gclip_clip_per_tensor_", "gclip_contrib_create", "gclip_contrib_destroy", "gclip_accumulate_norm",
+           "gclip_accumulate_clip_")

@@ -37,6 +37,8 @@ hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, doubl
 hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
                               gclip_tensor_result* out, gclip_result* res, hipStream_t st);
 hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st);
+hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
+                                  gclip_tensor_result* out, gclip_result* res, hipStream_t st);
 }  // namespace gclip
 
 // How long a workgroup of the fused kernel waits at the grid-wide decision
@@ -50,6 +52,9 @@ struct gclip_list {
   gclip::DevPlan dev{};
   gclip::TensorHostPlan tplan;
   gclip::TensorPlan tdev{};
+  gclip_tensor_result* tscratch = nullptr;  // per-tensor figures when the caller passes none
+  std::vector<uint64_t> addrs;              // the tensors, as given
+  std::vector<int64_t> numels;
   void* blob = nullptr;
   int device = 0;
   bool fused_ok = false;
@@ -58,6 +63,12 @@ struct gclip_list {
   int64_t wait_us = kDefaultWaitUs;
   uint64_t clock_khz = 0;  // device wall clock
   uint64_t wait_ticks = 0;
+};
+
+struct gclip_contrib {
+  const gclip_list* list = nullptr;
+  uint64_t* delta = nullptr;  // device: n_tensors byte offsets, contribution minus list tensor
+  int device = 0;
 };
 
 struct gclip_adamw {
@@ -260,7 +271,8 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
                  o_fuss = take(nchs * 4), o_sum = take(nsum * 4), o_wksc = take((nw + 1) * 8),
                  o_sca = take(nsc * 8), o_part = take((nsum * waves + nw) * 8), o_bc = take(8),
                  o_sync = take((size_t)gclip::kSyncWords * 4), o_bst = take(nw * 4),
-                 o_tpc = take(ntp * sizeof(gclip::TPiece)), o_tfi = take(ntf * 4), o_tpa = take(ntp * 8);
+                 o_tpc = take(ntp * sizeof(gclip::TPiece)), o_tfi = take(ntf * 4), o_tpa = take(ntp * 8),
+                 o_tsc = take((size_t)P.n_tensors * sizeof(gclip_tensor_result));
     if ((e = hipMalloc(&L->blob, off)) != hipSuccess) {
       delete L;
       g_last_hip = (int32_t)e;
@@ -315,6 +327,9 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     T.npieces = (uint32_t)ntp;
     T.ntensors = (int32_t)P.n_tensors;
     T.nt_store = D.nt_store;
+    L->tscratch = reinterpret_cast<gclip_tensor_result*>(b + o_tsc);
+    L->addrs.assign(addrs, addrs + n_tensors);
+    L->numels.assign(numels, numels + n_tensors);
     *out = L;
     return GCLIP_OK;
   } catch (const std::bad_alloc&) {
@@ -453,6 +468,90 @@ gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double av
   hipError_t e = gclip::launch_tensor_norm(list->tdev, list->plan.dtype, gclip::AvgSrc{avg_factor, nullptr},
                                            max_norm, 1, error_if_nonfinite ? 1 : 0, d_tensors, d_result, s);
   if (e == hipSuccess) e = gclip::launch_tensor_scale(list->tdev, list->plan.dtype, d_tensors, s);
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_contrib_create(const gclip_list* list, void* const* d_contrib, gclip_contrib** out) {
+  if (!out) return GCLIP_EINVAL;
+  *out = nullptr;
+  if (!list) return GCLIP_EINVAL;
+  const size_t n = list->addrs.size();
+  if (n > 0 && !d_contrib) return GCLIP_EINVAL;
+  const uint64_t es = (uint64_t)gclip::dtype_bytes(list->plan.dtype);
+  try {
+    std::vector<uint64_t> delta(n, 0);
+    std::vector<std::pair<uint64_t, uint64_t>> ranges;
+    for (size_t t = 0; t < n; ++t) {
+      const uint64_t a = list->addrs[t], g = reinterpret_cast<uint64_t>(d_contrib[t]);
+      const uint64_t bytes = (uint64_t)list->numels[t] * es;
+      if (bytes == 0) continue;
+      if (g == 0 || g % es != 0 || (g - a) % 16 != 0 || g + bytes < g) return GCLIP_EINVAL;
+      delta[t] = g - a;
+      ranges.emplace_back(a, a + bytes);
+      ranges.emplace_back(g, g + bytes);
+    }
+    std::sort(ranges.begin(), ranges.end());
+    for (size_t i = 1; i < ranges.size(); ++i)
+      if (ranges[i].first < ranges[i - 1].second) return GCLIP_EINVAL;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev != list->device) return GCLIP_EINVAL;
+    gclip_contrib* C = new gclip_contrib();
+    C->list = list;
+    C->device = dev;
+    if ((e = hipMalloc(&C->delta, (n ? n : 1) * 8)) != hipSuccess) {
+      delete C;
+      g_last_hip = (int32_t)e;
+      return GCLIP_ENOMEM;
+    }
+    if (n && (e = hipMemcpy(C->delta, delta.data(), n * 8, hipMemcpyHostToDevice)) != hipSuccess) {
+      (void)hipFree(C->delta);
+      delete C;
+      return hip_fail(e);
+    }
+    *out = C;
+    return GCLIP_OK;
+  } catch (const std::bad_alloc&) {
+    return GCLIP_ENOMEM;
+  }
+}
+
+gclip_status gclip_contrib_destroy(gclip_contrib* contrib) {
+  if (!contrib) return GCLIP_OK;
+  const hipError_t e = contrib->delta ? hipFree(contrib->delta) : hipSuccess;
+  delete contrib;
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_accumulate_norm(gclip_list* list, const gclip_contrib* contrib, double avg_factor,
+                                   gclip_tensor_result* d_tensors, gclip_result* d_result, void* stream) {
+  if (!list || !contrib || contrib->list != list || !result_ptr_ok(d_result) || !factor_ok(avg_factor) ||
+      (d_tensors && !tensor_out_ok(list, d_tensors)))
+    return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
+  const hipError_t e = gclip::launch_accumulate_norm(list->tdev, list->plan.dtype, contrib->delta,
+                                                     gclip::AvgSrc{avg_factor, nullptr},
+                                                     d_tensors ? d_tensors : list->tscratch, d_result,
+                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_accumulate_clip_(gclip_list* list, const gclip_contrib* contrib, double max_norm,
+                                    double avg_factor, int32_t error_if_nonfinite, gclip_result* d_result,
+                                    void* stream) {
+  if (!list || !contrib || contrib->list != list || !result_ptr_ok(d_result) || !threshold_ok(max_norm) ||
+      !factor_ok(avg_factor))
+    return GCLIP_EINVAL;
+  gclip_status st = check_device(list);
+  if (st != GCLIP_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const gclip::AvgSrc avg{avg_factor, nullptr};
+  hipError_t e = gclip::launch_accumulate_norm(list->tdev, list->plan.dtype, contrib->delta, avg, list->tscratch,
+                                               d_result, s);
+  if (e == hipSuccess)
+    e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg, error_if_nonfinite ? 1 : 0, d_result, s);
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 

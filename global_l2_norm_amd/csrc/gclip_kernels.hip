@@ -1136,6 +1136,83 @@ __global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const g
   piece_scale<DT, NTS>(T, pc, s64, (float)s64);
 }
 
+// ---------------------------------------------------------------- the last microbatch's += with the norm
+// Backprop lesson, "Accumulation across microbatches": acc += g, rounded once
+// to the storage format.  The 16-bit formats add in fp32 and round to the
+// format: fp32 has at least 2p + 2 bits for both (p = 11, 8), so the two
+// roundings agree with the format's own correctly rounded addition.  The
+// squares of the values written are summed as in the norm pass, one partial
+// per piece; k_tensor_decide then reduces them.
+template <int DT>
+__device__ __forceinline__ uint32_t add_elem(uint32_t a, uint32_t g) {
+  if constexpr (DT == GCLIP_F32) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(g));
+  } else if constexpr (DT == GCLIP_F16) {
+    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)a) + (float)__builtin_bit_cast(_Float16, (uint16_t)g);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
+  } else {
+    const float s = __uint_as_float(a << 16) + __uint_as_float(g << 16);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 add_vec(u32x4 a, u32x4 g) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (DT == GCLIP_F32) {
+      r[c] = add_elem<DT>(a[c], g[c]);
+    } else {
+      r[c] = add_elem<DT>(a[c] & 0xffffu, g[c] & 0xffffu) | (add_elem<DT>(a[c] >> 16, g[c] >> 16) << 16);
+    }
+  }
+  return r;
+}
+
+// One workgroup per piece; gdelta[t] is the byte offset from tensor t of the
+// list to tensor t of the contribution (same alignment, so the same vector
+// layout).
+template <int DT, bool NTS>
+__global__ __launch_bounds__(kThreads) void k_accum_partial(TensorPlan T, const uint64_t* gdelta) {
+  __shared__ double red[kWaves];
+  const TPiece pc = ld_table(T.pieces, blockIdx.x);
+  const uint64_t d = ld_table(gdelta, (uint64_t)uniform32(pc.tensor));
+  const uint32_t t = threadIdx.x;
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+  g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
+  const g_u32x4* gbase = reinterpret_cast<const g_u32x4*>(uniform64(pc.addr + d));
+  const uint32_t nvec = uniform32(pc.nvec);
+  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
+    u32x4 q[kUnroll], h[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      const bool ok = i < nvec;
+      q[u] = ok ? ld_vec<kNtSum>(base + i) : u32x4{0u, 0u, 0u, 0u};
+      h[u] = ok ? ld_vec<kNtSum>(gbase + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      const u32x4 n = add_vec<DT>(q[u], h[u]);
+      if (i < nvec) st_vec<NTS>(base + i, n);
+      acc[u] += vec_sumsq<DT>(n);
+    }
+  }
+  double s = 0.0;
+  for (uint32_t i = t; i < pc.sc_count; i += kThreads) {
+    const uint64_t a = T.sc_addr[pc.sc_begin + i];
+    const uint32_t v = add_elem<DT>(load_elem<DT>(a), load_elem<DT>(a + d));
+    store_elem<DT>(a, v);
+    s += elem_square<DT>(v);
+  }
+  const double part = wg_sum(lane_total(acc, s), red);
+  if (t == 0) T.partials[blockIdx.x] = part;
+}
+
 // ---------------------------------------------------------------- AdamW on the clipped gradient
 // Grad clip lesson, "Order matters: Pre-Adam": the optimizer's moments see
 // the clipped gradient.  Each workgroup updates one piece of one tensor: the
@@ -1331,6 +1408,26 @@ hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_t
   void* args[] = {&tc, &out};
   const void* fn = T.nt_store ? tensor_scale_kernel<true>(dtype) : tensor_scale_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
+}
+
+template <bool NTS>
+const void* accum_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_accum_partial<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_accum_partial<GCLIP_F16, NTS>
+                              : (const void*)k_accum_partial<GCLIP_BF16, NTS>;
+}
+
+hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
+                                  gclip_tensor_result* out, gclip_result* res, hipStream_t st) {
+  if (T.npieces > 0) {
+    TensorPlan tc = T;
+    void* args[] = {&tc, &gdelta};
+    const void* fn = T.nt_store ? accum_kernel<true>(dtype) : accum_kernel<false>(dtype);
+    const hipError_t e = hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, 0.0, 0, 0, out, res);
+  return hipGetLastError();
 }
 
 hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,

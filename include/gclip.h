@@ -317,6 +317,48 @@ gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double av
                                     gclip_result* d_result, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The norm pass fused into the last microbatch's +=.
+ *
+ * Backprop lesson, section "Accumulation across microbatches": the backward
+ * pass of every microbatch adds its gradient into the gradient buffer (+=);
+ * the glossary page, section "Order changes the result", clips once the last
+ * contribution is in.  The last += reads the buffer and the contribution and
+ * writes the buffer anyway, so it sums the squares of the values it writes:
+ * the norm then needs no read pass of its own.
+ * ------------------------------------------------------------------------- */
+
+typedef struct gclip_contrib gclip_contrib;
+
+/* Register the buffers of one microbatch's contribution to a list's
+ * gradients: d_contrib[t] holds the list's numels[t] elements of its dtype,
+ * at the same address modulo 16 bytes as the list's tensor t (as separately
+ * allocated tensors are), overlapping no tensor of the list and no other
+ * contribution tensor.  The caller keeps the buffers alive and unmoved while
+ * the handle is used; they are only read.  Uploads one 8-byte offset per
+ * tensor; allocates and synchronises (not a hot call).  GCLIP_EINVAL on a
+ * NULL pointer, a misaligned address or an overlap. */
+gclip_status gclip_contrib_create(const gclip_list* list, void* const* d_contrib, gclip_contrib** out);
+gclip_status gclip_contrib_destroy(gclip_contrib* contrib);
+
+/* The last +=, fused with the norm pass: for every element of the list,
+ * acc <- acc + g rounded once to the storage format (the format's own IEEE
+ * addition) and written back; the norm of a * acc (the new values) goes into
+ * d_result (sumsq, norm, nonfinite; decided = 0) and, when d_tensors is not
+ * NULL, every tensor's figures into d_tensors (n_tensors entries, as for
+ * gclip_tensor_norms).  gclip_scale can then finish the global clip, or
+ * gclip_adamw_step the optimizer step.  contrib must have been registered
+ * for this list.  Two kernels on `stream`; no allocation, no
+ * synchronisation. */
+gclip_status gclip_accumulate_norm(gclip_list* list, const gclip_contrib* contrib, double avg_factor,
+                                   gclip_tensor_result* d_tensors, gclip_result* d_result, void* stream);
+
+/* gclip_accumulate_norm followed by gclip_scale: the last += and the global
+ * clip of a * acc.  Three kernels; no allocation, no synchronisation. */
+gclip_status gclip_accumulate_clip_(gclip_list* list, const gclip_contrib* contrib, double max_norm,
+                                    double avg_factor, int32_t error_if_nonfinite, gclip_result* d_result,
+                                    void* stream);
+
+/* ---------------------------------------------------------------------------
  * Loss-scaled steps (mixed precision).
  *
  * Glossary page, introduction and section "Order changes the result": with

@@ -186,6 +186,28 @@ def andrea120m_f32_accum4(seed: int = 4, threads=None):
     return g
 
 
+def andrea120m_f32_accum4_parts(seed: int = 4, threads=None):
+    """The same four microbatch draws as andrea120m_f32_accum4, split before
+    the last +=: the buffer after three contributions ((c0 + c1) + c2, float32
+    adds in order) and the fourth contribution c3.  (buffer, contribution)."""
+    shapes = shapes_andrea120m()
+    threads = threads or _default_threads()
+
+    def one(t):
+        n = int(np.prod(shapes[t][1]))
+        acc = to_storage(_draw([seed, 0, t], n, 1e-3), F32)
+        for k in range(1, 3):
+            acc = acc + to_storage(_draw([seed, k, t], n, 1e-3), F32)
+        return acc, to_storage(_draw([seed, 3, t], n, 1e-3), F32)
+
+    pairs = _pool_map(one, list(range(len(shapes))), threads)
+    names, dims = [s[0] for s in shapes], [tuple(s[1]) for s in shapes]
+    buf = GradSet("andrea120m_f32_accum4_buffer", F32, names, dims, [p[0] for p in pairs])
+    buf.avg_factor = 0.25
+    buf.notes["microbatches"] = 4
+    return buf, GradSet("andrea120m_f32_accum4_last", F32, names, dims, [p[1] for p in pairs])
+
+
 def flat_f32(seed: int = 6, threads=None):
     """The ANDREA-120M element count as one fp32 tensor (the same bytes with
     no tensor boundaries), N(0, 1e-3^2), max_norm 1.0."""

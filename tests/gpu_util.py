@@ -73,7 +73,12 @@ def assert_elems_close(gpu_list, ref_list, dtype, what=""):
 
 def assert_bitwise_equal(a_list, b_list, what=""):
     for t, (a, b) in enumerate(zip(a_list, b_list)):
-        assert a.tobytes() == b.tobytes(), f"{what}: tensor {t} differs"
+        if a.tobytes() != b.tobytes():
+            ua = a.view(np.uint32 if a.itemsize == 4 else np.uint16)
+            ub = b.view(np.uint32 if b.itemsize == 4 else np.uint16)
+            bad = np.flatnonzero(ua != ub)[:6]
+            raise AssertionError(f"{what}: tensor {t} differs at {bad.size}+ places, first (index, got bits, "
+                                 f"expected bits): {[(int(i), hex(int(ua[i])), hex(int(ub[i]))) for i in bad]}")
 
 
 def assert_norm_close(gpu_norm, ref_norm, what=""):
@@ -85,3 +90,12 @@ def assert_norm_close(gpu_norm, ref_norm, what=""):
         return
     assert abs(gpu_norm - ref_norm) <= TOL_NORM * abs(ref_norm) + (0.0 if ref_norm else 0.0), \
         f"{what}: gpu norm {gpu_norm!r} vs oracle {ref_norm!r}"
+
+
+def assert_bitwise_equal_but_nan(a_list, b_list, dtype, what=""):
+    """Bit for bit, except that a NaN matches any NaN: IEEE 754 leaves the
+    sign and payload of a NaN an operation returns to the implementation."""
+    for t, (a, b) in enumerate(zip(a_list, b_list)):
+        na, nb = np.isnan(values(a, dtype)), np.isnan(values(b, dtype))
+        assert np.array_equal(na, nb), f"{what}: tensor {t}: NaN at different places"
+        assert_bitwise_equal([a[~na]], [b[~nb]], f"{what} (tensor {t}, NaNs aside)")
