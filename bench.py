@@ -282,7 +282,8 @@ def bench_adamw(a, G, g, grads, pristine, flush, gl):
             x.copy_(y)
         for x in m + v:
             x.zero_()
-        flush.sum()
+        if not a.no_flush:
+            flush.sum()
 
     def run(fused, ev):
         restore()
@@ -354,7 +355,8 @@ def bench_amp(a, G, g, grads, pristine, flush, gl):
         for x, y in zip(grads, pristine):
             x.copy_(y)
         amp.set(AMP_SCALE)
-        flush.sum()
+        if not a.no_flush:
+            flush.sum()
 
     def run(loss_scaled, ev):
         restore()
@@ -424,7 +426,8 @@ def bench_accum(a, G, gs):
     def restore():
         for x, y in zip(acc, pristine):
             x.copy_(y)
-        flush.sum()
+        if not a.no_flush:
+            flush.sum()
 
     def run(which, ev):
         restore()
@@ -493,7 +496,8 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
     def restore():
         for x, y in zip(grads, pristine):
             x.copy_(y)
-        flush.sum()
+        if not a.no_flush:
+            flush.sum()
 
     def run(which, ev):
         restore()

@@ -1032,7 +1032,7 @@ __device__ __forceinline__ void piece_scale(const TensorPlan& T, const TPiece& p
   }
 }
 
-constexpr int kStage = 16384;  // partials staged in LDS at once by k_tensor_decide (128 KB)
+constexpr int kStage = 12288;  // partials staged in LDS at once by k_tensor_decide (96 KB + 48 KB of owners)
 constexpr int kStageBatch = 16;  // loads in flight per lane while staging
 
 template <int DT>
@@ -1045,46 +1045,103 @@ __global__ __launch_bounds__(kThreads) void k_tensor_partial(TensorPlan T) {
 
 // One workgroup.  Every tensor's figures and, for the per-tensor clip (clip
 // != 0), its decision; then the list's result block.  With the stop switch,
-// a NaN/Inf in any tensor stops the whole update.  Tensor k is summed by
-// lane k % kThreads, in piece order, across the staged windows; its running
-// sum is kept in out[k].sumsq until the last window.
+// a NaN/Inf in any tensor stops the whole update.
+//
+// The partials are staged in LDS in windows of kStage, with the tensor of
+// each piece.  A segmented sum in two levels, in a fixed order: lane i sums
+// the staged pieces [i C, (i + 1) C) in order, cut where a tensor starts,
+// and leaves each fragment's sum in place at the fragment's first piece;
+// then the lane that owns tensor k (k % kThreads) adds the tensor's
+// fragments in order -- the one at its first piece in the window and one at
+// every chunk start inside it.  A lane keeps its first tensor's running sum
+// in a register and any further tensor's in out[k].
+__device__ __forceinline__ double tensor_in_window(const double* stage, uint32_t C, uint32_t lo, uint32_t hi) {
+  double S = stage[lo];
+  for (uint32_t j = (lo / C + 1) * C; j < hi; j += C) S += stage[j];
+  return S;
+}
+
 __global__ __launch_bounds__(kThreads) void k_tensor_decide(TensorPlan T, AvgSrc avs, double max_norm, int clip,
                                                             int err, gclip_tensor_result* out, gclip_result* res) {
   __shared__ double stage[kStage];
+  __shared__ uint32_t owner[kStage];
   __shared__ double red[kWaves];
   const double avg = avg_value(avs);
   const uint32_t t = threadIdx.x;
-  for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) out[k].sumsq = 0.0;
+  const int32_t k0 = (int32_t)t;  // this lane's first tensor
+  const bool has0 = k0 < T.ntensors;
+  const uint32_t b0 = has0 ? T.first[k0] : 0u, e0 = has0 ? T.first[k0 + 1] : 0u;
+  double S0 = 0.0;
+  for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) out[k].sumsq = 0.0;  // further tensors' sums
   for (uint32_t w0 = 0; w0 < T.npieces; w0 += kStage) {
     const uint32_t wn = T.npieces - w0 < (uint32_t)kStage ? T.npieces - w0 : (uint32_t)kStage;
     __syncthreads();  // the previous window is no longer read
     for (uint32_t i0 = 0; i0 < wn; i0 += (uint32_t)(kThreads * kStageBatch)) {
       double v[kStageBatch];
+      uint32_t o[kStageBatch];
 #pragma unroll
       for (int u = 0; u < kStageBatch; ++u) {
         const uint32_t i = i0 + (uint32_t)u * kThreads + t;
         v[u] = i < wn ? T.partials[w0 + i] : 0.0;
+        o[u] = i < wn ? T.pieces[w0 + i].tensor : 0u;
       }
 #pragma unroll
       for (int u = 0; u < kStageBatch; ++u) {
         const uint32_t i = i0 + (uint32_t)u * kThreads + t;
-        if (i < wn) stage[i] = v[u];
+        if (i < wn) {
+          stage[i] = v[u];
+          owner[i] = o[u];
+        }
       }
     }
     __syncthreads();
-    for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) {
+    // level 1: this lane's chunk, cut where a tensor starts
+    const uint32_t C = (wn + kThreads - 1) / kThreads;
+    {
+      const uint32_t cb = t * C, ce = cb + C < wn ? cb + C : wn;
+      if (cb < ce) {
+        uint32_t start = cb;
+        double acc = stage[cb];
+        for (uint32_t i = cb + 1; i < ce; ++i) {
+          const double v = stage[i];
+          if (owner[i] != owner[i - 1]) {
+            stage[start] = acc;
+            start = i;
+            acc = v;
+          } else {
+            acc += v;
+          }
+        }
+        stage[start] = acc;
+      }
+    }
+    __syncthreads();
+    // level 2: each tensor's fragments in this window
+    const uint32_t wend = w0 + wn;
+    if (has0) {
+      const uint32_t lo = b0 > w0 ? b0 : w0, hi = e0 < wend ? e0 : wend;
+      if (lo < hi) S0 += tensor_in_window(stage, C, lo - w0, hi - w0);
+    }
+    for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) {
       const uint32_t b = T.first[k], e = T.first[k + 1];
-      const uint32_t lo = b > w0 ? b : w0, hi = e < w0 + wn ? e : w0 + wn;
-      if (lo >= hi) continue;
-      double S = out[k].sumsq;
-#pragma unroll 8
-      for (uint32_t i = lo; i < hi; ++i) S += stage[i - w0];
-      out[k].sumsq = S;
+      const uint32_t lo = b > w0 ? b : w0, hi = e < wend ? e : wend;
+      if (lo < hi) out[k].sumsq += tensor_in_window(stage, C, lo - w0, hi - w0);
     }
   }
   double mine = 0.0;
   int nf_mine = 0;
-  for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) {
+  double sumsq0 = 0.0;
+  int nf0 = 0;
+  if (has0) {
+    sumsq0 = (avg * avg) * S0;
+    nf0 = nonfinite_of(S0, avg);
+    out[k0].sumsq = sumsq0;
+    out[k0].norm = sqrt(sumsq0);
+    out[k0].nonfinite = nf0;
+    mine = S0;
+    nf_mine = nf0;
+  }
+  for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) {
     const double S = out[k].sumsq;
     const double sumsq = (avg * avg) * S;
     const int nf = nonfinite_of(S, avg);
@@ -1098,9 +1155,11 @@ __global__ __launch_bounds__(kThreads) void k_tensor_decide(TensorPlan T, AvgSrc
   const int nf_any = __syncthreads_or(nf_mine);
   const int skip = (clip && err && nf_any) ? 1 : 0;
   int clipped_mine = 0;
-  for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) {
+  for (int32_t k = k0; k < T.ntensors; k += kThreads) {
+    const double sumsq = k == k0 ? sumsq0 : out[k].sumsq;
+    const int nf = k == k0 ? nf0 : out[k].nonfinite;
     if (clip) {
-      const Decision d = decide(out[k].sumsq, out[k].nonfinite, max_norm, avg, err);
+      const Decision d = decide(sumsq, nf, max_norm, avg, err);
       out[k].scale = (skip || d.s == 1.0) ? 1.0 : d.s;
       out[k].clipped = d.clipped;
       clipped_mine |= d.clipped;
