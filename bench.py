@@ -37,7 +37,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "clip_grad_norm GB/s and % of HBM peak, ANDREA-120M-shaped grads"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["global_l2_norm_amd/csrc/gclip_kernels.hip", "global_l2_norm_amd/csrc/gclip_cursor.hpp"]
+KERNEL_SOURCES = ["global_l2_norm_amd/csrc/gclip_kernels.hip", "global_l2_norm_amd/csrc/gclip_cursor.hpp",
+                  "global_l2_norm_amd/csrc/gclip_device.hpp"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_grad_clip_fused__andrea120m_f32__pmc.txt")
 WORKLOADS = {
     "andrea120m_f32": "ANDREA-120M-shaped fp32 gradient list: 124 tensors (tok_embed [8449,768], pos_embed "

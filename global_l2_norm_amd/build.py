@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgclip.so")
 BENCH = os.path.join(HERE, "gclip_bench")
-SOURCES = ["gclip_api.cpp", "gclip_plan.cpp", "gclip_trace.cpp", "gclip_kernels.hip"]
+SOURCES = ["gclip_api.cpp", "gclip_plan.cpp", "gclip_trace.cpp", "gclip_kernels.hip", "gclip_tensor.hip",
+           "gclip_adamw.hip"]
 ARCH = os.environ.get("GCLIP_OFFLOAD_ARCH", "gfx950")
 
 

@@ -40,180 +40,10 @@
 
 #include "../../include/gclip.h"
 #include "gclip_cursor.hpp"
+#include "gclip_device.hpp"
 #include "gclip_plan.hpp"
 
 namespace gclip {
-
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Gradient memory is accessed through global-address-space pointers so that
-// the loads are global_load (vector memory counter only), not flat loads,
-// which would also be waited for by every scalar-load and LDS wait.
-typedef __attribute__((address_space(1))) u32x4 g_u32x4;
-typedef __attribute__((address_space(1))) uint32_t g_u32;
-typedef __attribute__((address_space(1))) uint16_t g_u16;
-
-// Gradient vectors are read once per pass with no reuse that a cache could
-// catch (the Infinity Cache does not keep read data between the passes), so
-// they are read with nontemporal loads, which stream through the caches
-// without displacing other lines: a cold 369 MB read ran about 10% faster
-// that way on MI355X.  Stores are ordinary for lists below kNtStoreMinBytes
-// -- the 256 MB Infinity Cache then absorbs much of the write-back, and
-// nontemporal stores made a 369 MB scale pass 18% slower -- and nontemporal
-// for larger lists, whose writes only thrash it (3% faster at 2.6 GB).
-// (The load kind of each pass can be chosen at build time.)
-constexpr bool kNtSum = GCLIP_NT_SUM != 0;
-constexpr bool kNtScale = GCLIP_NT_SCALE != 0;
-
-template <bool NT>
-__device__ __forceinline__ u32x4 ld_vec(const g_u32x4* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(p);
-  else return *p;
-}
-template <bool NT>
-__device__ __forceinline__ void st_vec(g_u32x4* p, u32x4 q) {
-  if constexpr (NT) __builtin_nontemporal_store(q, p);
-  else *p = q;
-}
-template <bool NT>
-__device__ __forceinline__ u32x4 load_vec(uint64_t a) { return ld_vec<NT>(reinterpret_cast<const g_u32x4*>(a)); }
-template <bool NT>
-__device__ __forceinline__ void store_vec(uint64_t a, u32x4 q) { st_vec<NT>(reinterpret_cast<g_u32x4*>(a), q); }
-
-// ---------------------------------------------------------------- element arithmetic
-// Sum of the squares of one vector's elements, exact in binary64 for the
-// fallback and within 7 * 2^-24 relative otherwise.  The common case sums the
-// squares in fp32 (binary64 arithmetic on every element would cost more
-// issue slots than the memory pass leaves), which is safe while the fp32 sum
-// lies in [2^-100, 2^126): no square overflowed and an underflowed square
-// (< 2^-126, at most 8 of them) is below 2^-24 of the sum.  Any other vector
-// -- huge or tiny elements, NaN, Inf -- is summed again in binary64, where
-// squares of every finite fp32/fp16/bf16 value are exact and cannot
-// overflow; an all-zero vector is 0 exactly.  fp16 values can never leave
-// the safe range (|x| <= 65504, squares of subnormals are normal fp32).
-__device__ __forceinline__ double sumsq64_f32(const u32x4 q) {
-  double d = 0.0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const double x = (double)__uint_as_float(q[c]);
-    d = __builtin_fma(x, x, d);
-  }
-  return d;
-}
-
-__device__ __forceinline__ double sumsq64_bf16(const u32x4 q) {
-  double d = 0.0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const double lo = (double)__uint_as_float(q[c] << 16), hi = (double)__uint_as_float(q[c] & 0xffff0000u);
-    d = __builtin_fma(lo, lo, d);
-    d = __builtin_fma(hi, hi, d);
-  }
-  return d;
-}
-
-__device__ __forceinline__ bool fp32_sum_safe(float s) { return s >= 0x1p-100f && s < 0x1p+126f; }
-
-template <int DT>
-__device__ __forceinline__ double vec_sumsq(const u32x4 q) {
-  if constexpr (DT == GCLIP_F32) {
-    const float x0 = __uint_as_float(q[0]), x1 = __uint_as_float(q[1]);
-    const float x2 = __uint_as_float(q[2]), x3 = __uint_as_float(q[3]);
-    float s = x0 * x0;
-    s = __builtin_fmaf(x1, x1, s);
-    s = __builtin_fmaf(x2, x2, s);
-    s = __builtin_fmaf(x3, x3, s);
-    if (__builtin_expect(fp32_sum_safe(s), 1)) return (double)s;
-    if (((q[0] | q[1] | q[2] | q[3]) & 0x7fffffffu) == 0u) return 0.0;
-    return sumsq64_f32(q);
-  } else if constexpr (DT == GCLIP_F16) {
-    float s = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[c] & 0xffffu));
-      const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[c] >> 16));
-      s = __builtin_fmaf(lo, lo, s);
-      s = __builtin_fmaf(hi, hi, s);
-    }
-    return (double)s;
-  } else {
-    float s = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float lo = __uint_as_float(q[c] << 16), hi = __uint_as_float(q[c] & 0xffff0000u);
-      s = __builtin_fmaf(lo, lo, s);
-      s = __builtin_fmaf(hi, hi, s);
-    }
-    if (__builtin_expect(fp32_sum_safe(s), 1)) return (double)s;
-    if (((q[0] | q[1] | q[2] | q[3]) & 0x7fff7fffu) == 0u) return 0.0;
-    return sumsq64_bf16(q);
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ double elem_square(uint32_t bits) {
-  double x;
-  if constexpr (DT == GCLIP_F32) {
-    x = (double)__uint_as_float(bits);
-  } else if constexpr (DT == GCLIP_F16) {
-    x = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-  } else {
-    x = (double)__uint_as_float(bits << 16);
-  }
-  return x * x;
-}
-
-// g * s rounded to nearest-even in the storage format.  fp32 storage is
-// multiplied in binary64 (one rounding of the binary64 product); the 16-bit
-// formats multiply in fp32 by s rounded to fp32.
-template <int DT>
-__device__ __forceinline__ uint32_t scale_elem(uint32_t bits, double s64, float s32) {
-  if constexpr (DT == GCLIP_F32) {
-    return __float_as_uint((float)((double)__uint_as_float(bits) * s64));
-  } else if constexpr (DT == GCLIP_F16) {
-    const _Float16 h = (_Float16)((float)__builtin_bit_cast(_Float16, (uint16_t)bits) * s32);
-    return (uint32_t)__builtin_bit_cast(uint16_t, h);
-  } else {
-    const __bf16 h = (__bf16)(__uint_as_float(bits << 16) * s32);
-    return (uint32_t)__builtin_bit_cast(uint16_t, h);
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ u32x4 scale_vec(u32x4 q, double s64, float s32) {
-  u32x4 r;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t w = q[c];
-    if constexpr (DT == GCLIP_F32) {
-      r[c] = scale_elem<DT>(w, s64, s32);
-    } else {
-      r[c] = scale_elem<DT>(w & 0xffffu, s64, s32) | (scale_elem<DT>(w >> 16, s64, s32) << 16);
-    }
-  }
-  return r;
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t load_elem(uint64_t a) {
-  if constexpr (DT == GCLIP_F32) return *reinterpret_cast<const g_u32*>(a);
-  else return (uint32_t)*reinterpret_cast<const g_u16*>(a);
-}
-
-template <int DT>
-__device__ __forceinline__ void store_elem(uint64_t a, uint32_t bits) {
-  if constexpr (DT == GCLIP_F32) *reinterpret_cast<g_u32*>(a) = bits;
-  else *reinterpret_cast<g_u16*>(a) = (uint16_t)bits;
-}
-
-// A lane's total: its per-slot accumulators in slot order, then its single elements.
-__device__ __forceinline__ double lane_total(const double (&acc)[kUnroll], double accs) {
-  double t = acc[0];
-#pragma unroll
-  for (int u = 1; u < kUnroll; ++u) t += acc[u];
-  return t + accs;
-}
 
 // ---------------------------------------------------------------- group loads and stores
 // Load the vectors of one group into q (zeros where a lane has no vector).
@@ -336,25 +166,6 @@ __device__ __forceinline__ void scale_scalars(const DevPlan& p, int w, double s6
 }
 
 // ---------------------------------------------------------------- counters in the workspace
-// Cross-workgroup data (partials, the decision, the counters) is written and
-// read only with agent-scope atomics, which go to the device-coherent level
-// of the memory system.
-__device__ __forceinline__ uint32_t atomic_ld(const uint32_t* a) {
-  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_st(uint32_t* a, uint32_t v) {
-  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t atomic_add(uint32_t* a, uint32_t v) {
-  return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ double atomic_ld(const double* a) {
-  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_st(double* a, double v) {
-  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Words of line 0 of sync.
 constexpr int kEpochWord = 0, kSkipWord = 1, kHandedWord = 2;
 
@@ -365,16 +176,6 @@ __device__ __forceinline__ uint32_t* arrival_tickets(const DevPlan& p) {
 }
 __device__ __forceinline__ uint32_t* finish_tickets(const DevPlan& p) {
   return p.sync + (2 + 3 * kPools) * kSyncLineWords;
-}
-
-// Waiting for this workgroup's stores to complete before its next atomic is
-// issued orders them for every reader, so no agent-scope fence is needed: on
-// gfx950 such a fence writes back and invalidates the whole L2 of the XCD,
-// which costs ~18 us when 256 workgroups do it at the end of a pass.
-__device__ __forceinline__ void complete_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Ticket over every workgroup of a launch, in two levels: workgroup w counts
@@ -600,22 +401,6 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, c
 }
 
 // ---------------------------------------------------------------- reductions and the decision
-// Sum of v over the workgroup, the same bits in every thread.  Butterfly
-// inside each wave (a + b == b + a, so every lane holds the same sum), then
-// the wave sums in wave order.
-__device__ __forceinline__ double wg_sum(double v, double* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();  // red may still be read by a previous call
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  double t = red[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) t += red[i];
-  return t;
-}
-
 // Partials: one per wave per sum chunk, then one per worker.
 __device__ __forceinline__ uint32_t npartials(const DevPlan& p) {
   return p.nsum * (uint32_t)kWaves + (uint32_t)p.nworkers;
@@ -638,53 +423,6 @@ __device__ __forceinline__ double partials_sum(const DevPlan& p, double* red) {
 __device__ __forceinline__ void poison_partials(const DevPlan& p) {
   const uint32_t n = npartials(p);
   for (uint32_t i = threadIdx.x; i < n; i += kThreads) atomic_st(&p.partials[i], __builtin_nan(""));
-}
-
-struct Decision {
-  double s;
-  int clipped, skip;
-};
-
-// Grad clip lesson "Math" / glossary "Mechanism and details": unchanged when
-// norm <= c, factor c / norm when norm > c; times the averaging factor a.
-__device__ __forceinline__ Decision decide(double sumsq, int nonfinite, double max_norm, double avg, int err) {
-  Decision d;
-  const double norm = sqrt(sumsq);
-  d.clipped = norm > max_norm ? 1 : 0;
-  const double coef = d.clipped ? max_norm / norm : 1.0;
-  d.skip = (nonfinite && err) ? 1 : 0;
-  d.s = avg * coef;
-  return d;
-}
-
-// The averaging factor: given by the host, or 1 / (n * S) with the loss
-// scale S read from device memory (loss-scaled steps).
-__device__ __forceinline__ double avg_value(const AvgSrc& s) {
-  return s.scale ? 1.0 / (s.a * (double)*s.scale) : s.a;
-}
-
-// The flag of a NaN/Inf element: the raw sum of squares is not finite.  An
-// averaging factor that is not finite and positive (only possible when it
-// comes from a loss scale that is not) counts as one too, so that nothing
-// is written.
-__device__ __forceinline__ int nonfinite_of(double S, double avg) {
-  return (__builtin_isfinite(S) && __builtin_isfinite(avg) && avg > 0.0) ? 0 : 1;
-}
-
-__device__ __forceinline__ void write_norm(gclip_result* res, double S, double avg) {
-  const double sumsq = (avg * avg) * S;
-  res->sumsq = sumsq;
-  res->norm = sqrt(sumsq);
-  res->nonfinite = nonfinite_of(S, avg);
-}
-
-__device__ __forceinline__ void write_decision(gclip_result* res, const Decision& d, double max_norm) {
-  const bool wrote = !(d.skip || d.s == 1.0);
-  res->scale = wrote ? d.s : 1.0;
-  res->clipped = d.clipped;
-  res->skipped = d.skip;
-  res->max_norm = max_norm;
-  res->decided = 1;
 }
 
 // Arrival after the summing pass: true in the last workgroup (all threads).
@@ -973,418 +711,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   finish<DT>(p, res, true, hs, &flag);
 }
 
-// ---------------------------------------------------------------- per-tensor norms and clipping
-// Grad clip lesson, "Two variants: Per-Tensor or Global": every tensor by its
-// own norm, in the three kernels of the lesson's pipeline.  k_tensor_partial:
-// one workgroup per piece (a run of one tensor, TPiece), kUnroll vectors in
-// flight per lane, one partial per piece, plain stores and no atomics (a
-// returning atomic per workgroup held each workgroup's slot for a round trip
-// to the device-coherent level, and the pieces of one large tensor queued on
-// its counter).  k_tensor_decide: one workgroup stages the partials in LDS,
-// every lane loading many at once, sums each tensor's pieces in piece order
-// and takes the decisions.  k_tensor_scale: one workgroup per piece.  Every
-// sum is taken in a fixed order, so the bits do not depend on scheduling.
-
-template <int DT>
-__device__ __forceinline__ double piece_sumsq(const TensorPlan& T, const TPiece& pc) {
-  const uint32_t t = threadIdx.x;
-  double acc[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
-  const g_u32x4* base = reinterpret_cast<const g_u32x4*>(uniform64(pc.addr));
-  const uint32_t nvec = uniform32(pc.nvec);
-  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
-    u32x4 q[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t i = piece_index(j, u, t);
-      q[u] = i < nvec ? ld_vec<kNtSum>(base + i) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
-  }
-  double s = 0.0;
-  for (uint32_t i = t; i < pc.sc_count; i += kThreads) s += elem_square<DT>(load_elem<DT>(T.sc_addr[pc.sc_begin + i]));
-  return lane_total(acc, s);
-}
-
-template <int DT, bool NTS>
-__device__ __forceinline__ void piece_scale(const TensorPlan& T, const TPiece& pc, double s64, float s32) {
-  const uint32_t t = threadIdx.x;
-  g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
-  const uint32_t nvec = uniform32(pc.nvec);
-  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
-    u32x4 q[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t i = piece_index(j, u, t);
-      if (i < nvec) q[u] = ld_vec<kNtScale>(base + i);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t i = piece_index(j, u, t);
-      if (i < nvec) st_vec<NTS>(base + i, scale_vec<DT>(q[u], s64, s32));
-    }
-  }
-  for (uint32_t i = t; i < pc.sc_count; i += kThreads) {
-    const uint64_t a = T.sc_addr[pc.sc_begin + i];
-    store_elem<DT>(a, scale_elem<DT>(load_elem<DT>(a), s64, s32));
-  }
-}
-
-constexpr int kStage = 12288;  // partials staged in LDS at once by k_tensor_decide (96 KB + 48 KB of owners)
-constexpr int kStageBatch = 16;  // loads in flight per lane while staging
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_tensor_partial(TensorPlan T) {
-  __shared__ double red[kWaves];
-  const TPiece pc = ld_table(T.pieces, blockIdx.x);
-  const double part = wg_sum(piece_sumsq<DT>(T, pc), red);
-  if (threadIdx.x == 0) T.partials[blockIdx.x] = part;
-}
-
-// One workgroup.  Every tensor's figures and, for the per-tensor clip (clip
-// != 0), its decision; then the list's result block.  With the stop switch,
-// a NaN/Inf in any tensor stops the whole update.
-//
-// The partials are staged in LDS in windows of kStage, with the tensor of
-// each piece.  A segmented sum in two levels, in a fixed order: lane i sums
-// the staged pieces [i C, (i + 1) C) in order, cut where a tensor starts,
-// and leaves each fragment's sum in place at the fragment's first piece;
-// then the lane that owns tensor k (k % kThreads) adds the tensor's
-// fragments in order -- the one at its first piece in the window and one at
-// every chunk start inside it.  A lane keeps its first tensor's running sum
-// in a register and any further tensor's in out[k].
-__device__ __forceinline__ double tensor_in_window(const double* stage, uint32_t C, uint32_t lo, uint32_t hi) {
-  double S = stage[lo];
-  for (uint32_t j = (lo / C + 1) * C; j < hi; j += C) S += stage[j];
-  return S;
-}
-
-__global__ __launch_bounds__(kThreads) void k_tensor_decide(TensorPlan T, AvgSrc avs, double max_norm, int clip,
-                                                            int err, gclip_tensor_result* out, gclip_result* res) {
-  __shared__ double stage[kStage];
-  __shared__ uint32_t owner[kStage];
-  __shared__ double red[kWaves];
-  const double avg = avg_value(avs);
-  const uint32_t t = threadIdx.x;
-  const int32_t k0 = (int32_t)t;  // this lane's first tensor
-  const bool has0 = k0 < T.ntensors;
-  const uint32_t b0 = has0 ? T.first[k0] : 0u, e0 = has0 ? T.first[k0 + 1] : 0u;
-  double S0 = 0.0;
-  for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) out[k].sumsq = 0.0;  // further tensors' sums
-  for (uint32_t w0 = 0; w0 < T.npieces; w0 += kStage) {
-    const uint32_t wn = T.npieces - w0 < (uint32_t)kStage ? T.npieces - w0 : (uint32_t)kStage;
-    __syncthreads();  // the previous window is no longer read
-    for (uint32_t i0 = 0; i0 < wn; i0 += (uint32_t)(kThreads * kStageBatch)) {
-      double v[kStageBatch];
-      uint32_t o[kStageBatch];
-#pragma unroll
-      for (int u = 0; u < kStageBatch; ++u) {
-        const uint32_t i = i0 + (uint32_t)u * kThreads + t;
-        v[u] = i < wn ? T.partials[w0 + i] : 0.0;
-        o[u] = i < wn ? T.pieces[w0 + i].tensor : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kStageBatch; ++u) {
-        const uint32_t i = i0 + (uint32_t)u * kThreads + t;
-        if (i < wn) {
-          stage[i] = v[u];
-          owner[i] = o[u];
-        }
-      }
-    }
-    __syncthreads();
-    // level 1: this lane's chunk, cut where a tensor starts
-    const uint32_t C = (wn + kThreads - 1) / kThreads;
-    {
-      const uint32_t cb = t * C, ce = cb + C < wn ? cb + C : wn;
-      if (cb < ce) {
-        uint32_t start = cb;
-        double acc = stage[cb];
-        for (uint32_t i = cb + 1; i < ce; ++i) {
-          const double v = stage[i];
-          if (owner[i] != owner[i - 1]) {
-            stage[start] = acc;
-            start = i;
-            acc = v;
-          } else {
-            acc += v;
-          }
-        }
-        stage[start] = acc;
-      }
-    }
-    __syncthreads();
-    // level 2: each tensor's fragments in this window
-    const uint32_t wend = w0 + wn;
-    if (has0) {
-      const uint32_t lo = b0 > w0 ? b0 : w0, hi = e0 < wend ? e0 : wend;
-      if (lo < hi) S0 += tensor_in_window(stage, C, lo - w0, hi - w0);
-    }
-    for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) {
-      const uint32_t b = T.first[k], e = T.first[k + 1];
-      const uint32_t lo = b > w0 ? b : w0, hi = e < wend ? e : wend;
-      if (lo < hi) out[k].sumsq += tensor_in_window(stage, C, lo - w0, hi - w0);
-    }
-  }
-  double mine = 0.0;
-  int nf_mine = 0;
-  double sumsq0 = 0.0;
-  int nf0 = 0;
-  if (has0) {
-    sumsq0 = (avg * avg) * S0;
-    nf0 = nonfinite_of(S0, avg);
-    out[k0].sumsq = sumsq0;
-    out[k0].norm = sqrt(sumsq0);
-    out[k0].nonfinite = nf0;
-    mine = S0;
-    nf_mine = nf0;
-  }
-  for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) {
-    const double S = out[k].sumsq;
-    const double sumsq = (avg * avg) * S;
-    const int nf = nonfinite_of(S, avg);
-    out[k].sumsq = sumsq;
-    out[k].norm = sqrt(sumsq);
-    out[k].nonfinite = nf;
-    mine += S;
-    nf_mine |= nf;
-  }
-  const double S = wg_sum(mine, red);
-  const int nf_any = __syncthreads_or(nf_mine);
-  const int skip = (clip && err && nf_any) ? 1 : 0;
-  int clipped_mine = 0;
-  for (int32_t k = k0; k < T.ntensors; k += kThreads) {
-    const double sumsq = k == k0 ? sumsq0 : out[k].sumsq;
-    const int nf = k == k0 ? nf0 : out[k].nonfinite;
-    if (clip) {
-      const Decision d = decide(sumsq, nf, max_norm, avg, err);
-      out[k].scale = (skip || d.s == 1.0) ? 1.0 : d.s;
-      out[k].clipped = d.clipped;
-      clipped_mine |= d.clipped;
-    } else {
-      out[k].scale = 1.0;
-      out[k].clipped = 0;
-    }
-  }
-  const int clipped_any = __syncthreads_or(clipped_mine);
-  // the partials have all been read: overwrite them with NaN, so that a
-  // partial read before it is written could only show up as a NaN norm
-  for (uint32_t i = t; i < T.npieces; i += kThreads) T.partials[i] = __builtin_nan("");
-  if (t == 0) {
-    write_norm(res, S, avg);
-    res->nonfinite = nf_any | res->nonfinite;
-    res->scale = 1.0;
-    res->clipped = clipped_any;
-    res->skipped = skip;
-    if (clip) res->max_norm = max_norm;
-    res->decided = clip ? 1 : 0;
-    res->status = 0;
-    res->handed_back = 0;
-  }
-}
-
-// Every piece multiplied by its tensor's factor (nothing written where that
-// factor is 1).  Grid: npieces.
-template <int DT, bool NTS>
-__global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const gclip_tensor_result* out) {
-  const TPiece pc = ld_table(T.pieces, blockIdx.x);
-  const double s64 = out[uniform32(pc.tensor)].scale;
-  if (s64 == 1.0) return;
-  piece_scale<DT, NTS>(T, pc, s64, (float)s64);
-}
-
-// ---------------------------------------------------------------- the last microbatch's += with the norm
-// Backprop lesson, "Accumulation across microbatches": acc += g, rounded once
-// to the storage format.  The 16-bit formats add in fp32 and round to the
-// format: fp32 has at least 2p + 2 bits for both (p = 11, 8), so the two
-// roundings agree with the format's own correctly rounded addition.  The
-// squares of the values written are summed as in the norm pass, one partial
-// per piece; k_tensor_decide then reduces them.
-template <int DT>
-__device__ __forceinline__ uint32_t add_elem(uint32_t a, uint32_t g) {
-  if constexpr (DT == GCLIP_F32) {
-    return __float_as_uint(__uint_as_float(a) + __uint_as_float(g));
-  } else if constexpr (DT == GCLIP_F16) {
-    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)a) + (float)__builtin_bit_cast(_Float16, (uint16_t)g);
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
-  } else {
-    const float s = __uint_as_float(a << 16) + __uint_as_float(g << 16);
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s);
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ u32x4 add_vec(u32x4 a, u32x4 g) {
-  u32x4 r;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if constexpr (DT == GCLIP_F32) {
-      r[c] = add_elem<DT>(a[c], g[c]);
-    } else {
-      r[c] = add_elem<DT>(a[c] & 0xffffu, g[c] & 0xffffu) | (add_elem<DT>(a[c] >> 16, g[c] >> 16) << 16);
-    }
-  }
-  return r;
-}
-
-// One workgroup per piece; gdelta[t] is the byte offset from tensor t of the
-// list to tensor t of the contribution (same alignment, so the same vector
-// layout).
-template <int DT, bool NTS>
-__global__ __launch_bounds__(kThreads) void k_accum_partial(TensorPlan T, const uint64_t* gdelta) {
-  __shared__ double red[kWaves];
-  const TPiece pc = ld_table(T.pieces, blockIdx.x);
-  const uint64_t d = ld_table(gdelta, (uint64_t)uniform32(pc.tensor));
-  const uint32_t t = threadIdx.x;
-  double acc[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
-  g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
-  const g_u32x4* gbase = reinterpret_cast<const g_u32x4*>(uniform64(pc.addr + d));
-  const uint32_t nvec = uniform32(pc.nvec);
-  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
-    u32x4 q[kUnroll], h[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t i = piece_index(j, u, t);
-      const bool ok = i < nvec;
-      q[u] = ok ? ld_vec<kNtSum>(base + i) : u32x4{0u, 0u, 0u, 0u};
-      h[u] = ok ? ld_vec<kNtSum>(gbase + i) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t i = piece_index(j, u, t);
-      const u32x4 n = add_vec<DT>(q[u], h[u]);
-      if (i < nvec) st_vec<NTS>(base + i, n);
-      acc[u] += vec_sumsq<DT>(n);
-    }
-  }
-  double s = 0.0;
-  for (uint32_t i = t; i < pc.sc_count; i += kThreads) {
-    const uint64_t a = T.sc_addr[pc.sc_begin + i];
-    const uint32_t v = add_elem<DT>(load_elem<DT>(a), load_elem<DT>(a + d));
-    store_elem<DT>(a, v);
-    s += elem_square<DT>(v);
-  }
-  const double part = wg_sum(lane_total(acc, s), red);
-  if (t == 0) T.partials[blockIdx.x] = part;
-}
-
-// ---------------------------------------------------------------- AdamW on the clipped gradient
-// Grad clip lesson, "Order matters: Pre-Adam": the optimizer's moments see
-// the clipped gradient.  Each workgroup updates one piece of one tensor: the
-// weights p and moments m, v (binary32) from the gradient times the factor s
-// of the clip decision, which is read from the result block -- the clipped
-// gradient itself is never written.
-typedef __attribute__((address_space(1))) float g_f32;
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(1))) u32x2 g_u32x2;
-
-template <int DT>
-__device__ __forceinline__ float grad_value(uint32_t bits) {
-  if constexpr (DT == GCLIP_F32) return __uint_as_float(bits);
-  else if constexpr (DT == GCLIP_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-  else return __uint_as_float(bits << 16);
-}
-
-// Four consecutive gradient values from a 4-element-aligned address.
-template <int DT>
-__device__ __forceinline__ void load_grad4(uint64_t a, float (&g)[4]) {
-  if constexpr (DT == GCLIP_F32) {
-    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const g_u32x4*>(a));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) g[k] = __uint_as_float(q[k]);
-  } else {
-    const u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const g_u32x2*>(a));
-    g[0] = grad_value<DT>(q[0] & 0xffffu);
-    g[1] = grad_value<DT>(q[0] >> 16);
-    g[2] = grad_value<DT>(q[1] & 0xffffu);
-    g[3] = grad_value<DT>(q[1] >> 16);
-  }
-}
-
-__device__ __forceinline__ void adamw_elem(float& p, float& m, float& v, float g, const AdamHp& h) {
-  m = h.b1 * m + h.omb1 * g;
-  v = h.b2 * v + h.omb2 * (g * g);
-  const float denom = sqrtf(v) * h.inv_sqrt_bc2 + h.eps;
-  p = p * h.decay - h.step_size * (m / denom);
-}
-
-#ifndef GCLIP_ADAM_UNROLL
-#define GCLIP_ADAM_UNROLL 4
-#endif
-#ifndef GCLIP_ADAM_NT_STORE
-#define GCLIP_ADAM_NT_STORE 0
-#endif
-constexpr int kAdamUnroll = GCLIP_ADAM_UNROLL;
-constexpr bool kAdamNtStore = GCLIP_ADAM_NT_STORE != 0;
-#ifndef GCLIP_ADAM_NT_LOAD
-#define GCLIP_ADAM_NT_LOAD 1
-#endif
-constexpr bool kAdamNtLoad = GCLIP_ADAM_NT_LOAD != 0;
-
-template <int DT>
-__global__ __launch_bounds__(kAdamThreads) void k_adamw_clip(AdamPlan P, AdamHp h, double max_norm, AvgSrc avs,
-                                                             int err, gclip_result* res) {
-  const double avg = avg_value(avs);
-  const Decision d = decide(res->sumsq, res->nonfinite, max_norm, avg, err);
-  if (blockIdx.x == 0 && threadIdx.x == 0) write_decision(res, d, max_norm);
-  if (d.skip || blockIdx.x >= P.npieces) return;
-  const float s = (float)d.s;
-  const AdamPiece pc = ld_table(P.pieces, blockIdx.x);
-  constexpr uint32_t es = DT == GCLIP_F32 ? 4u : 2u;
-  if (pc.vec) {
-    // kAdamUnroll iterations at a time: every load first, then the math, then the stores
-    constexpr uint32_t stride = kAdamThreads * 4u;
-    for (uint32_t i0 = threadIdx.x * 4u; i0 < pc.count; i0 += stride * kAdamUnroll) {
-      u32x4 p4[kAdamUnroll], m4[kAdamUnroll], v4[kAdamUnroll];
-      float g[kAdamUnroll][4];
-#pragma unroll
-      for (int u = 0; u < kAdamUnroll; ++u) {
-        const uint32_t i = i0 + (uint32_t)u * stride;
-        if (i < pc.count) {
-          p4[u] = ld_vec<kAdamNtLoad>(reinterpret_cast<const g_u32x4*>(pc.p + (uint64_t)i * 4u));
-          m4[u] = ld_vec<kAdamNtLoad>(reinterpret_cast<const g_u32x4*>(pc.m + (uint64_t)i * 4u));
-          v4[u] = ld_vec<kAdamNtLoad>(reinterpret_cast<const g_u32x4*>(pc.v + (uint64_t)i * 4u));
-          load_grad4<DT>(pc.g + (uint64_t)i * es, g[u]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kAdamUnroll; ++u) {
-        const uint32_t i = i0 + (uint32_t)u * stride;
-        if (i < pc.count) {
-          u32x4 po, mo, vo;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            float pk = __uint_as_float(p4[u][k]), mk = __uint_as_float(m4[u][k]), vk = __uint_as_float(v4[u][k]);
-            adamw_elem(pk, mk, vk, g[u][k] * s, h);
-            po[k] = __float_as_uint(pk);
-            mo[k] = __float_as_uint(mk);
-            vo[k] = __float_as_uint(vk);
-          }
-          st_vec<kAdamNtStore>(reinterpret_cast<g_u32x4*>(pc.p + (uint64_t)i * 4u), po);
-          st_vec<kAdamNtStore>(reinterpret_cast<g_u32x4*>(pc.m + (uint64_t)i * 4u), mo);
-          st_vec<kAdamNtStore>(reinterpret_cast<g_u32x4*>(pc.v + (uint64_t)i * 4u), vo);
-        }
-      }
-    }
-  } else {
-    for (uint32_t i = threadIdx.x; i < pc.count; i += kAdamThreads) {
-      g_f32* pp = reinterpret_cast<g_f32*>(pc.p + (uint64_t)i * 4u);
-      g_f32* mp = reinterpret_cast<g_f32*>(pc.m + (uint64_t)i * 4u);
-      g_f32* vp = reinterpret_cast<g_f32*>(pc.v + (uint64_t)i * 4u);
-      float pk = *pp, mk = *mp, vk = *vp;
-      const float g = grad_value<DT>(load_elem<DT>(pc.g + (uint64_t)i * es));
-      adamw_elem(pk, mk, vk, g * s, h);
-      *pp = pk;
-      *mp = mk;
-      *vp = vk;
-    }
-  }
-}
-
 // ---------------------------------------------------------------- host launchers
 int worker_threads() { return kThreads; }
 uint64_t resident_cap_vectors() { return kResidentCap; }
@@ -1436,99 +762,6 @@ hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc
   void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch, &wait_ticks};
   const void* fn = p.nt_store ? fused_kernel<true>(dtype) : fused_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
-}
-
-hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
-                              gclip_tensor_result* out, gclip_result* res, hipStream_t st) {
-  if (T.npieces > 0) {
-    const dim3 grid(T.npieces), block(kThreads);
-    switch (dtype) {
-      case GCLIP_F32: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F32>, grid, block, 0, st, T); break;
-      case GCLIP_F16: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F16>, grid, block, 0, st, T); break;
-      default: hipLaunchKernelGGL(k_tensor_partial<GCLIP_BF16>, grid, block, 0, st, T); break;
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, max_norm, clip, err, out, res);
-  return hipGetLastError();
-}
-
-template <bool NTS>
-const void* tensor_scale_kernel(int32_t dtype) {
-  return dtype == GCLIP_F32   ? (const void*)k_tensor_scale<GCLIP_F32, NTS>
-         : dtype == GCLIP_F16 ? (const void*)k_tensor_scale<GCLIP_F16, NTS>
-                              : (const void*)k_tensor_scale<GCLIP_BF16, NTS>;
-}
-
-hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st) {
-  if (T.npieces == 0) return hipSuccess;
-  TensorPlan tc = T;
-  void* args[] = {&tc, &out};
-  const void* fn = T.nt_store ? tensor_scale_kernel<true>(dtype) : tensor_scale_kernel<false>(dtype);
-  return hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
-}
-
-template <bool NTS>
-const void* accum_kernel(int32_t dtype) {
-  return dtype == GCLIP_F32   ? (const void*)k_accum_partial<GCLIP_F32, NTS>
-         : dtype == GCLIP_F16 ? (const void*)k_accum_partial<GCLIP_F16, NTS>
-                              : (const void*)k_accum_partial<GCLIP_BF16, NTS>;
-}
-
-hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
-                                  gclip_tensor_result* out, gclip_result* res, hipStream_t st) {
-  if (T.npieces > 0) {
-    TensorPlan tc = T;
-    void* args[] = {&tc, &gdelta};
-    const void* fn = T.nt_store ? accum_kernel<true>(dtype) : accum_kernel<false>(dtype);
-    const hipError_t e = hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, 0.0, 0, 0, out, res);
-  return hipGetLastError();
-}
-
-hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,
-                        gclip_result* res, hipStream_t st) {
-  const dim3 grid(plan.npieces > 0 ? plan.npieces : 1u), block(kAdamThreads);
-  switch (dtype) {
-    case GCLIP_F32: hipLaunchKernelGGL(k_adamw_clip<GCLIP_F32>, grid, block, 0, st, plan, h, max_norm, avg, err, res); break;
-    case GCLIP_F16: hipLaunchKernelGGL(k_adamw_clip<GCLIP_F16>, grid, block, 0, st, plan, h, max_norm, avg, err, res); break;
-    default: hipLaunchKernelGGL(k_adamw_clip<GCLIP_BF16>, grid, block, 0, st, plan, h, max_norm, avg, err, res); break;
-  }
-  return hipGetLastError();
-}
-
-// The loss scale after a step (dynamic loss scaling as published by
-// Micikevicius et al.): found-inf multiplies it by backoff and restarts the
-// count of clean steps; a clean step counts, and the interval-th one
-// multiplies the scale by growth unless that is not finite in binary32.
-// One thread; the step's kernels ran before it on the same stream.
-__global__ void k_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
-                             int32_t interval) {
-  if (blockIdx.x != 0 || threadIdx.x != 0) return;
-  const int32_t inf = res->nonfinite ? 1 : 0;
-  st->found_inf = inf;
-  if (inf) {
-    st->scale = (float)((double)st->scale * backoff);
-    st->growth_tracker = 0;
-    return;
-  }
-  const int32_t clean = st->growth_tracker + 1;
-  if (clean == interval) {
-    const float grown = (float)((double)st->scale * growth);
-    if (__builtin_isfinite(grown)) st->scale = grown;
-    st->growth_tracker = 0;
-  } else {
-    st->growth_tracker = clean;
-  }
-}
-
-hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
-                             int32_t interval, hipStream_t s) {
-  hipLaunchKernelGGL(k_amp_update, dim3(1), dim3(64), 0, s, res, st, growth, backoff, interval);
-  return hipGetLastError();
 }
 
 // Workgroups of the fused kernel that fit on one compute unit at once (the

@@ -1,0 +1,366 @@
+// gclip_tensor.hip -- gfx950 kernels that work per tensor: per-tensor norms
+// and per-tensor clipping, and the last microbatch's += fused with the norm
+// pass.  Both walk the list's per-tensor pieces (TPiece, gclip_plan.hpp).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/gclip.h"
+#include "gclip_cursor.hpp"
+#include "gclip_device.hpp"
+#include "gclip_plan.hpp"
+
+namespace gclip {
+
+// ---------------------------------------------------------------- per-tensor norms and clipping
+// Grad clip lesson, "Two variants: Per-Tensor or Global": every tensor by its
+// own norm, in the three kernels of the lesson's pipeline.  k_tensor_partial:
+// one workgroup per piece (a run of one tensor, TPiece), kUnroll vectors in
+// flight per lane, one partial per piece, plain stores and no atomics (a
+// returning atomic per workgroup held each workgroup's slot for a round trip
+// to the device-coherent level, and the pieces of one large tensor queued on
+// its counter).  k_tensor_decide: one workgroup stages the partials in LDS,
+// every lane loading many at once, sums each tensor's pieces in piece order
+// and takes the decisions.  k_tensor_scale: one workgroup per piece.  Every
+// sum is taken in a fixed order, so the bits do not depend on scheduling.
+
+template <int DT>
+__device__ __forceinline__ double piece_sumsq(const TensorPlan& T, const TPiece& pc) {
+  const uint32_t t = threadIdx.x;
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+  const g_u32x4* base = reinterpret_cast<const g_u32x4*>(uniform64(pc.addr));
+  const uint32_t nvec = uniform32(pc.nvec);
+  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
+    u32x4 q[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      q[u] = i < nvec ? ld_vec<kNtSum>(base + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
+  }
+  double s = 0.0;
+  for (uint32_t i = t; i < pc.sc_count; i += kThreads) s += elem_square<DT>(load_elem<DT>(T.sc_addr[pc.sc_begin + i]));
+  return lane_total(acc, s);
+}
+
+template <int DT, bool NTS>
+__device__ __forceinline__ void piece_scale(const TensorPlan& T, const TPiece& pc, double s64, float s32) {
+  const uint32_t t = threadIdx.x;
+  g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
+  const uint32_t nvec = uniform32(pc.nvec);
+  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
+    u32x4 q[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      if (i < nvec) q[u] = ld_vec<kNtScale>(base + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      if (i < nvec) st_vec<NTS>(base + i, scale_vec<DT>(q[u], s64, s32));
+    }
+  }
+  for (uint32_t i = t; i < pc.sc_count; i += kThreads) {
+    const uint64_t a = T.sc_addr[pc.sc_begin + i];
+    store_elem<DT>(a, scale_elem<DT>(load_elem<DT>(a), s64, s32));
+  }
+}
+
+constexpr int kStage = 12288;  // partials staged in LDS at once by k_tensor_decide (96 KB + 48 KB of owners)
+constexpr int kStageBatch = 16;  // loads in flight per lane while staging
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_tensor_partial(TensorPlan T) {
+  __shared__ double red[kWaves];
+  const TPiece pc = ld_table(T.pieces, blockIdx.x);
+  const double part = wg_sum(piece_sumsq<DT>(T, pc), red);
+  if (threadIdx.x == 0) T.partials[blockIdx.x] = part;
+}
+
+// One workgroup.  Every tensor's figures and, for the per-tensor clip (clip
+// != 0), its decision; then the list's result block.  With the stop switch,
+// a NaN/Inf in any tensor stops the whole update.
+//
+// The partials are staged in LDS in windows of kStage, with the tensor of
+// each piece.  A segmented sum in two levels, in a fixed order: lane i sums
+// the staged pieces [i C, (i + 1) C) in order, cut where a tensor starts,
+// and leaves each fragment's sum in place at the fragment's first piece;
+// then the lane that owns tensor k (k % kThreads) adds the tensor's
+// fragments in order -- the one at its first piece in the window and one at
+// every chunk start inside it.  A lane keeps its first tensor's running sum
+// in a register and any further tensor's in out[k].
+__device__ __forceinline__ double tensor_in_window(const double* stage, uint32_t C, uint32_t lo, uint32_t hi) {
+  double S = stage[lo];
+  for (uint32_t j = (lo / C + 1) * C; j < hi; j += C) S += stage[j];
+  return S;
+}
+
+__global__ __launch_bounds__(kThreads) void k_tensor_decide(TensorPlan T, AvgSrc avs, double max_norm, int clip,
+                                                            int err, gclip_tensor_result* out, gclip_result* res) {
+  __shared__ double stage[kStage];
+  __shared__ uint32_t owner[kStage];
+  __shared__ double red[kWaves];
+  const double avg = avg_value(avs);
+  const uint32_t t = threadIdx.x;
+  const int32_t k0 = (int32_t)t;  // this lane's first tensor
+  const bool has0 = k0 < T.ntensors;
+  const uint32_t b0 = has0 ? T.first[k0] : 0u, e0 = has0 ? T.first[k0 + 1] : 0u;
+  double S0 = 0.0;
+  for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) out[k].sumsq = 0.0;  // further tensors' sums
+  for (uint32_t w0 = 0; w0 < T.npieces; w0 += kStage) {
+    const uint32_t wn = T.npieces - w0 < (uint32_t)kStage ? T.npieces - w0 : (uint32_t)kStage;
+    __syncthreads();  // the previous window is no longer read
+    for (uint32_t i0 = 0; i0 < wn; i0 += (uint32_t)(kThreads * kStageBatch)) {
+      double v[kStageBatch];
+      uint32_t o[kStageBatch];
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const uint32_t i = i0 + (uint32_t)u * kThreads + t;
+        v[u] = i < wn ? T.partials[w0 + i] : 0.0;
+        o[u] = i < wn ? T.pieces[w0 + i].tensor : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const uint32_t i = i0 + (uint32_t)u * kThreads + t;
+        if (i < wn) {
+          stage[i] = v[u];
+          owner[i] = o[u];
+        }
+      }
+    }
+    __syncthreads();
+    // level 1: this lane's chunk, cut where a tensor starts
+    const uint32_t C = (wn + kThreads - 1) / kThreads;
+    {
+      const uint32_t cb = t * C, ce = cb + C < wn ? cb + C : wn;
+      if (cb < ce) {
+        uint32_t start = cb;
+        double acc = stage[cb];
+        for (uint32_t i = cb + 1; i < ce; ++i) {
+          const double v = stage[i];
+          if (owner[i] != owner[i - 1]) {
+            stage[start] = acc;
+            start = i;
+            acc = v;
+          } else {
+            acc += v;
+          }
+        }
+        stage[start] = acc;
+      }
+    }
+    __syncthreads();
+    // level 2: each tensor's fragments in this window
+    const uint32_t wend = w0 + wn;
+    if (has0) {
+      const uint32_t lo = b0 > w0 ? b0 : w0, hi = e0 < wend ? e0 : wend;
+      if (lo < hi) S0 += tensor_in_window(stage, C, lo - w0, hi - w0);
+    }
+    for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) {
+      const uint32_t b = T.first[k], e = T.first[k + 1];
+      const uint32_t lo = b > w0 ? b : w0, hi = e < wend ? e : wend;
+      if (lo < hi) out[k].sumsq += tensor_in_window(stage, C, lo - w0, hi - w0);
+    }
+  }
+  double mine = 0.0;
+  int nf_mine = 0;
+  double sumsq0 = 0.0;
+  int nf0 = 0;
+  if (has0) {
+    sumsq0 = (avg * avg) * S0;
+    nf0 = nonfinite_of(S0, avg);
+    out[k0].sumsq = sumsq0;
+    out[k0].norm = sqrt(sumsq0);
+    out[k0].nonfinite = nf0;
+    mine = S0;
+    nf_mine = nf0;
+  }
+  for (int32_t k = k0 + kThreads; k < T.ntensors; k += kThreads) {
+    const double S = out[k].sumsq;
+    const double sumsq = (avg * avg) * S;
+    const int nf = nonfinite_of(S, avg);
+    out[k].sumsq = sumsq;
+    out[k].norm = sqrt(sumsq);
+    out[k].nonfinite = nf;
+    mine += S;
+    nf_mine |= nf;
+  }
+  const double S = wg_sum(mine, red);
+  const int nf_any = __syncthreads_or(nf_mine);
+  const int skip = (clip && err && nf_any) ? 1 : 0;
+  int clipped_mine = 0;
+  for (int32_t k = k0; k < T.ntensors; k += kThreads) {
+    const double sumsq = k == k0 ? sumsq0 : out[k].sumsq;
+    const int nf = k == k0 ? nf0 : out[k].nonfinite;
+    if (clip) {
+      const Decision d = decide(sumsq, nf, max_norm, avg, err);
+      out[k].scale = (skip || d.s == 1.0) ? 1.0 : d.s;
+      out[k].clipped = d.clipped;
+      clipped_mine |= d.clipped;
+    } else {
+      out[k].scale = 1.0;
+      out[k].clipped = 0;
+    }
+  }
+  const int clipped_any = __syncthreads_or(clipped_mine);
+  // the partials have all been read: overwrite them with NaN, so that a
+  // partial read before it is written could only show up as a NaN norm
+  for (uint32_t i = t; i < T.npieces; i += kThreads) T.partials[i] = __builtin_nan("");
+  if (t == 0) {
+    write_norm(res, S, avg);
+    res->nonfinite = nf_any | res->nonfinite;
+    res->scale = 1.0;
+    res->clipped = clipped_any;
+    res->skipped = skip;
+    if (clip) res->max_norm = max_norm;
+    res->decided = clip ? 1 : 0;
+    res->status = 0;
+    res->handed_back = 0;
+  }
+}
+
+// Every piece multiplied by its tensor's factor (nothing written where that
+// factor is 1).  Grid: npieces.
+template <int DT, bool NTS>
+__global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const gclip_tensor_result* out) {
+  const TPiece pc = ld_table(T.pieces, blockIdx.x);
+  const double s64 = out[uniform32(pc.tensor)].scale;
+  if (s64 == 1.0) return;
+  piece_scale<DT, NTS>(T, pc, s64, (float)s64);
+}
+
+// ---------------------------------------------------------------- the last microbatch's += with the norm
+// Backprop lesson, "Accumulation across microbatches": acc += g, rounded once
+// to the storage format.  The 16-bit formats add in fp32 and round to the
+// format: fp32 has at least 2p + 2 bits for both (p = 11, 8), so the two
+// roundings agree with the format's own correctly rounded addition.  The
+// squares of the values written are summed as in the norm pass, one partial
+// per piece; k_tensor_decide then reduces them.
+template <int DT>
+__device__ __forceinline__ uint32_t add_elem(uint32_t a, uint32_t g) {
+  if constexpr (DT == GCLIP_F32) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(g));
+  } else if constexpr (DT == GCLIP_F16) {
+    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)a) + (float)__builtin_bit_cast(_Float16, (uint16_t)g);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
+  } else {
+    const float s = __uint_as_float(a << 16) + __uint_as_float(g << 16);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 add_vec(u32x4 a, u32x4 g) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (DT == GCLIP_F32) {
+      r[c] = add_elem<DT>(a[c], g[c]);
+    } else {
+      r[c] = add_elem<DT>(a[c] & 0xffffu, g[c] & 0xffffu) | (add_elem<DT>(a[c] >> 16, g[c] >> 16) << 16);
+    }
+  }
+  return r;
+}
+
+// One workgroup per piece; gdelta[t] is the byte offset from tensor t of the
+// list to tensor t of the contribution (same alignment, so the same vector
+// layout).
+template <int DT, bool NTS>
+__global__ __launch_bounds__(kThreads) void k_accum_partial(TensorPlan T, const uint64_t* gdelta) {
+  __shared__ double red[kWaves];
+  const TPiece pc = ld_table(T.pieces, blockIdx.x);
+  const uint64_t d = ld_table(gdelta, (uint64_t)uniform32(pc.tensor));
+  const uint32_t t = threadIdx.x;
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+  g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
+  const g_u32x4* gbase = reinterpret_cast<const g_u32x4*>(uniform64(pc.addr + d));
+  const uint32_t nvec = uniform32(pc.nvec);
+  for (uint32_t j = 0; j < nvec; j += kPieceGroup) {
+    u32x4 q[kUnroll], h[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      const bool ok = i < nvec;
+      q[u] = ok ? ld_vec<kNtSum>(base + i) : u32x4{0u, 0u, 0u, 0u};
+      h[u] = ok ? ld_vec<kNtSum>(gbase + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = piece_index(j, u, t);
+      const u32x4 n = add_vec<DT>(q[u], h[u]);
+      if (i < nvec) st_vec<NTS>(base + i, n);
+      acc[u] += vec_sumsq<DT>(n);
+    }
+  }
+  double s = 0.0;
+  for (uint32_t i = t; i < pc.sc_count; i += kThreads) {
+    const uint64_t a = T.sc_addr[pc.sc_begin + i];
+    const uint32_t v = add_elem<DT>(load_elem<DT>(a), load_elem<DT>(a + d));
+    store_elem<DT>(a, v);
+    s += elem_square<DT>(v);
+  }
+  const double part = wg_sum(lane_total(acc, s), red);
+  if (t == 0) T.partials[blockIdx.x] = part;
+}
+
+// ---------------------------------------------------------------- host launchers
+hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
+                              gclip_tensor_result* out, gclip_result* res, hipStream_t st) {
+  if (T.npieces > 0) {
+    const dim3 grid(T.npieces), block(kThreads);
+    switch (dtype) {
+      case GCLIP_F32: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F32>, grid, block, 0, st, T); break;
+      case GCLIP_F16: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F16>, grid, block, 0, st, T); break;
+      default: hipLaunchKernelGGL(k_tensor_partial<GCLIP_BF16>, grid, block, 0, st, T); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, max_norm, clip, err, out, res);
+  return hipGetLastError();
+}
+
+template <bool NTS>
+const void* tensor_scale_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_tensor_scale<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_tensor_scale<GCLIP_F16, NTS>
+                              : (const void*)k_tensor_scale<GCLIP_BF16, NTS>;
+}
+
+hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st) {
+  if (T.npieces == 0) return hipSuccess;
+  TensorPlan tc = T;
+  void* args[] = {&tc, &out};
+  const void* fn = T.nt_store ? tensor_scale_kernel<true>(dtype) : tensor_scale_kernel<false>(dtype);
+  return hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
+}
+
+template <bool NTS>
+const void* accum_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_accum_partial<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_accum_partial<GCLIP_F16, NTS>
+                              : (const void*)k_accum_partial<GCLIP_BF16, NTS>;
+}
+
+hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
+                                  gclip_tensor_result* out, gclip_result* res, hipStream_t st) {
+  if (T.npieces > 0) {
+    TensorPlan tc = T;
+    void* args[] = {&tc, &gdelta};
+    const void* fn = T.nt_store ? accum_kernel<true>(dtype) : accum_kernel<false>(dtype);
+    const hipError_t e = hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, 0.0, 0, 0, out, res);
+  return hipGetLastError();
+}
+
+}  // namespace gclip
