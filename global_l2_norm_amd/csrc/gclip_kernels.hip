@@ -505,6 +505,10 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
     if (threadIdx.x == 0) {
       res->handed_back = (int32_t)handed;
       atomic_st(&p.sync[kHandedWord], 0u);
+      // every workgroup has left its wait for the decision: clear the
+      // release word, so that the next launch waits again whatever epoch it
+      // carries (a replayed graph carries the one it was captured with)
+      atomic_st(&p.sync[kEpochWord], 0u);
     }
   }
   if (threadIdx.x == 0) reset_pools(scale_pools(p));

@@ -32,8 +32,13 @@
  *     (NULL = the default stream).
  *   - Every function returns a gclip_status.  Argument errors are detected on
  *     the host before anything is enqueued; nothing is thrown or aborted.
- *   - The hot calls (gclip_norm, gclip_scale, gclip_clip_) only enqueue work:
- *     they allocate nothing, copy nothing to the host and never block.
+ *   - The hot calls (every call on an existing list or optimizer other than
+ *     create, destroy, info and gclip_result_read) only enqueue kernels: they
+ *     allocate nothing, copy nothing, set no memory with a fill and never
+ *     block.  Every launch leaves the list's workspace as it found it, so a
+ *     hot call may be captured into a HIP graph and the graph replayed.
+ *     Calls on one list must not overlap in time (they share its workspace):
+ *     keep them on one stream, or order the streams.
  *   - Data-dependent status (a NaN or Inf in the gradients) is asynchronous:
  *     it lands in the device result block and gclip_result_read turns it into
  *     GCLIP_ENONFINITE.
