@@ -121,6 +121,23 @@ __host__ __device__ __forceinline__ uint64_t step_addr(const DevPlan& p, Cursor&
   return a;
 }
 
+// step_addr, also giving the segment that holds vector v (for reads of a
+// second list laid out like this one, at an offset per segment).
+__host__ __device__ __forceinline__ uint64_t step_addr_seg(const DevPlan& p, Cursor& c, uint64_t b, uint64_t ve,
+                                                           uint64_t v, uint32_t& sv) {
+  const uint64_t last = (b + kThreads < ve ? b + kThreads : ve) - 1;
+  uint64_t a = c.addr + (v - c.beg) * kVecBytes;
+  sv = c.s;
+  while (last >= c.end) {
+    cursor_load(p, c, c.s + 1);
+    if (v >= c.beg) {
+      a = c.addr + (v - c.beg) * kVecBytes;
+      sv = c.s;
+    }
+  }
+  return a;
+}
+
 // A uniform 64-bit value held in scalar registers (the compiler cannot always
 // prove that cursor fields loaded with vector loads are uniform).
 __host__ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {

@@ -438,8 +438,8 @@ __device__ __forceinline__ bool arrive(const DevPlan& p, int* flag) {
 
 // Blocks handed back by the fused kernel.  Worker w's state word is kHeld
 // while w holds its block (or has written it), kHanded once w has stopped
-// waiting at the decision and left its block unscaled in memory, kTaken once
-// another workgroup has taken it over.  Line 0's kHandedWord counts the
+// waiting at the decision and left its block -- and its first scale chunk --
+// unscaled in memory, kTaken once another workgroup has taken it over.  Line 0's kHandedWord counts the
 // hand-backs.
 constexpr uint32_t kHeld = 0u, kHanded = 2u, kTaken = 3u;
 
@@ -449,7 +449,9 @@ struct HandSlots {
 };
 
 // Take over every block handed back so far and scale it from memory, with
-// the worker's single elements (whole workgroup).
+// the worker's single elements and its own first scale chunk of the
+// streamed region (chunk w is taken by workgroup w without a claim, so no
+// other workgroup scales it) -- the whole workgroup.
 template <int DT>
 __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, float s32) {
   for (uint32_t base = 0; base < (uint32_t)p.nworkers; base += kThreads) {
@@ -473,6 +475,12 @@ __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& 
         scale_steps<DT>(p, cur, r.b, r.e, 0, range_steps(r), s64, s32);
       }
       scale_scalars<DT>(p, v, s64, s32);
+      if ((uint32_t)v < p.nchs) {
+        const Range c = tab_chunk_range(p.fus_vb, p.fus_seg, (uint32_t)v);
+        Cursor cur;
+        cursor_load(p, cur, c.seg);
+        scale_steps<DT>(p, cur, c.b, c.e, 0, range_steps(c), s64, s32);
+      }
     }
     __syncthreads();
   }

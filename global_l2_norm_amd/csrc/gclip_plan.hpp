@@ -136,6 +136,14 @@ struct AvgSrc {
   const float* scale;
 };
 
+// A microbatch's contribution laid out like a list: the contribution to
+// vector v of segment s is at (address of v) + seg_gdelta[s], the one to
+// single element i at sc_addr[i] + sc_gdelta[i].
+struct AccSrc {
+  const uint64_t* seg_gdelta;  // nseg
+  const uint64_t* sc_gdelta;   // nsc
+};
+
 // ---------------------------------------------------------------- AdamW on the clipped gradient
 // One piece of the optimizer's work: elements [0, count) of one tensor in the
 // four parallel lists, from the given addresses.  vec != 0 when the weights

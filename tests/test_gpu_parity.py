@@ -491,6 +491,22 @@ def test_handed_back_blocks_give_the_same_bits(dtype):
     gu.assert_elems_close(out, ref, dtype, f"hand-back {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_handed_back_with_a_streamed_region(dtype):
+    """A list larger than what the fused kernel keeps on chip: besides the
+    blocks, every worker that hands back leaves its own first scale chunk of
+    the streamed region to whoever takes the block over."""
+    rng = np.random.default_rng(34)
+    n_total = 60_000_000 if dtype == "f32" else 120_000_000
+    sizes = [n_total // 2 + 7, n_total // 4 + 3, n_total - n_total // 2 - n_total // 4 - 10]
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-3, dtype) for n in sizes]
+    [(st, r)], out = _clip_with_wait(arrays, dtype, 1.0, 0)
+    assert st == 0 and r["status"] == 0 and r["handed_back"] >= 1, r
+    _, r_split, out_split = gpu_clip(arrays, dtype, 1.0, path="split")
+    assert r["sumsq"] == r_split["sumsq"] and r["scale"] == r_split["scale"] and r["clipped"]
+    gu.assert_bitwise_equal(out, out_split, f"hand-back with streamed region {dtype} vs split")
+
+
 def test_hand_back_then_normal_wait_on_one_list():
     """The block states are cleared after a launch with hand-backs: the next
     calls on the same list (no wait, then the default wait) each scale
