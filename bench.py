@@ -324,6 +324,7 @@ def bench_adamw(a, G, g, grads, pristine, flush, gl):
                                "eps 1e-8, wd 0.1, step 1", "name": a.config, "path": "norm + adamw",
                    "launches_per_step": 2, "algorithmic_bytes_per_step": alg},
         "pct_hbm_peak": round(100.0 * alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "three_kernels_ms_per_step": round(three_ms, 5),
         "separate_ms_per_step": round(sep_ms, 5),
         "separate_algorithmic_bytes": 3 * n * esize + adam_bytes,
         "saved_vs_separate": round(1.0 - step_ms / sep_ms, 4),
@@ -404,14 +405,16 @@ def bench_amp(a, G, g, grads, pristine, flush, gl):
 
 
 def bench_accum(a, G, gs):
-    """The last microbatch's += fused with the norm pass, then the scale pass
-    (gclip_accumulate_clip_: three kernels), on the four-microbatch ANDREA-
-    120M fp32 list: the buffer holds ((c0 + c1) + c2), the contribution is c3,
-    a = 1/4, max_norm 1.0 (the average has norm ~4.8, so every step clips).
-    Against the separate form: torch's += (torch._foreach_add_) and then
-    gclip_clip_.  The buffer is restored and the caches flushed before every
-    step; each step and the accumulate kernel alone are timed with HIP
-    events."""
+    """The last microbatch's += fused with the clip (gclip_accumulate_clip_:
+    one launch on the fused path, which keeps each worker's block of sums on
+    chip across the decision), on the four-microbatch ANDREA-120M fp32 list:
+    the buffer holds ((c0 + c1) + c2), the contribution is c3, a = 1/4,
+    max_norm 1.0 (the average has norm ~4.8, so every step clips).  Also
+    timed: the same call on the split path (the += with the norm, the
+    per-tensor reduction, the scale pass), the += with the norm alone, and the
+    separate form -- torch's += (torch._foreach_add_) then gclip_clip_.  The
+    buffer is restored and the caches flushed before every step; every step
+    is timed with HIP events."""
     import torch
     buf, last = gs.andrea120m_f32_accum4_parts()
     acc = upload(buf.arrays, "f32")
@@ -433,7 +436,7 @@ def bench_accum(a, G, gs):
     def run(which, ev):
         restore()
         ev[0].record(stream)
-        if which == "fused":
+        if which in ("fused", "three_kernels"):
             gl.accumulate_clip_(c, max_norm, avg)
         elif which == "norm_only":
             gl.accumulate_norm(c, avg)
@@ -443,7 +446,8 @@ def bench_accum(a, G, gs):
         ev[1].record(stream)
 
     times = {}
-    for which in ("fused", "norm_only", "separate"):
+    for which in ("fused", "norm_only", "three_kernels", "separate"):
+        gl.set_path(G.GCLIP_PATH_SPLIT if which == "three_kernels" else G.GCLIP_PATH_AUTO)
         for _ in range(a.warmup):
             run(which, [torch.cuda.Event(enable_timing=True) for _ in range(2)])
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
@@ -457,6 +461,7 @@ def bench_accum(a, G, gs):
     gl.close()
     ms = statistics.fmean(times["fused"])
     acc_ms = statistics.fmean(times["norm_only"])
+    three_ms = statistics.fmean(times["three_kernels"])
     sep_ms = statistics.fmean(times["separate"])
     alg = 5 * n * 4  # += reads the buffer and c3, writes the buffer; the scale pass reads and writes it
     acc_alg = 3 * n * 4
@@ -468,7 +473,8 @@ def bench_accum(a, G, gs):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": WORKLOADS["andrea120m_f32"].replace(", N(0,1e-3^2), max_norm 1.0", "") +
                    "; buffer ((c0+c1)+c2) and contribution c3, each N(0,1e-3^2), a = 1/4, max_norm 1.0",
-                   "name": "andrea120m_f32_accum4", "launches_per_step": 3, "algorithmic_bytes_per_step": alg,
+                   "name": "andrea120m_f32_accum4", "path": "fused", "launches_per_step": 1,
+                   "algorithmic_bytes_per_step": alg,
                    "clipped": bool(r["clipped"]), "norm": r["norm"]},
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "accumulate_norm_ms": round(acc_ms, 5),
@@ -476,6 +482,8 @@ def bench_accum(a, G, gs):
         "separate_ms_per_step": round(sep_ms, 5),
         "separate_note": "torch._foreach_add_ then gclip_clip_ (fused kernel)",
         "saved_vs_separate": round(1.0 - ms / sep_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_accum_clip_fused"},
         "status": st,
     }
     print(json.dumps(out), flush=True)

@@ -119,7 +119,8 @@ def gclip_plan_query(addrs, numels, dtype, n_workers, worker_threads):
 
 def gclip_plan_trace(addrs, numels, dtype, n_workers, mode):
     """(addresses, workers) numpy arrays of every lane access a kernel would
-    make (mode 0 norm, 1 scale, 2/3 fused first/second pass); no GPU involved."""
+    make (mode 0 norm, 1 scale, 2/3 fused first/second pass, 4 per-tensor pieces, 5/6 contribution reads of
+    the fused kernel with the +=, first pass / a block handed back); no GPU involved."""
     import numpy as np
     n = len(addrs)
     a = (ctypes.c_uint64 * max(n, 1))(*addrs)

@@ -39,6 +39,8 @@ hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, do
 hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st);
 hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
                                   gclip_tensor_result* out, gclip_result* res, hipStream_t st);
+hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, double max_norm, AvgSrc avg,
+                              int err, gclip_result* res, uint32_t epoch, uint64_t wait_ticks, hipStream_t st);
 }  // namespace gclip
 
 // How long a workgroup of the fused kernel waits at the grid-wide decision
@@ -67,7 +69,9 @@ struct gclip_list {
 
 struct gclip_contrib {
   const gclip_list* list = nullptr;
-  uint64_t* delta = nullptr;  // device: n_tensors byte offsets, contribution minus list tensor
+  uint64_t* delta = nullptr;  // device: n_tensors byte offsets, contribution minus list tensor, then the same
+                              // offset per segment and per single element of the list's plan
+  gclip::AccSrc acc{};        // the per-segment and per-single-element tables
   int device = 0;
 };
 
@@ -497,19 +501,27 @@ gclip_status gclip_contrib_create(const gclip_list* list, void* const* d_contrib
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
     if (dev != list->device) return GCLIP_EINVAL;
+    // the same offsets per segment and per single element, for the fused kernel
+    const gclip::HostPlan& P = list->plan;
+    const size_t nseg = (size_t)P.nseg(), nsc = (size_t)P.nsc();
+    for (size_t k = 0; k < nseg; ++k) delta.push_back(delta[(size_t)P.seg_tensor[k]]);
+    for (size_t k = 0; k < nsc; ++k) delta.push_back(delta[(size_t)P.sc_tensor[k]]);
     gclip_contrib* C = new gclip_contrib();
     C->list = list;
     C->device = dev;
-    if ((e = hipMalloc(&C->delta, (n ? n : 1) * 8)) != hipSuccess) {
+    if ((e = hipMalloc(&C->delta, (delta.empty() ? 1 : delta.size()) * 8)) != hipSuccess) {
       delete C;
       g_last_hip = (int32_t)e;
       return GCLIP_ENOMEM;
     }
-    if (n && (e = hipMemcpy(C->delta, delta.data(), n * 8, hipMemcpyHostToDevice)) != hipSuccess) {
+    if (!delta.empty() &&
+        (e = hipMemcpy(C->delta, delta.data(), delta.size() * 8, hipMemcpyHostToDevice)) != hipSuccess) {
       (void)hipFree(C->delta);
       delete C;
       return hip_fail(e);
     }
+    C->acc.seg_gdelta = C->delta + n;
+    C->acc.sc_gdelta = C->delta + n + nseg;
     *out = C;
     return GCLIP_OK;
   } catch (const std::bad_alloc&) {
@@ -548,10 +560,17 @@ gclip_status gclip_accumulate_clip_(gclip_list* list, const gclip_contrib* contr
   if (st != GCLIP_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const gclip::AvgSrc avg{avg_factor, nullptr};
-  hipError_t e = gclip::launch_accumulate_norm(list->tdev, list->plan.dtype, contrib->delta, avg, list->tscratch,
-                                               d_result, s);
-  if (e == hipSuccess)
-    e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg, error_if_nonfinite ? 1 : 0, d_result, s);
+  const int err = error_if_nonfinite ? 1 : 0;
+  hipError_t e;
+  if (list->path == GCLIP_PATH_FUSED) {
+    if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
+    e = gclip::launch_accum_fused(list->dev, contrib->acc, list->plan.dtype, max_norm, avg, err, d_result,
+                                  list->epoch, list->wait_ticks, s);
+  } else {
+    e = gclip::launch_accumulate_norm(list->tdev, list->plan.dtype, contrib->delta, avg, list->tscratch, d_result,
+                                      s);
+    if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg, err, d_result, s);
+  }
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 

@@ -184,6 +184,37 @@ __device__ __forceinline__ double lane_total(const double (&acc)[kUnroll], doubl
   return t + accs;
 }
 
+// acc + g rounded once to the storage format (the last microbatch's +=).
+// The 16-bit formats add in fp32 and round to the format: fp32 has at least
+// 2p + 2 bits for both (p = 11, 8), so the two roundings agree with the
+// format's own correctly rounded addition.
+template <int DT>
+__device__ __forceinline__ uint32_t add_elem(uint32_t a, uint32_t g) {
+  if constexpr (DT == GCLIP_F32) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(g));
+  } else if constexpr (DT == GCLIP_F16) {
+    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)a) + (float)__builtin_bit_cast(_Float16, (uint16_t)g);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
+  } else {
+    const float s = __uint_as_float(a << 16) + __uint_as_float(g << 16);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 add_vec(u32x4 a, u32x4 g) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (DT == GCLIP_F32) {
+      r[c] = add_elem<DT>(a[c], g[c]);
+    } else {
+      r[c] = add_elem<DT>(a[c] & 0xffffu, g[c] & 0xffffu) | (add_elem<DT>(a[c] >> 16, g[c] >> 16) << 16);
+    }
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- agent-scope atomics
 // Cross-workgroup data (partials, the decision, the counters) is written and
 // read only with agent-scope atomics, which go to the device-coherent level

@@ -165,6 +165,80 @@ __device__ __forceinline__ void scale_scalars(const DevPlan& p, int w, double s6
   }
 }
 
+// ---------------------------------------------------------------- the last += in the same launch
+// Backprop lesson, "Accumulation across microbatches": with a contribution
+// (AccSrc), every vector of the list is read together with the contribution
+// laid out like it, and the sum acc + g (add_vec) takes the vector's place.
+
+// The contribution's vectors for one group (the walk of load_group, on the
+// caller's own cursor): at the list's addresses plus the offset of the
+// segment that holds each vector.
+template <bool NT>
+__device__ __forceinline__ void load_group_contrib(const DevPlan& p, const AccSrc& A, Cursor& cur, uint64_t vb,
+                                                   uint64_t ve, uint64_t j, uint64_t j1, u32x4 (&h)[kUnroll]) {
+  const uint32_t t = threadIdx.x;
+  uint64_t base = 0;
+  const int kind = group_kind(cur, vb, ve, j, j1, base);
+  if (kind != kGroupCross) {
+    const uint64_t d = ld_table(A.seg_gdelta, (uint64_t)uniform32(cur.s));
+    const g_u32x4* g = reinterpret_cast<const g_u32x4*>(uniform64(base + d));
+    if (kind == kGroupFull) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) h[u] = ld_vec<NT>(&g[u * kThreads + t]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        h[u] = tail_ok(vb, ve, j, j1, u, t) ? ld_vec<NT>(&g[u * kThreads + t]) : u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
+    const uint64_t b0 = vb + j * kThreads;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      h[u] = u32x4{0u, 0u, 0u, 0u};
+      if (j + u < j1) {
+        const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
+        uint32_t sv = 0;
+        const uint64_t a = step_addr_seg(p, cur, b, ve, v, sv);
+        if (v < ve) h[u] = load_vec<NT>(a + A.seg_gdelta[sv]);
+      }
+    }
+  }
+}
+
+// Worker w's single elements: acc + g written back; returns the sum of the
+// new values' squares.
+template <int DT>
+__device__ __forceinline__ double accum_scalars(const DevPlan& p, const AccSrc& A, int w) {
+  double s = 0.0;
+  const uint64_t b = ld_table(p.wk_scbegin, (uint64_t)w), e = ld_table(p.wk_scbegin, (uint64_t)w + 1);
+  for (uint64_t i = b + threadIdx.x; i < e; i += kThreads) {
+    const uint64_t a = p.sc_addr[i];
+    const uint32_t v = add_elem<DT>(load_elem<DT>(a), load_elem<DT>(a + A.sc_gdelta[i]));
+    store_elem<DT>(a, v);
+    s += elem_square<DT>(v);
+  }
+  return s;
+}
+
+// Steps [j0, j1) of the run [vb, ve): acc + g, times s when `scale`, written
+// back (a block handed back before it was written).
+template <int DT>
+__device__ __forceinline__ void accum_scale_steps(const DevPlan& p, const AccSrc& A, Cursor& cur, uint64_t vb,
+                                                  uint64_t ve, uint64_t j0, uint64_t j1, double s64, float s32,
+                                                  bool scale) {
+  Cursor cg = cur;
+  for (uint64_t j = j0; j < j1; j += kUnroll) {
+    u32x4 q[kUnroll], h[kUnroll];
+    Cursor cs = cur;
+    load_group<kNtScale>(p, cur, vb, ve, j, j1, q);
+    load_group_contrib<kNtScale>(p, A, cg, vb, ve, j, j1, h);
+    store_group<false>(p, cs, vb, ve, j, j1, [&](int u) {
+      const u32x4 n = add_vec<DT>(q[u], h[u]);
+      return scale ? scale_vec<DT>(n, s64, s32) : n;
+    });
+  }
+}
+
 // ---------------------------------------------------------------- counters in the workspace
 // Words of line 0 of sync.
 constexpr int kEpochWord = 0, kSkipWord = 1, kHandedWord = 2;
@@ -400,6 +474,83 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, c
   }
 }
 
+// The sum chunks this workgroup takes, with the +=: every group is read
+// with its contribution (both one group ahead), added, written back and
+// summed, one partial per chunk and wave as in norm_chunks.
+template <int DT, bool NTS>
+__device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, ClaimSlots& sl) {
+  const uint32_t nch = p.nsum;
+  if (blockIdx.x >= nch) return;  // then no chunk is left to claim either
+  const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+  Claimer cl = make_claimer(sum_pools(p), p, nch);
+  uint32_t c = blockIdx.x, cn;
+  Cursor cur, cg;
+  u32x4 q[kUnroll], h[kUnroll];
+  {
+    uint32_t tk = 0;
+    if (t == 0) tk = claim_issue(cl);
+    const Range r = sum_chunk_range(p, c);
+    cursor_load(p, cur, r.seg);
+    cg = cur;
+    load_group<kNtSum>(p, cur, r.b, r.e, 0, range_steps(r), q);
+    load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, 0, range_steps(r), h);
+    if (t == 0) sl.claim[1] = claim_resolve(cl, tk);
+    __syncthreads();
+    cn = uniform32(sl.claim[1]);
+  }
+  for (uint32_t i = 0; c != kNone; ++i) {
+    const Range r = sum_chunk_range(p, c);
+    const uint64_t ns = range_steps(r);
+    uint32_t tk = 0;
+    if (t == 0 && cn != kNone) tk = claim_issue(cl);
+    Cursor cst;
+    cursor_load(p, cst, r.seg);
+    double acc[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+    uint64_t j = 0;
+    for (; j + kUnroll < ns; j += kUnroll) {
+      u32x4 q2[kUnroll], h2[kUnroll];
+      load_group<kNtSum>(p, cur, r.b, r.e, j + kUnroll, ns, q2);
+      load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, j + kUnroll, ns, h2);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q[u] = add_vec<DT>(q[u], h[u]);
+      store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return q[u]; });
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        q[u] = q2[u];
+        h[u] = h2[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = add_vec<DT>(q[u], h[u]);
+    store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return q[u]; });
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
+    const uint32_t par = i & 1u;
+    if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(cl, tk) : kNone;
+    Cursor curn, cgn;
+    if (cn != kNone) {
+      const Range rn = sum_chunk_range(p, cn);
+      cursor_load(p, curn, rn.seg);
+      cgn = curn;
+      load_group<kNtSum>(p, curn, rn.b, rn.e, 0, range_steps(rn), q);
+      load_group_contrib<kNtSum>(p, A, cgn, rn.b, rn.e, 0, range_steps(rn), h);
+    }
+    double v = lane_total(acc, 0.0);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) atomic_st(&p.partials[(size_t)c * kWaves + wave], v);
+    __syncthreads();
+    c = cn;
+    cn = uniform32(sl.claim[par]);
+    cur = curn;
+    cg = cgn;
+  }
+}
+
 // ---------------------------------------------------------------- reductions and the decision
 // Partials: one per wave per sum chunk, then one per worker.
 __device__ __forceinline__ uint32_t npartials(const DevPlan& p) {
@@ -452,8 +603,13 @@ struct HandSlots {
 // the worker's single elements and its own first scale chunk of the
 // streamed region (chunk w is taken by workgroup w without a claim, so no
 // other workgroup scales it) -- the whole workgroup.
-template <int DT>
-__device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, float s32) {
+// With the += (ACC) the block was never written: it is read with its
+// contribution, added and written -- times s only when `scale` (the sum is
+// written whatever the decision); the single elements and the chunk already
+// hold their sums, and are scaled only when `scale`.
+template <int DT, bool ACC = false>
+__device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, float s32,
+                                                   const AccSrc& A = AccSrc{}, bool scale = true) {
   for (uint32_t base = 0; base < (uint32_t)p.nworkers; base += kThreads) {
     if (threadIdx.x == 0) hs.n = 0;
     __syncthreads();
@@ -472,8 +628,13 @@ __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& 
       if (r.b < r.e) {
         Cursor cur;
         cursor_load(p, cur, r.seg);
-        scale_steps<DT>(p, cur, r.b, r.e, 0, range_steps(r), s64, s32);
+        if constexpr (ACC) {
+          accum_scale_steps<DT>(p, A, cur, r.b, r.e, 0, range_steps(r), s64, s32, scale);
+        } else {
+          scale_steps<DT>(p, cur, r.b, r.e, 0, range_steps(r), s64, s32);
+        }
       }
+      if (ACC && !scale) continue;
       scale_scalars<DT>(p, v, s64, s32);
       if ((uint32_t)v < p.nchs) {
         const Range c = tab_chunk_range(p.fus_vb, p.fus_seg, (uint32_t)v);
@@ -492,8 +653,9 @@ __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& 
 // handed back (the decision is published before the deciding workgroup
 // finishes, so it is known here), clears their states and records how many
 // workers handed their block back.
-template <int DT>
-__device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool fused, HandSlots& hs, int* flag) {
+template <int DT, bool ACC = false>
+__device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool fused, HandSlots& hs, int* flag,
+                                       const AccSrc& A = AccSrc{}) {
   __syncthreads();
   if (threadIdx.x == 0) {
     complete_stores();
@@ -506,7 +668,11 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
     if (handed != 0u) {
       const double s = atomic_ld(&p.bcast[0]);
       const uint32_t skip = atomic_ld(&p.sync[kSkipWord]);
-      if (skip == 0u && s != 1.0) take_handed_blocks<DT>(p, hs, s, (float)s);
+      if constexpr (ACC) {
+        take_handed_blocks<DT, true>(p, hs, s, (float)s, A, skip == 0u && s != 1.0);
+      } else {
+        if (skip == 0u && s != 1.0) take_handed_blocks<DT>(p, hs, s, (float)s);
+      }
       __syncthreads();
       for (uint32_t i = threadIdx.x; i < (uint32_t)p.nworkers; i += kThreads) atomic_st(&p.bstate[i], kHeld);
     }
@@ -608,6 +774,32 @@ __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSl
   scale_chunks<DT, NTS>(p, sl, p.fus_vb, p.fus_seg, p.nchs, s64, s32);
 }
 
+// With the += (ACC): the block's sums, scaled when `scale`, and -- only then
+// -- the scale chunks of the streamed region (which hold sums already).
+template <int DT, bool NTS>
+__device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& sl, const Range& r,
+                                                 const BlockSplit& bs, const u32x4 (&keep)[kRegSteps],
+                                                 const u32x4* keep_lds, double s64, float s32, bool scale) {
+  const uint32_t t = threadIdx.x;
+  if (r.b < r.e) {
+    Cursor cur;
+    cursor_load(p, cur, r.seg);
+#pragma unroll
+    for (int g = 0; g < kRegSteps / kUnroll; ++g) {
+      if ((uint32_t)(g * kUnroll) < bs.nreg)
+        store_group<NTS>(p, cur, r.b, r.e, g * kUnroll, bs.nreg, [&](int u) {
+          return scale ? scale_vec<DT>(keep[g * kUnroll + u], s64, s32) : keep[g * kUnroll + u];
+        });
+    }
+    for (uint32_t k0 = 0; k0 < bs.nlds; k0 += kUnroll)
+      store_group<NTS>(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps, [&](int u) {
+        const u32x4 n = keep_lds[(k0 + u) * kThreads + t];
+        return scale ? scale_vec<DT>(n, s64, s32) : n;
+      });
+  }
+  if (scale) scale_chunks<DT, NTS>(p, sl, p.fus_vb, p.fus_seg, p.nchs, s64, s32);
+}
+
 // The whole path in one launch.  Phase 1 sums the chunks of the streamed
 // region the workgroup claims, then reads its block into VGPRs and LDS; the
 // last workgroup to arrive reduces the partials and decides; phase 2 writes
@@ -618,10 +810,16 @@ __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSl
 // freeing its compute unit for the workgroups still to run, and the
 // workgroups that do see the decision -- in the end the last one to finish
 // -- scale the handed-back blocks from memory.
-template <int DT, bool NTS>
-__global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, double max_norm, AvgSrc avs, int err,
-                                                                 gclip_result* res, uint32_t epoch,
-                                                                 uint64_t wait_ticks) {
+//
+// With the last microbatch's contribution (ACC), phase 1 adds it as it reads:
+// the chunks of the streamed region are written back as sums at once, the
+// block is kept as sums on chip (its LDS steps are read first, while the
+// registers that will hold the rest are still free), and phase 2 writes the
+// block's sums -- scaled, unless the decision writes nothing, when they are
+// written as they are -- so the block is written once.
+template <int DT, bool NTS, bool ACC>
+__device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, double max_norm, AvgSrc avs, int err,
+                                           gclip_result* res, uint32_t epoch, uint64_t wait_ticks) {
   const double avg = avg_value(avs);
   __shared__ u32x4 keep_lds[kLdsSteps * kThreads];
   __shared__ double red[kWaves];
@@ -635,14 +833,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   const int w = blockIdx.x;
   const uint32_t t = threadIdx.x;
 
-  norm_chunks<DT>(p, sl);
+  if constexpr (ACC) {
+    accum_chunks<DT, NTS>(p, A, sl);
+  } else {
+    norm_chunks<DT>(p, sl);
+  }
   double acc[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
   const Range r = block_range(p, w);
   const BlockSplit bs = block_split(r);
   u32x4 keep[kRegSteps];
-  if (r.b < r.e) {
+  if (ACC && r.b < r.e) {
+    Cursor c0;
+    cursor_load(p, c0, r.seg);
+    {  // LDS steps
+      Cursor cur = c0, cg = c0;
+      for (uint32_t k0 = 0; k0 < bs.nlds; k0 += kUnroll) {
+        u32x4 q[kUnroll], h[kUnroll];
+        load_group<kNtSum>(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps, q);
+        load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, bs.nreg + k0, bs.nsteps, h);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (k0 + u < bs.nlds) {
+            const u32x4 n = add_vec<DT>(q[u], h[u]);
+            acc[u] += vec_sumsq<DT>(n);
+            keep_lds[(k0 + u) * kThreads + t] = n;
+          }
+        }
+      }
+    }
+    {  // register steps: every load of the list first, then the contribution group by group
+      Cursor cur = c0;
+#pragma unroll
+      for (int g = 0; g < kRegSteps / kUnroll; ++g) {
+        u32x4 q[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) q[u] = u32x4{0u, 0u, 0u, 0u};
+        if ((uint32_t)(g * kUnroll) < bs.nreg) load_group<kNtSum>(p, cur, r.b, r.e, g * kUnroll, bs.nreg, q);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) keep[g * kUnroll + u] = q[u];
+      }
+      Cursor cg = c0;
+#pragma unroll
+      for (int g = 0; g < kRegSteps / kUnroll; ++g) {
+        if ((uint32_t)(g * kUnroll) < bs.nreg) {
+          u32x4 h[kUnroll];
+          load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, g * kUnroll, bs.nreg, h);
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) keep[g * kUnroll + u] = add_vec<DT>(keep[g * kUnroll + u], h[u]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kRegSteps; ++k)
+        if ((uint32_t)k < bs.nreg) acc[k % kUnroll] += vec_sumsq<DT>(keep[k]);
+    }
+  } else if (!ACC && r.b < r.e) {
     Cursor cur;
     cursor_load(p, cur, r.seg);
     // register steps: issue every load first, then accumulate in step order
@@ -670,7 +916,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
       }
     }
   }
-  const double part = wg_sum(lane_total(acc, norm_scalars<DT>(p, w)), red);
+  double sc = 0.0;
+  if constexpr (ACC) {
+    sc = accum_scalars<DT>(p, A, w);
+  } else {
+    sc = norm_scalars<DT>(p, w);
+  }
+  const double part = wg_sum(lane_total(acc, sc), red);
   if (t == 0) atomic_st(worker_partial(p, w), part);
 
   // grid-wide decision: the last workgroup to arrive reduces and releases
@@ -712,15 +964,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, doub
   }
   __syncthreads();
   const double s64 = bc_s;
-  if (!gave_up && !bc_skip && s64 != 1.0) {
-    const float s32 = (float)s64;
-    write_block_and_chunks<DT, NTS>(p, sl, r, bs, keep, keep_lds, s64, s32);
-    scale_scalars<DT>(p, w, s64, s32);
-    if (t == 0) handed = (int)atomic_ld(&p.sync[kHandedWord]);
-    __syncthreads();
-    if (handed) take_handed_blocks<DT>(p, hs, s64, s32);
+  if constexpr (ACC) {
+    if (!gave_up) {
+      const bool scale = !bc_skip && s64 != 1.0;
+      const float s32 = (float)s64;
+      write_block_sums<DT, NTS>(p, sl, r, bs, keep, keep_lds, s64, s32, scale);
+      if (scale) scale_scalars<DT>(p, w, s64, s32);
+      if (t == 0) handed = (int)atomic_ld(&p.sync[kHandedWord]);
+      __syncthreads();
+      if (handed) take_handed_blocks<DT, true>(p, hs, s64, s32, A, scale);
+    }
+  } else {
+    if (!gave_up && !bc_skip && s64 != 1.0) {
+      const float s32 = (float)s64;
+      write_block_and_chunks<DT, NTS>(p, sl, r, bs, keep, keep_lds, s64, s32);
+      scale_scalars<DT>(p, w, s64, s32);
+      if (t == 0) handed = (int)atomic_ld(&p.sync[kHandedWord]);
+      __syncthreads();
+      if (handed) take_handed_blocks<DT>(p, hs, s64, s32);
+    }
   }
-  finish<DT>(p, res, true, hs, &flag);
+  finish<DT, ACC>(p, res, true, hs, &flag, A);
+}
+
+template <int DT, bool NTS>
+__global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, double max_norm, AvgSrc avs, int err,
+                                                                 gclip_result* res, uint32_t epoch,
+                                                                 uint64_t wait_ticks) {
+  clip_fused<DT, NTS, false>(p, AccSrc{nullptr, nullptr}, max_norm, avs, err, res, epoch, wait_ticks);
+}
+
+// The last microbatch's += and the clip in one launch.
+template <int DT, bool NTS>
+__global__ __launch_bounds__(kThreads, 1) void k_accum_clip_fused(DevPlan p, AccSrc A, double max_norm, AvgSrc avs,
+                                                                  int err, gclip_result* res, uint32_t epoch,
+                                                                  uint64_t wait_ticks) {
+  clip_fused<DT, NTS, true>(p, A, max_norm, avs, err, res, epoch, wait_ticks);
 }
 
 // ---------------------------------------------------------------- host launchers
@@ -768,6 +1047,22 @@ hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }
 
+template <bool NTS>
+const void* accum_fused_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_accum_clip_fused<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_accum_clip_fused<GCLIP_F16, NTS>
+                              : (const void*)k_accum_clip_fused<GCLIP_BF16, NTS>;
+}
+
+hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, double max_norm, AvgSrc avg,
+                              int err, gclip_result* res, uint32_t epoch, uint64_t wait_ticks, hipStream_t st) {
+  DevPlan pc = p;
+  AccSrc ac = A;
+  void* args[] = {&pc, &ac, &max_norm, &avg, &err, &res, &epoch, &wait_ticks};
+  const void* fn = p.nt_store ? accum_fused_kernel<true>(dtype) : accum_fused_kernel<false>(dtype);
+  return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
+}
+
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         uint32_t epoch, uint64_t wait_ticks, hipStream_t st) {
   DevPlan pc = p;
@@ -776,14 +1071,20 @@ hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }
 
-// Workgroups of the fused kernel that fit on one compute unit at once (the
-// smaller of its two store variants).
+// Workgroups of the fused kernels that fit on one compute unit at once (the
+// smallest over the store variants, with and without the +=).
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu) {
-  int a = 0, b = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, fused_kernel<false>(dtype), kThreads, 0);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fused_kernel<true>(dtype), kThreads, 0);
-  *blocks_per_cu = a < b ? a : b;
-  return e;
+  const void* fns[] = {fused_kernel<false>(dtype), fused_kernel<true>(dtype), accum_fused_kernel<false>(dtype),
+                       accum_fused_kernel<true>(dtype)};
+  int lo = 1 << 30;
+  for (const void* fn : fns) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, 0);
+    if (e != hipSuccess) return e;
+    lo = n < lo ? n : lo;
+  }
+  *blocks_per_cu = lo;
+  return hipSuccess;
 }
 
 }  // namespace gclip

@@ -241,33 +241,6 @@ __global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const g
 // roundings agree with the format's own correctly rounded addition.  The
 // squares of the values written are summed as in the norm pass, one partial
 // per piece; k_tensor_decide then reduces them.
-template <int DT>
-__device__ __forceinline__ uint32_t add_elem(uint32_t a, uint32_t g) {
-  if constexpr (DT == GCLIP_F32) {
-    return __float_as_uint(__uint_as_float(a) + __uint_as_float(g));
-  } else if constexpr (DT == GCLIP_F16) {
-    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)a) + (float)__builtin_bit_cast(_Float16, (uint16_t)g);
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
-  } else {
-    const float s = __uint_as_float(a << 16) + __uint_as_float(g << 16);
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s);
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ u32x4 add_vec(u32x4 a, u32x4 g) {
-  u32x4 r;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if constexpr (DT == GCLIP_F32) {
-      r[c] = add_elem<DT>(a[c], g[c]);
-    } else {
-      r[c] = add_elem<DT>(a[c] & 0xffffu, g[c] & 0xffffu) | (add_elem<DT>(a[c] >> 16, g[c] >> 16) << 16);
-    }
-  }
-  return r;
-}
-
 // One workgroup per piece; gdelta[t] is the byte offset from tensor t of the
 // list to tensor t of the contribution (same alignment, so the same vector
 // layout).

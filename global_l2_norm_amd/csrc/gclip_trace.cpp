@@ -72,6 +72,39 @@ void replay_group(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint6
   cur = end;
 }
 
+// The contribution's addresses for one group (load_group_contrib's walk).
+void replay_contrib_group(const DevPlan& p, const AccSrc& A, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j,
+                          uint64_t j1, int32_t w, Recorder* rec) {
+  uint64_t base = 0;
+  const int kind = group_kind(cur, vb, ve, j, j1, base);
+  if (kind != kGroupCross) {
+    const uint64_t d = A.seg_gdelta[cur.s];
+    for (uint32_t t = 0; t < (uint32_t)kThreads; ++t)
+      for (int u = 0; u < kUnroll; ++u)
+        if (kind == kGroupFull || tail_ok(vb, ve, j, j1, u, t))
+          rec->put(w, base + d + ((uint64_t)u * kThreads + t) * kVecBytes);
+    return;
+  }
+  Cursor end{};
+  const uint64_t b0 = vb + j * kThreads;
+  for (uint32_t t = 0; t < (uint32_t)kThreads; ++t) {
+    Cursor c = cur;
+    for (int u = 0; u < kUnroll; ++u) {
+      if (j + u >= j1) continue;
+      const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
+      uint32_t sv = 0;
+      const uint64_t a = step_addr_seg(p, c, b, ve, v, sv);
+      if (v < ve) rec->put(w, a + A.seg_gdelta[sv]);
+    }
+    if (t == 0) {
+      end = c;
+    } else if (c.s != end.s || c.beg != end.beg || c.end != end.end || c.addr != end.addr) {
+      rec->uniform_ok = false;
+    }
+  }
+  cur = end;
+}
+
 void replay_groups(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j0, uint64_t j1, int32_t w,
                    Recorder* rec) {
   for (uint64_t j = j0; j < j1; j += kUnroll) replay_group(p, cur, vb, ve, j, j1, w, rec);
@@ -82,7 +115,7 @@ void replay_groups(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint
 extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* numels, int32_t n_tensors,
                                          int32_t dtype, int32_t n_workers, int32_t mode, uint64_t* out_addr,
                                          int32_t* out_worker, int64_t cap, int64_t* n_out) {
-  if (!n_out || cap < 0 || (cap > 0 && (!out_addr || !out_worker)) || mode < 0 || mode > 4)
+  if (!n_out || cap < 0 || (cap > 0 && (!out_addr || !out_worker)) || mode < 0 || mode > 6)
     return GCLIP_EINVAL;
   try {
     HostPlan hp;
@@ -110,6 +143,51 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
     p.nworkers = hp.nworkers;
     p.nseg = (int32_t)hp.nseg();
     Recorder rec{out_addr, out_worker, cap};
+    if (mode == 5 || mode == 6) {
+      // a contribution at addrs[t] + D_t, D_t = 2^44 + t 2^34 (aligned like
+      // the list's tensor); the per-segment and per-element offsets as the
+      // library builds them
+      std::vector<uint64_t> dseg((size_t)hp.nseg()), dsc((size_t)hp.nsc());
+      auto off = [](int32_t t) { return (1ull << 44) + ((uint64_t)t << 34); };
+      for (size_t k = 0; k < dseg.size(); ++k) dseg[k] = off(hp.seg_tensor[k]);
+      for (size_t k = 0; k < dsc.size(); ++k) dsc[k] = off(hp.sc_tensor[k]);
+      const AccSrc A{dseg.data(), dsc.data()};
+      if (mode == 5) {  // k_accum_clip_fused, first pass: sum chunks, then each block and its single elements
+        for (uint32_t c = 0; c < p.nsum; ++c) {
+          const Range r = sum_chunk_range(p, c);
+          Cursor cg;
+          cursor_load(p, cg, r.seg);
+          for (uint64_t j = 0; j < range_steps(r); j += kUnroll)
+            replay_contrib_group(p, A, cg, r.b, r.e, j, range_steps(r), -1, &rec);
+        }
+      }
+      for (int32_t w = 0; w < p.nworkers; ++w) {
+        const Range r = block_range(p, w);
+        if (r.b < r.e) {
+          Cursor c0;
+          cursor_load(p, c0, r.seg);
+          const BlockSplit bs = block_split(r);
+          if (mode == 5) {  // LDS steps, then register steps, each from the block's start
+            Cursor cg = c0;
+            for (uint32_t k0 = 0; k0 < bs.nlds; k0 += kUnroll)
+              replay_contrib_group(p, A, cg, r.b, r.e, bs.nreg + k0, bs.nsteps, w, &rec);
+            cg = c0;
+            for (int g = 0; g < kRegSteps / kUnroll; ++g)
+              if ((uint32_t)(g * kUnroll) < bs.nreg) replay_contrib_group(p, A, cg, r.b, r.e, g * kUnroll, bs.nreg, w, &rec);
+          } else {  // a block handed back: the whole block in one walk
+            Cursor cg = c0;
+            for (uint64_t j = 0; j < bs.nsteps; j += kUnroll)
+              replay_contrib_group(p, A, cg, r.b, r.e, j, bs.nsteps, w, &rec);
+          }
+        }
+        if (mode == 5)
+          for (uint64_t i = p.wk_scbegin[w]; i < p.wk_scbegin[w + 1]; ++i)
+            rec.put(w, (p.sc_addr[i] + A.sc_gdelta[i]) | kElementTag);
+      }
+      *n_out = rec.n;
+      if (!rec.uniform_ok) return GCLIP_EINVAL;
+      return rec.n > cap ? GCLIP_ERANGE : GCLIP_OK;
+    }
     if (mode == 4) {  // k_tensor_partial and k_tensor_scale: one workgroup per piece
       TensorHostPlan tp;
       if (tensor_plan_build(hp, kTensorPieceVectors, tp) != 0) return GCLIP_EINVAL;

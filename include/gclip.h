@@ -432,7 +432,10 @@ gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int3
  *   mode 0  norm kernel, 1  scale kernel,
  *        2  fused kernel, first pass, 3  fused kernel, second pass,
  *        4  per-tensor kernels (out_worker is then the tensor a piece
- *           belongs to, not a worker)
+ *           belongs to, not a worker),
+ *        5  the contribution reads of the fused kernel with the += (first
+ *           pass), 6  those of a block handed back, for a contribution
+ *           tensor t placed at addrs[t] + 2^44 + t 2^34
  * Fills out_addr[i] (address of a 16-byte vector, or, with bit 63 set, of a
  * single element) and out_worker[i] for every lane access; accesses to
  * chunks, which any worker may claim at run time, carry worker -1.  n_out

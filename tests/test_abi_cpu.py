@@ -200,3 +200,47 @@ def test_tensor_pieces_on_andrea120m_shapes():
     ta, tw = g.gclip_plan_trace(addrs, numels, 0, 256, 4)
     check_walk(ta, addrs, numels, 4)
     _check_tensor_attribution(ta, tw, addrs, numels, 4)
+
+
+# ---------------------------------------------------------------- the += in the fused kernel
+def _contrib_addrs(addrs):
+    return [a + (1 << 44) + (t << 34) for t, a in enumerate(addrs)]
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+@pytest.mark.parametrize("seed", range(4))
+def test_fused_accumulate_reads_every_contribution_byte_once(dtype, seed):
+    """The contribution reads of the fused kernel with the += (first pass):
+    inside the contribution tensors, no overlap, every byte once -- so the
+    per-segment offsets and the per-lane segment of crossing groups are
+    right."""
+    rng = np.random.default_rng(500 + seed)
+    es = ESIZE[dtype]
+    numels = _random_numels(rng)
+    if seed >= 2:
+        numels += [3_000_001, 777_777]
+    addrs = fake_layout(rng, numels, es, misalign=bool(seed % 2))
+    nw = [1, 3, 4, 8][seed]
+    ta, tw = g.gclip_plan_trace(addrs, numels, dtype, nw, 5)
+    check_walk(ta, _contrib_addrs(addrs), numels, es)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_handed_back_block_reads_its_contribution(seed):
+    """A block handed back is read with its contribution in one walk: the
+    same vectors as the first pass read for the blocks."""
+    rng = np.random.default_rng(600 + seed)
+    numels = _random_numels(rng) + [2_000_003]
+    addrs = fake_layout(rng, numels, 4, misalign=bool(seed % 2))
+    ta6, tw6 = g.gclip_plan_trace(addrs, numels, 0, 4, 6)
+    ta5, tw5 = g.gclip_plan_trace(addrs, numels, 0, 4, 5)
+    blocks5 = np.sort(ta5[(tw5 >= 0) & ((ta5 & TAG) == 0)])
+    assert np.array_equal(np.sort(ta6), blocks5)
+
+
+def test_fused_accumulate_on_andrea120m_shapes():
+    shapes = gs.shapes_andrea120m()
+    numels = [int(np.prod(s)) for _, s in shapes]
+    addrs = fake_layout(np.random.default_rng(10), numels, 4, misalign=False)
+    ta, _ = g.gclip_plan_trace(addrs, numels, 0, 256, 5)
+    check_walk(ta, _contrib_addrs(addrs), numels, 4)

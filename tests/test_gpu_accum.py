@@ -20,6 +20,7 @@ from tests.test_gpu_parity import ragged_arrays
 pytestmark = pytest.mark.gpu
 
 DTYPES = ("f32", "f16", "bf16")
+PATHS = ("fused", "split")  # one launch, or the += with the norm then the scale pass
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,7 +59,8 @@ def odd_offsets(rng, arrays):
     return offs
 
 
-def gpu_accumulate(acc, contrib, dtype, call, max_norm=1.0, avg=1.0, err=False, offsets=None, per_tensor=False):
+def gpu_accumulate(acc, contrib, dtype, call, max_norm=1.0, avg=1.0, err=False, offsets=None, per_tensor=False,
+                   path="fused", wait_us=None):
     G = _G()
     if offsets is None:
         ta, tg = gu.upload(acc, dtype), gu.upload(contrib, dtype)
@@ -68,6 +70,9 @@ def gpu_accumulate(acc, contrib, dtype, call, max_norm=1.0, avg=1.0, err=False, 
         bg, tg = views_at(contrib, dtype, offsets)
         keep = (ba, bg)
     gl = G.GradList(ta)
+    gl.set_path(G.GCLIP_PATH_FUSED if path == "fused" else G.GCLIP_PATH_SPLIT)
+    if wait_us is not None:
+        gl.set_wait(wait_us)
     c = G.Contribution(gl, tg)
     if call == "norm":
         gl.accumulate_norm(c, avg, per_tensor=per_tensor)
@@ -82,7 +87,7 @@ def gpu_accumulate(acc, contrib, dtype, call, max_norm=1.0, avg=1.0, err=False, 
     return st, r, out, g_after, tr
 
 
-def check_accumulate(acc, contrib, dtype, max_norm=1.0, avg=1.0, err=False, offsets=None, what=""):
+def check_accumulate(acc, contrib, dtype, max_norm=1.0, avg=1.0, err=False, offsets=None, what="", path="fused"):
     # the += with the norm
     st, r, out, g_after, tr = gpu_accumulate(acc, contrib, dtype, "norm", avg=avg, offsets=offsets,
                                              per_tensor=True)
@@ -96,7 +101,9 @@ def check_accumulate(acc, contrib, dtype, max_norm=1.0, avg=1.0, err=False, offs
     for k, ps in enumerate(oracle.tensor_sumsq(ref, dtype, avg)):
         gu.assert_norm_close(float(tr[k]["sumsq"]), ps, f"{what} tensor {k}")
     # the += with the clip
-    st, r, out, g_after, _ = gpu_accumulate(acc, contrib, dtype, "clip", max_norm, avg, err, offsets)
+    st, r, out, g_after, _ = gpu_accumulate(acc, contrib, dtype, "clip", max_norm, avg, err, offsets, path=path)
+    what = f"{what} ({path})"
+    gu.assert_bitwise_equal(g_after, contrib, what + " (contribution only read)")
     ref = [a.copy() for a in acc]
     ro = oracle.accumulate_clip_(ref, contrib, dtype, max_norm, avg, err)
     summed = [a.copy() for a in acc]
@@ -121,9 +128,10 @@ def test_order_example(dtype):
     assert r["norm"] == 1.0 and not r["clipped"]
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("seed", range(4))
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_ragged_lists(dtype, seed):
+def test_ragged_lists(dtype, seed, path):
     """Tensors of 1 .. 3M elements; seeds 1 and 3 as views at odd element
     offsets (single elements at both ends of each vector run)."""
     rng = np.random.default_rng(3000 + seed)
@@ -135,12 +143,13 @@ def test_ragged_lists(dtype, seed):
     s, _ = oracle.sumsq([x.copy() for x in acc], dtype, avg)
     offsets = odd_offsets(rng, acc) if seed % 2 else None
     check_accumulate(acc, contrib, dtype, max_norm=0.5 * math.sqrt(s) + 1e-3, avg=avg, offsets=offsets,
-                     what=f"ragged {dtype} seed {seed}")
+                     what=f"ragged {dtype} seed {seed}", path=path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("err", (False, True))
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_special_values(dtype, err):
+def test_special_values(dtype, err, path):
     """Overflow to Inf, Inf - Inf, subnormals, exact cancellation, signed
     zeros, a NaN; with the stop switch the sum is still written but not
     scaled."""
@@ -155,7 +164,8 @@ def test_special_values(dtype, err):
     for k, (x, y) in enumerate(pairs):
         a[100 * k + 3], g[100 * k + 3] = x, y
     acc, contrib = [gs.to_storage(a, dtype)], [gs.to_storage(g, dtype)]
-    r, ro = check_accumulate(acc, contrib, dtype, max_norm=1.0, err=err, what=f"special {dtype} err={err}")
+    r, ro = check_accumulate(acc, contrib, dtype, max_norm=1.0, err=err, what=f"special {dtype} err={err}",
+                             path=path)
     assert r["nonfinite"] and r["skipped"] == err
 
 
@@ -248,10 +258,54 @@ def test_invalid_contributions():
     gl.close()
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("cfg", ("andrea120m_f32", "andrea120m_f16_spike"))
-def test_andrea120m(cfg):
+def test_andrea120m(cfg, path):
     """The 124-tensor list plus a second draw of it, averaged by 1/2, clipped
     at 1.0 (the fp32 sum has norm ~6.8, so it clips)."""
     g = gs.make(cfg)
     h = gs.make(cfg, seed=11)
-    check_accumulate(g.arrays, h.arrays, g.dtype, max_norm=1.0, avg=0.5, what=cfg)
+    check_accumulate(g.arrays, h.arrays, g.dtype, max_norm=1.0, avg=0.5, what=cfg, path=path)
+
+
+# ------------------------------------------------------------------ the fused kernel's hand-backs with the +=
+@pytest.mark.parametrize("dtype", ("f32", "bf16"))
+def test_handed_back_blocks_with_the_accumulate(dtype):
+    """With no wait at all nearly every workgroup hands its block back before
+    writing it; whoever takes a block over reads it with its contribution,
+    adds, scales and writes it.  A list larger than the on-chip share, so
+    that the streamed region's chunks are handed over too.  Bit for bit the
+    result of the same call with the normal wait."""
+    rng = np.random.default_rng(3400)
+    n_total = 35_000_000 if dtype == "f32" else 70_000_000
+    sizes = [n_total // 2 + 5, n_total - n_total // 2 - 5]
+    acc = [gs.to_storage(rng.standard_normal(n) * 1e-3, dtype) for n in sizes]
+    contrib = [gs.to_storage(rng.standard_normal(n) * 1e-3, dtype) for n in sizes]
+    st, r0, out0, _, _ = gpu_accumulate(acc, contrib, dtype, "clip", 1.0, 0.5, False, path="fused")
+    st, r, out, g_after, _ = gpu_accumulate(acc, contrib, dtype, "clip", 1.0, 0.5, False, path="fused", wait_us=0)
+    assert r["handed_back"] >= 1 and r0["handed_back"] == 0, (r, r0)
+    assert r["sumsq"] == r0["sumsq"] and r["scale"] == r0["scale"] and r["clipped"]
+    gu.assert_bitwise_equal(out, out0, f"hand-back with += {dtype}")
+    gu.assert_bitwise_equal(g_after, contrib, "contribution only read")
+    ref = [a.copy() for a in acc]
+    ro = oracle.accumulate_clip_(ref, contrib, dtype, 1.0, 0.5)
+    gu.assert_norm_close(r["norm"], ro["norm"], "hand-back with +=")
+    gu.assert_elems_close(out, ref, dtype, f"hand-back with += {dtype}")
+
+
+@pytest.mark.parametrize("bad", (math.nan, None))
+def test_handed_back_blocks_write_the_sum_when_nothing_is_scaled(bad):
+    """Stop switch (a NaN) or factor 1 (norm under max_norm): nothing is
+    scaled, but the += is still written, by whoever holds each block."""
+    rng = np.random.default_rng(3500)
+    sizes = [30_000_001, 4_000_000, 7]
+    acc = [gs.to_storage(rng.standard_normal(n) * 1e-4, "f32") for n in sizes]
+    contrib = [gs.to_storage(rng.standard_normal(n) * 1e-4, "f32") for n in sizes]
+    if bad is not None:
+        contrib[1][123] = np.float32(bad)
+    st, r, out, _, _ = gpu_accumulate(acc, contrib, "f32", "clip", 1e30, 1.0, True, path="fused", wait_us=0)
+    assert r["handed_back"] >= 1
+    assert r["skipped"] == (bad is not None) and r["scale"] == 1.0
+    summed = [a.copy() for a in acc]
+    oracle.accumulate_(summed, contrib, "f32")
+    gu.assert_bitwise_equal_but_nan(out, summed, "f32", "sum written, nothing scaled")
