@@ -357,8 +357,12 @@ gclip_status gclip_contrib_destroy(gclip_contrib* contrib);
 gclip_status gclip_accumulate_norm(gclip_list* list, const gclip_contrib* contrib, double avg_factor,
                                    gclip_tensor_result* d_tensors, gclip_result* d_result, void* stream);
 
-/* gclip_accumulate_norm followed by gclip_scale: the last += and the global
- * clip of a * acc.  Three kernels; no allocation, no synchronisation. */
+/* The last += and the global clip of a * acc: the sum is written whatever
+ * the decision, and scaled when the clip (and the stop switch) say so.  On
+ * the fused path one kernel, which keeps part of the sums on chip across the
+ * decision and so writes them only once; on the split path
+ * gclip_accumulate_norm followed by gclip_scale.  No allocation, no
+ * synchronisation. */
 gclip_status gclip_accumulate_clip_(gclip_list* list, const gclip_contrib* contrib, double max_norm,
                                     double avg_factor, int32_t error_if_nonfinite, gclip_result* d_result,
                                     void* stream);
