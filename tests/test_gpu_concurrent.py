@@ -1,0 +1,77 @@
+"""Two fused launches at once, on two streams, on two lists.
+
+The fused kernel is an ordinary launch: it needs one workgroup per compute
+unit resident to decide without waiting, and it gets that only when nothing
+else runs.  With two such launches in flight they take compute units from
+each other; a workgroup that waits longer than the list's bound at the
+decision hands its block back and leaves, so both launches finish, and each
+list must come out exactly as when it is clipped alone (the split path's
+bits)."""
+import numpy as np
+import pytest
+
+from synth import gradsets as gs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("the gpu tests need an MI355X")
+    import global_l2_norm_amd  # noqa: F401  (fails loudly when libgclip.so is missing)
+
+
+def _G():
+    import global_l2_norm_amd as G
+    return G
+
+
+def _alone(arrays, dtype, max_norm):
+    G = _G()
+    ts = gu.upload(arrays, dtype)
+    gl = G.GradList(ts)
+    gl.set_path(G.GCLIP_PATH_SPLIT)
+    gl.clip_(max_norm)
+    st, r = gl.read()
+    out = gu.download(ts, dtype)
+    gl.close()
+    return r, out
+
+
+@pytest.mark.parametrize("wait_us", (0, 200, 1000))
+def test_two_fused_launches_at_once(wait_us):
+    import torch
+    G = _G()
+    rng = np.random.default_rng(4300)
+    a = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in (40_000_003, 9_000_001, 5)]
+    b = [gs.to_storage(rng.standard_normal(n) * 1e-3, "bf16") for n in (50_000_001, 30_000_000, 77)]
+    ra, out_a = _alone(a, "f32", 1.0)
+    rb, out_b = _alone(b, "bf16", 1.0)
+    ta, tb = gu.upload(a, "f32"), gu.upload(b, "bf16")
+    pa, pb = [t.clone() for t in ta], [t.clone() for t in tb]
+    la, lb = G.GradList(ta), G.GradList(tb)
+    for gl in (la, lb):
+        gl.set_path(G.GCLIP_PATH_FUSED)
+        gl.set_wait(wait_us)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    handed = 0
+    for rep in range(3):
+        for t, p in zip(ta + tb, pa + pb):
+            t.copy_(p)
+        torch.cuda.synchronize()
+        la.clip_(1.0, stream=s1)
+        lb.clip_(1.0, stream=s2)
+        st1, r1 = la.read(stream=s1)
+        st2, r2 = lb.read(stream=s2)
+        assert st1 == 0 and st2 == 0 and r1["status"] == 0 and r2["status"] == 0, (rep, r1, r2)
+        handed += r1["handed_back"] + r2["handed_back"]
+        assert r1["sumsq"] == ra["sumsq"] and r1["scale"] == ra["scale"], rep
+        assert r2["sumsq"] == rb["sumsq"] and r2["scale"] == rb["scale"], rep
+        gu.assert_bitwise_equal(gu.download(ta, "f32"), out_a, f"list a, repeat {rep}")
+        gu.assert_bitwise_equal(gu.download(tb, "bf16"), out_b, f"list b, repeat {rep}")
+    print(f"wait {wait_us} us: {handed} blocks handed back over 3 repeats")
+    la.close()
+    lb.close()
