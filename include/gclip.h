@@ -52,7 +52,9 @@
 extern "C" {
 #endif
 
-#define GCLIP_VERSION 1
+/* 1: the global clip; 2: adds AdamW on the clipped gradient, loss-scaled
+ * steps, per-tensor norms and clipping, and the last microbatch's +=. */
+#define GCLIP_VERSION 2
 
 /* Storage format of every element of a list (one format per list). */
 typedef enum gclip_dtype {
