@@ -345,6 +345,10 @@ typedef struct gclip_contrib gclip_contrib;
  * tensor; allocates and synchronises (not a hot call).  GCLIP_EINVAL on a
  * NULL pointer, a misaligned address or an overlap. */
 gclip_status gclip_contrib_create(const gclip_list* list, void* const* d_contrib, gclip_contrib** out);
+
+/* Free a contribution handle's device table.  Synchronises.  NULL is a
+ * no-op.  A handle belongs to the list it was registered for: destroy it
+ * before that list. */
 gclip_status gclip_contrib_destroy(gclip_contrib* contrib);
 
 /* The last +=, fused with the norm pass: for every element of the list,
