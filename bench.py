@@ -90,6 +90,21 @@ def read_traffic(numel_bytes_alg):
         return None
 
 
+def oracle_rate(run, restore, nbytes, sample, min_seconds=6.0):
+    """The oracle timed on this host: run() repeated (restore() before each,
+    untimed) for at least min_seconds; nbytes algorithmic bytes per run."""
+    reps, total = 0, 0.0
+    while total < min_seconds or reps == 0:
+        restore()
+        t0 = time.perf_counter()
+        run()
+        total += time.perf_counter() - t0
+        reps += 1
+    sec = total / reps
+    return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}, {reps} rep(s), {sec:.2f} s each, single-threaded binary64 C"}
+
+
 def cpu_baseline(g, min_seconds=10.0):
     """The oracle as it stands, on this host, on the same workload."""
     import oracle
@@ -315,6 +330,25 @@ def bench_adamw(a, G, g, grads, pristine, flush, gl):
     sep_ms = statistics.fmean(times[False][0])
     adam_bytes = n * (esize + 3 * 4 + 3 * 4)  # read g, p, m, v; write p, m, v
     alg = n * esize + adam_bytes
+    cpu = None
+    if not a.no_cpu_baseline:
+        import numpy as np
+
+        import oracle
+        k, tot = 0, 0
+        while k < len(g.arrays) and tot + g.arrays[k].size <= 12_000_000:
+            tot += g.arrays[k].size
+            k += 1
+        k = max(k, 1)
+        rng = np.random.default_rng(12)
+        sg = [x for x in g.arrays[:k]]
+        sp = [(rng.standard_normal(x.size) * 0.02).astype(np.float32) for x in sg]
+        sm = [np.zeros(x.size, np.float32) for x in sg]
+        ns = sum(x.size for x in sg)
+        cpu = oracle_rate(lambda: oracle.clip_adamw(sp, sg, sm, [x.copy() for x in sm], g.dtype, g.max_norm,
+                                                    g.avg_factor, False, step=1, **ADAMW_HP),
+                          lambda: None, ns * esize + ns * (esize + 24),
+                          f"the first {k} tensors ({ns} elements): norm, decision, AdamW step")
     out = {
         "metric": "clip + AdamW step GB/s, ANDREA-120M-shaped fp32 weights, moments and grads",
         "value": round(alg / (step_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
@@ -332,6 +366,8 @@ def bench_adamw(a, G, g, grads, pristine, flush, gl):
                      "frac": round(adam_bytes / (adam_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "k_adamw_clip", "ms_per_launch": round(adam_ms, 5)},
     }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 
@@ -399,6 +435,16 @@ def bench_amp(a, G, g, grads, pristine, flush, gl):
         "loss_scale_overhead_ms": round(ms - plain_ms, 5),
         "state_after": {"scale": state[0], "growth_tracker": state[1], "found_inf": state[2]},
     }
+    if not a.no_cpu_baseline:
+        import oracle
+        work = [x.copy() for x in g.arrays]
+
+        def restore_cpu():
+            for w, x in zip(work, g.arrays):
+                w[...] = x
+
+        out["cpu_baseline"] = oracle_rate(lambda: oracle.clip_amp_(work, g.dtype, max_norm, n_mb, AMP_SCALE),
+                                          restore_cpu, alg, f"the whole {a.config} list, loss-scaled clip")
     print(json.dumps(out), flush=True)
     return 0
 
@@ -486,6 +532,16 @@ def bench_accum(a, G, gs):
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_accum_clip_fused"},
         "status": st,
     }
+    if not a.no_cpu_baseline:
+        import oracle
+        work = [x.copy() for x in buf.arrays]
+
+        def restore_cpu():
+            for w, x in zip(work, buf.arrays):
+                w[...] = x
+
+        out["cpu_baseline"] = oracle_rate(lambda: oracle.accumulate_clip_(work, last.arrays, "f32", max_norm, avg),
+                                          restore_cpu, alg, "the whole four-microbatch list, last += and clip")
     print(json.dumps(out), flush=True)
     return 0
 
@@ -550,6 +606,17 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
         "tensor_norms_pct_hbm_peak": round(100.0 * norm_gbps / HBM_PEAK_GBPS, 2),
         "status": st,
     }
+    if not a.no_cpu_baseline:
+        import oracle
+        work = [x.copy() for x in g.arrays]
+
+        def restore_cpu():
+            for w, x in zip(work, g.arrays):
+                w[...] = x
+
+        out["cpu_baseline"] = oracle_rate(lambda: oracle.clip_per_tensor_(work, g.dtype, PER_TENSOR_MAX_NORM,
+                                                                          g.avg_factor),
+                                          restore_cpu, alg, f"the whole {a.config} list, per-tensor clip")
     print(json.dumps(out), flush=True)
     return 0
 
