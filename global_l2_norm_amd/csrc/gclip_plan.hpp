@@ -158,7 +158,10 @@ struct AdamPiece {
 #ifndef GCLIP_ADAM_PIECE
 #define GCLIP_ADAM_PIECE 4096
 #endif
-constexpr int kAdamThreads = 256;
+#ifndef GCLIP_ADAM_THREADS
+#define GCLIP_ADAM_THREADS 256
+#endif
+constexpr int kAdamThreads = GCLIP_ADAM_THREADS;
 constexpr uint32_t kAdamPieceElems = GCLIP_ADAM_PIECE;
 
 struct AdamPlan {
