@@ -250,6 +250,20 @@ def inject_value(g: GradSet, tensor: str, index: int, value: float) -> GradSet:
     return g
 
 
+def bf16_bits(n: int, seed: int, exp_lo: int = 116, chunk: int = 1 << 27) -> np.ndarray:
+    """n bfloat16 bit patterns with a random sign, a random mantissa and a
+    biased exponent in exp_lo .. exp_lo + 3 (116: magnitudes in [2^-11,
+    2^-7)), drawn in chunks from one seeded generator (cheap for billions of
+    elements: no binary64 temporaries)."""
+    rng = np.random.default_rng([seed, 0xbf16])
+    out = np.empty(n, dtype=np.uint16)
+    for b in range(0, n, chunk):
+        r = rng.integers(0, 1 << 16, size=min(chunk, n - b), dtype=np.uint16)
+        out[b:b + r.size] = (r & np.uint16(0x807F)) | ((((r >> np.uint16(7)) & np.uint16(3)) + np.uint16(exp_lo))
+                                                       << np.uint16(7))
+    return out
+
+
 CONFIGS = {
     "tiny_f32": tiny_f32,
     "andrea120m_f32": andrea120m_f32,

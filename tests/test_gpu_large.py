@@ -1,0 +1,137 @@
+"""Maximum sizes: one tensor of more than 2^31 elements and 4 GiB, and a
+list of more than 1 GiB through the one-launch += with the clip.
+
+The 4.3 GB bf16 tensor exercises 64-bit byte offsets in every walk, the
+nontemporal-store variants (lists of 1 GiB and more), and the per-tensor
+reduction over more partials than it stages in LDS at once (~65,500
+pieces, six windows).  Outputs are compared at sampled positions (both
+ends of every tensor and one element in a thousand) with the oracle's
+rounding of g*s; the norms against the oracle's sums over every element."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gradsets as gs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+BIG = (1 << 31) + 1027
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("the gpu tests need an MI355X")
+    import global_l2_norm_amd  # noqa: F401  (fails loudly when libgclip.so is missing)
+
+
+def _G():
+    import global_l2_norm_amd as G
+    return G
+
+
+def sample_indices(n, rng, k=256, frac=1e-3):
+    idx = np.concatenate([np.arange(min(k, n)), np.arange(max(0, n - k), n),
+                          rng.integers(0, n, size=int(n * frac)) if n > 0 else np.zeros(0, dtype=np.int64)])
+    return np.unique(idx)
+
+
+def gather(t, idx, dtype):
+    """Storage bits of device tensor t at idx (only those cross to the host)."""
+    import torch
+    sel = t[torch.from_numpy(idx).to(t.device)]
+    return gu.download([sel], dtype)[0]
+
+
+def check_sampled(arrays, ts, dtype, scales, rng, what):
+    for k, (a, t, s) in enumerate(zip(arrays, ts, scales)):
+        idx = sample_indices(a.size, rng)
+        got = gather(t, idx, dtype)
+        ref = [a[idx].copy()]
+        if s != 1.0:
+            oracle.scale_(ref, dtype, s)
+        bad = gu.elem_mismatches(got, ref[0], dtype)
+        assert not bad.any(), f"{what}: tensor {k}, {int(bad.sum())} of {idx.size} sampled elements off"
+
+
+@pytest.fixture(scope="module")
+def big_list():
+    rng = np.random.default_rng(9000)
+    arrays = [gs.bf16_bits(BIG, 9001), gs.to_storage(rng.standard_normal(5) * 1e-2, "bf16"),
+              gs.to_storage(rng.standard_normal(70_001) * 1e-2, "bf16")]
+    per = oracle.tensor_sumsq(arrays, "bf16")
+    return arrays, per
+
+
+@pytest.mark.timeout(900)
+def test_over_4gib_tensor(big_list):
+    import torch
+    G = _G()
+    arrays, per = big_list
+    s_ref = float(np.sum(per))
+    n_ref = math.sqrt(s_ref)
+    ts = gu.upload(arrays, "bf16")
+    pristine = [t.clone() for t in ts]
+    gl = G.GradList(ts)
+    assert gl.info()["n_bytes"] > (1 << 32)
+    s, clipped, _ = oracle.decide(n_ref, False, 1.0)
+    assert clipped
+    for path in ("fused", "split"):
+        for t, p in zip(ts, pristine):
+            t.copy_(p)
+        gl.set_path(G.GCLIP_PATH_FUSED if path == "fused" else G.GCLIP_PATH_SPLIT)
+        gl.clip_(1.0)
+        st, r = gl.read()
+        assert st == 0 and r["status"] == 0 and r["clipped"] and not r["nonfinite"], (path, r)
+        gu.assert_norm_close(r["norm"], n_ref, f"4 GiB {path}")
+        check_sampled(arrays, ts, "bf16", [s] * 3, np.random.default_rng(5), f"4 GiB clip {path}")
+    # every tensor by its own norm: ~65,500 pieces, staged in several windows
+    for t, p in zip(ts, pristine):
+        t.copy_(p)
+    gl.clip_per_tensor_(0.05)
+    st, r = gl.read()
+    tr = gl.read_tensors()
+    scales = []
+    for k, ps in enumerate(per):
+        gu.assert_norm_close(float(tr[k]["sumsq"]), ps, f"4 GiB per-tensor sumsq {k}")
+        sk, ck, _ = oracle.decide(math.sqrt(ps), False, 0.05)
+        assert bool(tr[k]["clipped"]) == ck, k
+        scales.append(sk)
+    check_sampled(arrays, ts, "bf16", scales, np.random.default_rng(6), "4 GiB per-tensor clip")
+    gl.close()
+    del pristine
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_over_1gib_accumulate_fused():
+    """The one-launch += with the clip on a 1.2 GB fp32 list (its
+    nontemporal-store variant): the sums at sampled positions scaled by the
+    oracle's decision."""
+    import torch
+    G = _G()
+    rng = np.random.default_rng(9100)
+    sizes = [200_000_003, 100_000_001, 7]
+    acc = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in sizes]
+    contrib = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in sizes]
+    ta, tc = gu.upload(acc, "f32"), gu.upload(contrib, "f32")
+    gl = G.GradList(ta)
+    assert gl.info()["n_bytes"] >= (1 << 30)
+    c = G.Contribution(gl, tc)
+    gl.accumulate_clip_(c, 1.0, 0.5)
+    st, r = gl.read()
+    summed = [a.copy() for a in acc]
+    oracle.accumulate_(summed, contrib, "f32")
+    s_ref, nf = oracle.sumsq(summed, "f32", 0.5)
+    n_ref = math.sqrt(s_ref)
+    s, clipped, _ = oracle.decide(n_ref, nf, 1.0, 0.5)
+    assert clipped and r["clipped"] and st == 0
+    gu.assert_norm_close(r["norm"], n_ref, "1 GiB +=")
+    check_sampled(summed, ta, "f32", [s] * 3, np.random.default_rng(7), "1 GiB += with the clip")
+    c.close()
+    gl.close()
+    torch.cuda.empty_cache()
