@@ -432,11 +432,6 @@ bool tensor_out_ok(const gclip_list* list, const gclip_tensor_result* t) {
   if (list->plan.n_tensors == 0) return true;
   return t && reinterpret_cast<uintptr_t>(t) % 8 == 0;
 }
-// The one-launch += with the clip (k_accum_clip_fused).  Off until its
-// cross-workgroup release/acquire is verified on the GPU: then the split
-// path's kernels run instead.
-constexpr bool kAccumFusedEnabled = false;
-
 bool amp_state_ptr_ok(const gclip_amp_state* a) { return a && reinterpret_cast<uintptr_t>(a) % 4 == 0; }
 bool amp_params_ok(const gclip_amp_params* a) {
   return a && std::isfinite(a->growth_factor) && a->growth_factor >= 1.0 && std::isfinite(a->backoff_factor) &&
@@ -567,7 +562,7 @@ gclip_status gclip_accumulate_clip_(gclip_list* list, const gclip_contrib* contr
   const gclip::AvgSrc avg{avg_factor, nullptr};
   const int err = error_if_nonfinite ? 1 : 0;
   hipError_t e;
-  if (list->path == GCLIP_PATH_FUSED && kAccumFusedEnabled) {
+  if (list->path == GCLIP_PATH_FUSED) {
     if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
     e = gclip::launch_accum_fused(list->dev, contrib->acc, list->plan.dtype, max_norm, avg, err, d_result,
                                   list->epoch, list->wait_ticks, s);

@@ -27,7 +27,9 @@
 //     in index order, so the bits of the norm do not depend on scheduling or
 //     on which workgroup took which chunk, and both paths give the same
 //     bits; cross-workgroup data moves only through agent-scope atomics (see
-//     complete_stores);
+//     complete_stores), except in the += kernel, whose phase 2 reads sums
+//     that phase 1 wrote with plain stores on other XCDs: those pass through
+//     an agent-scope release at the arrival and an acquire at the decision;
 //   - the fused kernel keeps each worker's block (up to kRegSteps +
 //     kLdsSteps steps) in VGPRs and LDS across the grid-wide decision, so the
 //     scale pass writes those bytes without reading them again from HBM; it
@@ -259,6 +261,11 @@ __device__ __forceinline__ uint32_t* finish_tickets(const DevPlan& p) {
 // workgroup, the last to take the ticket.  The counter a workgroup completes
 // is reset by it for the next launch.  Thread 0 only; its stores must be
 // complete (complete_stores) before the call.
+// CHAIN passes plain stores along: every caller has released them
+// (release_agent) before the call, the last of each group acquires and
+// releases again before it counts in the top line, and the winner acquires,
+// so it sees every caller's stores.
+template <bool CHAIN = false>
 __device__ __forceinline__ bool take_ticket(uint32_t* lines, int32_t nworkers) {
   const uint32_t g = blockIdx.x % (uint32_t)kPools;
   const uint32_t members = ((uint32_t)nworkers - g + kPools - 1) / kPools;
@@ -267,8 +274,10 @@ __device__ __forceinline__ bool take_ticket(uint32_t* lines, int32_t nworkers) {
   uint32_t* top = lines + kPools * kSyncLineWords;
   if (atomic_add(mine, 1u) != members - 1u) return false;
   atomic_st(mine, 0u);
+  if constexpr (CHAIN) acq_rel_agent();
   if (atomic_add(top, 1u) != groups - 1u) return false;
   atomic_st(top, 0u);
+  if constexpr (CHAIN) acquire_agent();
   return true;
 }
 
@@ -577,11 +586,24 @@ __device__ __forceinline__ void poison_partials(const DevPlan& p) {
 }
 
 // Arrival after the summing pass: true in the last workgroup (all threads).
-// The caller's partials must already be stored.
+// The caller's partials must already be stored.  PUBLISH (the += kernel,
+// whose summing pass writes the sums with plain stores that other
+// workgroups read in the scaling pass): every wave completes its stores,
+// then thread 0 releases them at agent scope before its ticket; the last
+// workgroup has acquired every workgroup's stores when this returns.
+template <bool PUBLISH = false>
 __device__ __forceinline__ bool arrive(const DevPlan& p, int* flag) {
-  if (threadIdx.x == 0) {
+  if constexpr (PUBLISH) {
     complete_stores();
-    *flag = take_ticket(arrival_tickets(p), p.nworkers) ? 1 : 0;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if constexpr (PUBLISH) {
+      release_agent();
+    } else {
+      complete_stores();
+    }
+    *flag = take_ticket<PUBLISH>(arrival_tickets(p), p.nworkers) ? 1 : 0;
   }
   __syncthreads();
   return *flag != 0;
@@ -659,7 +681,11 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
   __syncthreads();
   if (threadIdx.x == 0) {
     complete_stores();
-    *flag = take_ticket(finish_tickets(p), p.nworkers) ? 1 : 0;
+    // with the +=, the last workgroup may read the sums a handed-back worker
+    // wrote before its arrival: the deciding workgroup acquired them and
+    // released them again before it published the decision and came here,
+    // so the ticket chain carries them to the last workgroup
+    *flag = take_ticket<ACC>(finish_tickets(p), p.nworkers) ? 1 : 0;
   }
   __syncthreads();
   if (*flag == 0) return;
@@ -925,9 +951,12 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   const double part = wg_sum(lane_total(acc, sc), red);
   if (t == 0) atomic_st(worker_partial(p, w), part);
 
-  // grid-wide decision: the last workgroup to arrive reduces and releases
+  // grid-wide decision: the last workgroup to arrive reduces and releases.
+  // With the +=, the sums written so far are read in phase 2 by whichever
+  // workgroup claims them, on any XCD: they are released at the arrival and
+  // acquired by every workgroup that goes on to phase 2.
   if (t == 0) gave_up = 0;
-  if (arrive(p, &flag)) {
+  if (arrive<ACC>(p, &flag)) {
     const double S = partials_sum(p, red);
     poison_partials(p);
     if (t == 0) {
@@ -941,7 +970,11 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       reset_pools(sum_pools(p));
       atomic_st(&p.bcast[0], d.s);
       atomic_st(&p.sync[kSkipWord], (uint32_t)d.skip);
-      complete_stores();
+      if constexpr (ACC) {
+        release_agent();  // passes on the sums acquired at the arrival
+      } else {
+        complete_stores();
+      }
       atomic_st(&p.sync[kEpochWord], epoch);
     }
   } else if (t == 0) {
@@ -958,6 +991,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       }
     }
     if (!gave_up) {
+      if constexpr (ACC) acquire_agent();
       bc_s = atomic_ld(&p.bcast[0]);
       bc_skip = (int)atomic_ld(&p.sync[kSkipWord]);
     }

@@ -47,7 +47,10 @@ def gather(t, idx, dtype):
     return gu.download([sel], dtype)[0]
 
 
-def check_sampled(arrays, ts, dtype, scales, rng, what):
+def check_sampled(arrays, ts, dtype, scales, rng, what, before=None):
+    """Sampled outputs of ts against arrays[k] scaled by scales[k]; on a
+    mismatch the message shows the first bad elements with the unscaled
+    value and, if given, what the tensor held before the call."""
     for k, (a, t, s) in enumerate(zip(arrays, ts, scales)):
         idx = sample_indices(a.size, rng)
         got = gather(t, idx, dtype)
@@ -55,7 +58,16 @@ def check_sampled(arrays, ts, dtype, scales, rng, what):
         if s != 1.0:
             oracle.scale_(ref, dtype, s)
         bad = gu.elem_mismatches(got, ref[0], dtype)
-        assert not bad.any(), f"{what}: tensor {k}, {int(bad.sum())} of {idx.size} sampled elements off"
+        if bad.any():
+            rows = []
+            for i in np.flatnonzero(bad)[:6]:
+                row = (f"[{int(idx[i])}] got {gu.values(got[i:i + 1], dtype)[0]!r} want "
+                       f"{gu.values(ref[0][i:i + 1], dtype)[0]!r} unscaled {gu.values(a[idx[i]:idx[i] + 1], dtype)[0]!r}")
+                if before is not None:
+                    row += f" before {gu.values(before[k][idx[i]:idx[i] + 1], dtype)[0]!r}"
+                rows.append(row)
+            raise AssertionError(f"{what}: tensor {k}, {int(bad.sum())} of {idx.size} sampled elements off: "
+                                 + "; ".join(rows))
 
 
 @pytest.fixture(scope="module")
@@ -111,7 +123,9 @@ def test_over_4gib_tensor(big_list):
 def test_over_1gib_accumulate_fused():
     """The one-launch += with the clip on a 1.2 GB fp32 list (its
     nontemporal-store variant): the sums at sampled positions scaled by the
-    oracle's decision."""
+    oracle's decision.  Its scaling pass reads sums that other workgroups,
+    on other XCDs, wrote in its summing pass: a missing release or acquire
+    between the two shows here as stale elements."""
     import torch
     G = _G()
     rng = np.random.default_rng(9100)
@@ -131,7 +145,7 @@ def test_over_1gib_accumulate_fused():
     s, clipped, _ = oracle.decide(n_ref, nf, 1.0, 0.5)
     assert clipped and r["clipped"] and st == 0
     gu.assert_norm_close(r["norm"], n_ref, "1 GiB +=")
-    check_sampled(summed, ta, "f32", [s] * 3, np.random.default_rng(7), "1 GiB += with the clip")
+    check_sampled(summed, ta, "f32", [s] * 3, np.random.default_rng(7), "1 GiB += with the clip", before=acc)
     c.close()
     gl.close()
     torch.cuda.empty_cache()
