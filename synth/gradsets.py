@@ -264,6 +264,19 @@ def bf16_bits(n: int, seed: int, exp_lo: int = 116, chunk: int = 1 << 27) -> np.
     return out
 
 
+def f16_bits(n: int, seed: int, exp_lo: int = 7, chunk: int = 1 << 27) -> np.ndarray:
+    """n IEEE binary16 bit patterns with a random sign, a random mantissa and
+    a biased exponent in exp_lo .. exp_lo + 3 (7: magnitudes in [2^-8,
+    2^-4)), drawn in chunks like bf16_bits."""
+    rng = np.random.default_rng([seed, 0xf16])
+    out = np.empty(n, dtype=np.uint16)
+    for b in range(0, n, chunk):
+        r = rng.integers(0, 1 << 16, size=min(chunk, n - b), dtype=np.uint16)
+        out[b:b + r.size] = (r & np.uint16(0x83FF)) | ((((r >> np.uint16(10)) & np.uint16(3)) + np.uint16(exp_lo))
+                                                       << np.uint16(10))
+    return out
+
+
 CONFIGS = {
     "tiny_f32": tiny_f32,
     "andrea120m_f32": andrea120m_f32,

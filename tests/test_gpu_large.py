@@ -1,5 +1,6 @@
-"""Maximum sizes: one tensor of more than 2^31 elements and 4 GiB, and a
-list of more than 1 GiB through the one-launch += with the clip.
+"""Maximum sizes: one tensor of more than 2^31 elements and 4 GiB, and
+lists of more than 1 GiB (fp32 and fp16) through the one-launch += with the
+clip.
 
 The 4.3 GB bf16 tensor exercises 64-bit byte offsets in every walk, the
 nontemporal-store variants (lists of 1 GiB and more), and the per-tensor
@@ -120,32 +121,40 @@ def test_over_4gib_tensor(big_list):
 
 
 @pytest.mark.timeout(900)
-def test_over_1gib_accumulate_fused():
-    """The one-launch += with the clip on a 1.2 GB fp32 list (its
+@pytest.mark.parametrize("dtype", ("f32", "f16"))
+def test_over_1gib_accumulate_fused(dtype):
+    """The one-launch += with the clip on a list of more than 1 GiB (its
     nontemporal-store variant): the sums at sampled positions scaled by the
     oracle's decision.  Its scaling pass reads sums that other workgroups,
     on other XCDs, wrote in its summing pass: a missing release or acquire
     between the two shows here as stale elements."""
     import torch
     G = _G()
-    rng = np.random.default_rng(9100)
-    sizes = [200_000_003, 100_000_001, 7]
-    acc = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in sizes]
-    contrib = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in sizes]
-    ta, tc = gu.upload(acc, "f32"), gu.upload(contrib, "f32")
+    if dtype == "f32":
+        rng = np.random.default_rng(9100)
+        sizes = [200_000_003, 100_000_001, 7]
+        acc = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in sizes]
+        contrib = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in sizes]
+    else:
+        sizes = [420_000_003, 130_000_001, 9]
+        acc = [gs.f16_bits(n, 9200 + k) for k, n in enumerate(sizes)]
+        contrib = [gs.f16_bits(n, 9300 + k) for k, n in enumerate(sizes)]
+    ta, tc = gu.upload(acc, dtype), gu.upload(contrib, dtype)
     gl = G.GradList(ta)
     assert gl.info()["n_bytes"] >= (1 << 30)
     c = G.Contribution(gl, tc)
     gl.accumulate_clip_(c, 1.0, 0.5)
     st, r = gl.read()
     summed = [a.copy() for a in acc]
-    oracle.accumulate_(summed, contrib, "f32")
-    s_ref, nf = oracle.sumsq(summed, "f32", 0.5)
+    oracle.accumulate_(summed, contrib, dtype)
+    s_ref, nf = oracle.sumsq(summed, dtype, 0.5)
     n_ref = math.sqrt(s_ref)
     s, clipped, _ = oracle.decide(n_ref, nf, 1.0, 0.5)
     assert clipped and r["clipped"] and st == 0
-    gu.assert_norm_close(r["norm"], n_ref, "1 GiB +=")
-    check_sampled(summed, ta, "f32", [s] * 3, np.random.default_rng(7), "1 GiB += with the clip", before=acc)
+    gu.assert_norm_close(r["norm"], n_ref, f"1 GiB += {dtype}")
+    check_sampled(summed, ta, dtype, [s] * 3, np.random.default_rng(7), f"1 GiB += with the clip, {dtype}",
+                  before=acc)
     c.close()
     gl.close()
+    del ta, tc
     torch.cuda.empty_cache()
