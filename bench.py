@@ -569,12 +569,16 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
         ev[0].record(stream)
         if which == "clip":
             gl.clip_per_tensor_(PER_TENSOR_MAX_NORM, g.avg_factor)
+        elif which == "clip_stop":
+            # with the stop switch on (no NaN/Inf here, so the same work):
+            # the reduction and decisions in a kernel of their own
+            gl.clip_per_tensor_(PER_TENSOR_MAX_NORM, g.avg_factor, True)
         else:
             gl.tensor_norms(g.avg_factor)
         ev[1].record(stream)
 
     times = {}
-    for which in ("clip", "norms"):
+    for which in ("clip", "clip_stop", "norms"):
         for _ in range(a.warmup):
             run(which, [torch.cuda.Event(enable_timing=True) for _ in range(2)])
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
@@ -601,6 +605,8 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
                    "tensors_clipped": int(sum(int(t["clipped"]) for t in tr)), "n_tensors": len(grads),
                    "elements_written": clipped_elems},
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "stop_switch_ms_per_step": round(statistics.fmean(times["clip_stop"]), 5),
+        "stop_switch_note": "error_if_nonfinite=True: partial, decide, scale (three launches)",
         "tensor_norms_ms": round(norm_ms, 5),
         "tensor_norms_gbps": round(norm_gbps, 1),
         "tensor_norms_pct_hbm_peak": round(100.0 * norm_gbps / HBM_PEAK_GBPS, 2),

@@ -23,11 +23,15 @@ __all__ = ["GclipError", "GclipResult", "GradList", "clip_grad_norm_", "gclip_li
            "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string", "gclip_version",
            "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step", "AdamWList",
            "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp", "AmpState",
-           "gclip_tensor_norms", "gclip_clip_per_tensor_", "TENSOR_RESULT_DTYPE", "gclip_contrib_create",
+           "gclip_tensor_norms", "gclip_clip_per_tensor_", "gclip_set_gather_wait", "TENSOR_RESULT_DTYPE",
+           "GCLIP_DEVICE_WAIT_TIMEOUT", "gclip_contrib_create",
            "gclip_contrib_destroy", "gclip_accumulate_norm", "gclip_accumulate_clip_", "Contribution",
            "GCLIP_F32", "GCLIP_F16", "GCLIP_BF16", "GCLIP_PATH_AUTO", "GCLIP_PATH_FUSED", "GCLIP_PATH_SPLIT"]
 
 DTYPE_CODES = {"f32": GCLIP_F32, "f16": GCLIP_F16, "bf16": GCLIP_BF16}
+
+# gclip_result.status: the per-tensor clip's gathering workgroup gave up waiting
+GCLIP_DEVICE_WAIT_TIMEOUT = 1
 
 # gclip_tensor_result, 32 bytes per tensor
 TENSOR_RESULT_DTYPE = [("sumsq", "<f8"), ("norm", "<f8"), ("scale", "<f8"), ("nonfinite", "<i4"),
@@ -179,6 +183,12 @@ def gclip_clip_per_tensor_(handle, max_norm, avg_factor, error_if_nonfinite, d_t
     _check(_lib.lib.gclip_clip_per_tensor_(handle, float(max_norm), float(avg_factor), int(bool(error_if_nonfinite)),
                                            ctypes.c_void_p(int(d_tensors)), ctypes.c_void_p(int(d_result)),
                                            ctypes.c_void_p(int(stream))), "gclip_clip_per_tensor_")
+
+
+def gclip_set_gather_wait(microseconds):
+    """Process-wide wait of the per-tensor clip's gathering workgroup
+    (negative: the default, 10 s); for tests of GCLIP_DEVICE_WAIT_TIMEOUT."""
+    _check(_lib.lib.gclip_set_gather_wait(int(microseconds)), "gclip_set_gather_wait")
 
 
 def gclip_contrib_create(handle, d_contrib):

@@ -91,6 +91,7 @@ def _declare(lib):
         "gclip_accumulate_norm": ([vp, vp, dbl, vp, vp, vp], i32),
         "gclip_accumulate_clip_": ([vp, vp, dbl, dbl, i32, vp, vp], i32),
         "gclip_clip_per_tensor_": ([vp, dbl, dbl, i32, vp, vp, vp], i32),
+        "gclip_set_gather_wait": ([i64], i32),
         "gclip_norm_amp": ([vp, dbl, vp, vp, vp], i32),
         "gclip_clip_amp_": ([vp, dbl, dbl, vp, ctypes.POINTER(GclipAmpParams), vp, vp], i32),
         "gclip_adamw_step_amp": ([vp, ctypes.POINTER(GclipAdamwHparams), dbl, dbl, vp,
@@ -131,4 +132,4 @@ EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_
            "gclip_last_hip_error", "gclip_version", "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step",
            "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp", "gclip_tensor_norms",
            "gclip_clip_per_tensor_", "gclip_contrib_create", "gclip_contrib_destroy", "gclip_accumulate_norm",
-           "gclip_accumulate_clip_")
+           "gclip_accumulate_clip_", "gclip_set_gather_wait")

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -37,6 +38,8 @@ hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, doubl
 hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
                               gclip_tensor_result* out, gclip_result* res, hipStream_t st);
 hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st);
+hipError_t launch_tensor_clip(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm,
+                              gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, hipStream_t st);
 hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
                                   gclip_tensor_result* out, gclip_result* res, hipStream_t st);
 hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, double max_norm, AvgSrc avg,
@@ -48,6 +51,10 @@ hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, 
 // arrives some tens of microseconds after the first.
 constexpr int64_t kDefaultWaitUs = 1000;
 constexpr int64_t kMaxWaitUs = 60 * 1000 * 1000;
+// How long the per-tensor clip's workgroup 0 waits for every tensor's sum
+// (GCLIP_DEVICE_WAIT_TIMEOUT past it); gclip_set_gather_wait changes it.
+constexpr int64_t kTensorGatherWaitUs = 10 * 1000 * 1000;
+std::atomic<int64_t> g_gather_wait_us{kTensorGatherWaitUs};
 
 struct gclip_list {
   gclip::HostPlan plan;
@@ -276,7 +283,8 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
                  o_sca = take(nsc * 8), o_part = take((nsum * waves + nw) * 8), o_bc = take(8),
                  o_sync = take((size_t)gclip::kSyncWords * 4), o_bst = take(nw * 4),
                  o_tpc = take(ntp * sizeof(gclip::TPiece)), o_tfi = take(ntf * 4), o_tpa = take(ntp * 8),
-                 o_tsc = take((size_t)P.n_tensors * sizeof(gclip_tensor_result));
+                 o_tsc = take((size_t)P.n_tensors * sizeof(gclip_tensor_result)),
+                 o_tsum = take((size_t)P.n_tensors * 8), o_tsy = take(128);
     if ((e = hipMalloc(&L->blob, off)) != hipSuccess) {
       delete L;
       g_last_hip = (int32_t)e;
@@ -328,8 +336,12 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     T.first = reinterpret_cast<const uint32_t*>(b + o_tfi);
     T.sc_addr = D.sc_addr;
     T.partials = reinterpret_cast<double*>(b + o_tpa);
+    T.tsum = reinterpret_cast<double*>(b + o_tsum);
+    T.tsync = reinterpret_cast<uint32_t*>(b + o_tsy);
     T.npieces = (uint32_t)ntp;
     T.ntensors = (int32_t)P.n_tensors;
+    T.nlive = 0;
+    for (size_t k = 0; k + 1 < ntf; ++k) T.nlive += L->tplan.first[k] < L->tplan.first[k + 1] ? 1u : 0u;
     T.nt_store = D.nt_store;
     L->tscratch = reinterpret_cast<gclip_tensor_result*>(b + o_tsc);
     L->addrs.assign(addrs, addrs + n_tensors);
@@ -469,10 +481,24 @@ gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double av
   gclip_status st = check_device(list);
   if (st != GCLIP_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = gclip::launch_tensor_norm(list->tdev, list->plan.dtype, gclip::AvgSrc{avg_factor, nullptr},
-                                           max_norm, 1, error_if_nonfinite ? 1 : 0, d_tensors, d_result, s);
-  if (e == hipSuccess) e = gclip::launch_tensor_scale(list->tdev, list->plan.dtype, d_tensors, s);
+  const gclip::AvgSrc avg{avg_factor, nullptr};
+  hipError_t e;
+  if (!error_if_nonfinite && list->clock_khz > 0) {
+    const uint64_t us = (uint64_t)g_gather_wait_us.load(std::memory_order_relaxed);
+    e = gclip::launch_tensor_clip(list->tdev, list->plan.dtype, avg, max_norm, d_tensors, d_result,
+                                  us * list->clock_khz / 1000, s);
+  } else {
+    e = gclip::launch_tensor_norm(list->tdev, list->plan.dtype, avg, max_norm, 1, error_if_nonfinite ? 1 : 0,
+                                  d_tensors, d_result, s);
+    if (e == hipSuccess) e = gclip::launch_tensor_scale(list->tdev, list->plan.dtype, d_tensors, s);
+  }
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
+}
+
+gclip_status gclip_set_gather_wait(int64_t microseconds) {
+  if (microseconds > kMaxWaitUs) return GCLIP_EINVAL;
+  g_gather_wait_us.store(microseconds < 0 ? kTensorGatherWaitUs : microseconds, std::memory_order_relaxed);
+  return GCLIP_OK;
 }
 
 gclip_status gclip_contrib_create(const gclip_list* list, void* const* d_contrib, gclip_contrib** out) {

@@ -203,8 +203,11 @@ struct TensorPlan {
   const uint32_t* first;
   const uint64_t* sc_addr;
   double* partials;  // one per piece
+  double* tsum;      // one per tensor: raw sums published by k_tensor_clip
+  uint32_t* tsync;   // [0]: tensors counted by k_tensor_clip (zero between calls)
   uint32_t npieces;
   int32_t ntensors;
+  uint32_t nlive;    // tensors with at least one piece
   uint32_t nt_store;
 };
 

@@ -23,6 +23,8 @@ namespace gclip {
 // every lane loading many at once, sums each tensor's pieces in piece order
 // and takes the decisions.  k_tensor_scale: one workgroup per piece.  Every
 // sum is taken in a fixed order, so the bits do not depend on scheduling.
+// Without the stop switch the clip takes two kernels instead of three
+// (k_tensor_clip below).
 
 template <int DT>
 __device__ __forceinline__ double piece_sumsq(const TensorPlan& T, const TPiece& pc) {
@@ -234,6 +236,115 @@ __global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const g
   piece_scale<DT, NTS>(T, pc, s64, (float)s64);
 }
 
+// ---------------------------------------------------------------- per-tensor clip in two kernels
+// Without the stop switch no tensor's decision depends on any other tensor,
+// so the decision needs no kernel of its own: after k_tensor_partial, every
+// workgroup of k_tensor_clip sums the partials of its own piece's tensor --
+// lane i takes pieces i, i + kThreads, ... of the tensor, then the
+// workgroup sum, the same order in every workgroup of the tensor, so they
+// agree on the bits -- decides and scales its piece.  The workgroup of a
+// tensor's first piece writes the tensor's figures and publishes its raw sum
+// with an agent-scope atomic store, then counts it (an add whose result is
+// not waited for).  Workgroup 0, after its own piece, waits until every
+// tensor with elements has been counted and writes the list's result block
+// from the sums in tensor order; then it clears the count for the next
+// call.  No other workgroup waits for anything, so the launch finishes
+// whatever the residency; workgroup 0's wait is bounded by wall-clock time
+// and, past it, the result block reports GCLIP_DEVICE_WAIT_TIMEOUT (every
+// count of the launch still arrives before the launch ends, so taking them
+// back leaves the count at zero for the next call).  The figures of tensors
+// without elements (no piece) are written by workgroup 0 before it waits.
+__device__ __forceinline__ double tensor_sum(const TensorPlan& T, uint32_t b, uint32_t e, double* red) {
+  double v = 0.0;
+  for (uint32_t i = b + threadIdx.x; i < e; i += kThreads) v += T.partials[i];
+  return wg_sum(v, red);
+}
+
+// A tensor's figures from its raw sum, as k_tensor_decide writes them
+// without the stop switch.
+__device__ __forceinline__ int tensor_figures(gclip_tensor_result* o, double S, double avg, double max_norm) {
+  const double sumsq = (avg * avg) * S;
+  const int nf = nonfinite_of(S, avg);
+  const Decision d = decide(sumsq, nf, max_norm, avg, 0);
+  o->sumsq = sumsq;
+  o->norm = sqrt(sumsq);
+  o->nonfinite = nf;
+  o->scale = d.s == 1.0 ? 1.0 : d.s;
+  o->clipped = d.clipped;
+  return d.clipped;
+}
+
+template <int DT, bool NTS>
+__global__ __launch_bounds__(kThreads) void k_tensor_clip(TensorPlan T, AvgSrc avs, double max_norm,
+                                                          gclip_tensor_result* out, gclip_result* res,
+                                                          uint64_t wait_ticks) {
+  __shared__ double red[kWaves];
+  __shared__ int in_time;
+  const double avg = avg_value(avs);
+  const uint32_t t = threadIdx.x;
+  if (blockIdx.x < T.npieces) {
+    const TPiece pc = ld_table(T.pieces, blockIdx.x);
+    const uint32_t k = uniform32(pc.tensor);
+    const uint32_t b = ld_table(T.first, (uint64_t)k), e = ld_table(T.first, (uint64_t)k + 1);
+    const double S = tensor_sum(T, b, e, red);
+    const Decision d = decide((avg * avg) * S, nonfinite_of(S, avg), max_norm, avg, 0);
+    if (blockIdx.x == b && t == 0) {
+      tensor_figures(&out[k], S, avg, max_norm);
+      atomic_st(&T.tsum[k], S);
+      complete_stores();
+      (void)atomic_add(T.tsync, 1u);
+    }
+    if (d.s != 1.0) piece_scale<DT, NTS>(T, pc, d.s, (float)d.s);
+  }
+  if (blockIdx.x != 0) return;
+  // tensors without elements have no piece: their figures, before the wait
+  for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads)
+    if (ld_table(T.first, (uint64_t)k) == ld_table(T.first, (uint64_t)k + 1)) tensor_figures(&out[k], 0.0, avg, max_norm);
+  if (t == 0) {
+    in_time = 1;
+    const uint64_t t0 = wall_clock64();
+    while (atomic_ld(T.tsync) != T.nlive) {
+      __builtin_amdgcn_s_sleep(2);
+      if (wall_clock64() - t0 > wait_ticks) {
+        in_time = 0;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (!in_time) {
+    if (t == 0) {
+      res->status = GCLIP_DEVICE_WAIT_TIMEOUT;
+      (void)atomic_add(T.tsync, 0u - T.nlive);
+    }
+    return;
+  }
+  double v = 0.0;
+  int nf_mine = 0, clipped_mine = 0;
+  for (int32_t k = (int32_t)t; k < T.ntensors; k += kThreads) {
+    const bool live = ld_table(T.first, (uint64_t)k) < ld_table(T.first, (uint64_t)k + 1);
+    const double S = live ? atomic_ld(&T.tsum[k]) : 0.0;
+    v += S;
+    nf_mine |= nonfinite_of(S, avg);
+    clipped_mine |= decide((avg * avg) * S, nonfinite_of(S, avg), max_norm, avg, 0).clipped;
+  }
+  const double S = wg_sum(v, red);
+  const int nf_any = __syncthreads_or(nf_mine);
+  const int clipped_any = __syncthreads_or(clipped_mine);
+  if (t == 0) {
+    write_norm(res, S, avg);
+    res->nonfinite = nf_any | res->nonfinite;
+    res->scale = 1.0;
+    res->clipped = clipped_any;
+    res->skipped = 0;
+    res->max_norm = max_norm;
+    res->decided = 1;
+    res->status = 0;
+    res->handed_back = 0;
+    atomic_st(T.tsync, 0u);  // every count of this launch has arrived
+  }
+}
+
 // ---------------------------------------------------------------- the last microbatch's += with the norm
 // Backprop lesson, "Accumulation across microbatches": acc += g, rounded once
 // to the storage format.  The 16-bit formats add in fp32 and round to the
@@ -314,6 +425,32 @@ hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_t
   void* args[] = {&tc, &out};
   const void* fn = T.nt_store ? tensor_scale_kernel<true>(dtype) : tensor_scale_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
+}
+
+template <bool NTS>
+const void* tensor_clip_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_tensor_clip<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_tensor_clip<GCLIP_F16, NTS>
+                              : (const void*)k_tensor_clip<GCLIP_BF16, NTS>;
+}
+
+// The per-tensor clip without the stop switch: k_tensor_partial, then
+// k_tensor_clip (one workgroup per piece; one workgroup when there is none).
+hipError_t launch_tensor_clip(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm,
+                              gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, hipStream_t st) {
+  if (T.npieces > 0) {
+    TensorPlan tc = T;
+    void* args[] = {&tc};
+    const void* fn = dtype == GCLIP_F32   ? (const void*)k_tensor_partial<GCLIP_F32>
+                     : dtype == GCLIP_F16 ? (const void*)k_tensor_partial<GCLIP_F16>
+                                          : (const void*)k_tensor_partial<GCLIP_BF16>;
+    const hipError_t e = hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  TensorPlan tc = T;
+  void* args[] = {&tc, &avg, &max_norm, &out, &res, &wait_ticks};
+  const void* fn = T.nt_store ? tensor_clip_kernel<true>(dtype) : tensor_clip_kernel<false>(dtype);
+  return hipLaunchKernel(fn, dim3(T.npieces > 0 ? T.npieces : 1u), dim3(kThreads), args, 0, st);
 }
 
 template <bool NTS>

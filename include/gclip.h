@@ -98,11 +98,21 @@ typedef struct gclip_result {
   int32_t clipped;    /* 1 when norm > max_norm (NaN > c is false) */
   int32_t skipped;    /* 1 when nothing was written because nonfinite && error_if_nonfinite */
   int32_t decided;    /* 1 once a scale pass has made its decision; 0 after gclip_norm alone */
-  int32_t status;     /* 0, or a device-side failure code */
+  int32_t status;     /* 0, or a device-side failure code (GCLIP_DEVICE_*) */
   int32_t handed_back; /* fused path: workgroups that stopped waiting at the grid-wide decision
                           (gclip_list_set_wait); their blocks were scaled from memory by others */
   int32_t reserved[2];
 } gclip_result;
+
+/* Device-side failure codes in gclip_result.status. */
+enum {
+  /* gclip_clip_per_tensor_ without the stop switch: the workgroup that
+   * gathers every tensor's sum into the result block waited more than ten
+   * seconds for them and gave up (only under an extreme device load); the
+   * tensors' figures and their scaling are complete, the list's figures in
+   * the result block are not. */
+  GCLIP_DEVICE_WAIT_TIMEOUT = 1
+};
 
 /* Summary of a list's descriptor table (gclip_list_info). */
 typedef struct gclip_list_info_t {
@@ -305,8 +315,9 @@ typedef struct gclip_tensor_result {
 /* Norms of every tensor of the list, of a*g, into d_tensors[0 .. n_tensors),
  * and the list's norm into d_result (sumsq, norm, nonfinite; decided = 0),
  * so that gclip_scale can follow to finish a global clip with per-tensor
- * figures.  Writes no gradient.  Enqueues one kernel; no allocation, no
- * synchronisation.  Errors as gclip_norm, plus GCLIP_EINVAL for a NULL or
+ * figures.  Writes no gradient.  Enqueues two kernels (partial sums per
+ * piece, then the reduction; only the second for a list with no element);
+ * no allocation, no synchronisation.  Errors as gclip_norm, plus GCLIP_EINVAL for a NULL or
  * misaligned d_tensors when the list has tensors. */
 gclip_status gclip_tensor_norms(gclip_list* list, double avg_factor, gclip_tensor_result* d_tensors,
                                 gclip_result* d_result, void* stream);
@@ -317,11 +328,23 @@ gclip_status gclip_tensor_norms(gclip_list* list, double avg_factor, gclip_tenso
  * list stops the whole update: no tensor is written and d_result->skipped is
  * set.  d_tensors receives every tensor's figures; d_result the list's sumsq,
  * norm and nonfinite, clipped = 1 when any tensor was clipped, scale = 1.0
- * (the factors are per tensor).  Two kernels on `stream`; no allocation, no
- * synchronisation.  Errors as gclip_clip_. */
+ * (the factors are per tensor).  Without error_if_nonfinite no tensor waits
+ * for another, and two kernels run on `stream` (partial sums per piece; then
+ * every piece decides for its own tensor and scales, and the list's figures
+ * are gathered in the same launch, see GCLIP_DEVICE_WAIT_TIMEOUT); with it,
+ * three (the reduction and every decision in a kernel of their own, between
+ * the two).  No allocation, no synchronisation.  Errors as gclip_clip_. */
 gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double avg_factor,
                                     int32_t error_if_nonfinite, gclip_tensor_result* d_tensors,
                                     gclip_result* d_result, void* stream);
+
+/* How long, in microseconds, gclip_clip_per_tensor_ without the stop switch
+ * lets its gathering workgroup wait for every tensor's sum before it reports
+ * GCLIP_DEVICE_WAIT_TIMEOUT: for every list of the process, from the next
+ * call on.  Default 10 s (a negative value restores it); at most 60 s, else
+ * GCLIP_EINVAL.  Meant for tests of that failure path: a short wait makes it
+ * happen without any fault. */
+gclip_status gclip_set_gather_wait(int64_t microseconds);
 
 /* ---------------------------------------------------------------------------
  * The norm pass fused into the last microbatch's +=.

@@ -97,17 +97,19 @@ def test_contrast_6_8_and_small(dtype):
 
 
 # ------------------------------------------------------------------ ragged lists
+@pytest.mark.parametrize("err", (False, True))
 @pytest.mark.parametrize("seed", range(4))
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_ragged_lists_misaligned_views(dtype, seed):
+def test_ragged_lists_misaligned_views(dtype, seed, err):
     """Tensors of 1 .. 3M elements at odd element offsets (single elements at
-    both ends of each vector run), several pieces per big tensor."""
+    both ends of each vector run), several pieces per big tensor; without the
+    stop switch (two kernels) and with it (three)."""
     rng = np.random.default_rng(2000 + seed)
     arrays = ragged_arrays(rng, dtype, big=seed >= 2)
     avg = [1.0, 0.25, 1.0, 1.0 / 3.0][seed]
     c = _threshold_off_ties(rng, arrays, dtype, avg)
     buf, views = upload_as_views(arrays, dtype, rng)
-    check_per_tensor(arrays, dtype, c, avg, views=views, what=f"ragged {dtype} seed {seed}")
+    check_per_tensor(arrays, dtype, c, avg, err=err, views=views, what=f"ragged {dtype} seed {seed} err {err}")
     import torch
     mask = torch.ones(buf.numel(), dtype=torch.bool, device="cuda")
     for v in views:
@@ -210,11 +212,116 @@ def test_invalid_arguments():
 
 
 # ------------------------------------------------------------------ full size
+@pytest.mark.parametrize("err", (False, True))
 @pytest.mark.parametrize("dtype_cfg", ("andrea120m_f32", "andrea120m_f16_spike"))
-def test_andrea120m(dtype_cfg):
+def test_andrea120m(dtype_cfg, err):
     """The 124-tensor list at c = 0.5: the big matrices are clipped, the norm
     vectors are not (their norms are ~0.03)."""
     g = gs.make(dtype_cfg)
-    r, ro, tr, out = check_per_tensor(g.arrays, g.dtype, 0.5, what=dtype_cfg)
+    r, ro, tr, out = check_per_tensor(g.arrays, g.dtype, 0.5, err=err, what=f"{dtype_cfg} err {err}")
     flags = [t["clipped"] for t in ro["tensors"]]
     assert any(flags) and not all(flags)
+
+
+# ------------------------------------------------------------------ two kernels: every piece decides for its tensor
+def _reload(ts, arrays, dtype):
+    for t, a in zip(ts, gu.upload(arrays, dtype)):
+        t.copy_(a)
+
+
+def _check_call(gl, ts, arrays, ref, ro, dtype, what, complete=True):
+    """One call's outputs against the oracle's; the list's figures too when
+    the result block is complete."""
+    st, r = gl.read()
+    tr = gl.read_tensors()
+    out = gu.download(ts, dtype)
+    if complete:
+        assert st == 0 and r["status"] == 0, (what, r)
+        gu.assert_norm_close(r["norm"], ro["norm"], what)
+        assert r["clipped"] == ro["clipped"] and r["nonfinite"] == ro["nonfinite"] and not r["skipped"], what
+    check_tensor_figures(tr, ro, what)
+    for k, (g, o, a) in enumerate(zip(out, ref, arrays)):
+        if ro["tensors"][k]["scale"] == 1.0:
+            gu.assert_bitwise_equal([g], [a], f"{what} tensor {k} (must be untouched)")
+        else:
+            gu.assert_elems_close([g], [o], dtype, f"{what} tensor {k}")
+    return st, r, tr, out
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_two_kernel_clip_many_tensors_repeated(dtype):
+    """Without the stop switch every piece sums its own tensor's partials and
+    decides; the first piece of each tensor publishes the tensor's sum and
+    workgroup 0 gathers the list's figures.  A list of 2,300 tensors (two
+    big ones, empty ones, 2,000 single elements, 300 short runs), three calls
+    in a row on one list -- the publication count must be back at zero after
+    each -- every call against the oracle, and the same bits every time."""
+    rng = np.random.default_rng(2600)
+    sizes = [1_000_003, 0] + [1] * 2000 + [0, 3_000_001] + [int(n) for n in rng.integers(2, 200, size=300)] + [0]
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-2, dtype) for n in sizes]
+    # the two big tensors' norms are ~5 and ~8.7 at a = 0.5, the others' at most ~0.1
+    c = 1.0
+    assert all(abs(math.sqrt(x) - c) > 1e-3 for x in oracle.tensor_sumsq(arrays, dtype, 0.5))
+    ref = [a.copy() for a in arrays]
+    ro = oracle.clip_per_tensor_(ref, dtype, c, 0.5, False)
+    assert any(t["clipped"] for t in ro["tensors"]) and not all(t["clipped"] for t in ro["tensors"])
+    ts = gu.upload(arrays, dtype)
+    gl = _G().GradList(ts)
+    runs = []
+    for rep in range(3):
+        _reload(ts, arrays, dtype)
+        gl.clip_per_tensor_(c, 0.5, False)
+        st, r, tr, out = _check_call(gl, ts, arrays, ref, ro, dtype, f"many tensors {dtype} call {rep}")
+        runs.append((r["sumsq"], tr.tobytes(), b"".join(o.tobytes() for o in out)))
+    assert runs[0] == runs[1] == runs[2]
+    gl.close()
+
+
+def test_gather_wait_timeout_is_reported_and_recovers():
+    """With the gathering workgroup's wait cut to nothing (a bound on the
+    kernel's own wait, set from the host) it gives up before the other
+    tensors have published: the result block says so
+    (GCLIP_DEVICE_WAIT_TIMEOUT, and gclip_result_read returns GCLIP_EDEVICE),
+    every tensor is still decided, scaled and given its figures, and later
+    calls with the normal wait are complete again (the counts of the
+    abandoned wait were taken back)."""
+    G = _G()
+    from global_l2_norm_amd import _lib
+    rng = np.random.default_rng(2700)
+    sizes = [5] + [1] * 1500 + [4_000_001] + [300] * 200 + [0]
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-2, "f32") for n in sizes]
+    c = 1.0  # clips the 4M-element tensor (norm ~20), none of the others (at most ~0.2)
+    assert all(abs(math.sqrt(x) - c) > 1e-3 for x in oracle.tensor_sumsq(arrays, "f32"))
+    ref = [a.copy() for a in arrays]
+    ro = oracle.clip_per_tensor_(ref, "f32", c)
+    assert any(t["clipped"] for t in ro["tensors"]) and not all(t["clipped"] for t in ro["tensors"])
+    ts = gu.upload(arrays, "f32")
+    gl = G.GradList(ts)
+    timeouts = 0
+    try:
+        G.gclip_set_gather_wait(0)
+        for rep in range(3):
+            _reload(ts, arrays, "f32")
+            gl.clip_per_tensor_(c)
+            st, r = gl.read()
+            assert r["status"] in (0, G.GCLIP_DEVICE_WAIT_TIMEOUT), r
+            if r["status"]:
+                timeouts += 1
+                assert st == _lib.GCLIP_EDEVICE
+            _check_call(gl, ts, arrays, ref, ro, "f32", f"wait 0, call {rep}", complete=r["status"] == 0)
+    finally:
+        G.gclip_set_gather_wait(-1)
+    print(f"{timeouts} of 3 calls gave up waiting")
+    assert timeouts >= 1
+    for rep in range(2):
+        _reload(ts, arrays, "f32")
+        gl.clip_per_tensor_(c)
+        _check_call(gl, ts, arrays, ref, ro, "f32", f"normal wait, call {rep}")
+    gl.close()
+
+
+def test_gather_wait_bounds():
+    G = _G()
+    with pytest.raises(G.GclipError):
+        G.gclip_set_gather_wait(61 * 1000 * 1000)
+    G.gclip_set_gather_wait(-1)
