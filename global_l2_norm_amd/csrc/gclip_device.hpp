@@ -239,27 +239,16 @@ __device__ __forceinline__ void atomic_st(double* a, double v) {
 // issued orders them for every reader of agent-scope atomics, so no
 // agent-scope fence is needed for those: on gfx950 such a fence writes back
 // and invalidates the whole L2 of the XCD, which costs ~18 us when 256
-// workgroups do it at the end of a pass.  It does not publish plain stores:
-// those stay in the L2 of the writer's XCD (each XCD has its own) until it
-// writes them back.
+// workgroups do it at the end of a pass.  It does not publish plain stores
+// to other XCDs: those stay in the L2 of the writer's XCD (each XCD has its
+// own) until it writes them back, so plain data that another workgroup reads
+// in the same launch needs the memory model's agent-scope release and
+// acquire.
 __device__ __forceinline__ void complete_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-
-// Plain stores that a workgroup on another XCD reads in the same launch (the
-// += kernel's sums) need the memory model's agent-scope release and acquire.
-// release_agent() writes back the dirty lines of this XCD's L2 (buffer_wbl2
-// on gfx950) and waits; called by one thread, it covers the whole
-// workgroup's stores only once every wave has completed them and passed a
-// barrier (__syncthreads() alone does not wait for stores).
-// acquire_agent() drops this CU's L1 and this XCD's L2 copies of lines
-// written elsewhere (buffer_inv), so the loads issued after it -- by any wave
-// of the workgroup, after a barrier -- see what was released.
-__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void acq_rel_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent"); }
 
 // ---------------------------------------------------------------- workgroup sum and the decision
 // Sum of v over the workgroup, the same bits in every thread.  Butterfly

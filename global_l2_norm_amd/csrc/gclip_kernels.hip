@@ -27,9 +27,9 @@
 //     in index order, so the bits of the norm do not depend on scheduling or
 //     on which workgroup took which chunk, and both paths give the same
 //     bits; cross-workgroup data moves only through agent-scope atomics (see
-//     complete_stores), except in the += kernel, whose phase 2 reads sums
-//     that phase 1 wrote with plain stores on other XCDs: those pass through
-//     an agent-scope release at the arrival and an acquire at the decision;
+//     complete_stores); the += kernel's phase 2 rescales only the sums the
+//     same workgroup wrote in phase 1, except when a block is handed back,
+//     which passes them on with an agent-scope release and acquire;
 //   - the fused kernel keeps each worker's block (up to kRegSteps +
 //     kLdsSteps steps) in VGPRs and LDS across the grid-wide decision, so the
 //     scale pass writes those bytes without reading them again from HBM; it
@@ -261,11 +261,6 @@ __device__ __forceinline__ uint32_t* finish_tickets(const DevPlan& p) {
 // workgroup, the last to take the ticket.  The counter a workgroup completes
 // is reset by it for the next launch.  Thread 0 only; its stores must be
 // complete (complete_stores) before the call.
-// CHAIN passes plain stores along: every caller has released them
-// (release_agent) before the call, the last of each group acquires and
-// releases again before it counts in the top line, and the winner acquires,
-// so it sees every caller's stores.
-template <bool CHAIN = false>
 __device__ __forceinline__ bool take_ticket(uint32_t* lines, int32_t nworkers) {
   const uint32_t g = blockIdx.x % (uint32_t)kPools;
   const uint32_t members = ((uint32_t)nworkers - g + kPools - 1) / kPools;
@@ -274,10 +269,8 @@ __device__ __forceinline__ bool take_ticket(uint32_t* lines, int32_t nworkers) {
   uint32_t* top = lines + kPools * kSyncLineWords;
   if (atomic_add(mine, 1u) != members - 1u) return false;
   atomic_st(mine, 0u);
-  if constexpr (CHAIN) acq_rel_agent();
   if (atomic_add(top, 1u) != groups - 1u) return false;
   atomic_st(top, 0u);
-  if constexpr (CHAIN) acquire_agent();
   return true;
 }
 
@@ -586,24 +579,11 @@ __device__ __forceinline__ void poison_partials(const DevPlan& p) {
 }
 
 // Arrival after the summing pass: true in the last workgroup (all threads).
-// The caller's partials must already be stored.  PUBLISH (the += kernel,
-// whose summing pass writes the sums with plain stores that other
-// workgroups read in the scaling pass): every wave completes its stores,
-// then thread 0 releases them at agent scope before its ticket; the last
-// workgroup has acquired every workgroup's stores when this returns.
-template <bool PUBLISH = false>
+// The caller's partials must already be stored.
 __device__ __forceinline__ bool arrive(const DevPlan& p, int* flag) {
-  if constexpr (PUBLISH) {
-    complete_stores();
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    if constexpr (PUBLISH) {
-      release_agent();
-    } else {
-      complete_stores();
-    }
-    *flag = take_ticket<PUBLISH>(arrival_tickets(p), p.nworkers) ? 1 : 0;
+    complete_stores();
+    *flag = take_ticket(arrival_tickets(p), p.nworkers) ? 1 : 0;
   }
   __syncthreads();
   return *flag != 0;
@@ -637,9 +617,11 @@ __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& 
     __syncthreads();
     const uint32_t i = base + threadIdx.x;
     if (i < (uint32_t)p.nworkers && atomic_ld(&p.bstate[i]) == kHanded) {
+      // with the +=, acquire: the giver released its sums with the state
+      constexpr int kTakeOrder = ACC ? __ATOMIC_ACQUIRE : __ATOMIC_RELAXED;
       uint32_t expected = kHanded;
-      if (__hip_atomic_compare_exchange_strong(&p.bstate[i], &expected, kTaken, __ATOMIC_RELAXED,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      if (__hip_atomic_compare_exchange_strong(&p.bstate[i], &expected, kTaken, kTakeOrder, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
         hs.list[atomicAdd(&hs.n, 1u)] = i;
     }
     __syncthreads();
@@ -658,8 +640,11 @@ __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& 
       }
       if (ACC && !scale) continue;
       scale_scalars<DT>(p, v, s64, s32);
-      if ((uint32_t)v < p.nchs) {
-        const Range c = tab_chunk_range(p.fus_vb, p.fus_seg, (uint32_t)v);
+      // the worker's own chunk: with the +=, the sum chunk it summed; else
+      // the first scale chunk, which it takes without a claim
+      const bool own = ACC ? (uint32_t)v < p.nsum : (uint32_t)v < p.nchs;
+      if (own) {
+        const Range c = ACC ? sum_chunk_range(p, (uint32_t)v) : tab_chunk_range(p.fus_vb, p.fus_seg, (uint32_t)v);
         Cursor cur;
         cursor_load(p, cur, c.seg);
         scale_steps<DT>(p, cur, c.b, c.e, 0, range_steps(c), s64, s32);
@@ -681,11 +666,7 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
   __syncthreads();
   if (threadIdx.x == 0) {
     complete_stores();
-    // with the +=, the last workgroup may read the sums a handed-back worker
-    // wrote before its arrival: the deciding workgroup acquired them and
-    // released them again before it published the decision and came here,
-    // so the ticket chain carries them to the last workgroup
-    *flag = take_ticket<ACC>(finish_tickets(p), p.nworkers) ? 1 : 0;
+    *flag = take_ticket(finish_tickets(p), p.nworkers) ? 1 : 0;
   }
   __syncthreads();
   if (*flag == 0) return;
@@ -779,6 +760,28 @@ __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_n
 
 // Phase 2 of the fused kernel: the block straight from VGPRs and LDS, then
 // the scale chunks of the streamed region this workgroup claims.
+// Scale one range in place, the next group's loads issued before the
+// current group is stored (the += kernel's own sum chunk).
+template <int DT, bool NTS>
+__device__ __forceinline__ void scale_range(const DevPlan& p, const Range& r, double s64, float s32) {
+  const uint64_t ns = range_steps(r);
+  if (ns == 0) return;
+  Cursor cur;
+  cursor_load(p, cur, r.seg);
+  Cursor cst = cur;
+  u32x4 q[kUnroll];
+  load_group<kNtScale>(p, cur, r.b, r.e, 0, ns, q);
+  uint64_t j = 0;
+  for (; j + kUnroll < ns; j += kUnroll) {
+    u32x4 q2[kUnroll];
+    load_group<kNtScale>(p, cur, r.b, r.e, j + kUnroll, ns, q2);
+    store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
+  }
+  store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
+}
+
 template <int DT, bool NTS>
 __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSlots& sl, const Range& r,
                                                        const BlockSplit& bs, const u32x4 (&keep)[kRegSteps],
@@ -823,7 +826,7 @@ __device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& s
         return scale ? scale_vec<DT>(n, s64, s32) : n;
       });
   }
-  if (scale) scale_chunks<DT, NTS>(p, sl, p.fus_vb, p.fus_seg, p.nchs, s64, s32);
+  if (scale && blockIdx.x < p.nsum) scale_range<DT, NTS>(p, sum_chunk_range(p, blockIdx.x), s64, s32);
 }
 
 // The whole path in one launch.  Phase 1 sums the chunks of the streamed
@@ -860,6 +863,8 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   const uint32_t t = threadIdx.x;
 
   if constexpr (ACC) {
+    static_assert(kSumChunksPerWorker == 1,
+                  "the += kernel rescales the sum chunk it summed: one sum chunk per worker, none claimed");
     accum_chunks<DT, NTS>(p, A, sl);
   } else {
     norm_chunks<DT>(p, sl);
@@ -952,11 +957,17 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   if (t == 0) atomic_st(worker_partial(p, w), part);
 
   // grid-wide decision: the last workgroup to arrive reduces and releases.
-  // With the +=, the sums written so far are read in phase 2 by whichever
-  // workgroup claims them, on any XCD: they are released at the arrival and
-  // acquired by every workgroup that goes on to phase 2.
+  // With the +=, phase 2 rescales only what this workgroup wrote in phase 1
+  // (its sum chunk and single elements), which a barrier makes visible to it;
+  // only a hand-back passes them to another workgroup, and that is done with
+  // an agent-scope release (the state word) and acquire (the taker's
+  // compare-and-swap), once every wave's stores here have completed.
+  if constexpr (ACC) {
+    complete_stores();
+    __syncthreads();
+  }
   if (t == 0) gave_up = 0;
-  if (arrive<ACC>(p, &flag)) {
+  if (arrive(p, &flag)) {
     const double S = partials_sum(p, red);
     poison_partials(p);
     if (t == 0) {
@@ -970,11 +981,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       reset_pools(sum_pools(p));
       atomic_st(&p.bcast[0], d.s);
       atomic_st(&p.sync[kSkipWord], (uint32_t)d.skip);
-      if constexpr (ACC) {
-        release_agent();  // passes on the sums acquired at the arrival
-      } else {
-        complete_stores();
-      }
+      complete_stores();
       atomic_st(&p.sync[kEpochWord], epoch);
     }
   } else if (t == 0) {
@@ -982,8 +989,13 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
     while (atomic_ld(&p.sync[kEpochWord]) != epoch) {
       __builtin_amdgcn_s_sleep(2);
       if (wall_clock64() - t0 > wait_ticks) {
-        // hand the block back: its state is visible before the count
-        atomic_st(&p.bstate[w], kHanded);
+        // hand the block back: its state is visible before the count (with
+        // the +=, released: the taker rescales this workgroup's sums)
+        if constexpr (ACC) {
+          __hip_atomic_store(&p.bstate[w], kHanded, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          atomic_st(&p.bstate[w], kHanded);
+        }
         complete_stores();
         atomic_add(&p.sync[kHandedWord], 1u);
         gave_up = 1;
@@ -991,7 +1003,6 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       }
     }
     if (!gave_up) {
-      if constexpr (ACC) acquire_agent();
       bc_s = atomic_ld(&p.bcast[0]);
       bc_skip = (int)atomic_ld(&p.sync[kSkipWord]);
     }
