@@ -1,4 +1,5 @@
-"""Two fused launches at once, on two streams, on two lists.
+"""Two fused launches at once, on two streams, on two lists; and two
+per-tensor clips at once.
 
 The fused kernel is an ordinary launch: it needs one workgroup per compute
 unit resident to decide without waiting, and it gets that only when nothing
@@ -73,5 +74,50 @@ def test_two_fused_launches_at_once(wait_us):
         gu.assert_bitwise_equal(gu.download(ta, "f32"), out_a, f"list a, repeat {rep}")
         gu.assert_bitwise_equal(gu.download(tb, "bf16"), out_b, f"list b, repeat {rep}")
     print(f"wait {wait_us} us: {handed} blocks handed back over 3 repeats")
+    la.close()
+    lb.close()
+
+
+def _per_tensor_alone(arrays, dtype, max_norm):
+    G = _G()
+    ts = gu.upload(arrays, dtype)
+    gl = G.GradList(ts)
+    gl.clip_per_tensor_(max_norm)
+    st, r = gl.read()
+    tr = gl.read_tensors()
+    out = gu.download(ts, dtype)
+    gl.close()
+    return r, tr, out
+
+
+def test_two_per_tensor_clips_at_once():
+    """Without the stop switch the per-tensor clip's workgroup 0 waits in the
+    launch for every tensor's sum; with a second such launch on another
+    stream holding compute units meanwhile, both lists must still come out
+    exactly as when clipped alone."""
+    import torch
+    G = _G()
+    rng = np.random.default_rng(4400)
+    a = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in (30_000_003, 1, 5_000_001) + (77,) * 500]
+    b = [gs.to_storage(rng.standard_normal(n) * 1e-3, "bf16") for n in (40_000_001, 3) + (1,) * 800 + (20_000_000,)]
+    ra, tra, out_a = _per_tensor_alone(a, "f32", 1.0)
+    rb, trb, out_b = _per_tensor_alone(b, "bf16", 1.0)
+    ta, tb = gu.upload(a, "f32"), gu.upload(b, "bf16")
+    pa, pb = [t.clone() for t in ta], [t.clone() for t in tb]
+    la, lb = G.GradList(ta), G.GradList(tb)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        for t, p in zip(ta + tb, pa + pb):
+            t.copy_(p)
+        torch.cuda.synchronize()
+        la.clip_per_tensor_(1.0, stream=s1)
+        lb.clip_per_tensor_(1.0, stream=s2)
+        st1, r1 = la.read(stream=s1)
+        st2, r2 = lb.read(stream=s2)
+        assert st1 == 0 and st2 == 0 and r1["status"] == 0 and r2["status"] == 0, (rep, r1, r2)
+        assert r1["sumsq"] == ra["sumsq"] and r2["sumsq"] == rb["sumsq"], rep
+        assert la.read_tensors().tobytes() == tra.tobytes() and lb.read_tensors().tobytes() == trb.tobytes(), rep
+        gu.assert_bitwise_equal(gu.download(ta, "f32"), out_a, f"list a, repeat {rep}")
+        gu.assert_bitwise_equal(gu.download(tb, "bf16"), out_b, f"list b, repeat {rep}")
     la.close()
     lb.close()
