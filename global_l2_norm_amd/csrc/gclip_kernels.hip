@@ -878,18 +878,33 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   if (ACC && r.b < r.e) {
     Cursor c0;
     cursor_load(p, c0, r.seg);
-    {  // LDS steps
+    {  // LDS steps, the next group's loads (both lists) in flight while one is added
       Cursor cur = c0, cg = c0;
+      u32x4 q[kUnroll], h[kUnroll];
+      if (bs.nlds > 0) {
+        load_group<kNtSum>(p, cur, r.b, r.e, bs.nreg, bs.nsteps, q);
+        load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, bs.nreg, bs.nsteps, h);
+      }
       for (uint32_t k0 = 0; k0 < bs.nlds; k0 += kUnroll) {
-        u32x4 q[kUnroll], h[kUnroll];
-        load_group<kNtSum>(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps, q);
-        load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, bs.nreg + k0, bs.nsteps, h);
+        const bool more = k0 + kUnroll < bs.nlds;
+        u32x4 q2[kUnroll], h2[kUnroll];
+        if (more) {
+          load_group<kNtSum>(p, cur, r.b, r.e, bs.nreg + k0 + kUnroll, bs.nsteps, q2);
+          load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, bs.nreg + k0 + kUnroll, bs.nsteps, h2);
+        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           if (k0 + u < bs.nlds) {
             const u32x4 n = add_vec<DT>(q[u], h[u]);
             acc[u] += vec_sumsq<DT>(n);
             keep_lds[(k0 + u) * kThreads + t] = n;
+          }
+        }
+        if (more) {
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) {
+            q[u] = q2[u];
+            h[u] = h2[u];
           }
         }
       }
