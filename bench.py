@@ -428,7 +428,8 @@ def bench_amp(a, G, g, grads, pristine, flush, gl):
         "scaling": "weak", "vs_baseline": None, "dtype": g.dtype, "data": "synthetic",
         "config": {"workload": WORKLOADS.get(a.config, a.config) + f"; read as scaled by S = {AMP_SCALE:g}, "
                                f"{n_mb:g} microbatch(es), max_norm {max_norm:g}", "name": a.config,
-                   "path": gl.info()["path"], "launches_per_step": "clip + 1 (loss-scale update)",
+                   "path": {1: "fused", 2: "split"}[gl.info()["path"]],
+                   "launches_per_step": 1 if gl.info()["path"] == G.GCLIP_PATH_FUSED else 3,
                    "algorithmic_bytes_per_step": alg, "clipped": bool(r["clipped"])},
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "host_factor_ms_per_step": round(plain_ms, 5),

@@ -145,29 +145,12 @@ hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, do
   return hipGetLastError();
 }
 
-// The loss scale after a step (dynamic loss scaling as published by
-// Micikevicius et al.): found-inf multiplies it by backoff and restarts the
-// count of clean steps; a clean step counts, and the interval-th one
-// multiplies the scale by growth unless that is not finite in binary32.
-// One thread; the step's kernels ran before it on the same stream.
+// The loss-scale update as a kernel of its own (one thread), after the
+// step's kernels that read the scale.
 __global__ void k_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
                              int32_t interval) {
   if (blockIdx.x != 0 || threadIdx.x != 0) return;
-  const int32_t inf = res->nonfinite ? 1 : 0;
-  st->found_inf = inf;
-  if (inf) {
-    st->scale = (float)((double)st->scale * backoff);
-    st->growth_tracker = 0;
-    return;
-  }
-  const int32_t clean = st->growth_tracker + 1;
-  if (clean == interval) {
-    const float grown = (float)((double)st->scale * growth);
-    if (__builtin_isfinite(grown)) st->scale = grown;
-    st->growth_tracker = 0;
-  } else {
-    st->growth_tracker = clean;
-  }
+  amp_update(st, res->nonfinite, AmpUpdate{st, growth, backoff, interval});
 }
 
 hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,

@@ -29,7 +29,7 @@ hipError_t launch_norm(const DevPlan& p, int32_t dtype, AvgSrc avg, gclip_result
 hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         hipStream_t st);
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
-                        uint32_t epoch, uint64_t wait_ticks, hipStream_t st);
+                        uint32_t epoch, uint64_t wait_ticks, AmpUpdate amp, hipStream_t st);
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu);
 hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,
                         gclip_result* res, hipStream_t st);
@@ -428,15 +428,18 @@ gclip_status gclip_scale(gclip_list* list, double max_norm, double avg_factor, i
 
 namespace {
 // The path's kernels on an already validated list: fused, or norm then scale.
+// A loss-scale update (amp.st != nullptr) is taken by the fused kernel's
+// deciding workgroup, or by a kernel of its own after the split path's two.
 hipError_t launch_clip(gclip_list* list, double max_norm, gclip::AvgSrc avg, int err, gclip_result* d_result,
-                       hipStream_t s) {
+                       hipStream_t s, gclip::AmpUpdate amp = gclip::AmpUpdate{nullptr, 0.0, 0.0, 0}) {
   if (list->path == GCLIP_PATH_FUSED) {
     if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
     return gclip::launch_fused(list->dev, list->plan.dtype, max_norm, avg, err, d_result, list->epoch,
-                               list->wait_ticks, s);
+                               list->wait_ticks, amp, s);
   }
   hipError_t e = gclip::launch_norm(list->dev, list->plan.dtype, avg, d_result, s);
   if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg, err, d_result, s);
+  if (e == hipSuccess && amp.st) e = gclip::launch_amp_update(d_result, amp.st, amp.growth, amp.backoff, amp.interval, s);
   return e;
 }
 
@@ -619,9 +622,9 @@ gclip_status gclip_clip_amp_(gclip_list* list, double max_norm, double n_microba
   gclip_status st = check_device(list);
   if (st != GCLIP_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_clip(list, max_norm, gclip::AvgSrc{n_microbatches, &d_amp->scale}, 1, d_result, s);
-  if (e == hipSuccess)
-    e = gclip::launch_amp_update(d_result, d_amp, amp->growth_factor, amp->backoff_factor, amp->growth_interval, s);
+  const hipError_t e = launch_clip(list, max_norm, gclip::AvgSrc{n_microbatches, &d_amp->scale}, 1, d_result, s,
+                                   gclip::AmpUpdate{d_amp, amp->growth_factor, amp->backoff_factor,
+                                                    amp->growth_interval});
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 

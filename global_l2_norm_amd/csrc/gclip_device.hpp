@@ -314,4 +314,27 @@ __device__ __forceinline__ void write_decision(gclip_result* res, const Decision
   res->decided = 1;
 }
 
+// The loss scale after a step (dynamic loss scaling as published by
+// Micikevicius et al.): found-inf multiplies it by backoff and restarts the
+// count of clean steps; a clean step counts, and the interval-th one
+// multiplies the scale by growth unless that is not finite in binary32.
+// One thread, once every kernel that reads the scale for this step has read
+// it.
+__device__ __forceinline__ void amp_update(gclip_amp_state* st, int found_inf, const AmpUpdate& u) {
+  st->found_inf = found_inf ? 1 : 0;
+  if (found_inf) {
+    st->scale = (float)((double)st->scale * u.backoff);
+    st->growth_tracker = 0;
+    return;
+  }
+  const int32_t clean = st->growth_tracker + 1;
+  if (clean == u.interval) {
+    const float grown = (float)((double)st->scale * u.growth);
+    if (__builtin_isfinite(grown)) st->scale = grown;
+    st->growth_tracker = 0;
+  } else {
+    st->growth_tracker = clean;
+  }
+}
+
 }  // namespace gclip

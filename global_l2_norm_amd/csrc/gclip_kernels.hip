@@ -848,7 +848,8 @@ __device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& s
 // written as they are -- so the block is written once.
 template <int DT, bool NTS, bool ACC>
 __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, double max_norm, AvgSrc avs, int err,
-                                           gclip_result* res, uint32_t epoch, uint64_t wait_ticks) {
+                                           gclip_result* res, uint32_t epoch, uint64_t wait_ticks,
+                                           const AmpUpdate& amp) {
   const double avg = avg_value(avs);
   __shared__ u32x4 keep_lds[kLdsSteps * kThreads];
   __shared__ double red[kWaves];
@@ -998,6 +999,9 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       atomic_st(&p.sync[kSkipWord], (uint32_t)d.skip);
       complete_stores();
       atomic_st(&p.sync[kEpochWord], epoch);
+      // every workgroup has arrived, so each has read the loss scale it uses:
+      // the state can move on to the next step's
+      if (amp.st) amp_update(amp.st, nonfinite_of(S, avg), amp);
     }
   } else if (t == 0) {
     const uint64_t t0 = wall_clock64();
@@ -1050,8 +1054,8 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
 template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, double max_norm, AvgSrc avs, int err,
                                                                  gclip_result* res, uint32_t epoch,
-                                                                 uint64_t wait_ticks) {
-  clip_fused<DT, NTS, false>(p, AccSrc{nullptr, nullptr}, max_norm, avs, err, res, epoch, wait_ticks);
+                                                                 uint64_t wait_ticks, AmpUpdate amp) {
+  clip_fused<DT, NTS, false>(p, AccSrc{nullptr, nullptr}, max_norm, avs, err, res, epoch, wait_ticks, amp);
 }
 
 // The last microbatch's += and the clip in one launch.
@@ -1059,7 +1063,7 @@ template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads, 1) void k_accum_clip_fused(DevPlan p, AccSrc A, double max_norm, AvgSrc avs,
                                                                   int err, gclip_result* res, uint32_t epoch,
                                                                   uint64_t wait_ticks) {
-  clip_fused<DT, NTS, true>(p, A, max_norm, avs, err, res, epoch, wait_ticks);
+  clip_fused<DT, NTS, true>(p, A, max_norm, avs, err, res, epoch, wait_ticks, AmpUpdate{nullptr, 0.0, 0.0, 0});
 }
 
 // ---------------------------------------------------------------- host launchers
@@ -1124,9 +1128,9 @@ hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, 
 }
 
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
-                        uint32_t epoch, uint64_t wait_ticks, hipStream_t st) {
+                        uint32_t epoch, uint64_t wait_ticks, AmpUpdate amp, hipStream_t st) {
   DevPlan pc = p;
-  void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch, &wait_ticks};
+  void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch, &wait_ticks, &amp};
   const void* fn = p.nt_store ? fused_kernel<true>(dtype) : fused_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }

@@ -28,6 +28,8 @@
 #include <string>
 #include <vector>
 
+#include "../../include/gclip.h"
+
 namespace gclip {
 
 constexpr int kVecBytes = 16;
@@ -134,6 +136,14 @@ struct DevPlan {
 struct AvgSrc {
   double a;
   const float* scale;
+};
+
+// The loss-scale update of a loss-scaled step, when the kernel that decides
+// also updates the state (st == nullptr: no update).
+struct AmpUpdate {
+  gclip_amp_state* st;
+  double growth, backoff;
+  int32_t interval;
 };
 
 // A microbatch's contribution laid out like a list: the contribution to

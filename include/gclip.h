@@ -437,7 +437,9 @@ gclip_status gclip_norm_amp(gclip_list* list, double n_microbatches, const gclip
 
 /* gclip_clip_ with a = 1 / (n_microbatches * S) and error_if_nonfinite on,
  * then the loss-scale update of d_amp (found_inf, scale, growth_tracker).
- * The path's kernels plus one single-thread kernel; no allocation, no sync. */
+ * On the fused path the update is made in the same launch, by the workgroup
+ * that decides, once every workgroup has read S; on the split path by one
+ * more single-thread kernel after the two.  No allocation, no sync. */
 gclip_status gclip_clip_amp_(gclip_list* list, double max_norm, double n_microbatches, gclip_amp_state* d_amp,
                              const gclip_amp_params* amp, gclip_result* d_result, void* stream);
 
