@@ -591,8 +591,9 @@ __device__ __forceinline__ bool arrive(const DevPlan& p, int* flag) {
 
 // Blocks handed back by the fused kernel.  Worker w's state word is kHeld
 // while w holds its block (or has written it), kHanded once w has stopped
-// waiting at the decision and left its block -- and its first scale chunk --
-// unscaled in memory, kTaken once another workgroup has taken it over.  Line 0's kHandedWord counts the
+// waiting at the decision and left its block -- and its own chunk (the first
+// scale chunk; with the +=, its sum chunk) -- unscaled in memory, kTaken once
+// another workgroup has taken it over.  Line 0's kHandedWord counts the
 // hand-backs.
 constexpr uint32_t kHeld = 0u, kHanded = 2u, kTaken = 3u;
 
@@ -602,13 +603,13 @@ struct HandSlots {
 };
 
 // Take over every block handed back so far and scale it from memory, with
-// the worker's single elements and its own first scale chunk of the
-// streamed region (chunk w is taken by workgroup w without a claim, so no
-// other workgroup scales it) -- the whole workgroup.
-// With the += (ACC) the block was never written: it is read with its
-// contribution, added and written -- times s only when `scale` (the sum is
-// written whatever the decision); the single elements and the chunk already
-// hold their sums, and are scaled only when `scale`.
+// the worker's single elements and its own chunk of the streamed region (no
+// other workgroup scales it: the first scale chunk, which workgroup w takes
+// without a claim; with the +=, the sum chunk it summed) -- the whole
+// workgroup.  With the += (ACC) the block was never written: it is read with
+// its contribution, added and written -- times s only when `scale` (the sum
+// is written whatever the decision); the single elements and the chunk
+// already hold their sums, and are scaled only when `scale`.
 template <int DT, bool ACC = false>
 __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, float s32,
                                                    const AccSrc& A = AccSrc{}, bool scale = true) {
@@ -841,11 +842,12 @@ __device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& s
 // -- scale the handed-back blocks from memory.
 //
 // With the last microbatch's contribution (ACC), phase 1 adds it as it reads:
-// the chunks of the streamed region are written back as sums at once, the
-// block is kept as sums on chip (its LDS steps are read first, while the
-// registers that will hold the rest are still free), and phase 2 writes the
-// block's sums -- scaled, unless the decision writes nothing, when they are
-// written as they are -- so the block is written once.
+// the workgroup's sum chunk of the streamed region is written back as sums at
+// once, the block is kept as sums on chip (its LDS steps are read first, one
+// group of both lists ahead, while the registers that will hold the rest are
+// still free), and phase 2 writes the block's sums -- scaled, unless the
+// decision writes nothing, when they are written as they are -- so the block
+// is written once; then it rescales its own sum chunk.
 template <int DT, bool NTS, bool ACC>
 __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, double max_norm, AvgSrc avs, int err,
                                            gclip_result* res, uint32_t epoch, uint64_t wait_ticks,
