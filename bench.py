@@ -25,6 +25,7 @@ Prints one JSON line.  Other modes:
 import argparse
 import glob
 import hashlib
+import re
 import json
 import math
 import os
@@ -60,11 +61,19 @@ def upload(arrays, dtype):
     return [torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(tdt) for a in arrays]
 
 
+def _code_only(text):
+    """A source file's code alone: comments dropped and spacing collapsed, so
+    that a comment edit is not taken for a change of the measured kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
