@@ -53,8 +53,10 @@ extern "C" {
 #endif
 
 /* 1: the global clip; 2: adds AdamW on the clipped gradient, loss-scaled
- * steps, per-tensor norms and clipping, and the last microbatch's +=. */
-#define GCLIP_VERSION 2
+ * steps, per-tensor norms and clipping, and the last microbatch's +=; 3: the
+ * per-tensor clip without the stop switch in two kernels, with its device
+ * status code GCLIP_DEVICE_WAIT_TIMEOUT and gclip_set_gather_wait. */
+#define GCLIP_VERSION 3
 
 /* Storage format of every element of a list (one format per list). */
 typedef enum gclip_dtype {

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert g.gclip_version() == 2
+    assert g.gclip_version() == 3
     for code in range(8):
         assert g.gclip_status_string(code) not in ("", "unknown status")
     assert g.gclip_status_string(99) == "unknown status"
