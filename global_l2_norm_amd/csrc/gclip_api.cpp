@@ -41,7 +41,10 @@ hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_t
 hipError_t launch_tensor_clip(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm,
                               gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, hipStream_t st);
 hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
-                                  gclip_tensor_result* out, gclip_result* res, hipStream_t st);
+                                  gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, bool gather,
+                                  hipStream_t st);
+hipError_t launch_tensor_norms(const TensorPlan& T, int32_t dtype, AvgSrc avg, gclip_tensor_result* out,
+                               gclip_result* res, uint64_t wait_ticks, bool gather, hipStream_t st);
 hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, double max_norm, AvgSrc avg,
                               int err, gclip_result* res, uint32_t epoch, uint64_t wait_ticks, hipStream_t st);
 }  // namespace gclip
@@ -73,6 +76,11 @@ struct gclip_list {
   uint64_t clock_khz = 0;  // device wall clock
   uint64_t wait_ticks = 0;
 };
+
+// The per-tensor gathering wait (gclip_set_gather_wait) in wall-clock ticks.
+uint64_t gather_wait_ticks(const gclip_list* list) {
+  return (uint64_t)g_gather_wait_us.load(std::memory_order_relaxed) * list->clock_khz / 1000;
+}
 
 struct gclip_contrib {
   const gclip_list* list = nullptr;
@@ -470,8 +478,9 @@ gclip_status gclip_tensor_norms(gclip_list* list, double avg_factor, gclip_tenso
     return GCLIP_EINVAL;
   gclip_status st = check_device(list);
   if (st != GCLIP_OK) return st;
-  const hipError_t e = gclip::launch_tensor_norm(list->tdev, list->plan.dtype, gclip::AvgSrc{avg_factor, nullptr},
-                                                 0.0, 0, 0, d_tensors, d_result, static_cast<hipStream_t>(stream));
+  const hipError_t e = gclip::launch_tensor_norms(list->tdev, list->plan.dtype, gclip::AvgSrc{avg_factor, nullptr},
+                                                  d_tensors, d_result, gather_wait_ticks(list), list->clock_khz > 0,
+                                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
 
@@ -487,9 +496,8 @@ gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double av
   const gclip::AvgSrc avg{avg_factor, nullptr};
   hipError_t e;
   if (!error_if_nonfinite && list->clock_khz > 0) {
-    const uint64_t us = (uint64_t)g_gather_wait_us.load(std::memory_order_relaxed);
     e = gclip::launch_tensor_clip(list->tdev, list->plan.dtype, avg, max_norm, d_tensors, d_result,
-                                  us * list->clock_khz / 1000, s);
+                                  gather_wait_ticks(list), s);
   } else {
     e = gclip::launch_tensor_norm(list->tdev, list->plan.dtype, avg, max_norm, 1, error_if_nonfinite ? 1 : 0,
                                   d_tensors, d_result, s);
@@ -575,6 +583,7 @@ gclip_status gclip_accumulate_norm(gclip_list* list, const gclip_contrib* contri
   const hipError_t e = gclip::launch_accumulate_norm(list->tdev, list->plan.dtype, contrib->delta,
                                                      gclip::AvgSrc{avg_factor, nullptr},
                                                      d_tensors ? d_tensors : list->tscratch, d_result,
+                                                     gather_wait_ticks(list), list->clock_khz > 0,
                                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }
@@ -597,7 +606,7 @@ gclip_status gclip_accumulate_clip_(gclip_list* list, const gclip_contrib* contr
                                   list->epoch, list->wait_ticks, s);
   } else {
     e = gclip::launch_accumulate_norm(list->tdev, list->plan.dtype, contrib->delta, avg, list->tscratch, d_result,
-                                      s);
+                                      gather_wait_ticks(list), list->clock_khz > 0, s);
     if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg, err, d_result, s);
   }
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);

@@ -345,6 +345,81 @@ __global__ __launch_bounds__(kThreads) void k_tensor_clip(TensorPlan T, AvgSrc a
   }
 }
 
+// The per-tensor figures alone (no decision), after k_tensor_partial or
+// k_accum_partial: one workgroup per tensor (one when there is none).
+// Workgroup k sums tensor k's partials (the order of k_tensor_clip), writes
+// its figures and publishes its raw sum as k_tensor_clip's first pieces do;
+// workgroup 0 gathers the list's figures the same way, under the same bounded
+// wait, then overwrites the partials with NaN: every workgroup has read its
+// tensor's partials before it counted.
+__global__ __launch_bounds__(kThreads) void k_tensor_gather(TensorPlan T, AvgSrc avs, gclip_tensor_result* out,
+                                                            gclip_result* res, uint64_t wait_ticks) {
+  __shared__ double red[kWaves];
+  __shared__ int in_time;
+  const double avg = avg_value(avs);
+  const uint32_t t = threadIdx.x;
+  const uint32_t k = blockIdx.x;
+  if ((int32_t)k < T.ntensors) {
+    const uint32_t b = ld_table(T.first, (uint64_t)k), e = ld_table(T.first, (uint64_t)k + 1);
+    const double S = b < e ? tensor_sum(T, b, e, red) : 0.0;
+    if (t == 0) {
+      const double sumsq = (avg * avg) * S;
+      out[k].sumsq = sumsq;
+      out[k].norm = sqrt(sumsq);
+      out[k].nonfinite = nonfinite_of(S, avg);
+      out[k].scale = 1.0;
+      out[k].clipped = 0;
+      if (b < e) {
+        atomic_st(&T.tsum[k], S);
+        complete_stores();
+        (void)atomic_add(T.tsync, 1u);
+      }
+    }
+  }
+  if (k != 0) return;
+  if (t == 0) {
+    in_time = 1;
+    const uint64_t t0 = wall_clock64();
+    while (atomic_ld(T.tsync) != T.nlive) {
+      __builtin_amdgcn_s_sleep(2);
+      if (wall_clock64() - t0 > wait_ticks) {
+        in_time = 0;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (!in_time) {
+    if (t == 0) {
+      res->status = GCLIP_DEVICE_WAIT_TIMEOUT;
+      (void)atomic_add(T.tsync, 0u - T.nlive);
+    }
+    return;
+  }
+  double v = 0.0;
+  int nf_mine = 0;
+  for (int32_t j = (int32_t)t; j < T.ntensors; j += kThreads) {
+    const bool live = ld_table(T.first, (uint64_t)j) < ld_table(T.first, (uint64_t)j + 1);
+    const double S = live ? atomic_ld(&T.tsum[j]) : 0.0;
+    v += S;
+    nf_mine |= nonfinite_of(S, avg);
+  }
+  const double S = wg_sum(v, red);
+  const int nf_any = __syncthreads_or(nf_mine);
+  for (uint32_t i = t; i < T.npieces; i += kThreads) T.partials[i] = __builtin_nan("");
+  if (t == 0) {
+    write_norm(res, S, avg);
+    res->nonfinite = nf_any | res->nonfinite;
+    res->scale = 1.0;
+    res->clipped = 0;
+    res->skipped = 0;
+    res->decided = 0;
+    res->status = 0;
+    res->handed_back = 0;
+    atomic_st(T.tsync, 0u);  // every count of this launch has arrived
+  }
+}
+
 // ---------------------------------------------------------------- the last microbatch's += with the norm
 // Backprop lesson, "Accumulation across microbatches": acc += g, rounded once
 // to the storage format.  The 16-bit formats add in fp32 and round to the
@@ -396,20 +471,42 @@ __global__ __launch_bounds__(kThreads) void k_accum_partial(TensorPlan T, const 
 }
 
 // ---------------------------------------------------------------- host launchers
+// One partial per piece (nothing when the list has no piece).
+hipError_t launch_tensor_partial(const TensorPlan& T, int32_t dtype, hipStream_t st) {
+  if (T.npieces == 0) return hipSuccess;
+  const dim3 grid(T.npieces), block(kThreads);
+  switch (dtype) {
+    case GCLIP_F32: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F32>, grid, block, 0, st, T); break;
+    case GCLIP_F16: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F16>, grid, block, 0, st, T); break;
+    default: hipLaunchKernelGGL(k_tensor_partial<GCLIP_BF16>, grid, block, 0, st, T); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
                               gclip_tensor_result* out, gclip_result* res, hipStream_t st) {
-  if (T.npieces > 0) {
-    const dim3 grid(T.npieces), block(kThreads);
-    switch (dtype) {
-      case GCLIP_F32: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F32>, grid, block, 0, st, T); break;
-      case GCLIP_F16: hipLaunchKernelGGL(k_tensor_partial<GCLIP_F16>, grid, block, 0, st, T); break;
-      default: hipLaunchKernelGGL(k_tensor_partial<GCLIP_BF16>, grid, block, 0, st, T); break;
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const hipError_t e = launch_tensor_partial(T, dtype, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, max_norm, clip, err, out, res);
   return hipGetLastError();
+}
+
+hipError_t launch_tensor_gather(const TensorPlan& T, AvgSrc avg, gclip_tensor_result* out, gclip_result* res,
+                                uint64_t wait_ticks, hipStream_t st) {
+  hipLaunchKernelGGL(k_tensor_gather, dim3(T.ntensors > 0 ? (uint32_t)T.ntensors : 1u), dim3(kThreads), 0, st, T,
+                     avg, out, res, wait_ticks);
+  return hipGetLastError();
+}
+
+// Per-tensor norms alone: the partials, then the per-tensor reduction --
+// gathered in one workgroup per tensor when the device has a wall clock to
+// bound the gathering wait (wait_ticks != 0), else in k_tensor_decide.
+hipError_t launch_tensor_norms(const TensorPlan& T, int32_t dtype, AvgSrc avg, gclip_tensor_result* out,
+                               gclip_result* res, uint64_t wait_ticks, bool gather, hipStream_t st) {
+  if (!gather) return launch_tensor_norm(T, dtype, avg, 0.0, 0, 0, out, res, st);
+  const hipError_t e = launch_tensor_partial(T, dtype, st);
+  if (e != hipSuccess) return e;
+  return launch_tensor_gather(T, avg, out, res, wait_ticks, st);
 }
 
 template <bool NTS>
@@ -461,7 +558,8 @@ const void* accum_kernel(int32_t dtype) {
 }
 
 hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
-                                  gclip_tensor_result* out, gclip_result* res, hipStream_t st) {
+                                  gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, bool gather,
+                                  hipStream_t st) {
   if (T.npieces > 0) {
     TensorPlan tc = T;
     void* args[] = {&tc, &gdelta};
@@ -469,6 +567,7 @@ hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint
     const hipError_t e = hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
+  if (gather) return launch_tensor_gather(T, avg, out, res, wait_ticks, st);
   hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, 0.0, 0, 0, out, res);
   return hipGetLastError();
 }

@@ -108,11 +108,12 @@ typedef struct gclip_result {
 
 /* Device-side failure codes in gclip_result.status. */
 enum {
-  /* gclip_clip_per_tensor_ without the stop switch: the workgroup that
-   * gathers every tensor's sum into the result block waited more than ten
-   * seconds for them and gave up (only under an extreme device load); the
-   * tensors' figures and their scaling are complete, the list's figures in
-   * the result block are not. */
+  /* gclip_clip_per_tensor_ without the stop switch, gclip_tensor_norms or
+   * gclip_accumulate_norm (and the split path of gclip_accumulate_clip_):
+   * the workgroup that gathers every tensor's sum into the result block
+   * waited more than ten seconds for them and gave up (only under an extreme
+   * device load); the tensors' figures and any scaling of the per-tensor
+   * clip are complete, the list's figures in the result block are not. */
   GCLIP_DEVICE_WAIT_TIMEOUT = 1
 };
 
@@ -318,8 +319,10 @@ typedef struct gclip_tensor_result {
  * and the list's norm into d_result (sumsq, norm, nonfinite; decided = 0),
  * so that gclip_scale can follow to finish a global clip with per-tensor
  * figures.  Writes no gradient.  Enqueues two kernels (partial sums per
- * piece, then the reduction; only the second for a list with no element);
- * no allocation, no synchronisation.  Errors as gclip_norm, plus GCLIP_EINVAL for a NULL or
+ * piece; then one workgroup per tensor sums its pieces, and the list's
+ * figures are gathered in the same launch, see GCLIP_DEVICE_WAIT_TIMEOUT;
+ * only the second for a list with no element); no allocation, no
+ * synchronisation.  Errors as gclip_norm, plus GCLIP_EINVAL for a NULL or
  * misaligned d_tensors when the list has tensors. */
 gclip_status gclip_tensor_norms(gclip_list* list, double avg_factor, gclip_tensor_result* d_tensors,
                                 gclip_result* d_result, void* stream);
