@@ -37,7 +37,8 @@ hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, doubl
                              int32_t interval, hipStream_t s);
 hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
                               gclip_tensor_result* out, gclip_result* res, hipStream_t st);
-hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st);
+hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out,
+                               const gclip_result* res, hipStream_t st);
 hipError_t launch_tensor_clip(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm,
                               gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, hipStream_t st);
 hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
@@ -45,6 +46,9 @@ hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint
                                   hipStream_t st);
 hipError_t launch_tensor_norms(const TensorPlan& T, int32_t dtype, AvgSrc avg, gclip_tensor_result* out,
                                gclip_result* res, uint64_t wait_ticks, bool gather, hipStream_t st);
+hipError_t launch_tensor_decisions(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int err,
+                                   gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, bool gather,
+                                   hipStream_t st);
 hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, double max_norm, AvgSrc avg,
                               int err, gclip_result* res, uint32_t epoch, uint64_t wait_ticks, hipStream_t st);
 }  // namespace gclip
@@ -499,9 +503,9 @@ gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double av
     e = gclip::launch_tensor_clip(list->tdev, list->plan.dtype, avg, max_norm, d_tensors, d_result,
                                   gather_wait_ticks(list), s);
   } else {
-    e = gclip::launch_tensor_norm(list->tdev, list->plan.dtype, avg, max_norm, 1, error_if_nonfinite ? 1 : 0,
-                                  d_tensors, d_result, s);
-    if (e == hipSuccess) e = gclip::launch_tensor_scale(list->tdev, list->plan.dtype, d_tensors, s);
+    e = gclip::launch_tensor_decisions(list->tdev, list->plan.dtype, avg, max_norm, error_if_nonfinite ? 1 : 0,
+                                       d_tensors, d_result, gather_wait_ticks(list), list->clock_khz > 0, s);
+    if (e == hipSuccess) e = gclip::launch_tensor_scale(list->tdev, list->plan.dtype, d_tensors, d_result, s);
   }
   return e == hipSuccess ? GCLIP_OK : hip_fail(e);
 }

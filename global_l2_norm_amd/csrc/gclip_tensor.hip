@@ -227,9 +227,13 @@ __global__ __launch_bounds__(kThreads) void k_tensor_decide(TensorPlan T, AvgSrc
 }
 
 // Every piece multiplied by its tensor's factor (nothing written where that
-// factor is 1).  Grid: npieces.
+// factor is 1, nor at all when the result block reports a failure: a
+// gathering wait that gave up has not taken the stop switch's decision).
+// Grid: npieces.
 template <int DT, bool NTS>
-__global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const gclip_tensor_result* out) {
+__global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const gclip_tensor_result* out,
+                                                           const gclip_result* res) {
+  if (res->status != 0) return;
   const TPiece pc = ld_table(T.pieces, blockIdx.x);
   const double s64 = out[uniform32(pc.tensor)].scale;
   if (s64 == 1.0) return;
@@ -345,15 +349,19 @@ __global__ __launch_bounds__(kThreads) void k_tensor_clip(TensorPlan T, AvgSrc a
   }
 }
 
-// The per-tensor figures alone (no decision), after k_tensor_partial or
-// k_accum_partial: one workgroup per tensor (one when there is none).
-// Workgroup k sums tensor k's partials (the order of k_tensor_clip), writes
-// its figures and publishes its raw sum as k_tensor_clip's first pieces do;
-// workgroup 0 gathers the list's figures the same way, under the same bounded
-// wait, then overwrites the partials with NaN: every workgroup has read its
+// The per-tensor reduction after k_tensor_partial or k_accum_partial: one
+// workgroup per tensor (one when there is none).  Workgroup k sums tensor k's
+// partials (the order of k_tensor_clip), writes its figures -- with clip != 0
+// also its decision -- and publishes its raw sum as k_tensor_clip's first
+// pieces do; workgroup 0 gathers the list's figures the same way, under the
+// same bounded wait.  With the stop switch and a NaN/Inf anywhere, workgroup
+// 0 then sets every tensor's factor to 1 (every tensor's own write was
+// counted before it read the counts), so that k_tensor_scale writes nothing.
+// Last, it overwrites the partials with NaN: every workgroup has read its
 // tensor's partials before it counted.
-__global__ __launch_bounds__(kThreads) void k_tensor_gather(TensorPlan T, AvgSrc avs, gclip_tensor_result* out,
-                                                            gclip_result* res, uint64_t wait_ticks) {
+__global__ __launch_bounds__(kThreads) void k_tensor_gather(TensorPlan T, AvgSrc avs, double max_norm, int clip,
+                                                            int err, gclip_tensor_result* out, gclip_result* res,
+                                                            uint64_t wait_ticks) {
   __shared__ double red[kWaves];
   __shared__ int in_time;
   const double avg = avg_value(avs);
@@ -363,12 +371,16 @@ __global__ __launch_bounds__(kThreads) void k_tensor_gather(TensorPlan T, AvgSrc
     const uint32_t b = ld_table(T.first, (uint64_t)k), e = ld_table(T.first, (uint64_t)k + 1);
     const double S = b < e ? tensor_sum(T, b, e, red) : 0.0;
     if (t == 0) {
-      const double sumsq = (avg * avg) * S;
-      out[k].sumsq = sumsq;
-      out[k].norm = sqrt(sumsq);
-      out[k].nonfinite = nonfinite_of(S, avg);
-      out[k].scale = 1.0;
-      out[k].clipped = 0;
+      if (clip) {
+        tensor_figures(&out[k], S, avg, max_norm);
+      } else {
+        const double sumsq = (avg * avg) * S;
+        out[k].sumsq = sumsq;
+        out[k].norm = sqrt(sumsq);
+        out[k].nonfinite = nonfinite_of(S, avg);
+        out[k].scale = 1.0;
+        out[k].clipped = 0;
+      }
       if (b < e) {
         atomic_st(&T.tsum[k], S);
         complete_stores();
@@ -397,23 +409,29 @@ __global__ __launch_bounds__(kThreads) void k_tensor_gather(TensorPlan T, AvgSrc
     return;
   }
   double v = 0.0;
-  int nf_mine = 0;
+  int nf_mine = 0, clipped_mine = 0;
   for (int32_t j = (int32_t)t; j < T.ntensors; j += kThreads) {
     const bool live = ld_table(T.first, (uint64_t)j) < ld_table(T.first, (uint64_t)j + 1);
     const double S = live ? atomic_ld(&T.tsum[j]) : 0.0;
     v += S;
     nf_mine |= nonfinite_of(S, avg);
+    if (clip) clipped_mine |= decide((avg * avg) * S, nonfinite_of(S, avg), max_norm, avg, err).clipped;
   }
   const double S = wg_sum(v, red);
   const int nf_any = __syncthreads_or(nf_mine);
+  const int clipped_any = __syncthreads_or(clipped_mine);
+  const int skip = (clip && err && nf_any) ? 1 : 0;
+  if (skip)
+    for (int32_t j = (int32_t)t; j < T.ntensors; j += kThreads) out[j].scale = 1.0;
   for (uint32_t i = t; i < T.npieces; i += kThreads) T.partials[i] = __builtin_nan("");
   if (t == 0) {
     write_norm(res, S, avg);
     res->nonfinite = nf_any | res->nonfinite;
     res->scale = 1.0;
-    res->clipped = 0;
-    res->skipped = 0;
-    res->decided = 0;
+    res->clipped = clipped_any;
+    res->skipped = skip;
+    if (clip) res->max_norm = max_norm;
+    res->decided = clip ? 1 : 0;
     res->status = 0;
     res->handed_back = 0;
     atomic_st(T.tsync, 0u);  // every count of this launch has arrived
@@ -491,10 +509,25 @@ hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, do
   return hipGetLastError();
 }
 
-hipError_t launch_tensor_gather(const TensorPlan& T, AvgSrc avg, gclip_tensor_result* out, gclip_result* res,
-                                uint64_t wait_ticks, hipStream_t st) {
+hipError_t launch_tensor_gather(const TensorPlan& T, AvgSrc avg, double max_norm, int clip, int err,
+                                gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, hipStream_t st);
+
+// The per-tensor clip's partials and every decision: gathered in one
+// workgroup per tensor, or in k_tensor_decide without a wall clock to bound
+// the gathering wait.  k_tensor_scale follows.
+hipError_t launch_tensor_decisions(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int err,
+                                   gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, bool gather,
+                                   hipStream_t st) {
+  if (!gather) return launch_tensor_norm(T, dtype, avg, max_norm, 1, err, out, res, st);
+  const hipError_t e = launch_tensor_partial(T, dtype, st);
+  if (e != hipSuccess) return e;
+  return launch_tensor_gather(T, avg, max_norm, 1, err, out, res, wait_ticks, st);
+}
+
+hipError_t launch_tensor_gather(const TensorPlan& T, AvgSrc avg, double max_norm, int clip, int err,
+                                gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, hipStream_t st) {
   hipLaunchKernelGGL(k_tensor_gather, dim3(T.ntensors > 0 ? (uint32_t)T.ntensors : 1u), dim3(kThreads), 0, st, T,
-                     avg, out, res, wait_ticks);
+                     avg, max_norm, clip, err, out, res, wait_ticks);
   return hipGetLastError();
 }
 
@@ -506,7 +539,7 @@ hipError_t launch_tensor_norms(const TensorPlan& T, int32_t dtype, AvgSrc avg, g
   if (!gather) return launch_tensor_norm(T, dtype, avg, 0.0, 0, 0, out, res, st);
   const hipError_t e = launch_tensor_partial(T, dtype, st);
   if (e != hipSuccess) return e;
-  return launch_tensor_gather(T, avg, out, res, wait_ticks, st);
+  return launch_tensor_gather(T, avg, 0.0, 0, 0, out, res, wait_ticks, st);
 }
 
 template <bool NTS>
@@ -516,10 +549,11 @@ const void* tensor_scale_kernel(int32_t dtype) {
                               : (const void*)k_tensor_scale<GCLIP_BF16, NTS>;
 }
 
-hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out, hipStream_t st) {
+hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out,
+                               const gclip_result* res, hipStream_t st) {
   if (T.npieces == 0) return hipSuccess;
   TensorPlan tc = T;
-  void* args[] = {&tc, &out};
+  void* args[] = {&tc, &out, &res};
   const void* fn = T.nt_store ? tensor_scale_kernel<true>(dtype) : tensor_scale_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
 }
@@ -567,7 +601,7 @@ hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint
     const hipError_t e = hipLaunchKernel(fn, dim3(T.npieces), dim3(kThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
-  if (gather) return launch_tensor_gather(T, avg, out, res, wait_ticks, st);
+  if (gather) return launch_tensor_gather(T, avg, 0.0, 0, 0, out, res, wait_ticks, st);
   hipLaunchKernelGGL(k_tensor_decide, dim3(1), dim3(kThreads), 0, st, T, avg, 0.0, 0, 0, out, res);
   return hipGetLastError();
 }

@@ -108,12 +108,15 @@ typedef struct gclip_result {
 
 /* Device-side failure codes in gclip_result.status. */
 enum {
-  /* gclip_clip_per_tensor_ without the stop switch, gclip_tensor_norms or
-   * gclip_accumulate_norm (and the split path of gclip_accumulate_clip_):
-   * the workgroup that gathers every tensor's sum into the result block
-   * waited more than ten seconds for them and gave up (only under an extreme
-   * device load); the tensors' figures and any scaling of the per-tensor
-   * clip are complete, the list's figures in the result block are not. */
+  /* gclip_clip_per_tensor_, gclip_tensor_norms or gclip_accumulate_norm
+   * (and the split path of gclip_accumulate_clip_): the workgroup that
+   * gathers every tensor's sum into the result block waited longer than
+   * gclip_set_gather_wait allows (10 s by default, so only under an extreme
+   * device load) and gave up.  The list's figures in the result block are
+   * not complete.  Without the stop switch every tensor's figures and its
+   * scaling still are; with it nothing is written, and the per-tensor factors
+   * in the figures are not meaningful.  gclip_result_read returns
+   * GCLIP_EDEVICE. */
   GCLIP_DEVICE_WAIT_TIMEOUT = 1
 };
 
@@ -337,14 +340,15 @@ gclip_status gclip_tensor_norms(gclip_list* list, double avg_factor, gclip_tenso
  * for another, and two kernels run on `stream` (partial sums per piece; then
  * every piece decides for its own tensor and scales, and the list's figures
  * are gathered in the same launch, see GCLIP_DEVICE_WAIT_TIMEOUT); with it,
- * three (the reduction and every decision in a kernel of their own, between
- * the two).  No allocation, no synchronisation.  Errors as gclip_clip_. */
+ * three (the partials; one workgroup per tensor for the decisions, gathered
+ * with the stop decision; the scale).  No allocation, no synchronisation.
+ * Errors as gclip_clip_. */
 gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double avg_factor,
                                     int32_t error_if_nonfinite, gclip_tensor_result* d_tensors,
                                     gclip_result* d_result, void* stream);
 
-/* How long, in microseconds, gclip_clip_per_tensor_ without the stop switch
- * lets its gathering workgroup wait for every tensor's sum before it reports
+/* How long, in microseconds, the per-tensor calls let their gathering
+ * workgroup wait for every tensor's sum before it reports
  * GCLIP_DEVICE_WAIT_TIMEOUT: for every list of the process, from the next
  * call on.  Default 10 s (a negative value restores it); at most 60 s, else
  * GCLIP_EINVAL.  Meant for tests of that failure path: a short wait makes it

@@ -320,6 +320,48 @@ def test_gather_wait_timeout_is_reported_and_recovers():
     gl.close()
 
 
+def test_gather_wait_timeout_with_the_stop_switch_writes_nothing():
+    """With the stop switch the decisions are gathered before the scale
+    kernel runs; when the gathering wait gives up, the stop decision has not
+    been taken, so nothing may be written: the scale kernel reads the failure
+    in the result block.  Later calls with the normal wait clip as the
+    oracle does."""
+    G = _G()
+    from global_l2_norm_amd import _lib
+    rng = np.random.default_rng(2800)
+    sizes = [5] + [1] * 1500 + [4_000_001] + [300] * 200 + [0]
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-2, "f32") for n in sizes]
+    c = 1.0
+    assert all(abs(math.sqrt(x) - c) > 1e-3 for x in oracle.tensor_sumsq(arrays, "f32"))
+    ref = [a.copy() for a in arrays]
+    ro = oracle.clip_per_tensor_(ref, "f32", c, 1.0, True)
+    ts = gu.upload(arrays, "f32")
+    gl = G.GradList(ts)
+    timeouts = 0
+    try:
+        G.gclip_set_gather_wait(0)
+        for rep in range(3):
+            _reload(ts, arrays, "f32")
+            gl.clip_per_tensor_(c, 1.0, True)
+            st, r = gl.read(True)
+            assert r["status"] in (0, G.GCLIP_DEVICE_WAIT_TIMEOUT), r
+            if r["status"]:
+                timeouts += 1
+                assert st == _lib.GCLIP_EDEVICE
+                gu.assert_bitwise_equal(gu.download(ts, "f32"), arrays, f"gave up, call {rep}: nothing written")
+            else:
+                _check_call(gl, ts, arrays, ref, ro, "f32", f"stop switch, wait 0, call {rep}")
+    finally:
+        G.gclip_set_gather_wait(-1)
+    print(f"{timeouts} of 3 calls gave up waiting")
+    assert timeouts >= 1
+    for rep in range(2):
+        _reload(ts, arrays, "f32")
+        gl.clip_per_tensor_(c, 1.0, True)
+        _check_call(gl, ts, arrays, ref, ro, "f32", f"stop switch, normal wait, call {rep}")
+    gl.close()
+
+
 def test_gather_wait_bounds():
     G = _G()
     with pytest.raises(G.GclipError):
