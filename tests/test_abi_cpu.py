@@ -50,6 +50,15 @@ def test_version_and_status_strings():
     assert g.gclip_status_string(99) == "unknown status"
 
 
+def test_gather_wait_setter_bounds():
+    """The process-wide bound of the per-tensor gathering wait: above 60 s is
+    rejected, a negative value restores the default (no GPU involved)."""
+    assert _lib.lib.gclip_set_gather_wait(61 * 1000 * 1000) == _lib.GCLIP_EINVAL
+    assert _lib.lib.gclip_set_gather_wait(60 * 1000 * 1000) == _lib.GCLIP_OK
+    assert _lib.lib.gclip_set_gather_wait(0) == _lib.GCLIP_OK
+    assert _lib.lib.gclip_set_gather_wait(-1) == _lib.GCLIP_OK
+
+
 @pytest.mark.parametrize("args,code", [
     (([0x1000], [-1], 0), _lib.GCLIP_EINVAL),               # negative size
     (([0x1002], [10], 0), _lib.GCLIP_EINVAL),               # fp32 tensor not 4-byte aligned
