@@ -37,7 +37,7 @@ hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, doubl
                              int32_t interval, hipStream_t s);
 hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
                               gclip_tensor_result* out, gclip_result* res, hipStream_t st);
-hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out,
+hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, gclip_tensor_result* out,
                                const gclip_result* res, hipStream_t st);
 hipError_t launch_tensor_clip(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm,
                               gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, hipStream_t st);

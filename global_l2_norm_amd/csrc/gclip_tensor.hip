@@ -227,13 +227,19 @@ __global__ __launch_bounds__(kThreads) void k_tensor_decide(TensorPlan T, AvgSrc
 }
 
 // Every piece multiplied by its tensor's factor (nothing written where that
-// factor is 1, nor at all when the result block reports a failure: a
-// gathering wait that gave up has not taken the stop switch's decision).
-// Grid: npieces.
+// factor is 1, nor at all when the result block reports a failure -- a
+// gathering wait that gave up has not taken the stop switch's decision -- or
+// that the stop switch stopped the update, when workgroup 0 sets every
+// tensor's factor in the figures to 1).  Grid: npieces.
 template <int DT, bool NTS>
-__global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, const gclip_tensor_result* out,
+__global__ __launch_bounds__(kThreads) void k_tensor_scale(TensorPlan T, gclip_tensor_result* out,
                                                            const gclip_result* res) {
   if (res->status != 0) return;
+  if (res->skipped) {
+    if (blockIdx.x == 0)
+      for (int32_t j = (int32_t)threadIdx.x; j < T.ntensors; j += kThreads) out[j].scale = 1.0;
+    return;
+  }
   const TPiece pc = ld_table(T.pieces, blockIdx.x);
   const double s64 = out[uniform32(pc.tensor)].scale;
   if (s64 == 1.0) return;
@@ -354,11 +360,13 @@ __global__ __launch_bounds__(kThreads) void k_tensor_clip(TensorPlan T, AvgSrc a
 // partials (the order of k_tensor_clip), writes its figures -- with clip != 0
 // also its decision -- and publishes its raw sum as k_tensor_clip's first
 // pieces do; workgroup 0 gathers the list's figures the same way, under the
-// same bounded wait.  With the stop switch and a NaN/Inf anywhere, workgroup
-// 0 then sets every tensor's factor to 1 (every tensor's own write was
-// counted before it read the counts), so that k_tensor_scale writes nothing.
-// Last, it overwrites the partials with NaN: every workgroup has read its
-// tensor's partials before it counted.
+// same bounded wait, and takes the stop decision (a NaN/Inf anywhere with the
+// switch on): it records it in the result block only, and k_tensor_scale,
+// the next launch, then writes nothing and sets every tensor's factor in the
+// figures to 1 -- overwriting them here could race with the tensors' own
+// writes, which sit in other XCDs' L2 until the launch ends.  Last, it
+// overwrites the partials with NaN: every workgroup has read its tensor's
+// partials before it counted.
 __global__ __launch_bounds__(kThreads) void k_tensor_gather(TensorPlan T, AvgSrc avs, double max_norm, int clip,
                                                             int err, gclip_tensor_result* out, gclip_result* res,
                                                             uint64_t wait_ticks) {
@@ -421,8 +429,6 @@ __global__ __launch_bounds__(kThreads) void k_tensor_gather(TensorPlan T, AvgSrc
   const int nf_any = __syncthreads_or(nf_mine);
   const int clipped_any = __syncthreads_or(clipped_mine);
   const int skip = (clip && err && nf_any) ? 1 : 0;
-  if (skip)
-    for (int32_t j = (int32_t)t; j < T.ntensors; j += kThreads) out[j].scale = 1.0;
   for (uint32_t i = t; i < T.npieces; i += kThreads) T.partials[i] = __builtin_nan("");
   if (t == 0) {
     write_norm(res, S, avg);
@@ -549,7 +555,7 @@ const void* tensor_scale_kernel(int32_t dtype) {
                               : (const void*)k_tensor_scale<GCLIP_BF16, NTS>;
 }
 
-hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, const gclip_tensor_result* out,
+hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, gclip_tensor_result* out,
                                const gclip_result* res, hipStream_t st) {
   if (T.npieces == 0) return hipSuccess;
   TensorPlan tc = T;
