@@ -390,8 +390,10 @@ gclip_status gclip_contrib_destroy(gclip_contrib* contrib);
  * NULL, every tensor's figures into d_tensors (n_tensors entries, as for
  * gclip_tensor_norms).  gclip_scale can then finish the global clip, or
  * gclip_adamw_step the optimizer step.  contrib must have been registered
- * for this list.  Two kernels on `stream`; no allocation, no
- * synchronisation. */
+ * for this list.  Two kernels on `stream` (the += with partial sums per
+ * piece; then one workgroup per tensor sums its pieces, and the list's
+ * figures are gathered in the same launch, see GCLIP_DEVICE_WAIT_TIMEOUT);
+ * no allocation, no synchronisation. */
 gclip_status gclip_accumulate_norm(gclip_list* list, const gclip_contrib* contrib, double avg_factor,
                                    gclip_tensor_result* d_tensors, gclip_result* d_result, void* stream);
 
