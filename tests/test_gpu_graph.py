@@ -116,6 +116,7 @@ def test_per_tensor_and_accumulate_replays():
     gl = G.GradList(ts)
     c = G.Contribution(gl, tc)
     for name, call in (("per_tensor", lambda: gl.clip_per_tensor_(0.5, 1.0, False)),
+                       ("per_tensor_stop", lambda: gl.clip_per_tensor_(0.5, 1.0, True)),
                        ("accumulate", lambda: gl.accumulate_clip_(c, 1.0, 0.5, False))):
         g = capture(call)
         for k, arrays in enumerate(contents):
@@ -130,6 +131,10 @@ def test_per_tensor_and_accumulate_replays():
             _, r = gl.read()
             gu.assert_bitwise_equal_but_nan(out, eager, "f32", f"{name} replay {k}")
             assert r["clipped"] == r_eager["clipped"] and r["nonfinite"] == r_eager["nonfinite"], (name, k)
+            assert r["skipped"] == r_eager["skipped"], (name, k)
+            if name == "per_tensor_stop" and r["nonfinite"]:
+                assert r["skipped"], (name, k)
+                gu.assert_bitwise_equal_but_nan(out, arrays, "f32", f"{name} replay {k}: stopped, nothing written")
     gu.assert_bitwise_equal(gu.download(tc, "f32"), contrib, "contribution only read")
     c.close()
     gl.close()
