@@ -38,8 +38,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "clip_grad_norm GB/s and % of HBM peak, ANDREA-120M-shaped grads"
 HBM_PEAK_GBPS = 8000.0
+# The sources that decide what the measured kernels move: the kernels, the
+# device walk, and the host plan and workspace layout (chunk and block split,
+# store kinds, pools).  A committed counter summary is used only while these
+# hash to the value recorded in it.
 KERNEL_SOURCES = ["global_l2_norm_amd/csrc/gclip_kernels.hip", "global_l2_norm_amd/csrc/gclip_cursor.hpp",
-                  "global_l2_norm_amd/csrc/gclip_device.hpp"]
+                  "global_l2_norm_amd/csrc/gclip_device.hpp", "global_l2_norm_amd/csrc/gclip_plan.hpp",
+                  "global_l2_norm_amd/csrc/gclip_plan.cpp", "global_l2_norm_amd/csrc/gclip_api.cpp"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_grad_clip_fused__andrea120m_f32__pmc.txt")
 WORKLOADS = {
     "andrea120m_f32": "ANDREA-120M-shaped fp32 gradient list: 124 tensors (tok_embed [8449,768], pos_embed "

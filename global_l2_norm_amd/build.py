@@ -7,12 +7,12 @@ that it does not know the feature, which is harmless.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgclip.so")
-BENCH = os.path.join(HERE, "gclip_bench")
 SOURCES = ["gclip_api.cpp", "gclip_plan.cpp", "gclip_trace.cpp", "gclip_kernels.hip", "gclip_tensor.hip",
            "gclip_adamw.hip"]
 ARCH = os.environ.get("GCLIP_OFFLOAD_ARCH", "gfx950")
@@ -30,21 +30,35 @@ def compile_flags():
             "-packed-fp32-ops", "-Wall", "-Wextra", "-Wno-unused-parameter", "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False, defines=(), lib_path: str = LIB, bench_path: str = BENCH) -> str:
-    """Always recompile the library and the native timing driver; return the
-    library's path.  `defines` are extra -D flags (tuning sweeps)."""
-    objs = []
+def _jobs() -> int:
+    try:
+        n = int(os.environ.get("MAX_JOBS", "0"))
+    except ValueError:
+        n = 0
+    return max(1, min(n if n > 0 else (os.cpu_count() or 1), 16))
+
+
+def build(verbose: bool = False, defines=(), lib_path: str = LIB) -> str:
+    """Always recompile the library (the sources in parallel); return its
+    path.  `defines` are extra -D flags (tuning sweeps)."""
     odir = os.path.join(HERE, "_build")
     os.makedirs(odir, exist_ok=True)
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(odir, os.path.splitext(src)[0] + ".o")
         cmd = [hipcc()] + compile_flags() + [f"-D{d}" for d in defines] + ["-x", "hip", "-c",
                                                                              os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
+        return src, obj, cmd, r.returncode, errs
+
+    with ThreadPoolExecutor(max_workers=min(_jobs(), len(SOURCES))) as pool:
+        results = list(pool.map(compile_one, SOURCES))
+    objs = []
+    for src, obj, cmd, rc, errs in results:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if rc != 0:
             sys.stderr.write(errs + "\n")
             raise RuntimeError(f"hipcc failed on {src}")
         if verbose and errs.strip():
@@ -56,18 +70,6 @@ def build(verbose: bool = False, defines=(), lib_path: str = LIB, bench_path: st
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, lib_path)
-    # native timing driver, linked to the library next to it
-    libdir, libname = os.path.split(lib_path)
-    tmpb = bench_path + ".tmp"
-    cmd = [hipcc()] + compile_flags() + ["-x", "hip", os.path.join(CSRC, "gclip_bench.cpp"), "-x", "none",
-                                         f"-L{libdir}", f"-l:{libname}", "-Wl,-rpath,$ORIGIN", "-o", tmpb]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write("\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l) + "\n")
-        raise RuntimeError("hipcc failed on gclip_bench.cpp")
-    os.replace(tmpb, bench_path)
     return lib_path
 
 

@@ -76,6 +76,9 @@ constexpr bool kAdamNtLoad = GCLIP_ADAM_NT_LOAD != 0;
 template <int DT>
 __global__ __launch_bounds__(kAdamThreads) void k_adamw_clip(AdamPlan P, AdamHp h, double max_norm, AvgSrc avs,
                                                              int err, gclip_result* res) {
+  // a result block that reports a failure (a gathering wait gave up) holds
+  // no norm of this step: no decision, no update
+  if (res->status != 0) return;
   const double avg = avg_value(avs);
   const Decision d = decide(res->sumsq, res->nonfinite, max_norm, avg, err);
   if (blockIdx.x == 0 && threadIdx.x == 0) write_decision(res, d, max_norm);
@@ -146,10 +149,11 @@ hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, do
 }
 
 // The loss-scale update as a kernel of its own (one thread), after the
-// step's kernels that read the scale.
+// step's kernels that read the scale.  No update when the result block
+// reports a failure: that step was neither taken nor found non-finite.
 __global__ void k_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
                              int32_t interval) {
-  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  if (blockIdx.x != 0 || threadIdx.x != 0 || res->status != 0) return;
   amp_update(st, res->nonfinite, AmpUpdate{st, growth, backoff, interval});
 }
 

@@ -29,7 +29,7 @@ hipError_t launch_norm(const DevPlan& p, int32_t dtype, AvgSrc avg, gclip_result
 hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         hipStream_t st);
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
-                        uint32_t epoch, uint64_t wait_ticks, AmpUpdate amp, hipStream_t st);
+                        uint64_t wait_ticks, AmpUpdate amp, hipStream_t st);
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu);
 hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,
                         gclip_result* res, hipStream_t st);
@@ -50,7 +50,7 @@ hipError_t launch_tensor_decisions(const TensorPlan& T, int32_t dtype, AvgSrc av
                                    gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, bool gather,
                                    hipStream_t st);
 hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, double max_norm, AvgSrc avg,
-                              int err, gclip_result* res, uint32_t epoch, uint64_t wait_ticks, hipStream_t st);
+                              int err, gclip_result* res, uint64_t wait_ticks, hipStream_t st);
 }  // namespace gclip
 
 // How long a workgroup of the fused kernel waits at the grid-wide decision
@@ -75,7 +75,6 @@ struct gclip_list {
   int device = 0;
   bool fused_ok = false;
   int32_t path = GCLIP_PATH_SPLIT;
-  uint32_t epoch = 0;
   int64_t wait_us = kDefaultWaitUs;
   uint64_t clock_khz = 0;  // device wall clock
   uint64_t wait_ticks = 0;
@@ -313,7 +312,8 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
         (e = up(o_fusv, P.fus_vb.data(), (nchs + 1) * 8)) || (e = up(o_fuss, P.fus_seg.data(), nchs * 4)) || (e = up(o_sum, P.sum_seg.data(), nsum * 4)) || (e = up(o_wksc, P.wk_scbegin.data(), (nw + 1) * 8)) ||
         (e = up(o_sca, P.sc_addr.data(), nsc * 8)) ||
         (e = up(o_tpc, L->tplan.pieces.data(), ntp * sizeof(gclip::TPiece))) ||
-        (e = up(o_tfi, L->tplan.first.data(), ntf * 4)) || (e = hipDeviceSynchronize()) != hipSuccess) {
+        (e = up(o_tfi, L->tplan.first.data(), ntf * 4)) || (e = up(o_bc, &gclip::kUndecided, 8)) ||
+        (e = hipDeviceSynchronize()) != hipSuccess) {
       (void)hipFree(L->blob);
       delete L;
       return hip_fail(e);
@@ -330,7 +330,7 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     D.wk_scbegin = reinterpret_cast<const uint64_t*>(b + o_wksc);
     D.sc_addr = reinterpret_cast<const uint64_t*>(b + o_sca);
     D.partials = reinterpret_cast<double*>(b + o_part);
-    D.bcast = reinterpret_cast<double*>(b + o_bc);
+    D.bcast = reinterpret_cast<uint64_t*>(b + o_bc);
     D.sync = reinterpret_cast<uint32_t*>(b + o_sync);
     D.bstate = reinterpret_cast<uint32_t*>(b + o_bst);
     D.nvec = P.nvec();
@@ -445,9 +445,8 @@ namespace {
 hipError_t launch_clip(gclip_list* list, double max_norm, gclip::AvgSrc avg, int err, gclip_result* d_result,
                        hipStream_t s, gclip::AmpUpdate amp = gclip::AmpUpdate{nullptr, 0.0, 0.0, 0}) {
   if (list->path == GCLIP_PATH_FUSED) {
-    if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
-    return gclip::launch_fused(list->dev, list->plan.dtype, max_norm, avg, err, d_result, list->epoch,
-                               list->wait_ticks, amp, s);
+    return gclip::launch_fused(list->dev, list->plan.dtype, max_norm, avg, err, d_result, list->wait_ticks, amp,
+                               s);
   }
   hipError_t e = gclip::launch_norm(list->dev, list->plan.dtype, avg, d_result, s);
   if (e == hipSuccess) e = gclip::launch_scale(list->dev, list->plan.dtype, max_norm, avg, err, d_result, s);
@@ -605,9 +604,8 @@ gclip_status gclip_accumulate_clip_(gclip_list* list, const gclip_contrib* contr
   const int err = error_if_nonfinite ? 1 : 0;
   hipError_t e;
   if (list->path == GCLIP_PATH_FUSED) {
-    if (++list->epoch == 0) list->epoch = 1;  // 0 is the workspace's initial value
     e = gclip::launch_accum_fused(list->dev, contrib->acc, list->plan.dtype, max_norm, avg, err, d_result,
-                                  list->epoch, list->wait_ticks, s);
+                                  list->wait_ticks, s);
   } else {
     e = gclip::launch_accumulate_norm(list->tdev, list->plan.dtype, contrib->delta, avg, list->tscratch, d_result,
                                       gather_wait_ticks(list), list->clock_khz > 0, s);

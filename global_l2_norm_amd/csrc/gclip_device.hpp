@@ -231,6 +231,12 @@ __device__ __forceinline__ uint32_t atomic_add(uint32_t* a, uint32_t v) {
 __device__ __forceinline__ double atomic_ld(const double* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t atomic_ld(const uint64_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_st(uint64_t* a, uint64_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void atomic_st(double* a, double v) {
   __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -249,6 +255,15 @@ __device__ __forceinline__ void complete_stores() {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+
+// The reader's side of that: once a wait on another workgroup's flag or
+// ticket has ended, an agent-scope acquire before reading what the flag
+// guards.  The compiler may then move no later load above the flag's load,
+// and the hardware serves none of them from a stale cache line: on gfx950
+// it is one buffer_inv sc1, which invalidates the compute unit's vector L1
+// and its XCD's L2 lines that may be stale.  Taken once per workgroup per
+// wait, never inside a loop over the data.
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // ---------------------------------------------------------------- workgroup sum and the decision
 // Sum of v over the workgroup, the same bits in every thread.  Butterfly

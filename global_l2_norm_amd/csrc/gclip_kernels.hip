@@ -242,8 +242,8 @@ __device__ __forceinline__ void accum_scale_steps(const DevPlan& p, const AccSrc
 }
 
 // ---------------------------------------------------------------- counters in the workspace
-// Words of line 0 of sync.
-constexpr int kEpochWord = 0, kSkipWord = 1, kHandedWord = 2;
+// Word of line 0 of sync.
+constexpr int kHandedWord = 0;
 
 __device__ __forceinline__ uint32_t* sum_pools(const DevPlan& p) { return p.sync + kSyncLineWords; }
 __device__ __forceinline__ uint32_t* scale_pools(const DevPlan& p) { return p.sync + (1 + kPools) * kSyncLineWords; }
@@ -563,10 +563,24 @@ __device__ __forceinline__ double* worker_partial(const DevPlan& p, int w) {
 }
 
 // Sum of all partials in index order (lane i takes i, i + kThreads, ...).
+// A lane issues the loads of kPartialBatch partials before it adds any, so
+// the sum waits for one round trip per batch, not one per partial (it is on
+// the path to the grid-wide decision); adding 0.0 for the slots past the end
+// leaves the sum's bits as they are.
+constexpr int kPartialBatch = 8;
 __device__ __forceinline__ double partials_sum(const DevPlan& p, double* red) {
   double v = 0.0;
   const uint32_t n = npartials(p);
-  for (uint32_t i = threadIdx.x; i < n; i += kThreads) v += atomic_ld(&p.partials[i]);
+  for (uint32_t i0 = threadIdx.x; i0 < n; i0 += kThreads * kPartialBatch) {
+    double x[kPartialBatch];
+#pragma unroll
+    for (int k = 0; k < kPartialBatch; ++k) {
+      const uint32_t i = i0 + (uint32_t)k * kThreads;
+      x[k] = i < n ? atomic_ld(&p.partials[i]) : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPartialBatch; ++k) v += x[k];
+  }
   return wg_sum(v, red);
 }
 
@@ -584,6 +598,7 @@ __device__ __forceinline__ bool arrive(const DevPlan& p, int* flag) {
   if (threadIdx.x == 0) {
     complete_stores();
     *flag = take_ticket(arrival_tickets(p), p.nworkers) ? 1 : 0;
+    if (*flag) acquire_agent();  // before the partials are read
   }
   __syncthreads();
   return *flag != 0;
@@ -668,18 +683,21 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
   if (threadIdx.x == 0) {
     complete_stores();
     *flag = take_ticket(finish_tickets(p), p.nworkers) ? 1 : 0;
+    if (*flag) acquire_agent();  // before the hand-back count, the decision and the states are read
   }
   __syncthreads();
   if (*flag == 0) return;
   if (fused) {
     const uint32_t handed = atomic_ld(&p.sync[kHandedWord]);
     if (handed != 0u) {
-      const double s = atomic_ld(&p.bcast[0]);
-      const uint32_t skip = atomic_ld(&p.sync[kSkipWord]);
+      // the deciding workgroup published before it took its finish ticket
+      const uint64_t dw = atomic_ld(&p.bcast[0]);
+      const bool skip = dw == kDecidedSkip || dw == kUndecided;
+      const double s = skip ? 1.0 : __builtin_bit_cast(double, dw);
       if constexpr (ACC) {
-        take_handed_blocks<DT, true>(p, hs, s, (float)s, A, skip == 0u && s != 1.0);
+        take_handed_blocks<DT, true>(p, hs, s, (float)s, A, !skip && s != 1.0);
       } else {
-        if (skip == 0u && s != 1.0) take_handed_blocks<DT>(p, hs, s, (float)s);
+        if (!skip && s != 1.0) take_handed_blocks<DT>(p, hs, s, (float)s);
       }
       __syncthreads();
       for (uint32_t i = threadIdx.x; i < (uint32_t)p.nworkers; i += kThreads) atomic_st(&p.bstate[i], kHeld);
@@ -687,10 +705,9 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
     if (threadIdx.x == 0) {
       res->handed_back = (int32_t)handed;
       atomic_st(&p.sync[kHandedWord], 0u);
-      // every workgroup has left its wait for the decision: clear the
-      // release word, so that the next launch waits again whatever epoch it
-      // carries (a replayed graph carries the one it was captured with)
-      atomic_st(&p.sync[kEpochWord], 0u);
+      // every workgroup has left its wait for the decision: the next launch
+      // (a replayed graph's too) starts from an undecided word
+      atomic_st(&p.bcast[0], kUndecided);
     }
   }
   if (threadIdx.x == 0) reset_pools(scale_pools(p));
@@ -739,7 +756,11 @@ __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, AvgSr
 }
 
 // Kernel 3: the decision from the device result block, then g <- g * s over
-// the chunks each workgroup claims, or no write at all.
+// the chunks each workgroup claims, or no write at all.  A block whose status
+// reports a failure (a gathering wait before this pass gave up, so sumsq and
+// nonfinite are not this call's) is left as it is and nothing is written:
+// deciding from it could scale by a stale norm, or miss a NaN the stop switch
+// would have caught.
 template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_norm, AvgSrc avs, int err,
                                                          gclip_result* res) {
@@ -748,9 +769,10 @@ __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_n
   __shared__ HandSlots hs;
   __shared__ int flag;
   const int w = blockIdx.x;
+  const bool failed = res->status != 0;
   const Decision d = decide(res->sumsq, res->nonfinite, max_norm, avg, err);
-  if (w == 0 && threadIdx.x == 0) write_decision(res, d, max_norm);
-  if (!(d.skip || d.s == 1.0)) {
+  if (w == 0 && threadIdx.x == 0 && !failed) write_decision(res, d, max_norm);
+  if (!failed && !(d.skip || d.s == 1.0)) {
     const double s64 = d.s;
     const float s32 = (float)d.s;
     scale_chunks<DT, NTS>(p, sl, p.spl_vb, p.spl_seg, p.nchunk, s64, s32);
@@ -850,8 +872,7 @@ __device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& s
 // is written once; then it rescales its own sum chunk.
 template <int DT, bool NTS, bool ACC>
 __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, double max_norm, AvgSrc avs, int err,
-                                           gclip_result* res, uint32_t epoch, uint64_t wait_ticks,
-                                           const AmpUpdate& amp) {
+                                           gclip_result* res, uint64_t wait_ticks, const AmpUpdate& amp) {
   const double avg = avg_value(avs);
   __shared__ u32x4 keep_lds[kLdsSteps * kThreads];
   __shared__ double red[kWaves];
@@ -996,18 +1017,18 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       res->status = 0;
       bc_s = d.s;
       bc_skip = d.skip;
+      // the decision is published by value: the word is the flag, so the
+      // workgroups waiting for it need no ordering against any other store
+      atomic_st(&p.bcast[0], d.skip ? kDecidedSkip : __builtin_bit_cast(uint64_t, d.s));
       reset_pools(sum_pools(p));
-      atomic_st(&p.bcast[0], d.s);
-      atomic_st(&p.sync[kSkipWord], (uint32_t)d.skip);
-      complete_stores();
-      atomic_st(&p.sync[kEpochWord], epoch);
       // every workgroup has arrived, so each has read the loss scale it uses:
       // the state can move on to the next step's
       if (amp.st) amp_update(amp.st, nonfinite_of(S, avg), amp);
     }
   } else if (t == 0) {
     const uint64_t t0 = wall_clock64();
-    while (atomic_ld(&p.sync[kEpochWord]) != epoch) {
+    uint64_t dw;
+    while ((dw = atomic_ld(&p.bcast[0])) == kUndecided) {
       __builtin_amdgcn_s_sleep(2);
       if (wall_clock64() - t0 > wait_ticks) {
         // hand the block back: its state is visible before the count (with
@@ -1024,8 +1045,8 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       }
     }
     if (!gave_up) {
-      bc_s = atomic_ld(&p.bcast[0]);
-      bc_skip = (int)atomic_ld(&p.sync[kSkipWord]);
+      bc_skip = dw == kDecidedSkip ? 1 : 0;
+      bc_s = bc_skip ? 1.0 : __builtin_bit_cast(double, dw);
     }
   }
   __syncthreads();
@@ -1055,17 +1076,17 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
 
 template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads, 1) void k_grad_clip_fused(DevPlan p, double max_norm, AvgSrc avs, int err,
-                                                                 gclip_result* res, uint32_t epoch,
-                                                                 uint64_t wait_ticks, AmpUpdate amp) {
-  clip_fused<DT, NTS, false>(p, AccSrc{nullptr, nullptr}, max_norm, avs, err, res, epoch, wait_ticks, amp);
+                                                                 gclip_result* res, uint64_t wait_ticks,
+                                                                 AmpUpdate amp) {
+  clip_fused<DT, NTS, false>(p, AccSrc{nullptr, nullptr}, max_norm, avs, err, res, wait_ticks, amp);
 }
 
 // The last microbatch's += and the clip in one launch.
 template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads, 1) void k_accum_clip_fused(DevPlan p, AccSrc A, double max_norm, AvgSrc avs,
-                                                                  int err, gclip_result* res, uint32_t epoch,
+                                                                  int err, gclip_result* res,
                                                                   uint64_t wait_ticks) {
-  clip_fused<DT, NTS, true>(p, A, max_norm, avs, err, res, epoch, wait_ticks, AmpUpdate{nullptr, 0.0, 0.0, 0});
+  clip_fused<DT, NTS, true>(p, A, max_norm, avs, err, res, wait_ticks, AmpUpdate{nullptr, 0.0, 0.0, 0});
 }
 
 // ---------------------------------------------------------------- host launchers
@@ -1121,18 +1142,18 @@ const void* accum_fused_kernel(int32_t dtype) {
 }
 
 hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, double max_norm, AvgSrc avg,
-                              int err, gclip_result* res, uint32_t epoch, uint64_t wait_ticks, hipStream_t st) {
+                              int err, gclip_result* res, uint64_t wait_ticks, hipStream_t st) {
   DevPlan pc = p;
   AccSrc ac = A;
-  void* args[] = {&pc, &ac, &max_norm, &avg, &err, &res, &epoch, &wait_ticks};
+  void* args[] = {&pc, &ac, &max_norm, &avg, &err, &res, &wait_ticks};
   const void* fn = p.nt_store ? accum_fused_kernel<true>(dtype) : accum_fused_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }
 
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
-                        uint32_t epoch, uint64_t wait_ticks, AmpUpdate amp, hipStream_t st) {
+                        uint64_t wait_ticks, AmpUpdate amp, hipStream_t st) {
   DevPlan pc = p;
-  void* args[] = {&pc, &max_norm, &avg, &err, &res, &epoch, &wait_ticks, &amp};
+  void* args[] = {&pc, &max_norm, &avg, &err, &res, &wait_ticks, &amp};
   const void* fn = p.nt_store ? fused_kernel<true>(dtype) : fused_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
 }

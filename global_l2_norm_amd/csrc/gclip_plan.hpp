@@ -93,10 +93,18 @@ struct ChunkShape {
 int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
                int32_t threads, uint64_t resident_cap, const ChunkShape& shape, HostPlan& out, std::string* why);
 
+// The fused kernel's decision word (bcast[0]): the bits of the factor s, or
+// one of two signalling-NaN patterns.  Arithmetic never yields a signalling
+// NaN, and s is finite whenever it is written, so no factor collides with
+// them.  The word holds kUndecided from the list's creation on and again
+// after every launch (its last workgroup resets it).
+constexpr uint64_t kUndecided = 0x7ff4000000000001ull;
+constexpr uint64_t kDecidedSkip = 0x7ff4000000000002ull;
+
 // Device view of a plan plus the list's workspace (all device addresses).
 // sync holds 128-byte lines of counters (one line per counter group, so that
 // the XCDs do not share lines):
-//   line 0                       epoch, skip flag, count of handed-back blocks
+//   line 0                       count of handed-back blocks
 //   lines 1 .. kPools            chunk pools of the summing passes (one per XCD)
 //   lines 1 + kPools ..          chunk pools of the scaling passes
 //   lines 1 + 2 kPools ..        arrival tickets: one per XCD group, then the top one
@@ -118,7 +126,7 @@ struct DevPlan {
   const uint64_t* wk_scbegin;
   const uint64_t* sc_addr;
   double* partials;   // nsum * kWaves sum-chunk partials, then nworkers worker partials (block + single elements)
-  double* bcast;      // [0]: factor decided inside the fused kernel
+  uint64_t* bcast;    // [0]: the decision of the fused kernel, published by value (kUndecided between launches)
   uint32_t* sync;     // kSyncWords counters (see above)
   uint32_t* bstate;   // nworkers: whether each block was handed back by the fused kernel
   uint64_t nvec, rb, sb, cvs;

@@ -320,6 +320,7 @@ __global__ __launch_bounds__(kThreads) void k_tensor_clip(TensorPlan T, AvgSrc a
         break;
       }
     }
+    if (in_time) acquire_agent();  // every counted tensor stored its sum before its count
   }
   __syncthreads();
   if (!in_time) {
@@ -407,6 +408,7 @@ __global__ __launch_bounds__(kThreads) void k_tensor_gather(TensorPlan T, AvgSrc
         break;
       }
     }
+    if (in_time) acquire_agent();  // every counted tensor stored its sum before its count
   }
   __syncthreads();
   if (!in_time) {

@@ -115,8 +115,10 @@ enum {
    * device load) and gave up.  The list's figures in the result block are
    * not complete.  Without the stop switch every tensor's figures and its
    * scaling still are; with it nothing is written, and the per-tensor factors
-   * in the figures are not meaningful.  gclip_result_read returns
-   * GCLIP_EDEVICE. */
+   * in the figures are not meaningful.  A gclip_scale or gclip_adamw_step
+   * that follows on the same block (the split path of gclip_accumulate_clip_
+   * is one) then writes nothing: after gclip_accumulate_clip_ the buffer
+   * holds the sums, unscaled.  gclip_result_read returns GCLIP_EDEVICE. */
   GCLIP_DEVICE_WAIT_TIMEOUT = 1
 };
 
@@ -219,7 +221,11 @@ gclip_status gclip_norm(gclip_list* list, double avg_factor, gclip_result* d_res
  *   max_norm     c > 0, not NaN; +inf means never clip
  *   avg_factor   the same a given to gclip_norm
  *   error_if_nonfinite  nonzero: a NaN/Inf element stops the update
- * Writes scale, clipped, skipped, max_norm and decided = 1 into d_result. */
+ * Writes scale, clipped, skipped, max_norm and decided = 1 into d_result.
+ * When d_result->status != 0 (the norm before it reported a failure, e.g.
+ * GCLIP_DEVICE_WAIT_TIMEOUT, so sumsq and nonfinite are not this step's) it
+ * decides nothing, writes no gradient and leaves d_result as it is; a block
+ * the caller fills in must therefore hold status 0. */
 gclip_status gclip_scale(gclip_list* list, double max_norm, double avg_factor, int32_t error_if_nonfinite,
                          gclip_result* d_result, void* stream);
 
@@ -291,7 +297,9 @@ gclip_status gclip_adamw_destroy(gclip_adamw* opt);
  * max_norm and decided = 1 into d_result; then, unless skipped (a NaN/Inf
  * gradient with error_if_nonfinite: weights and moments stay bitwise
  * unchanged), updates every weight and both moments with g = s * grad.  The
- * gradients are only read.  One kernel launch, no allocation, no sync. */
+ * gradients are only read.  As gclip_scale, it takes no step and leaves
+ * d_result as it is when d_result->status != 0.  One kernel launch, no
+ * allocation, no sync. */
 gclip_status gclip_adamw_step(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm, double avg_factor,
                               int32_t error_if_nonfinite, gclip_result* d_result, void* stream);
 
@@ -456,7 +464,8 @@ gclip_status gclip_clip_amp_(gclip_list* list, double max_norm, double n_microba
 
 /* gclip_adamw_step with a = 1 / (n_microbatches * S) and error_if_nonfinite
  * on (found-inf: weights and moments stay unchanged), then the loss-scale
- * update.  To follow gclip_norm_amp over the same gradients and d_amp. */
+ * update (none when d_result->status != 0: no step was taken).  To follow
+ * gclip_norm_amp over the same gradients and d_amp. */
 gclip_status gclip_adamw_step_amp(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm,
                                   double n_microbatches, gclip_amp_state* d_amp, const gclip_amp_params* amp,
                                   gclip_result* d_result, void* stream);

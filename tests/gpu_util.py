@@ -58,15 +58,26 @@ def elem_mismatches(gpu, ref, dtype):
     return bad
 
 
+def _bits(a):
+    return a.view(np.uint32 if a.itemsize == 4 else np.uint16)
+
+
 def assert_elems_close(gpu_list, ref_list, dtype, what=""):
+    """Every element of every tensor within tolerance.  Elements whose bits
+    equal the oracle's pass at once; only the others go through the
+    tolerance test, so lists of several GB compare in seconds."""
     nbad, first = 0, None
     for t, (g, r) in enumerate(zip(gpu_list, ref_list)):
         assert g.shape == r.shape
-        bad = elem_mismatches(g, r, dtype)
+        g1, r1 = g.reshape(-1), r.reshape(-1)
+        idx = np.flatnonzero(_bits(g1) != _bits(r1))
+        if idx.size == 0:
+            continue
+        bad = elem_mismatches(g1[idx], r1[idx], dtype)
         k = int(bad.sum())
         if k and first is None:
-            i = int(np.argmax(bad))
-            first = (t, i, values(g[i:i + 1], dtype)[0], values(r[i:i + 1], dtype)[0])
+            i = int(idx[np.argmax(bad)])
+            first = (t, i, values(g1[i:i + 1], dtype)[0], values(r1[i:i + 1], dtype)[0])
         nbad += k
     assert nbad == 0, f"{what}: {nbad} elements outside tolerance, first (tensor, index, gpu, oracle) = {first}"
 

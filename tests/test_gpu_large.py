@@ -5,9 +5,9 @@ clip.
 The 4.3 GB bf16 tensor exercises 64-bit byte offsets in every walk, the
 nontemporal-store variants (lists of 1 GiB and more), and the per-tensor
 reduction over more partials than it stages in LDS at once (~65,500
-pieces, six windows).  Outputs are compared at sampled positions (both
-ends of every tensor and one element in a thousand) with the oracle's
-rounding of g*s; the norms against the oracle's sums over every element."""
+pieces, six windows).  Every output element is compared with the oracle's
+(the oracle's reference is computed once per list and compared tensor by
+tensor); the norms against the oracle's sums over every element."""
 import math
 
 import numpy as np
@@ -35,40 +35,21 @@ def _G():
     return G
 
 
-def sample_indices(n, rng, k=256, frac=1e-3):
-    idx = np.concatenate([np.arange(min(k, n)), np.arange(max(0, n - k), n),
-                          rng.integers(0, n, size=int(n * frac)) if n > 0 else np.zeros(0, dtype=np.int64)])
-    return np.unique(idx)
-
-
-def gather(t, idx, dtype):
-    """Storage bits of device tensor t at idx (only those cross to the host)."""
-    import torch
-    sel = t[torch.from_numpy(idx).to(t.device)]
-    return gu.download([sel], dtype)[0]
-
-
-def check_sampled(arrays, ts, dtype, scales, rng, what, before=None):
-    """Sampled outputs of ts against arrays[k] scaled by scales[k]; on a
-    mismatch the message shows the first bad elements with the unscaled
-    value and, if given, what the tensor held before the call."""
-    for k, (a, t, s) in enumerate(zip(arrays, ts, scales)):
-        idx = sample_indices(a.size, rng)
-        got = gather(t, idx, dtype)
-        ref = [a[idx].copy()]
-        if s != 1.0:
-            oracle.scale_(ref, dtype, s)
-        bad = gu.elem_mismatches(got, ref[0], dtype)
-        if bad.any():
-            rows = []
-            for i in np.flatnonzero(bad)[:6]:
-                row = (f"[{int(idx[i])}] got {gu.values(got[i:i + 1], dtype)[0]!r} want "
-                       f"{gu.values(ref[0][i:i + 1], dtype)[0]!r} unscaled {gu.values(a[idx[i]:idx[i] + 1], dtype)[0]!r}")
-                if before is not None:
-                    row += f" before {gu.values(before[k][idx[i]:idx[i] + 1], dtype)[0]!r}"
-                rows.append(row)
-            raise AssertionError(f"{what}: tensor {k}, {int(bad.sum())} of {idx.size} sampled elements off: "
-                                 + "; ".join(rows))
+def check_all(ref, ts, dtype, what, before=None):
+    """Every element of the device tensors ts against the oracle's ref, one
+    tensor at a time; on a mismatch the message shows the first bad elements
+    and, if given, what the tensor held before the call."""
+    for k, (rf, t) in enumerate(zip(ref, ts)):
+        got = gu.download([t], dtype)[0]
+        try:
+            gu.assert_elems_close([got], [rf], dtype, f"{what}: tensor {k}")
+        except AssertionError as e:
+            idx = np.flatnonzero(gu.elem_mismatches(got, rf, dtype))[:6]
+            rows = [f"[{int(i)}] got {gu.values(got[i:i + 1], dtype)[0]!r} want {gu.values(rf[i:i + 1], dtype)[0]!r}"
+                    + (f" before {gu.values(before[k][i:i + 1], dtype)[0]!r}" if before is not None else "")
+                    for i in idx]
+            raise AssertionError(f"{e}; " + "; ".join(rows)) from None
+        del got
 
 
 @pytest.fixture(scope="module")
@@ -93,6 +74,8 @@ def test_over_4gib_tensor(big_list):
     assert gl.info()["n_bytes"] > (1 << 32)
     s, clipped, _ = oracle.decide(n_ref, False, 1.0)
     assert clipped
+    ref = [a.copy() for a in arrays]
+    oracle.scale_(ref, "bf16", s)
     for path in ("fused", "split"):
         for t, p in zip(ts, pristine):
             t.copy_(p)
@@ -101,20 +84,22 @@ def test_over_4gib_tensor(big_list):
         st, r = gl.read()
         assert st == 0 and r["status"] == 0 and r["clipped"] and not r["nonfinite"], (path, r)
         gu.assert_norm_close(r["norm"], n_ref, f"4 GiB {path}")
-        check_sampled(arrays, ts, "bf16", [s] * 3, np.random.default_rng(5), f"4 GiB clip {path}")
+        check_all(ref, ts, "bf16", f"4 GiB clip {path}")
+    del ref
     # every tensor by its own norm: ~65,500 pieces, staged in several windows
     for t, p in zip(ts, pristine):
         t.copy_(p)
     gl.clip_per_tensor_(0.05)
     st, r = gl.read()
     tr = gl.read_tensors()
-    scales = []
+    ref = [a.copy() for a in arrays]
     for k, ps in enumerate(per):
         gu.assert_norm_close(float(tr[k]["sumsq"]), ps, f"4 GiB per-tensor sumsq {k}")
         sk, ck, _ = oracle.decide(math.sqrt(ps), False, 0.05)
         assert bool(tr[k]["clipped"]) == ck, k
-        scales.append(sk)
-    check_sampled(arrays, ts, "bf16", scales, np.random.default_rng(6), "4 GiB per-tensor clip")
+        oracle.scale_(ref[k:k + 1], "bf16", sk)
+    check_all(ref, ts, "bf16", "4 GiB per-tensor clip")
+    del ref
     gl.close()
     del pristine
     torch.cuda.empty_cache()
@@ -124,10 +109,10 @@ def test_over_4gib_tensor(big_list):
 @pytest.mark.parametrize("dtype", ("f32", "f16"))
 def test_over_1gib_accumulate_fused(dtype):
     """The one-launch += with the clip on a list of more than 1 GiB (its
-    nontemporal-store variant): the sums at sampled positions scaled by the
-    oracle's decision.  Its scaling pass reads sums that other workgroups,
-    on other XCDs, wrote in its summing pass: a missing release or acquire
-    between the two shows here as stale elements."""
+    nontemporal-store variant): every element against the oracle's sums
+    scaled by its decision.  Its scaling pass reads sums that other
+    workgroups, on other XCDs, wrote in its summing pass: a missing release
+    or acquire between the two shows here as stale elements."""
     import torch
     G = _G()
     if dtype == "f32":
@@ -152,8 +137,8 @@ def test_over_1gib_accumulate_fused(dtype):
     s, clipped, _ = oracle.decide(n_ref, nf, 1.0, 0.5)
     assert clipped and r["clipped"] and st == 0
     gu.assert_norm_close(r["norm"], n_ref, f"1 GiB += {dtype}")
-    check_sampled(summed, ta, dtype, [s] * 3, np.random.default_rng(7), f"1 GiB += with the clip, {dtype}",
-                  before=acc)
+    oracle.scale_(summed, dtype, s)
+    check_all(summed, ta, dtype, f"1 GiB += with the clip, {dtype}", before=acc)
     c.close()
     gl.close()
     del ta, tc
