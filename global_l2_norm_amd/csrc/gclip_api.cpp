@@ -21,37 +21,7 @@
 #include "../../include/gclip.h"
 #include "gclip_plan.hpp"
 
-namespace gclip {
-int worker_threads();
-uint64_t resident_cap_vectors();
-ChunkShape chunk_shape();
-hipError_t launch_norm(const DevPlan& p, int32_t dtype, AvgSrc avg, gclip_result* res, hipStream_t st);
-hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
-                        hipStream_t st);
-hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
-                        uint64_t wait_ticks, AmpUpdate amp, hipStream_t st);
-hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu);
-hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,
-                        gclip_result* res, hipStream_t st);
-hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,
-                             int32_t interval, hipStream_t s);
-hipError_t launch_tensor_norm(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int clip, int err,
-                              gclip_tensor_result* out, gclip_result* res, hipStream_t st);
-hipError_t launch_tensor_scale(const TensorPlan& T, int32_t dtype, gclip_tensor_result* out,
-                               const gclip_result* res, hipStream_t st);
-hipError_t launch_tensor_clip(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm,
-                              gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, hipStream_t st);
-hipError_t launch_accumulate_norm(const TensorPlan& T, int32_t dtype, const uint64_t* gdelta, AvgSrc avg,
-                                  gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, bool gather,
-                                  hipStream_t st);
-hipError_t launch_tensor_norms(const TensorPlan& T, int32_t dtype, AvgSrc avg, gclip_tensor_result* out,
-                               gclip_result* res, uint64_t wait_ticks, bool gather, hipStream_t st);
-hipError_t launch_tensor_decisions(const TensorPlan& T, int32_t dtype, AvgSrc avg, double max_norm, int err,
-                                   gclip_tensor_result* out, gclip_result* res, uint64_t wait_ticks, bool gather,
-                                   hipStream_t st);
-hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, double max_norm, AvgSrc avg,
-                              int err, gclip_result* res, uint64_t wait_ticks, hipStream_t st);
-}  // namespace gclip
+#include "gclip_host.hpp"
 
 // How long a workgroup of the fused kernel waits at the grid-wide decision
 // before it hands its block back.  On an idle device the last workgroup
@@ -104,16 +74,12 @@ namespace {
 
 thread_local int32_t g_last_hip = 0;
 
-gclip_status hip_fail(hipError_t e) {
-  g_last_hip = (int32_t)e;
-  return GCLIP_EHIP;
-}
-
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-bool factor_ok(double a) { return std::isfinite(a) && a > 0.0; }
-bool threshold_ok(double c) { return !std::isnan(c) && c > 0.0; }
-bool result_ptr_ok(const gclip_result* r) { return r && reinterpret_cast<uintptr_t>(r) % 8 == 0; }
+using gclip::factor_ok;
+using gclip::hip_fail;
+using gclip::result_ptr_ok;
+using gclip::threshold_ok;
 
 // Device check of a hot call (argument values are checked before this).
 gclip_status check_device(const gclip_list* list) {
@@ -154,6 +120,11 @@ void adamw_pieces(const uint64_t* p, const uint64_t* g, const uint64_t* m, const
 bool unit_interval(double b) { return std::isfinite(b) && b >= 0.0 && b < 1.0; }
 
 }  // namespace
+
+gclip_status gclip::hip_fail(hipError_t e) {
+  g_last_hip = (int32_t)e;
+  return GCLIP_EHIP;
+}
 
 extern "C" {
 
@@ -278,22 +249,14 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     }
     const gclip::HostPlan& P = L->plan;
     const size_t ntp = L->tplan.pieces.size(), ntf = L->tplan.first.size();
-    const size_t nseg = (size_t)P.nseg(), nw = (size_t)P.nworkers, nsc = (size_t)P.nsc(), nch = (size_t)P.nchunk();
-    const size_t nchs = (size_t)P.nchunk_streamed(), nsum = (size_t)P.nsum();
-    const size_t waves = (size_t)gclip::worker_threads() / 64;
-    const size_t A = 256;
-    size_t off = 0;
+    const gclip::PlanLayout PL = gclip::plan_layout(P, gclip::worker_threads() / 64);
+    size_t off = PL.bytes;
     auto take = [&](size_t bytes) {
       const size_t at = off;
-      off = round_up(off + (bytes ? bytes : 8), A);
+      off = round_up(off + (bytes ? bytes : 8), 256);
       return at;
     };
-    const size_t o_segv = take((nseg + 1) * 8), o_sega = take(nseg * 8), o_blk = take(nw * 4),
-                 o_splv = take((nch + 1) * 8), o_spls = take(nch * 4), o_fusv = take((nchs + 1) * 8),
-                 o_fuss = take(nchs * 4), o_sum = take(nsum * 4), o_wksc = take((nw + 1) * 8),
-                 o_sca = take(nsc * 8), o_part = take((nsum * waves + nw) * 8), o_bc = take(8),
-                 o_sync = take((size_t)gclip::kSyncWords * 4), o_bst = take(nw * 4),
-                 o_tpc = take(ntp * sizeof(gclip::TPiece)), o_tfi = take(ntf * 4), o_tpa = take(ntp * 8),
+    const size_t o_tpc = take(ntp * sizeof(gclip::TPiece)), o_tfi = take(ntf * 4), o_tpa = take(ntp * 8),
                  o_tsc = take((size_t)P.n_tensors * sizeof(gclip_tensor_result)),
                  o_tsum = take((size_t)P.n_tensors * 8), o_tsy = take(128);
     if ((e = hipMalloc(&L->blob, off)) != hipSuccess) {
@@ -301,48 +264,22 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       g_last_hip = (int32_t)e;
       return GCLIP_ENOMEM;
     }
-    char* b = static_cast<char*>(L->blob);
+    unsigned char* b = static_cast<unsigned char*>(L->blob);
     auto up = [&](size_t o, const void* src, size_t bytes) -> hipError_t {
       if (bytes == 0) return hipSuccess;
       return hipMemcpy(b + o, src, bytes, hipMemcpyHostToDevice);
     };
-    if ((e = hipMemset(L->blob, 0, off)) != hipSuccess || (e = up(o_segv, P.seg_vbegin.data(), (nseg + 1) * 8)) ||
-        (e = up(o_sega, P.seg_addr.data(), nseg * 8)) || (e = up(o_blk, P.blk_seg.data(), nw * 4)) ||
-        (e = up(o_splv, P.spl_vb.data(), (nch + 1) * 8)) || (e = up(o_spls, P.spl_seg.data(), nch * 4)) ||
-        (e = up(o_fusv, P.fus_vb.data(), (nchs + 1) * 8)) || (e = up(o_fuss, P.fus_seg.data(), nchs * 4)) || (e = up(o_sum, P.sum_seg.data(), nsum * 4)) || (e = up(o_wksc, P.wk_scbegin.data(), (nw + 1) * 8)) ||
-        (e = up(o_sca, P.sc_addr.data(), nsc * 8)) ||
+    std::vector<unsigned char> image(PL.header);
+    gclip::plan_image(P, PL, image.data());
+    if ((e = hipMemset(L->blob, 0, off)) != hipSuccess || (e = up(0, image.data(), PL.header)) ||
         (e = up(o_tpc, L->tplan.pieces.data(), ntp * sizeof(gclip::TPiece))) ||
-        (e = up(o_tfi, L->tplan.first.data(), ntf * 4)) || (e = up(o_bc, &gclip::kUndecided, 8)) ||
-        (e = hipDeviceSynchronize()) != hipSuccess) {
+        (e = up(o_tfi, L->tplan.first.data(), ntf * 4)) || (e = hipDeviceSynchronize()) != hipSuccess) {
       (void)hipFree(L->blob);
       delete L;
       return hip_fail(e);
     }
-    gclip::DevPlan& D = L->dev;
-    D.seg_vbegin = reinterpret_cast<const uint64_t*>(b + o_segv);
-    D.seg_addr = reinterpret_cast<const uint64_t*>(b + o_sega);
-    D.blk_seg = reinterpret_cast<const uint32_t*>(b + o_blk);
-    D.spl_vb = reinterpret_cast<const uint64_t*>(b + o_splv);
-    D.spl_seg = reinterpret_cast<const uint32_t*>(b + o_spls);
-    D.fus_vb = reinterpret_cast<const uint64_t*>(b + o_fusv);
-    D.fus_seg = reinterpret_cast<const uint32_t*>(b + o_fuss);
-    D.sum_seg = reinterpret_cast<const uint32_t*>(b + o_sum);
-    D.wk_scbegin = reinterpret_cast<const uint64_t*>(b + o_wksc);
-    D.sc_addr = reinterpret_cast<const uint64_t*>(b + o_sca);
-    D.partials = reinterpret_cast<double*>(b + o_part);
-    D.bcast = reinterpret_cast<uint64_t*>(b + o_bc);
-    D.sync = reinterpret_cast<uint32_t*>(b + o_sync);
-    D.bstate = reinterpret_cast<uint32_t*>(b + o_bst);
-    D.nvec = P.nvec();
-    D.rb = P.rb;
-    D.sb = P.sb;
-    D.nchunk = (uint32_t)nch;
-    D.nchs = (uint32_t)nchs;
-    D.nsum = (uint32_t)nsum;
-    D.nt_store = P.n_bytes >= gclip::kNtStoreMinBytes ? 1u : 0u;
-    D.cvs = P.cvs;
-    D.nworkers = P.nworkers;
-    D.nseg = (int32_t)nseg;
+    L->dev = gclip::plan_view(P, PL, b);
+    const gclip::DevPlan& D = L->dev;
     gclip::TensorPlan& T = L->tdev;
     T.pieces = reinterpret_cast<const gclip::TPiece*>(b + o_tpc);
     T.first = reinterpret_cast<const uint32_t*>(b + o_tfi);

@@ -3,6 +3,7 @@
 #include "gclip_plan.hpp"
 
 #include <algorithm>
+#include <cstring>
 #include <utility>
 
 namespace gclip {
@@ -164,6 +165,84 @@ int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t 
   for (int32_t w = 0; w <= nworkers; ++w) p.wk_scbegin[(size_t)w] = share_begin(ns, nworkers, w);
   out = std::move(p);
   return 0;
+}
+
+PlanLayout plan_layout(const HostPlan& p, int waves) {
+  const size_t nseg = (size_t)p.nseg(), nw = (size_t)p.nworkers, nsc = (size_t)p.nsc(), nch = (size_t)p.nchunk();
+  const size_t nchs = (size_t)p.nchunk_streamed(), nsum = (size_t)p.nsum();
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = (off + (bytes ? bytes : 8) + 255) / 256 * 256;
+    return at;
+  };
+  PlanLayout L;
+  L.segv = take((nseg + 1) * 8);
+  L.sega = take(nseg * 8);
+  L.blk = take(nw * 4);
+  L.splv = take((nch + 1) * 8);
+  L.spls = take(nch * 4);
+  L.fusv = take((nchs + 1) * 8);
+  L.fuss = take(nchs * 4);
+  L.sum = take(nsum * 4);
+  L.wksc = take((nw + 1) * 8);
+  L.sca = take(nsc * 8);
+  L.bc = take(8);
+  L.sync = take((size_t)kSyncWords * 4);
+  L.bst = take(nw * 4);
+  L.header = off;
+  L.part = take((nsum * (size_t)waves + nw) * 8);
+  L.bytes = off;
+  return L;
+}
+
+void plan_image(const HostPlan& p, const PlanLayout& L, unsigned char* img) {
+  std::memset(img, 0, L.header);
+  auto put = [&](size_t o, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(img + o, src, bytes);
+  };
+  const size_t nseg = (size_t)p.nseg(), nw = (size_t)p.nworkers, nsc = (size_t)p.nsc(), nch = (size_t)p.nchunk();
+  const size_t nchs = (size_t)p.nchunk_streamed(), nsum = (size_t)p.nsum();
+  put(L.segv, p.seg_vbegin.data(), (nseg + 1) * 8);
+  put(L.sega, p.seg_addr.data(), nseg * 8);
+  put(L.blk, p.blk_seg.data(), nw * 4);
+  put(L.splv, p.spl_vb.data(), (nch + 1) * 8);
+  put(L.spls, p.spl_seg.data(), nch * 4);
+  put(L.fusv, p.fus_vb.data(), (nchs + 1) * 8);
+  put(L.fuss, p.fus_seg.data(), nchs * 4);
+  put(L.sum, p.sum_seg.data(), nsum * 4);
+  put(L.wksc, p.wk_scbegin.data(), (nw + 1) * 8);
+  put(L.sca, p.sc_addr.data(), nsc * 8);
+  put(L.bc, &kUndecided, 8);
+}
+
+DevPlan plan_view(const HostPlan& p, const PlanLayout& L, unsigned char* b) {
+  DevPlan D{};
+  D.seg_vbegin = reinterpret_cast<const uint64_t*>(b + L.segv);
+  D.seg_addr = reinterpret_cast<const uint64_t*>(b + L.sega);
+  D.blk_seg = reinterpret_cast<const uint32_t*>(b + L.blk);
+  D.spl_vb = reinterpret_cast<const uint64_t*>(b + L.splv);
+  D.spl_seg = reinterpret_cast<const uint32_t*>(b + L.spls);
+  D.fus_vb = reinterpret_cast<const uint64_t*>(b + L.fusv);
+  D.fus_seg = reinterpret_cast<const uint32_t*>(b + L.fuss);
+  D.sum_seg = reinterpret_cast<const uint32_t*>(b + L.sum);
+  D.wk_scbegin = reinterpret_cast<const uint64_t*>(b + L.wksc);
+  D.sc_addr = reinterpret_cast<const uint64_t*>(b + L.sca);
+  D.partials = reinterpret_cast<double*>(b + L.part);
+  D.bcast = reinterpret_cast<uint64_t*>(b + L.bc);
+  D.sync = reinterpret_cast<uint32_t*>(b + L.sync);
+  D.bstate = reinterpret_cast<uint32_t*>(b + L.bst);
+  D.nvec = p.nvec();
+  D.rb = p.rb;
+  D.sb = p.sb;
+  D.cvs = p.cvs;
+  D.nchunk = (uint32_t)p.nchunk();
+  D.nchs = (uint32_t)p.nchunk_streamed();
+  D.nsum = (uint32_t)p.nsum();
+  D.nt_store = p.n_bytes >= kNtStoreMinBytes ? 1u : 0u;
+  D.nworkers = p.nworkers;
+  D.nseg = (int32_t)p.nseg();
+  return D;
 }
 
 int tensor_plan_build(const HostPlan& p, uint32_t piece_vectors, TensorHostPlan& out) {

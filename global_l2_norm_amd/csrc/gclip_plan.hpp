@@ -138,6 +138,28 @@ struct DevPlan {
   int32_t nseg;
 };
 
+// Where a plan's tables and workspace lie in one device allocation (byte
+// offsets, each 256-byte aligned).  [0, header) holds the tables and the
+// workspace words that must hold their initial value when a launch starts
+// (the decision word, the counters, the block states); the partials follow,
+// up to `bytes`, and need no initial value (every launch writes each one
+// before it is read).
+struct PlanLayout {
+  size_t segv, sega, blk, splv, spls, fusv, fuss, sum, wksc, sca, bc, sync, bst, part;
+  size_t header;
+  size_t bytes;
+};
+
+// The layout of plan p for workgroups of `waves` wave64s.
+PlanLayout plan_layout(const HostPlan& p, int waves);
+
+// The host image of [0, L.header): every table, the decision word undecided,
+// counters and block states zero.  img must hold L.header bytes.
+void plan_image(const HostPlan& p, const PlanLayout& L, unsigned char* img);
+
+// The device view of plan p laid out by L at device address base.
+DevPlan plan_view(const HostPlan& p, const PlanLayout& L, unsigned char* base);
+
 // The averaging factor of a call: a itself, or, for a loss-scaled step,
 // 1 / (a * S) with a = n_microbatches and the binary32 loss scale S read from
 // device memory when the kernel starts.

@@ -3,6 +3,7 @@ include/gclip.h declares; argument errors come back before any GPU work; the
 descriptor table covers every element exactly once, in balanced shares; and
 the kernels' own address walk, replayed on the host, stays inside the
 tensors and visits every byte once per pass."""
+import glob
 import os
 import re
 import subprocess
@@ -16,13 +17,16 @@ from synth import gradsets as gs
 from tests.abi_util import ESIZE, TAG, check_walk, fake_layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gclip.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gclip_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(gclip_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
