@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(HERE, "libgclip.so")
 
 GCLIP_F32, GCLIP_F16, GCLIP_BF16 = 0, 1, 2
 GCLIP_OK, GCLIP_EINVAL, GCLIP_EDTYPE, GCLIP_ENOMEM, GCLIP_EHIP, GCLIP_ENONFINITE, GCLIP_EDEVICE, GCLIP_ERANGE = range(8)
+GCLIP_NOALLOC_SCRATCH_BYTES = 4 << 20
 GCLIP_PATH_AUTO, GCLIP_PATH_FUSED, GCLIP_PATH_SPLIT = 0, 1, 2
 
 STATUS_NAMES = {GCLIP_OK: "GCLIP_OK", GCLIP_EINVAL: "GCLIP_EINVAL", GCLIP_EDTYPE: "GCLIP_EDTYPE",
@@ -96,6 +97,7 @@ def _declare(lib):
         "gclip_clip_amp_": ([vp, dbl, dbl, vp, ctypes.POINTER(GclipAmpParams), vp, vp], i32),
         "gclip_adamw_step_amp": ([vp, ctypes.POINTER(GclipAdamwHparams), dbl, dbl, vp,
                                   ctypes.POINTER(GclipAmpParams), vp, vp], i32),
+        "gclip_clip_noalloc_": ([ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32, dbl, dbl, i32, vp, vp], i32),
         "gclip_status_string": ([i32], ctypes.c_char_p),
         "gclip_last_hip_error": ([], i32),
         "gclip_version": ([], i32),
@@ -132,4 +134,4 @@ EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_
            "gclip_last_hip_error", "gclip_version", "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step",
            "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp", "gclip_tensor_norms",
            "gclip_clip_per_tensor_", "gclip_contrib_create", "gclip_contrib_destroy", "gclip_accumulate_norm",
-           "gclip_accumulate_clip_", "gclip_set_gather_wait")
+           "gclip_accumulate_clip_", "gclip_set_gather_wait", "gclip_clip_noalloc_")

@@ -141,7 +141,7 @@ const char* gclip_status_string(int32_t status) {
     case GCLIP_EHIP: return "HIP runtime error";
     case GCLIP_ENONFINITE: return "non-finite gradient element";
     case GCLIP_EDEVICE: return "device-side failure";
-    case GCLIP_ERANGE: return "output buffer too small";
+    case GCLIP_ERANGE: return "size out of range (a query buffer too small, or a list too large for a fixed scratch)";
     default: return "unknown status";
   }
 }

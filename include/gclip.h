@@ -73,7 +73,8 @@ typedef enum gclip_status {
   GCLIP_EHIP = 4,       /* a HIP runtime call failed; gclip_last_hip_error() holds its code */
   GCLIP_ENONFINITE = 5, /* gclip_result_read: a NaN/Inf element was seen and the caller asked to stop */
   GCLIP_EDEVICE = 6,    /* gclip_result_read: the kernels reported a failure (result.status != 0) */
-  GCLIP_ERANGE = 7      /* a buffer given to a query function is too small */
+  GCLIP_ERANGE = 7      /* a buffer given to a query function is too small, or a list too large for
+                           gclip_clip_noalloc_'s fixed scratch */
 } gclip_status;
 
 /* Which kernels gclip_clip_ uses (gclip_list_set_path). */
@@ -469,6 +470,40 @@ gclip_status gclip_clip_amp_(gclip_list* list, double max_norm, double n_microba
 gclip_status gclip_adamw_step_amp(gclip_adamw* opt, const gclip_adamw_hparams* hp, double max_norm,
                                   double n_microbatches, gclip_amp_state* d_amp, const gclip_amp_params* amp,
                                   gclip_result* d_result, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * For callers that cannot allocate device memory: serving loops and
+ * harnesses that forbid hipMalloc.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the static device array, one per GPU, that holds the descriptor
+ * table and workspace of gclip_clip_noalloc_. */
+#define GCLIP_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* gclip_list_create + gclip_clip_ + gclip_list_destroy in one call that
+ * allocates no device memory: the list's descriptor table and workspace go
+ * into a static device array of GCLIP_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends.  Arguments as
+ * gclip_list_create (d_ptrs, numels, n_tensors, dtype) and gclip_clip_
+ * (max_norm, avg_factor, error_if_nonfinite, d_result, stream); the same
+ * kernels run on the same table, so the result block and the gradients come
+ * out bit for bit as from those calls.  Each call builds the table in host
+ * memory and copies it into this GPU's array with one hipMemcpyAsync on
+ * `stream` (from pageable memory: it returns once the copy is staged), then
+ * enqueues the kernels; it never synchronises the device.
+ * Limits and errors: a list whose table and workspace need more than
+ * GCLIP_NOALLOC_SCRATCH_BYTES -- a list of more than about 20 GB, or fewer
+ * bytes with very many tensors or many elements handled one by one (8 bytes
+ * of table each) -- is rejected with GCLIP_ERANGE; argument errors as the
+ * two calls; nothing is enqueued on any error.
+ * Every call on one GPU shares its array, which keeps the last call's
+ * contents (each call rewrites what it reads): calls that overlap in time on
+ * one GPU -- on two streams, or from two host threads -- race, and the caller
+ * must order them.  Not for HIP graph capture (the copy is from pageable
+ * memory). */
+gclip_status gclip_clip_noalloc_(void* const* d_ptrs, const int64_t* numels, int32_t n_tensors, int32_t dtype,
+                                 double max_norm, double avg_factor, int32_t error_if_nonfinite,
+                                 gclip_result* d_result, void* stream);
 
 /* Describe, without touching any GPU, how a list would be split: the runs
  * of each worker, in the order the kernels visit them.  Addresses only need
