@@ -9,7 +9,10 @@ cache holds the list (a read, so no dirty lines are left to drain into the
 timed call).  Each step is bracketed by HIP events on the stream the kernels
 run on; value = algorithmic bytes / mean event time, where the algorithmic
 bytes are N*s read by the norm pass plus 2*N*s read and written by the scale
-pass.
+pass.  The same run times the library's reference kernels (include/
+gclip_ref.h: a plain read and a plain in-place copy of the same number of
+bytes, cold) for the attainable rate of those two passes, the same steps
+warm (no flush), and the oracle on the host's cores.
 
 Prints one JSON line.  Other modes:
   --config NAME        another synthetic set (synth.gradsets.CONFIGS)
@@ -17,6 +20,7 @@ Prints one JSON line.  Other modes:
   --path adamw|amp     the clip fused into AdamW; the loss-scaled clip
   --path per_tensor    per-tensor clipping and per-tensor norms
   --path accum         the last microbatch's += fused with the norm pass
+  --path ref           the reference kernels alone, at the workloads' sizes
   --profile-pass       a short run for rocprofv3 (no CPU baseline, plus a
                        calibration copy of known size for the PMC counters)
   --summarize-rocprof  turn rocprofv3 output into the summaries kept in
@@ -45,7 +49,10 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ["global_l2_norm_amd/csrc/gclip_kernels.hip", "global_l2_norm_amd/csrc/gclip_cursor.hpp",
                   "global_l2_norm_amd/csrc/gclip_device.hpp", "global_l2_norm_amd/csrc/gclip_plan.hpp",
                   "global_l2_norm_amd/csrc/gclip_plan.cpp", "global_l2_norm_amd/csrc/gclip_api.cpp"]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_grad_clip_fused__andrea120m_f32__pmc.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+# byte sizes of the workloads' lists: 120M fp16, 120M fp32, twice that, and 1.3B bf16
+REF_SIZES = [184_496_640, 368_993_280, 737_986_560, 2_622_365_696]
+CPU_REPS = 5
 WORKLOADS = {
     "andrea120m_f32": "ANDREA-120M-shaped fp32 gradient list: 124 tensors (tok_embed [8449,768], pos_embed "
                       "[1024,768], 12 blocks of W_Q/W_K/W_V/W_O [768,768], W_1 [768,3072], W_2 [3072,768], four "
@@ -86,13 +93,19 @@ def algorithmic_bytes(numel, esize, wrote):
     return numel * esize * (3 if wrote else 1)
 
 
-def read_traffic(numel_bytes_alg):
-    """HBM bytes per launch from the committed PMC summary, or None when it
-    is missing or was taken on other kernel source."""
-    if not os.path.exists(PMC_SUMMARY):
+def pmc_summary_path(kernels, config):
+    return os.path.join(PROFILES, f"{kernels}__{config}__pmc.txt")
+
+
+def read_traffic(kernels, config):
+    """HBM bytes per step of the given kernel(s) ('a+b' for a two-kernel
+    path) from the committed PMC summary, or None when it is missing or was
+    taken on other kernel source."""
+    path = pmc_summary_path(kernels, config)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PMC_SUMMARY):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -104,40 +117,120 @@ def read_traffic(numel_bytes_alg):
         return None
 
 
-def oracle_rate(run, restore, nbytes, sample, min_seconds=6.0):
-    """The oracle timed on this host: run() repeated (restore() before each,
-    untimed) for at least min_seconds; nbytes algorithmic bytes per run."""
-    reps, total = 0, 0.0
-    while total < min_seconds or reps == 0:
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_threads():
+    """Threads for the oracle's threaded leg: the cores this process may run
+    on, capped by OMP_NUM_THREADS where that is set (a machine's share of a
+    shared host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return max(1, min(n, cap) if cap > 0 else n)
+
+
+def oracle_rate(run, restore, nbytes, sample, reps=CPU_REPS):
+    """The oracle timed on this host: the median of `reps` runs of run()
+    (restore() before each, untimed); nbytes algorithmic bytes per run."""
+    times = []
+    for _ in range(reps):
         restore()
         t0 = time.perf_counter()
         run()
-        total += time.perf_counter() - t0
-        reps += 1
-    sec = total / reps
+        times.append(time.perf_counter() - t0)
+    sec = statistics.median(times)
     return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample}, {reps} rep(s), {sec:.2f} s each, single-threaded binary64 C"}
+            "sample": f"{sample}; median of {reps} reps, {sec:.2f} s each, single-threaded binary64 C",
+            "cpu_model": cpu_model()}
 
 
-def cpu_baseline(g, min_seconds=10.0):
-    """The oracle as it stands, on this host, on the same workload."""
+def cpu_baseline(g, reps=CPU_REPS):
+    """The oracle as it stands, on this host's cores, on the same workload:
+    norm, decision and scale of the whole list, the median of `reps` runs
+    with the list restored before each (untimed); on T threads (the list cut
+    into T runs of consecutive elements, oracle.clip_sharded_) and on one
+    thread (oracle.clip_)."""
     import oracle
-    reps, total = 0, 0.0
     work = [a.copy() for a in g.arrays]
-    while total < min_seconds or reps == 0:
-        for w, a in zip(work, g.arrays):
-            w[...] = a
-        t0 = time.perf_counter()
-        r = oracle.clip_(work, g.dtype, g.max_norm, g.avg_factor, g.error_if_nonfinite)
-        total += time.perf_counter() - t0
-        reps += 1
-    wrote = not (r["skipped"] or r["scale"] == 1.0)
     esize = 4 if g.dtype == "f32" else 2
-    sec = total / reps
-    return {"value": round(algorithmic_bytes(g.numel, esize, wrote) / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"the whole {g.name} list ({g.numel} elements), norm+decision+scale, {reps} rep(s), "
-                      f"{sec:.2f} s each, single-threaded binary64 C"}
+
+    def timed(threads):
+        times, r = [], None
+        for _ in range(reps):
+            for w, a in zip(work, g.arrays):
+                w[...] = a
+            t0 = time.perf_counter()
+            if threads == 1:
+                r = oracle.clip_(work, g.dtype, g.max_norm, g.avg_factor, g.error_if_nonfinite)
+            else:
+                r = oracle.clip_sharded_(work, g.dtype, g.max_norm, g.avg_factor, g.error_if_nonfinite, threads)
+            times.append(time.perf_counter() - t0)
+        return statistics.median(times), r
+
+    T = host_threads()
+    sec1, r = timed(1)
+    secT, _ = timed(T) if T > 1 else (sec1, r)
+    wrote = not (r["skipped"] or r["scale"] == 1.0)
+    alg = algorithmic_bytes(g.numel, esize, wrote)
+    return {"value": round(alg / secT / 1e9, 3), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": f"the whole {g.name} list ({g.numel} elements), norm+decision+scale, binary64 C; "
+                      f"{T} threads over {T} runs of consecutive elements; median of {reps} reps, "
+                      f"{secT:.3f} s each",
+            "statistic": f"median of {reps}", "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+            "single_thread": {"value": round(alg / sec1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "s_per_rep": round(sec1, 3)}}
+
+
+def ref_times(nbytes, reps, flush, stream, copy_too=True):
+    """Mean event time (ms) of the reference kernels over nbytes, cold: the
+    plain read, the in-place copy and (copy_too) the copy to a second buffer."""
+    import torch
+    from global_l2_norm_amd import _lib
+    n16 = (nbytes + 15) // 16 * 16
+    src = torch.ones(n16 // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src) if copy_too else None
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sp = stream.cuda_stream
+    runs = {"read": lambda: _lib.lib.gclip_ref_read(src.data_ptr(), n16, sink.data_ptr(), sp),
+            "in_place": lambda: _lib.lib.gclip_ref_copy(src.data_ptr(), src.data_ptr(), n16, sp)}
+    if copy_too:
+        runs["copy"] = lambda: _lib.lib.gclip_ref_copy(dst.data_ptr(), src.data_ptr(), n16, sp)
+    out = {}
+    for name, run in runs.items():
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps + 2)]
+        for e0, e1 in evs:
+            flush.sum()
+            e0.record(stream)
+            if run() != 0:
+                raise RuntimeError(f"gclip_ref {name} failed")
+            e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs[2:])
+    del src, dst
+    return n16, out
+
+
+def calibration_copy(flush):
+    """For the PMC counters: an elementwise kernel that reads and writes
+    exactly CALIBRATION_BYTES each (torch.neg), cold, three times."""
+    import torch
+    src = torch.full((CALIBRATION_BYTES // 4,), 3.0, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        flush.sum()
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -146,7 +239,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="andrea120m_f32")
-    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw", "amp", "per_tensor", "accum"],
+    ap.add_argument("--path", choices=["auto", "fused", "split", "adamw", "amp", "per_tensor", "accum", "ref"],
                     default="auto",
                     help="adamw: time the clip fused into an AdamW step (gclip_norm + gclip_adamw_step) "
                          "against gclip_clip_ followed by the same AdamW step; amp: time the loss-scaled "
@@ -154,13 +247,16 @@ def main():
                          "per_tensor: time the per-tensor clip (gclip_clip_per_tensor_) and the per-tensor "
                          "norms alone (gclip_tensor_norms); accum: time the last microbatch's += fused with the "
                          "clip (gclip_accumulate_clip_) on the four-microbatch list against torch's += followed "
-                         "by gclip_clip_")
+                         "by gclip_clip_; ref: the reference read and copy kernels at the workloads' sizes")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="a calibration copy of known size first (for PMC counters), then the run without the "
+                         "CPU baseline")
     ap.add_argument("--summarize-rocprof", nargs="+", metavar="ARG",
                     help="KIND OUT DIR...: KIND is 'trace' (a --kernel-trace --stats output dir) or 'pmc' "
-                         "(FETCH_SIZE dir, then WRITE_SIZE dir); OUT is the summary file to write")
+                         "(FETCH_SIZE dir, then WRITE_SIZE dir); OUT is the summary file to write, named "
+                         "KERNEL[+KERNEL]__CONFIG__KIND.txt")
     ap.add_argument("--rocprof-command", action="append", default=[],
                     help="with --summarize-rocprof: the command that produced each output dir (repeatable)")
     a = ap.parse_args()
@@ -181,15 +277,21 @@ def main():
         print("bench.py needs the GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if a.profile_pass:
+        a.no_cpu_baseline = True
+    # read-only flush: a sum over an int64 view (no cast, so no temporaries
+    # are written and no dirty lines are left to drain into the timed call)
+    flush = torch.ones((2 << 30) // 8, dtype=torch.int64, device="cuda")
+    if a.profile_pass:
+        calibration_copy(flush)
+    if a.path == "ref":
+        return bench_ref(a, flush)
     if a.path == "accum":
-        return bench_accum(a, G, gs)
+        return bench_accum(a, G, gs, flush)
     g = gs.make(a.config)
     esize = 4 if g.dtype == "f32" else 2
     tensors = upload(g.arrays, g.dtype)
     pristine = [t.clone() for t in tensors]
-    # read-only flush: a sum over an int64 view (no cast, so no temporaries
-    # are written and no dirty lines are left to drain into the timed call)
-    flush = torch.ones((2 << 30) // 8, dtype=torch.int64, device="cuda")
     gl = G.GradList(tensors)
     if a.path == "adamw":
         return bench_adamw(a, G, g, tensors, pristine, flush, gl)
@@ -203,50 +305,53 @@ def main():
     path_name = {1: "fused", 2: "split"}[info["path"]]
     stream = torch.cuda.current_stream()
 
-    def restore():
+    def restore(cold=True):
         for t, p in zip(tensors, pristine):
             t.copy_(p)
-        if not a.no_flush:
+        if cold:
             flush.sum()
 
-    if a.profile_pass:
-        # calibration for the PMC counters: an elementwise kernel that reads
-        # and writes exactly CALIBRATION_BYTES each (torch.neg), then a few clips
-        src = torch.full((CALIBRATION_BYTES // 4,), 3.0, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            flush.sum()
-            torch.neg(src, out=dst)
-        for _ in range(max(a.steps, 1)):
-            restore()
+    def timed_steps(cold):
+        for _ in range(a.warmup):
+            restore(cold)
             gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
         torch.cuda.synchronize()
-        st, r = gl.read()
-        print(json.dumps({"profile_pass": True, "config": a.config, "path": path_name, "steps": a.steps,
-                          "norm": r["norm"], "status": st}), flush=True)
-        return 0
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            restore(cold)
+            ev[i][0].record(stream)
+            gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in ev], time.perf_counter() - t0
 
-    for _ in range(a.warmup):
-        restore()
-        gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    for i in range(a.steps):
-        restore()
-        ev[i][0].record(stream)
-        gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
+    ms, t_wall = timed_steps(not a.no_flush)
     st, r = gl.read(g.error_if_nonfinite)
-    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     mean_ms = statistics.fmean(ms)
     wrote = not (r["skipped"] or r["scale"] == 1.0)
     alg = algorithmic_bytes(g.numel, esize, wrote)
     gbps = alg / (mean_ms * 1e-3) / 1e9
-    traffic = read_traffic(alg) if (a.config == "andrea120m_f32" and path_name == "fused") else None
+    kernels = "k_grad_clip_fused" if path_name == "fused" else "k_grad_norm_partial+k_grad_scale"
+    traffic = read_traffic(kernels, a.config)
+    roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernels,
+                "resident_bytes": info["resident_vectors"] * 16}
+    if traffic is not None:
+        # the rate of the bytes that actually crossed HBM, against the same peak
+        roofline["traffic_gbps"] = round(traffic / (mean_ms * 1e-3) / 1e9, 1)
+        roofline["traffic_frac"] = round(traffic / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    if not a.profile_pass:
+        # attainable: the reference read of the list's bytes, plus (when the
+        # step writes) the reference in-place copy of them, cold, same events
+        nref, rt = ref_times(g.numel * esize, a.steps, flush, stream, copy_too=False)
+        att_ms = rt["read"] + (rt["in_place"] if wrote else 0.0)
+        roofline["attainable"] = round(alg / (att_ms * 1e-3) / 1e9, 1)
+        roofline["frac_of_attainable"] = round(gbps / roofline["attainable"], 4)
+        roofline["attainable_basis"] = (f"gclip_ref_read {rt['read'] * 1e3:.1f} us"
+                                        + (f" + gclip_ref_copy in place {rt['in_place'] * 1e3:.1f} us" if wrote else "")
+                                        + f" over {nref} bytes, cold")
     out = {
         "metric": METRIC if a.config == "andrea120m_f32" else f"clip_grad_norm GB/s and % of HBM peak, {a.config}",
         "value": round(gbps, 1),
@@ -269,17 +374,50 @@ def main():
         "ms_per_step_median": round(statistics.median(ms), 5),
         "ms_per_step_min": round(min(ms), 5),
         "wall_s_timed_loop_incl_restore_and_flush": round(t_wall, 4),
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "k_grad_clip_fused" if path_name == "fused" else "k_grad_norm_partial+k_grad_scale",
-                     "resident_bytes": info["resident_vectors"] * 16},
+        "roofline": roofline,
         "norm": r["norm"],
     }
+    if not a.profile_pass and not a.no_flush:
+        wms, _ = timed_steps(False)
+        wmean = statistics.fmean(wms)
+        out["warm"] = {"ms_per_step": round(wmean, 5), "value": round(alg / (wmean * 1e-3) / 1e9, 1),
+                       "pct_hbm_peak": round(100.0 * alg / (wmean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                       "note": "the same steps without the cache flush: the restore copy leaves part of the "
+                               "list in the caches"}
     if st not in (0,) or r["status"] != 0:
         out["error"] = f"status {st}, device status {r['status']}"
     gl.close()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(g)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_ref(a, flush):
+    """The reference kernels (include/gclip_ref.h) alone, cold, at the byte
+    sizes of the workloads' lists: the attainable rates of a read pass and of
+    a read + write pass (in place, and to a second buffer) on this device."""
+    import torch
+    stream = torch.cuda.current_stream()
+    rows = []
+    for nb in REF_SIZES:
+        n16, rt = ref_times(nb, a.steps, flush, stream)
+        rows.append({"bytes": n16,
+                     "read_us": round(rt["read"] * 1e3, 2),
+                     "read_gbps": round(n16 / (rt["read"] * 1e-3) / 1e9, 1),
+                     "in_place_us": round(rt["in_place"] * 1e3, 2),
+                     "in_place_gbps": round(2 * n16 / (rt["in_place"] * 1e-3) / 1e9, 1),
+                     "copy_us": round(rt["copy"] * 1e3, 2),
+                     "copy_gbps": round(2 * n16 / (rt["copy"] * 1e-3) / 1e9, 1)})
+        torch.cuda.empty_cache()
+    head = rows[1]
+    out = {"metric": "attainable streaming GB/s, own reference kernels (read; read+write in place; copy)",
+           "value": head["read_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": 2,
+           "ms_per_step": round(head["read_us"] * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "u32x4", "data": "synthetic",
+           "config": {"workload": "plain streaming over one flat buffer, cold (2 GiB read between reps)",
+                      "kernels": "k_ref_read (128 KB per workgroup), k_ref_copy (32 KB per workgroup)"},
+           "sizes": rows}
     print(json.dumps(out), flush=True)
     return 0
 
@@ -464,7 +602,7 @@ def bench_amp(a, G, g, grads, pristine, flush, gl):
     return 0
 
 
-def bench_accum(a, G, gs):
+def bench_accum(a, G, gs, flush):
     """The last microbatch's += fused with the clip (gclip_accumulate_clip_:
     one launch on the fused path, which keeps each worker's block of sums on
     chip across the decision), on the four-microbatch ANDREA-120M fp32 list:
@@ -480,7 +618,6 @@ def bench_accum(a, G, gs):
     acc = upload(buf.arrays, "f32")
     contrib = upload(last.arrays, "f32")
     pristine = [t.clone() for t in acc]
-    flush = torch.ones((2 << 30) // 8, dtype=torch.int64, device="cuda")
     gl = G.GradList(acc)
     c = G.Contribution(gl, contrib)
     stream = torch.cuda.current_stream()
@@ -662,7 +799,8 @@ def _counter_rows(d):
 
 def _short_kernel(name):
     base = name.split("(")[0]
-    for k in ("k_grad_clip_fused", "k_grad_norm_partial", "k_grad_scale", "k_calib_copy", "k_flush_read"):
+    for k in ("k_grad_clip_fused", "k_grad_norm_partial", "k_grad_scale", "k_accum_clip_fused", "k_ref_read",
+              "k_ref_copy"):
         if k in base:
             return base.replace("void ", "").strip()
     if "neg_kernel" in name:
@@ -692,6 +830,8 @@ def summarize(args, commands):
                          f"{float(r.get('MinNs', 0)):12.1f} {float(r.get('MaxNs', 0)):12.1f} "
                          f"{float(r.get('Percentage', 0)):6.2f}")
     elif kind == "pmc":
+        # the kernels are named by the summary file: KERNEL[+KERNEL]__CONFIG__pmc.txt
+        kernels = os.path.basename(out).split("__")[0].split("+")
         per = {}
         for d, counter in zip(dirs, ("FETCH_SIZE", "WRITE_SIZE")):
             rows = _counter_rows(d)
@@ -700,23 +840,30 @@ def summarize(args, commands):
                 if r.get("Counter_Name", "") != counter:
                     continue
                 name = r.get("Kernel_Name", "")
-                key = ("clip" if "k_grad_clip_fused" in name else
-                       "copy" if ("neg_kernel" in name or "k_calib_copy" in name) else None)
+                if "neg_kernel" in name or "k_calib_copy" in name:
+                    key = "copy"
+                else:
+                    key = next((k for k in kernels if re.search(r"\b" + re.escape(k) + r"\b", name)), None)
                 if key is None:
                     continue
                 acc.setdefault(key, []).append(float(r["Counter_Value"]))
             per[counter] = {k: statistics.median(v) for k, v in acc.items()}
+        missing = [k for k in kernels + ["copy"] for c in per if k not in per[c]]
+        if missing:
+            raise SystemExit(f"no counter rows for {sorted(set(missing))}")
         copy_bytes = CALIBRATION_BYTES
         f_cal = per["FETCH_SIZE"]["copy"] * 1024 / copy_bytes
         w_cal = per["WRITE_SIZE"]["copy"] * 1024 / copy_bytes
-        fetch = per["FETCH_SIZE"]["clip"] * 1024 / f_cal
-        write = per["WRITE_SIZE"]["clip"] * 1024 / w_cal
         lines += ["# rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, median over dispatches);",
                   "# each scaled by what the counter reads for a copy kernel that reads and writes",
-                  f"# exactly {CALIBRATION_BYTES} bytes",
-                  f"fetch_kib_per_dispatch_clip: {per['FETCH_SIZE']['clip']:.1f}",
-                  f"write_kib_per_dispatch_clip: {per['WRITE_SIZE']['clip']:.1f}",
-                  f"fetch_kib_per_dispatch_copy: {per['FETCH_SIZE']['copy']:.1f}",
+                  f"# exactly {CALIBRATION_BYTES} bytes; a step of several kernels is their sum"]
+        fetch = write = 0.0
+        for k in kernels:
+            lines += [f"fetch_kib_per_dispatch {k}: {per['FETCH_SIZE'][k]:.1f}",
+                      f"write_kib_per_dispatch {k}: {per['WRITE_SIZE'][k]:.1f}"]
+            fetch += per["FETCH_SIZE"][k] * 1024 / f_cal
+            write += per["WRITE_SIZE"][k] * 1024 / w_cal
+        lines += [f"fetch_kib_per_dispatch_copy: {per['FETCH_SIZE']['copy']:.1f}",
                   f"write_kib_per_dispatch_copy: {per['WRITE_SIZE']['copy']:.1f}",
                   f"fetch_calibration (counter bytes / copy bytes): {f_cal:.4f}",
                   f"write_calibration (counter bytes / copy bytes): {w_cal:.4f}",

@@ -98,6 +98,8 @@ def _declare(lib):
         "gclip_adamw_step_amp": ([vp, ctypes.POINTER(GclipAdamwHparams), dbl, dbl, vp,
                                   ctypes.POINTER(GclipAmpParams), vp, vp], i32),
         "gclip_clip_noalloc_": ([ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32, dbl, dbl, i32, vp, vp], i32),
+        "gclip_ref_read": ([vp, i64, vp, vp], i32),
+        "gclip_ref_copy": ([vp, vp, i64, vp], i32),
         "gclip_status_string": ([i32], ctypes.c_char_p),
         "gclip_last_hip_error": ([], i32),
         "gclip_version": ([], i32),
@@ -127,11 +129,12 @@ def load():
 
 lib = load()
 
-# The C ABI's declared entry points (include/gclip.h), for the export check.
+# The C ABI's declared entry points (include/gclip.h, include/gclip_ref.h), for the export check.
 EXPORTS = ("gclip_list_create", "gclip_list_destroy", "gclip_list_info", "gclip_list_set_path",
            "gclip_list_set_wait", "gclip_norm",
            "gclip_scale", "gclip_clip_", "gclip_result_read", "gclip_plan_query", "gclip_plan_trace", "gclip_status_string",
            "gclip_last_hip_error", "gclip_version", "gclip_adamw_create", "gclip_adamw_destroy", "gclip_adamw_step",
            "gclip_norm_amp", "gclip_clip_amp_", "gclip_adamw_step_amp", "gclip_tensor_norms",
            "gclip_clip_per_tensor_", "gclip_contrib_create", "gclip_contrib_destroy", "gclip_accumulate_norm",
-           "gclip_accumulate_clip_", "gclip_set_gather_wait", "gclip_clip_noalloc_")
+           "gclip_accumulate_clip_", "gclip_set_gather_wait", "gclip_clip_noalloc_", "gclip_ref_read",
+           "gclip_ref_copy")

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgclip.so")
 SOURCES = ["gclip_api.cpp", "gclip_plan.cpp", "gclip_trace.cpp", "gclip_kernels.hip", "gclip_tensor.hip",
-           "gclip_adamw.hip", "gclip_noalloc.hip"]
+           "gclip_adamw.hip", "gclip_noalloc.hip", "gclip_ref.hip"]
 ARCH = os.environ.get("GCLIP_OFFLOAD_ARCH", "gfx950")
 
 

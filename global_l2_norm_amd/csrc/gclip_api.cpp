@@ -249,7 +249,7 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     }
     const gclip::HostPlan& P = L->plan;
     const size_t ntp = L->tplan.pieces.size(), ntf = L->tplan.first.size();
-    const gclip::PlanLayout PL = gclip::plan_layout(P, gclip::worker_threads() / 64);
+    const gclip::PlanLayout PL = gclip::plan_layout(P);
     size_t off = PL.bytes;
     auto take = [&](size_t bytes) {
       const size_t at = off;

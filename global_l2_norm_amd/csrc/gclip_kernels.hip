@@ -20,9 +20,9 @@
 //     binary64 accumulators (vec_sumsq states when a vector is summed again
 //     in binary64), so the sum cannot overflow and is non-finite exactly when
 //     some element is NaN or +-Inf;
-//   - lane sums are reduced by an xor butterfly inside each wave into one
-//     partial per chunk and wave (a slot of the chunk's own), and over the
-//     workgroup into one partial per worker for its block; the last
+//   - lane sums are reduced by an xor butterfly inside each wave, and the
+//     waves' sums in wave order into one partial per chunk (a slot of the
+//     chunk's own) and one per worker for its block; the last
 //     workgroup to arrive (a two-level agent-scope ticket) sums all partials
 //     in index order, so the bits of the norm do not depend on scheduling or
 //     on which workgroup took which chunk, and both paths give the same
@@ -345,6 +345,7 @@ __device__ __forceinline__ void reset_pools(uint32_t* pools) {
 // LDS slot i % 2 (a slot is rewritten only two barriers after it was read).
 struct ClaimSlots {
   uint32_t claim[2];
+  double wsum[2][kWaves];  // each wave's sum of the current chunk (by chunk parity)
 };
 
 // The chunk loops below draw the ticket for the chunk after next when a
@@ -357,11 +358,20 @@ struct ClaimSlots {
 // ticket for the second chunk is drawn before the first chunk's first group
 // is loaded and resolved after it.
 
+// A sum chunk's partial: its waves' sums added in wave order.
+__device__ __forceinline__ double chunk_total(const double (&ws)[kWaves]) {
+  double s = ws[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) s += ws[k];
+  return s;
+}
+
 // Sum every sum chunk of the streamed region [0, sb) that this workgroup
-// takes.  Each wave reduces its lanes' sums over a chunk to one value and
-// stores it in the chunk's own slot, partials[c * kWaves + wave], so the
-// final sum does not depend on which workgroup took the chunk; the only
-// barrier per chunk hands the next claim to every wave.
+// takes.  Each wave reduces its lanes' sums over a chunk to one value; at
+// the chunk's barrier (the only one, which also hands the next claim to
+// every wave) thread 0 adds the waves' values in wave order into the chunk's
+// own slot, partials[c], so the final sum does not depend on which workgroup
+// took the chunk.
 template <int DT>
 __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
   const uint32_t nch = p.nsum;
@@ -410,8 +420,9 @@ __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
     double v = lane_total(acc, 0.0);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (lane == 0) atomic_st(&p.partials[(size_t)c * kWaves + wave], v);
+    if (lane == 0) sl.wsum[par][wave] = v;
     __syncthreads();
+    if (t == 0) atomic_st(&p.partials[c], chunk_total(sl.wsum[par]));
     c = cn;
     cn = uniform32(sl.claim[par]);
     cur = curn;
@@ -478,7 +489,7 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, c
 
 // The sum chunks this workgroup takes, with the +=: every group is read
 // with its contribution (both one group ahead), added, written back and
-// summed, one partial per chunk and wave as in norm_chunks.
+// summed, one partial per chunk as in norm_chunks.
 template <int DT, bool NTS>
 __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, ClaimSlots& sl) {
   const uint32_t nch = p.nsum;
@@ -544,8 +555,9 @@ __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, 
     double v = lane_total(acc, 0.0);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (lane == 0) atomic_st(&p.partials[(size_t)c * kWaves + wave], v);
+    if (lane == 0) sl.wsum[par][wave] = v;
     __syncthreads();
+    if (t == 0) atomic_st(&p.partials[c], chunk_total(sl.wsum[par]));
     c = cn;
     cn = uniform32(sl.claim[par]);
     cur = curn;
@@ -554,12 +566,12 @@ __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, 
 }
 
 // ---------------------------------------------------------------- reductions and the decision
-// Partials: one per wave per sum chunk, then one per worker.
+// Partials: one per sum chunk, then one per worker.
 __device__ __forceinline__ uint32_t npartials(const DevPlan& p) {
-  return p.nsum * (uint32_t)kWaves + (uint32_t)p.nworkers;
+  return p.nsum + (uint32_t)p.nworkers;
 }
 __device__ __forceinline__ double* worker_partial(const DevPlan& p, int w) {
-  return p.partials + (size_t)p.nsum * kWaves + w;
+  return p.partials + (size_t)p.nsum + w;
 }
 
 // Sum of all partials in index order (lane i takes i, i + kThreads, ...).

@@ -106,7 +106,7 @@ extern "C" gclip_status gclip_clip_noalloc_(void* const* d_ptrs, const int64_t* 
     const int rc = plan_build(addrs, numels, n_tensors, dtype, ds->ncu, worker_threads(), resident_cap_vectors(),
                               chunk_shape(), plan, nullptr);
     if (rc != 0) return (gclip_status)rc;
-    const PlanLayout L = plan_layout(plan, worker_threads() / 64);
+    const PlanLayout L = plan_layout(plan);
     if (L.bytes > kScratchBytes) return GCLIP_ERANGE;
     image.resize(L.header);
     plan_image(plan, L, image.data());

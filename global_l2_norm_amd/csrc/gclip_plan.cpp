@@ -167,7 +167,7 @@ int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t 
   return 0;
 }
 
-PlanLayout plan_layout(const HostPlan& p, int waves) {
+PlanLayout plan_layout(const HostPlan& p) {
   const size_t nseg = (size_t)p.nseg(), nw = (size_t)p.nworkers, nsc = (size_t)p.nsc(), nch = (size_t)p.nchunk();
   const size_t nchs = (size_t)p.nchunk_streamed(), nsum = (size_t)p.nsum();
   size_t off = 0;
@@ -191,7 +191,7 @@ PlanLayout plan_layout(const HostPlan& p, int waves) {
   L.sync = take((size_t)kSyncWords * 4);
   L.bst = take(nw * 4);
   L.header = off;
-  L.part = take((nsum * (size_t)waves + nw) * 8);
+  L.part = take((nsum + nw) * 8);
   L.bytes = off;
   return L;
 }

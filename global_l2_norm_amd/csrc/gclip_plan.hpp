@@ -125,7 +125,7 @@ struct DevPlan {
   const uint32_t* sum_seg;
   const uint64_t* wk_scbegin;
   const uint64_t* sc_addr;
-  double* partials;   // nsum * kWaves sum-chunk partials, then nworkers worker partials (block + single elements)
+  double* partials;   // nsum sum-chunk partials, then nworkers worker partials (block + single elements)
   uint64_t* bcast;    // [0]: the decision of the fused kernel, published by value (kUndecided between launches)
   uint32_t* sync;     // kSyncWords counters (see above)
   uint32_t* bstate;   // nworkers: whether each block was handed back by the fused kernel
@@ -150,8 +150,8 @@ struct PlanLayout {
   size_t bytes;
 };
 
-// The layout of plan p for workgroups of `waves` wave64s.
-PlanLayout plan_layout(const HostPlan& p, int waves);
+// The layout of plan p.
+PlanLayout plan_layout(const HostPlan& p);
 
 // The host image of [0, L.header): every table, the decision word undecided,
 // counters and block states zero.  img must hold L.header bytes.

@@ -261,6 +261,55 @@ def lib_path() -> str:
     return _build.LIB
 
 
+def shards(arrays, parts: int):
+    """The list cut into `parts` runs of consecutive elements, as equal in
+    size as whole elements allow, each a list of contiguous views (a tensor
+    may be split between two runs)."""
+    total = sum(a.size for a in arrays)
+    bounds = [total * k // parts for k in range(parts + 1)]
+    out, t, off = [], 0, 0
+    for k in range(parts):
+        want, run = bounds[k + 1] - bounds[k], []
+        while want > 0:
+            a = arrays[t]
+            take = min(want, a.size - off)
+            run.append(a[off:off + take])
+            want -= take
+            off += take
+            if off == a.size:
+                t, off = t + 1, 0
+        out.append(run)
+    return out
+
+
+def clip_sharded_(arrays, dtype: str, max_norm: float, avg_factor: float = 1.0, error_if_nonfinite: bool = False,
+                  threads: int = 1) -> dict:
+    """The clip of clip_ with its two passes spread over `threads` host
+    threads, for timing the oracle on every core of a machine: the list is
+    cut into as many runs of consecutive elements (shards); each thread sums
+    one run with the oracle's own sum of squares, the runs' sums are added in
+    run order, the decision is the oracle's, and each thread scales one run
+    with the oracle's scale.  The C calls release the interpreter lock.  The
+    elements come out as clip_ writes them for the same factor; the sum
+    differs from clip_'s only by the order of its binary64 additions."""
+    import math
+    from concurrent.futures import ThreadPoolExecutor
+    o = default()
+    runs = shards(arrays, max(1, threads))
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as pool:
+        parts = list(pool.map(lambda r: o.sumsq(r, dtype, avg_factor), runs))
+        S = 0.0
+        for p, _ in parts:
+            S += p
+        nonfinite = any(nf for _, nf in parts)
+        norm = math.sqrt(S)
+        s, clipped, skipped = o.decide(norm, nonfinite, max_norm, avg_factor, error_if_nonfinite)
+        if not skipped and s != 1.0:
+            list(pool.map(lambda r: o.scale_(r, dtype, s), runs))
+    return {"sumsq": S, "norm": norm, "scale": s if not skipped else 1.0, "nonfinite": nonfinite,
+            "clipped": clipped, "skipped": skipped}
+
+
 def _marshal(arrays, dtype):
     if dtype not in _CODE:
         raise ValueError(f"unknown dtype {dtype!r}")

@@ -54,6 +54,23 @@ def test_version_and_status_strings():
     assert g.gclip_status_string(99) == "unknown status"
 
 
+def test_reference_kernels_reject_bad_spans_before_any_gpu_work():
+    """gclip_ref_read / gclip_ref_copy check their spans on the host: an
+    empty span is a no-op, a misaligned or ragged one or an overlapping copy
+    is GCLIP_EINVAL, and neither touches a GPU."""
+    L = _lib.lib
+    sink = 0x1000
+    assert L.gclip_ref_read(None, 0, sink, None) == _lib.GCLIP_OK
+    assert L.gclip_ref_copy(None, None, 0, None) == _lib.GCLIP_OK
+    assert L.gclip_ref_read(0x1008, 64, sink, None) == _lib.GCLIP_EINVAL   # misaligned
+    assert L.gclip_ref_read(0x1000, 24, sink, None) == _lib.GCLIP_EINVAL   # not whole vectors
+    assert L.gclip_ref_read(0x1000, -16, sink, None) == _lib.GCLIP_EINVAL
+    assert L.gclip_ref_read(0x1000, 64, None, None) == _lib.GCLIP_EINVAL
+    assert L.gclip_ref_copy(0x2000, 0x1000, 8192, None) == _lib.GCLIP_EINVAL  # overlapping ranges
+    assert L.gclip_ref_copy(0x1000, 0x2000, 8192, None) == _lib.GCLIP_EINVAL
+    assert L.gclip_ref_copy(0x3000, 0x1001, 64, None) == _lib.GCLIP_EINVAL
+
+
 def test_gather_wait_setter_bounds():
     """The process-wide bound of the per-tensor gathering wait: above 60 s is
     rejected, a negative value restores the default (no GPU involved)."""

@@ -57,3 +57,33 @@ def test_shapes_match_the_pages():
     assert len(b) == 4289
     assert sum(int(np.prod(s)) for _, s in b) == 1_311_182_848
     assert sum(int(np.prod(s)) for _, s in gs.shapes_tiny()) == 4788
+
+
+@pytest.mark.parametrize("threads", [1, 2, 7, 16])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_sharded_leg_matches_the_sequential_oracle(dtype, threads):
+    """The CPU baseline's threaded leg: its sum lies within N 2^-53 (relative)
+    of the sequential oracle's -- both add the same exact binary64 squares,
+    in another order -- it takes the same decision, and every element is the
+    oracle's own rounding of g * s for the factor it decided; one thread is
+    the sequential oracle bit for bit."""
+    rng = np.random.default_rng(600 + threads)
+    arrays = [gs.to_storage(rng.standard_normal(n) * 0.3, dtype) for n in (1, 5, 4097, 70_001, 3, 250_000)]
+    n = sum(a.size for a in arrays)
+    seq = [a.copy() for a in arrays]
+    rs = oracle.clip_(seq, dtype, 1.0, 0.5)
+    par = [a.copy() for a in arrays]
+    rp = oracle.clip_sharded_(par, dtype, 1.0, 0.5, threads=threads)
+    assert abs(rp["sumsq"] - rs["sumsq"]) <= n * 2.0 ** -53 * rs["sumsq"]
+    assert rp["clipped"] == rs["clipped"] and rp["nonfinite"] == rs["nonfinite"]
+    ref = [a.copy() for a in arrays]
+    oracle.scale_(ref, dtype, rp["scale"])
+    for a, b in zip(par, ref):
+        assert a.tobytes() == b.tobytes()
+    if threads == 1:
+        assert rp["sumsq"] == rs["sumsq"] and rp["scale"] == rs["scale"]
+        for a, b in zip(par, seq):
+            assert a.tobytes() == b.tobytes()
+    runs = oracle.shards(arrays, threads)
+    assert len(runs) == threads and sum(v.size for r in runs for v in r) == n
+    assert max(sum(v.size for v in r) for r in runs) - min(sum(v.size for v in r) for r in runs) <= 1
