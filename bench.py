@@ -42,13 +42,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "clip_grad_norm GB/s and % of HBM peak, ANDREA-120M-shaped grads"
 HBM_PEAK_GBPS = 8000.0
-# The sources that decide what the measured kernels move: the kernels, the
-# device walk, and the host plan and workspace layout (chunk and block split,
-# store kinds, pools).  A committed counter summary is used only while these
-# hash to the value recorded in it.
-KERNEL_SOURCES = ["global_l2_norm_amd/csrc/gclip_kernels.hip", "global_l2_norm_amd/csrc/gclip_cursor.hpp",
-                  "global_l2_norm_amd/csrc/gclip_device.hpp", "global_l2_norm_amd/csrc/gclip_plan.hpp",
-                  "global_l2_norm_amd/csrc/gclip_plan.cpp", "global_l2_norm_amd/csrc/gclip_api.cpp"]
+# The sources that decide what the measured kernels move: every kernel, the
+# device walk, the host plan and workspace layout (chunk and block split,
+# store kinds, pools) and the public headers.  A committed profile summary
+# is used only while these hash to the value recorded in it.
+KERNEL_SOURCES = sorted([os.path.join("global_l2_norm_amd", "csrc", f)
+                         for f in os.listdir(os.path.join(ROOT, "global_l2_norm_amd", "csrc"))
+                         if f.endswith((".hip", ".hpp", ".cpp"))] +
+                        [os.path.join("include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                         if f.endswith(".h")])
 PROFILES = os.path.join(ROOT, "profiles")
 # byte sizes of the workloads' lists: 120M fp16, 120M fp32, twice that, and 1.3B bf16
 REF_SIZES = [184_496_640, 368_993_280, 737_986_560, 2_622_365_696]
