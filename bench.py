@@ -831,6 +831,28 @@ def summarize(args, commands):
             lines.append(f"{short:62s} {r.get('Calls', ''):>6s} {float(r.get('AverageNs', 0)):12.1f} "
                          f"{float(r.get('MinNs', 0)):12.1f} {float(r.get('MaxNs', 0)):12.1f} "
                          f"{float(r.get('Percentage', 0)):6.2f}")
+        # this library's kernels per launch shape, from the per-dispatch trace:
+        # one line per (kernel, grid), with the resources each launch held
+        import csv
+        files = glob.glob(os.path.join(dirs[0], "**", "*kernel_trace.csv"), recursive=True)
+        if files:
+            groups = {}
+            for r in csv.DictReader(open(files[0])):
+                name = r.get("Kernel_Name", "")
+                if "gclip::" not in name:
+                    continue
+                key = (_short_kernel(name)[:52], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+                       int(r["Workgroup_Size_X"]), r.get("VGPR_Count", ""), r.get("Accum_VGPR_Count", ""),
+                       r.get("LDS_Block_Size", ""), r.get("Scratch_Size", ""))
+                groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            lines.append("# per launch shape (from the per-dispatch trace): workgroups x lanes, VGPRs, AGPRs, LDS and "
+                         "scratch bytes per workgroup")
+            lines.append(f"{'kernel':52s} {'wgs':>7s} {'lanes':>5s} {'vgpr':>4s} {'agpr':>4s} {'lds':>7s} "
+                         f"{'scr':>4s} {'calls':>5s} {'avg_ns':>11s} {'median_ns':>11s}")
+            for key in sorted(groups):
+                d = groups[key]
+                lines.append(f"{key[0]:52s} {key[1]:7d} {key[2]:5d} {key[3]:>4s} {key[4]:>4s} {key[5]:>7s} "
+                             f"{key[6]:>4s} {len(d):5d} {statistics.fmean(d):11.1f} {statistics.median(d):11.1f}")
     elif kind == "pmc":
         # the kernels are named by the summary file: KERNEL[+KERNEL]__CONFIG__pmc.txt
         kernels = os.path.basename(out).split("__")[0].split("+")

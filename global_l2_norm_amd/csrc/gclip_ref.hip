@@ -16,7 +16,6 @@
 #include "gclip_host.hpp"
 
 namespace gclip {
-namespace {
 
 constexpr int kRefThreads = 512;
 constexpr int kReadUnroll = 16;  // vectors in flight per lane: one piece is 16 x 512 x 16 B = 128 KB
@@ -54,6 +53,8 @@ __global__ __launch_bounds__(kRefThreads) void k_ref_copy(g_u32x4* dst, const g_
     if (v < nvec) st_vec<false>(dst + v, q[u]);
   }
 }
+
+namespace {
 
 bool span_ok(const void* p, int64_t bytes) {
   return bytes >= 0 && bytes % 16 == 0 && (bytes == 0 || (p && reinterpret_cast<uintptr_t>(p) % 16 == 0));

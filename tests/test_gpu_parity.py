@@ -349,6 +349,39 @@ def test_power_of_two_scaling_is_exact(dtype):
     assert r1["sumsq"] == 16.0 * r0["sumsq"] and r1["norm"] == 4.0 * r0["norm"]
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_permuted_list_same_norm_and_elements(c2, path):
+    """The ANDREA-120M list in another tensor order (a fixed random
+    permutation): the norm is the same sum in another order, so it agrees
+    with the original order's within the accumulation bound, the decision is
+    the same, and every element matches the oracle (and the original run's
+    element for the same tensor, within the element tolerance)."""
+    rng = np.random.default_rng(4242)
+    perm = rng.permutation(len(c2.arrays))
+    arrays = [c2.arrays[i] for i in perm]
+    st0, r0, out0 = gpu_clip(c2.arrays, "f32", c2.max_norm, path=path)
+    st1, r1, ro, out1 = check_against_oracle(arrays, "f32", c2.max_norm, path=path, what=f"permuted {path}")
+    bound = 2 * (8 * 2.0 ** -24 + c2.numel * 2.0 ** -53)
+    assert abs(r1["sumsq"] - r0["sumsq"]) <= bound * r0["sumsq"]
+    assert abs(r1["norm"] - r0["norm"]) <= 1e-5 * r0["norm"]
+    assert r1["clipped"] == r0["clipped"]
+    gu.assert_elems_close([out1[k] for k in np.argsort(perm)], out0, "f32", f"permuted vs original {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_concatenated_list_same_norm_and_elements(c2, path):
+    """The same 92.2M values as one tensor (the list concatenated): one
+    segment and no tensor boundaries, the same norm within the accumulation
+    bound, and every element within tolerance of the per-tensor run's."""
+    flat = [np.concatenate(c2.arrays)]
+    st0, r0, out0 = gpu_clip(c2.arrays, "f32", c2.max_norm, path=path)
+    st1, r1, ro, out1 = check_against_oracle(flat, "f32", c2.max_norm, path=path, what=f"concatenated {path}")
+    bound = 2 * (8 * 2.0 ** -24 + c2.numel * 2.0 ** -53)
+    assert abs(r1["sumsq"] - r0["sumsq"]) <= bound * r0["sumsq"]
+    assert r1["clipped"] == r0["clipped"]
+    gu.assert_elems_close(out1, [np.concatenate(out0)], "f32", f"concatenated vs list {path}")
+
+
 def test_scale_with_caller_supplied_sumsq():
     """gclip_scale decides from the sumsq in the result block, e.g. one
     summed over several ranks: a block claiming 4x the local sumsq doubles
