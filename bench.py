@@ -25,6 +25,11 @@ Prints one JSON line.  Other modes:
                        calibration copy of known size for the PMC counters)
   --summarize-rocprof  turn rocprofv3 output into the summaries kept in
                        profiles/ (see the --help of that mode)
+  --phase-stamps       the fused kernel's phase timeline, from the diagnostic
+                       build of include/gclip_stamps.h (built first with
+                       `python -m global_l2_norm_amd.build --phase-stamps`):
+                       the same cold steps, then a table of when the median
+                       and the last workgroup ended each phase
 """
 import argparse
 import glob
@@ -44,7 +49,7 @@ METRIC = "clip_grad_norm GB/s and % of HBM peak, ANDREA-120M-shaped grads"
 HBM_PEAK_GBPS = 8000.0
 # The sources that decide what the measured kernels move: every kernel, the
 # device walk, the host plan and workspace layout (chunk and block split,
-# store kinds, pools) and the public headers.  A committed profile summary
+# store kinds, claims) and the public headers.  A committed profile summary
 # is used only while these hash to the value recorded in it.
 KERNEL_SOURCES = sorted([os.path.join("global_l2_norm_amd", "csrc", f)
                          for f in os.listdir(os.path.join(ROOT, "global_l2_norm_amd", "csrc"))
@@ -259,6 +264,8 @@ def main():
                     help="KIND OUT DIR...: KIND is 'trace' (a --kernel-trace --stats output dir) or 'pmc' "
                          "(FETCH_SIZE dir, then WRITE_SIZE dir); OUT is the summary file to write, named "
                          "KERNEL[+KERNEL]__CONFIG__KIND.txt")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="the fused kernel's phase timeline (needs the --phase-stamps build of the library)")
     ap.add_argument("--rocprof-command", action="append", default=[],
                     help="with --summarize-rocprof: the command that produced each output dir (repeatable)")
     a = ap.parse_args()
@@ -270,6 +277,13 @@ def main():
               file=sys.stderr)
         return 2
 
+    if a.phase_stamps:
+        stamps_lib = os.path.join(ROOT, "global_l2_norm_amd", "_stamps", "libgclip.so")
+        if not os.path.exists(stamps_lib):
+            print("--phase-stamps needs the diagnostic build: python -m global_l2_norm_amd.build --phase-stamps",
+                  file=sys.stderr)
+            return 2
+        os.environ["GCLIP_LIBRARY"] = stamps_lib
     import torch
 
     import global_l2_norm_amd as G
@@ -301,6 +315,8 @@ def main():
         return bench_amp(a, G, g, tensors, pristine, flush, gl)
     if a.path == "per_tensor":
         return bench_per_tensor(a, G, g, tensors, pristine, flush, gl)
+    if a.phase_stamps:
+        return bench_phases(a, G, g, tensors, pristine, flush, gl)
     if a.path != "auto":
         gl.set_path(G.GCLIP_PATH_FUSED if a.path == "fused" else G.GCLIP_PATH_SPLIT)
     info = gl.info()
@@ -393,6 +409,79 @@ def main():
         out["cpu_baseline"] = cpu_baseline(g)
     print(json.dumps(out), flush=True)
     return 0
+
+
+PHASES = [(1, "sum chunks done"), (2, "block read into VGPRs and LDS"), (3, "decision seen"),
+          (4, "block written back from VGPRs and LDS"), (5, "scale chunks done"), (6, "end")]
+
+
+def bench_phases(a, G, g, tensors, pristine, flush, gl):
+    """The fused kernel's phase timeline over `steps` cold steps: per step,
+    every workgroup's stamps from the earliest workgroup start; per phase,
+    the median over steps of the median workgroup and of the last one (a
+    workgroup that handed its block back counts up to the block read)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = G._lib.lib
+    f = lib.gclip_phase_stamps
+    f.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
+    f.restype = ctypes.c_int32
+    gl.set_path(G.GCLIP_PATH_FUSED)
+    nw = gl.info()["n_workers"]
+    points = 8
+    buf = np.zeros(nw * points, dtype=np.uint64)
+    rate = ctypes.c_int64(0)
+    per_step = []
+    ev_ms = []
+    stream = torch.cuda.current_stream()
+    for i in range(a.warmup + a.steps):
+        for t, p in zip(tensors, pristine):
+            t.copy_(p)
+        if not a.no_flush:
+            flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        st = f(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), nw, ctypes.byref(rate))
+        if st != 0:
+            raise RuntimeError(f"gclip_phase_stamps: status {st}")
+        if i < a.warmup:
+            continue
+        s = buf.reshape(nw, points).astype(np.int64)
+        t0 = s[:, 0].min()
+        row = {}
+        for k, _ in PHASES:
+            ok = s[:, k] >= s[:, 0]
+            v = (s[ok, k] - t0) / rate.value * 1e6
+            row[k] = (float(np.median(v)), float(v.max()), int(ok.sum())) if ok.any() else None
+        per_step.append(row)
+        ev_ms.append(e0.elapsed_time(e1))
+    st, r = gl.read(g.error_if_nonfinite)
+    gl.close()
+    print(f"# phase timeline of k_grad_clip_fused, {a.config} ({g.dtype}, {g.numel} elements), "
+          f"{a.steps} cold steps after {a.warmup} warm-up")
+    print(f"# {nw} workgroups; wall clock {rate.value / 1e6:.0f} MHz; norm {r['norm']:.6g}, scale {r['scale']:.6g}, "
+          f"handed back {r['handed_back']} (last step)")
+    print(f"# event time per step: median {statistics.median(ev_ms) * 1e3:.1f} us")
+    print(f"# kernel sources sha256/16: {kernel_source_hash()}")
+    print("| phase (times from the first workgroup's start) | median workgroup | last workgroup | workgroups |")
+    print("|---|---|---|---|")
+    for k, name in PHASES:
+        rows = [row[k] for row in per_step if row.get(k) is not None]
+        if not rows:
+            print(f"| {name} | — | — | 0 |")
+            continue
+        med = statistics.median(x[0] for x in rows)
+        last = statistics.median(x[1] for x in rows)
+        cnt = min(x[2] for x in rows)
+        print(f"| {name} | {med:.1f} us | {last:.1f} us | {cnt} |")
+    print("# each figure is the median over the steps of that step's median (or last) workgroup")
+    return 0 if st == 0 and r["status"] == 0 else 1
 
 
 def bench_ref(a, flush):

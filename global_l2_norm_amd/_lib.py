@@ -8,7 +8,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgclip.so")
+# GCLIP_LIBRARY may name another build of the same library to load instead:
+# the phase-timeline build of include/gclip_stamps.h, _stamps/libgclip.so.
+LIB_PATH = os.environ.get("GCLIP_LIBRARY") or os.path.join(HERE, "libgclip.so")
 
 GCLIP_F32, GCLIP_F16, GCLIP_BF16 = 0, 1, 2
 GCLIP_OK, GCLIP_EINVAL, GCLIP_EDTYPE, GCLIP_ENOMEM, GCLIP_EHIP, GCLIP_ENONFINITE, GCLIP_EDEVICE, GCLIP_ERANGE = range(8)

@@ -3,6 +3,11 @@
 Every HIP source is compiled with packed fp32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops); hipcc's host pass warns
 that it does not know the feature, which is harmless.
+
+`python -m global_l2_norm_amd.build --phase-stamps` builds instead the
+diagnostic library of include/gclip_stamps.h, with -DGCLIP_PHASE_STAMPS,
+into _stamps/libgclip.so (the fused kernel then records its phase
+timeline); the library itself is not touched.
 """
 import os
 import subprocess
@@ -13,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgclip.so")
+STAMPS_LIB = os.path.join(HERE, "_stamps", "libgclip.so")
 SOURCES = ["gclip_api.cpp", "gclip_plan.cpp", "gclip_trace.cpp", "gclip_kernels.hip", "gclip_tensor.hip",
            "gclip_adamw.hip", "gclip_noalloc.hip", "gclip_ref.hip"]
 ARCH = os.environ.get("GCLIP_OFFLOAD_ARCH", "gfx950")
@@ -40,8 +46,9 @@ def _jobs() -> int:
 
 def build(verbose: bool = False, defines=(), lib_path: str = LIB) -> str:
     """Always recompile the library (the sources in parallel); return its
-    path.  `defines` are extra -D flags (tuning sweeps)."""
-    odir = os.path.join(HERE, "_build")
+    path.  `defines` are extra -D flags (tuning sweeps); objects go to a
+    _build folder beside lib_path."""
+    odir = os.path.join(os.path.dirname(lib_path), "_build")
     os.makedirs(odir, exist_ok=True)
 
     def compile_one(src):
@@ -73,5 +80,15 @@ def build(verbose: bool = False, defines=(), lib_path: str = LIB) -> str:
     return lib_path
 
 
+def build_phase_stamps(verbose: bool = False) -> str:
+    """The diagnostic build of include/gclip_stamps.h."""
+    return build(verbose=verbose, defines=("GCLIP_PHASE_STAMPS",), lib_path=STAMPS_LIB)
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if sys.argv[1:] == ["--phase-stamps"]:
+        print(build_phase_stamps(verbose=True))
+    elif sys.argv[1:]:
+        sys.exit("usage: python -m global_l2_norm_amd.build [--phase-stamps]")
+    else:
+        print(build(verbose=True))

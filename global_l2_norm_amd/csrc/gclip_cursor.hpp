@@ -36,10 +36,10 @@ namespace gclip {
 #define GCLIP_SUM_CHUNKS_PER_WORKER 1
 #endif
 #ifndef GCLIP_SCALE_MIN_STEPS
-#define GCLIP_SCALE_MIN_STEPS 16
+#define GCLIP_SCALE_MIN_STEPS 8
 #endif
 #ifndef GCLIP_SCALE_MAX_STEPS
-#define GCLIP_SCALE_MAX_STEPS 16
+#define GCLIP_SCALE_MAX_STEPS 8
 #endif
 #ifndef GCLIP_SCALE_GUIDE
 #define GCLIP_SCALE_GUIDE 2

@@ -11,9 +11,9 @@
 // MI355X design:
 //   - one workgroup of kThreads per compute unit.  The list's 16-byte
 //     vector space (gclip_plan.hpp) ends with one block per worker; the rest
-//     is cut into chunks that the workers claim at run time from eight
-//     pools, one per XCD, so that the XCDs that stream faster take more of
-//     them -- in the summing pass as in the scaling pass.  Loads are dwordx4
+//     is cut into chunks: each worker takes two without a claim, and the
+//     rest are claimed at run time from one counter, so that the XCDs that
+//     stream faster take more of them.  Loads are dwordx4
 //     with kUnroll vectors in flight per lane, the next group's loads issued
 //     before the current group is used;
 //   - each vector's squares are summed in fp32 and added into per-lane
@@ -44,8 +44,29 @@
 #include "gclip_cursor.hpp"
 #include "gclip_device.hpp"
 #include "gclip_plan.hpp"
+#ifdef GCLIP_PHASE_STAMPS
+#include "../../include/gclip_stamps.h"
+#include "gclip_host.hpp"
+#endif
 
 namespace gclip {
+
+// Phase timeline, in a separate build only (-DGCLIP_PHASE_STAMPS, see
+// include/gclip_stamps.h): thread 0 of each workgroup of the fused kernel
+// stores the wall clock at the kernel's phase boundaries.  In the library
+// itself the stamps compile to nothing.
+#ifdef GCLIP_PHASE_STAMPS
+__device__ uint64_t g_phase_stamps[GCLIP_STAMP_WORKERS * GCLIP_STAMP_POINTS];
+#define GCLIP_STAMP(k)                                                                  \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && blockIdx.x < GCLIP_STAMP_WORKERS)                           \
+      ::gclip::g_phase_stamps[blockIdx.x * GCLIP_STAMP_POINTS + (k)] = wall_clock64(); \
+  } while (0)
+#else
+#define GCLIP_STAMP(k) \
+  do {                 \
+  } while (0)
+#endif
 
 // ---------------------------------------------------------------- group loads and stores
 // Load the vectors of one group into q (zeros where a lane has no vector).
@@ -245,28 +266,26 @@ __device__ __forceinline__ void accum_scale_steps(const DevPlan& p, const AccSrc
 // Word of line 0 of sync.
 constexpr int kHandedWord = 0;
 
-__device__ __forceinline__ uint32_t* sum_pools(const DevPlan& p) { return p.sync + kSyncLineWords; }
-__device__ __forceinline__ uint32_t* scale_pools(const DevPlan& p) { return p.sync + (1 + kPools) * kSyncLineWords; }
-__device__ __forceinline__ uint32_t* arrival_tickets(const DevPlan& p) {
-  return p.sync + (1 + 2 * kPools) * kSyncLineWords;
-}
+__device__ __forceinline__ uint32_t* sum_claims(const DevPlan& p) { return p.sync + kSyncLineWords; }
+__device__ __forceinline__ uint32_t* scale_claims(const DevPlan& p) { return p.sync + 2 * kSyncLineWords; }
+__device__ __forceinline__ uint32_t* arrival_tickets(const DevPlan& p) { return p.sync + 3 * kSyncLineWords; }
 __device__ __forceinline__ uint32_t* finish_tickets(const DevPlan& p) {
-  return p.sync + (2 + 3 * kPools) * kSyncLineWords;
+  return p.sync + (4 + kTicketGroups) * kSyncLineWords;
 }
 
 // Ticket over every workgroup of a launch, in two levels: workgroup w counts
-// in the line of its group w % kPools (its XCD: workgroups are dealt to the
-// XCDs in turn), the last of each group counts in the top line.  No counter
-// takes more than ~nworkers / kPools atomics at once.  True in exactly one
+// in the line of its group w % kTicketGroups (its XCD: workgroups are dealt
+// to the XCDs in turn), the last of each group counts in the top line.  No
+// counter takes more than ~nworkers / kTicketGroups atomics at once.  True in exactly one
 // workgroup, the last to take the ticket.  The counter a workgroup completes
 // is reset by it for the next launch.  Thread 0 only; its stores must be
 // complete (complete_stores) before the call.
 __device__ __forceinline__ bool take_ticket(uint32_t* lines, int32_t nworkers) {
-  const uint32_t g = blockIdx.x % (uint32_t)kPools;
-  const uint32_t members = ((uint32_t)nworkers - g + kPools - 1) / kPools;
-  const uint32_t groups = nworkers < kPools ? (uint32_t)nworkers : (uint32_t)kPools;
+  const uint32_t g = blockIdx.x % (uint32_t)kTicketGroups;
+  const uint32_t members = ((uint32_t)nworkers - g + kTicketGroups - 1) / kTicketGroups;
+  const uint32_t groups = nworkers < kTicketGroups ? (uint32_t)nworkers : (uint32_t)kTicketGroups;
   uint32_t* mine = lines + g * kSyncLineWords;
-  uint32_t* top = lines + kPools * kSyncLineWords;
+  uint32_t* top = lines + kTicketGroups * kSyncLineWords;
   if (atomic_add(mine, 1u) != members - 1u) return false;
   atomic_st(mine, 0u);
   if (atomic_add(top, 1u) != groups - 1u) return false;
@@ -275,69 +294,47 @@ __device__ __forceinline__ bool take_ticket(uint32_t* lines, int32_t nworkers) {
 }
 
 // ---------------------------------------------------------------- chunk claiming
-// Workgroup w takes chunk w first, without any claim; chunks nworkers ..
-// nch - 1 are claimed at run time from kPools pools, the one of the
-// workgroup's own XCD first.  Pool q holds chunks nworkers + q, nworkers + q
-// + kPools, ...; a claim is a ticket drawn on a pool's counter.
+// Workgroup w takes chunks w and nworkers + w without any claim; chunks
+// 2 nworkers .. nch - 1 are claimed at run time in index order, a claim
+// being a ticket drawn on one counter, so that the workgroups that stream
+// faster take more of them.  Every claim is then one atomic, whose reply
+// comes back while a chunk streams.  (With one pool per XCD, a workgroup
+// whose own pool was empty had to read every pool's counter before it could
+// claim again: two round trips that no chunk hid, taken just as the last
+// chunks ran out; on the 2.6 GB list the pass ran 4.5 % slower.)  The two
+// chunks taken without a claim keep the first tickets, which every
+// workgroup draws at once, off the start of the pass: drawn there and waited
+// for at once, they queued on the counter for up to 3 us.
 constexpr uint32_t kNone = 0xffffffffu;
 
 struct Claimer {
-  uint32_t* pools;
-  uint32_t base;   // first claimed chunk (nworkers)
-  uint32_t ndyn;   // claimed chunks
-  uint32_t pool;   // pool drawn from
-  bool dry;        // every pool found empty
+  uint32_t* counter;
+  uint32_t base;  // first claimed chunk: 2 nworkers
+  uint32_t ndyn;  // claimed chunks
 };
 
-__device__ __forceinline__ Claimer make_claimer(uint32_t* pools, const DevPlan& p, uint32_t nch) {
-  const uint32_t base = (uint32_t)p.nworkers;
-  const uint32_t ndyn = nch > base ? nch - base : 0u;
-  return Claimer{pools, base, ndyn, blockIdx.x % (uint32_t)kPools, ndyn == 0u};
+__device__ __forceinline__ Claimer make_claimer(uint32_t* counter, const DevPlan& p, uint32_t nch) {
+  const uint32_t base = 2u * (uint32_t)p.nworkers;
+  return Claimer{counter, base, nch > base ? nch - base : 0u};
 }
 
-__device__ __forceinline__ uint32_t pool_size(const Claimer& cl, uint32_t q) {
-  return q < cl.ndyn ? (cl.ndyn - q + kPools - 1) / kPools : 0u;
+// The chunk workgroup w takes second, without a claim (kNone if none).
+__device__ __forceinline__ uint32_t second_chunk(const DevPlan& p, uint32_t nch, uint32_t w) {
+  const uint32_t c = (uint32_t)p.nworkers + w;
+  return c < nch ? c : kNone;
 }
 
 // A claim is taken in two steps: the ticket is drawn before a chunk streams
 // and turned into a chunk after it, so waiting for the counter's reply
 // overlaps the chunk's loads instead of draining them.  Thread 0 only.
+// Tickets are drawn only while claims succeed, so the counter stays below
+// ndyn + nworkers.
 __device__ __forceinline__ uint32_t claim_issue(const Claimer& cl) {
-  return cl.dry ? 0u : atomic_add(&cl.pools[cl.pool * kSyncLineWords], 1u);
+  return cl.ndyn == 0u ? kNone : atomic_add(cl.counter, 1u);
 }
 
-// The chunk of ticket tk (drawn on pool cl.pool), or, when that pool is
-// empty, a chunk of another pool: every pool's counter is read at once and a
-// pool that still has chunks is claimed from, until a claim succeeds or all
-// are empty (kNone).  Counters only grow during a launch, so a pool found
-// empty stays empty, and a failed claim leaves its pool empty: the loop ends
-// within kPools failures.
-__device__ __forceinline__ uint32_t claim_resolve(Claimer& cl, uint32_t tk) {
-  if (cl.dry) return kNone;
-  if (tk < pool_size(cl, cl.pool)) return cl.base + cl.pool + tk * (uint32_t)kPools;
-  for (int round = 0; round <= kPools; ++round) {
-    // the first pool after cl.pool, in circular order, that still has chunks
-    uint32_t pick = kNone, best = kPools;
-#pragma unroll
-    for (int q = 0; q < kPools; ++q) {
-      const uint32_t cnt = atomic_ld(&cl.pools[q * kSyncLineWords]);
-      const uint32_t dist = ((uint32_t)q + 2u * kPools - cl.pool - 1u) % (uint32_t)kPools;
-      if (cnt < pool_size(cl, (uint32_t)q) && dist < best) {
-        best = dist;
-        pick = (uint32_t)q;
-      }
-    }
-    if (pick == kNone) break;
-    cl.pool = pick;
-    const uint32_t k2 = atomic_add(&cl.pools[pick * kSyncLineWords], 1u);
-    if (k2 < pool_size(cl, pick)) return cl.base + pick + k2 * (uint32_t)kPools;
-  }
-  cl.dry = true;
-  return kNone;
-}
-
-__device__ __forceinline__ void reset_pools(uint32_t* pools) {
-  for (int q = 0; q < kPools; ++q) atomic_st(&pools[q * kSyncLineWords], 0u);
+__device__ __forceinline__ uint32_t claim_resolve(const Claimer& cl, uint32_t tk) {
+  return tk < cl.ndyn ? cl.base + tk : kNone;
 }
 
 // Claims run two chunks ahead: the chunk after next is claimed while the
@@ -354,9 +351,9 @@ struct ClaimSlots {
 // order, so by then the ticket's reply is in and resolving it costs no wait.
 // Only then is the next chunk's first group loaded, so it stays in flight
 // across the chunk's barrier.  (Resolving after that load made the wave wait
-// for it too: every chunk ended with nothing in flight.)  At the start, the
-// ticket for the second chunk is drawn before the first chunk's first group
-// is loaded and resolved after it.
+// for it too: every chunk ended with nothing in flight.)  The first two
+// chunks need no claim, so the first ticket is drawn as the first chunk
+// starts, for the third.
 
 // A sum chunk's partial: its waves' sums added in wave order.
 __device__ __forceinline__ double chunk_total(const double (&ws)[kWaves]) {
@@ -377,19 +374,14 @@ __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
   const uint32_t nch = p.nsum;
   if (blockIdx.x >= nch) return;  // then no chunk is left to claim either
   const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
-  Claimer cl = make_claimer(sum_pools(p), p, nch);
-  uint32_t c = blockIdx.x, cn;
+  const Claimer cl = make_claimer(sum_claims(p), p, nch);
+  uint32_t c = blockIdx.x, cn = second_chunk(p, nch, blockIdx.x);
   Cursor cur;
   u32x4 q[kUnroll];
   {
-    uint32_t tk = 0;
-    if (t == 0) tk = claim_issue(cl);
     const Range r = sum_chunk_range(p, c);
     cursor_load(p, cur, r.seg);
     load_group<kNtSum>(p, cur, r.b, r.e, 0, range_steps(r), q);
-    if (t == 0) sl.claim[1] = claim_resolve(cl, tk);
-    __syncthreads();
-    cn = uniform32(sl.claim[1]);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
     const Range r = sum_chunk_range(p, c);
@@ -437,19 +429,14 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, c
                                              const uint32_t* seg, uint32_t nch, double s64, float s32) {
   if (blockIdx.x >= nch) return;  // then no chunk is left to claim either
   const uint32_t t = threadIdx.x;
-  Claimer cl = make_claimer(scale_pools(p), p, nch);
-  uint32_t c = blockIdx.x, cn;
+  const Claimer cl = make_claimer(scale_claims(p), p, nch);
+  uint32_t c = blockIdx.x, cn = second_chunk(p, nch, blockIdx.x);
   Cursor cur;
   u32x4 q[kUnroll];
   {
-    uint32_t tk = 0;
-    if (t == 0) tk = claim_issue(cl);
     const Range r = tab_chunk_range(vb, seg, c);
     cursor_load(p, cur, r.seg);
     load_group<kNtScale>(p, cur, r.b, r.e, 0, range_steps(r), q);
-    if (t == 0) sl.claim[1] = claim_resolve(cl, tk);
-    __syncthreads();
-    cn = uniform32(sl.claim[1]);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
     const Range r = tab_chunk_range(vb, seg, c);
@@ -495,21 +482,16 @@ __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, 
   const uint32_t nch = p.nsum;
   if (blockIdx.x >= nch) return;  // then no chunk is left to claim either
   const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
-  Claimer cl = make_claimer(sum_pools(p), p, nch);
-  uint32_t c = blockIdx.x, cn;
+  const Claimer cl = make_claimer(sum_claims(p), p, nch);
+  uint32_t c = blockIdx.x, cn = second_chunk(p, nch, blockIdx.x);
   Cursor cur, cg;
   u32x4 q[kUnroll], h[kUnroll];
   {
-    uint32_t tk = 0;
-    if (t == 0) tk = claim_issue(cl);
     const Range r = sum_chunk_range(p, c);
     cursor_load(p, cur, r.seg);
     cg = cur;
     load_group<kNtSum>(p, cur, r.b, r.e, 0, range_steps(r), q);
     load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, 0, range_steps(r), h);
-    if (t == 0) sl.claim[1] = claim_resolve(cl, tk);
-    __syncthreads();
-    cn = uniform32(sl.claim[1]);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
     const Range r = sum_chunk_range(p, c);
@@ -668,14 +650,24 @@ __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& 
       }
       if (ACC && !scale) continue;
       scale_scalars<DT>(p, v, s64, s32);
-      // the worker's own chunk: with the +=, the sum chunk it summed; else
-      // the first scale chunk, which it takes without a claim
-      const bool own = ACC ? (uint32_t)v < p.nsum : (uint32_t)v < p.nchs;
-      if (own) {
-        const Range c = ACC ? sum_chunk_range(p, (uint32_t)v) : tab_chunk_range(p.fus_vb, p.fus_seg, (uint32_t)v);
-        Cursor cur;
-        cursor_load(p, cur, c.seg);
-        scale_steps<DT>(p, cur, c.b, c.e, 0, range_steps(c), s64, s32);
+      // the worker's own chunks: with the +=, the sum chunk it summed; else
+      // the two scale chunks it takes without a claim
+      if constexpr (ACC) {
+        if ((uint32_t)v < p.nsum) {
+          const Range c = sum_chunk_range(p, (uint32_t)v);
+          Cursor cur;
+          cursor_load(p, cur, c.seg);
+          scale_steps<DT>(p, cur, c.b, c.e, 0, range_steps(c), s64, s32);
+        }
+      } else {
+        for (uint32_t k = 0; k < 2; ++k) {
+          const uint32_t own = (uint32_t)v + k * (uint32_t)p.nworkers;
+          if (own >= p.nchs) break;
+          const Range c = tab_chunk_range(p.fus_vb, p.fus_seg, own);
+          Cursor cur;
+          cursor_load(p, cur, c.seg);
+          scale_steps<DT>(p, cur, c.b, c.e, 0, range_steps(c), s64, s32);
+        }
       }
     }
     __syncthreads();
@@ -683,11 +675,11 @@ __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& 
 }
 
 // Second ticket, at the very end.  The last workgroup to finish -- every
-// other one has then left the pools and the block states alone -- resets the
-// scale pools and, after a fused launch, scales whatever blocks are still
-// handed back (the decision is published before the deciding workgroup
-// finishes, so it is known here), clears their states and records how many
-// workers handed their block back.
+// other one has then left the claim counter and the block states alone --
+// resets the scale pass's claim counter and, after a fused launch, scales
+// whatever blocks are still handed back (the decision is published before
+// the deciding workgroup finishes, so it is known here), clears their
+// states and records how many workers handed their block back.
 template <int DT, bool ACC = false>
 __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool fused, HandSlots& hs, int* flag,
                                        const AccSrc& A = AccSrc{}) {
@@ -722,7 +714,7 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
       atomic_st(&p.bcast[0], kUndecided);
     }
   }
-  if (threadIdx.x == 0) reset_pools(scale_pools(p));
+  if (threadIdx.x == 0) atomic_st(scale_claims(p), 0u);
 }
 
 // ---------------------------------------------------------------- kernels
@@ -755,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, AvgSr
     const double S = partials_sum(p, red);
     poison_partials(p);
     if (threadIdx.x == 0) {
-      reset_pools(sum_pools(p));
+      atomic_st(sum_claims(p), 0u);
       write_norm(res, S, avg);
       res->scale = 1.0;
       res->clipped = 0;
@@ -835,7 +827,9 @@ __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSl
       store_group<NTS>(p, cur, r.b, r.e, bs.nreg + k0, bs.nsteps,
                        [&](int u) { return scale_vec<DT>(keep_lds[(k0 + u) * kThreads + t], s64, s32); });
   }
+  GCLIP_STAMP(GCLIP_STAMP_BLOCK_WRITTEN);
   scale_chunks<DT, NTS>(p, sl, p.fus_vb, p.fus_seg, p.nchs, s64, s32);
+  GCLIP_STAMP(GCLIP_STAMP_CHUNKS_SCALED);
 }
 
 // With the += (ACC): the block's sums, scaled when `scale`, and -- only then
@@ -897,6 +891,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   __shared__ int bc_skip;
   const int w = blockIdx.x;
   const uint32_t t = threadIdx.x;
+  GCLIP_STAMP(GCLIP_STAMP_START);
 
   if constexpr (ACC) {
     static_assert(kSumChunksPerWorker == 1,
@@ -905,6 +900,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   } else {
     norm_chunks<DT>(p, sl);
   }
+  GCLIP_STAMP(GCLIP_STAMP_CHUNKS_SUMMED);
   double acc[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
@@ -998,6 +994,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       }
     }
   }
+  GCLIP_STAMP(GCLIP_STAMP_BLOCK_READ);
   double sc = 0.0;
   if constexpr (ACC) {
     sc = accum_scalars<DT>(p, A, w);
@@ -1032,7 +1029,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
       // the decision is published by value: the word is the flag, so the
       // workgroups waiting for it need no ordering against any other store
       atomic_st(&p.bcast[0], d.skip ? kDecidedSkip : __builtin_bit_cast(uint64_t, d.s));
-      reset_pools(sum_pools(p));
+      atomic_st(sum_claims(p), 0u);
       // every workgroup has arrived, so each has read the loss scale it uses:
       // the state can move on to the next step's
       if (amp.st) amp_update(amp.st, nonfinite_of(S, avg), amp);
@@ -1062,6 +1059,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
     }
   }
   __syncthreads();
+  if (!gave_up) GCLIP_STAMP(GCLIP_STAMP_DECISION_SEEN);
   const double s64 = bc_s;
   if constexpr (ACC) {
     if (!gave_up) {
@@ -1084,6 +1082,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
     }
   }
   finish<DT, ACC>(p, res, true, hs, &flag, A);
+  GCLIP_STAMP(GCLIP_STAMP_END);
 }
 
 template <int DT, bool NTS>
@@ -1187,3 +1186,18 @@ hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu) {
 }
 
 }  // namespace gclip
+
+#ifdef GCLIP_PHASE_STAMPS
+extern "C" gclip_status gclip_phase_stamps(uint64_t* host, int32_t n_workers, int64_t* ticks_per_s) {
+  if (!host || !ticks_per_s || n_workers < 0 || n_workers > GCLIP_STAMP_WORKERS) return GCLIP_EINVAL;
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbol(host, HIP_SYMBOL(gclip::g_phase_stamps),
+                            (size_t)n_workers * GCLIP_STAMP_POINTS * sizeof(uint64_t), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return gclip::hip_fail(e);
+  *ticks_per_s = (int64_t)khz * 1000;
+  return GCLIP_OK;
+}
+#endif

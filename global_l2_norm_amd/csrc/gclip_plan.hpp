@@ -13,9 +13,9 @@
 //     list of single elements ("scalars"), shared out equally by worker;
 //   - the vector space ends with one "block" of rb vectors per worker
 //     (workgroup): what the fused kernel keeps on chip between its passes;
-//   - the rest, the streamed region [0, sb), is cut into chunks that the
-//     workers claim at run time, so that the XCDs that stream faster take
-//     more of them: "sum chunks" of cvs vectors for the summing passes (a
+//   - the rest, the streamed region [0, sb), is cut into chunks; each
+//     worker takes two without a claim, the rest are claimed at run time, so
+//     that the XCDs that stream faster take more of them: "sum chunks" of cvs vectors for the summing passes (a
 //     sum chunk's partial goes to a slot of its own, so the content and
 //     order of the final sum do not depend on which worker took which
 //     chunk), and "scale chunks" for the fused kernel's scale pass.  The
@@ -104,15 +104,15 @@ constexpr uint64_t kDecidedSkip = 0x7ff4000000000002ull;
 // Device view of a plan plus the list's workspace (all device addresses).
 // sync holds 128-byte lines of counters (one line per counter group, so that
 // the XCDs do not share lines):
-//   line 0                       count of handed-back blocks
-//   lines 1 .. kPools            chunk pools of the summing passes (one per XCD)
-//   lines 1 + kPools ..          chunk pools of the scaling passes
-//   lines 1 + 2 kPools ..        arrival tickets: one per XCD group, then the top one
-//   lines 2 + 3 kPools ..        finish tickets: one per XCD group, then the top one
-constexpr int kPools = 8;
+//   line 0                           count of handed-back blocks
+//   line 1                           claim counter of the summing passes
+//   line 2                           claim counter of the scaling passes
+//   lines 3 .. 3 + kTicketGroups     arrival tickets: one per XCD group, then the top one
+//   lines 4 + kTicketGroups ..       finish tickets: one per XCD group, then the top one
+constexpr int kTicketGroups = 8;
 constexpr int64_t kNtStoreMinBytes = (int64_t)1 << 30;
 constexpr int kSyncLineWords = 32;  // 128 bytes
-constexpr int kSyncWords = kSyncLineWords * (3 + 4 * kPools);
+constexpr int kSyncWords = kSyncLineWords * (5 + 2 * kTicketGroups);
 
 struct DevPlan {
   const uint64_t* seg_vbegin;

@@ -17,16 +17,25 @@ from synth import gradsets as gs
 from tests.abi_util import ESIZE, TAG, check_walk, fake_layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+# the diagnostic header's call is exported by the phase-stamps build only
+STAMPS_HEADER = os.path.join(ROOT, "include", "gclip_stamps.h")
+STAMPS_LIB = os.path.join(ROOT, "global_l2_norm_amd", "_stamps", "libgclip.so")
+HEADERS = sorted(h for h in glob.glob(os.path.join(ROOT, "include", "*.h")) if h != STAMPS_HEADER)
 
 
-def declared_functions():
+def declared_functions(headers=HEADERS):
     names = set()
-    for h in HEADERS:
+    for h in headers:
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         names |= set(re.findall(r"\b(gclip_[a-z_]+)\s*\(", text))
     return sorted(names)
+
+
+def exported_functions(lib_path):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True, text=True,
+                         check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.strip()}
 
 
 def test_header_declares_the_boundary():
@@ -37,14 +46,25 @@ def test_header_declares_the_boundary():
 
 
 def test_library_exports_every_declared_function():
-    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
-                         check=True).stdout
-    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    exported = exported_functions(_lib.LIB_PATH)
     missing = [n for n in declared_functions() if n not in exported]
     assert not missing, missing
     assert set(_lib.EXPORTS) == set(declared_functions())
     for n in declared_functions():
         assert hasattr(_lib.lib, n)
+
+
+def test_phase_stamps_only_in_the_diagnostic_build():
+    """The library records no phase timeline and does not export its reader;
+    the --phase-stamps build exports it besides every other call."""
+    stamps_calls = declared_functions([STAMPS_HEADER])
+    assert stamps_calls == ["gclip_phase_stamps"]
+    assert not set(stamps_calls) & exported_functions(_lib.LIB_PATH)
+    if not os.path.exists(STAMPS_LIB):
+        pytest.skip("the --phase-stamps build is not there (python -m global_l2_norm_amd.build --phase-stamps)")
+    exported = exported_functions(STAMPS_LIB)
+    missing = [n for n in declared_functions() + stamps_calls if n not in exported]
+    assert not missing, missing
 
 
 def test_version_and_status_strings():
