@@ -303,6 +303,8 @@ def main():
     if a.path == "ref":
         return bench_ref(a, flush)
     if a.path == "accum":
+        if a.phase_stamps:
+            return bench_phases_accum(a, G, gs, flush)
         return bench_accum(a, G, gs, flush)
     g = gs.make(a.config)
     esize = 4 if g.dtype == "f32" else 2
@@ -411,26 +413,69 @@ def main():
     return 0
 
 
+XCDS = 8
 PHASES = [(1, "sum chunks done"), (2, "block read into VGPRs and LDS"), (3, "decision seen"),
           (4, "block written back from VGPRs and LDS"), (5, "scale chunks done"), (6, "end")]
 
 
 def bench_phases(a, G, g, tensors, pristine, flush, gl):
-    """The fused kernel's phase timeline over `steps` cold steps: per step,
-    every workgroup's stamps from the earliest workgroup start; per phase,
-    the median over steps of the median workgroup and of the last one (a
-    workgroup that handed its block back counts up to the block read)."""
+    """The fused clip's phase timeline (gclip_clip_ on the fused path)."""
+    gl.set_path(G.GCLIP_PATH_FUSED)
+
+    def prepare():
+        for t, p in zip(tensors, pristine):
+            t.copy_(p)
+        if not a.no_flush:
+            flush.sum()
+
+    title = f"k_grad_clip_fused, {a.config} ({g.dtype}, {g.numel} elements)"
+    rc = phase_timeline(a, G, gl.info()["n_workers"], prepare,
+                        lambda: gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite),
+                        lambda: gl.read(g.error_if_nonfinite), title)
+    gl.close()
+    return rc
+
+
+def bench_phases_accum(a, G, gs, flush):
+    """The fused += kernel's phase timeline (gclip_accumulate_clip_ on the
+    four-microbatch list of --path accum)."""
+    buf, last = gs.andrea120m_f32_accum4_parts()
+    acc = upload(buf.arrays, "f32")
+    contrib = upload(last.arrays, "f32")
+    pristine = [t.clone() for t in acc]
+    gl = G.GradList(acc)
+    gl.set_path(G.GCLIP_PATH_FUSED)
+    c = G.Contribution(gl, contrib)
+
+    def prepare():
+        for x, y in zip(acc, pristine):
+            x.copy_(y)
+        if not a.no_flush:
+            flush.sum()
+
+    title = f"k_accum_clip_fused, andrea120m_f32_accum4 (f32, {buf.numel} elements)"
+    rc = phase_timeline(a, G, gl.info()["n_workers"], prepare, lambda: gl.accumulate_clip_(c, 1.0, buf.avg_factor),
+                        gl.read, title)
+    c.close()
+    gl.close()
+    return rc
+
+
+def phase_timeline(a, G, nw, prepare, launch, read, title):
+    """Run prepare() (restore, flush) and launch() (one fused launch, timed
+    with HIP events) warmup + steps times and print the launch's
+    phase timeline: per step, every workgroup's stamps from the earliest
+    workgroup start; per phase, the median over steps of the median
+    workgroup and of the last one (a workgroup that handed its block back
+    counts up to the block read)."""
     import ctypes
 
     import numpy as np
     import torch
 
-    lib = G._lib.lib
-    f = lib.gclip_phase_stamps
+    f = G._lib.lib.gclip_phase_stamps
     f.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
     f.restype = ctypes.c_int32
-    gl.set_path(G.GCLIP_PATH_FUSED)
-    nw = gl.info()["n_workers"]
     points = 8
     buf = np.zeros(nw * points, dtype=np.uint64)
     rate = ctypes.c_int64(0)
@@ -438,13 +483,10 @@ def bench_phases(a, G, g, tensors, pristine, flush, gl):
     ev_ms = []
     stream = torch.cuda.current_stream()
     for i in range(a.warmup + a.steps):
-        for t, p in zip(tensors, pristine):
-            t.copy_(p)
-        if not a.no_flush:
-            flush.sum()
+        prepare()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        gl.clip_(g.max_norm, g.avg_factor, g.error_if_nonfinite)
+        launch()
         e1.record(stream)
         torch.cuda.synchronize()
         st = f(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), nw, ctypes.byref(rate))
@@ -459,15 +501,18 @@ def bench_phases(a, G, g, tensors, pristine, flush, gl):
             ok = s[:, k] >= s[:, 0]
             v = (s[ok, k] - t0) / rate.value * 1e6
             row[k] = (float(np.median(v)), float(v.max()), int(ok.sum())) if ok.any() else None
+            # workgroups are dealt to the XCDs in turn: XCD of w = w % XCDS
+            xcd = np.arange(nw)[ok] % XCDS
+            row[("xcd", k)] = [float(np.median(v[xcd == x])) if (xcd == x).any() else float("nan")
+                               for x in range(XCDS)]
         per_step.append(row)
         ev_ms.append(e0.elapsed_time(e1))
-    st, r = gl.read(g.error_if_nonfinite)
-    gl.close()
-    print(f"# phase timeline of k_grad_clip_fused, {a.config} ({g.dtype}, {g.numel} elements), "
-          f"{a.steps} cold steps after {a.warmup} warm-up")
+    st, r = read()
+    print(f"# phase timeline of {title}, {a.steps} cold steps after {a.warmup} warm-up")
     print(f"# {nw} workgroups; wall clock {rate.value / 1e6:.0f} MHz; norm {r['norm']:.6g}, scale {r['scale']:.6g}, "
           f"handed back {r['handed_back']} (last step)")
-    print(f"# event time per step: median {statistics.median(ev_ms) * 1e3:.1f} us")
+    print(f"# event time per launch: median "
+          f"{statistics.median(ev_ms) * 1e3:.1f} us")
     print(f"# kernel sources sha256/16: {kernel_source_hash()}")
     print("| phase (times from the first workgroup's start) | median workgroup | last workgroup | workgroups |")
     print("|---|---|---|---|")
@@ -481,6 +526,16 @@ def bench_phases(a, G, g, tensors, pristine, flush, gl):
         cnt = min(x[2] for x in rows)
         print(f"| {name} | {med:.1f} us | {last:.1f} us | {cnt} |")
     print("# each figure is the median over the steps of that step's median (or last) workgroup")
+    print()
+    print("| phase: median workgroup of each XCD (workgroup index mod 8) | "
+          + " | ".join(f"XCD {x}" for x in range(XCDS)) + " |")
+    print("|---|" + "---|" * XCDS)
+    for k, name in PHASES:
+        rows = [row[("xcd", k)] for row in per_step if row.get(k) is not None]
+        if not rows:
+            continue
+        cells = [statistics.median(r_[x] for r_ in rows) for x in range(XCDS)]
+        print(f"| {name} | " + " | ".join(f"{c:.1f}" for c in cells) + " |")
     return 0 if st == 0 and r["status"] == 0 else 1
 
 

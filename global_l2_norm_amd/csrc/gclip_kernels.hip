@@ -855,7 +855,9 @@ __device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& s
         return scale ? scale_vec<DT>(n, s64, s32) : n;
       });
   }
+  GCLIP_STAMP(GCLIP_STAMP_BLOCK_WRITTEN);
   if (scale && blockIdx.x < p.nsum) scale_range<DT, NTS>(p, sum_chunk_range(p, blockIdx.x), s64, s32);
+  GCLIP_STAMP(GCLIP_STAMP_CHUNKS_SCALED);
 }
 
 // The whole path in one launch.  Phase 1 sums the chunks of the streamed

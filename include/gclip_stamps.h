@@ -4,10 +4,12 @@
  *
  * The grad clip lesson (unhomeschool.com, ru), section "ANDREA's three-kernel
  * pipeline", splits the clip into a summing pass, a final reduction with the
- * decision, and a scaling pass.  The fused kernel (gclip_clip_ with the fused
- * path) runs all three in one launch; this build records, per workgroup, the
- * wall-clock time at which each of its phases ended, so that the time of one
- * launch can be split between them.
+ * decision, and a scaling pass.  The fused kernels (gclip_clip_ and
+ * gclip_accumulate_clip_ on the fused path) run all three in one launch; this
+ * build records, per workgroup, the wall-clock time at which each of its
+ * phases ended, so that the time of one launch can be split between them.
+ * With the += the summing pass also writes the sums of the streamed region,
+ * and the scaling pass rescales the workgroup's own sum chunk.
  *
  * Only the library built with -DGCLIP_PHASE_STAMPS exports gclip_phase_stamps
  * (`python -m global_l2_norm_amd.build --phase-stamps` writes it to
@@ -34,8 +36,8 @@
 #define GCLIP_STAMP_CHUNKS_SUMMED 1   /* had summed its chunks of the streamed region */
 #define GCLIP_STAMP_BLOCK_READ 2      /* had read its block into VGPRs and LDS */
 #define GCLIP_STAMP_DECISION_SEEN 3   /* knew the decision (every wave) */
-#define GCLIP_STAMP_BLOCK_WRITTEN 4   /* had issued the writes of its block (when it scales) */
-#define GCLIP_STAMP_CHUNKS_SCALED 5   /* had scaled its chunks of the streamed region (when it scales) */
+#define GCLIP_STAMP_BLOCK_WRITTEN 4   /* had issued the writes of its block (when it writes) */
+#define GCLIP_STAMP_CHUNKS_SCALED 5   /* had scaled its chunks of the streamed region (when it writes) */
 #define GCLIP_STAMP_END 6             /* was done, finish ticket included */
 
 #ifdef __cplusplus
