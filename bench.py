@@ -104,10 +104,9 @@ def pmc_summary_path(kernels, config):
     return os.path.join(PROFILES, f"{kernels}__{config}__pmc.txt")
 
 
-def read_traffic(kernels, config):
-    """HBM bytes per step of the given kernel(s) ('a+b' for a two-kernel
-    path) from the committed PMC summary, or None when it is missing or was
-    taken on other kernel source."""
+def _pmc_summary(kernels, config):
+    """The key: value lines of a committed PMC summary, or None when it is
+    missing or was taken on other kernel source."""
     path = pmc_summary_path(kernels, config)
     if not os.path.exists(path):
         return None
@@ -118,10 +117,35 @@ def read_traffic(kernels, config):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    try:
-        return int(float(kv["hbm_bytes_per_dispatch"]))
-    except (KeyError, ValueError):
+    return kv
+
+
+def read_traffic(kernels, config, kernel=None):
+    """HBM bytes per step of the given kernel(s) ('a+b' for a two-kernel
+    path) from the committed PMC summary -- or, with `kernel`, of that one
+    kernel of the summary per launch -- or None when the summary is missing
+    or was taken on other kernel source."""
+    kv = _pmc_summary(kernels, config)
+    if kv is None:
         return None
+    try:
+        if kernel is None:
+            return int(float(kv["hbm_bytes_per_dispatch"]))
+        fetch_cal = float(kv["fetch_calibration (counter bytes / copy bytes)"])
+        write_cal = float(kv["write_calibration (counter bytes / copy bytes)"])
+        return int(float(kv[f"fetch_kib_per_dispatch {kernel}"]) * 1024 / fetch_cal
+                   + float(kv[f"write_kib_per_dispatch {kernel}"]) * 1024 / write_cal)
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+def traffic_fields(roofline, traffic, seconds):
+    """Add the measured-traffic rate and fraction to a roofline object."""
+    roofline["traffic"] = traffic
+    if traffic is not None:
+        roofline["traffic_gbps"] = round(traffic / seconds / 1e9, 1)
+        roofline["traffic_frac"] = round(traffic / seconds / 1e9 / HBM_PEAK_GBPS, 4)
+    return roofline
 
 
 def cpu_model():
@@ -358,10 +382,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernels,
                 "resident_bytes": info["resident_vectors"] * 16}
-    if traffic is not None:
-        # the rate of the bytes that actually crossed HBM, against the same peak
-        roofline["traffic_gbps"] = round(traffic / (mean_ms * 1e-3) / 1e9, 1)
-        roofline["traffic_frac"] = round(traffic / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    # the rate of the bytes that actually crossed HBM, against the same peak
+    traffic_fields(roofline, traffic, mean_ms * 1e-3)
     if not a.profile_pass:
         # attainable: the reference read of the list's bytes, plus (when the
         # step writes) the reference in-place copy of them, cold, same events
@@ -659,10 +681,12 @@ def bench_adamw(a, G, g, grads, pristine, flush, gl):
         "separate_ms_per_step": round(sep_ms, 5),
         "separate_algorithmic_bytes": 3 * n * esize + adam_bytes,
         "saved_vs_separate": round(1.0 - step_ms / sep_ms, 4),
-        "roofline": {"bound": "hbm", "achieved": round(adam_bytes / (adam_ms * 1e-3) / 1e9, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(adam_bytes / (adam_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "k_adamw_clip", "ms_per_launch": round(adam_ms, 5)},
+        "roofline": traffic_fields(
+            {"bound": "hbm", "achieved": round(adam_bytes / (adam_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+             "unit": "GB/s", "frac": round(adam_bytes / (adam_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+             "kernel": "k_adamw_clip", "ms_per_launch": round(adam_ms, 5)},
+            read_traffic("k_grad_norm_partial+k_adamw_clip", a.config, kernel="k_adamw_clip"), adam_ms * 1e-3),
+        "step_traffic": read_traffic("k_grad_norm_partial+k_adamw_clip", a.config),
     }
     if cpu is not None:
         out["cpu_baseline"] = cpu
@@ -733,6 +757,11 @@ def bench_amp(a, G, g, grads, pristine, flush, gl):
         "host_factor_ms_per_step": round(plain_ms, 5),
         "loss_scale_overhead_ms": round(ms - plain_ms, 5),
         "state_after": {"scale": state[0], "growth_tracker": state[1], "found_inf": state[2]},
+        "roofline": traffic_fields({"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                                    "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                                    "kernel": "k_grad_clip_fused"},
+                                   read_traffic("k_grad_clip_fused", f"{a.config}_loss_scaled")
+                                   if gl.info()["path"] == G.GCLIP_PATH_FUSED else None, ms * 1e-3),
     }
     if not a.no_cpu_baseline:
         import oracle
@@ -826,8 +855,9 @@ def bench_accum(a, G, gs, flush):
         "separate_ms_per_step": round(sep_ms, 5),
         "separate_note": "torch._foreach_add_ then gclip_clip_ (fused kernel)",
         "saved_vs_separate": round(1.0 - ms / sep_ms, 4),
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_accum_clip_fused"},
+        "roofline": traffic_fields({"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                    "frac": round(gbps / HBM_PEAK_GBPS, 4), "kernel": "k_accum_clip_fused"},
+                                   read_traffic("k_accum_clip_fused", "andrea120m_f32_accum4_last"), ms * 1e-3),
         "status": st,
     }
     if not a.no_cpu_baseline:
@@ -908,8 +938,23 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
         "tensor_norms_ms": round(norm_ms, 5),
         "tensor_norms_gbps": round(norm_gbps, 1),
         "tensor_norms_pct_hbm_peak": round(100.0 * norm_gbps / HBM_PEAK_GBPS, 2),
+        "roofline": traffic_fields({"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                                    "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                                    "kernel": "k_tensor_partial+k_tensor_clip"},
+                                   read_traffic("k_tensor_partial+k_tensor_clip", a.config), ms * 1e-3),
         "status": st,
     }
+    if not a.profile_pass:
+        # attainable: the reference read of the list, plus the reference
+        # in-place copy of the share of it that the clip writes
+        nref, rt = ref_times(g.numel * esize, a.steps, flush, stream, copy_too=False)
+        wshare = clipped_elems / g.numel if g.numel else 0.0
+        att_ms = rt["read"] + rt["in_place"] * wshare
+        out["roofline"]["attainable"] = round(alg / (att_ms * 1e-3) / 1e9, 1)
+        out["roofline"]["frac_of_attainable"] = round(gbps / out["roofline"]["attainable"], 4)
+        out["roofline"]["attainable_basis"] = (f"gclip_ref_read {rt['read'] * 1e3:.1f} us + {wshare:.4f} x "
+                                               f"gclip_ref_copy in place {rt['in_place'] * 1e3:.1f} us over "
+                                               f"{nref} bytes, cold")
     if not a.no_cpu_baseline:
         import oracle
         work = [x.copy() for x in g.arrays]
