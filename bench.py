@@ -340,6 +340,8 @@ def main():
     if a.path == "amp":
         return bench_amp(a, G, g, tensors, pristine, flush, gl)
     if a.path == "per_tensor":
+        if a.phase_stamps:
+            return bench_phases_per_tensor(a, G, g, tensors, pristine, flush, gl)
         return bench_per_tensor(a, G, g, tensors, pristine, flush, gl)
     if a.phase_stamps:
         return bench_phases(a, G, g, tensors, pristine, flush, gl)
@@ -438,6 +440,9 @@ def main():
 XCDS = 8
 PHASES = [(1, "sum chunks done"), (2, "block read into VGPRs and LDS"), (3, "decision seen"),
           (4, "block written back from VGPRs and LDS"), (5, "scale chunks done"), (6, "end")]
+TENSOR_PHASES = [(1, "streamed run summed"), (2, "resident pieces read into VGPRs and LDS"),
+                 (7, "pieces counted, completed tensors summed"), (3, "decision seen"),
+                 (4, "resident pieces written"), (5, "claimed pieces scaled"), (6, "end")]
 
 
 def bench_phases(a, G, g, tensors, pristine, flush, gl):
@@ -483,7 +488,26 @@ def bench_phases_accum(a, G, gs, flush):
     return rc
 
 
-def phase_timeline(a, G, nw, prepare, launch, read, title):
+def bench_phases_per_tensor(a, G, g, tensors, pristine, flush, gl):
+    """The one-launch per-tensor clip's phase timeline (gclip_clip_per_tensor_
+    on the fused path, at the per-tensor max_norm of --path per_tensor)."""
+    gl.set_path(G.GCLIP_PATH_FUSED)
+
+    def prepare():
+        for t, p in zip(tensors, pristine):
+            t.copy_(p)
+        if not a.no_flush:
+            flush.sum()
+
+    title = f"k_tensor_clip_fused, {a.config} ({g.dtype}, {g.numel} elements), per-tensor max_norm {PER_TENSOR_MAX_NORM}"
+    rc = phase_timeline(a, G, gl.info()["n_workers"], prepare,
+                        lambda: gl.clip_per_tensor_(PER_TENSOR_MAX_NORM, g.avg_factor), gl.read, title,
+                        phases=TENSOR_PHASES)
+    gl.close()
+    return rc
+
+
+def phase_timeline(a, G, nw, prepare, launch, read, title, phases=PHASES):
     """Run prepare() (restore, flush) and launch() (one fused launch, timed
     with HIP events) warmup + steps times and print the launch's
     phase timeline: per step, every workgroup's stamps from the earliest
@@ -519,7 +543,7 @@ def phase_timeline(a, G, nw, prepare, launch, read, title):
         s = buf.reshape(nw, points).astype(np.int64)
         t0 = s[:, 0].min()
         row = {}
-        for k, _ in PHASES:
+        for k, _ in phases:
             ok = s[:, k] >= s[:, 0]
             v = (s[ok, k] - t0) / rate.value * 1e6
             row[k] = (float(np.median(v)), float(v.max()), int(ok.sum())) if ok.any() else None
@@ -538,7 +562,7 @@ def phase_timeline(a, G, nw, prepare, launch, read, title):
     print(f"# kernel sources sha256/16: {kernel_source_hash()}")
     print("| phase (times from the first workgroup's start) | median workgroup | last workgroup | workgroups |")
     print("|---|---|---|---|")
-    for k, name in PHASES:
+    for k, name in phases:
         rows = [row[k] for row in per_step if row.get(k) is not None]
         if not rows:
             print(f"| {name} | — | — | 0 |")
@@ -552,7 +576,7 @@ def phase_timeline(a, G, nw, prepare, launch, read, title):
     print("| phase: median workgroup of each XCD (workgroup index mod 8) | "
           + " | ".join(f"XCD {x}" for x in range(XCDS)) + " |")
     print("|---|" + "---|" * XCDS)
-    for k, name in PHASES:
+    for k, name in phases:
         rows = [row[("xcd", k)] for row in per_step if row.get(k) is not None]
         if not rows:
             continue
@@ -879,9 +903,11 @@ PER_TENSOR_MAX_NORM = 0.5
 
 def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
     """Per-tensor clipping (every tensor by its own norm) at max_norm 0.5,
-    which clips the large matrices and leaves the norm vectors alone; and the
-    per-tensor norms alone.  Gradients are restored and the caches flushed
-    before every step; each step is timed with HIP events."""
+    which clips the large matrices and leaves the norm vectors alone: in one
+    launch (the fused path, timed as the step), and on the split path (two
+    kernels; three with the stop switch); and the per-tensor norms alone.
+    Gradients are restored and the caches flushed before every step; each
+    step is timed with HIP events."""
     import torch
     stream = torch.cuda.current_stream()
     esize = 4 if g.dtype == "f32" else 2
@@ -893,11 +919,12 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
             flush.sum()
 
     def run(which, ev):
+        gl.set_path(G.GCLIP_PATH_SPLIT if which.startswith("split") else G.GCLIP_PATH_AUTO)
         restore()
         ev[0].record(stream)
-        if which == "clip":
+        if which in ("clip", "split"):
             gl.clip_per_tensor_(PER_TENSOR_MAX_NORM, g.avg_factor)
-        elif which == "clip_stop":
+        elif which in ("clip_stop", "split_stop"):
             # with the stop switch on (no NaN/Inf here, so the same work):
             # the reduction and decisions in a kernel of their own
             gl.clip_per_tensor_(PER_TENSOR_MAX_NORM, g.avg_factor, True)
@@ -906,7 +933,7 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
         ev[1].record(stream)
 
     times = {}
-    for which in ("clip", "clip_stop", "norms"):
+    for which in ("clip", "clip_stop", "split", "split_stop", "norms"):
         for _ in range(a.warmup):
             run(which, [torch.cuda.Event(enable_timing=True) for _ in range(2)])
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
@@ -917,6 +944,7 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
         if which == "clip":
             st, r = gl.read()
             tr = gl.read_tensors()
+            fused = gl.info()["path"] == G.GCLIP_PATH_FUSED
     numel = [t.numel() for t in grads]
     clipped_elems = sum(n for n, t in zip(numel, tr) if float(t["scale"]) != 1.0)
     alg = g.numel * esize + 2 * clipped_elems * esize
@@ -924,24 +952,31 @@ def bench_per_tensor(a, G, g, grads, pristine, flush, gl):
     norm_ms = statistics.fmean(times["norms"])
     gbps = alg / (ms * 1e-3) / 1e9
     norm_gbps = g.numel * esize / (norm_ms * 1e-3) / 1e9
+    pt_kernels = "k_tensor_clip_fused" if fused else "k_tensor_partial+k_tensor_clip"
     out = {
         "metric": f"per-tensor clip GB/s, {a.config}", "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": g.dtype, "data": "synthetic",
         "config": {"workload": WORKLOADS.get(a.config, a.config) + f"; per-tensor max_norm {PER_TENSOR_MAX_NORM}",
-                   "name": a.config, "launches_per_step": 2, "algorithmic_bytes_per_step": alg,
+                   "name": a.config, "path": "fused" if fused else "split",
+                   "launches_per_step": 1 if fused else 2, "algorithmic_bytes_per_step": alg,
                    "tensors_clipped": int(sum(int(t["clipped"]) for t in tr)), "n_tensors": len(grads),
                    "elements_written": clipped_elems},
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "stop_switch_ms_per_step": round(statistics.fmean(times["clip_stop"]), 5),
-        "stop_switch_note": "error_if_nonfinite=True: partial, decide, scale (three launches)",
+        "stop_switch_note": "error_if_nonfinite=True" + (", the same one launch" if fused else
+                                                          ": partial, decide, scale (three launches)"),
+        "split_ms_per_step": round(statistics.fmean(times["split"]), 5),
+        "split_stop_switch_ms_per_step": round(statistics.fmean(times["split_stop"]), 5),
+        "split_note": "the split path: partial, then decide-and-scale per piece (two launches); with the stop "
+                      "switch partial, decide, scale (three)",
         "tensor_norms_ms": round(norm_ms, 5),
         "tensor_norms_gbps": round(norm_gbps, 1),
         "tensor_norms_pct_hbm_peak": round(100.0 * norm_gbps / HBM_PEAK_GBPS, 2),
         "roofline": traffic_fields({"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                                    "kernel": "k_tensor_partial+k_tensor_clip"},
-                                   read_traffic("k_tensor_partial+k_tensor_clip", a.config), ms * 1e-3),
+                                    "kernel": pt_kernels},
+                                   read_traffic(pt_kernels, a.config), ms * 1e-3),
         "status": st,
     }
     if not a.profile_pass:

@@ -44,6 +44,7 @@ struct gclip_list {
   void* blob = nullptr;
   int device = 0;
   bool fused_ok = false;
+  bool tensor_fused_ok = false;  // the one-launch per-tensor clip fits on a compute unit
   int32_t path = GCLIP_PATH_SPLIT;
   int64_t wait_us = kDefaultWaitUs;
   uint64_t clock_khz = 0;  // device wall clock
@@ -231,6 +232,11 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       return hip_fail(e);
     }
     L->fused_ok = bpc >= 1 && clk > 0;
+    if ((e = gclip::tensor_fused_capacity(dtype, &bpc)) != hipSuccess) {
+      delete L;
+      return hip_fail(e);
+    }
+    L->tensor_fused_ok = L->fused_ok && bpc >= 1;
     L->path = L->fused_ok ? GCLIP_PATH_FUSED : GCLIP_PATH_SPLIT;
     L->clock_khz = clk > 0 ? (uint64_t)clk : 0;
     L->wait_ticks = (uint64_t)L->wait_us * L->clock_khz / 1000;
@@ -256,9 +262,10 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
       off = round_up(off + (bytes ? bytes : 8), 256);
       return at;
     };
+    const size_t ntt = (size_t)P.n_tensors, nwb = (size_t)P.nworkers + 1;
     const size_t o_tpc = take(ntp * sizeof(gclip::TPiece)), o_tfi = take(ntf * 4), o_tpa = take(ntp * 8),
-                 o_tsc = take((size_t)P.n_tensors * sizeof(gclip_tensor_result)),
-                 o_tsum = take((size_t)P.n_tensors * 8), o_tsy = take(128);
+                 o_tsc = take(ntt * sizeof(gclip_tensor_result)), o_tsum = take(ntt * 8), o_tsy = take(128),
+                 o_trb = take(nwb * 4), o_trs = take(nwb * 4), o_tcn = take(ntt * 4), o_tfa = take(ntt * 8);
     if ((e = hipMalloc(&L->blob, off)) != hipSuccess) {
       delete L;
       g_last_hip = (int32_t)e;
@@ -271,9 +278,13 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     };
     std::vector<unsigned char> image(PL.header);
     gclip::plan_image(P, PL, image.data());
+    // every tensor's factor slot empty (see the one-launch per-tensor clip)
+    const std::vector<uint64_t> no_factor(ntt, gclip::kUndecided);
     if ((e = hipMemset(L->blob, 0, off)) != hipSuccess || (e = up(0, image.data(), PL.header)) ||
         (e = up(o_tpc, L->tplan.pieces.data(), ntp * sizeof(gclip::TPiece))) ||
-        (e = up(o_tfi, L->tplan.first.data(), ntf * 4)) || (e = hipDeviceSynchronize()) != hipSuccess) {
+        (e = up(o_tfi, L->tplan.first.data(), ntf * 4)) || (e = up(o_trb, L->tplan.run_b.data(), nwb * 4)) ||
+        (e = up(o_trs, L->tplan.res_b.data(), nwb * 4)) || (e = up(o_tfa, no_factor.data(), ntt * 8)) ||
+        (e = hipDeviceSynchronize()) != hipSuccess) {
       (void)hipFree(L->blob);
       delete L;
       return hip_fail(e);
@@ -292,6 +303,11 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
     T.nlive = 0;
     for (size_t k = 0; k + 1 < ntf; ++k) T.nlive += L->tplan.first[k] < L->tplan.first[k + 1] ? 1u : 0u;
     T.nt_store = D.nt_store;
+    T.run_b = reinterpret_cast<const uint32_t*>(b + o_trb);
+    T.res_b = reinterpret_cast<const uint32_t*>(b + o_trs);
+    T.ps = L->tplan.ps;
+    T.tcount = reinterpret_cast<uint32_t*>(b + o_tcn);
+    T.tfac = reinterpret_cast<double*>(b + o_tfa);
     L->tscratch = reinterpret_cast<gclip_tensor_result*>(b + o_tsc);
     L->addrs.assign(addrs, addrs + n_tensors);
     L->numels.assign(numels, numels + n_tensors);
@@ -435,7 +451,10 @@ gclip_status gclip_clip_per_tensor_(gclip_list* list, double max_norm, double av
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const gclip::AvgSrc avg{avg_factor, nullptr};
   hipError_t e;
-  if (!error_if_nonfinite && list->clock_khz > 0) {
+  if (list->path == GCLIP_PATH_FUSED && list->tensor_fused_ok) {
+    e = gclip::launch_tensor_clip_fused(list->dev, list->tdev, list->plan.dtype, avg, max_norm,
+                                        error_if_nonfinite ? 1 : 0, d_tensors, d_result, list->wait_ticks, s);
+  } else if (!error_if_nonfinite && list->clock_khz > 0) {
     e = gclip::launch_tensor_clip(list->tdev, list->plan.dtype, avg, max_norm, d_tensors, d_result,
                                   gather_wait_ticks(list), s);
   } else {

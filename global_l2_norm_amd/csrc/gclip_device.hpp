@@ -329,6 +329,20 @@ __device__ __forceinline__ void write_decision(gclip_result* res, const Decision
   res->decided = 1;
 }
 
+// A tensor's figures from its raw sum, as the per-tensor clip writes them
+// without the stop switch; returns whether it is clipped.
+__device__ __forceinline__ int tensor_figures(gclip_tensor_result* o, double S, double avg, double max_norm) {
+  const double sumsq = (avg * avg) * S;
+  const int nf = nonfinite_of(S, avg);
+  const Decision d = decide(sumsq, nf, max_norm, avg, 0);
+  o->sumsq = sumsq;
+  o->norm = sqrt(sumsq);
+  o->nonfinite = nf;
+  o->scale = d.s == 1.0 ? 1.0 : d.s;
+  o->clipped = d.clipped;
+  return d.clipped;
+}
+
 // The loss scale after a step (dynamic loss scaling as published by
 // Micikevicius et al.): found-inf multiplies it by backoff and restarts the
 // count of clean steps; a clean step counts, and the interval-th one

@@ -21,6 +21,10 @@ hipError_t launch_scale(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         uint64_t wait_ticks, AmpUpdate amp, hipStream_t st);
 hipError_t fused_capacity(int32_t dtype, int* blocks_per_cu);
+hipError_t launch_tensor_clip_fused(const DevPlan& p, const TensorPlan& T, int32_t dtype, AvgSrc avg,
+                                    double max_norm, int err, gclip_tensor_result* out, gclip_result* res,
+                                    uint64_t wait_ticks, hipStream_t st);
+hipError_t tensor_fused_capacity(int32_t dtype, int* blocks_per_cu);
 hipError_t launch_adamw(const AdamPlan& plan, int32_t dtype, const AdamHp& h, double max_norm, AvgSrc avg, int err,
                         gclip_result* res, hipStream_t st);
 hipError_t launch_amp_update(const gclip_result* res, gclip_amp_state* st, double growth, double backoff,

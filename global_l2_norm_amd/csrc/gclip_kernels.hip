@@ -1102,6 +1102,517 @@ __global__ __launch_bounds__(kThreads, 1) void k_accum_clip_fused(DevPlan p, Acc
   clip_fused<DT, NTS, true>(p, A, max_norm, avs, err, res, wait_ticks, AmpUpdate{nullptr, 0.0, 0.0, 0});
 }
 
+// ---------------------------------------------------------------- per-tensor clip in one launch
+// Grad clip lesson, "Two variants: Per-Tensor or Global": every tensor by its
+// own norm, in one launch that keeps part of the list on chip across the
+// decisions, as clip_fused does for the global norm.  It walks the list's
+// per-tensor pieces (TPiece: a run of one tensor, at most one group of
+// vectors, the tensor's single elements on its first piece).  Worker w:
+//   phase 1 -- sums its run of streamed pieces [run_b[w], run_b[w + 1]),
+//     then loads its resident pieces (the last pieces of the list, at most
+//     kTensorResidentPieces) into VGPRs and LDS and sums them.  Each piece's
+//     partial is taken exactly as k_tensor_partial takes it: per lane the
+//     piece's vectors and single elements, per wave an xor butterfly, then
+//     the waves in wave order (the wave sums wait in LDS, so a piece costs
+//     no barrier).  It then counts the pieces of every tensor it summed on
+//     the tensor's counter; the workgroup that completes a tensor sums its
+//     partials in k_tensor_clip's order, stores its figures, raw sum and
+//     factor, and clears the counter.  Then the arrival ticket: the last
+//     workgroup gathers the list's figures as k_tensor_clip's workgroup 0
+//     does, and publishes the decision word (kDecidedSkip when the stop
+//     switch meets a NaN/Inf).  So every figure and every written bit is the
+//     two-kernel path's;
+//   phase 2 -- writes its resident pieces scaled by their tensors' factors
+//     (nothing where a factor is 1), then scales streamed pieces as one-piece
+//     chunks: pieces w and nworkers + w without a claim, the rest claimed.
+// A tensor's factor is read by value: its slot holds kUndecided until the
+// tensor's completer stores the factor (before its arrival ticket, so before
+// the decision), and the last workgroup to finish empties it again.  Waits
+// are bounded as in clip_fused: a workgroup that waits too long for the
+// decision hands its resident pieces and its two unclaimed streamed pieces
+// back, and the workgroups that see the decision -- in the end the last one
+// to finish -- scale those from memory.
+static_assert(kTensorPieceVectors <= kGroupVectors, "a piece is at most one group");
+static_assert(kTensorRegPieces * kUnroll == kRegSteps, "the register pieces fill the register steps");
+static_assert(kTensorLdsPieces * kUnroll <= kLdsSteps, "the LDS pieces fit the LDS steps");
+constexpr uint32_t kPieceSlots = 64;      // piece partials waiting in LDS for their waves' sum
+constexpr int kTensorBatch = 8;           // completed tensors summed at once
+constexpr uint32_t kFactorMissWord = 1;   // line 0 of sync: factors never seen (the launch then fails)
+
+// The piece's vectors into q (one group; lane t holds vector u kThreads + t).
+template <bool NT>
+__device__ __forceinline__ void load_piece(const TPiece& pc, u32x4 (&q)[kUnroll]) {
+  const g_u32x4* base = reinterpret_cast<const g_u32x4*>(uniform64(pc.addr));
+  const uint32_t nvec = uniform32(pc.nvec);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t i = piece_index(0, u, threadIdx.x);
+    q[u] = i < nvec ? ld_vec<NT>(base + i) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// One lane's share of a piece's sum of squares, as piece_sumsq takes it.
+template <int DT>
+__device__ __forceinline__ double piece_lane_sum(const TensorPlan& T, const TPiece& pc, const u32x4 (&q)[kUnroll]) {
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    acc[u] = 0.0;
+    acc[u] += vec_sumsq<DT>(q[u]);
+  }
+  double s = 0.0;
+  const uint32_t nsc = uniform32(pc.sc_count), sc0 = uniform32(pc.sc_begin);
+  for (uint32_t i = threadIdx.x; i < nsc; i += kThreads) s += elem_square<DT>(load_elem<DT>(T.sc_addr[sc0 + i]));
+  return lane_total(acc, s);
+}
+
+// The wave's sum of v (an xor butterfly, as wg_sum takes it) into slot[wave].
+__device__ __forceinline__ void wave_sum_to(double v, double* slot) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = v;
+}
+
+// The partials of pieces [base, base + n): each slot's wave sums added in
+// wave order (as wg_sum adds them), stored by lanes of wave 0.
+__device__ __forceinline__ void flush_partials(const TensorPlan& T, double (*pred)[kWaves], uint32_t base, uint32_t n) {
+  __syncthreads();
+  if (threadIdx.x < n) {
+    double s = pred[threadIdx.x][0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) s += pred[threadIdx.x][k];
+    atomic_st(&T.partials[base + threadIdx.x], s);
+  }
+  __syncthreads();
+}
+
+// A tensor's figures, every field with an agent-scope store.
+__device__ __forceinline__ void store_figures(gclip_tensor_result* dst, const gclip_tensor_result& o) {
+  atomic_st(&dst->sumsq, o.sumsq);
+  atomic_st(&dst->norm, o.norm);
+  atomic_st(&dst->scale, o.scale);
+  atomic_st(reinterpret_cast<uint32_t*>(&dst->nonfinite), (uint32_t)o.nonfinite);
+  atomic_st(reinterpret_cast<uint32_t*>(&dst->clipped), (uint32_t)o.clipped);
+}
+
+// A tensor's factor slot, read once (the read is issued with a piece's loads).
+__device__ __forceinline__ uint64_t factor_bits(const TensorPlan& T, uint32_t k) {
+  return atomic_ld(reinterpret_cast<const uint64_t*>(&T.tfac[k]));
+}
+
+// A tensor's factor by value (see above), from bits already read; 1.0 --
+// nothing written -- and a counted miss if it does not show within
+// kFactorWaitTicks (about a second of the device's wall clock), which cannot
+// happen unless a store is lost.
+constexpr uint64_t kFactorWaitTicks = 1ull << 27;
+__device__ __forceinline__ double tensor_factor(const DevPlan& p, const TensorPlan& T, uint32_t k, uint64_t b) {
+  const uint64_t* slot = reinterpret_cast<const uint64_t*>(&T.tfac[k]);
+  if (b == kUndecided) {
+    const uint64_t t0 = wall_clock64();
+    while ((b = atomic_ld(slot)) == kUndecided) {
+      __builtin_amdgcn_s_sleep(1);
+      if (wall_clock64() - t0 > kFactorWaitTicks) {
+        if (threadIdx.x == 0) (void)atomic_add(&p.sync[kFactorMissWord], 1u);
+        return 1.0;
+      }
+    }
+  }
+  return __builtin_bit_cast(double, b);
+}
+
+// A piece scaled from memory (a handed-back piece): every vector, then its
+// single elements.
+template <int DT, bool NTS>
+__device__ __forceinline__ void scale_piece_mem(const TensorPlan& T, const TPiece& pc, double s64, float s32) {
+  u32x4 q[kUnroll];
+  load_piece<kNtScale>(pc, q);
+  g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
+  const uint32_t nvec = uniform32(pc.nvec);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t i = piece_index(0, u, threadIdx.x);
+    if (i < nvec) st_vec<NTS>(base + i, scale_vec<DT>(q[u], s64, s32));
+  }
+  const uint32_t nsc = uniform32(pc.sc_count), sc0 = uniform32(pc.sc_begin);
+  for (uint32_t i = threadIdx.x; i < nsc; i += kThreads) {
+    const uint64_t a = T.sc_addr[sc0 + i];
+    store_elem<DT>(a, scale_elem<DT>(load_elem<DT>(a), s64, s32));
+  }
+}
+
+// Piece c scaled by its tensor's factor, from memory, when that is not 1.
+template <int DT, bool NTS>
+__device__ __forceinline__ void scale_piece_by_tensor(const DevPlan& p, const TensorPlan& T, uint32_t c) {
+  const TPiece pc = ld_table(T.pieces, c);
+  const uint32_t k = uniform32(pc.tensor);
+  const double f = tensor_factor(p, T, k, factor_bits(T, k));
+  if (f != 1.0) scale_piece_mem<DT, NTS>(T, pc, f, (float)f);
+}
+
+// Take over every handed-back worker's pieces and scale them from memory:
+// its resident pieces and the two streamed pieces it takes without a claim.
+template <int DT, bool NTS>
+__device__ __forceinline__ void take_handed_pieces(const DevPlan& p, const TensorPlan& T, HandSlots& hs) {
+  const uint32_t nw = (uint32_t)p.nworkers;
+  for (uint32_t base = 0; base < nw; base += kThreads) {
+    if (threadIdx.x == 0) hs.n = 0;
+    __syncthreads();
+    const uint32_t i = base + threadIdx.x;
+    if (i < nw && atomic_ld(&p.bstate[i]) == kHanded) {
+      uint32_t expected = kHanded;
+      if (__hip_atomic_compare_exchange_strong(&p.bstate[i], &expected, kTaken, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        hs.list[atomicAdd(&hs.n, 1u)] = i;
+    }
+    __syncthreads();
+    const uint32_t n = hs.n;
+    for (uint32_t k = 0; k < n; ++k) {
+      const uint32_t v = hs.list[k];
+      const uint32_t ra = T.ps + ld_table(T.res_b, (uint64_t)v), rz = T.ps + ld_table(T.res_b, (uint64_t)v + 1);
+      for (uint32_t c = ra; c < rz; ++c) scale_piece_by_tensor<DT, NTS>(p, T, c);
+      for (uint32_t c = v; c < T.ps && c < v + 2u * nw; c += nw) scale_piece_by_tensor<DT, NTS>(p, T, c);
+    }
+    __syncthreads();
+  }
+}
+
+template <int DT, bool NTS>
+__global__ __launch_bounds__(kThreads, 1) void k_tensor_clip_fused(DevPlan p, TensorPlan T, AvgSrc avs,
+                                                                   double max_norm, int err,
+                                                                   gclip_tensor_result* out, gclip_result* res,
+                                                                   uint64_t wait_ticks) {
+  const double avg = avg_value(avs);
+  __shared__ u32x4 keep_lds[kTensorLdsPieces * kUnroll * kThreads];
+  __shared__ double pred[kPieceSlots][kWaves];
+  __shared__ double red[kWaves];
+  __shared__ uint32_t done[kPieceSlots];
+  __shared__ uint32_t ndone;
+  __shared__ ClaimSlots sl;
+  __shared__ HandSlots hs;
+  __shared__ int flag;
+  __shared__ int gave_up;
+  __shared__ int skip_all;
+  const uint32_t w = blockIdx.x, t = threadIdx.x;
+  const uint32_t nw = (uint32_t)p.nworkers;
+  GCLIP_STAMP(GCLIP_STAMP_START);
+
+  // ---- phase 1: the streamed run, then the resident pieces: data one piece
+  // ahead, descriptors two (a piece's loads need its descriptor's address,
+  // a scalar load).  Resident piece k goes to LDS for k < kTensorLdsPieces --
+  // first, while the registers are free -- and to VGPRs after.
+  const uint32_t rb = ld_table(T.run_b, (uint64_t)w), re = ld_table(T.run_b, (uint64_t)w + 1);
+  const uint32_t ra = T.ps + ld_table(T.res_b, (uint64_t)w), rz = T.ps + ld_table(T.res_b, (uint64_t)w + 1);
+  const uint32_t ns = re - rb, nr = rz - ra, m = ns + nr;
+  // piece i of the two runs
+  auto run_piece = [&](uint32_t i) { return i < ns ? rb + i : ra + (i - ns); };
+  u32x4 q[kUnroll];
+  TPiece pc{}, pcn{};
+  if (m > 0) {
+    pc = ld_table(T.pieces, run_piece(0));
+    load_piece<kNtSum>(pc, q);
+  }
+  if (m > 1) pcn = ld_table(T.pieces, run_piece(1));
+  {
+    uint32_t nslot = 0;
+    for (uint32_t i = 0; i < ns; ++i) {
+      u32x4 q2[kUnroll];
+      TPiece pcnn{};
+      const bool more = i + 1 < m;
+      if (i + 2 < m) pcnn = ld_table(T.pieces, run_piece(i + 2));
+      if (more) load_piece<kNtSum>(pcn, q2);
+      wave_sum_to(piece_lane_sum<DT>(T, pc, q), pred[nslot]);
+      if (++nslot == kPieceSlots) {
+        flush_partials(T, pred, rb + i + 1 - nslot, nslot);
+        nslot = 0;
+      }
+      if (more) {
+        pc = pcn;
+        pcn = pcnn;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
+      }
+    }
+    if (nslot) flush_partials(T, pred, re - nslot, nslot);
+  }
+  GCLIP_STAMP(GCLIP_STAMP_CHUNKS_SUMMED);
+  u32x4 keep[kTensorRegPieces * kUnroll];
+#pragma unroll
+  for (int k = 0; k < kTensorResidentPieces; ++k) {
+    if ((uint32_t)k < nr) {
+      u32x4 q2[kUnroll];
+      TPiece pcnn{};
+      const bool more = (uint32_t)k + 1 < nr;
+      if ((uint32_t)k + 2 < nr) pcnn = ld_table(T.pieces, ra + (uint32_t)k + 2);
+      if (more) load_piece<kNtSum>(pcn, q2);
+      wave_sum_to(piece_lane_sum<DT>(T, pc, q), pred[k]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (k < kTensorLdsPieces) {
+          keep_lds[(k * kUnroll + u) * kThreads + t] = q[u];
+        } else {
+          keep[(k >= kTensorLdsPieces ? k - kTensorLdsPieces : 0) * kUnroll + u] = q[u];
+        }
+      }
+      if (more) {
+        pc = pcn;
+        pcn = pcnn;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
+      }
+    }
+  }
+  if (nr) flush_partials(T, pred, ra, nr);
+  GCLIP_STAMP(GCLIP_STAMP_BLOCK_READ);
+
+  // ---- phase 1: count the pieces of every tensor summed here; complete tensors
+  // The two runs are taken kPieceSlots pieces at a time, a lane per piece; a
+  // run's pieces of one tensor form a segment, counted on the tensor's
+  // counter by the lane of its first piece (segments end where the run or
+  // the tensor does: pieces are in tensor order).  A window holds at most
+  // kPieceSlots segment starts, so at most kPieceSlots completions.
+  if (t == 0) complete_stores();  // the partials (wave 0's stores) before the counts
+  {
+    const uint32_t m = ns + nr;
+    for (uint32_t w0 = 0; w0 < m; w0 += kPieceSlots) {
+      if (t == 0) ndone = 0;
+      __syncthreads();
+      const uint32_t i = w0 + t;
+      if (t < kPieceSlots && i < m) {
+        const uint32_t c = i < ns ? rb + i : ra + (i - ns);
+        const uint32_t run_end = i < ns ? re : rz;
+        const uint32_t k = T.pieces[c].tensor;
+        const uint32_t b = T.first[k], f = T.first[k + 1];
+        if (i == 0 || i == ns || c == b) {
+          const uint32_t e = f < run_end ? f : run_end;
+          if (atomic_add(&T.tcount[k], e - c) + (e - c) == f - b) done[atomicAdd(&ndone, 1u)] = k;
+        }
+      }
+      __syncthreads();
+      const uint32_t nd = ndone;
+      if (nd == 0) continue;
+      if (t == 0) acquire_agent();  // every piece of these tensors stored its partial before its count
+      __syncthreads();
+      // kTensorBatch tensors at a time, their partials' loads all in flight:
+      // lane t sums partials b + t, b + t + kThreads, ... of each (the order of
+      // k_tensor_clip), then the waves in wave order
+      for (uint32_t d0 = 0; d0 < nd; d0 += kTensorBatch) {
+        uint32_t tb[kTensorBatch], te[kTensorBatch], rounds = 0;
+#pragma unroll
+        for (int j = 0; j < kTensorBatch; ++j) {
+          tb[j] = te[j] = 0;
+          if (d0 + (uint32_t)j < nd) {
+            const uint32_t k = done[d0 + j];
+            tb[j] = T.first[k];
+            te[j] = T.first[k + 1];
+            const uint32_t r = (te[j] - tb[j] + kThreads - 1) / kThreads;
+            rounds = r > rounds ? r : rounds;
+          }
+        }
+        double v[kTensorBatch];
+#pragma unroll
+        for (int j = 0; j < kTensorBatch; ++j) v[j] = 0.0;
+        for (uint32_t r = 0; r < rounds; ++r) {
+          double x[kTensorBatch];
+#pragma unroll
+          for (int j = 0; j < kTensorBatch; ++j) {
+            const uint32_t pi = tb[j] + r * kThreads + t;
+            x[j] = pi < te[j] ? atomic_ld(&T.partials[pi]) : 0.0;
+          }
+#pragma unroll
+          for (int j = 0; j < kTensorBatch; ++j) v[j] += x[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kTensorBatch; ++j)
+          if (d0 + (uint32_t)j < nd) wave_sum_to(v[j], pred[j]);
+        __syncthreads();
+        if (t < kTensorBatch && d0 + t < nd) {
+          const uint32_t k = done[d0 + t];
+          double S = pred[t][0];
+#pragma unroll
+          for (int j = 1; j < kWaves; ++j) S += pred[t][j];
+          gclip_tensor_result o;
+          tensor_figures(&o, S, avg, max_norm);
+          const Decision dd = decide((avg * avg) * S, nonfinite_of(S, avg), max_norm, avg, 0);
+          // every figure with agent-scope stores: the last workgroup may
+          // overwrite the factor (the stop switch), from another XCD
+          store_figures(&out[k], o);
+          atomic_st(&T.tsum[k], S);
+          atomic_st(reinterpret_cast<uint64_t*>(&T.tfac[k]), __builtin_bit_cast(uint64_t, dd.s));
+          atomic_st(&T.tcount[k], 0u);  // every piece of k has been counted
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  GCLIP_STAMP(GCLIP_STAMP_TENSORS_DONE);
+
+  // ---- the grid-wide decision: the last workgroup gathers the list's figures
+  if (t == 0) gave_up = 0;
+  if (arrive(p, &flag)) {
+    double v = 0.0;
+    int nf_mine = 0, clipped_mine = 0;
+    for (int32_t j = (int32_t)t; j < T.ntensors; j += kThreads) {
+      const bool live = ld_table(T.first, (uint64_t)j) < ld_table(T.first, (uint64_t)j + 1);
+      const double S = live ? atomic_ld(&T.tsum[j]) : 0.0;
+      v += S;
+      nf_mine |= nonfinite_of(S, avg);
+      clipped_mine |= decide((avg * avg) * S, nonfinite_of(S, avg), max_norm, avg, err).clipped;
+      if (!live) {
+        gclip_tensor_result o;
+        tensor_figures(&o, 0.0, avg, max_norm);
+        store_figures(&out[j], o);
+      }
+    }
+    const double S = wg_sum(v, red);
+    const int nf_any = __syncthreads_or(nf_mine);
+    const int clipped_any = __syncthreads_or(clipped_mine);
+    const int skip = (err && nf_any) ? 1 : 0;
+    if (skip) {
+      // the stop switch: no tensor is written, every factor in the figures is 1
+      for (int32_t j = (int32_t)t; j < T.ntensors; j += kThreads) atomic_st(&out[j].scale, 1.0);
+    }
+    if (t == 0) {
+      write_norm(res, S, avg);
+      res->nonfinite = nf_any | res->nonfinite;
+      res->scale = 1.0;
+      res->clipped = clipped_any;
+      res->skipped = skip;
+      res->max_norm = max_norm;
+      res->decided = 1;
+      atomic_st(reinterpret_cast<uint32_t*>(&res->status), 0u);
+      skip_all = skip;
+      complete_stores();  // the stop switch's factors before the decision
+      atomic_st(&p.bcast[0], skip ? kDecidedSkip : __builtin_bit_cast(uint64_t, 1.0));
+    }
+  } else if (t == 0) {
+    const uint64_t t0 = wall_clock64();
+    uint64_t dw;
+    while ((dw = atomic_ld(&p.bcast[0])) == kUndecided) {
+      __builtin_amdgcn_s_sleep(2);
+      if (wall_clock64() - t0 > wait_ticks) {
+        atomic_st(&p.bstate[w], kHanded);
+        complete_stores();
+        atomic_add(&p.sync[kHandedWord], 1u);
+        gave_up = 1;
+        break;
+      }
+    }
+    if (!gave_up) skip_all = dw == kDecidedSkip ? 1 : 0;
+  }
+  __syncthreads();
+  if (!gave_up) GCLIP_STAMP(GCLIP_STAMP_DECISION_SEEN);
+
+  // ---- phase 2: the resident pieces, then claimed streamed pieces
+  if (!gave_up && !skip_all) {
+    uint64_t fb[kTensorResidentPieces];
+#pragma unroll
+    for (int k = 0; k < kTensorResidentPieces; ++k)
+      fb[k] = (uint32_t)k < nr ? factor_bits(T, uniform32(ld_table(T.pieces, ra + (uint32_t)k).tensor)) : 0;
+#pragma unroll
+    for (int k = 0; k < kTensorResidentPieces; ++k) {
+      if ((uint32_t)k < nr) {
+        const TPiece pc = ld_table(T.pieces, ra + (uint32_t)k);
+        const double f = tensor_factor(p, T, uniform32(pc.tensor), fb[k]);
+        if (f != 1.0) {
+          const float f32 = (float)f;
+          g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
+          const uint32_t nvec = uniform32(pc.nvec);
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t i = piece_index(0, u, t);
+            if (i < nvec) {
+              const u32x4 x = k < kTensorLdsPieces ? keep_lds[(k * kUnroll + u) * kThreads + t]
+                                                   : keep[(k >= kTensorLdsPieces ? k - kTensorLdsPieces : 0) * kUnroll + u];
+              st_vec<NTS>(base + i, scale_vec<DT>(x, f, f32));
+            }
+          }
+          const uint32_t nsc = uniform32(pc.sc_count), sc0 = uniform32(pc.sc_begin);
+          for (uint32_t i = t; i < nsc; i += kThreads) {
+            const uint64_t a = T.sc_addr[sc0 + i];
+            store_elem<DT>(a, scale_elem<DT>(load_elem<DT>(a), f, f32));
+          }
+        }
+      }
+    }
+    GCLIP_STAMP(GCLIP_STAMP_BLOCK_WRITTEN);
+    // streamed pieces: one-piece chunks, the next one loaded while this one is written
+    const uint32_t nch = T.ps;
+    if (w < nch) {
+      const Claimer cl = make_claimer(scale_claims(p), p, nch);
+      uint32_t c = w, cn = second_chunk(p, nch, w);
+      u32x4 q[kUnroll];
+      TPiece pc = ld_table(T.pieces, c);
+      load_piece<kNtScale>(pc, q);
+      uint64_t fb = factor_bits(T, uniform32(pc.tensor));
+      for (uint32_t i = 0; c != kNone; ++i) {
+        uint32_t tk = 0;
+        if (t == 0 && cn != kNone) tk = claim_issue(cl);
+        const double f = tensor_factor(p, T, uniform32(pc.tensor), fb);
+        const uint32_t par = i & 1u;
+        if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(cl, tk) : kNone;
+        if (f != 1.0) {
+          const float f32 = (float)f;
+          g_u32x4* base = reinterpret_cast<g_u32x4*>(uniform64(pc.addr));
+          const uint32_t nvec = uniform32(pc.nvec);
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t vi = piece_index(0, u, t);
+            if (vi < nvec) st_vec<NTS>(base + vi, scale_vec<DT>(q[u], f, f32));
+          }
+          const uint32_t nsc = uniform32(pc.sc_count), sc0 = uniform32(pc.sc_begin);
+          for (uint32_t vi = t; vi < nsc; vi += kThreads) {
+            const uint64_t a = T.sc_addr[sc0 + vi];
+            store_elem<DT>(a, scale_elem<DT>(load_elem<DT>(a), f, f32));
+          }
+        }
+        if (cn != kNone) {
+          pc = ld_table(T.pieces, cn);
+          load_piece<kNtScale>(pc, q);
+          fb = factor_bits(T, uniform32(pc.tensor));
+        }
+        __syncthreads();
+        c = cn;
+        cn = uniform32(sl.claim[par]);
+      }
+    }
+    GCLIP_STAMP(GCLIP_STAMP_CHUNKS_SCALED);
+    if (t == 0) flag = (int)atomic_ld(&p.sync[kHandedWord]);
+    __syncthreads();
+    if (flag) take_handed_pieces<DT, NTS>(p, T, hs);
+  }
+
+  // ---- finish: the last workgroup takes what is still handed back and resets the workspace
+  __syncthreads();
+  if (t == 0) {
+    complete_stores();
+    flag = take_ticket(finish_tickets(p), p.nworkers) ? 1 : 0;
+    if (flag) acquire_agent();  // before the hand-back count, the decision and the states are read
+  }
+  __syncthreads();
+  GCLIP_STAMP(GCLIP_STAMP_END);
+  if (flag == 0) return;
+  const uint32_t handed = atomic_ld(&p.sync[kHandedWord]);
+  if (handed != 0u) {
+    if (atomic_ld(&p.bcast[0]) != kDecidedSkip) take_handed_pieces<DT, NTS>(p, T, hs);
+    __syncthreads();
+    for (uint32_t i = t; i < nw; i += kThreads) atomic_st(&p.bstate[i], kHeld);
+  }
+  __syncthreads();
+  for (int32_t j = (int32_t)t; j < T.ntensors; j += kThreads)
+    atomic_st(reinterpret_cast<uint64_t*>(&T.tfac[j]), kUndecided);
+  if (t == 0) {
+    res->handed_back = (int32_t)handed;
+    atomic_st(&p.sync[kHandedWord], 0u);
+    if (atomic_ld(&p.sync[kFactorMissWord]) != 0u) {
+      atomic_st(reinterpret_cast<uint32_t*>(&res->status), (uint32_t)GCLIP_DEVICE_WAIT_TIMEOUT);
+      atomic_st(&p.sync[kFactorMissWord], 0u);
+    }
+    atomic_st(&p.bcast[0], kUndecided);
+    atomic_st(scale_claims(p), 0u);
+  }
+}
+
 // ---------------------------------------------------------------- host launchers
 int worker_threads() { return kThreads; }
 uint64_t resident_cap_vectors() { return kResidentCap; }
@@ -1169,6 +1680,36 @@ hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc
   void* args[] = {&pc, &max_norm, &avg, &err, &res, &wait_ticks, &amp};
   const void* fn = p.nt_store ? fused_kernel<true>(dtype) : fused_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
+}
+
+template <bool NTS>
+const void* tensor_fused_kernel(int32_t dtype) {
+  return dtype == GCLIP_F32   ? (const void*)k_tensor_clip_fused<GCLIP_F32, NTS>
+         : dtype == GCLIP_F16 ? (const void*)k_tensor_clip_fused<GCLIP_F16, NTS>
+                              : (const void*)k_tensor_clip_fused<GCLIP_BF16, NTS>;
+}
+
+hipError_t launch_tensor_clip_fused(const DevPlan& p, const TensorPlan& T, int32_t dtype, AvgSrc avg,
+                                    double max_norm, int err, gclip_tensor_result* out, gclip_result* res,
+                                    uint64_t wait_ticks, hipStream_t st) {
+  DevPlan pc = p;
+  TensorPlan tc = T;
+  void* args[] = {&pc, &tc, &avg, &max_norm, &err, &out, &res, &wait_ticks};
+  const void* fn = p.nt_store ? tensor_fused_kernel<true>(dtype) : tensor_fused_kernel<false>(dtype);
+  return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);
+}
+
+// Workgroups of the one-launch per-tensor clip that fit on one compute unit.
+hipError_t tensor_fused_capacity(int32_t dtype, int* blocks_per_cu) {
+  int lo = 1 << 30;
+  for (const void* fn : {tensor_fused_kernel<false>(dtype), tensor_fused_kernel<true>(dtype)}) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, 0);
+    if (e != hipSuccess) return e;
+    lo = n < lo ? n : lo;
+  }
+  *blocks_per_cu = lo;
+  return hipSuccess;
 }
 
 // Workgroups of the fused kernels that fit on one compute unit at once (the

@@ -273,6 +273,19 @@ int tensor_plan_build(const HostPlan& p, uint32_t piece_vectors, TensorHostPlan&
     if (out.pieces.size() > 0x7fffffffull) return 1;
   }
   out.first[(size_t)p.n_tensors] = (uint32_t)out.pieces.size();
+  const uint64_t np = out.pieces.size(), nw = (uint64_t)(p.nworkers > 0 ? p.nworkers : 1);
+  const uint64_t nres = np < nw * (uint64_t)kTensorResidentPieces ? np : nw * (uint64_t)kTensorResidentPieces;
+  out.ps = (uint32_t)(np - nres);
+  out.run_b.resize((size_t)nw + 1);
+  out.res_b.resize((size_t)nw + 1);
+  // both shared out by piece count: with one piece in flight a short piece
+  // costs about a round trip, nearly what a whole one does, so balancing by
+  // bytes loads the workers that get the short pieces (measured: 57 ms
+  // instead of 1.1 ms on a list that ends with 4,096 one-element tensors)
+  for (uint64_t w = 0; w <= nw; ++w) {
+    out.run_b[(size_t)w] = (uint32_t)share_begin(out.ps, (int32_t)nw, (int32_t)w);
+    out.res_b[(size_t)w] = (uint32_t)share_begin(nres, (int32_t)nw, (int32_t)w);
+  }
   return 0;
 }
 

@@ -104,7 +104,8 @@ constexpr uint64_t kDecidedSkip = 0x7ff4000000000002ull;
 // Device view of a plan plus the list's workspace (all device addresses).
 // sync holds 128-byte lines of counters (one line per counter group, so that
 // the XCDs do not share lines):
-//   line 0                           count of handed-back blocks
+//   line 0                           count of handed-back blocks (word 0); tensor factors the
+//                                    one-launch per-tensor clip never saw (word 1)
 //   line 1                           claim counter of the summing passes
 //   line 2                           claim counter of the scaling passes
 //   lines 3 .. 3 + kTicketGroups     arrival tickets: one per XCD group, then the top one
@@ -229,13 +230,30 @@ static_assert(sizeof(TPiece) == 32, "one piece is one 32-byte scalar load");
 #endif
 constexpr uint32_t kTensorPieceVectors = GCLIP_TENSOR_PIECE_VECTORS;
 
+// The one-launch per-tensor clip keeps up to kTensorResidentPieces pieces
+// per worker on chip across the decisions: kTensorRegPieces in VGPRs (one
+// piece is at most one group, kUnroll steps of kThreads vectors) and the rest
+// in LDS.
+constexpr int kTensorRegPieces = 5;
+constexpr int kTensorLdsPieces = 2;
+constexpr int kTensorResidentPieces = kTensorRegPieces + kTensorLdsPieces;
+
 struct TensorHostPlan {
   std::vector<TPiece> pieces;
   std::vector<uint32_t> first;  // n_tensors + 1
+  // The one-launch per-tensor clip over nworkers workers: the last
+  // nres = min(npieces, nworkers * kTensorResidentPieces) pieces are kept on
+  // chip, worker w holding [ps + res_b[w], ps + res_b[w + 1]); the streamed
+  // pieces [0, ps) are summed in runs [run_b[w], run_b[w + 1]) and scaled as
+  // claimed one-piece chunks.
+  uint32_t ps = 0;
+  std::vector<uint32_t> run_b;  // nworkers + 1
+  std::vector<uint32_t> res_b;  // nworkers + 1
 };
 
-// Cut a list's plan into per-tensor pieces of at most piece_vectors vectors.
-// Returns a gclip_status code (0 = OK).
+// Cut a list's plan into per-tensor pieces of at most piece_vectors vectors,
+// and share them out over the plan's workers for the one-launch per-tensor
+// clip.  Returns a gclip_status code (0 = OK).
 int tensor_plan_build(const HostPlan& p, uint32_t piece_vectors, TensorHostPlan& out);
 
 struct TensorPlan {
@@ -249,6 +267,12 @@ struct TensorPlan {
   int32_t ntensors;
   uint32_t nlive;    // tensors with at least one piece
   uint32_t nt_store;
+  // the one-launch per-tensor clip (TensorHostPlan's run_b, res_b, ps)
+  const uint32_t* run_b;
+  const uint32_t* res_b;
+  uint32_t ps;
+  uint32_t* tcount;  // n_tensors: pieces summed so far (zero between calls)
+  double* tfac;      // n_tensors: each tensor's factor, stored by the workgroup that completes it
 };
 
 // Per-step constants, rounded to binary32 from binary64 on the host.

@@ -281,20 +281,6 @@ __device__ __forceinline__ double tensor_sum(const TensorPlan& T, uint32_t b, ui
   return wg_sum(v, red);
 }
 
-// A tensor's figures from its raw sum, as k_tensor_decide writes them
-// without the stop switch.
-__device__ __forceinline__ int tensor_figures(gclip_tensor_result* o, double S, double avg, double max_norm) {
-  const double sumsq = (avg * avg) * S;
-  const int nf = nonfinite_of(S, avg);
-  const Decision d = decide(sumsq, nf, max_norm, avg, 0);
-  o->sumsq = sumsq;
-  o->norm = sqrt(sumsq);
-  o->nonfinite = nf;
-  o->scale = d.s == 1.0 ? 1.0 : d.s;
-  o->clipped = d.clipped;
-  return d.clipped;
-}
-
 template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads) void k_tensor_clip(TensorPlan T, AvgSrc avs, double max_norm,
                                                           gclip_tensor_result* out, gclip_result* res,

@@ -9,7 +9,11 @@
  * build records, per workgroup, the wall-clock time at which each of its
  * phases ended, so that the time of one launch can be split between them.
  * With the += the summing pass also writes the sums of the streamed region,
- * and the scaling pass rescales the workgroup's own sum chunk.
+ * and the scaling pass rescales the workgroup's own sum chunk.  The
+ * one-launch per-tensor clip (gclip_clip_per_tensor_ on the fused path)
+ * records the same points over pieces: its streamed run summed, its resident
+ * pieces read, its tensors counted and completed, the decision seen, its
+ * resident pieces written, its claimed pieces scaled.
  *
  * Only the library built with -DGCLIP_PHASE_STAMPS exports gclip_phase_stamps
  * (`python -m global_l2_norm_amd.build --phase-stamps` writes it to
@@ -38,7 +42,9 @@
 #define GCLIP_STAMP_DECISION_SEEN 3   /* knew the decision (every wave) */
 #define GCLIP_STAMP_BLOCK_WRITTEN 4   /* had issued the writes of its block (when it writes) */
 #define GCLIP_STAMP_CHUNKS_SCALED 5   /* had scaled its chunks of the streamed region (when it writes) */
-#define GCLIP_STAMP_END 6             /* was done, finish ticket included */
+#define GCLIP_STAMP_END 6             /* was done, finish ticket included (the per-tensor clip: taken) */
+#define GCLIP_STAMP_TENSORS_DONE 7    /* the per-tensor clip: had counted its pieces and summed the
+                                         tensors it completed */
 
 #ifdef __cplusplus
 extern "C" {

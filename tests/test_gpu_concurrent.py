@@ -78,10 +78,16 @@ def test_two_fused_launches_at_once(wait_us):
     lb.close()
 
 
-def _per_tensor_alone(arrays, dtype, max_norm):
+def _set_path(gl, path):
+    G = _G()
+    gl.set_path(G.GCLIP_PATH_FUSED if path == "fused" else G.GCLIP_PATH_SPLIT)
+
+
+def _per_tensor_alone(arrays, dtype, max_norm, path):
     G = _G()
     ts = gu.upload(arrays, dtype)
     gl = G.GradList(ts)
+    _set_path(gl, path)
     gl.clip_per_tensor_(max_norm)
     st, r = gl.read()
     tr = gl.read_tensors()
@@ -90,21 +96,25 @@ def _per_tensor_alone(arrays, dtype, max_norm):
     return r, tr, out
 
 
-def test_two_per_tensor_clips_at_once():
-    """Without the stop switch the per-tensor clip's workgroup 0 waits in the
-    launch for every tensor's sum; with a second such launch on another
-    stream holding compute units meanwhile, both lists must still come out
-    exactly as when clipped alone."""
+@pytest.mark.parametrize("path", ("fused", "split"))
+def test_two_per_tensor_clips_at_once(path):
+    """Two per-tensor clips at once on two streams, each taking compute units
+    from the other: in one launch every workgroup waits for the decisions
+    (and hands its pieces back when it waits too long); in two kernels the
+    second kernel's workgroup 0 waits for every tensor's sum.  Both lists
+    must come out exactly as when clipped alone."""
     import torch
     G = _G()
     rng = np.random.default_rng(4400)
     a = [gs.to_storage(rng.standard_normal(n) * 1e-3, "f32") for n in (30_000_003, 1, 5_000_001) + (77,) * 500]
     b = [gs.to_storage(rng.standard_normal(n) * 1e-3, "bf16") for n in (40_000_001, 3) + (1,) * 800 + (20_000_000,)]
-    ra, tra, out_a = _per_tensor_alone(a, "f32", 1.0)
-    rb, trb, out_b = _per_tensor_alone(b, "bf16", 1.0)
+    ra, tra, out_a = _per_tensor_alone(a, "f32", 1.0, path)
+    rb, trb, out_b = _per_tensor_alone(b, "bf16", 1.0, path)
     ta, tb = gu.upload(a, "f32"), gu.upload(b, "bf16")
     pa, pb = [t.clone() for t in ta], [t.clone() for t in tb]
     la, lb = G.GradList(ta), G.GradList(tb)
+    _set_path(la, path)
+    _set_path(lb, path)
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     for rep in range(3):
         for t, p in zip(ta + tb, pa + pb):

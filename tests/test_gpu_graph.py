@@ -105,7 +105,8 @@ def test_clip_replays(dtype, path):
     gl.close()
 
 
-def test_per_tensor_and_accumulate_replays():
+@pytest.mark.parametrize("path", ("fused", "split"))
+def test_per_tensor_and_accumulate_replays(path):
     import torch
     G = _G()
     rng = np.random.default_rng(4100)
@@ -114,6 +115,7 @@ def test_per_tensor_and_accumulate_replays():
     ts = gu.upload(contents[0], "f32")
     tc = gu.upload(contrib, "f32")
     gl = G.GradList(ts)
+    gl.set_path(G.GCLIP_PATH_FUSED if path == "fused" else G.GCLIP_PATH_SPLIT)
     c = G.Contribution(gl, tc)
     for name, call in (("per_tensor", lambda: gl.clip_per_tensor_(0.5, 1.0, False)),
                        ("per_tensor_stop", lambda: gl.clip_per_tensor_(0.5, 1.0, True)),

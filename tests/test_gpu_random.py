@@ -20,7 +20,8 @@ from tests.test_gpu_accum import odd_offsets, views_at
 pytestmark = pytest.mark.gpu
 
 DTYPES = ("f32", "f16", "bf16")
-CALLS = ("clip_fused", "clip_split", "norm_scale", "per_tensor", "accum_fused", "accum_split", "amp")
+CALLS = ("clip_fused", "clip_split", "norm_scale", "per_tensor", "accum_fused", "accum_split", "amp",
+         "per_tensor_split")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -89,7 +90,7 @@ def test_random_case(case):
     print(what, flush=True)
     ts, buf, offs = upload(rng, arrays, dtype, as_views)
     gl = G.GradList(ts)
-    if call in ("clip_split", "norm_scale", "accum_split"):
+    if call in ("clip_split", "norm_scale", "accum_split", "per_tensor_split"):
         gl.set_path(G.GCLIP_PATH_SPLIT)
 
     if call in ("clip_fused", "clip_split", "norm_scale", "amp"):
@@ -117,7 +118,7 @@ def test_random_case(case):
             sc, tr, fi = amp.read()
             esc, etr = oracle.amp_update(scale, 0, ro["nonfinite"], 2.0, 0.5, 3)
             assert fi == ro["nonfinite"] and sc == esc and tr == etr, what
-    elif call == "per_tensor":
+    elif call in ("per_tensor", "per_tensor_split"):
         norms = [math.sqrt(x) for x in oracle.tensor_sumsq(arrays, dtype, avg)]
         c = threshold(rng, norms)
         gl.clip_per_tensor_(c, avg, err)
@@ -156,7 +157,7 @@ def test_random_case(case):
     if not math.isnan(ro["norm"]):
         gu.assert_norm_close(r["norm"], ro["norm"], what)
         assert r["clipped"] == ro["clipped"], what
-    if call == "per_tensor":
+    if call in ("per_tensor", "per_tensor_split"):
         for k, (o, rr, a, t) in enumerate(zip(out, ref, arrays, ro["tensors"])):
             if ro["skipped"] or t["scale"] == 1.0:
                 gu.assert_bitwise_equal_but_nan([o], [a], dtype, f"{what} tensor {k} untouched")

@@ -16,6 +16,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 STAMPS_LIB = os.path.join(ROOT, "global_l2_norm_amd", "_stamps", "libgclip.so")
 PHASES = ["sum chunks done", "block read into VGPRs and LDS", "decision seen",
           "block written back from VGPRs and LDS", "scale chunks done", "end"]
+TENSOR_PHASES = ["streamed run summed", "resident pieces read into VGPRs and LDS",
+                 "pieces counted, completed tensors summed", "decision seen", "resident pieces written",
+                 "claimed pieces scaled", "end"]
 
 
 def _timeline(args):
@@ -54,3 +57,16 @@ def test_phase_timeline_without_writes():
     assert [n for n in PHASES if n in rows] == ["sum chunks done", "block read into VGPRs and LDS",
                                                   "decision seen", "end"], rows
     assert all(rows[n][2] == workers for n in rows)
+
+
+def test_phase_timeline_of_the_per_tensor_clip():
+    """The one-launch per-tensor clip stamps its own phases, in order."""
+    rows, workers = _timeline(["--path", "per_tensor", "--config", "andrea120m_f16_spike", "--steps", "3",
+                               "--warmup", "1"])
+    assert list(rows) == TENSOR_PHASES, rows
+    prev = (0.0, 0.0)
+    for name in TENSOR_PHASES:
+        med, last, n = rows[name]
+        assert n == workers, (name, n, workers)
+        assert 0.0 <= med <= last and med >= prev[0] - 1e-9 and last >= prev[1] - 1e-9, (name, rows)
+        prev = (med, last)

@@ -1,5 +1,7 @@
 """GPU parity of the per-tensor calls (gclip_tensor_norms, gclip_clip_per_tensor_),
-through the C ABI, against the oracle's per-tensor clip.
+through the C ABI, against the oracle's per-tensor clip -- the per-tensor
+clip on both paths: one launch (the fused path, a list's default) and two or
+three kernels (the split path), which must also agree bit for bit.
 
 Tolerances are those of the global path: every tensor's norm and the list's
 within relative 1e-5 of the oracle's; clipped fp32 elements within relative
@@ -20,6 +22,7 @@ from tests.test_gpu_parity import ragged_arrays, upload_as_views
 pytestmark = pytest.mark.gpu
 
 DTYPES = ("f32", "f16", "bf16")
+PATHS = ("fused", "split")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,9 +38,15 @@ def _G():
     return G
 
 
-def gpu_per_tensor(arrays, dtype, max_norm, avg=1.0, err=False, views=None):
+def set_path(gl, path):
+    G = _G()
+    gl.set_path(G.GCLIP_PATH_FUSED if path == "fused" else G.GCLIP_PATH_SPLIT)
+
+
+def gpu_per_tensor(arrays, dtype, max_norm, avg=1.0, err=False, views=None, path="fused"):
     ts = views if views is not None else gu.upload(arrays, dtype)
     gl = _G().GradList(ts)
+    set_path(gl, path)
     gl.clip_per_tensor_(max_norm, avg, err)
     st, r = gl.read(err)
     tr = gl.read_tensors()
@@ -60,8 +69,9 @@ def check_tensor_figures(tr, ro, what):
                 assert abs(float(g["scale"]) - o["scale"]) <= 1e-5 * abs(o["scale"]), (what, k)
 
 
-def check_per_tensor(arrays, dtype, max_norm, avg=1.0, err=False, views=None, what=""):
-    st, r, tr, out = gpu_per_tensor(arrays, dtype, max_norm, avg, err, views)
+def check_per_tensor(arrays, dtype, max_norm, avg=1.0, err=False, views=None, what="", path="fused"):
+    st, r, tr, out = gpu_per_tensor(arrays, dtype, max_norm, avg, err, views, path)
+    what = f"{what} ({path})"
     ref = [a.copy() for a in arrays]
     ro = oracle.clip_per_tensor_(ref, dtype, max_norm, avg, err)
     assert r["status"] == 0, what
@@ -87,29 +97,33 @@ def _threshold_off_ties(rng, arrays, dtype, avg=1.0):
 
 
 # ------------------------------------------------------------------ the page's contrast
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_contrast_6_8_and_small(dtype):
+def test_contrast_6_8_and_small(dtype, path):
     """[6, 8] and [0.3, 0.4] at c = 1: [0.6, 0.8] and the second unchanged."""
     a = [gs.to_storage(np.array([6.0, 8.0]), dtype), gs.to_storage(np.array([0.3, 0.4]), dtype)]
-    r, ro, tr, out = check_per_tensor(a, dtype, 1.0, what=f"contrast {dtype}")
+    r, ro, tr, out = check_per_tensor(a, dtype, 1.0, what=f"contrast {dtype}", path=path)
     assert float(tr[0]["norm"]) == 10.0 and tr[0]["clipped"] and not tr[1]["clipped"]
     assert np.array_equal(out[0], gs.to_storage(np.array([0.6, 0.8]), dtype))
 
 
 # ------------------------------------------------------------------ ragged lists
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("err", (False, True))
 @pytest.mark.parametrize("seed", range(4))
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_ragged_lists_misaligned_views(dtype, seed, err):
+def test_ragged_lists_misaligned_views(dtype, seed, err, path):
     """Tensors of 1 .. 3M elements at odd element offsets (single elements at
-    both ends of each vector run), several pieces per big tensor; without the
-    stop switch (two kernels) and with it (three)."""
+    both ends of each vector run), several pieces per big tensor; in one
+    launch, and on the split path without the stop switch (two kernels) and
+    with it (three)."""
     rng = np.random.default_rng(2000 + seed)
     arrays = ragged_arrays(rng, dtype, big=seed >= 2)
     avg = [1.0, 0.25, 1.0, 1.0 / 3.0][seed]
     c = _threshold_off_ties(rng, arrays, dtype, avg)
     buf, views = upload_as_views(arrays, dtype, rng)
-    check_per_tensor(arrays, dtype, c, avg, err=err, views=views, what=f"ragged {dtype} seed {seed} err {err}")
+    check_per_tensor(arrays, dtype, c, avg, err=err, views=views, what=f"ragged {dtype} seed {seed} err {err}",
+                     path=path)
     import torch
     mask = torch.ones(buf.numel(), dtype=torch.bool, device="cuda")
     for v in views:
@@ -149,25 +163,28 @@ def test_tensor_norms_then_global_scale(dtype):
 
 
 # ------------------------------------------------------------------ non-finite, empty, repeatability
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("err", (False, True))
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_nonfinite(dtype, err):
+def test_nonfinite(dtype, err, path):
     rng = np.random.default_rng(2200)
     arrays = [gs.to_storage(rng.standard_normal(n) * 3.0, dtype) for n in (5000, 70_001, 33, 4096 * 8)]
     arrays[1][12_345] = gs.to_storage(np.array([math.nan]), dtype)[0]
     arrays[3][7] = gs.to_storage(np.array([-math.inf]), dtype)[0]
-    r, ro, tr, out = check_per_tensor(arrays, dtype, 1.0, err=err, what=f"nonfinite {dtype} err={err}")
+    r, ro, tr, out = check_per_tensor(arrays, dtype, 1.0, err=err, what=f"nonfinite {dtype} err={err}", path=path)
     assert r["nonfinite"] and list(tr["nonfinite"]) == [0, 1, 0, 1]
     assert r["skipped"] == err
 
 
-def test_empty_lists_and_tensors():
+@pytest.mark.parametrize("path", PATHS)
+def test_empty_lists_and_tensors(path):
     G = _G()
     import torch
     for arrays in ([], [np.zeros(0, np.float32)], [np.zeros(0, np.float32), np.ones(3, np.float32) * 2.0,
                                                     np.zeros(0, np.float32)]):
         ts = gu.upload(arrays, "f32") if arrays else []
         gl = G.GradList(ts)
+        set_path(gl, path)
         gl.clip_per_tensor_(1.0)
         st, r = gl.read()
         tr = gl.read_tensors()
@@ -212,13 +229,14 @@ def test_invalid_arguments():
 
 
 # ------------------------------------------------------------------ full size
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("err", (False, True))
 @pytest.mark.parametrize("dtype_cfg", ("andrea120m_f32", "andrea120m_f16_spike"))
-def test_andrea120m(dtype_cfg, err):
+def test_andrea120m(dtype_cfg, err, path):
     """The 124-tensor list at c = 0.5: the big matrices are clipped, the norm
     vectors are not (their norms are ~0.03)."""
     g = gs.make(dtype_cfg)
-    r, ro, tr, out = check_per_tensor(g.arrays, g.dtype, 0.5, err=err, what=f"{dtype_cfg} err {err}")
+    r, ro, tr, out = check_per_tensor(g.arrays, g.dtype, 0.5, err=err, what=f"{dtype_cfg} err {err}", path=path)
     flags = [t["clipped"] for t in ro["tensors"]]
     assert any(flags) and not all(flags)
 
@@ -267,6 +285,7 @@ def test_two_kernel_clip_many_tensors_repeated(dtype):
     assert any(t["clipped"] for t in ro["tensors"]) and not all(t["clipped"] for t in ro["tensors"])
     ts = gu.upload(arrays, dtype)
     gl = _G().GradList(ts)
+    set_path(gl, "split")
     runs = []
     for rep in range(3):
         _reload(ts, arrays, dtype)
@@ -297,6 +316,7 @@ def test_gather_wait_timeout_is_reported_and_recovers():
     assert any(t["clipped"] for t in ro["tensors"]) and not all(t["clipped"] for t in ro["tensors"])
     ts = gu.upload(arrays, "f32")
     gl = G.GradList(ts)
+    set_path(gl, "split")  # the two-kernel form's gathering wait
     timeouts = 0
     try:
         G.gclip_set_gather_wait(0)
@@ -337,6 +357,7 @@ def test_gather_wait_timeout_with_the_stop_switch_writes_nothing():
     ro = oracle.clip_per_tensor_(ref, "f32", c, 1.0, True)
     ts = gu.upload(arrays, "f32")
     gl = G.GradList(ts)
+    set_path(gl, "split")  # the three-kernel form's gathering wait
     timeouts = 0
     try:
         G.gclip_set_gather_wait(0)
@@ -367,3 +388,94 @@ def test_gather_wait_bounds():
     with pytest.raises(G.GclipError):
         G.gclip_set_gather_wait(61 * 1000 * 1000)
     G.gclip_set_gather_wait(-1)
+
+
+# ------------------------------------------------------------------ one launch against the split path, bit for bit
+def _both_paths(arrays, dtype, max_norm, avg, err, wait_us=None):
+    """The one-launch clip and the split path on the same input: every
+    written bit, every figure and the result block's figures must agree."""
+    got = {}
+    for path in PATHS:
+        ts = gu.upload(arrays, dtype)
+        gl = _G().GradList(ts)
+        set_path(gl, path)
+        if wait_us is not None and path == "fused":
+            gl.set_wait(wait_us)
+        gl.clip_per_tensor_(max_norm, avg, err)
+        st, r = gl.read(err)
+        got[path] = (st, r, gl.read_tensors(), gu.download(ts, dtype))
+        gl.close()
+    (sf, rf, tf, of), (ss, rs, tsp, osp) = got["fused"], got["split"]
+    what = f"{dtype} {[a.size for a in arrays][:6]}... avg {avg} err {err} wait {wait_us}"
+    assert sf == ss and rf["status"] == rs["status"] == 0, (what, rf, rs)
+    for key in ("sumsq", "norm", "nonfinite", "clipped", "skipped", "scale", "decided"):
+        same = rf[key] == rs[key] or (isinstance(rf[key], float) and math.isnan(rf[key]) and math.isnan(rs[key]))
+        assert same, (what, key, rf[key], rs[key])
+    assert tf.tobytes() == tsp.tobytes(), what
+    gu.assert_bitwise_equal(of, osp, f"one launch vs split, {what}")
+    return rf
+
+
+@pytest.mark.parametrize("err", (False, True))
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_one_launch_equals_split_bitwise(dtype, err):
+    """Ragged lists (one with a streamed region: more pieces than the
+    workers keep on chip), many small tensors, a NaN with and without the
+    stop switch: the one-launch clip writes what the split path writes."""
+    rng = np.random.default_rng(2900)
+    for big in (False, True):
+        arrays = ragged_arrays(rng, dtype, big=big)
+        _both_paths(arrays, dtype, _threshold_off_ties(rng, arrays, dtype, 0.5), 0.5, err)
+    sizes = [3_000_001, 0] + [1] * 700 + [int(n) for n in rng.integers(2, 5000, size=300)] + [9_000_000, 0]
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-2, dtype) for n in sizes]
+    _both_paths(arrays, dtype, 0.05, 1.0, err)
+    arrays[705][1] = gs.to_storage(np.array([math.nan]), dtype)[0]  # a tensor of 2 .. 4999 elements
+    r = _both_paths(arrays, dtype, 0.05, 1.0, err)
+    assert r["nonfinite"] and r["skipped"] == err
+
+
+def test_one_launch_hand_back_equals_split():
+    """With no wait at the decision every workgroup but the deciding one
+    hands its resident pieces back (and the two streamed pieces it takes
+    without a claim); they are scaled from memory with the same bits."""
+    rng = np.random.default_rng(2950)
+    sizes = [20_000_003, 7, 1, 0] + [int(n) for n in rng.integers(1, 70_000, size=200)] + [15_000_000]
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-2, "f32") for n in sizes]
+    _both_paths(arrays, "f32", 0.5, 1.0, False, wait_us=0)
+    ts = gu.upload(arrays, "f32")
+    gl = _G().GradList(ts)
+    gl.set_wait(0)
+    gl.clip_per_tensor_(0.5)
+    st, r = gl.read()
+    assert st == 0 and r["handed_back"] >= 1, r
+    gl.close()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_one_launch_many_tensors_repeated(dtype):
+    """Three calls in a row on one list of 2,300 tensors: the tensors'
+    counters and factor slots must be back to empty after each (a stale
+    factor would scale the next call by the previous one's), every call
+    against the oracle and the split path, the same bits every time."""
+    rng = np.random.default_rng(2600)
+    sizes = [1_000_003, 0] + [1] * 2000 + [0, 3_000_001] + [int(n) for n in rng.integers(2, 200, size=300)] + [0]
+    arrays = [gs.to_storage(rng.standard_normal(n) * 1e-2, dtype) for n in sizes]
+    c = 1.0
+    assert all(abs(math.sqrt(x) - c) > 1e-3 for x in oracle.tensor_sumsq(arrays, dtype, 0.5))
+    ref = [a.copy() for a in arrays]
+    ro = oracle.clip_per_tensor_(ref, dtype, c, 0.5, False)
+    ts = gu.upload(arrays, dtype)
+    gl = _G().GradList(ts)
+    set_path(gl, "fused")
+    runs = []
+    for rep in range(3):
+        # a different input in between, so that stale state would show
+        _reload(ts, [a[::-1].copy() for a in arrays], dtype)
+        gl.clip_per_tensor_(0.3, 1.0, False)
+        _reload(ts, arrays, dtype)
+        gl.clip_per_tensor_(c, 0.5, False)
+        st, r, tr, out = _check_call(gl, ts, arrays, ref, ro, dtype, f"one launch, many tensors {dtype} call {rep}")
+        runs.append((r["sumsq"], tr.tobytes(), b"".join(o.tobytes() for o in out)))
+    assert runs[0] == runs[1] == runs[2]
+    gl.close()
+    _both_paths(arrays, dtype, c, 0.5, False)
