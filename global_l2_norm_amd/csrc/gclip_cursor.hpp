@@ -121,19 +121,19 @@ __host__ __device__ __forceinline__ uint64_t step_addr(const DevPlan& p, Cursor&
   return a;
 }
 
-// step_addr, also giving the segment that holds vector v (for reads of a
-// second list laid out like this one, at an offset per segment).
-__host__ __device__ __forceinline__ uint64_t step_addr_seg(const DevPlan& p, Cursor& c, uint64_t b, uint64_t ve,
-                                                           uint64_t v, uint32_t& sv) {
+// step_addr for a second list laid out like this one at an offset per
+// segment (delta[s]): the address of vector v in that list.  d is the
+// offset of the cursor's segment and moves with the cursor; each new
+// segment's offset is read like the rest of the table (a scalar load on the
+// device), so a crossing step waits for no vector load before its own.
+__host__ __device__ __forceinline__ uint64_t step_addr_delta(const DevPlan& p, const uint64_t* delta, Cursor& c,
+                                                             uint64_t& d, uint64_t b, uint64_t ve, uint64_t v) {
   const uint64_t last = (b + kThreads < ve ? b + kThreads : ve) - 1;
-  uint64_t a = c.addr + (v - c.beg) * kVecBytes;
-  sv = c.s;
+  uint64_t a = c.addr + d + (v - c.beg) * kVecBytes;
   while (last >= c.end) {
     cursor_load(p, c, c.s + 1);
-    if (v >= c.beg) {
-      a = c.addr + (v - c.beg) * kVecBytes;
-      sv = c.s;
-    }
+    d = ld_table(delta, c.s);
+    if (v >= c.beg) a = c.addr + d + (v - c.beg) * kVecBytes;
   }
   return a;
 }

@@ -50,6 +50,41 @@ __device__ __forceinline__ u32x4 load_vec(uint64_t a) { return ld_vec<NT>(reinte
 template <bool NT>
 __device__ __forceinline__ void store_vec(uint64_t a, u32x4 q) { st_vec<NT>(reinterpret_cast<g_u32x4*>(a), q); }
 
+// Device-scope vector accesses, for data that one workgroup writes and
+// another, on any XCD, reads later in the same launch.  Each XCD has an L2
+// of its own that ordinary stores only reach (it is written back to memory
+// at the end of the kernel), so such data is stored with the device-scope
+// bit (sc1: written through to memory) and loaded with it (served from
+// memory, not from a line an L2 may hold), the encoding of agent-scope
+// atomic accesses.  The 16-byte forms go through a buffer resource, whose
+// base must be the same in every lane: a group's base address; a vector at
+// an address of its own takes two agent-scope 8-byte accesses instead.
+constexpr int kAuxNt = 2;    // cache policy bits of the buffer builtins: nt
+constexpr int kAuxSc1 = 16;  // sc1
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer: 32-bit data format, no swizzle
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(uint64_t base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_vec_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAuxSc1 | (NT ? kAuxNt : 0));
+}
+template <bool NT>
+__device__ __forceinline__ void st_vec_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 q) {
+  __builtin_amdgcn_raw_buffer_store_b128(q, r, (int)off, 0, kAuxSc1 | (NT ? kAuxNt : 0));
+}
+__device__ __forceinline__ u32x4 load_vec_dev(uint64_t a) {
+  const uint64_t* p = reinterpret_cast<const uint64_t*>(a);
+  const uint64_t lo = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+__device__ __forceinline__ void store_vec_dev(uint64_t a, u32x4 q) {
+  uint64_t* p = reinterpret_cast<uint64_t*>(a);
+  __hip_atomic_store(p, (uint64_t)q[0] | ((uint64_t)q[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 1, (uint64_t)q[2] | ((uint64_t)q[3] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- element arithmetic
 // Sum of the squares of one vector's elements, exact in binary64 for the
 // fallback and within 7 * 2^-24 relative otherwise.  The common case sums the

@@ -69,14 +69,22 @@ __device__ uint64_t g_phase_stamps[GCLIP_STAMP_WORKERS * GCLIP_STAMP_POINTS];
 #endif
 
 // ---------------------------------------------------------------- group loads and stores
-// Load the vectors of one group into q (zeros where a lane has no vector).
-template <bool NT>
+// Load the vectors of one group into q (zeros where a lane has no vector);
+// DEV: with device-scope loads (data another XCD wrote in this launch).
+template <bool NT, bool DEV = false>
 __device__ __forceinline__ void load_group(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j,
                                            uint64_t j1, u32x4 (&q)[kUnroll]) {
   const uint32_t t = threadIdx.x;
   uint64_t base = 0;
   const int kind = group_kind(cur, vb, ve, j, j1, base);
-  if (kind == kGroupFull) {
+  if (DEV && kind != kGroupCross) {
+    const __amdgpu_buffer_rsrc_t rs = group_rsrc(uniform64(base), (uint32_t)kGroupVectors * kVecBytes);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      q[u] = kind == kGroupFull || tail_ok(vb, ve, j, j1, u, t)
+                 ? ld_vec_dev<NT>(rs, ((uint32_t)u * kThreads + t) * kVecBytes)
+                 : u32x4{0u, 0u, 0u, 0u};
+  } else if (kind == kGroupFull) {
     const g_u32x4* g = reinterpret_cast<const g_u32x4*>(uniform64(base));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) q[u] = ld_vec<NT>(&g[u * kThreads + t]);
@@ -95,21 +103,28 @@ __device__ __forceinline__ void load_group(const DevPlan& p, Cursor& cur, uint64
       if (j + u < j1) {
         const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
         const uint64_t a = step_addr(p, cur, b, ve, v);
-        if (v < ve) q[u] = load_vec<NT>(a);
+        if (v < ve) q[u] = DEV ? load_vec_dev(a) : load_vec<NT>(a);
       }
     }
   }
 }
 
 // Store f(vector u) for every vector of one group (the addresses of the
-// group are recomputed exactly as load_group computed them).
-template <bool NT, typename F>
+// group are recomputed exactly as load_group computed them); DEV: with
+// device-scope stores (data another XCD reads in this launch).
+template <bool NT, bool DEV = false, typename F>
 __device__ __forceinline__ void store_group(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j,
                                             uint64_t j1, F&& f) {
   const uint32_t t = threadIdx.x;
   uint64_t base = 0;
   const int kind = group_kind(cur, vb, ve, j, j1, base);
-  if (kind == kGroupFull) {
+  if (DEV && kind != kGroupCross) {
+    const __amdgpu_buffer_rsrc_t rs = group_rsrc(uniform64(base), (uint32_t)kGroupVectors * kVecBytes);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (kind == kGroupFull || tail_ok(vb, ve, j, j1, u, t))
+        st_vec_dev<NT>(rs, ((uint32_t)u * kThreads + t) * kVecBytes, f(u));
+  } else if (kind == kGroupFull) {
     g_u32x4* g = reinterpret_cast<g_u32x4*>(uniform64(base));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) st_vec<NT>(&g[u * kThreads + t], f(u));
@@ -125,7 +140,13 @@ __device__ __forceinline__ void store_group(const DevPlan& p, Cursor& cur, uint6
       if (j + u < j1) {
         const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
         const uint64_t a = step_addr(p, cur, b, ve, v);
-        if (v < ve) store_vec<NT>(a, f(u));
+        if (v < ve) {
+          if constexpr (DEV) {
+            store_vec_dev(a, f(u));
+          } else {
+            store_vec<NT>(a, f(u));
+          }
+        }
       }
     }
   }
@@ -166,15 +187,16 @@ __device__ __forceinline__ double norm_scalars(const DevPlan& p, int w) {
   return s;
 }
 
-// Steps [j0, j1) of the run [vb, ve): read, multiply, write back.  A group's
-// loads are all issued before its first store.
-template <int DT>
+// Steps [j0, j1) of the run [vb, ve): read (DEV: with device-scope loads),
+// multiply, write back.  A group's loads are all issued before its first
+// store.
+template <int DT, bool DEV = false>
 __device__ __forceinline__ void scale_steps(const DevPlan& p, Cursor& cur, uint64_t vb, uint64_t ve, uint64_t j0,
                                             uint64_t j1, double s64, float s32) {
   for (uint64_t j = j0; j < j1; j += kUnroll) {
     u32x4 q[kUnroll];
     Cursor c2 = cur;
-    load_group<kNtScale>(p, cur, vb, ve, j, j1, q);
+    load_group<kNtScale, DEV>(p, cur, vb, ve, j, j1, q);
     store_group<false>(p, c2, vb, ve, j, j1, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
   }
 }
@@ -215,14 +237,14 @@ __device__ __forceinline__ void load_group_contrib(const DevPlan& p, const AccSr
     }
   } else {
     const uint64_t b0 = vb + j * kThreads;
+    uint64_t d = ld_table(A.seg_gdelta, (uint64_t)uniform32(cur.s));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       h[u] = u32x4{0u, 0u, 0u, 0u};
       if (j + u < j1) {
         const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
-        uint32_t sv = 0;
-        const uint64_t a = step_addr_seg(p, cur, b, ve, v, sv);
-        if (v < ve) h[u] = load_vec<NT>(a + A.seg_gdelta[sv]);
+        const uint64_t a = step_addr_delta(p, A.seg_gdelta, cur, d, b, ve, v);
+        if (v < ve) h[u] = load_vec<NT>(a);
       }
     }
   }
@@ -422,9 +444,9 @@ __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
 }
 
 // Scale in place every chunk of the table (vb, seg, nch) that this workgroup
-// takes.  A chunk's last group is scaled into registers before the ticket is
-// resolved, and stored after it.
-template <int DT, bool NTS>
+// takes (DEV: read with device-scope loads).  A chunk's last group is scaled
+// into registers before the ticket is resolved, and stored after it.
+template <int DT, bool NTS, bool DEV = false>
 __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, const uint64_t* vb,
                                              const uint32_t* seg, uint32_t nch, double s64, float s32) {
   if (blockIdx.x >= nch) return;  // then no chunk is left to claim either
@@ -436,7 +458,7 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, c
   {
     const Range r = tab_chunk_range(vb, seg, c);
     cursor_load(p, cur, r.seg);
-    load_group<kNtScale>(p, cur, r.b, r.e, 0, range_steps(r), q);
+    load_group<kNtScale, DEV>(p, cur, r.b, r.e, 0, range_steps(r), q);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
     const Range r = tab_chunk_range(vb, seg, c);
@@ -448,7 +470,7 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, c
     uint64_t j = 0;
     for (; j + kUnroll < ns; j += kUnroll) {
       u32x4 q2[kUnroll];
-      load_group<kNtScale>(p, cur, r.b, r.e, j + kUnroll, ns, q2);
+      load_group<kNtScale, DEV>(p, cur, r.b, r.e, j + kUnroll, ns, q2);
       store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
@@ -463,7 +485,7 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, c
       u32x4 q2[kUnroll];
       const Range rn = tab_chunk_range(vb, seg, cn);
       cursor_load(p, curn, rn.seg);
-      load_group<kNtScale>(p, curn, rn.b, rn.e, 0, range_steps(rn), q2);
+      load_group<kNtScale, DEV>(p, curn, rn.b, rn.e, 0, range_steps(rn), q2);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
     }
@@ -475,8 +497,9 @@ __device__ __forceinline__ void scale_chunks(const DevPlan& p, ClaimSlots& sl, c
 }
 
 // The sum chunks this workgroup takes, with the +=: every group is read
-// with its contribution (both one group ahead), added, written back and
-// summed, one partial per chunk as in norm_chunks.
+// with its contribution (both one group ahead), added, written back with
+// device-scope stores (after the decision any workgroup may rescale them)
+// and summed, one partial per chunk as in norm_chunks.
 template <int DT, bool NTS>
 __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, ClaimSlots& sl) {
   const uint32_t nch = p.nsum;
@@ -510,7 +533,7 @@ __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, 
       load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, j + kUnroll, ns, h2);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) q[u] = add_vec<DT>(q[u], h[u]);
-      store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return q[u]; });
+      store_group<NTS, true>(p, cst, r.b, r.e, j, ns, [&](int u) { return q[u]; });
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
 #pragma unroll
@@ -521,7 +544,7 @@ __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, 
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) q[u] = add_vec<DT>(q[u], h[u]);
-    store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return q[u]; });
+    store_group<NTS, true>(p, cst, r.b, r.e, j, ns, [&](int u) { return q[u]; });
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc[u] += vec_sumsq<DT>(q[u]);
     const uint32_t par = i & 1u;
@@ -612,13 +635,14 @@ struct HandSlots {
 };
 
 // Take over every block handed back so far and scale it from memory, with
-// the worker's single elements and its own chunk of the streamed region (no
-// other workgroup scales it: the first scale chunk, which workgroup w takes
-// without a claim; with the +=, the sum chunk it summed) -- the whole
-// workgroup.  With the += (ACC) the block was never written: it is read with
-// its contribution, added and written -- times s only when `scale` (the sum
-// is written whatever the decision); the single elements and the chunk
-// already hold their sums, and are scaled only when `scale`.
+// the worker's single elements and its own chunks of the streamed region (no
+// other workgroup scales them: the two scale chunks workgroup w takes
+// without a claim) -- the whole workgroup.  With the += (ACC) the block was
+// never written: it is read with its contribution, added and written --
+// times s only when `scale` (the sum is written whatever the decision); the
+// single elements and the chunks already hold their sums, and are scaled
+// only when `scale` (the chunks' sums, which any workgroup may have written,
+// read with device-scope loads).
 template <int DT, bool ACC = false>
 __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& hs, double s64, float s32,
                                                    const AccSrc& A = AccSrc{}, bool scale = true) {
@@ -650,24 +674,13 @@ __device__ __forceinline__ void take_handed_blocks(const DevPlan& p, HandSlots& 
       }
       if (ACC && !scale) continue;
       scale_scalars<DT>(p, v, s64, s32);
-      // the worker's own chunks: with the +=, the sum chunk it summed; else
-      // the two scale chunks it takes without a claim
-      if constexpr (ACC) {
-        if ((uint32_t)v < p.nsum) {
-          const Range c = sum_chunk_range(p, (uint32_t)v);
-          Cursor cur;
-          cursor_load(p, cur, c.seg);
-          scale_steps<DT>(p, cur, c.b, c.e, 0, range_steps(c), s64, s32);
-        }
-      } else {
-        for (uint32_t k = 0; k < 2; ++k) {
-          const uint32_t own = (uint32_t)v + k * (uint32_t)p.nworkers;
-          if (own >= p.nchs) break;
-          const Range c = tab_chunk_range(p.fus_vb, p.fus_seg, own);
-          Cursor cur;
-          cursor_load(p, cur, c.seg);
-          scale_steps<DT>(p, cur, c.b, c.e, 0, range_steps(c), s64, s32);
-        }
+      for (uint32_t k = 0; k < 2; ++k) {
+        const uint32_t own = (uint32_t)v + k * (uint32_t)p.nworkers;
+        if (own >= p.nchs) break;
+        const Range c = tab_chunk_range(p.fus_vb, p.fus_seg, own);
+        Cursor cur;
+        cursor_load(p, cur, c.seg);
+        scale_steps<DT, ACC>(p, cur, c.b, c.e, 0, range_steps(c), s64, s32);
       }
     }
     __syncthreads();
@@ -790,26 +803,6 @@ __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_n
 // Scale one range in place, the next group's loads issued before the
 // current group is stored (the += kernel's own sum chunk).
 template <int DT, bool NTS>
-__device__ __forceinline__ void scale_range(const DevPlan& p, const Range& r, double s64, float s32) {
-  const uint64_t ns = range_steps(r);
-  if (ns == 0) return;
-  Cursor cur;
-  cursor_load(p, cur, r.seg);
-  Cursor cst = cur;
-  u32x4 q[kUnroll];
-  load_group<kNtScale>(p, cur, r.b, r.e, 0, ns, q);
-  uint64_t j = 0;
-  for (; j + kUnroll < ns; j += kUnroll) {
-    u32x4 q2[kUnroll];
-    load_group<kNtScale>(p, cur, r.b, r.e, j + kUnroll, ns, q2);
-    store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) q[u] = q2[u];
-  }
-  store_group<NTS>(p, cst, r.b, r.e, j, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
-}
-
-template <int DT, bool NTS>
 __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSlots& sl, const Range& r,
                                                        const BlockSplit& bs, const u32x4 (&keep)[kRegSteps],
                                                        const u32x4* keep_lds, double s64, float s32) {
@@ -833,7 +826,8 @@ __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSl
 }
 
 // With the += (ACC): the block's sums, scaled when `scale`, and -- only then
-// -- the scale chunks of the streamed region (which hold sums already).
+// -- the scale chunks of the streamed region it claims (which hold sums
+// already, written by any workgroup: read with device-scope loads).
 template <int DT, bool NTS>
 __device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& sl, const Range& r,
                                                  const BlockSplit& bs, const u32x4 (&keep)[kRegSteps],
@@ -856,7 +850,7 @@ __device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& s
       });
   }
   GCLIP_STAMP(GCLIP_STAMP_BLOCK_WRITTEN);
-  if (scale && blockIdx.x < p.nsum) scale_range<DT, NTS>(p, sum_chunk_range(p, blockIdx.x), s64, s32);
+  if (scale) scale_chunks<DT, NTS, true>(p, sl, p.fus_vb, p.fus_seg, p.nchs, s64, s32);
   GCLIP_STAMP(GCLIP_STAMP_CHUNKS_SCALED);
 }
 
@@ -873,11 +867,13 @@ __device__ __forceinline__ void write_block_sums(const DevPlan& p, ClaimSlots& s
 //
 // With the last microbatch's contribution (ACC), phase 1 adds it as it reads:
 // the workgroup's sum chunk of the streamed region is written back as sums at
-// once, the block is kept as sums on chip (its LDS steps are read first, one
-// group of both lists ahead, while the registers that will hold the rest are
-// still free), and phase 2 writes the block's sums -- scaled, unless the
-// decision writes nothing, when they are written as they are -- so the block
-// is written once; then it rescales its own sum chunk.
+// once (device-scope stores), the block is kept as sums on chip (its LDS
+// steps are read first, one group of both lists ahead, while the registers
+// that will hold the rest are still free), and phase 2 writes the block's
+// sums -- scaled, unless the decision writes nothing, when they are written
+// as they are -- so the block is written once; then, when the decision
+// scales, it rescales the scale chunks of the streamed region it claims, as
+// the plain clip scales them, with device-scope loads.
 template <int DT, bool NTS, bool ACC>
 __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, double max_norm, AvgSrc avs, int err,
                                            gclip_result* res, uint64_t wait_ticks, const AmpUpdate& amp) {
@@ -896,8 +892,6 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   GCLIP_STAMP(GCLIP_STAMP_START);
 
   if constexpr (ACC) {
-    static_assert(kSumChunksPerWorker == 1,
-                  "the += kernel rescales the sum chunk it summed: one sum chunk per worker, none claimed");
     accum_chunks<DT, NTS>(p, A, sl);
   } else {
     norm_chunks<DT>(p, sl);
@@ -1007,11 +1001,14 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   if (t == 0) atomic_st(worker_partial(p, w), part);
 
   // grid-wide decision: the last workgroup to arrive reduces and releases.
-  // With the +=, phase 2 rescales only what this workgroup wrote in phase 1
-  // (its sum chunk and single elements), which a barrier makes visible to it;
-  // only a hand-back passes them to another workgroup, and that is done with
-  // an agent-scope release (the state word) and acquire (the taker's
-  // compare-and-swap), once every wave's stores here have completed.
+  // With the +=, the sums of the streamed region were stored with
+  // device-scope stores, every wave's completed before the arrival ticket,
+  // and whoever rescales them after the decision loads them with
+  // device-scope loads.  The single elements were stored with ordinary
+  // stores: phase 2 rescales only this workgroup's own, which a barrier makes
+  // visible to it, and only a hand-back passes them to another workgroup,
+  // with an agent-scope release (the state word) and acquire (the taker's
+  // compare-and-swap).
   if constexpr (ACC) {
     complete_stores();
     __syncthreads();

@@ -89,12 +89,12 @@ void replay_contrib_group(const DevPlan& p, const AccSrc& A, Cursor& cur, uint64
   const uint64_t b0 = vb + j * kThreads;
   for (uint32_t t = 0; t < (uint32_t)kThreads; ++t) {
     Cursor c = cur;
+    uint64_t d = A.seg_gdelta[c.s];
     for (int u = 0; u < kUnroll; ++u) {
       if (j + u >= j1) continue;
       const uint64_t b = b0 + (uint64_t)u * kThreads, v = b + t;
-      uint32_t sv = 0;
-      const uint64_t a = step_addr_seg(p, c, b, ve, v, sv);
-      if (v < ve) rec->put(w, a + A.seg_gdelta[sv]);
+      const uint64_t a = step_addr_delta(p, A.seg_gdelta, c, d, b, ve, v);
+      if (v < ve) rec->put(w, a);
     }
     if (t == 0) {
       end = c;
