@@ -1450,8 +1450,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_tensor_clip_fused(DevPlan p, Te
     double v = 0.0;
     int nf_mine = 0, clipped_mine = 0;
     for (int32_t j = (int32_t)t; j < T.ntensors; j += kThreads) {
+      // the raw sum is loaded with the table entries, not after them (an
+      // empty tensor's slot holds no sum and is not used)
+      const double Sr = atomic_ld(&T.tsum[j]);
       const bool live = ld_table(T.first, (uint64_t)j) < ld_table(T.first, (uint64_t)j + 1);
-      const double S = live ? atomic_ld(&T.tsum[j]) : 0.0;
+      const double S = live ? Sr : 0.0;
       v += S;
       nf_mine |= nonfinite_of(S, avg);
       clipped_mine |= decide((avg * avg) * S, nonfinite_of(S, avg), max_norm, avg, err).clipped;
@@ -1479,7 +1482,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_tensor_clip_fused(DevPlan p, Te
       res->decided = 1;
       atomic_st(reinterpret_cast<uint32_t*>(&res->status), 0u);
       skip_all = skip;
-      complete_stores();  // the stop switch's factors before the decision
+      // published by value, as in clip_fused: no workgroup reads the figures
+      // or the result block after it, so no store here need complete first
       atomic_st(&p.bcast[0], skip ? kDecidedSkip : __builtin_bit_cast(uint64_t, 1.0));
     }
   } else if (t == 0) {
