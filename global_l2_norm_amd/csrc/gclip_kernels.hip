@@ -27,9 +27,11 @@
 //     in index order, so the bits of the norm do not depend on scheduling or
 //     on which workgroup took which chunk, and both paths give the same
 //     bits; cross-workgroup data moves only through agent-scope atomics (see
-//     complete_stores); the += kernel's phase 2 rescales only the sums the
-//     same workgroup wrote in phase 1, except when a block is handed back,
-//     which passes them on with an agent-scope release and acquire;
+//     complete_stores) and, for the += kernel's sums, device-scope vector
+//     stores and loads (ld_vec_dev); the += kernel's single elements are
+//     rescaled by the workgroup that wrote them, except when a block is
+//     handed back, which passes them on with an agent-scope release and
+//     acquire;
 //   - the fused kernel keeps each worker's block (up to kRegSteps +
 //     kLdsSteps steps) in VGPRs and LDS across the grid-wide decision, so the
 //     scale pass writes those bytes without reading them again from HBM; it
@@ -800,8 +802,6 @@ __global__ __launch_bounds__(kThreads) void k_grad_scale(DevPlan p, double max_n
 
 // Phase 2 of the fused kernel: the block straight from VGPRs and LDS, then
 // the scale chunks of the streamed region this workgroup claims.
-// Scale one range in place, the next group's loads issued before the
-// current group is stored (the += kernel's own sum chunk).
 template <int DT, bool NTS>
 __device__ __forceinline__ void write_block_and_chunks(const DevPlan& p, ClaimSlots& sl, const Range& r,
                                                        const BlockSplit& bs, const u32x4 (&keep)[kRegSteps],

@@ -9,7 +9,7 @@
  * build records, per workgroup, the wall-clock time at which each of its
  * phases ended, so that the time of one launch can be split between them.
  * With the += the summing pass also writes the sums of the streamed region,
- * and the scaling pass rescales the workgroup's own sum chunk.  The
+ * and the scaling pass rescales the scale chunks the workgroup claims.  The
  * one-launch per-tensor clip (gclip_clip_per_tensor_ on the fused path)
  * records the same points over pieces: its streamed run summed, its resident
  * pieces read, its tensors counted and completed, the decision seen, its
