@@ -243,8 +243,8 @@ gclip_status gclip_list_create(void* const* d_ptrs, const int64_t* numels, int32
 
     const uint64_t* addrs = reinterpret_cast<const uint64_t*>(d_ptrs);
     std::string why;
-    const int rc = gclip::plan_build(addrs, numels, n_tensors, dtype, ncu, gclip::worker_threads(),
-                                     gclip::resident_cap_vectors(), gclip::chunk_shape(), L->plan, &why);
+    const int rc = gclip::plan_build_list(addrs, numels, n_tensors, dtype, ncu, gclip::worker_threads(),
+                                          gclip::resident_cap_vectors(), gclip::chunk_shape(), L->plan, &why);
     if (rc != 0) {
       delete L;
       return (gclip_status)rc;

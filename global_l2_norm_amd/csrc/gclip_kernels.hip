@@ -1099,6 +1099,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_accum_clip_fused(DevPlan p, Acc
   clip_fused<DT, NTS, true>(p, A, max_norm, avs, err, res, wait_ticks, AmpUpdate{nullptr, 0.0, 0.0, 0});
 }
 
+// ---------------------------------------------------------------- a list of one group, one workgroup
+// A plan with one_group set has a single worker whose block is the whole
+// vector space (one group of steps) and at most one single element per
+// lane.  One workgroup then takes the whole clip: the group's loads, its
+// sum, the decision and -- only if it writes -- the scaled group from the
+// same registers.  It adds the same values in the same order as the grid
+// kernels do on this plan (the block's steps into acc[j % kUnroll], the
+// single elements per lane, wg_sum into the worker's partial), and the
+// partial is the norm's sum as it is: the grid kernels' last workgroup adds
+// the one partial to zeros, which leaves its bits as they are.  So the bits
+// are those of both paths, without a ticket, an atomic or a wait.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_grad_clip_small(DevPlan p, double max_norm, AvgSrc avs, int err,
+                                                              gclip_result* res, AmpUpdate amp) {
+  const double avg = avg_value(avs);
+  __shared__ double red[kWaves];
+  __shared__ double bc_s;
+  __shared__ int bc_write;
+  const Range r = block_range(p, 0);
+  const uint64_t ns = range_steps(r);
+  Cursor cur;
+  u32x4 q[kUnroll];
+  double acc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    q[u] = u32x4{0u, 0u, 0u, 0u};
+    acc[u] = 0.0;
+  }
+  if (ns > 0) {
+    cursor_load(p, cur, r.seg);
+    Cursor c0 = cur;
+    load_group<kNtSum>(p, c0, r.b, r.e, 0, ns, q);
+  }
+  const double sc = norm_scalars<DT>(p, 0);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if ((uint64_t)u < ns) acc[u] += vec_sumsq<DT>(q[u]);
+  const double S = wg_sum(lane_total(acc, sc), red);
+  if (threadIdx.x == 0) {
+    const Decision d = decide((avg * avg) * S, nonfinite_of(S, avg), max_norm, avg, err);
+    write_norm(res, S, avg);
+    write_decision(res, d, max_norm);
+    res->status = 0;
+    res->handed_back = 0;
+    if (amp.st) amp_update(amp.st, nonfinite_of(S, avg), amp);
+    bc_s = d.s;
+    bc_write = !(d.skip || d.s == 1.0);
+  }
+  __syncthreads();
+  if (!bc_write) return;
+  const double s64 = bc_s;
+  const float s32 = (float)s64;
+  if (ns > 0) store_group<false>(p, cur, r.b, r.e, 0, ns, [&](int u) { return scale_vec<DT>(q[u], s64, s32); });
+  scale_scalars<DT>(p, 0, s64, s32);
+}
+
 // ---------------------------------------------------------------- per-tensor clip in one launch
 // Grad clip lesson, "Two variants: Per-Tensor or Global": every tensor by its
 // own norm, in one launch that keeps part of the list on chip across the
@@ -1678,6 +1734,13 @@ hipError_t launch_accum_fused(const DevPlan& p, const AccSrc& A, int32_t dtype, 
 hipError_t launch_fused(const DevPlan& p, int32_t dtype, double max_norm, AvgSrc avg, int err, gclip_result* res,
                         uint64_t wait_ticks, AmpUpdate amp, hipStream_t st) {
   DevPlan pc = p;
+  if (p.one_group) {
+    void* args[] = {&pc, &max_norm, &avg, &err, &res, &amp};
+    const void* fn = dtype == GCLIP_F32   ? (const void*)k_grad_clip_small<GCLIP_F32>
+                     : dtype == GCLIP_F16 ? (const void*)k_grad_clip_small<GCLIP_F16>
+                                          : (const void*)k_grad_clip_small<GCLIP_BF16>;
+    return hipLaunchKernel(fn, dim3(1), dim3(kThreads), args, 0, st);
+  }
   void* args[] = {&pc, &max_norm, &avg, &err, &res, &wait_ticks, &amp};
   const void* fn = p.nt_store ? fused_kernel<true>(dtype) : fused_kernel<false>(dtype);
   return hipLaunchKernel(fn, dim3((unsigned)p.nworkers), dim3(kThreads), args, 0, st);

@@ -103,8 +103,8 @@ extern "C" gclip_status gclip_clip_noalloc_(void* const* d_ptrs, const int64_t* 
     // calls reuse it
     thread_local HostPlan plan;
     thread_local std::vector<unsigned char> image;
-    const int rc = plan_build(addrs, numels, n_tensors, dtype, ds->ncu, worker_threads(), resident_cap_vectors(),
-                              chunk_shape(), plan, nullptr);
+    const int rc = plan_build_list(addrs, numels, n_tensors, dtype, ds->ncu, worker_threads(),
+                                   resident_cap_vectors(), chunk_shape(), plan, nullptr);
     if (rc != 0) return (gclip_status)rc;
     const PlanLayout L = plan_layout(plan);
     if (L.bytes > kScratchBytes) return GCLIP_ERANGE;

@@ -240,9 +240,23 @@ DevPlan plan_view(const HostPlan& p, const PlanLayout& L, unsigned char* b) {
   D.nchs = (uint32_t)p.nchunk_streamed();
   D.nsum = (uint32_t)p.nsum();
   D.nt_store = p.n_bytes >= kNtStoreMinBytes ? 1u : 0u;
+  D.one_group = p.one_group ? 1u : 0u;
   D.nworkers = p.nworkers;
   D.nseg = (int32_t)p.nseg();
   return D;
+}
+
+int plan_build_list(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t ncu,
+                    int32_t threads, uint64_t resident_cap, const ChunkShape& shape, HostPlan& out,
+                    std::string* why) {
+  int rc = plan_build(addrs, numels, n, dtype, ncu, threads, resident_cap, shape, out, why);
+  if (rc != 0) return rc;
+  auto fits = [&](const HostPlan& p) {
+    return p.nvec() <= shape.group_vectors && p.nsc() <= (uint64_t)threads;
+  };
+  if (ncu > 1 && fits(out)) rc = plan_build(addrs, numels, n, dtype, 1, threads, resident_cap, shape, out, why);
+  if (rc == 0) out.one_group = out.nworkers == 1 && out.sb == 0 && fits(out);
+  return rc;
 }
 
 int tensor_plan_build(const HostPlan& p, uint32_t piece_vectors, TensorHostPlan& out) {

@@ -64,6 +64,8 @@ struct HostPlan {
   std::vector<int32_t> sc_tensor;    // nsc
   std::vector<int64_t> sc_elem;      // nsc
   std::vector<uint64_t> wk_scbegin;  // nworkers + 1
+  bool one_group = false;            // one worker, and the whole list is one group of vectors plus at most
+                                     // one single element per lane (see plan_build_list)
 
   int64_t nseg() const { return (int64_t)seg_addr.size(); }
   uint64_t nvec() const { return seg_vbegin.empty() ? 0 : seg_vbegin.back(); }
@@ -92,6 +94,15 @@ struct ChunkShape {
 
 int plan_build(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t nworkers,
                int32_t threads, uint64_t resident_cap, const ChunkShape& shape, HostPlan& out, std::string* why);
+
+// The plan of a list on a device of ncu compute units: one worker per
+// compute unit, unless the whole list is one group of vectors and at most
+// one single element per lane -- then a single worker, so that one
+// workgroup can take the whole clip with no grid-wide decision (its launch
+// and round trips, not its bytes, set the time of such a list).
+int plan_build_list(const uint64_t* addrs, const int64_t* numels, int32_t n, int32_t dtype, int32_t ncu,
+                    int32_t threads, uint64_t resident_cap, const ChunkShape& shape, HostPlan& out,
+                    std::string* why);
 
 // The fused kernel's decision word (bcast[0]): the bits of the factor s, or
 // one of two signalling-NaN patterns.  Arithmetic never yields a signalling
@@ -135,6 +146,7 @@ struct DevPlan {
   uint32_t nchs;      // fused scale chunks over the streamed region [0, sb)
   uint32_t nsum;      // sum chunks over the streamed region [0, sb)
   uint32_t nt_store;  // 1: the scale passes write with nontemporal stores (lists of kNtStoreMinBytes or more)
+  uint32_t one_group; // 1: HostPlan::one_group
   int32_t nworkers;
   int32_t nseg;
 };

@@ -408,6 +408,56 @@ def test_scale_with_caller_supplied_sumsq():
     gu.assert_elems_close(out, ref, "f32", "external sumsq")
 
 
+# ------------------------------------------------------------------ lists of one group
+# A list whose vectors fit in one group of steps (512 lanes x 8 = 4,096
+# vectors of 16 bytes) with at most one single element per lane gets a plan
+# with one worker, and the fused path clips it in one workgroup with no
+# grid-wide decision; the split path runs its two kernels on the same plan.
+# Both must give the same bits, and the oracle's values.
+ONE_GROUP_CASES = [
+    ("tiny", "f32", [2, 64 * 64, 128, 33 * 17, 1], True),
+    ("6_8", "f32", [2], True),
+    ("4096 vectors f32", "f32", [16384], True),
+    ("4097 vectors f32", "f32", [16388], False),
+    ("4096 vectors bf16", "bf16", [32768], True),
+    ("512 single elements", "f16", [1] * 512, True),
+    ("513 single elements", "f16", [1] * 513, False),
+    ("mixed", "bf16", [3, 1000, 63, 20000, 5], True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ONE_GROUP_CASES)))
+def test_one_group_lists(case):
+    import torch
+    name, dtype, numels, one = ONE_GROUP_CASES[case]
+    rng = np.random.default_rng(900 + case)
+    arrays = [gs.to_storage(rng.standard_normal(n), dtype) for n in numels]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    norm = oracle.clip_([a.copy() for a in arrays], dtype, 1e30)["norm"]
+    for max_norm, err, bad in ((0.5 * norm, False, False), (2.0 * norm, False, False), (0.5 * norm, True, True),
+                               (0.5 * norm, False, True)):
+        cur = [a.copy() for a in arrays]
+        if bad:
+            cur[-1][-1] = gs.to_storage(np.array([math.nan]), dtype)[0]
+        what = f"{name} max_norm {max_norm:.4g} err {err} nan {bad}"
+        outs = {}
+        for path in PATHS:
+            ts = gu.upload(cur, dtype)
+            gl = make_list(ts, path)
+            assert gl.info()["n_workers"] == (1 if one else ncu), what
+            gl.clip_(max_norm, 1.0, err)
+            st, r = gl.read(err)
+            outs[path] = (r, gu.download(ts, dtype))
+            gl.close()
+        (rf, of), (rs, os_) = outs["fused"], outs["split"]
+        gu.assert_bitwise_equal(of, os_, what + " (fused vs split)")
+        for k in ("clipped", "skipped", "nonfinite"):
+            assert rf[k] == rs[k], (what, k)
+        if not bad:
+            assert rf["sumsq"] == rs["sumsq"] and rf["scale"] == rs["scale"], what
+        check_against_oracle(cur, dtype, max_norm, err=err, path="fused", what=what)
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("path", PATHS)
 def test_empty_list(path):
