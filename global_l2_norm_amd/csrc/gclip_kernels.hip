@@ -1055,6 +1055,11 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
     if (!gave_up) {
       bc_skip = dw == kDecidedSkip ? 1 : 0;
       bc_s = bc_skip ? 1.0 : __builtin_bit_cast(double, dw);
+      // with the +=, phase 2 loads sums that other workgroups stored: an
+      // agent-scope acquire first, so that no copy of their lines that this
+      // XCD's caches took earlier (a line shared with a single element or a
+      // block) is read in their place
+      if constexpr (ACC) acquire_agent();
     }
   }
   __syncthreads();
