@@ -379,7 +379,10 @@ def main():
     wrote = not (r["skipped"] or r["scale"] == 1.0)
     alg = algorithmic_bytes(g.numel, esize, wrote)
     gbps = alg / (mean_ms * 1e-3) / 1e9
-    kernels = "k_grad_clip_fused" if path_name == "fused" else "k_grad_norm_partial+k_grad_scale"
+    # a list of one group (one worker) is clipped by one workgroup on the fused path
+    one_group = info["n_workers"] == 1 and info["n_vectors"] <= 4096 and info["n_scalars"] <= info["worker_threads"]
+    kernels = (("k_grad_clip_small" if one_group else "k_grad_clip_fused") if path_name == "fused"
+               else "k_grad_norm_partial+k_grad_scale")
     traffic = read_traffic(kernels, a.config)
     roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernels,
@@ -1025,8 +1028,8 @@ def _counter_rows(d):
 
 def _short_kernel(name):
     base = name.split("(")[0]
-    for k in ("k_grad_clip_fused", "k_grad_norm_partial", "k_grad_scale", "k_accum_clip_fused", "k_ref_read",
-              "k_ref_copy"):
+    for k in ("k_grad_clip_fused", "k_grad_clip_small", "k_grad_norm_partial", "k_grad_scale", "k_accum_clip_fused",
+              "k_ref_read", "k_ref_copy"):
         if k in base:
             return base.replace("void ", "").strip()
     if "neg_kernel" in name:

@@ -131,7 +131,9 @@ typedef struct gclip_list_info_t {
   int64_t n_segments;      /* 16-byte-aligned vector runs */
   int64_t n_vectors;       /* 16-byte vectors over all runs */
   int64_t n_scalars;       /* elements handled one by one (unaligned ends, tiny tensors) */
-  int32_t n_workers;       /* workgroups of the launch (one per compute unit) */
+  int32_t n_workers;       /* workgroups of the launch: one per compute unit, or one for a list whose
+                              vectors fit in one group (4,096 vectors) with at most one single element
+                              per thread, which the fused path clips in one workgroup */
   int32_t worker_threads;  /* threads per workgroup */
   int32_t dtype;
   int32_t path;            /* gclip_path that gclip_clip_ will use */
