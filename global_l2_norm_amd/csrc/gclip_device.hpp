@@ -54,9 +54,10 @@ __device__ __forceinline__ void store_vec(uint64_t a, u32x4 q) { st_vec<NT>(rein
 // another, on any XCD, reads later in the same launch.  Each XCD has an L2
 // of its own that ordinary stores only reach (it is written back to memory
 // at the end of the kernel), so such data is stored with the device-scope
-// bit (sc1: written through to memory) and loaded with it (served from
-// memory, not from a line an L2 may hold), the encoding of agent-scope
-// atomic accesses.  The 16-byte forms go through a buffer resource, whose
+// bit (sc1: written through to memory) and loaded with it, the encoding of
+// agent-scope atomic accesses; the reader takes an agent-scope acquire
+// before its loads, since a line it shares with other data may sit in its
+// own caches.  The 16-byte forms go through a buffer resource, whose
 // base must be the same in every lane: a group's base address; a vector at
 // an address of its own takes two agent-scope 8-byte accesses instead.
 constexpr int kAuxNt = 2;    // cache policy bits of the buffer builtins: nt
