@@ -188,8 +188,9 @@ gclip_status gclip_plan_query(const uint64_t* addrs, const int64_t* numels, int3
     }
     for (uint64_t c = 0; c < p.nchunk(); ++c) emit_vectors(-1, p.spl_vb[c], p.spl_vb[c + 1], 2);
     for (uint64_t c = 0; c < p.nsum(); ++c) {
-      const uint64_t b = c * p.cvs;
-      emit_vectors(-1, b, b + p.cvs < p.sb ? b + p.cvs : p.sb, 3);
+      const uint64_t b = gclip::sum_chunk_begin(p.cvs_even, p.cvs_odd, c);
+      const uint64_t e = gclip::sum_chunk_begin(p.cvs_even, p.cvs_odd, c + 1);
+      emit_vectors(-1, b, e < p.sb ? e : p.sb, 3);
     }
     for (uint64_t c = 0; c < p.nchunk_streamed(); ++c) emit_vectors(-1, p.fus_vb[c], p.fus_vb[c + 1], 4);
     *n_out = k;

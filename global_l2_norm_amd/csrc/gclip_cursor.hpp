@@ -218,11 +218,23 @@ __host__ __device__ __forceinline__ Range tab_chunk_range(const uint64_t* vb, co
   return r;
 }
 
-// Sum chunk c (cut at sb).
+// Sum chunk c (cut at sb).  TWO: a list of kNtStoreMinBytes or more, whose
+// sum chunks alternate between two sizes (sum_groups); otherwise all are cvs
+// vectors.  The kernels of such lists (NTS) take TWO, the others keep the
+// one-size arithmetic.
+template <bool TWO = false>
 __host__ __device__ __forceinline__ Range sum_chunk_range(const DevPlan& p, uint32_t c) {
   Range r;
-  r.b = (uint64_t)c * p.cvs;
-  r.e = r.b + p.cvs < p.sb ? r.b + p.cvs : p.sb;
+  if constexpr (TWO) {
+    const uint64_t ce = (uint64_t)(p.sum_groups & 0xffffu) * kGroupVectors;
+    const uint64_t co = (uint64_t)(p.sum_groups >> 16) * kGroupVectors;
+    r.b = sum_chunk_begin(ce, co, c);
+    const uint64_t e = r.b + ((c & 1u) ? co : ce);
+    r.e = e < p.sb ? e : p.sb;
+  } else {
+    r.b = (uint64_t)c * p.cvs;
+    r.e = r.b + p.cvs < p.sb ? r.b + p.cvs : p.sb;
+  }
   r.seg = ld_table(p.sum_seg, c);
   return r;
 }

@@ -393,7 +393,7 @@ __device__ __forceinline__ double chunk_total(const double (&ws)[kWaves]) {
 // every wave) thread 0 adds the waves' values in wave order into the chunk's
 // own slot, partials[c], so the final sum does not depend on which workgroup
 // took the chunk.
-template <int DT>
+template <int DT, bool TWO>
 __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
   const uint32_t nch = p.nsum;
   if (blockIdx.x >= nch) return;  // then no chunk is left to claim either
@@ -403,12 +403,12 @@ __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
   Cursor cur;
   u32x4 q[kUnroll];
   {
-    const Range r = sum_chunk_range(p, c);
+    const Range r = sum_chunk_range<TWO>(p, c);
     cursor_load(p, cur, r.seg);
     load_group<kNtSum>(p, cur, r.b, r.e, 0, range_steps(r), q);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
-    const Range r = sum_chunk_range(p, c);
+    const Range r = sum_chunk_range<TWO>(p, c);
     const uint64_t ns = range_steps(r);
     uint32_t tk = 0;
     if (t == 0 && cn != kNone) tk = claim_issue(cl);
@@ -429,7 +429,7 @@ __device__ __forceinline__ void norm_chunks(const DevPlan& p, ClaimSlots& sl) {
     if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(cl, tk) : kNone;
     Cursor curn;
     if (cn != kNone) {
-      const Range rn = sum_chunk_range(p, cn);
+      const Range rn = sum_chunk_range<TWO>(p, cn);
       cursor_load(p, curn, rn.seg);
       load_group<kNtSum>(p, curn, rn.b, rn.e, 0, range_steps(rn), q);
     }
@@ -527,14 +527,14 @@ __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, 
   Cursor cur, cg;
   u32x4 q[kUnroll], h[kUnroll];
   {
-    const Range r = sum_chunk_range(p, c);
+    const Range r = sum_chunk_range<NTS>(p, c);
     cursor_load(p, cur, r.seg);
     cg = cur;
     load_group<kNtSum>(p, cur, r.b, r.e, 0, range_steps(r), q);
     load_group_contrib<kNtSum>(p, A, cg, r.b, r.e, 0, range_steps(r), h);
   }
   for (uint32_t i = 0; c != kNone; ++i) {
-    const Range r = sum_chunk_range(p, c);
+    const Range r = sum_chunk_range<NTS>(p, c);
     const uint64_t ns = range_steps(r);
     uint32_t tk = 0;
     if (t == 0 && cn != kNone) tk = claim_issue(cl);
@@ -568,7 +568,7 @@ __device__ __forceinline__ void accum_chunks(const DevPlan& p, const AccSrc& A, 
     if (t == 0) sl.claim[par] = cn != kNone ? claim_resolve(cl, tk) : kNone;
     Cursor curn, cgn;
     if (cn != kNone) {
-      const Range rn = sum_chunk_range(p, cn);
+      const Range rn = sum_chunk_range<NTS>(p, cn);
       cursor_load(p, curn, rn.seg);
       cgn = curn;
       load_group<kNtSum>(p, curn, rn.b, rn.e, 0, range_steps(rn), q);
@@ -754,14 +754,14 @@ __device__ __forceinline__ void finish(const DevPlan& p, gclip_result* res, bool
 // worker); the last workgroup to arrive sums every partial in index order.
 // The fused kernel adds the same values in the same order, so both paths
 // give the same bits.
-template <int DT>
+template <int DT, bool TWO>
 __global__ __launch_bounds__(kThreads) void k_grad_norm_partial(DevPlan p, AvgSrc avs, gclip_result* res) {
   const double avg = avg_value(avs);
   __shared__ double red[kWaves];
   __shared__ ClaimSlots sl;
   __shared__ int flag;
   const int w = blockIdx.x;
-  norm_chunks<DT>(p, sl);
+  norm_chunks<DT, TWO>(p, sl);
   double acc[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
@@ -909,7 +909,7 @@ __device__ __forceinline__ void clip_fused(const DevPlan& p, const AccSrc& A, do
   if constexpr (ACC) {
     accum_chunks<DT, NTS>(p, A, sl);
   } else {
-    norm_chunks<DT>(p, sl);
+    norm_chunks<DT, NTS>(p, sl);
   }
   GCLIP_STAMP(GCLIP_STAMP_CHUNKS_SUMMED);
   double acc[kUnroll];
@@ -1714,10 +1714,18 @@ ChunkShape chunk_shape() {
 
 hipError_t launch_norm(const DevPlan& p, int32_t dtype, AvgSrc avg, gclip_result* res, hipStream_t st) {
   const dim3 grid((unsigned)p.nworkers), block(kThreads);
-  switch (dtype) {
-    case GCLIP_F32: hipLaunchKernelGGL(k_grad_norm_partial<GCLIP_F32>, grid, block, 0, st, p, avg, res); break;
-    case GCLIP_F16: hipLaunchKernelGGL(k_grad_norm_partial<GCLIP_F16>, grid, block, 0, st, p, avg, res); break;
-    default: hipLaunchKernelGGL(k_grad_norm_partial<GCLIP_BF16>, grid, block, 0, st, p, avg, res); break;
+  if (p.nt_store) {
+    switch (dtype) {
+      case GCLIP_F32: hipLaunchKernelGGL((k_grad_norm_partial<GCLIP_F32, true>), grid, block, 0, st, p, avg, res); break;
+      case GCLIP_F16: hipLaunchKernelGGL((k_grad_norm_partial<GCLIP_F16, true>), grid, block, 0, st, p, avg, res); break;
+      default: hipLaunchKernelGGL((k_grad_norm_partial<GCLIP_BF16, true>), grid, block, 0, st, p, avg, res); break;
+    }
+  } else {
+    switch (dtype) {
+      case GCLIP_F32: hipLaunchKernelGGL((k_grad_norm_partial<GCLIP_F32, false>), grid, block, 0, st, p, avg, res); break;
+      case GCLIP_F16: hipLaunchKernelGGL((k_grad_norm_partial<GCLIP_F16, false>), grid, block, 0, st, p, avg, res); break;
+      default: hipLaunchKernelGGL((k_grad_norm_partial<GCLIP_BF16, false>), grid, block, 0, st, p, avg, res); break;
+    }
   }
   return hipGetLastError();
 }

@@ -15,7 +15,8 @@
 //     (workgroup): what the fused kernel keeps on chip between its passes;
 //   - the rest, the streamed region [0, sb), is cut into chunks; each
 //     worker takes two without a claim, the rest are claimed at run time, so
-//     that the XCDs that stream faster take more of them: "sum chunks" of cvs vectors for the summing passes (a
+//     that the XCDs that stream faster take more of them: "sum chunks" for the summing passes (cvs vectors
+//     each; in lists of kNtStoreMinBytes or more two sizes in turn, see HostPlan::cvs_even) (a
 //     sum chunk's partial goes to a slot of its own, so the content and
 //     order of the final sum do not depend on which worker took which
 //     chunk), and "scale chunks" for the fused kernel's scale pass.  The
@@ -36,6 +37,12 @@ constexpr int kVecBytes = 16;
 constexpr int64_t kMinSegVectors = 64;  // aligned bodies shorter than 1 KB are handled element by element
 
 inline int dtype_bytes(int32_t dtype) { return dtype == 0 ? 4 : 2; }
+
+// Start of sum chunk c when the chunks alternate between ce vectors (even c)
+// and co vectors (odd c).  (constexpr: host and device code alike.)
+constexpr uint64_t sum_chunk_begin(uint64_t ce, uint64_t co, uint64_t c) {
+  return (c >> 1) * (ce + co) + ((c & 1u) ? ce : 0u);
+}
 inline bool dtype_valid(int32_t dtype) { return dtype == 0 || dtype == 1 || dtype == 2; }
 
 struct HostPlan {
@@ -53,7 +60,10 @@ struct HostPlan {
   std::vector<int64_t> seg_elem0;    // nseg: element index of the segment start in its tensor
   uint64_t rb = 0;                   // vectors per block: worker w's is [sb + w rb, sb + (w + 1) rb) cut at nvec
   uint64_t sb = 0;                   // end of the streamed region, start of the blocks
-  uint64_t cvs = 0;                  // vectors per sum chunk: chunk c is [c cvs, (c + 1) cvs) cut at sb
+  uint64_t cvs_even = 0;             // vectors per sum chunk: chunks of cvs_even (even index) and cvs_odd (odd
+  uint64_t cvs_odd = 0;              // index) in turn from 0, cut at sb (sum_chunk_begin); equal unless the list
+                                     // is of kNtStoreMinBytes or more
+  uint32_t sum_groups = 0;           // in such a list, both sizes in groups: cvs_even | cvs_odd << 16
   std::vector<uint32_t> blk_seg;     // nworkers: segment holding each block's first vector
   std::vector<uint64_t> spl_vb;      // nchunk + 1: scale chunk c of the split kernel is [spl_vb[c], spl_vb[c + 1])
   std::vector<uint32_t> spl_seg;     // nchunk: segment holding each of those chunks' first vector
@@ -141,7 +151,7 @@ struct DevPlan {
   uint64_t* bcast;    // [0]: the decision of the fused kernel, published by value (kUndecided between launches)
   uint32_t* sync;     // kSyncWords counters (see above)
   uint32_t* bstate;   // nworkers: whether each block was handed back by the fused kernel
-  uint64_t nvec, rb, sb, cvs;
+  uint64_t nvec, rb, sb, cvs;  // cvs: the sum chunks' size when it is one (lists under kNtStoreMinBytes)
   uint32_t nchunk;    // split scale chunks over [0, nvec)
   uint32_t nchs;      // fused scale chunks over the streamed region [0, sb)
   uint32_t nsum;      // sum chunks over the streamed region [0, sb)
@@ -149,6 +159,7 @@ struct DevPlan {
   uint32_t one_group; // 1: HostPlan::one_group
   int32_t nworkers;
   int32_t nseg;
+  uint32_t sum_groups;  // HostPlan::sum_groups (lists of kNtStoreMinBytes or more)
 };
 
 // Where a plan's tables and workspace lie in one device allocation (byte

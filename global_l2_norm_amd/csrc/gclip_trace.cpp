@@ -139,7 +139,8 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
     p.nchunk = (uint32_t)hp.nchunk();
     p.nchs = (uint32_t)hp.nchunk_streamed();
     p.nsum = (uint32_t)hp.nsum();
-    p.cvs = hp.cvs;
+    p.cvs = hp.cvs_even;
+    p.sum_groups = hp.sum_groups;
     p.nworkers = hp.nworkers;
     p.nseg = (int32_t)hp.nseg();
     Recorder rec{out_addr, out_worker, cap};
@@ -154,7 +155,7 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
       const AccSrc A{dseg.data(), dsc.data()};
       if (mode == 5) {  // k_accum_clip_fused, first pass: sum chunks, then each block and its single elements
         for (uint32_t c = 0; c < p.nsum; ++c) {
-          const Range r = sum_chunk_range(p, c);
+          const Range r = p.sum_groups ? sum_chunk_range<true>(p, c) : sum_chunk_range<false>(p, c);
           Cursor cg;
           cursor_load(p, cg, r.seg);
           for (uint64_t j = 0; j < range_steps(r); j += kUnroll)
@@ -222,7 +223,7 @@ extern "C" gclip_status gclip_plan_trace(const uint64_t* addrs, const int64_t* n
     // the summing passes claim the sum chunks of the streamed region first
     if (mode == 0 || mode == 2) {
       for (uint32_t c = 0; c < p.nsum; ++c) {
-        const Range r = sum_chunk_range(p, c);
+        const Range r = p.sum_groups ? sum_chunk_range<true>(p, c) : sum_chunk_range<false>(p, c);
         Cursor cur;
         cursor_load(p, cur, r.seg);
         replay_groups(p, cur, r.b, r.e, 0, range_steps(r), -1, &rec);

@@ -177,6 +177,49 @@ def test_plan_covers_every_element_once(dtype, seed):
     assert sc_per_worker.max() - sc_per_worker.min() <= 1
 
 
+def _runs_cover_once(entries, numels, kinds):
+    runs = [[] for _ in numels]
+    for w, t, b, c, kind in entries:
+        if kind in kinds:
+            runs[t].append((b, c))
+    for t, n in enumerate(numels):
+        at = 0
+        for b, c in sorted(runs[t]):
+            assert b == at, f"tensor {t}: gap or overlap at element {at}"
+            at = b + c
+        assert at == n, f"tensor {t}: {at} of {n} elements covered"
+
+
+def test_plan_over_1gib_covers_every_element_once():
+    """A list of 1 GiB or more (the 1.3B bf16 shapes, 2.6 GB) has sum chunks
+    of two sizes in turn; the summing passes (blocks, single elements, sum
+    chunks) and both scale passes still take every element exactly once.
+    Counted by runs, without a per-element array."""
+    numels = [int(np.prod(s)) for _, s in gs.shapes_gpt1p3b()]
+    assert sum(numels) * 2 >= 1 << 30
+    addrs = fake_layout(np.random.default_rng(9), numels, 2, misalign=True)
+    entries = g.gclip_plan_query(addrs, numels, 2, 256, 512)
+    _runs_cover_once(entries, numels, (0, 1, 3))
+    _runs_cover_once(entries, numels, (1, 2))
+    _runs_cover_once(entries, numels, (0, 1, 4))
+    # inside the largest tensor the sum-chunk runs are whole chunks, larger
+    # and smaller in turn (even- and odd-numbered workers), 1.07 : 0.93 to
+    # within a group; a list under 1 GiB keeps one size
+    big = int(np.argmax(numels))
+    lens = [c for _, c in sorted((b, c) for w, t, b, c, k in entries if k == 3 and t == big)][1:-1]
+    assert len(lens) >= 4 and len(set(lens)) == 2
+    assert all(lens[i] != lens[i + 1] for i in range(len(lens) - 1))
+    hi, lo = max(lens), min(lens)
+    group = 8 * 512 * 8  # elements of a group of bf16 vectors
+    assert abs(hi * 0.93 - lo * 1.07) <= 2 * group
+    numels = [int(np.prod(s)) for _, s in gs.shapes_andrea120m()]
+    addrs = fake_layout(np.random.default_rng(9), numels, 4, misalign=False)
+    entries = g.gclip_plan_query(addrs, numels, 0, 256, 512)
+    big = int(np.argmax(numels))
+    lens = [c for _, c in sorted((b, c) for w, t, b, c, k in entries if k == 3 and t == big)][1:-1]
+    assert len(set(lens)) == 1
+
+
 @pytest.mark.parametrize("mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("dtype", [0, 1, 2])
 @pytest.mark.parametrize("seed", range(4))
