@@ -258,6 +258,19 @@ def test_gpt1p3b_bf16(c5, c5_clipped, path):
     gu.assert_elems_close(out, ref, "bf16", f"gpt1p3b {path}")
 
 
+@pytest.mark.timeout(900)
+def test_gpt1p3b_bf16_paths_agree_bitwise(c5):
+    """On the 2.6 GB list, whose sum chunks come in two sizes (weighted by
+    XCD), the fused kernel and the split norm kernel add the same partials
+    in the same order: the same sum, norm and factor to the bit, and the
+    same bits in every element."""
+    runs = [gpu_clip(c5.arrays, "bf16", c5.max_norm, path=path) for path in PATHS]
+    (_, rf, of), (_, rs, os_) = runs
+    for k in ("sumsq", "norm", "scale", "clipped", "nonfinite", "status"):
+        assert rf[k] == rs[k], k
+    gu.assert_bitwise_equal(of, os_, "gpt1p3b fused vs split")
+
+
 def with_value(g, tensor, index, bits):
     arrays = list(g.arrays)
     t = g.names.index(tensor)
